@@ -1,0 +1,136 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 training quantizer.
+ *
+ * Pages cited (title, then the section):
+ *   [P1] "在 RTX 5090 (SM120) 上补全 NVFP4 量化相关 kernel" -- blog post on polyfilling NVFP4 quantization kernels
+ *        for the RTX 5090 (harrychen.xyz, 2026-04-14).
+ *   [P2] "nvfp4-sm120" repository README.
+ *   [P3] pytorch/ao pull request #4852, "Add a CuTe DSL fast-path kernel for four-over-six quantize".
+ *
+ * The method.  A bf16 tensor is quantized to NVFP4: E2M1 4-bit codes (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6;
+ * [P1, FP4 quantization techniques]) with one E4M3 scale per block of 16 consecutive elements (or per 16x16
+ * tile) on top of one FP32 global scale g = amax / (6 * 448) per tensor or per row ([P2, layout]; [P3]).
+ * Rounding is round-to-nearest-even or stochastic rounding with Philox random bytes ([P1, stochastic rounding]);
+ * optionally each 16-element block is first rotated by a 16x16 Hadamard matrix with random signs
+ * ([P1, random Hadamard transform]).  Four-over-six ([P3]) encodes every block at the map-to-6 and the
+ * 1.5x-scale map-to-4 scale and keeps the one with lower squared error.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor argument is DEVICE memory owned by the caller.  The library never allocates, frees or
+ *     synchronises; every call is asynchronous on `stream` (a hipStream_t; NULL = the default stream).
+ *     The global amax stays on the device: nothing is read back to the host ([P2, results: a host sync on the
+ *     amax dominated quantization time]).
+ *   - Inputs are bf16 bit patterns (uint16), row-major and contiguous, [rows, cols].
+ *   - "View" V: row-wise quantization works on V = X ([rows, cols]); column-wise on V = X^T ([cols, rows]),
+ *     read directly from X without a transposed copy.  Blocks are 16 consecutive elements of a row of V.
+ *   - Outputs of a quantization (struct nvfp4_out, all device pointers):
+ *       codes  [Rv, Cv/2] uint8: byte k of a row holds element 2k in its low nibble and 2k+1 in its high nibble;
+ *              a code is sign << 3 | m, m indexing the magnitude list above;
+ *       scales [Rv, Cv/16] uint8: E4M3 ("fn": bias 7, max 448, 0x7F = NaN) block scales;
+ *       g      [1] (per tensor) or [Rv] (per row of V) float: the global scale amax / 2688 actually used.
+ *   - Element scaling: with T = 6, s = bamax / fl(T g) (correctly rounded), sb = E4M3(s) (round to nearest even,
+ *     saturating at 448, NaN -> 0x7F), S = fl(decode(sb) g), r = fl(1 / S) (r = 0 if S = 0, NaN if S is NaN,
+ *     FLT_MAX if it overflows), q_i = fl(y_i r); E2M1(q_i) saturates at +-6 and maps NaN to 0x7.
+ *   - NaN propagates: the amax is the integer maximum of the magnitude bit patterns, so one NaN (or inf) makes
+ *     the amax NaN (or inf) and every block of that tensor (or row) decodes to NaN ([P1, RHT GEMM rewrite and
+ *     vibe-coding sections: dropping NaN in min/max was a bug]).
+ *   - Errors: arguments are validated on the host before anything is enqueued.  On an error the call returns a
+ *     non-zero nvfp4_status and enqueues nothing; there is no fallback path.  NVFP4_ERR_HIP reports a failed
+ *     launch (the kernels may then not have run).
+ *   - Alignment: x, codes, scales and y must be 16-byte aligned; amax and g 4-byte aligned.
+ *   - Sizes: rows, cols >= 0; rows * cols < 2^36.  A zero-sized tensor is valid: its amax is 0 and a quantize
+ *     call only writes g.
+ *   - Calls on different streams may run concurrently; they share no state.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NVFP4_OK = 0,
+    NVFP4_ERR_NULL = 1,        /* a required pointer is NULL */
+    NVFP4_ERR_SHAPE = 2,       /* a size is negative, too large, or not the multiple of 16 (or 8) required */
+    NVFP4_ERR_ALIGN = 3,       /* a pointer is not aligned as required */
+    NVFP4_ERR_UNSUPPORTED = 4, /* an unknown enum value or an unsupported combination */
+    NVFP4_ERR_HIP = 5          /* the HIP runtime reported an error when launching */
+} nvfp4_status;
+
+typedef enum { NVFP4_ROWWISE = 1, NVFP4_COLWISE = 2, NVFP4_BOTH = 3 } nvfp4_orient;
+typedef enum { NVFP4_BLOCK_1X16 = 0, NVFP4_BLOCK_16X16 = 1 } nvfp4_block;
+typedef enum { NVFP4_G_PER_TENSOR = 0, NVFP4_G_PER_ROW = 1 } nvfp4_gmode;
+
+typedef struct {
+    uint8_t* codes;  /* [Rv, Cv/2] */
+    uint8_t* scales; /* [Rv, Cv/16] */
+    float* g;        /* [1] or [Rv] */
+} nvfp4_out;
+
+/* Absolute maximum ([P2, results: per-tensor amax kept on the device]; [P3]: row-scaled global scales).
+ *   x [rows, cols] bf16; orient NVFP4_ROWWISE or NVFP4_COLWISE selects the view V;
+ *   gmode NVFP4_G_PER_TENSOR writes amax[0], NVFP4_G_PER_ROW writes amax[Rv] (one per row of V);
+ *   use_rht != 0: the maximum is taken over the Hadamard-transformed blocks (same sign_mask as the quantize call).
+ *   Shape: the same rules as the quantize call it feeds: row-wise cols % 16 == 0; column-wise rows % 16 == 0
+ *   and cols % 8 == 0. */
+nvfp4_status nvfp4_amax(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_orient orient, nvfp4_gmode gmode,
+                        int use_rht, uint16_t sign_mask, float* amax, void* stream);
+
+/* Round-to-nearest quantization ([P1, stochastic rounding: IEEE round-to-nearest is the hardware default];
+ * [P2, layout and results: forward activations and both weight orientations use round-to-nearest]).
+ *   block NVFP4_BLOCK_1X16: orient ROWWISE writes *row_out, COLWISE writes *col_out (the other may be NULL).
+ *   block NVFP4_BLOCK_16X16 ([P2, intro: 2D weight scaling]; [P3]: 16x16 blocks): one E4M3 scale per 16x16 tile
+ *     of X, per-tensor g only; orient ROWWISE writes W to *row_out ([rows, cols/2] codes, [rows, cols/16] scales),
+ *     COLWISE writes W^T to *col_out ([cols, rows/2], [cols, rows/16]), BOTH writes both from one read of X.
+ *     Each tile's scale is repeated in the 1x16 scale layout of each orientation (16 entries per tile).
+ *   amax: [1] or [Rv] device floats from nvfp4_amax (without RHT).
+ *   Shape: 1x16 row-wise needs cols % 16 == 0; column-wise rows % 16 == 0 and cols % 8 == 0; 16x16 needs both
+ *   rows and cols multiples of 16.  Unsupported: 16x16 with per-row g; 1x16 with BOTH. */
+nvfp4_status nvfp4_quantize_rn(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_block block,
+                               nvfp4_orient orient, nvfp4_gmode gmode, const float* amax, const nvfp4_out* row_out,
+                               const nvfp4_out* col_out, void* stream);
+
+/* Stochastic-rounding quantization, 1x16 blocks ([P1, stochastic rounding]: P(up) = (x - a) / (b - a); the
+ * random source is 8 bits per element).  Element j of the block with row-major index n in V rounds up iff
+ * rho < floor(256 (t - a) / (b - a)), rho = byte (j % 4) of word (j / 4) of Philox4x32-10 with
+ * key = (seed lo, seed hi) and counter = (n lo, n hi, offset lo, offset hi).  A new offset per call gives fresh
+ * randomness; the same (seed, offset) reproduces the same bits.
+ *   orient ROWWISE or COLWISE (writes *out).  amax from nvfp4_amax without RHT. */
+nvfp4_status nvfp4_quantize_sr(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_orient orient,
+                               nvfp4_gmode gmode, const float* amax, uint64_t seed, uint64_t offset,
+                               const nvfp4_out* out, void* stream);
+
+/* Random Hadamard Transform + stochastic rounding, 1x16 blocks ([P1, random Hadamard transform and RHT GEMM
+ * rewrite]: the fused rotate-and-quantize used for weight-gradient operands, [P2, results: Wgrad RHT+SR]).
+ * Each 16-element block v of V becomes y = (1/4) H16 diag(s) v (Sylvester H16, s_i = -1 where bit i of
+ * sign_mask is set), evaluated as the butterfly with strides 1, 2, 4, 8 in binary32 followed by one multiply
+ * by 0.25; y is then quantized as in nvfp4_quantize_sr.
+ *   amax: from nvfp4_amax with use_rht = 1 and the same sign_mask (the amax of the transformed values). */
+nvfp4_status nvfp4_quantize_rht_sr(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_orient orient,
+                                   nvfp4_gmode gmode, const float* amax, uint16_t sign_mask, uint64_t seed,
+                                   uint64_t offset, const nvfp4_out* out, void* stream);
+
+/* Four-over-six quantization ([P3]): row-wise 1x16 blocks, round-to-nearest, no RHT.  Each block is encoded with
+ * T = 6 and with T = 4 (scale bamax / fl(4 g), 1.5x the map-to-6 scale); both are decoded as
+ * fl(fl(val * decode(sb)) * g); the squared errors fl(d * d), d = fl(xhat - x), are summed by the tree
+ * (i, i+8), then strides 4, 2, 1; map-to-4 is kept only if its sum is strictly smaller (ties and NaN keep 6).
+ *   amax: [1] or [rows] from nvfp4_amax (row-wise, no RHT).  Shape: cols % 16 == 0. */
+nvfp4_status nvfp4_quantize_4o6(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_gmode gmode,
+                                const float* amax, const nvfp4_out* out, void* stream);
+
+/* Standard NVFP4 decode ([P3]: the recipe-agnostic decode): y = fl(fl(val(code) * decode(sb)) * g) as binary32.
+ *   codes [rv, cv/2], scales [rv, cv/16], g [1] or [rv] (gmode), y [rv, cv] float.  Shape: cv % 16 == 0. */
+nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv, int64_t cv,
+                              nvfp4_gmode gmode, float* y, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* nvfp4_status_str(nvfp4_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

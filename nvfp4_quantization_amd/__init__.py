@@ -1,0 +1,11 @@
+"""MI355X-native (gfx950, HIP) NVFP4 training quantizer.
+
+The compute lives in the HIP library built from ``csrc/`` (C ABI: ``include/nvfp4.h``); this package is its thin
+Python binding (``binding``), the hipcc build step (``_build``) and the seeded synthetic inputs used by the tests
+and the benchmark (``workloads``).
+"""
+from .binding import (  # noqa: F401
+    BLOCK_1X16, BLOCK_16X16, BOTH, COLWISE, G_PER_ROW, G_PER_TENSOR, ROWWISE, NVFP4Error, Quantized, alloc_out,
+    nvfp4_amax, nvfp4_dequantize, nvfp4_quantize_4o6, nvfp4_quantize_rht_sr, nvfp4_quantize_rn, nvfp4_quantize_sr,
+    view_shape,
+)

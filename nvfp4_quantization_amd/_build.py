@@ -1,0 +1,67 @@
+"""Build the HIP library (libnvfp4_hip.so) for gfx950 with hipcc.
+
+The library is built in-tree next to this file so that it travels with the source tree.  Object files go to
+``_build/`` at the repository root.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libnvfp4_hip.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+SOURCES = ["nvfp4_kernels.hip", "nvfp4_capi.hip"]
+ARCH = "gfx950"
+
+# -ffp-contract=off: every a*b+c stays two correctly rounded operations (the rounding of each step is part of the
+# method).  No fast-math.  Packed FP32 instructions are disabled for the device code.
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the NVFP4 HIP library cannot be built")
+
+
+def _run(cmd: list[str]) -> None:
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    # the host pass of hipcc does not know the device-only feature flag; that warning is expected
+    noise = ("packed-fp32-ops", "warning: unknown target feature", "1 warning generated")
+    msg = "\n".join(l for l in (p.stdout + p.stderr).splitlines() if not any(n in l for n in noise))
+    if p.returncode != 0:
+        raise RuntimeError("hipcc failed (%d):\n%s\n%s" % (p.returncode, " ".join(cmd), msg))
+    if msg.strip():
+        print(msg)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link the shared library (always rebuilds)."""
+    obj_dir = os.path.join(ROOT, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
+        cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        _run(cmd)
+        objs.append(obj)
+    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

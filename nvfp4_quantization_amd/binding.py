@@ -1,0 +1,180 @@
+"""Thin Python binding over the C ABI of ``include/nvfp4.h`` (ctypes).
+
+Argument marshalling only: tensors must already live on the GPU; this module checks dtypes and contiguity,
+allocates missing outputs with torch (device memory is torch's job), passes raw pointers and the current HIP
+stream, and turns a non-zero ``nvfp4_status`` into an exception.  Every step of the method runs in the HIP
+library; there is no CPU path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import NamedTuple, Optional
+
+import torch
+
+from ._build import LIB_PATH
+
+ROWWISE, COLWISE, BOTH = 1, 2, 3
+BLOCK_1X16, BLOCK_16X16 = 0, 1
+G_PER_TENSOR, G_PER_ROW = 0, 1
+
+STATUS = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_SHAPE", 3: "NVFP4_ERR_ALIGN",
+          4: "NVFP4_ERR_UNSUPPORTED", 5: "NVFP4_ERR_HIP"}
+
+# name -> (restype, argtypes); the same names and order as include/nvfp4.h
+_P, _I64, _U64, _U16, _I = C.c_void_p, C.c_int64, C.c_uint64, C.c_uint16, C.c_int
+SIGNATURES = {
+    "nvfp4_amax": (_I, [_P, _I64, _I64, _I, _I, _I, _U16, _P, _P]),
+    "nvfp4_quantize_rn": (_I, [_P, _I64, _I64, _I, _I, _I, _P, _P, _P, _P]),
+    "nvfp4_quantize_sr": (_I, [_P, _I64, _I64, _I, _I, _P, _U64, _U64, _P, _P]),
+    "nvfp4_quantize_rht_sr": (_I, [_P, _I64, _I64, _I, _I, _P, _U16, _U64, _U64, _P, _P]),
+    "nvfp4_quantize_4o6": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
+    "nvfp4_dequantize": (_I, [_P, _P, _P, _I64, _I64, _I, _P, _P]),
+    "nvfp4_status_str": (C.c_char_p, [_I]),
+}
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+        self.status = status
+
+
+class _Out(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("g", C.c_void_p)]
+
+
+class Quantized(NamedTuple):
+    codes: torch.Tensor   # [Rv, Cv/2] uint8
+    scales: torch.Tensor  # [Rv, Cv/16] uint8 (E4M3 codes)
+    g: torch.Tensor       # [1] or [Rv] float32
+
+
+_lib: Optional[C.CDLL] = None
+
+
+def lib() -> C.CDLL:
+    """Load the in-tree HIP library (it must have been built: ``python -m nvfp4_quantization_amd._build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"NVFP4 HIP library not built: {LIB_PATH} is missing "
+                               "(run python -m nvfp4_quantization_amd._build)")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise NVFP4Error(status, where)
+
+
+def _dev(t: torch.Tensor, what: str) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{what} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t.data_ptr()
+
+
+def _bf16(x: torch.Tensor) -> int:
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or x.dim() != 2:
+        raise TypeError("x must be a 2-D bf16 tensor (or its int16 bit patterns)")
+    return _dev(x, "x")
+
+
+def _stream(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def view_shape(rows: int, cols: int, orient: int) -> tuple[int, int]:
+    return (rows, cols) if orient == ROWWISE else (cols, rows)
+
+
+def alloc_out(rv: int, cv: int, gmode: int, device) -> Quantized:
+    return Quantized(torch.empty((rv, cv // 2), dtype=torch.uint8, device=device),
+                     torch.empty((rv, cv // 16), dtype=torch.uint8, device=device),
+                     torch.empty((rv if gmode == G_PER_ROW else 1,), dtype=torch.float32, device=device))
+
+
+def _out(o: Optional[Quantized]):
+    if o is None:
+        return None
+    return C.byref(_Out(_dev(o.codes, "codes"), _dev(o.scales, "scales"), _dev(o.g, "g")))
+
+
+def nvfp4_amax(x: torch.Tensor, orient: int = ROWWISE, gmode: int = G_PER_TENSOR, use_rht: bool = False,
+               sign_mask: int = 0, amax: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    rows, cols = x.shape
+    rv, _ = view_shape(rows, cols, orient)
+    if amax is None:
+        amax = torch.empty((rv if gmode == G_PER_ROW else 1,), dtype=torch.float32, device=x.device)
+    _check(lib().nvfp4_amax(_bf16(x), rows, cols, orient, gmode, int(bool(use_rht)), sign_mask & 0xFFFF,
+                            _dev(amax, "amax"), _stream(x.device, stream)), "nvfp4_amax")
+    return amax
+
+
+def nvfp4_quantize_rn(x: torch.Tensor, amax: torch.Tensor, block: int = BLOCK_1X16, orient: int = ROWWISE,
+                      gmode: int = G_PER_TENSOR, row_out: Optional[Quantized] = None,
+                      col_out: Optional[Quantized] = None, stream=None):
+    """Returns (row_out, col_out); the orientation(s) not requested are None."""
+    rows, cols = x.shape
+    want_row = orient in (ROWWISE, BOTH)
+    want_col = orient in (COLWISE, BOTH)
+    if want_row and row_out is None:
+        row_out = alloc_out(rows, cols, gmode, x.device)
+    if want_col and col_out is None:
+        col_out = alloc_out(cols, rows, gmode, x.device)
+    _check(lib().nvfp4_quantize_rn(_bf16(x), rows, cols, block, orient, gmode, _dev(amax, "amax"),
+                                   _out(row_out if want_row else None), _out(col_out if want_col else None),
+                                   _stream(x.device, stream)), "nvfp4_quantize_rn")
+    return (row_out if want_row else None), (col_out if want_col else None)
+
+
+def nvfp4_quantize_sr(x: torch.Tensor, amax: torch.Tensor, seed: int, offset: int, orient: int = ROWWISE,
+                      gmode: int = G_PER_TENSOR, out: Optional[Quantized] = None, stream=None) -> Quantized:
+    rows, cols = x.shape
+    if out is None:
+        out = alloc_out(*view_shape(rows, cols, orient), gmode, x.device)
+    _check(lib().nvfp4_quantize_sr(_bf16(x), rows, cols, orient, gmode, _dev(amax, "amax"), seed, offset, _out(out),
+                                   _stream(x.device, stream)), "nvfp4_quantize_sr")
+    return out
+
+
+def nvfp4_quantize_rht_sr(x: torch.Tensor, amax: torch.Tensor, sign_mask: int, seed: int, offset: int,
+                          orient: int = ROWWISE, gmode: int = G_PER_TENSOR, out: Optional[Quantized] = None,
+                          stream=None) -> Quantized:
+    rows, cols = x.shape
+    if out is None:
+        out = alloc_out(*view_shape(rows, cols, orient), gmode, x.device)
+    _check(lib().nvfp4_quantize_rht_sr(_bf16(x), rows, cols, orient, gmode, _dev(amax, "amax"), sign_mask & 0xFFFF,
+                                       seed, offset, _out(out), _stream(x.device, stream)), "nvfp4_quantize_rht_sr")
+    return out
+
+
+def nvfp4_quantize_4o6(x: torch.Tensor, amax: torch.Tensor, gmode: int = G_PER_ROW,
+                       out: Optional[Quantized] = None, stream=None) -> Quantized:
+    rows, cols = x.shape
+    if out is None:
+        out = alloc_out(rows, cols, gmode, x.device)
+    _check(lib().nvfp4_quantize_4o6(_bf16(x), rows, cols, gmode, _dev(amax, "amax"), _out(out),
+                                    _stream(x.device, stream)), "nvfp4_quantize_4o6")
+    return out
+
+
+def nvfp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, g: torch.Tensor, gmode: int = G_PER_TENSOR,
+                     y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    rv, half = codes.shape
+    if y is None:
+        y = torch.empty((rv, 2 * half), dtype=torch.float32, device=codes.device)
+    _check(lib().nvfp4_dequantize(_dev(codes, "codes"), _dev(scales, "scales"), _dev(g, "g"), rv, 2 * half, gmode,
+                                  _dev(y, "y"), _stream(codes.device, stream)), "nvfp4_dequantize")
+    return y

@@ -1,0 +1,172 @@
+// nvfp4_capi.hip -- the extern "C" entry points declared in include/nvfp4.h.
+//
+// Every entry point validates its arguments on the host first (no HIP call happens before validation passes, so
+// invalid calls enqueue nothing and touch no device), then hands the work to the launchers in
+// nvfp4_kernels.hip on the caller's stream.  There is no fallback path: an unsupported request is an error.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nvfp4.h"
+#include "nvfp4_launch.h"
+
+namespace {
+
+// Kernels index 16-element blocks with 32-bit integers: at most 2^36 elements per tensor (128 GiB of bf16).
+constexpr int64_t kMaxElems = int64_t(1) << 36;
+
+#define NVFP4_TRY(expr)                  \
+    do {                                 \
+        const nvfp4_status st_ = (expr); \
+        if (st_ != NVFP4_OK) return st_; \
+    } while (0)
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+nvfp4_status check_sizes(int64_t rows, int64_t cols) {
+    if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
+    if (rows >= kMaxElems || cols >= kMaxElems) return NVFP4_ERR_SHAPE;
+    if (rows != 0 && cols > (kMaxElems - 1) / rows) return NVFP4_ERR_SHAPE;
+    return NVFP4_OK;
+}
+
+// Shape rules of a 1x16 quantization (and of the amax that feeds it).
+nvfp4_status check_view(int64_t rows, int64_t cols, nvfp4_orient orient) {
+    if (orient == NVFP4_ROWWISE) return (cols % 16) ? NVFP4_ERR_SHAPE : NVFP4_OK;
+    if (orient == NVFP4_COLWISE) return (rows % 16 || cols % 8) ? NVFP4_ERR_SHAPE : NVFP4_OK;
+    return NVFP4_ERR_UNSUPPORTED;
+}
+
+nvfp4_status check_gmode(nvfp4_gmode gmode) {
+    return (gmode == NVFP4_G_PER_TENSOR || gmode == NVFP4_G_PER_ROW) ? NVFP4_OK : NVFP4_ERR_UNSUPPORTED;
+}
+
+// A buffer of n elements: it may be NULL only when n == 0 (torch hands out NULL for empty tensors).
+nvfp4_status check_buf(const void* p, int64_t n, uintptr_t align) {
+    if (n > 0 && !p) return NVFP4_ERR_NULL;
+    if (!aligned(p, align)) return NVFP4_ERR_ALIGN;
+    return NVFP4_OK;
+}
+
+// Output of a quantization of the view V = [rv, cv].
+nvfp4_status check_out(const nvfp4_out* out, int64_t rv, int64_t cv, nvfp4_gmode gmode) {
+    if (!out) return NVFP4_ERR_NULL;
+    NVFP4_TRY(check_buf(out->codes, rv * (cv / 2), 16));
+    NVFP4_TRY(check_buf(out->scales, rv * (cv / 16), 16));
+    return check_buf(out->g, gmode == NVFP4_G_PER_ROW ? rv : 1, 4);
+}
+
+nvfp4_status check_input(const uint16_t* x, int64_t rows, int64_t cols, const float* amax, int64_t n_amax) {
+    NVFP4_TRY(check_buf(x, rows * cols, 16));
+    return check_buf(amax, n_amax, 4);
+}
+
+int64_t view_rows(int64_t rows, int64_t cols, nvfp4_orient orient) {
+    return orient == NVFP4_COLWISE ? cols : rows;
+}
+
+nvfp4_status done(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
+
+nvfp4_status quantize_1x16(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_orient orient, nvfp4_gmode gmode,
+                           const float* amax, nvfp4::Mode mode, uint16_t sign_mask, uint64_t seed, uint64_t offset,
+                           const nvfp4_out* out, void* stream) {
+    NVFP4_TRY(check_sizes(rows, cols));
+    NVFP4_TRY(check_gmode(gmode));
+    NVFP4_TRY(check_view(rows, cols, orient));
+    const int64_t rv = view_rows(rows, cols, orient), cv = orient == NVFP4_COLWISE ? rows : cols;
+    NVFP4_TRY(check_input(x, rows, cols, amax, gmode == NVFP4_G_PER_ROW ? rv : 1));
+    NVFP4_TRY(check_out(out, rv, cv, gmode));
+    return done(nvfp4::launch_quant_1x16(x, rows, cols, orient == NVFP4_COLWISE, gmode == NVFP4_G_PER_ROW, mode,
+                                         amax, sign_mask, nvfp4::Philox{seed, offset}, out->codes, out->scales,
+                                         out->g, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_amax(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_orient orient, nvfp4_gmode gmode,
+                        int use_rht, uint16_t sign_mask, float* amax, void* stream) {
+    NVFP4_TRY(check_sizes(rows, cols));
+    NVFP4_TRY(check_gmode(gmode));
+    NVFP4_TRY(check_view(rows, cols, orient));
+    NVFP4_TRY(check_input(x, rows, cols, amax, gmode == NVFP4_G_PER_ROW ? view_rows(rows, cols, orient) : 1));
+    return done(nvfp4::launch_amax(x, rows, cols, orient == NVFP4_COLWISE, gmode == NVFP4_G_PER_ROW, use_rht != 0,
+                                   sign_mask, amax, static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_quantize_rn(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_block block,
+                               nvfp4_orient orient, nvfp4_gmode gmode, const float* amax, const nvfp4_out* row_out,
+                               const nvfp4_out* col_out, void* stream) {
+    if (block == NVFP4_BLOCK_1X16) {
+        if (orient == NVFP4_ROWWISE)
+            return quantize_1x16(x, rows, cols, orient, gmode, amax, nvfp4::kRN, 0, 0, 0, row_out, stream);
+        if (orient == NVFP4_COLWISE)
+            return quantize_1x16(x, rows, cols, orient, gmode, amax, nvfp4::kRN, 0, 0, 0, col_out, stream);
+        return NVFP4_ERR_UNSUPPORTED;
+    }
+    if (block != NVFP4_BLOCK_16X16) return NVFP4_ERR_UNSUPPORTED;
+    NVFP4_TRY(check_sizes(rows, cols));
+    NVFP4_TRY(check_gmode(gmode));
+    if (gmode != NVFP4_G_PER_TENSOR) return NVFP4_ERR_UNSUPPORTED;
+    if (orient != NVFP4_ROWWISE && orient != NVFP4_COLWISE && orient != NVFP4_BOTH) return NVFP4_ERR_UNSUPPORTED;
+    if (rows % 16 || cols % 16) return NVFP4_ERR_SHAPE;
+    NVFP4_TRY(check_input(x, rows, cols, amax, 1));
+    const bool want_w = orient == NVFP4_ROWWISE || orient == NVFP4_BOTH;
+    const bool want_wt = orient == NVFP4_COLWISE || orient == NVFP4_BOTH;
+    if (want_w) NVFP4_TRY(check_out(row_out, rows, cols, gmode));
+    if (want_wt) NVFP4_TRY(check_out(col_out, cols, rows, gmode));
+    return done(nvfp4::launch_quant_16x16(
+        x, rows, cols, amax, want_w ? row_out->codes : nullptr, want_w ? row_out->scales : nullptr,
+        want_w ? row_out->g : nullptr, want_wt ? col_out->codes : nullptr, want_wt ? col_out->scales : nullptr,
+        want_wt ? col_out->g : nullptr, static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_quantize_sr(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_orient orient,
+                               nvfp4_gmode gmode, const float* amax, uint64_t seed, uint64_t offset,
+                               const nvfp4_out* out, void* stream) {
+    return quantize_1x16(x, rows, cols, orient, gmode, amax, nvfp4::kSR, 0, seed, offset, out, stream);
+}
+
+nvfp4_status nvfp4_quantize_rht_sr(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_orient orient,
+                                   nvfp4_gmode gmode, const float* amax, uint16_t sign_mask, uint64_t seed,
+                                   uint64_t offset, const nvfp4_out* out, void* stream) {
+    return quantize_1x16(x, rows, cols, orient, gmode, amax, nvfp4::kRHTSR, sign_mask, seed, offset, out, stream);
+}
+
+nvfp4_status nvfp4_quantize_4o6(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_gmode gmode,
+                                const float* amax, const nvfp4_out* out, void* stream) {
+    NVFP4_TRY(check_sizes(rows, cols));
+    NVFP4_TRY(check_gmode(gmode));
+    if (cols % 16) return NVFP4_ERR_SHAPE;
+    NVFP4_TRY(check_input(x, rows, cols, amax, gmode == NVFP4_G_PER_ROW ? rows : 1));
+    NVFP4_TRY(check_out(out, rows, cols, gmode));
+    return done(nvfp4::launch_quant_4o6(x, rows, cols, gmode == NVFP4_G_PER_ROW, amax, out->codes, out->scales,
+                                        out->g, static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv, int64_t cv,
+                              nvfp4_gmode gmode, float* y, void* stream) {
+    NVFP4_TRY(check_sizes(rv, cv));
+    NVFP4_TRY(check_gmode(gmode));
+    if (cv % 16) return NVFP4_ERR_SHAPE;
+    NVFP4_TRY(check_buf(codes, rv * (cv / 2), 16));
+    NVFP4_TRY(check_buf(scales, rv * (cv / 16), 16));
+    NVFP4_TRY(check_buf(g, gmode == NVFP4_G_PER_ROW ? rv : 1, 4));
+    NVFP4_TRY(check_buf(y, rv * cv, 16));
+    return done(nvfp4::launch_dequantize(codes, scales, g, rv, cv, gmode == NVFP4_G_PER_ROW, y,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+const char* nvfp4_status_str(nvfp4_status status) {
+    switch (status) {
+        case NVFP4_OK: return "NVFP4_OK";
+        case NVFP4_ERR_NULL: return "NVFP4_ERR_NULL: a required pointer is NULL";
+        case NVFP4_ERR_SHAPE: return "NVFP4_ERR_SHAPE: unsupported size";
+        case NVFP4_ERR_ALIGN: return "NVFP4_ERR_ALIGN: misaligned pointer";
+        case NVFP4_ERR_UNSUPPORTED: return "NVFP4_ERR_UNSUPPORTED: unsupported option or combination";
+        case NVFP4_ERR_HIP: return "NVFP4_ERR_HIP: kernel launch failed";
+    }
+    return "unknown nvfp4_status";
+}
+
+}  // extern "C"

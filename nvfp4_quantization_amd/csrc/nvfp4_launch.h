@@ -1,0 +1,39 @@
+// nvfp4_launch.h -- internal interface between the C-ABI shim (nvfp4_capi.hip) and the kernels
+// (nvfp4_kernels.hip).  Arguments reaching these launchers have already been validated; each launcher only
+// enqueues work on `stream` and returns the HIP error of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+enum Mode : int { kRN = 0, kSR = 1, kRHTSR = 2 };
+
+struct Philox {
+    uint64_t seed;
+    uint64_t offset;
+};
+
+// amax of V (row-wise: V = X, column-wise: V = X^T); per_row selects one value per row of V.
+hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, bool colwise, bool per_row, bool use_rht,
+                       uint32_t sign_mask, float* amax, hipStream_t stream);
+
+// 1x16 quantization of V (RN, SR or RHT+SR).
+hipError_t launch_quant_1x16(const uint16_t* x, int64_t rows, int64_t cols, bool colwise, bool per_row, Mode mode,
+                             const float* amax, uint32_t sign_mask, Philox rng, uint8_t* codes, uint8_t* scales,
+                             float* g, hipStream_t stream);
+
+// 16x16 RN quantization; either output (codes == nullptr) may be skipped.
+hipError_t launch_quant_16x16(const uint16_t* x, int64_t rows, int64_t cols, const float* amax, uint8_t* codes_w,
+                              uint8_t* scales_w, float* g_w, uint8_t* codes_wt, uint8_t* scales_wt, float* g_wt,
+                              hipStream_t stream);
+
+// Four-over-six, row-wise 1x16 RN.
+hipError_t launch_quant_4o6(const uint16_t* x, int64_t rows, int64_t cols, bool per_row, const float* amax,
+                            uint8_t* codes, uint8_t* scales, float* g, hipStream_t stream);
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv, int64_t cv,
+                             bool per_row, float* y, hipStream_t stream);
+
+}  // namespace nvfp4

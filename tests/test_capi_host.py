@@ -1,0 +1,102 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/nvfp4.h declares, and every
+invalid call is rejected on the host with the documented status before anything is enqueued.  The pointers below
+are aligned placeholders that validation never dereferences (a valid call would launch kernels, so none is
+made here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from nvfp4_quantization_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+OK, NULL, SHAPE, ALIGN, UNSUP = 0, 1, 2, 3, 4
+P = 0x10000          # 16-byte aligned placeholder
+MIS = 0x10008        # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("HIP library not built")
+    return B.lib()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(["nvfp4_amax", "nvfp4_quantize_rn", "nvfp4_quantize_sr",
+                                           "nvfp4_quantize_rht_sr", "nvfp4_quantize_4o6", "nvfp4_dequantize",
+                                           "nvfp4_status_str"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(B.SIGNATURES) == set(declared_functions())
+
+
+def test_status_strings(lib):
+    for code, name in B.STATUS.items():
+        assert lib.nvfp4_status_str(code).decode().startswith(name)
+
+
+def out(codes=P, scales=P, g=P):
+    return C.byref(B._Out(codes, scales, g))
+
+
+def test_amax_validation(lib):
+    f = lib.nvfp4_amax
+    assert f(None, 16, 16, 1, 0, 0, 0, P, None) == NULL
+    assert f(P, 16, 16, 1, 0, 0, 0, None, None) == NULL
+    assert f(P, -1, 16, 1, 0, 0, 0, P, None) == SHAPE
+    assert f(P, 16, 24, 1, 0, 0, 0, P, None) == SHAPE          # row-wise: cols % 16
+    assert f(P, 24, 16, 2, 0, 0, 0, P, None) == SHAPE          # column-wise: rows % 16
+    assert f(P, 32, 12, 2, 0, 0, 0, P, None) == SHAPE          # column-wise: cols % 8
+    assert f(MIS, 16, 16, 1, 0, 0, 0, P, None) == ALIGN
+    assert f(P, 16, 16, 1, 0, 0, 0, P + 2, None) == ALIGN
+    assert f(P, 16, 16, 3, 0, 0, 0, P, None) == UNSUP         # BOTH is not an amax view
+    assert f(P, 16, 16, 1, 7, 0, 0, P, None) == UNSUP
+    assert f(P, 1 << 20, 1 << 20, 1, 0, 0, 0, P, None) == SHAPE  # 2^40 elements
+
+
+def test_quantize_rn_validation(lib):
+    f = lib.nvfp4_quantize_rn
+    assert f(P, 16, 16, 0, 3, 0, P, out(), out(), None) == UNSUP      # 1x16 BOTH
+    assert f(P, 16, 16, 1, 1, 1, P, out(), None, None) == UNSUP       # 16x16 per-row g
+    assert f(P, 16, 24, 1, 1, 0, P, out(), None, None) == SHAPE       # 16x16 cols % 16
+    assert f(P, 24, 16, 1, 2, 0, P, None, out(), None) == SHAPE       # 16x16 rows % 16
+    assert f(P, 16, 16, 1, 3, 0, P, out(), None, None) == NULL        # BOTH needs both outputs
+    assert f(P, 16, 16, 0, 1, 0, P, None, out(), None) == NULL        # row-wise needs row_out
+    assert f(P, 16, 16, 0, 1, 0, P, out(g=None), None, None) == NULL
+    assert f(P, 16, 16, 0, 1, 0, P, out(codes=MIS), None, None) == ALIGN
+    assert f(P, 16, 16, 0, 1, 0, P, out(g=P + 1), None, None) == ALIGN
+    assert f(P, 16, 16, 5, 1, 0, P, out(), None, None) == UNSUP       # unknown block
+    assert f(P, 16, 16, 1, 4, 0, P, out(), out(), None) == UNSUP      # unknown orientation
+
+
+def test_quantize_sr_and_rht_sr_validation(lib):
+    for f, extra in ((lib.nvfp4_quantize_sr, ()), (lib.nvfp4_quantize_rht_sr, (0x1234,))):
+        assert f(P, 16, 16, 3, 0, P, *extra, 1, 2, out(), None) == UNSUP   # BOTH
+        assert f(P, 16, 24, 1, 0, P, *extra, 1, 2, out(), None) == SHAPE
+        assert f(P, 16, 16, 1, 0, None, *extra, 1, 2, out(), None) == NULL
+        assert f(P, 16, 16, 1, 0, P, *extra, 1, 2, None, None) == NULL
+        assert f(P, 16, 16, 1, 2, P, *extra, 1, 2, out(), None) == UNSUP
+
+
+def test_4o6_and_dequantize_validation(lib):
+    assert lib.nvfp4_quantize_4o6(P, 16, 24, 1, P, out(), None) == SHAPE
+    assert lib.nvfp4_quantize_4o6(P, 16, 16, 9, P, out(), None) == UNSUP
+    assert lib.nvfp4_quantize_4o6(P, 16, 16, 1, P, out(scales=None), None) == NULL
+    d = lib.nvfp4_dequantize
+    assert d(P, P, P, 4, 24, 0, P, None) == SHAPE
+    assert d(P, P, P, 4, 32, 0, P + 4, None) == ALIGN          # y must be 16-byte aligned
+    assert d(None, P, P, 4, 32, 0, P, None) == NULL
+    assert d(P, P, P, -4, 32, 0, P, None) == SHAPE

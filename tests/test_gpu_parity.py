@@ -1,0 +1,301 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle, element by element, on the same seeded inputs.
+
+Bar: codes and E4M3 scales bit-exact; amax and g bit-exact with NaN equal to NaN; decoded values bit-exact.
+Small shapes span several workgroup tiles and ragged tails; the five full-size workloads run in the same launch
+configuration the benchmark times and are compared in full (or on sampled rows where noted).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import nvfp4_quantization_amd as Q
+from nvfp4_quantization_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    Q.binding.lib()          # fails loudly if the HIP library is missing
+    O.lib()
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x_bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(x_bits.view(np.int16)).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def same_f32(a, b):
+    a = np.asarray(a, np.float32).ravel()
+    b = np.asarray(b, np.float32).ravel()
+    assert a.shape == b.shape
+    both_nan = np.isnan(a) & np.isnan(b)
+    eq = (a.view(np.uint32) == b.view(np.uint32)) | both_nan
+    bad = np.flatnonzero(~eq)
+    assert bad.size == 0, f"{bad.size} float mismatches, first at {bad[:5]}: {a[bad[:5]]} vs {b[bad[:5]]}"
+
+
+def same_u8(a, b, what):
+    a = np.asarray(a)
+    b = np.asarray(b)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    bad = np.argwhere(a != b)
+    assert bad.size == 0, f"{what}: {len(bad)} byte mismatches, first at {bad[:5].tolist()}"
+
+
+MODES = {"rn": O.MODE_RN, "sr": O.MODE_SR, "rht_sr": O.MODE_RHT_SR}
+
+
+def gpu_1x16(x, mode, orient, gmode, mask, seed, offset):
+    xd = dev(x)
+    a = Q.nvfp4_amax(xd, orient, gmode, use_rht=(mode == "rht_sr"), sign_mask=mask)
+    if mode == "rn":
+        r, c = Q.nvfp4_quantize_rn(xd, a, Q.BLOCK_1X16, orient, gmode)
+        out = r if orient == Q.ROWWISE else c
+    elif mode == "sr":
+        out = Q.nvfp4_quantize_sr(xd, a, seed, offset, orient, gmode)
+    else:
+        out = Q.nvfp4_quantize_rht_sr(xd, a, mask, seed, offset, orient, gmode)
+    return host(a), host(out.codes), host(out.scales), host(out.g)
+
+
+def check_1x16(x, mode, orient, gmode, mask=0xA53C, seed=0x1234_5678_9ABC, offset=7, vrows=None):
+    say("1x16", mode, "row" if orient == 1 else "col", "per-row" if gmode else "per-tensor", x.shape)
+    a, codes, scales, g = gpu_1x16(x, mode, orient, gmode, mask, seed, offset)
+    oa = O.amax(x, orient, gmode, mode == "rht_sr", mask)
+    same_f32(a, oa)
+    oc, os_, og = O.quantize_1x16(x, oa, MODES[mode], orient, gmode, mask, seed, offset, vrows=vrows)
+    if vrows is not None:
+        lo, hi = vrows
+        codes, scales, oc, os_ = codes[lo:hi], scales[lo:hi], oc[lo:hi], os_[lo:hi]
+        if gmode:
+            g, og = g[lo:hi], og[lo:hi]
+    same_u8(codes, oc, "codes")
+    same_u8(scales, os_, "scales")
+    same_f32(g, og)
+    return codes, scales, g
+
+
+SHAPES_ROW = [(256, 1024), (37, 160), (1, 16), (300, 48), (129, 4096)]
+SHAPES_COL = [(512, 200), (48, 8), (1040, 72), (16, 520), (2048, 1024)]
+
+
+@pytest.mark.parametrize("mode", ["rn", "sr", "rht_sr"])
+@pytest.mark.parametrize("gmode", [0, 1])
+@pytest.mark.parametrize("shape", SHAPES_ROW)
+def test_rowwise_1x16(mode, gmode, shape):
+    x = W.lognormal_gradients(*shape, seed=shape[0] * 131 + shape[1] + {"rn": 0, "sr": 1, "rht_sr": 2}[mode])
+    check_1x16(x, mode, Q.ROWWISE, gmode)
+
+
+@pytest.mark.parametrize("mode", ["rn", "sr", "rht_sr"])
+@pytest.mark.parametrize("gmode", [0, 1])
+@pytest.mark.parametrize("shape", SHAPES_COL)
+def test_colwise_1x16(mode, gmode, shape):
+    x = W.outlier_columns(*shape, seed=(shape[0] * 7 + shape[1]) & 0xFFFF, n_cols=min(4, shape[1]))
+    check_1x16(x, mode, Q.COLWISE, gmode)
+
+
+def test_small_config_rht_sr_and_rn():
+    """256x1024, N(0,1) with 4 outlier columns x50: RHT+SR (fresh mask) and the RN pass on the same input."""
+    x = W.make("rht_sr_small_256x1024")
+    mask = W.sign_mask(0, 0)
+    check_1x16(x, "rht_sr", Q.ROWWISE, 0, mask=mask, seed=0, offset=0)
+    check_1x16(x, "rn", Q.ROWWISE, 0)
+
+
+def test_edge_values_all_modes():
+    """Zeros, subnormals, exact E2M1 midpoints, powers of two, NaN and +-inf in separate rows."""
+    rng = np.random.default_rng(5)
+    rows = []
+    rows.append(np.zeros(64))
+    rows.append(rng.standard_normal(64) * 1e-39)                       # bf16 subnormals
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * 8)
+    rows.append(mids * np.where(np.arange(64) % 2, 1, -1))
+    rows.append(2.0 ** rng.integers(-30, 30, size=64))
+    r = rng.standard_normal(64)
+    r[5] = np.nan
+    rows.append(r)
+    r = rng.standard_normal(64)
+    r[40] = np.inf
+    rows.append(r)
+    r = rng.standard_normal(64)
+    r[3] = -np.inf
+    r[60] = np.inf
+    rows.append(r)
+    rows.append(-np.zeros(64))
+    x = W.to_bits(torch.tensor(np.array(rows, dtype=np.float32)))
+    x = np.concatenate([x, x[::-1]], axis=0)                            # 16 rows for the column-wise view
+    for mode in ("rn", "sr", "rht_sr"):
+        for orient in (Q.ROWWISE, Q.COLWISE):
+            check_1x16(x, mode, orient, 1)
+        check_1x16(x, mode, Q.ROWWISE, 0)
+
+
+def test_degenerate_amax_inputs():
+    """Caller-supplied amax values that are not the tensor's own: 0 (g = 0), negative, inf and NaN, with inf
+    elements present.  The element multiplier is then 0, negative or NaN and every element takes the general
+    path of the definition."""
+    x = W.gaussian(16, 64, seed=3)
+    xf = x.copy()
+    xf[2, 5] = 0x7F80   # +inf
+    xf[7, 9] = 0xFF80   # -inf
+    xd = dev(xf)
+    for amax_val in (0.0, -3.0, float("inf"), float("nan"), 1e-40, 3e38):
+        say("degenerate amax", amax_val)
+        a = torch.full((1,), amax_val, dtype=torch.float32, device="cuda")
+        for mode in ("rn", "sr"):
+            if mode == "rn":
+                out, _ = Q.nvfp4_quantize_rn(xd, a, Q.BLOCK_1X16, Q.ROWWISE, 0)
+            else:
+                out = Q.nvfp4_quantize_sr(xd, a, 5, 6, Q.ROWWISE, 0)
+            oc, os_, og = O.quantize_1x16(xf, np.array([amax_val], np.float32), MODES[mode], seed=5, offset=6)
+            same_u8(host(out.codes), oc, "codes")
+            same_u8(host(out.scales), os_, "scales")
+            same_f32(host(out.g), og)
+
+
+def test_empty_tensors():
+    for shape, orient in (((0, 64), Q.ROWWISE), ((0, 64), Q.COLWISE), ((32, 0), Q.ROWWISE)):
+        say("empty", shape, orient)
+        xd = torch.zeros(shape, dtype=torch.int16, device="cuda")
+        a = Q.nvfp4_amax(xd, orient, 0)
+        assert host(a)[0] == 0.0
+        out = Q.nvfp4_quantize_sr(xd, a, 1, 2, orient, 0)
+        assert host(out.g)[0] == 0.0
+
+
+def test_determinism_and_fresh_randomness():
+    x = W.lognormal_gradients(512, 256, seed=9)
+    xd = dev(x)
+    a = Q.nvfp4_amax(xd, Q.COLWISE, 0, True, 0x0F0F)
+    o1 = Q.nvfp4_quantize_rht_sr(xd, a, 0x0F0F, 11, 3, Q.COLWISE)
+    o2 = Q.nvfp4_quantize_rht_sr(xd, a, 0x0F0F, 11, 3, Q.COLWISE)
+    o3 = Q.nvfp4_quantize_rht_sr(xd, a, 0x0F0F, 11, 4, Q.COLWISE)
+    assert torch.equal(o1.codes, o2.codes) and torch.equal(o1.scales, o2.scales)
+    assert not torch.equal(o1.codes, o3.codes)          # a new offset draws new bits
+    assert torch.equal(o1.scales, o3.scales)            # scales do not depend on the random bits
+
+
+# ---------------------------------------------------------------------------------------------------- 16x16
+def check_16x16(x, orient, tile_rows=None):
+    say("16x16", orient, x.shape)
+    xd = dev(x)
+    a = Q.nvfp4_amax(xd, Q.ROWWISE, 0)
+    r, c = Q.nvfp4_quantize_rn(xd, a, Q.BLOCK_16X16, orient, 0)
+    oa = O.amax(x)
+    same_f32(host(a), oa)
+    (ow, osw, ogw), (ot, ost, ogt) = O.quantize_16x16(x, oa, tile_rows=tile_rows)
+    sl = slice(None) if tile_rows is None else slice(16 * tile_rows[0], 16 * tile_rows[1])
+    if r is not None:
+        same_u8(host(r.codes)[sl], ow[sl], "W codes")
+        same_u8(host(r.scales)[sl], osw[sl], "W scales")
+        same_f32(host(r.g), ogw)
+    if c is not None:
+        tcs = slice(None) if tile_rows is None else slice(8 * tile_rows[0], 8 * tile_rows[1])
+        tss = slice(None) if tile_rows is None else slice(tile_rows[0], tile_rows[1])
+        same_u8(host(c.codes)[:, tcs], ot[:, tcs], "W^T codes")
+        same_u8(host(c.scales)[:, tss], ost[:, tss], "W^T scales")
+        same_f32(host(c.g), ogt)
+
+
+@pytest.mark.parametrize("shape", [(64, 96), (272, 528), (16, 16), (1024, 2080)])
+@pytest.mark.parametrize("orient", [Q.ROWWISE, Q.COLWISE, Q.BOTH])
+def test_16x16(shape, orient):
+    check_16x16(W.weight_outliers(*shape, seed=shape[0] + shape[1]), orient)
+
+
+# ----------------------------------------------------------------------------------------------- four-over-six
+def check_4o6(x, gmode, rows_range=None):
+    say("4o6", gmode, x.shape)
+    xd = dev(x)
+    a = Q.nvfp4_amax(xd, Q.ROWWISE, gmode)
+    out = Q.nvfp4_quantize_4o6(xd, a, gmode)
+    if rows_range is None:
+        oa = O.amax(x, O.ROWWISE, gmode)
+        same_f32(host(a), oa)
+        oc, os_, og, _ = O.quantize_4o6(x, oa, gmode)
+        same_u8(host(out.codes), oc, "codes")
+        same_u8(host(out.scales), os_, "scales")
+        same_f32(host(out.g), og)
+    else:
+        lo, hi = rows_range
+        sub = np.ascontiguousarray(x[lo:hi])
+        oa = O.amax(sub, O.ROWWISE, 1)
+        same_f32(host(a)[lo:hi], oa)
+        oc, os_, og, _ = O.quantize_4o6(sub, oa, 1)
+        same_u8(host(out.codes)[lo:hi], oc, "codes")
+        same_u8(host(out.scales)[lo:hi], os_, "scales")
+        same_f32(host(out.g)[lo:hi], og)
+    return out
+
+
+@pytest.mark.parametrize("gmode", [0, 1])
+@pytest.mark.parametrize("shape", [(64, 256), (33, 48), (512, 1024)])
+def test_4o6(gmode, shape):
+    check_4o6(W.heavy_tail_rows(*shape, seed=shape[0], frac_special=0.0), gmode)
+
+
+def test_4o6_with_nan_inf():
+    check_4o6(W.heavy_tail_rows(256, 512, seed=4, frac_special=5e-4), 1)
+
+
+# ------------------------------------------------------------------------------------------------ dequantize
+@pytest.mark.parametrize("gmode", [0, 1])
+def test_dequantize(gmode):
+    x = W.heavy_tail_rows(128, 256, seed=2, frac_special=2e-4)
+    xd = dev(x)
+    a = Q.nvfp4_amax(xd, Q.ROWWISE, gmode)
+    out = Q.nvfp4_quantize_4o6(xd, a, gmode)
+    y = Q.nvfp4_dequantize(out.codes, out.scales, out.g, gmode)
+    same_f32(host(y), O.dequantize(host(out.codes), host(out.scales), host(out.g), gmode))
+    # arbitrary bytes too (every scale code, including the sign bit and NaN patterns)
+    codes = torch.randint(0, 256, (64, 32), dtype=torch.uint8, device="cuda")
+    scales = torch.arange(256, dtype=torch.uint8, device="cuda").reshape(64, 4)
+    g = torch.rand((64 if gmode else 1,), device="cuda")
+    y = Q.nvfp4_dequantize(codes, scales, g, gmode)
+    same_f32(host(y), O.dequantize(host(codes), host(scales), host(g), gmode))
+
+
+# ----------------------------------------------------------------------------------- full-size workloads
+@pytest.mark.slow
+def test_full_fprop_rn_8192x4096():
+    check_1x16(W.make("fprop_rn_8192x4096"), "rn", Q.ROWWISE, 0)
+
+
+@pytest.mark.slow
+def test_full_wgrad_colwise_rht_sr_8192x4096():
+    """The benchmarked workload: column-wise (blocks along the 8192 dimension), RHT with fresh signs, Philox SR;
+    call k uses the mask drawn for k and Philox offset k."""
+    x = W.make("wgrad_colwise_rht_sr_8192x4096")
+    for call in (0, 1):
+        check_1x16(x, "rht_sr", Q.COLWISE, 0, mask=W.sign_mask(2, call), seed=2, offset=call)
+    check_1x16(x, "rht_sr", Q.ROWWISE, 0, mask=W.sign_mask(2, 0), seed=2, offset=0)
+
+
+@pytest.mark.slow
+def test_full_weight_16x16_14336x4096():
+    x = W.make("weight_16x16_14336x4096")
+    check_16x16(x, Q.BOTH)
+
+
+@pytest.mark.slow
+def test_full_four_over_six_16384x8192():
+    """Per-row g; compared on 1024 rows spread over the tensor (the GPU ran the full tensor)."""
+    x = W.make("four_over_six_16384x8192")
+    for lo in (0, 5000, 16384 - 512):
+        check_4o6(x, 1, rows_range=(lo, lo + 512))
