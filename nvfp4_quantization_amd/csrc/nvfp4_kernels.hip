@@ -8,16 +8,20 @@
 //   Philox4x32-10: Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11.
 //
 // Design (MI355X-first):
-//   * The op is O(|X|) and HBM-bound ([P1, random Hadamard transform]: not a real GEMM).  A 16-point transform is
+//   * The op is O(|X|) and memory-bound ([P1, random Hadamard transform]: not a real GEMM).  A 16-point transform is
 //     far too narrow for MFMA, so the Hadamard product is an in-register butterfly; nothing is staged in LDS.
 //   * Every lane owns whole 16-element blocks, so block maxima, scales, Philox and packing need no cross-lane
-//     traffic.  Row-wise: a lane loads one block (two 16-byte loads).  Column-wise (blocks run down columns of X):
-//     a lane loads 16 rows x 8 columns with 16 coalesced 16-byte loads and transposes in registers, which yields 8
-//     complete column blocks; the 4 waves of a workgroup are stacked along rows so each output row of X^T receives
-//     a contiguous multi-line run from one CU.
-//   * Bit-exact rounding: every step is one IEEE binary32 operation (built with -ffp-contract=off, no fast-math,
-//     denormals kept); the divisions are HIP's correctly rounded ones.  E2M1/E4M3 encodes are integer
-//     manipulations of the binary32 pattern that reproduce round-to-nearest-even / the SR rule exactly.
+//     traffic.  Column-wise (blocks run down columns of X): a lane loads 16 rows x 8 columns with 16 loads of 16
+//     bytes (a wave reads 1 KiB contiguous per row) and transposes in registers into 8 complete column blocks.
+//   * Persistent waves: each wave walks a contiguous run of tiles with the next tile's loads in flight while the
+//     current one is computed (double-buffered registers), so HBM streaming overlaps the VALU work.
+//   * E2M1 rounding uses the gfx950 FP4 conversions with a unit scale: v_cvt_scalef32_pk_fp4_f32 rounds to nearest
+//     even and saturates at +-6; v_cvt_scalef32_sr_pk_fp4_f32 rounds the first element of its pair up exactly when
+//     the element's fraction (in grid steps) plus the seed's top bits carries, so the seed (255 - rho) << 24 makes it
+//     round up iff rho < floor(256 * frac) -- the stochastic-rounding rule [P1, stochastic rounding] with one random
+//     byte per element.  Both agree with the definition on every non-NaN binary32 input; NaN is patched to 0x7.
+//   * Bit-exact arithmetic: every step is one IEEE binary32 operation (built with -ffp-contract=off, no fast-math,
+//     denormals kept); divisions are HIP's correctly rounded ones.
 //   * No host synchronisation: the global scale is computed on the device from the amax buffer ([P2, results]).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -28,15 +32,24 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWavesPerGroup = kThreads / 64;
 constexpr float kFltMax = 3.402823466e38f;
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
 __device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
+// NaN-propagating maximum of magnitudes (v_maximum3_f32 with |.| modifiers).  On non-NaN inputs it equals the
+// integer maximum of the magnitude bit patterns; any NaN input gives NaN.
+__device__ __forceinline__ float absmax3(float m, float a, float b) {
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, __builtin_fabsf(a)), __builtin_fabsf(b));
+}
+
 // ------------------------------------------------------------------------------------------------------------
-// Philox4x32-10 (Salmon et al., SC'11).  Multipliers and Weyl increments are the published constants.  The key
-// is uniform across the launch, so its schedule lives in scalar registers.
+// Philox4x32-10 (Salmon et al., SC'11): published multipliers and Weyl increments; the key schedule is uniform
+// and lives in scalar registers; each output word's three-way xor is one v_bitop3.
 // ------------------------------------------------------------------------------------------------------------
 constexpr uint32_t kPhiloxMulA = 0xD2511F53u;  // multiplies counter word 0
 constexpr uint32_t kPhiloxMulB = 0xCD9E8D57u;  // multiplies counter word 2
@@ -47,14 +60,18 @@ struct Rand4 {
     uint32_t w[4];
 };
 
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 __device__ __forceinline__ Rand4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
                                                uint32_t k1) {
 #pragma unroll
     for (int round = 0; round < 10; ++round) {
         const uint64_t pa = (uint64_t)kPhiloxMulA * c0;
         const uint64_t pb = (uint64_t)kPhiloxMulB * c2;
-        const uint32_t n0 = (uint32_t)(pb >> 32) ^ c1 ^ k0;
-        const uint32_t n2 = (uint32_t)(pa >> 32) ^ c3 ^ k1;
+        const uint32_t n0 = xor3((uint32_t)(pb >> 32), c1, k0);
+        const uint32_t n2 = xor3((uint32_t)(pa >> 32), c3, k1);
         c1 = (uint32_t)pb;
         c3 = (uint32_t)pa;
         c0 = n0;
@@ -65,14 +82,38 @@ __device__ __forceinline__ Rand4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
     return Rand4{{c0, c1, c2, c3}};
 }
 
+// The same generator returning the bitwise complement of the four output words (folded into the last round's
+// three-way xors where possible).
+__device__ __forceinline__ Rand4 philox4x32_10_inv(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                                   uint32_t k1) {
+#pragma unroll
+    for (int round = 0; round < 9; ++round) {
+        const uint64_t pa = (uint64_t)kPhiloxMulA * c0;
+        const uint64_t pb = (uint64_t)kPhiloxMulB * c2;
+        const uint32_t n0 = xor3((uint32_t)(pb >> 32), c1, k0);
+        const uint32_t n2 = xor3((uint32_t)(pa >> 32), c3, k1);
+        c1 = (uint32_t)pb;
+        c3 = (uint32_t)pa;
+        c0 = n0;
+        c2 = n2;
+        k0 += kPhiloxWeylA;
+        k1 += kPhiloxWeylB;
+    }
+    const uint64_t pa = (uint64_t)kPhiloxMulA * c0;
+    const uint64_t pb = (uint64_t)kPhiloxMulB * c2;
+    return Rand4{{(uint32_t)__builtin_amdgcn_bitop3_b32((uint32_t)(pb >> 32), c1, k0, 0x69), ~(uint32_t)pb,
+                  (uint32_t)__builtin_amdgcn_bitop3_b32((uint32_t)(pa >> 32), c3, k1, 0x69), ~(uint32_t)pa}};
+}
+
 // Random bytes of the 1x16 block with row-major index n in the quantized view ([P1, vibe-coding and timeline
 // sections]: the counter layout is part of the semantics): key = seed, counter = (n, offset) as 32-bit words.
 struct RngArgs {
     uint32_t k0, k1, o0, o1;
 };
 
-__device__ __forceinline__ Rand4 block_rand(const RngArgs& a, uint64_t n) {
-    return philox4x32_10((uint32_t)n, (uint32_t)(n >> 32), a.o0, a.o1, a.k0, a.k1);
+// Complemented random words of the block (bytes 255 - rho).
+__device__ __forceinline__ Rand4 block_rand_inv(const RngArgs& a, uint64_t n) {
+    return philox4x32_10_inv((uint32_t)n, (uint32_t)(n >> 32), a.o0, a.o1, a.k0, a.k1);
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -80,126 +121,160 @@ __device__ __forceinline__ Rand4 block_rand(const RngArgs& a, uint64_t n) {
 // saturate above 448 (the "satfinite" convention of the conversions in [P1]), NaN -> 0x7F, s <= 0 -> 0.
 // ------------------------------------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t e4m3_encode(float s) {
-    if (s != s) return 0x7Fu;
-    if (!(s > 0.0f)) return 0u;
-    if (s > 448.0f) return 0x7Eu;
+    // branch-free: every candidate is computed and the special cases override it
     const uint32_t b = as_u(s);
-    if (b >= 0x3C800000u) {                             // s >= 2^-6: normal; round 23 mantissa bits to 3 (RNE)
-        const uint32_t u = b + 0x7FFFFu + ((b >> 20) & 1u);
-        return (u >> 20) - 960u;                        // ((e - 127 + 7) << 3) | m
-    }
-    return (uint32_t)__builtin_rintf(s * 512.0f);      // subnormal range: a multiple of 2^-9 (8 = min normal)
+    const uint32_t normal = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - 960u;  // s >= 2^-6: ((e - 120) << 3) | m, RNE
+    const uint32_t sub = (uint32_t)__builtin_rintf(s * 512.0f);                 // s < 2^-6: multiples of 2^-9
+    uint32_t c = (b >= 0x3C800000u) ? normal : sub;
+    c = (s > 448.0f) ? 0x7Eu : c;
+    c = (s > 0.0f) ? c : 0u;
+    return (s != s) ? 0x7Fu : c;
 }
 
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {  // c in [0, 0x7F]
-    if (c == 0x7Fu) return __builtin_nanf("");
     const uint32_t e = c >> 3, m = c & 7u;
-    if (e == 0) return (float)m * 0.001953125f;         // m * 2^-9, exact
-    return as_f(((e + 120u) << 23) | (m << 20));
+    const float v = (e == 0) ? (float)m * 0.001953125f : as_f(((e + 120u) << 23) | (m << 20));  // m * 2^-9 exact
+    return (c == 0x7Fu) ? __builtin_nanf("") : v;
 }
 
-// Block scale and element multiplier: s = bamax / d (d = fl(T g)), sb = E4M3(s), S = fl(decode(sb) g),
-// r = fl(1 / S) with r = 0 for S = 0, NaN for NaN S, FLT_MAX when the reciprocal overflows.
-struct BlockScale {
-    uint32_t sb;
-    float r;
+// Element multiplier of block scale code sb: S = fl(decode(sb) g), r = fl(1 / S), with r = 0 for S = 0, NaN for a
+// NaN S and FLT_MAX when the reciprocal overflows.
+__device__ __forceinline__ float scale_multiplier(uint32_t sb, float g) {
+    const float S = e4m3_decode(sb) * g;
+    float r = 1.0f / S;
+    r = __builtin_isinf(r) ? kFltMax : r;
+    r = (S == 0.0f) ? 0.0f : r;
+    return (S != S) ? S : r;
+}
+
+// Block scale code: s = bamax / d (d = fl(T g), correctly rounded division), sb = E4M3(s); s = 0 for bamax = 0.
+__device__ __forceinline__ uint32_t scale_code(float bamax, float d) {
+    const float s = bamax / d;
+    return e4m3_encode(bamax == 0.0f ? 0.0f : s);
+}
+
+// Per-tensor g: the 128 possible multipliers are tabulated once per workgroup in LDS.
+struct RTable {
+    float r[128];
 };
 
-__device__ __forceinline__ BlockScale block_scale(float bamax, float d, float g) {
-    const float s = (bamax == 0.0f) ? 0.0f : bamax / d;
-    const uint32_t sb = e4m3_encode(s);
-    const float S = e4m3_decode(sb) * g;
-    float r;
-    if (S != S) {
-        r = S;
-    } else if (S == 0.0f) {
-        r = 0.0f;
+__device__ __forceinline__ void fill_rtable(RTable& t, float g) {
+    if (threadIdx.x < 128) t.r[threadIdx.x] = scale_multiplier(threadIdx.x, g);
+    __syncthreads();
+}
+
+// ------------------------------------------------------------------------------------------------------------
+// E2M1 encoding with the gfx950 conversions (unit scale).  Element 2k goes to the low nibble of byte k.
+// ------------------------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t pack8_rn(const float (&q)[8]) {
+    uint32_t d = 0;
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, q[0], q[1], 1.0f, 0);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, q[2], q[3], 1.0f, 1);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, q[4], q[5], 1.0f, 2);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, q[6], q[7], 1.0f, 3);
+    return d;
+}
+
+// Stochastic rounding, one conversion per element on the natural pair (q[2k], q[2k+1]): the first slot draws its
+// random byte from seed bits 31..24, the second slot from bits 30..23 (the instruction shifts the seed left by one
+// for it).  Element 2k uses seed (255 - rho) << 24 and keeps the low nibble; element 2k+1 uses (255 - rho) << 23
+// and keeps the high nibble; the other nibble of each conversion is discarded by the final bit-select.
+__device__ __forceinline__ uint32_t seed_first(uint32_t inv_word, int byte) {   // byte 0 or 2
+    return (inv_word << (24 - 8 * byte)) & 0xFF000000u;
+}
+__device__ __forceinline__ uint32_t seed_second(uint32_t inv_word, int byte) {  // byte 1 or 3
+    return ((inv_word >> (8 * byte)) & 0xFFu) << 23;
+}
+
+// The byte-select chain needs the accumulator tied to the destination (each conversion writes one byte and keeps
+// the other three); the compiler's lowering of the SR conversion builtin does not carry that operand, so the
+// instruction is written out with a tied operand here.
+#define NVFP4_SR_PAIR(acc, k, seed, OPSEL)                                                \
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 " OPSEL                             \
+        : "+v"(acc)                                                                       \
+        : "v"(f32x2{q[2 * (k)], q[2 * (k) + 1]}), "v"(seed))
+
+__device__ __forceinline__ uint32_t pack8_sr(const float (&q)[8], uint32_t inv_lo, uint32_t inv_hi) {
+    // inv_lo holds the complemented random bytes of elements 0..3, inv_hi of elements 4..7
+    uint32_t e = 0, o = 0;
+    NVFP4_SR_PAIR(e, 0, seed_first(inv_lo, 0), "");
+    NVFP4_SR_PAIR(o, 0, seed_second(inv_lo, 1), "");
+    NVFP4_SR_PAIR(e, 1, seed_first(inv_lo, 2), "op_sel:[0,0,1,0]");
+    NVFP4_SR_PAIR(o, 1, seed_second(inv_lo, 3), "op_sel:[0,0,1,0]");
+    NVFP4_SR_PAIR(e, 2, seed_first(inv_hi, 0), "op_sel:[0,0,0,1]");
+    NVFP4_SR_PAIR(o, 2, seed_second(inv_hi, 1), "op_sel:[0,0,0,1]");
+    NVFP4_SR_PAIR(e, 3, seed_first(inv_hi, 2), "op_sel:[0,0,1,1]");
+    NVFP4_SR_PAIR(o, 3, seed_second(inv_hi, 3), "op_sel:[0,0,1,1]");
+    return (e & 0x0F0F0F0Fu) | (o & 0xF0F0F0F0u);
+}
+#undef NVFP4_SR_PAIR
+
+// NaN elements encode to 0x7 (the hardware keeps the NaN's sign).
+__device__ __forceinline__ uint32_t patch_nan8(uint32_t d, const float (&q)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (q[i] != q[i]) d = (d & ~(0xFu << (4 * i))) | (0x7u << (4 * i));
+    return d;
+}
+
+template <bool SR>
+__device__ __forceinline__ void encode16(const float (&q)[16], const Rand4& inv, uint32_t& lo, uint32_t& hi) {
+    const float(&q0)[8] = *reinterpret_cast<const float(*)[8]>(&q[0]);
+    const float(&q1)[8] = *reinterpret_cast<const float(*)[8]>(&q[8]);
+    if (SR) {
+        lo = pack8_sr(q0, inv.w[0], inv.w[1]);
+        hi = pack8_sr(q1, inv.w[2], inv.w[3]);
     } else {
-        r = 1.0f / S;
-        if (__builtin_isinf(r)) r = kFltMax;
+        lo = pack8_rn(q0);
+        hi = pack8_rn(q1);
     }
-    return BlockScale{sb, r};
+}
+
+// Quantize one 16-element block.  w[] are the values before the final 0.25 of the transform when RHT is set
+// (y = fl(0.25 w)), the values themselves otherwise.  r_of(sb) gives the element multiplier of scale code sb.
+// Fast path (no NaN possible): the block's multiplier r is finite and positive; with the RHT additionally
+// 2^-124 <= r < 2^117, where fl(fl(0.25 w) r) and fl(w fl(0.25 r)) give the same code for every w (they are equal
+// when 0.25 w is exact, and both are below 2^-9 -- code 0 with the sign of w -- when it is not).
+template <bool SR, bool RHT, typename ROf>
+__device__ __forceinline__ bool quantize_block_fast(const float (&w)[16], float d6, ROf r_of, const Rand4& inv,
+                                                    uint32_t& lo, uint32_t& hi, uint32_t& sb, float& r) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) m = absmax3(m, w[i], w[i + 1]);
+    const float bamax = RHT ? 0.25f * m : m;       // max_i fl(0.25 |w_i|) = fl(0.25 max_i |w_i|)
+    sb = scale_code(bamax, d6);
+    r = r_of(sb);
+    const float rq = RHT ? 0.25f * r : r;
+    float q[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) q[i] = w[i] * rq;
+    encode16<SR>(q, inv, lo, hi);
+    return RHT ? (r >= 0x1p-124f && r < 0x1p117f) : (r > 0.0f && r <= kFltMax);
+}
+
+// The definition step by step for blocks outside the fast path: y = fl(0.25 w) (RHT), q = fl(y r); NaN -> 0x7.
+template <bool SR, bool RHT>
+__device__ __forceinline__ void quantize_block_general(const float (&w)[16], float r, const Rand4& inv, uint32_t& lo,
+                                                       uint32_t& hi) {
+    float q[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) q[i] = (RHT ? 0.25f * w[i] : w[i]) * r;
+    encode16<SR>(q, inv, lo, hi);
+    lo = patch_nan8(lo, *reinterpret_cast<const float(*)[8]>(&q[0]));
+    hi = patch_nan8(hi, *reinterpret_cast<const float(*)[8]>(&q[8]));
+}
+
+template <bool SR, bool RHT, typename ROf>
+__device__ __forceinline__ void quantize_block(const float (&w)[16], float d6, ROf r_of, const Rand4& inv, uint32_t& lo,
+                                               uint32_t& hi, uint32_t& sb) {
+    float r;
+    if (!quantize_block_fast<SR, RHT>(w, d6, r_of, inv, lo, hi, sb, r)) [[unlikely]]
+        quantize_block_general<SR, RHT>(w, r, inv, lo, hi);
 }
 
 // ------------------------------------------------------------------------------------------------------------
-// E2M1 magnitude index (0..7 for 0, 0.5, 1, 1.5, 2, 3, 4, 6; [P1, FP4 quantization techniques]) of t >= 0.
-// t is clamped to 6 first (satfinite); NaN must be handled by the caller (fminf drops it).
-//   t >= 1: d = bits(t) - bits(0.5) puts the E2M1 exponent/mantissa pair in bits 22..24 (value index 2..7);
-//           the 22 bits below are the fraction of the way to the next grid point.
-//   t <  1: the grid is uniform with step 0.5.
-// ------------------------------------------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t e2m1_rn_mag(float t) {
-    t = __builtin_fminf(t, 6.0f);
-    const uint32_t d = as_u(t) - 0x3F000000u;
-    const uint32_t hi = (d + 0x1FFFFFu + ((d >> 22) & 1u)) >> 22;   // round to nearest, ties to even
-    const uint32_t lo = (uint32_t)__builtin_rintf(t + t);           // 2t rounded to nearest even: 0, 1, 2
-    return ((int32_t)d < 0x800000) ? lo : hi;
-}
-
-// Stochastic rounding ([P1, stochastic rounding]): up iff rho < floor(256 * frac).  rinv = (255 - rho) << 14;
-// adding it to the 22 fraction bits carries into bit 22 exactly when frac's top 8 bits exceed rho.
-// For t < 1, floor(t * 2^23) has the same layout (step 0.5 = 2^22 units).
-__device__ __forceinline__ uint32_t e2m1_sr_mag(float t, uint32_t rinv) {
-    t = __builtin_fminf(t, 6.0f);
-    const uint32_t d = as_u(t) - 0x3F000000u;
-    const uint32_t lo = (uint32_t)(t * 8388608.0f);
-    return ((((int32_t)d < 0x800000) ? lo : d) + rinv) >> 22;
-}
-
-template <bool SR>
-__device__ __forceinline__ uint32_t e2m1_code_fast(float y, float r, uint32_t rinv) {
-    // valid for finite r > 0: q = y r has the sign of y and is NaN only if y is, which cannot happen here
-    // (a NaN in the block makes its scale NaN)
-    const float t = __builtin_fabsf(y) * r;
-    const uint32_t m = SR ? e2m1_sr_mag(t, rinv) : e2m1_rn_mag(t);
-    return m | ((as_u(y) >> 28) & 8u);
-}
-
-template <bool SR>
-__device__ __forceinline__ uint32_t e2m1_code_general(float y, float r, uint32_t rinv) {
-    const float q = y * r;
-    if (q != q) return 7u;
-    const float t = __builtin_fabsf(q);
-    const uint32_t m = SR ? e2m1_sr_mag(t, rinv) : e2m1_rn_mag(t);
-    return m | ((as_u(q) >> 28) & 8u);
-}
-
-__device__ __forceinline__ uint32_t rinv_of(const Rand4& rnd, int i) {
-    return ((~rnd.w[i >> 2] >> (8 * (i & 3))) & 0xFFu) << 14;
-}
-
-// Quantize 16 binary32 values: block amax (integer max of magnitude bits, NaN dominant), scale, E2M1 codes
-// packed 8 per dword with element 2k in the low nibble of byte k.
-template <bool SR>
-__device__ __forceinline__ void quantize16(const float (&y)[16], float d6, float g, const Rand4& rnd, uint32_t& lo,
-                                           uint32_t& hi, uint32_t& sb) {
-    uint32_t mx = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = umax(mx, as_u(y[i]) & 0x7FFFFFFFu);
-    const BlockScale sc = block_scale(as_f(mx), d6, g);
-    sb = sc.sb;
-    uint32_t c0 = 0, c1 = 0;
-    if (sc.r > 0.0f) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) c0 |= e2m1_code_fast<SR>(y[i], sc.r, SR ? rinv_of(rnd, i) : 0u) << (4 * i);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            c1 |= e2m1_code_fast<SR>(y[8 + i], sc.r, SR ? rinv_of(rnd, 8 + i) : 0u) << (4 * i);
-    } else {  // r is 0, negative or NaN (degenerate amax or NaN block)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) c0 |= e2m1_code_general<SR>(y[i], sc.r, SR ? rinv_of(rnd, i) : 0u) << (4 * i);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            c1 |= e2m1_code_general<SR>(y[8 + i], sc.r, SR ? rinv_of(rnd, 8 + i) : 0u) << (4 * i);
-    }
-    lo = c0;
-    hi = c1;
-}
-
-// ------------------------------------------------------------------------------------------------------------
-// 16-point Random Hadamard Transform ([P1, random Hadamard transform]): y = (1/4) H16 diag(s) v with the
-// Sylvester H16, evaluated as the butterfly with strides 1, 2, 4, 8 ((a, b) -> (a + b, a - b)), then a multiply
-// by 0.25.  The random signs are applied by the caller on the packed bf16 words (an exact sign-bit flip).
+// 16-point Walsh-Hadamard butterfly, strides 1, 2, 4, 8, (a, b) -> (a + b, a - b) in binary32; the final 0.25 is
+// applied by the caller ([P1, random Hadamard transform]; y = (1/4) H16 diag(s) v, Sylvester order).
 // ------------------------------------------------------------------------------------------------------------
 __device__ __forceinline__ void fwht16(float (&w)[16]) {
 #pragma unroll
@@ -213,20 +288,56 @@ __device__ __forceinline__ void fwht16(float (&w)[16]) {
             }
         }
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) w[i] = 0.25f * w[i];
 }
 
-// XOR patterns that flip the bf16 sign bits of elements (2k, 2k+1) held in packed word k of a row-wise block.
-__device__ __forceinline__ uint32_t sign_word(uint32_t mask, int k) {
-    return (((mask >> (2 * k)) & 1u) << 15) | (((mask >> (2 * k + 1)) & 1u) << 31);
-}
+// bf16 halves of a packed word to binary32, with the random sign applied as an exact sign-bit flip
+// (flip = 0 or 0x80000000).
+__device__ __forceinline__ float bf16_lo(uint32_t w, uint32_t flip) { return as_f((w << 16) + flip); }
+__device__ __forceinline__ float bf16_hi(uint32_t w, uint32_t flip) { return as_f((w & 0xFFFF0000u) ^ flip); }
+__device__ __forceinline__ uint32_t flip_bit(uint32_t mask, int i) { return ((mask >> i) & 1u) << 31; }
 
-// 16-byte load of 8 bf16 values (the address is 16-byte aligned by the shape rules).
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return as_f(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return as_f(w & 0xFFFF0000u); }
+// Row-wise block: 16 consecutive bf16 of a row (two 16-byte words) -> binary32 (sign-flipped when RHT).
+template <bool RHT>
+__device__ __forceinline__ void widen_row_block(const uint4& a, const uint4& b, uint32_t mask, float (&w)[16]) {
+    const uint32_t ws[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        w[2 * k] = bf16_lo(ws[k], RHT ? flip_bit(mask, 2 * k) : 0u);
+        w[2 * k + 1] = bf16_hi(ws[k], RHT ? flip_bit(mask, 2 * k + 1) : 0u);
+    }
+    if (RHT) fwht16(w);
+}
+
+// Columns 2p and 2p+1 of a lane's 16 x 8 tile (the two halves of packed word p) -> two column blocks.
+template <bool RHT>
+__device__ __forceinline__ void widen_col_pair(const uint4 (&v)[16], int p, uint32_t mask, float (&wa)[16],
+                                               float (&wb)[16]) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const uint32_t word = p == 0 ? v[k].x : p == 1 ? v[k].y : p == 2 ? v[k].z : v[k].w;
+        const uint32_t f = RHT ? flip_bit(mask, k) : 0u;
+        wa[k] = bf16_lo(word, f);
+        wb[k] = bf16_hi(word, f);
+    }
+    if (RHT) {
+        fwht16(wa);
+        fwht16(wb);
+    }
+}
+
+// Column j (0..7) of a lane's 16 x 8 tile -> the 16 values of one column block.
+template <bool RHT>
+__device__ __forceinline__ void widen_col_block(const uint4 (&v)[16], int j, uint32_t mask, float (&w)[16]) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const uint32_t word = (j >> 1) == 0 ? v[k].x : (j >> 1) == 1 ? v[k].y : (j >> 1) == 2 ? v[k].z : v[k].w;
+        const uint32_t f = RHT ? flip_bit(mask, k) : 0u;
+        w[k] = (j & 1) ? bf16_hi(word, f) : bf16_lo(word, f);
+    }
+    if (RHT) fwht16(w);
+}
 
 // n / d for 32-bit n with a precomputed multiplier (Granlund-Montgomery "round-up" method).
 struct FastDiv {
@@ -247,7 +358,8 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
 __device__ __forceinline__ float global_scale(float amax) { return amax / 2688.0f; }
 
 // ------------------------------------------------------------------------------------------------------------
-// Row-wise 1x16 quantization: one block (32 bytes of bf16) per lane per iteration, grid-stride.
+// Row-wise 1x16 quantization: one 16-element block per lane per step; lanes walk the blocks with a grid stride
+// and keep the next block's two loads in flight.
 // ------------------------------------------------------------------------------------------------------------
 template <int MODE, bool PER_ROW>
 __global__ void __launch_bounds__(kThreads)
@@ -255,190 +367,260 @@ k_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, FastDiv per_
                 uint32_t sign_mask, RngArgs rng, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
                 float* __restrict__ gout) {
     constexpr bool SR = MODE != kRN;
+    constexpr bool RHT = MODE == kRHTSR;
+    __shared__ RTable tab;
     float g = 0.0f, d6 = 0.0f;
     if (!PER_ROW) {
         g = global_scale(amax[0]);
         d6 = 6.0f * g;
         if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
+        fill_rtable(tab, g);
     }
     const uint32_t stride = gridDim.x * kThreads;
-    for (uint32_t n = blockIdx.x * kThreads + threadIdx.x; n < total_blocks; n += stride) {
+    uint32_t n = blockIdx.x * kThreads + threadIdx.x;
+    if (n >= total_blocks) return;
+    uint4 a = ld16(x + 2 * (size_t)n), b = ld16(x + 2 * (size_t)n + 1);
+    for (; n < total_blocks; n += stride) {
+        const uint32_t nn = n + stride;
+        uint4 a2 = a, b2 = b;
+        if (nn < total_blocks) {
+            a2 = ld16(x + 2 * (size_t)nn);
+            b2 = ld16(x + 2 * (size_t)nn + 1);
+        }
+        float w[16];
+        widen_row_block<RHT>(a, b, sign_mask, w);
+        Rand4 rnd{{0, 0, 0, 0}};
+        if (SR) rnd = block_rand_inv(rng, n);
+        uint32_t lo, hi, sb;
         if (PER_ROW) {
             const uint32_t row = fdiv(n, per_row);
-            g = global_scale(amax[row]);
-            d6 = 6.0f * g;
-            if (n == row * per_row.d) gout[row] = g;
+            const float gr = global_scale(amax[row]);
+            if (n == row * per_row.d) gout[row] = gr;
+            quantize_block<SR, RHT>(w, 6.0f * gr, [&](uint32_t c) { return scale_multiplier(c, gr); }, rnd, lo, hi,
+                                    sb);
+        } else {
+            quantize_block<SR, RHT>(w, d6, [&](uint32_t c) { return tab.r[c]; }, rnd, lo, hi, sb);
         }
-        uint4 a = ld16(x + 2 * (size_t)n);
-        uint4 b = ld16(x + 2 * (size_t)n + 1);
-        if (MODE == kRHTSR) {
-            a.x ^= sign_word(sign_mask, 0);
-            a.y ^= sign_word(sign_mask, 1);
-            a.z ^= sign_word(sign_mask, 2);
-            a.w ^= sign_word(sign_mask, 3);
-            b.x ^= sign_word(sign_mask, 4);
-            b.y ^= sign_word(sign_mask, 5);
-            b.z ^= sign_word(sign_mask, 6);
-            b.w ^= sign_word(sign_mask, 7);
-        }
-        float y[16] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y), bf16_lo(a.z), bf16_hi(a.z),
-                       bf16_lo(a.w), bf16_hi(a.w), bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y),
-                       bf16_lo(b.z), bf16_hi(b.z), bf16_lo(b.w), bf16_hi(b.w)};
-        if (MODE == kRHTSR) fwht16(y);
-        Rand4 rnd{{0, 0, 0, 0}};
-        if (SR) rnd = block_rand(rng, n);
-        uint32_t lo, hi, sb;
-        quantize16<SR>(y, d6, g, rnd, lo, hi, sb);
         codes[n] = make_uint2(lo, hi);
         scales[n] = (uint8_t)sb;
+        a = a2;
+        b = b2;
     }
 }
 
 // ------------------------------------------------------------------------------------------------------------
-// Column-wise 1x16 quantization (V = X^T; a block is 16 consecutive rows of one column of X).
-// Lane (rb, cg) of a wave owns row-block rb (16 rows) and column group cg (8 columns): 16 loads of 16 bytes,
-// 8 complete blocks.  RBW row-blocks x (64 / RBW) column groups per wave; the 4 waves of a workgroup are stacked
-// along rows, so a workgroup covers 4*RBW row-blocks x 8*(64/RBW) columns.
+// Column-wise kernels (quantize, amax).  A workgroup covers 16 row-blocks (256 rows) by a strip of 512 columns.
+// Lane l owns columns 8l..8l+7 of the strip, so each load instruction reads 1 KiB of one row; each wave walks
+// kColSteps consecutive row-blocks (with more than one, the next row-block's 16 loads are in flight while the
+// current one is computed).  Workgroups are numbered
+// strip-fastest, so neighbouring workgroups read neighbouring strips of the same rows.  Results are staged in LDS
+// and written out so that every output row of X^T receives its 16 row-blocks (128 bytes of codes, 16 bytes of
+// scales) as contiguous stores.
 // ------------------------------------------------------------------------------------------------------------
-template <int MODE, bool PER_ROW, int RBW>
-__global__ void __launch_bounds__(kThreads)
-k_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, uint32_t col_tiles,
-                uint32_t total_tiles, const float* __restrict__ amax, uint32_t sign_mask, RngArgs rng,
-                uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gout) {
+constexpr int kColRB = 16;                     // row-blocks per workgroup
+constexpr int kColSteps = 1;                   // row-blocks per wave
+constexpr int kColThreads = 64 * kColRB / kColSteps;   // 256
+constexpr int kColPad = 17;                    // LDS row length (entries) per (column j, lane): 16 row-blocks + 1
+
+struct ColStage {
+    uint2 codes[8 * 64 * kColPad];             // [j][lane][row-block]: 8 codes bytes per block
+    uint8_t scales[8 * 64 * kColPad];          // [j][lane][row-block]
+};
+
+struct ColGrid {
+    uint32_t nrb;      // row-blocks (rows / 16)
+    uint32_t nstrips;  // strips of 512 columns
+};
+
+__device__ __forceinline__ void col_position(const ColGrid& g, uint32_t& group, uint32_t& strip, uint32_t& rb0,
+                                             uint32_t& c8) {
+    group = blockIdx.x / g.nstrips;
+    strip = blockIdx.x - group * g.nstrips;
+    rb0 = group * kColRB + (threadIdx.x >> 6) * kColSteps;   // first row-block of this wave
+    c8 = strip * 512 + 8 * (threadIdx.x & 63u);
+}
+
+__device__ __forceinline__ void load_col_tile(const uint16_t* x, uint32_t cols, uint32_t rb, uint32_t c8,
+                                              uint4 (&v)[16]) {
+    const uint16_t* src = x + (size_t)(16 * rb) * cols + c8;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = ld16(src + (size_t)k * cols);
+}
+
+// Calls body(v, step, rb) for the wave's row-blocks rb0 .. rb0+kColSteps-1 that exist, with the next one's loads
+// issued before the current one is processed (two register sets used alternately).
+template <typename Body>
+__device__ __forceinline__ void col_steps(const uint16_t* x, uint32_t cols, uint32_t nrb, uint32_t rb0, uint32_t c8,
+                                          Body body) {
+    if (c8 >= cols || rb0 >= nrb) return;
+    if constexpr (kColSteps == 1) {
+        uint4 v[16];
+        load_col_tile(x, cols, rb0, c8, v);
+        body(v, 0u, rb0);
+        return;
+    }
+    const uint32_t n = min((uint32_t)kColSteps, nrb - rb0);
+    uint4 va[16], vb[16];
+    load_col_tile(x, cols, rb0, c8, va);
+#pragma unroll
+    for (uint32_t s = 0; s < (uint32_t)kColSteps; s += 2) {
+        if (s >= n) break;
+        if (s + 1 < n) load_col_tile(x, cols, rb0 + s + 1, c8, vb);
+        body(va, s, rb0 + s);
+        if (s + 1 >= n) break;
+        if (s + 2 < n) load_col_tile(x, cols, rb0 + s + 2, c8, va);
+        body(vb, s + 1, rb0 + s + 1);
+    }
+}
+
+__device__ __forceinline__ uint32_t stage_index(uint32_t j, uint32_t lane, uint32_t rbl) {
+    return (j * 64 + lane) * kColPad + rbl;
+}
+
+// Writes the staged codes/scales of the workgroup: (column, row-block) pairs with the row-block fastest, so 16
+// consecutive threads store one output row's 128 contiguous bytes of codes and 16 bytes of scales.
+__device__ __forceinline__ void col_write_out(const ColStage& st, uint32_t group, uint32_t strip, uint32_t rows,
+                                              uint32_t cols, uint32_t nrb, uint8_t* __restrict__ codes,
+                                              uint8_t* __restrict__ scales) {
+    const uint32_t ncol = min(512u, cols - strip * 512), nr = min((uint32_t)kColRB, nrb - group * kColRB);
+    for (uint32_t idx = threadIdx.x; idx < 512 * kColRB; idx += kColThreads) {
+        const uint32_t cl = idx / kColRB, rbl = idx % kColRB;
+        if (cl < ncol && rbl < nr) {
+            const uint32_t si = stage_index(cl & 7, cl >> 3, rbl);
+            const uint32_t c = strip * 512 + cl, rb = group * kColRB + rbl;
+            *reinterpret_cast<uint2*>(codes + (size_t)c * (rows >> 1) + 8 * (size_t)rb) = st.codes[si];
+            scales[(size_t)c * nrb + rb] = st.scales[si];
+        }
+    }
+}
+
+template <int MODE, bool PER_ROW>
+__global__ void __launch_bounds__(kColThreads)
+k_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColGrid cg,
+                const float* __restrict__ amax, uint32_t sign_mask, RngArgs rng, uint8_t* __restrict__ codes,
+                uint8_t* __restrict__ scales, float* __restrict__ gout) {
     constexpr bool SR = MODE != kRN;
-    constexpr int CGW = 64 / RBW;                 // column groups per wave
-    constexpr int TILE_COLS = 8 * CGW;
-    constexpr int TILE_RB = 4 * RBW;              // row-blocks per workgroup tile
-    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
-    const uint32_t rbl = lane % RBW, cgl = lane / RBW;
-    const uint32_t nrb = rows >> 4;               // blocks per row of V
+    constexpr bool RHT = MODE == kRHTSR;
+    __shared__ ColStage st;
+    __shared__ RTable tab;
     float g = 0.0f, d6 = 0.0f;
     if (!PER_ROW) {
         g = global_scale(amax[0]);
         d6 = 6.0f * g;
         if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
+        fill_rtable(tab, g);
     }
-    for (uint32_t t = blockIdx.x; t < total_tiles; t += gridDim.x) {
-        const uint32_t tr = t / col_tiles, tc = t - tr * col_tiles;
-        const uint32_t rb = tr * TILE_RB + wave * RBW + rbl;
-        const uint32_t c8 = (tc * TILE_COLS) + 8 * cgl;
-        if (rb >= nrb || c8 >= cols) continue;
-        const uint16_t* src = x + (size_t)(16 * rb) * cols + c8;
-        uint4 v[16];
+    uint32_t group, strip, rb0, c8;
+    col_position(cg, group, strip, rb0, c8);
+    const uint32_t lane = threadIdx.x & 63u;
+    col_steps(x, cols, cg.nrb, rb0, c8, [&](const uint4 (&v)[16], uint32_t step, uint32_t rb) {
+        const uint32_t rbl = rb - group * kColRB;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) v[k] = ld16(src + (size_t)k * cols);
-        if (MODE == kRHTSR) {
+        for (int p = 0; p < 4; ++p) {
+            float wp[2][16];
+            widen_col_pair<RHT>(v, p, sign_mask, wp[0], wp[1]);
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const uint32_t f = ((sign_mask >> k) & 1u) ? 0x80008000u : 0u;
-                v[k].x ^= f;
-                v[k].y ^= f;
-                v[k].z ^= f;
-                v[k].w ^= f;
+            for (int t = 0; t < 2; ++t) {
+                const uint32_t j = 2 * p + t, c = c8 + j;
+                Rand4 inv{{0, 0, 0, 0}};
+                if (SR) inv = block_rand_inv(rng, (uint64_t)c * cg.nrb + rb);
+                uint32_t lo, hi, sb;
+                if (PER_ROW) {
+                    const float gr = global_scale(amax[c]);
+                    if (rb == 0) gout[c] = gr;
+                    quantize_block<SR, RHT>(wp[t], 6.0f * gr, [&](uint32_t sc) { return scale_multiplier(sc, gr); },
+                                            inv, lo, hi, sb);
+                } else {
+                    quantize_block<SR, RHT>(wp[t], d6, [&](uint32_t sc) { return tab.r[sc]; }, inv, lo, hi, sb);
+                }
+                const uint32_t si = stage_index(j, lane, rbl);
+                st.codes[si] = make_uint2(lo, hi);
+                st.scales[si] = (uint8_t)sb;
             }
         }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t c = c8 + j;
-            float y[16];
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const uint32_t w = (j >> 1) == 0 ? v[k].x : (j >> 1) == 1 ? v[k].y : (j >> 1) == 2 ? v[k].z : v[k].w;
-                y[k] = (j & 1) ? bf16_hi(w) : bf16_lo(w);
-            }
-            if (MODE == kRHTSR) fwht16(y);
-            if (PER_ROW) {
-                g = global_scale(amax[c]);
-                d6 = 6.0f * g;
-                if (rb == 0) gout[c] = g;
-            }
-            const uint64_t n = (uint64_t)c * nrb + rb;
-            Rand4 rnd{{0, 0, 0, 0}};
-            if (SR) rnd = block_rand(rng, n);
-            uint32_t lo, hi, sb;
-            quantize16<SR>(y, d6, g, rnd, lo, hi, sb);
-            *reinterpret_cast<uint2*>(codes + (size_t)c * (rows >> 1) + 8 * (size_t)rb) = make_uint2(lo, hi);
-            scales[(size_t)c * nrb + rb] = (uint8_t)sb;
-        }
-    }
+        (void)step;
+    });
+    __syncthreads();
+    col_write_out(st, group, strip, rows, cols, cg.nrb, codes, scales);
 }
 
 // ------------------------------------------------------------------------------------------------------------
 // 16x16 RN quantization, W and/or W^T from one read ([P2, intro: 2D weight scaling; results: both weight
-// orientations]).  Lane pair (2m, 2m+1) owns tile column tj (columns 16 tj + 8h .. +7 for half h); each lane
-// loads 16 rows x 16 bytes; the tile amax is the max over the pair.  Waves of a workgroup are stacked along tile
-// rows, each wave loops over TR tile rows.
+// orientations]).  Same workgroup layout as the column-wise kernels (a step is one tile-row of 16 rows, lane = 8
+// columns); lane pair (2m, 2m+1) holds the two halves of a 16x16 tile, whose amax is the max over the pair (both
+// lanes of a pair always take the same steps).  W rows are written directly (consecutive lanes write consecutive
+// 4-byte pieces of a row); W^T is staged in LDS like the column-wise codes.
 // ------------------------------------------------------------------------------------------------------------
-template <bool WANT_W, bool WANT_WT, int TR>
-__global__ void __launch_bounds__(kThreads)
-k_quant_16x16(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, uint32_t col_groups,
-              uint32_t total_groups, const float* __restrict__ amax, uint8_t* __restrict__ cw,
-              uint8_t* __restrict__ sw, float* __restrict__ gw, uint8_t* __restrict__ ct, uint8_t* __restrict__ st,
+template <bool WANT_W, bool WANT_WT>
+__global__ void __launch_bounds__(kColThreads)
+k_quant_16x16(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColGrid cg,
+              const float* __restrict__ amax, uint8_t* __restrict__ cw_codes, uint8_t* __restrict__ sw,
+              float* __restrict__ gw, uint8_t* __restrict__ ct, uint8_t* __restrict__ st_scales,
               float* __restrict__ gt) {
-    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
-    const uint32_t h = lane & 1u;
-    const uint32_t ntr = rows >> 4, ntc = cols >> 4;
+    __shared__ ColStage st;
+    __shared__ RTable tab;
     const float g = global_scale(amax[0]);
     const float d6 = 6.0f * g;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         if (WANT_W) gw[0] = g;
         if (WANT_WT) gt[0] = g;
     }
-    for (uint32_t grp = blockIdx.x; grp < total_groups; grp += gridDim.x) {
-        const uint32_t gr = grp / col_groups, gc = grp - gr * col_groups;
-        const uint32_t tj = gc * 32 + (lane >> 1);
-        const bool col_ok = tj < ntc;
-        for (int it = 0; it < TR; ++it) {
-            const uint32_t ti = (gr * 4 + wave) * TR + it;
-            // both lanes of a pair share ti and tj, so the pair is active or idle together (needed by the shuffle)
-            const bool ok = col_ok && ti < ntr;
-            uint4 v[16];
-            uint32_t m16 = 0;  // integer max of the bf16 magnitude bits of this half tile
-            if (ok) {
-                const uint16_t* src = x + (size_t)(16 * ti) * cols + 16 * tj + 8 * h;
+    fill_rtable(tab, g);
+    uint32_t group, strip, ti0, c8;
+    col_position(cg, group, strip, ti0, c8);
+    const uint32_t lane = threadIdx.x & 63u, h = lane & 1u;
+    const uint32_t ntc = cols >> 4, tj = c8 >> 4;
+    col_steps(x, cols, cg.nrb, ti0, c8, [&](const uint4 (&v)[16], uint32_t, uint32_t ti) {
+        float m = 0.0f;
 #pragma unroll
-                for (int k = 0; k < 16; ++k) v[k] = ld16(src + (size_t)k * cols);
+        for (int k = 0; k < 16; ++k) {
+            const uint32_t ws[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
-                for (int k = 0; k < 16; ++k) {
-                    const uint32_t ws[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+            for (int q = 0; q < 4; q += 2)
+                m = absmax3(absmax3(m, bf16_lo(ws[q], 0u), bf16_hi(ws[q], 0u)), bf16_lo(ws[q + 1], 0u),
+                            bf16_hi(ws[q + 1], 0u));
+        }
+        m = __builtin_elementwise_maximum(m, __shfl_xor(m, 1));
+        const uint32_t sb = scale_code(m, d6);
+        const float r = tab.r[sb];
+        const bool fast = r > 0.0f && r <= kFltMax;
+        uint32_t wt[8][2];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) m16 = umax(m16, umax(ws[q] & 0x7FFFu, (ws[q] >> 16) & 0x7FFFu));
-                }
-            }
-            m16 = umax(m16, (uint32_t)__shfl_xor((int)m16, 1));
-            if (!ok) continue;
-            const BlockScale sc = block_scale(as_f(m16 << 16), d6, g);
-            uint32_t wt[8][2];
+        for (int k = 0; k < 16; ++k) {
+            const uint32_t ws[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+            float q[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) wt[j][0] = wt[j][1] = 0;
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const uint32_t ws[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-                uint32_t rowc = 0;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float y = (j & 1) ? bf16_hi(ws[j >> 1]) : bf16_lo(ws[j >> 1]);
-                    const uint32_t code = sc.r > 0.0f ? e2m1_code_fast<false>(y, sc.r, 0u)
-                                                      : e2m1_code_general<false>(y, sc.r, 0u);
-                    rowc |= code << (4 * j);
-                    wt[j][k >> 3] |= code << (4 * (k & 7));
-                }
-                if (WANT_W)
-                    *reinterpret_cast<uint32_t*>(cw + (size_t)(16 * ti + k) * (cols >> 1) + 8 * tj + 4 * h) = rowc;
-            }
-            if (WANT_W) {
-#pragma unroll
-                for (int k = 0; k < 8; ++k) sw[(size_t)(16 * ti + 8 * h + k) * ntc + tj] = (uint8_t)sc.sb;
-            }
+            for (int j = 0; j < 8; ++j) q[j] = ((j & 1) ? bf16_hi(ws[j >> 1], 0u) : bf16_lo(ws[j >> 1], 0u)) * r;
+            uint32_t rowc = pack8_rn(q);
+            if (!fast) rowc = patch_nan8(rowc, q);
+            if (WANT_W)
+                *reinterpret_cast<uint32_t*>(cw_codes + (size_t)(16 * ti + k) * (cols >> 1) + (c8 >> 1)) = rowc;
             if (WANT_WT) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const uint32_t c = 16 * tj + 8 * h + j;
-                    *reinterpret_cast<uint2*>(ct + (size_t)c * (rows >> 1) + 8 * ti) = make_uint2(wt[j][0], wt[j][1]);
-                    st[(size_t)c * ntr + ti] = (uint8_t)sc.sb;
+                    const uint32_t code = (rowc >> (4 * j)) & 0xFu;
+                    if ((k & 7) == 0) wt[j][k >> 3] = code;
+                    else wt[j][k >> 3] |= code << (4 * (k & 7));
                 }
             }
         }
+        if (WANT_W) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) sw[(size_t)(16 * ti + 8 * h + k) * ntc + tj] = (uint8_t)sb;
+        }
+        if (WANT_WT) {
+            const uint32_t rbl = ti - group * kColRB;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t si = stage_index(j, lane, rbl);
+                st.codes[si] = make_uint2(wt[j][0], wt[j][1]);
+                st.scales[si] = (uint8_t)sb;
+            }
+        }
+    });
+    if (WANT_WT) {
+        __syncthreads();
+        col_write_out(st, group, strip, rows, cols, cg.nrb, ct, st_scales);
     }
 }
 
@@ -446,11 +628,14 @@ k_quant_16x16(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, uint
 // Four-over-six ([P3]): row-wise 1x16 RN; candidates T = 6 and T = 4; decode, squared errors, pinned tree sum
 // (i, i+8), then strides 4, 2, 1; map-to-4 kept only if strictly lower.
 // ------------------------------------------------------------------------------------------------------------
-__device__ __forceinline__ float e2m1_value(uint32_t code) {
-    const uint32_t m = code & 7u;
-    // m >= 2: exponent field (m >> 1) + 126 and mantissa bit m & 1, i.e. (m + 252) << 22; m = 1 is 0.5
-    const uint32_t mag = m >= 2u ? ((m + 252u) << 22) : (m == 1u ? 0x3F000000u : 0u);
-    return as_f(mag | ((code & 8u) << 28));
+// Decode 8 packed codes (element 2k in the low nibble of byte k) with the gfx950 FP4 -> f32 conversion.
+__device__ __forceinline__ void unpack8(uint32_t d, float (&v)[8]) {
+    const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
+    const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1);
+    const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);
+    const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3);
+    v[0] = p0.x; v[1] = p0.y; v[2] = p1.x; v[3] = p1.y;
+    v[4] = p2.x; v[5] = p2.y; v[6] = p3.x; v[7] = p3.y;
 }
 
 template <bool PER_ROW>
@@ -463,38 +648,51 @@ k_quant_4o6(const uint4* __restrict__ x, uint32_t total_blocks, FastDiv per_row,
         if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
     }
     const uint32_t stride = gridDim.x * kThreads;
-    for (uint32_t n = blockIdx.x * kThreads + threadIdx.x; n < total_blocks; n += stride) {
+    uint32_t n = blockIdx.x * kThreads + threadIdx.x;
+    if (n >= total_blocks) return;
+    uint4 a = ld16(x + 2 * (size_t)n), b = ld16(x + 2 * (size_t)n + 1);
+    for (; n < total_blocks; n += stride) {
+        const uint32_t nn = n + stride;
+        uint4 a2 = a, b2 = b;
+        if (nn < total_blocks) {
+            a2 = ld16(x + 2 * (size_t)nn);
+            b2 = ld16(x + 2 * (size_t)nn + 1);
+        }
         if (PER_ROW) {
             const uint32_t row = fdiv(n, per_row);
             g = global_scale(amax[row]);
             if (n == row * per_row.d) gout[row] = g;
         }
-        const uint4 a = ld16(x + 2 * (size_t)n);
-        const uint4 b = ld16(x + 2 * (size_t)n + 1);
-        const float xv[16] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y), bf16_lo(a.z), bf16_hi(a.z),
-                              bf16_lo(a.w), bf16_hi(a.w), bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y),
-                              bf16_lo(b.z), bf16_hi(b.z), bf16_lo(b.w), bf16_hi(b.w)};
-        uint32_t mx = 0;
+        float xv[16];
+        widen_row_block<false>(a, b, 0u, xv);
+        float m = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = umax(mx, as_u(xv[i]) & 0x7FFFFFFFu);
-        const float bamax = as_f(mx);
+        for (int i = 0; i < 16; i += 2) m = absmax3(m, xv[i], xv[i + 1]);
         uint32_t cand_lo[2], cand_hi[2], cand_sb[2];
         float err[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const float d = (c == 0 ? 6.0f : 4.0f) * g;
-            const BlockScale sc = block_scale(bamax, d, g);
-            const float sbf = e4m3_decode(sc.sb);
+            const uint32_t sb = scale_code(m, (c == 0 ? 6.0f : 4.0f) * g);
+            const float r = scale_multiplier(sb, g);
+            const bool fast = r > 0.0f && r <= kFltMax;
+            float q[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) q[i] = xv[i] * r;
+            const float(&q0)[8] = *reinterpret_cast<const float(*)[8]>(&q[0]);
+            const float(&q1)[8] = *reinterpret_cast<const float(*)[8]>(&q[8]);
+            uint32_t lo = pack8_rn(q0), hi = pack8_rn(q1);
+            if (!fast) {
+                lo = patch_nan8(lo, q0);
+                hi = patch_nan8(hi, q1);
+            }
+            const float sbf = e4m3_decode(sb);
+            float dv[16];
+            unpack8(lo, *reinterpret_cast<float(*)[8]>(&dv[0]));
+            unpack8(hi, *reinterpret_cast<float(*)[8]>(&dv[8]));
             float e[16];
-            uint32_t lo = 0, hi = 0;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const uint32_t code = sc.r > 0.0f ? e2m1_code_fast<false>(xv[i], sc.r, 0u)
-                                                  : e2m1_code_general<false>(xv[i], sc.r, 0u);
-                if (i < 8) lo |= code << (4 * i);
-                else hi |= code << (4 * (i - 8));
-                const float xh = (e2m1_value(code) * sbf) * g;
-                const float df = xh - xv[i];
+                const float df = (dv[i] * sbf) * g - xv[i];
                 e[i] = df * df;
             }
 #pragma unroll
@@ -503,12 +701,14 @@ k_quant_4o6(const uint4* __restrict__ x, uint32_t total_blocks, FastDiv per_row,
                 for (int i = 0; i < s; ++i) e[i] = e[i] + e[i + s];
             cand_lo[c] = lo;
             cand_hi[c] = hi;
-            cand_sb[c] = sc.sb;
+            cand_sb[c] = sb;
             err[c] = e[0];
         }
         const int pick = (err[1] < err[0]) ? 1 : 0;
         codes[n] = make_uint2(cand_lo[pick], cand_hi[pick]);
         scales[n] = (uint8_t)cand_sb[pick];
+        a = a2;
+        b = b2;
     }
 }
 
@@ -522,23 +722,22 @@ k_dequantize(const uint2* __restrict__ codes, const uint8_t* __restrict__ scales
     const uint32_t stride = gridDim.x * kThreads;
     for (uint32_t n = blockIdx.x * kThreads + threadIdx.x; n < total_blocks; n += stride) {
         const float gr = PER_ROW ? g[fdiv(n, per_row)] : g[0];
-        const float sbf = e4m3_decode(scales[n] & 0x7Fu) ;
-        const float sbf_signed = (scales[n] & 0x80u) ? -sbf : sbf;
+        const uint32_t s = scales[n];
+        const float sbf = (s & 0x80u) ? -e4m3_decode(s & 0x7Fu) : e4m3_decode(s & 0x7Fu);
         const uint2 c = codes[n];
-        float out[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint32_t code = ((i < 8 ? c.x : c.y) >> (4 * (i & 7))) & 0xFu;
-            out[i] = (e2m1_value(code) * sbf_signed) * gr;
-        }
+        float v[16];
+        unpack8(c.x, *reinterpret_cast<float(*)[8]>(&v[0]));
+        unpack8(c.y, *reinterpret_cast<float(*)[8]>(&v[8]));
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            y[4 * (size_t)n + q] = make_float4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
+            y[4 * (size_t)n + q] = make_float4((v[4 * q] * sbf) * gr, (v[4 * q + 1] * sbf) * gr,
+                                               (v[4 * q + 2] * sbf) * gr, (v[4 * q + 3] * sbf) * gr);
     }
 }
 
 // ------------------------------------------------------------------------------------------------------------
-// amax kernels.  The maximum is an integer maximum over magnitude bit patterns (NaN > inf > finite).
+// amax kernels.  The maximum of magnitudes with NaN dominating (v_maximum3); reductions combine the binary32 bit
+// patterns with an integer maximum, which orders NaN > inf > finite for magnitudes.
 // ------------------------------------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 #pragma unroll
@@ -546,6 +745,7 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
     return v;
 }
 
+template <int WAVES = kWavesPerGroup>
 __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* lds) {
     v = wave_max(v);
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
@@ -553,7 +753,7 @@ __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* lds) {
     __syncthreads();
     uint32_t r = 0;
     if (threadIdx.x == 0) {
-        for (int w = 0; w < kThreads / 64; ++w) r = umax(r, lds[w]);
+        for (int w = 0; w < WAVES; ++w) r = umax(r, lds[w]);
     }
     __syncthreads();
     return r;  // valid in thread 0
@@ -565,49 +765,53 @@ __global__ void k_fill_zero(uint32_t* __restrict__ p, uint32_t n) {
 
 // g = amax / 2688 for n entries (used when the tensor to quantize is empty, so no block writes g).
 __global__ void k_write_g(const float* __restrict__ amax, float* __restrict__ g, uint32_t n) {
-    for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < n; i += gridDim.x * kThreads) g[i] = global_scale(amax[i]);
+    for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < n; i += gridDim.x * kThreads)
+        g[i] = global_scale(amax[i]);
 }
 
-// Max magnitude bits of one row-wise block (optionally transformed).
+// Publishes a workgroup's partial maximum (magnitude bits) into a zeroed per-tensor amax.  Same-address atomics
+// from every workgroup would serialise, so the current value is read first and the atomic is issued only when the
+// partial is larger (the value only grows, so a stale read can only cause an extra atomic, never a missed one).
+__device__ __forceinline__ void publish_max(uint32_t* amax_bits, uint32_t m) {
+    const uint32_t cur = __hip_atomic_load(amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (m > cur) atomicMax(amax_bits, m);
+}
+
+// Magnitude bits of one row-wise block's maximum (after the transform when RHT).
 template <bool RHT>
-__device__ __forceinline__ uint32_t block_absmax_rowwise(const uint4* x, size_t n, uint32_t sign_mask) {
-    uint4 a = ld16(x + 2 * n);
-    uint4 b = ld16(x + 2 * n + 1);
-    if (!RHT) {
-        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        uint32_t m = 0;
+__device__ __forceinline__ uint32_t rowblock_absmax(const uint4& a, const uint4& b, uint32_t mask) {
+    float w[16];
+    widen_row_block<RHT>(a, b, mask, w);
+    float m = 0.0f;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) m = umax(m, umax(w[q] & 0x7FFFu, (w[q] >> 16) & 0x7FFFu));
-        return m << 16;
-    }
-    a.x ^= sign_word(sign_mask, 0);
-    a.y ^= sign_word(sign_mask, 1);
-    a.z ^= sign_word(sign_mask, 2);
-    a.w ^= sign_word(sign_mask, 3);
-    b.x ^= sign_word(sign_mask, 4);
-    b.y ^= sign_word(sign_mask, 5);
-    b.z ^= sign_word(sign_mask, 6);
-    b.w ^= sign_word(sign_mask, 7);
-    float y[16] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y), bf16_lo(a.z), bf16_hi(a.z),
-                   bf16_lo(a.w), bf16_hi(a.w), bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y),
-                   bf16_lo(b.z), bf16_hi(b.z), bf16_lo(b.w), bf16_hi(b.w)};
-    fwht16(y);
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) m = umax(m, as_u(y[i]) & 0x7FFFFFFFu);
-    return m;
+    for (int i = 0; i < 16; i += 2) m = absmax3(m, w[i], w[i + 1]);
+    return as_u(RHT ? 0.25f * m : m) & 0x7FFFFFFFu;
 }
 
 // Row-wise, per tensor: grid-stride over blocks, one atomic max per workgroup into a zeroed amax[0].
 template <bool RHT>
 __global__ void __launch_bounds__(kThreads)
 k_amax_rowwise_tensor(const uint4* __restrict__ x, uint32_t total_blocks, uint32_t sign_mask, uint32_t* amax_bits) {
-    __shared__ uint32_t lds[kThreads / 64];
+    __shared__ uint32_t lds[kWavesPerGroup];
     uint32_t m = 0;
-    for (uint32_t n = blockIdx.x * kThreads + threadIdx.x; n < total_blocks; n += gridDim.x * kThreads)
-        m = umax(m, block_absmax_rowwise<RHT>(x, n, sign_mask));
+    const uint32_t stride = gridDim.x * kThreads;
+    uint32_t n = blockIdx.x * kThreads + threadIdx.x;
+    if (n < total_blocks) {
+        uint4 a = ld16(x + 2 * (size_t)n), b = ld16(x + 2 * (size_t)n + 1);
+        for (; n < total_blocks; n += stride) {
+            const uint32_t nn = n + stride;
+            uint4 a2 = a, b2 = b;
+            if (nn < total_blocks) {
+                a2 = ld16(x + 2 * (size_t)nn);
+                b2 = ld16(x + 2 * (size_t)nn + 1);
+            }
+            m = umax(m, rowblock_absmax<RHT>(a, b, sign_mask));
+            a = a2;
+            b = b2;
+        }
+    }
     m = block_max(m, lds);
-    if (threadIdx.x == 0) atomicMax(amax_bits, m);
+    if (threadIdx.x == 0) publish_max(amax_bits, m);
 }
 
 // Row-wise, per row: one workgroup per row (grid-stride over rows), direct store.
@@ -615,96 +819,64 @@ template <bool RHT>
 __global__ void __launch_bounds__(kThreads)
 k_amax_rowwise_rows(const uint4* __restrict__ x, uint32_t rows, uint32_t blocks_per_row, uint32_t sign_mask,
                     uint32_t* __restrict__ amax_bits) {
-    __shared__ uint32_t lds[kThreads / 64];
+    __shared__ uint32_t lds[kWavesPerGroup];
     for (uint32_t r = blockIdx.x; r < rows; r += gridDim.x) {
         uint32_t m = 0;
-        for (uint32_t b = threadIdx.x; b < blocks_per_row; b += kThreads)
-            m = umax(m, block_absmax_rowwise<RHT>(x, (size_t)r * blocks_per_row + b, sign_mask));
+        for (uint32_t b = threadIdx.x; b < blocks_per_row; b += kThreads) {
+            const size_t n = (size_t)r * blocks_per_row + b;
+            m = umax(m, rowblock_absmax<RHT>(ld16(x + 2 * n), ld16(x + 2 * n + 1), sign_mask));
+        }
         m = block_max(m, lds);
         if (threadIdx.x == 0) amax_bits[r] = m;
     }
 }
 
-// Column-wise (V = X^T): same lane tiling as k_quant_colwise.  Per tensor: one atomic per workgroup; per row of V
-// (= per column of X): lanes sharing a column group reduce over row-blocks, then one atomic per column per wave.
-template <bool RHT, bool PER_ROW, int RBW>
-__global__ void __launch_bounds__(kThreads)
-k_amax_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, uint32_t col_tiles,
-               uint32_t total_tiles, uint32_t sign_mask, uint32_t* __restrict__ amax_bits) {
-    constexpr int CGW = 64 / RBW;
-    constexpr int TILE_COLS = 8 * CGW;
-    constexpr int TILE_RB = 4 * RBW;
-    __shared__ uint32_t lds[kThreads / 64];
+// Column-wise (V = X^T), same workgroup layout as k_quant_colwise.  Per tensor: one publish per workgroup.  Per row
+// of V (= per column of X): the waves' column maxima are combined in LDS, then one atomic per column.
+template <bool RHT, bool PER_ROW>
+__global__ void __launch_bounds__(kColThreads)
+k_amax_colwise(const uint16_t* __restrict__ x, uint32_t cols, ColGrid cg, uint32_t sign_mask,
+               uint32_t* __restrict__ amax_bits) {
+    constexpr int kWaves = kColThreads / 64;
+    __shared__ uint32_t colmax_lds[PER_ROW ? 512 * kWaves : kWaves];
+    uint32_t group, strip, rb0, c8;
+    col_position(cg, group, strip, rb0, c8);
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
-    const uint32_t rbl = lane % RBW, cgl = lane / RBW;
-    const uint32_t nrb = rows >> 4;
-    uint32_t total = 0;
-    for (uint32_t t = blockIdx.x; t < total_tiles; t += gridDim.x) {
-        const uint32_t tr = t / col_tiles, tc = t - tr * col_tiles;
-        const uint32_t rb = tr * TILE_RB + wave * RBW + rbl;
-        const uint32_t c8 = tc * TILE_COLS + 8 * cgl;
-        const bool ok = rb < nrb && c8 < cols;
-        uint32_t colmax[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (ok) {
-            const uint16_t* src = x + (size_t)(16 * rb) * cols + c8;
-            uint4 v[16];
+    float cm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    col_steps(x, cols, cg.nrb, rb0, c8, [&](const uint4 (&v)[16], uint32_t, uint32_t) {
 #pragma unroll
-            for (int k = 0; k < 16; ++k)
-                v[k] = ld16(src + (size_t)k * cols);
-            if (!RHT) {
+        for (int p = 0; p < 4; ++p) {
+            float wp[2][16];
+            widen_col_pair<RHT>(v, p, sign_mask, wp[0], wp[1]);
 #pragma unroll
-                for (int k = 0; k < 16; ++k) {
-                    const uint32_t ws[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+            for (int t = 0; t < 2; ++t) {
+                float m = cm[2 * p + t];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        colmax[j] = umax(colmax[j], ((j & 1) ? (ws[j >> 1] >> 16) : ws[j >> 1]) & 0x7FFFu);
-                }
-#pragma unroll
-                for (int j = 0; j < 8; ++j) colmax[j] <<= 16;
-            } else {
-#pragma unroll
-                for (int k = 0; k < 16; ++k) {
-                    const uint32_t f = ((sign_mask >> k) & 1u) ? 0x80008000u : 0u;
-                    v[k].x ^= f;
-                    v[k].y ^= f;
-                    v[k].z ^= f;
-                    v[k].w ^= f;
-                }
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    float y[16];
-#pragma unroll
-                    for (int k = 0; k < 16; ++k) {
-                        const uint32_t w =
-                            (j >> 1) == 0 ? v[k].x : (j >> 1) == 1 ? v[k].y : (j >> 1) == 2 ? v[k].z : v[k].w;
-                        y[k] = (j & 1) ? bf16_hi(w) : bf16_lo(w);
-                    }
-                    fwht16(y);
-#pragma unroll
-                    for (int k = 0; k < 16; ++k) colmax[j] = umax(colmax[j], as_u(y[k]) & 0x7FFFFFFFu);
-                }
+                for (int k = 0; k < 16; k += 2) m = absmax3(m, wp[t][k], wp[t][k + 1]);
+                cm[2 * p + t] = m;
             }
         }
-        if (PER_ROW) {
-            // lanes with the same cgl are RBW consecutive lanes: reduce over rbl with xor offsets < RBW
+    });
+    uint32_t cb[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 8; ++j) cb[j] = as_u(RHT ? 0.25f * cm[j] : cm[j]) & 0x7FFFFFFFu;
+    if (PER_ROW) {
 #pragma unroll
-                for (int off = RBW / 2; off >= 1; off >>= 1)
-                    colmax[j] = umax(colmax[j], (uint32_t)__shfl_xor((int)colmax[j], off));
-            }
-            if (rbl == 0 && c8 < cols) {
+        for (int j = 0; j < 8; ++j) colmax_lds[(8 * lane + j) * kWaves + wave] = cb[j];
+        __syncthreads();
+        for (uint32_t cl = threadIdx.x; cl < 512; cl += kColThreads) {
+            const uint32_t c = strip * 512 + cl;
+            uint32_t m = 0;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) atomicMax(amax_bits + c8 + j, colmax[j]);
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) total = umax(total, colmax[j]);
+            for (int w = 0; w < kWaves; ++w) m = umax(m, colmax_lds[cl * kWaves + w]);
+            if (c < cols) atomicMax(amax_bits + c, m);
         }
-    }
-    if (!PER_ROW) {
-        total = block_max(total, lds);
-        if (threadIdx.x == 0) atomicMax(amax_bits, total);
+    } else {
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = umax(m, cb[j]);
+        m = block_max<kWaves>(m, colmax_lds);
+        if (threadIdx.x == 0) publish_max(amax_bits, m);
     }
 }
 
@@ -730,16 +902,25 @@ uint32_t grid_for(uint64_t work_items, uint32_t per_group, uint32_t groups_per_c
     return (uint32_t)(g == 0 ? 1 : g);
 }
 
+// Column-wise grid: one workgroup per (16 row-blocks) x (512-column strip), strip-fastest.
+ColGrid col_grid(int64_t rows, int64_t cols, uint32_t& grid) {
+    ColGrid g;
+    g.nrb = (uint32_t)(rows / 16);
+    g.nstrips = (uint32_t)((cols + 511) / 512);
+    grid = ((g.nrb + kColRB - 1) / kColRB) * g.nstrips;
+    if (grid == 0) grid = 1;
+    return g;
+}
+
 RngArgs rng_args(Philox p) {
     return RngArgs{(uint32_t)p.seed, (uint32_t)(p.seed >> 32), (uint32_t)p.offset, (uint32_t)(p.offset >> 32)};
 }
-
-constexpr int kColRBW = 8;  // row-blocks per wave in the column-wise kernels
 
 hipError_t write_empty_g(const float* amax, float* g, uint32_t n, hipStream_t stream) {
     if (n) k_write_g<<<grid_for(n, kThreads, 1), kThreads, 0, stream>>>(amax, g, n);
     return hipGetLastError();
 }
+
 
 }  // namespace
 
@@ -756,38 +937,24 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, bool colwi
     if (!colwise) {
         const uint32_t bpr = (uint32_t)(cols / 16);
         const uint32_t total = (uint32_t)(rows * bpr);
+        const uint4* xv = reinterpret_cast<const uint4*>(x);
         if (per_row) {
             const uint32_t grid = (uint32_t)(rows < 65536 * 16 ? rows : 65536 * 16);
-            if (use_rht)
-                k_amax_rowwise_rows<true><<<grid, kThreads, 0, stream>>>(reinterpret_cast<const uint4*>(x),
-                                                                           (uint32_t)rows, bpr, sign_mask, bits);
-            else
-                k_amax_rowwise_rows<false><<<grid, kThreads, 0, stream>>>(reinterpret_cast<const uint4*>(x),
-                                                                            (uint32_t)rows, bpr, sign_mask, bits);
+            if (use_rht) k_amax_rowwise_rows<true><<<grid, kThreads, 0, stream>>>(xv, (uint32_t)rows, bpr, sign_mask, bits);
+            else k_amax_rowwise_rows<false><<<grid, kThreads, 0, stream>>>(xv, (uint32_t)rows, bpr, sign_mask, bits);
         } else {
             const uint32_t grid = grid_for(total, kThreads * 4, 8);
-            if (use_rht)
-                k_amax_rowwise_tensor<true><<<grid, kThreads, 0, stream>>>(reinterpret_cast<const uint4*>(x), total,
-                                                                             sign_mask, bits);
-            else
-                k_amax_rowwise_tensor<false><<<grid, kThreads, 0, stream>>>(reinterpret_cast<const uint4*>(x),
-                                                                              total, sign_mask, bits);
+            if (use_rht) k_amax_rowwise_tensor<true><<<grid, kThreads, 0, stream>>>(xv, total, sign_mask, bits);
+            else k_amax_rowwise_tensor<false><<<grid, kThreads, 0, stream>>>(xv, total, sign_mask, bits);
         }
     } else {
-        constexpr int RBW = kColRBW;
-        const uint32_t tile_cols = 8 * (64 / RBW), tile_rb = 4 * RBW;
-        const uint32_t col_tiles = (uint32_t)((cols + tile_cols - 1) / tile_cols);
-        const uint32_t row_tiles = (uint32_t)((rows / 16 + tile_rb - 1) / tile_rb);
-        const uint32_t total = col_tiles * row_tiles;
-        const uint32_t grid = grid_for(total, 1, 8);
-#define NVFP4_AMAX_COL(R, P)                                                                                     \
-    k_amax_colwise<R, P, RBW><<<grid, kThreads, 0, stream>>>(x, (uint32_t)rows, (uint32_t)cols, col_tiles, total, \
-                                                             sign_mask, bits)
-        if (use_rht && per_row) NVFP4_AMAX_COL(true, true);
-        else if (use_rht) NVFP4_AMAX_COL(true, false);
-        else if (per_row) NVFP4_AMAX_COL(false, true);
-        else NVFP4_AMAX_COL(false, false);
-#undef NVFP4_AMAX_COL
+        uint32_t grid;
+        const ColGrid w = col_grid(rows, cols, grid);
+        const uint32_t c = (uint32_t)cols;
+        if (use_rht && per_row) k_amax_colwise<true, true><<<grid, kColThreads, 0, stream>>>(x, c, w, sign_mask, bits);
+        else if (use_rht) k_amax_colwise<true, false><<<grid, kColThreads, 0, stream>>>(x, c, w, sign_mask, bits);
+        else if (per_row) k_amax_colwise<false, true><<<grid, kColThreads, 0, stream>>>(x, c, w, sign_mask, bits);
+        else k_amax_colwise<false, false><<<grid, kColThreads, 0, stream>>>(x, c, w, sign_mask, bits);
     }
     return hipGetLastError();
 }
@@ -802,7 +969,7 @@ hipError_t launch_quant_1x16(const uint16_t* x, int64_t rows, int64_t cols, bool
         const uint32_t bpr = (uint32_t)(cols / 16);
         const uint32_t total = (uint32_t)(rows * bpr);
         const FastDiv fd = make_fastdiv(bpr);
-        const uint32_t grid = grid_for(total, kThreads, 16);
+        const uint32_t grid = grid_for(total, kThreads, 8);
         const uint4* xv = reinterpret_cast<const uint4*>(x);
         uint2* cv = reinterpret_cast<uint2*>(codes);
 #define NVFP4_ROW(M, P) \
@@ -814,15 +981,11 @@ hipError_t launch_quant_1x16(const uint16_t* x, int64_t rows, int64_t cols, bool
         }
 #undef NVFP4_ROW
     } else {
-        constexpr int RBW = kColRBW;
-        const uint32_t tile_cols = 8 * (64 / RBW), tile_rb = 4 * RBW;
-        const uint32_t col_tiles = (uint32_t)((cols + tile_cols - 1) / tile_cols);
-        const uint32_t row_tiles = (uint32_t)((rows / 16 + tile_rb - 1) / tile_rb);
-        const uint32_t total = col_tiles * row_tiles;
-        const uint32_t grid = grid_for(total, 1, 16);
-#define NVFP4_COL(M, P)                                                                                       \
-    k_quant_colwise<M, P, RBW><<<grid, kThreads, 0, stream>>>(x, (uint32_t)rows, (uint32_t)cols, col_tiles, \
-                                                              total, amax, sign_mask, ra, codes, scales, g)
+        uint32_t grid;
+        const ColGrid w = col_grid(rows, cols, grid);
+#define NVFP4_COL(M, P)                                                                                     \
+    k_quant_colwise<M, P><<<grid, kColThreads, 0, stream>>>(x, (uint32_t)rows, (uint32_t)cols, w, amax,    \
+                                                            sign_mask, ra, codes, scales, g)
         switch (mode) {
             case kRN: if (per_row) NVFP4_COL(kRN, true); else NVFP4_COL(kRN, false); break;
             case kSR: if (per_row) NVFP4_COL(kSR, true); else NVFP4_COL(kSR, false); break;
@@ -842,15 +1005,11 @@ hipError_t launch_quant_16x16(const uint16_t* x, int64_t rows, int64_t cols, con
         if (e == hipSuccess && codes_wt) e = write_empty_g(amax, g_wt, 1u, stream);
         return e;
     }
-    constexpr int TR = 4;
-    const uint32_t ntr = (uint32_t)(rows / 16), ntc = (uint32_t)(cols / 16);
-    const uint32_t col_groups = (ntc + 31) / 32;
-    const uint32_t row_groups = (ntr + 4 * TR - 1) / (4 * TR);
-    const uint32_t total = col_groups * row_groups;
-    const uint32_t grid = grid_for(total, 1, 16);
+    uint32_t grid;
+    const ColGrid w = col_grid(rows, cols, grid);
 #define NVFP4_2D(W, T)                                                                                          \
-    k_quant_16x16<W, T, TR><<<grid, kThreads, 0, stream>>>(x, (uint32_t)rows, (uint32_t)cols, col_groups, total, \
-                                                           amax, codes_w, scales_w, g_w, codes_wt, scales_wt, g_wt)
+    k_quant_16x16<W, T><<<grid, kColThreads, 0, stream>>>(x, (uint32_t)rows, (uint32_t)cols, w, amax, codes_w, \
+                                                          scales_w, g_w, codes_wt, scales_wt, g_wt)
     if (codes_w && codes_wt) NVFP4_2D(true, true);
     else if (codes_w) NVFP4_2D(true, false);
     else NVFP4_2D(false, true);
@@ -864,7 +1023,7 @@ hipError_t launch_quant_4o6(const uint16_t* x, int64_t rows, int64_t cols, bool 
     const uint32_t bpr = (uint32_t)(cols / 16);
     const uint32_t total = (uint32_t)(rows * bpr);
     const FastDiv fd = make_fastdiv(bpr);
-    const uint32_t grid = grid_for(total, kThreads, 16);
+    const uint32_t grid = grid_for(total, kThreads, 8);
     if (per_row)
         k_quant_4o6<true><<<grid, kThreads, 0, stream>>>(reinterpret_cast<const uint4*>(x), total, fd, amax,
                                                           reinterpret_cast<uint2*>(codes), scales, g);

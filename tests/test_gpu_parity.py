@@ -299,3 +299,31 @@ def test_full_four_over_six_16384x8192():
     x = W.make("four_over_six_16384x8192")
     for lo in (0, 5000, 16384 - 512):
         check_4o6(x, 1, rows_range=(lo, lo + 512))
+
+
+# ------------------------------------------------------------------------------------------------ HIP graphs
+def test_graph_replays_match_eager():
+    """amax + RHT+SR quantize captured in a HIP graph (the zeroing of the amax is a kernel, not a memset node):
+    every replay, with eager work and synchronisation between replays, matches the eager result bit for bit."""
+    x = W.lognormal_gradients(1024, 768, seed=13)
+    xd = dev(x)
+    a_e = Q.nvfp4_amax(xd, Q.COLWISE, 0, True, 0x3C3C)
+    o_e = Q.nvfp4_quantize_rht_sr(xd, a_e, 0x3C3C, 5, 9, Q.COLWISE)
+    torch.cuda.synchronize()
+    a_g = torch.full((1,), 123.0, device="cuda")
+    o_g = Q.alloc_out(768, 1024, 0, xd.device)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        Q.nvfp4_amax(xd, Q.COLWISE, 0, True, 0x3C3C, amax=a_g)
+        Q.nvfp4_quantize_rht_sr(xd, a_g, 0x3C3C, 5, 9, Q.COLWISE, out=o_g)
+    for rep in range(4):
+        say("graph replay", rep)
+        a_g.fill_(1e30)                         # stale larger value: the graph must zero it again
+        o_g.codes.zero_()
+        Q.nvfp4_quantize_rn(xd, a_e, Q.BLOCK_1X16, Q.ROWWISE)   # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(a_g.view(torch.int32), a_e.view(torch.int32))
+        assert torch.equal(o_g.codes, o_e.codes) and torch.equal(o_g.scales, o_e.scales)
+        assert torch.equal(o_g.g, o_e.g)
