@@ -22,6 +22,7 @@ Also printed in the same JSON line:
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -38,6 +39,8 @@ MALL_BYTES = 256 << 20       # Infinity Cache
 WORKLOAD = "wgrad_colwise_rht_sr_8192x4096"
 ROWS, COLS = 8192, 4096
 SEED = 2
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_quant_colwise_rht_sr_8192x4096_traffic.txt")
+COPY_BYTES = 128 << 20       # the calibration copy for the L2-to-memory byte counters
 
 
 def algorithmic_bytes(rows: int, cols: int) -> int:
@@ -53,7 +56,35 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target duration of the CPU-oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--counter-launches", type=int, default=0, metavar="N",
+                   help="for a rocprofv3 --pmc run: launch N steps eagerly, then N copies of a 128 MiB buffer "
+                        "(the calibration copy), and exit without timing")
     return p.parse_args()
+
+
+def kernel_source_digest() -> str:
+    """sha256 of the HIP kernel sources; a traffic figure is reported only for the source it was measured on."""
+    h = hashlib.sha256()
+    for name in ("nvfp4_kernels.hip", "nvfp4_launch.h"):
+        with open(os.path.join(ROOT, "nvfp4_quantization_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per quantize launch from the committed counter summary, or None when the kernels have changed."""
+    fields = {}
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            for line in f:
+                key, sep, val = line.partition(":")
+                if sep:
+                    fields[key.strip()] = val.strip()
+    except OSError:
+        return None
+    if fields.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def run_step(Q, xs, outs, amaxes, k: int, masks):
@@ -73,8 +104,10 @@ def capture(fn, first: int, count: int) -> torch.cuda.CUDAGraph:
 
 
 def time_graph(g: torch.cuda.CUDAGraph) -> float:
-    """Milliseconds of one replay of g, bracketed by device synchronisation and events on the launch stream."""
+    """Milliseconds of one replay of g (after an untimed one), bracketed by device synchronisation and events on the
+    launch stream."""
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g.replay()
     torch.cuda.synchronize()
     start.record()
     g.replay()
@@ -126,11 +159,21 @@ def main():
     torch.cuda.synchronize()
 
     step = lambda k: run_step(Q, xs, outs, amaxes, k, masks)
+    if args.counter_launches:
+        for k in range(args.counter_launches):
+            step(k)
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).uniform_()
+        dst = torch.empty_like(src)
+        for _ in range(args.counter_launches):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"counter pass: {args.counter_launches} steps and {args.counter_launches} copies of "
+              f"{COPY_BYTES >> 20} MiB launched", flush=True)
+        return
     for k in range(args.warmup):                       # eager warm-up (also initialises the library)
         step(k)
     torch.cuda.synchronize()
     steps_graph = capture(step, args.warmup, args.steps)
-    steps_graph.replay()                               # untimed replay: graph upload and one more warm-up
     total_ms = time_graph(steps_graph)
     ms_per_step = total_ms / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -178,7 +221,7 @@ def main():
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {"kernel": "k_quant_colwise<RHT+SR>", "bound": "hbm", "achieved": round(q_gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(q_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "algorithmic_bytes_per_launch": step_bytes, "mean_launch_ms": round(q_ms, 5)},
+                     "traffic": measured_traffic(), "algorithmic_bytes_per_launch": step_bytes, "mean_launch_ms": round(q_ms, 5)},
         "extra": {
             "amax_call_ms": round(amax_ms, 5),
             "amax_call_gbs_read": round(2 * ROWS * COLS / (amax_ms * 1e-3) / 1e9, 2),
