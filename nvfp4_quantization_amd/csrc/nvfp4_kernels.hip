@@ -28,6 +28,7 @@
 
 #include "nvfp4_launch.h"
 
+
 namespace nvfp4 {
 namespace {
 
@@ -36,6 +37,7 @@ constexpr int kWavesPerGroup = kThreads / 64;
 constexpr float kFltMax = 3.402823466e38f;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
 __device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
@@ -119,22 +121,18 @@ __device__ __forceinline__ Rand4 block_rand_inv(const RngArgs& a, uint64_t n) {
 // ------------------------------------------------------------------------------------------------------------
 // E4M3 ("fn") block scale.  [P2, layout]: E4M3 per-block scale over an FP32 global scale.  Round to nearest even,
 // saturate above 448 (the "satfinite" convention of the conversions in [P1]), NaN -> 0x7F, s <= 0 -> 0.
+// gfx950's fp32 -> E4M3 conversion rounds to nearest even; clamping to [0, 448] first (NaN-propagating min/max)
+// supplies the saturation and the zero floor, and NaN is mapped to 0x7F explicitly.  Verified against the
+// definition on all 2^32 binary32 inputs; the E4M3 -> fp32 conversion equals the exact decode on all 256 codes.
 // ------------------------------------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t e4m3_encode(float s) {
-    // branch-free: every candidate is computed and the special cases override it
-    const uint32_t b = as_u(s);
-    const uint32_t normal = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - 960u;  // s >= 2^-6: ((e - 120) << 3) | m, RNE
-    const uint32_t sub = (uint32_t)__builtin_rintf(s * 512.0f);                 // s < 2^-6: multiples of 2^-9
-    uint32_t c = (b >= 0x3C800000u) ? normal : sub;
-    c = (s > 448.0f) ? 0x7Eu : c;
-    c = (s > 0.0f) ? c : 0u;
-    return (s != s) ? 0x7Fu : c;
+    const float c = __builtin_elementwise_minimum(__builtin_elementwise_maximum(s, 0.0f), 448.0f);
+    const uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, 0.0f, 0, false);   // byte 1 is fp8(0) = 0
+    return (s != s) ? 0x7Fu : code;
 }
 
-__device__ __forceinline__ float e4m3_decode(uint32_t c) {  // c in [0, 0x7F]
-    const uint32_t e = c >> 3, m = c & 7u;
-    const float v = (e == 0) ? (float)m * 0.001953125f : as_f(((e + 120u) << 23) | (m << 20));  // m * 2^-9 exact
-    return (c == 0x7Fu) ? __builtin_nanf("") : v;
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {  // any byte: sign bit, 0x7F/0xFF are NaN
+    return __builtin_amdgcn_cvt_f32_fp8((int)c, 0);
 }
 
 // Element multiplier of block scale code sb: S = fl(decode(sb) g), r = fl(1 / S), with r = 0 for S = 0, NaN for a
@@ -147,10 +145,43 @@ __device__ __forceinline__ float scale_multiplier(uint32_t sb, float g) {
     return (S != S) ? S : r;
 }
 
-// Block scale code: s = bamax / d (d = fl(T g), correctly rounded division), sb = E4M3(s); s = 0 for bamax = 0.
-__device__ __forceinline__ uint32_t scale_code(float bamax, float d) {
-    const float s = bamax / d;
+// Divisor of the block-scale quotient s = fl(bamax / d), d = fl(T g).  The quotient is formed with Markstein's
+// method (P. Markstein, "Computation of elementary functions on the IBM RISC System/6000 processor", IBM J. Res.
+// Dev. 34(1), 1990): from y = fl(1/d) and q = fl(bamax y), which is within one ulp of bamax/d, the exact FMA
+// residual e = bamax - q d gives the correctly rounded quotient fl(q + e y), provided no step underflows or
+// overflows.  That holds for 2^-60 <= d <= 2^60 and 2^-20 <= q <= 2^64; below that window of q the quotient is
+// under 2^-10 and the code is 0 either way, above it the code saturates either way.  Other d use the division.
+struct Divisor {
+    float d, y;
+    bool fast;
+};
+
+__device__ __forceinline__ Divisor make_divisor(float d) {
+    return Divisor{d, 1.0f / d, d >= 0x1p-60f && d <= 0x1p60f};
+}
+
+// Block scale code: sb = E4M3(fl(bamax / d)), with s = 0 for bamax = 0.
+__device__ __forceinline__ uint32_t scale_code(float bamax, const Divisor& dv) {
+    float s;
+    if (dv.fast) {
+        const float q = bamax * dv.y;
+        s = (q >= 0x1p-20f && q <= 0x1p64f) ? __builtin_fmaf(__builtin_fmaf(-q, dv.d, bamax), dv.y, q) : q;
+    } else {
+        s = bamax / dv.d;
+    }
     return e4m3_encode(bamax == 0.0f ? 0.0f : s);
+}
+
+// NaN-propagating maximum of the 16 magnitudes (a depth-3 tree of v_maximum3).
+__device__ __forceinline__ float absmax16(const float (&w)[16]) {
+    const float m0 = absmax3(__builtin_fabsf(w[0]), w[1], w[2]);
+    const float m1 = absmax3(__builtin_fabsf(w[3]), w[4], w[5]);
+    const float m2 = absmax3(__builtin_fabsf(w[6]), w[7], w[8]);
+    const float m3 = absmax3(__builtin_fabsf(w[9]), w[10], w[11]);
+    const float m4 = absmax3(__builtin_fabsf(w[12]), w[13], w[14]);
+    const float m5 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m0, m1), m2);
+    const float m6 = absmax3(__builtin_elementwise_maximum(m3, m4), w[15], w[15]);
+    return __builtin_elementwise_maximum(m5, m6);
 }
 
 // Per-tensor g: the 128 possible multipliers are tabulated once per workgroup in LDS.
@@ -166,6 +197,16 @@ __device__ __forceinline__ void fill_rtable(RTable& t, float g) {
 // ------------------------------------------------------------------------------------------------------------
 // E2M1 encoding with the gfx950 conversions (unit scale).  Element 2k goes to the low nibble of byte k.
 // ------------------------------------------------------------------------------------------------------------
+// Byte sel of d replaced by the codes of (a, b); the other bytes kept.
+__device__ __forceinline__ uint32_t cvt_fp4_byte(int sel, uint32_t d, float a, float b) {
+    switch (sel) {
+        case 0: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, a, b, 1.0f, 0);
+        case 1: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, a, b, 1.0f, 1);
+        case 2: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, a, b, 1.0f, 2);
+        default: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, a, b, 1.0f, 3);
+    }
+}
+
 __device__ __forceinline__ uint32_t pack8_rn(const float (&q)[8]) {
     uint32_t d = 0;
     d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, q[0], q[1], 1.0f, 0);
@@ -236,11 +277,10 @@ __device__ __forceinline__ void encode16(const float (&q)[16], const Rand4& inv,
 // 2^-124 <= r < 2^117, where fl(fl(0.25 w) r) and fl(w fl(0.25 r)) give the same code for every w (they are equal
 // when 0.25 w is exact, and both are below 2^-9 -- code 0 with the sign of w -- when it is not).
 template <bool SR, bool RHT, typename ROf>
-__device__ __forceinline__ bool quantize_block_fast(const float (&w)[16], float d6, ROf r_of, const Rand4& inv,
-                                                    uint32_t& lo, uint32_t& hi, uint32_t& sb, float& r) {
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) m = absmax3(m, w[i], w[i + 1]);
+__device__ __forceinline__ bool quantize_block_fast(const float (&w)[16], const Divisor& d6, ROf r_of,
+                                                    const Rand4& inv, uint32_t& lo, uint32_t& hi, uint32_t& sb,
+                                                    float& r) {
+    const float m = absmax16(w);
     const float bamax = RHT ? 0.25f * m : m;       // max_i fl(0.25 |w_i|) = fl(0.25 max_i |w_i|)
     sb = scale_code(bamax, d6);
     r = r_of(sb);
@@ -265,8 +305,8 @@ __device__ __forceinline__ void quantize_block_general(const float (&w)[16], flo
 }
 
 template <bool SR, bool RHT, typename ROf>
-__device__ __forceinline__ void quantize_block(const float (&w)[16], float d6, ROf r_of, const Rand4& inv, uint32_t& lo,
-                                               uint32_t& hi, uint32_t& sb) {
+__device__ __forceinline__ void quantize_block(const float (&w)[16], const Divisor& d6, ROf r_of, const Rand4& inv,
+                                               uint32_t& lo, uint32_t& hi, uint32_t& sb) {
     float r;
     if (!quantize_block_fast<SR, RHT>(w, d6, r_of, inv, lo, hi, sb, r)) [[unlikely]]
         quantize_block_general<SR, RHT>(w, r, inv, lo, hi);
@@ -369,10 +409,11 @@ k_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, FastDiv per_
     constexpr bool SR = MODE != kRN;
     constexpr bool RHT = MODE == kRHTSR;
     __shared__ RTable tab;
-    float g = 0.0f, d6 = 0.0f;
+    float g = 0.0f;
+    Divisor d6{};
     if (!PER_ROW) {
         g = global_scale(amax[0]);
-        d6 = 6.0f * g;
+        d6 = make_divisor(6.0f * g);
         if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
         fill_rtable(tab, g);
     }
@@ -396,7 +437,7 @@ k_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, FastDiv per_
             const uint32_t row = fdiv(n, per_row);
             const float gr = global_scale(amax[row]);
             if (n == row * per_row.d) gout[row] = gr;
-            quantize_block<SR, RHT>(w, 6.0f * gr, [&](uint32_t c) { return scale_multiplier(c, gr); }, rnd, lo, hi,
+            quantize_block<SR, RHT>(w, make_divisor(6.0f * gr), [&](uint32_t c) { return scale_multiplier(c, gr); }, rnd, lo, hi,
                                     sb);
         } else {
             quantize_block<SR, RHT>(w, d6, [&](uint32_t c) { return tab.r[c]; }, rnd, lo, hi, sb);
@@ -409,18 +450,20 @@ k_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, FastDiv per_
 }
 
 // ------------------------------------------------------------------------------------------------------------
-// Column-wise kernels (quantize, amax).  A workgroup covers 16 row-blocks (256 rows) by a strip of 512 columns.
-// Lane l owns columns 8l..8l+7 of the strip, so each load instruction reads 1 KiB of one row; each wave walks
-// kColSteps consecutive row-blocks (with more than one, the next row-block's 16 loads are in flight while the
-// current one is computed).  Workgroups are numbered
-// strip-fastest, so neighbouring workgroups read neighbouring strips of the same rows.  Results are staged in LDS
-// and written out so that every output row of X^T receives its 16 row-blocks (128 bytes of codes, 16 bytes of
-// scales) as contiguous stores.
+// Column-wise kernels (quantize, amax, 16x16).  A workgroup covers 16 row-blocks (256 rows) by a strip of 512
+// columns; each of its 16 waves takes one row-block (16 rows) of the strip, and lane l owns columns 8l..8l+7, so one
+// load instruction reads 1 KiB of a row.  A lane keeps its 16 rows x 8 columns in registers (word p of row k holds
+// its columns 2p and 2p+1) and transposes them into 8 column blocks there.  Workgroups are numbered strip-fastest
+// with the strip rotated by the row group: workgroups are dealt round-robin to the 8 XCDs, and the rotation makes
+// every XCD read every strip (without it, with 8 strips, each XCD would read one fixed 1 KiB column range of every
+// row, and the XCDs' read rates differ by a third).  Results are staged in LDS and written out so that every output
+// row of X^T receives its 16 row-blocks (128 bytes of codes, 16 bytes of scales) as contiguous stores; stores of
+// 8-byte pieces straight from the waves run at half the speed.
 // ------------------------------------------------------------------------------------------------------------
-constexpr int kColRB = 16;                     // row-blocks per workgroup
-constexpr int kColSteps = 1;                   // row-blocks per wave
-constexpr int kColThreads = 64 * kColRB / kColSteps;   // 256
+constexpr int kColRB = 16;                     // row-blocks per workgroup (one per wave)
+constexpr int kColThreads = 64 * kColRB;       // 1024
 constexpr int kColPad = 17;                    // LDS row length (entries) per (column j, lane): 16 row-blocks + 1
+constexpr int kEarlyRng = 2;                   // blocks whose random words are generated before the data arrive
 
 struct ColStage {
     uint2 codes[8 * 64 * kColPad];             // [j][lane][row-block]: 8 codes bytes per block
@@ -432,44 +475,38 @@ struct ColGrid {
     uint32_t nstrips;  // strips of 512 columns
 };
 
-__device__ __forceinline__ void col_position(const ColGrid& g, uint32_t& group, uint32_t& strip, uint32_t& rb0,
-                                             uint32_t& c8) {
-    group = blockIdx.x / g.nstrips;
-    strip = blockIdx.x - group * g.nstrips;
-    rb0 = group * kColRB + (threadIdx.x >> 6) * kColSteps;   // first row-block of this wave
-    c8 = strip * 512 + 8 * (threadIdx.x & 63u);
+struct ColPos {
+    uint32_t group;  // row group (16 row-blocks)
+    uint32_t strip;  // 512-column strip
+    uint32_t rb;     // this wave's row-block
+    uint32_t lane;
+    uint32_t c8;     // first of the lane's 8 columns
+};
+
+__device__ __forceinline__ ColPos col_position(const ColGrid& g) {
+    ColPos p;
+    p.group = blockIdx.x / g.nstrips;
+    const uint32_t s = blockIdx.x - p.group * g.nstrips + p.group % g.nstrips;
+    p.strip = s >= g.nstrips ? s - g.nstrips : s;
+    p.rb = p.group * kColRB + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    p.lane = threadIdx.x & 63u;
+    p.c8 = p.strip * 512 + 8 * p.lane;
+    return p;
 }
 
-__device__ __forceinline__ void load_col_tile(const uint16_t* x, uint32_t cols, uint32_t rb, uint32_t c8,
-                                              uint4 (&v)[16]) {
-    const uint16_t* src = x + (size_t)(16 * rb) * cols + c8;
+// Issues the 16 loads of the lane's 16 x 8 tile (cols is a multiple of 8: a lane's columns exist all or none).  The
+// loads go through a buffer resource over the wave's 16 rows (a wave-uniform base): the lane offset is one 32-bit
+// register and the row offset a scalar, where 64-bit addresses would take two registers per load in flight.  The
+// row-block spans 32 cols bytes, below 2^32 by the column-wise size limit.
+__device__ __forceinline__ void load_col_tile(const uint16_t* x, uint32_t cols, const ColPos& p, uint4 (&v)[16]) {
+    const uint16_t* base = x + (size_t)(16 * p.rb) * cols;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, (int)(32u * cols), 0x00020000);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) v[k] = ld16(src + (size_t)k * cols);
-}
-
-// Calls body(v, step, rb) for the wave's row-blocks rb0 .. rb0+kColSteps-1 that exist, with the next one's loads
-// issued before the current one is processed (two register sets used alternately).
-template <typename Body>
-__device__ __forceinline__ void col_steps(const uint16_t* x, uint32_t cols, uint32_t nrb, uint32_t rb0, uint32_t c8,
-                                          Body body) {
-    if (c8 >= cols || rb0 >= nrb) return;
-    if constexpr (kColSteps == 1) {
-        uint4 v[16];
-        load_col_tile(x, cols, rb0, c8, v);
-        body(v, 0u, rb0);
-        return;
-    }
-    const uint32_t n = min((uint32_t)kColSteps, nrb - rb0);
-    uint4 va[16], vb[16];
-    load_col_tile(x, cols, rb0, c8, va);
-#pragma unroll
-    for (uint32_t s = 0; s < (uint32_t)kColSteps; s += 2) {
-        if (s >= n) break;
-        if (s + 1 < n) load_col_tile(x, cols, rb0 + s + 1, c8, vb);
-        body(va, s, rb0 + s);
-        if (s + 1 >= n) break;
-        if (s + 2 < n) load_col_tile(x, cols, rb0 + s + 2, c8, va);
-        body(vb, s + 1, rb0 + s + 1);
+    for (int k = 0; k < 16; ++k) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(2u * p.c8), (int)(2u * k * cols), 0);
+        v[k] = make_uint4(t.x, t.y, t.z, t.w);
     }
 }
 
@@ -479,18 +516,18 @@ __device__ __forceinline__ uint32_t stage_index(uint32_t j, uint32_t lane, uint3
 
 // Writes the staged codes/scales of the workgroup: (column, row-block) pairs with the row-block fastest, so 16
 // consecutive threads store one output row's 128 contiguous bytes of codes and 16 bytes of scales.
-__device__ __forceinline__ void col_write_out(const ColStage& st, uint32_t group, uint32_t strip, uint32_t rows,
-                                              uint32_t cols, uint32_t nrb, uint8_t* __restrict__ codes,
+__device__ __forceinline__ void col_write_out(const ColStage& st, const ColPos& p, uint32_t rows, uint32_t cols,
+                                              uint32_t nrb, uint8_t* __restrict__ codes,
                                               uint8_t* __restrict__ scales) {
-    const uint32_t ncol = min(512u, cols - strip * 512), nr = min((uint32_t)kColRB, nrb - group * kColRB);
-    for (uint32_t idx = threadIdx.x; idx < 512 * kColRB; idx += kColThreads) {
-        const uint32_t cl = idx / kColRB, rbl = idx % kColRB;
-        if (cl < ncol && rbl < nr) {
-            const uint32_t si = stage_index(cl & 7, cl >> 3, rbl);
-            const uint32_t c = strip * 512 + cl, rb = group * kColRB + rbl;
-            *reinterpret_cast<uint2*>(codes + (size_t)c * (rows >> 1) + 8 * (size_t)rb) = st.codes[si];
-            scales[(size_t)c * nrb + rb] = st.scales[si];
-        }
+    const uint32_t col0 = p.strip * 512;
+    const uint32_t ncol = min(512u, cols - col0), nr = min((uint32_t)kColRB, nrb - p.group * kColRB);
+    const uint32_t rbl = threadIdx.x % kColRB, rb = p.group * kColRB + rbl;
+    if (rbl >= nr) return;
+    for (uint32_t cl = threadIdx.x / kColRB; cl < ncol; cl += kColThreads / kColRB) {
+        const uint32_t si = stage_index(cl & 7, cl >> 3, rbl);
+        const uint32_t c = col0 + cl;
+        *reinterpret_cast<uint2*>(codes + (size_t)c * (rows >> 1) + 8 * (size_t)rb) = st.codes[si];
+        scales[(size_t)c * nrb + rb] = st.scales[si];
     }
 }
 
@@ -503,45 +540,58 @@ k_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, Co
     constexpr bool RHT = MODE == kRHTSR;
     __shared__ ColStage st;
     __shared__ RTable tab;
-    float g = 0.0f, d6 = 0.0f;
+    float g = 0.0f;
+    Divisor d6{};
     if (!PER_ROW) {
         g = global_scale(amax[0]);
-        d6 = 6.0f * g;
+        d6 = make_divisor(6.0f * g);
         if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
         fill_rtable(tab, g);
     }
-    uint32_t group, strip, rb0, c8;
-    col_position(cg, group, strip, rb0, c8);
-    const uint32_t lane = threadIdx.x & 63u;
-    col_steps(x, cols, cg.nrb, rb0, c8, [&](const uint4 (&v)[16], uint32_t step, uint32_t rb) {
-        const uint32_t rbl = rb - group * kColRB;
+    const ColPos pos = col_position(cg);
+    if (pos.rb < cg.nrb && pos.c8 < cols) {
+        uint4 v[16];
+        load_col_tile(x, cols, pos, v);
+        // Random words of the first blocks, generated while the loads are in flight (they do not depend on the
+        // data); the empty asm keeps the compiler from sinking them behind the wait for the loads.  More would not
+        // fit in the registers next to the tile.
+        Rand4 inv[8];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            float wp[2][16];
-            widen_col_pair<RHT>(v, p, sign_mask, wp[0], wp[1]);
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const uint32_t j = 2 * p + t, c = c8 + j;
-                Rand4 inv{{0, 0, 0, 0}};
-                if (SR) inv = block_rand_inv(rng, (uint64_t)c * cg.nrb + rb);
-                uint32_t lo, hi, sb;
-                if (PER_ROW) {
-                    const float gr = global_scale(amax[c]);
-                    if (rb == 0) gout[c] = gr;
-                    quantize_block<SR, RHT>(wp[t], 6.0f * gr, [&](uint32_t sc) { return scale_multiplier(sc, gr); },
-                                            inv, lo, hi, sb);
-                } else {
-                    quantize_block<SR, RHT>(wp[t], d6, [&](uint32_t sc) { return tab.r[sc]; }, inv, lo, hi, sb);
-                }
-                const uint32_t si = stage_index(j, lane, rbl);
-                st.codes[si] = make_uint2(lo, hi);
-                st.scales[si] = (uint8_t)sb;
+        for (int j = 0; j < kEarlyRng; ++j) {
+            inv[j] = Rand4{{0, 0, 0, 0}};
+            if (SR) {
+                inv[j] = block_rand_inv(rng, (uint64_t)(pos.c8 + j) * cg.nrb + pos.rb);
+                asm volatile("" : "+v"(inv[j].w[0]), "+v"(inv[j].w[1]), "+v"(inv[j].w[2]), "+v"(inv[j].w[3]));
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        (void)step;
-    });
+        const uint32_t rbl = pos.rb - pos.group * kColRB;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t c = pos.c8 + j;
+            if (j >= kEarlyRng) {
+                inv[j] = Rand4{{0, 0, 0, 0}};
+                if (SR) inv[j] = block_rand_inv(rng, (uint64_t)c * cg.nrb + pos.rb);
+            }
+            float w[16];
+            widen_col_block<RHT>(v, j, sign_mask, w);
+            uint32_t lo, hi, sb;
+            if (PER_ROW) {
+                const float gr = global_scale(amax[c]);
+                if (pos.rb == 0) gout[c] = gr;
+                quantize_block<SR, RHT>(w, make_divisor(6.0f * gr),
+                                        [&](uint32_t sc) { return scale_multiplier(sc, gr); }, inv[j], lo, hi, sb);
+            } else {
+                quantize_block<SR, RHT>(w, d6, [&](uint32_t sc) { return tab.r[sc]; }, inv[j], lo, hi, sb);
+            }
+            const uint32_t si = stage_index(j, pos.lane, rbl);
+            st.codes[si] = make_uint2(lo, hi);
+            st.scales[si] = (uint8_t)sb;
+            if (j & 1) __builtin_amdgcn_sched_barrier(0);   // two blocks at a time bounds the live registers
+        }
+    }
     __syncthreads();
-    col_write_out(st, group, strip, rows, cols, cg.nrb, codes, scales);
+    col_write_out(st, pos, rows, cols, cg.nrb, codes, scales);
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -560,67 +610,105 @@ k_quant_16x16(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColG
     __shared__ ColStage st;
     __shared__ RTable tab;
     const float g = global_scale(amax[0]);
-    const float d6 = 6.0f * g;
+    const Divisor d6 = make_divisor(6.0f * g);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         if (WANT_W) gw[0] = g;
         if (WANT_WT) gt[0] = g;
     }
     fill_rtable(tab, g);
-    uint32_t group, strip, ti0, c8;
-    col_position(cg, group, strip, ti0, c8);
-    const uint32_t lane = threadIdx.x & 63u, h = lane & 1u;
+    const ColPos pos = col_position(cg);
+    const uint32_t lane = pos.lane, h = lane & 1u, c8 = pos.c8, ti = pos.rb;
     const uint32_t ntc = cols >> 4, tj = c8 >> 4;
-    col_steps(x, cols, cg.nrb, ti0, c8, [&](const uint4 (&v)[16], uint32_t, uint32_t ti) {
-        float m = 0.0f;
+    // lanes of a pair own the two halves of one tile, so both exist or neither (cols is a multiple of 16)
+    if (ti < cg.nrb && c8 < cols) {
+        uint4 v[16];
+        load_col_tile(x, cols, pos, v);
+        // Maximum magnitude of the lane's 128 inputs on the bf16 bit patterns (packed 16-bit integer maxima of
+        // the magnitude bits: NaN > inf > finite, as for the binary32 values they widen to exactly).
+        u16x2 mb = {0, 0};
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             const uint32_t ws[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
-            for (int q = 0; q < 4; q += 2)
-                m = absmax3(absmax3(m, bf16_lo(ws[q], 0u), bf16_hi(ws[q], 0u)), bf16_lo(ws[q + 1], 0u),
-                            bf16_hi(ws[q + 1], 0u));
+            for (int q = 0; q < 4; ++q) mb = __builtin_elementwise_max(mb, __builtin_bit_cast(u16x2, ws[q] & 0x7FFF7FFFu));
         }
+        float m = as_f((uint32_t)(mb.x > mb.y ? mb.x : mb.y) << 16);
         m = __builtin_elementwise_maximum(m, __shfl_xor(m, 1));
         const uint32_t sb = scale_code(m, d6);
         const float r = tab.r[sb];
         const bool fast = r > 0.0f && r <= kFltMax;
-        uint32_t wt[8][2];
+        // Every product is converted once and packed both ways: column pair (2p, 2p+1) gives byte p of every W row
+        // and the two W^T column blocks 2p, 2p+1.
+        uint32_t rowc[16];
+        const uint32_t rbl = ti - pos.group * kColRB;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const uint32_t ws[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-            float q[8];
+        for (int p = 0; p < 4; ++p) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) q[j] = ((j & 1) ? bf16_hi(ws[j >> 1], 0u) : bf16_lo(ws[j >> 1], 0u)) * r;
-            uint32_t rowc = pack8_rn(q);
-            if (!fast) rowc = patch_nan8(rowc, q);
-            if (WANT_W)
-                *reinterpret_cast<uint32_t*>(cw_codes + (size_t)(16 * ti + k) * (cols >> 1) + (c8 >> 1)) = rowc;
+            for (int half = 0; half < 2; ++half) {   // rows 8 half .. 8 half + 7
+                float qa[8], qb[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint4& row = v[8 * half + i];
+                    const uint32_t word = p == 0 ? row.x : p == 1 ? row.y : p == 2 ? row.z : row.w;
+                    qa[i] = bf16_lo(word, 0u) * r;
+                    qb[i] = bf16_hi(word, 0u) * r;
+                }
+                if (WANT_W) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        rowc[8 * half + i] = cvt_fp4_byte(p, p == 0 ? 0u : rowc[8 * half + i], qa[i], qb[i]);
+                }
+                if (WANT_WT) {
+                    uint32_t* ca = reinterpret_cast<uint32_t*>(&st.codes[stage_index(2 * p, lane, rbl)]);
+                    uint32_t* cb = reinterpret_cast<uint32_t*>(&st.codes[stage_index(2 * p + 1, lane, rbl)]);
+                    ca[half] = pack8_rn(qa);
+                    cb[half] = pack8_rn(qb);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (WANT_WT) {
+                st.scales[stage_index(2 * p, lane, rbl)] = (uint8_t)sb;
+                st.scales[stage_index(2 * p + 1, lane, rbl)] = (uint8_t)sb;
+            }
+        }
+        if (!fast) [[unlikely]] {
+            // NaN multiplier (NaN amax) or a degenerate scale: NaN products get code 0x7.  The tile is read again
+            // so that the registers of the common path can be released as it goes.
+            load_col_tile(x, cols, pos, v);
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const uint32_t ws[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+                float q[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) q[j] = ((j & 1) ? bf16_hi(ws[j >> 1], 0u) : bf16_lo(ws[j >> 1], 0u)) * r;
+                if (WANT_W) rowc[k] = patch_nan8(rowc[k], q);
+            }
             if (WANT_WT) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const uint32_t code = (rowc >> (4 * j)) & 0xFu;
-                    if ((k & 7) == 0) wt[j][k >> 3] = code;
-                    else wt[j][k >> 3] |= code << (4 * (k & 7));
+                    float w[16];
+                    widen_col_block<false>(v, j, 0u, w);
+                    float q[16];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) q[i] = w[i] * r;
+                    const uint32_t si = stage_index(j, lane, rbl);
+                    const uint2 c = st.codes[si];
+                    st.codes[si] = make_uint2(patch_nan8(c.x, *reinterpret_cast<const float(*)[8]>(&q[0])),
+                                              patch_nan8(c.y, *reinterpret_cast<const float(*)[8]>(&q[8])));
                 }
             }
         }
         if (WANT_W) {
 #pragma unroll
+            for (int k = 0; k < 16; ++k)
+                *reinterpret_cast<uint32_t*>(cw_codes + (size_t)(16 * ti + k) * (cols >> 1) + (c8 >> 1)) = rowc[k];
+#pragma unroll
             for (int k = 0; k < 8; ++k) sw[(size_t)(16 * ti + 8 * h + k) * ntc + tj] = (uint8_t)sb;
         }
-        if (WANT_WT) {
-            const uint32_t rbl = ti - group * kColRB;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t si = stage_index(j, lane, rbl);
-                st.codes[si] = make_uint2(wt[j][0], wt[j][1]);
-                st.scales[si] = (uint8_t)sb;
-            }
-        }
-    });
+    }
     if (WANT_WT) {
         __syncthreads();
-        col_write_out(st, group, strip, rows, cols, cg.nrb, ct, st_scales);
+        col_write_out(st, pos, rows, cols, cg.nrb, ct, st_scales);
     }
 }
 
@@ -643,9 +731,12 @@ __global__ void __launch_bounds__(kThreads)
 k_quant_4o6(const uint4* __restrict__ x, uint32_t total_blocks, FastDiv per_row, const float* __restrict__ amax,
             uint2* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gout) {
     float g = 0.0f;
+    Divisor dv[2] = {};   // T = 6 and T = 4
     if (!PER_ROW) {
         g = global_scale(amax[0]);
         if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
+        dv[0] = make_divisor(6.0f * g);
+        dv[1] = make_divisor(4.0f * g);
     }
     const uint32_t stride = gridDim.x * kThreads;
     uint32_t n = blockIdx.x * kThreads + threadIdx.x;
@@ -662,17 +753,17 @@ k_quant_4o6(const uint4* __restrict__ x, uint32_t total_blocks, FastDiv per_row,
             const uint32_t row = fdiv(n, per_row);
             g = global_scale(amax[row]);
             if (n == row * per_row.d) gout[row] = g;
+            dv[0] = make_divisor(6.0f * g);
+            dv[1] = make_divisor(4.0f * g);
         }
         float xv[16];
         widen_row_block<false>(a, b, 0u, xv);
-        float m = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) m = absmax3(m, xv[i], xv[i + 1]);
+        const float m = absmax16(xv);
         uint32_t cand_lo[2], cand_hi[2], cand_sb[2];
         float err[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const uint32_t sb = scale_code(m, (c == 0 ? 6.0f : 4.0f) * g);
+            const uint32_t sb = scale_code(m, dv[c]);
             const float r = scale_multiplier(sb, g);
             const bool fast = r > 0.0f && r <= kFltMax;
             float q[16];
@@ -723,7 +814,7 @@ k_dequantize(const uint2* __restrict__ codes, const uint8_t* __restrict__ scales
     for (uint32_t n = blockIdx.x * kThreads + threadIdx.x; n < total_blocks; n += stride) {
         const float gr = PER_ROW ? g[fdiv(n, per_row)] : g[0];
         const uint32_t s = scales[n];
-        const float sbf = (s & 0x80u) ? -e4m3_decode(s & 0x7Fu) : e4m3_decode(s & 0x7Fu);
+        const float sbf = e4m3_decode(s);
         const uint2 c = codes[n];
         float v[16];
         unpack8(c.x, *reinterpret_cast<float(*)[8]>(&v[0]));
@@ -782,9 +873,7 @@ template <bool RHT>
 __device__ __forceinline__ uint32_t rowblock_absmax(const uint4& a, const uint4& b, uint32_t mask) {
     float w[16];
     widen_row_block<RHT>(a, b, mask, w);
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) m = absmax3(m, w[i], w[i + 1]);
+    const float m = absmax16(w);
     return as_u(RHT ? 0.25f * m : m) & 0x7FFFFFFFu;
 }
 
@@ -839,33 +928,29 @@ k_amax_colwise(const uint16_t* __restrict__ x, uint32_t cols, ColGrid cg, uint32
                uint32_t* __restrict__ amax_bits) {
     constexpr int kWaves = kColThreads / 64;
     __shared__ uint32_t colmax_lds[PER_ROW ? 512 * kWaves : kWaves];
-    uint32_t group, strip, rb0, c8;
-    col_position(cg, group, strip, rb0, c8);
-    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    const ColPos pos = col_position(cg);
+    const uint32_t wave = threadIdx.x >> 6;
     float cm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    col_steps(x, cols, cg.nrb, rb0, c8, [&](const uint4 (&v)[16], uint32_t, uint32_t) {
+    if (pos.rb < cg.nrb && pos.c8 < cols) {
+        uint4 v[16];
+        load_col_tile(x, cols, pos, v);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             float wp[2][16];
             widen_col_pair<RHT>(v, p, sign_mask, wp[0], wp[1]);
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                float m = cm[2 * p + t];
-#pragma unroll
-                for (int k = 0; k < 16; k += 2) m = absmax3(m, wp[t][k], wp[t][k + 1]);
-                cm[2 * p + t] = m;
-            }
+            for (int t = 0; t < 2; ++t) cm[2 * p + t] = absmax16(wp[t]);
         }
-    });
+    }
     uint32_t cb[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) cb[j] = as_u(RHT ? 0.25f * cm[j] : cm[j]) & 0x7FFFFFFFu;
     if (PER_ROW) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) colmax_lds[(8 * lane + j) * kWaves + wave] = cb[j];
+        for (int j = 0; j < 8; ++j) colmax_lds[(8 * pos.lane + j) * kWaves + wave] = cb[j];
         __syncthreads();
         for (uint32_t cl = threadIdx.x; cl < 512; cl += kColThreads) {
-            const uint32_t c = strip * 512 + cl;
+            const uint32_t c = pos.strip * 512 + cl;
             uint32_t m = 0;
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) m = umax(m, colmax_lds[cl * kWaves + w]);
