@@ -40,7 +40,7 @@
  *   - Alignment: x, codes, scales and y must be 16-byte aligned; amax and g 4-byte aligned.
  *   - Sizes: rows, cols >= 0; rows * cols < 2^36.  A zero-sized tensor is valid: its amax is 0 and a quantize
  *     call only writes g.
- *   - Calls on different streams may run concurrently; they share no state.
+ *   - Calls on different streams may run concurrently; they share no state (nvfp4_amax_quantize excepted: see it).
  */
 #ifndef NVFP4_H
 #define NVFP4_H
@@ -63,6 +63,7 @@ typedef enum {
 typedef enum { NVFP4_ROWWISE = 1, NVFP4_COLWISE = 2, NVFP4_BOTH = 3 } nvfp4_orient;
 typedef enum { NVFP4_BLOCK_1X16 = 0, NVFP4_BLOCK_16X16 = 1 } nvfp4_block;
 typedef enum { NVFP4_G_PER_TENSOR = 0, NVFP4_G_PER_ROW = 1 } nvfp4_gmode;
+typedef enum { NVFP4_ROUND_RN = 0, NVFP4_ROUND_SR = 1, NVFP4_ROUND_RHT_SR = 2 } nvfp4_rounding;
 
 typedef struct {
     uint8_t* codes;  /* [Rv, Cv/2] */
@@ -112,6 +113,21 @@ nvfp4_status nvfp4_quantize_sr(const uint16_t* x, int64_t rows, int64_t cols, nv
 nvfp4_status nvfp4_quantize_rht_sr(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_orient orient,
                                    nvfp4_gmode gmode, const float* amax, uint16_t sign_mask, uint64_t seed,
                                    uint64_t offset, const nvfp4_out* out, void* stream);
+
+/* The amax pass and a 1x16 quantization with a per-tensor g in one call ([P2, results: amax and quantization
+ * with no host round trip]).  The result equals nvfp4_amax (per tensor, use_rht = rounding is RHT_SR) followed by
+ * nvfp4_quantize_rn / _sr / _rht_sr with the same arguments, and amax[0] is written too.
+ *   A column-wise tensor of at most one 256-row x 512-column tile per CU (8192 x 4096 on MI355X) is read from
+ *   memory once: a single cooperative launch keeps each tile in registers across a grid-wide barrier on the
+ *   amax.  Other shapes (and row-wise) run the two passes.  The single-read launch uses one barrier per GPU, whose
+ *   state resets itself between launches: calls of this entry point must not overlap on one GPU (consecutive
+ *   calls on a stream are fine).  If the launch could not hold every workgroup resident the barrier gives up
+ *   after about half a second and the call writes NaN scales instead of hanging.
+ *   rounding: NVFP4_ROUND_RN, _SR or _RHT_SR; sign_mask is used with RHT, seed and offset with SR.
+ *   amax: [1] device float (output).  Shapes and outputs as for the quantize calls. */
+nvfp4_status nvfp4_amax_quantize(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_orient orient,
+                                 nvfp4_rounding rounding, uint16_t sign_mask, uint64_t seed, uint64_t offset,
+                                 float* amax, const nvfp4_out* out, void* stream);
 
 /* Four-over-six quantization ([P3]): row-wise 1x16 blocks, round-to-nearest, no RHT.  Each block is encoded with
  * T = 6 and with T = 4 (scale bamax / fl(4 g), 1.5x the map-to-6 scale); both are decoded as

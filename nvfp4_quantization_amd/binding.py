@@ -18,6 +18,7 @@ from ._build import LIB_PATH
 ROWWISE, COLWISE, BOTH = 1, 2, 3
 BLOCK_1X16, BLOCK_16X16 = 0, 1
 G_PER_TENSOR, G_PER_ROW = 0, 1
+ROUND_RN, ROUND_SR, ROUND_RHT_SR = 0, 1, 2
 
 STATUS = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_SHAPE", 3: "NVFP4_ERR_ALIGN",
           4: "NVFP4_ERR_UNSUPPORTED", 5: "NVFP4_ERR_HIP"}
@@ -29,6 +30,7 @@ SIGNATURES = {
     "nvfp4_quantize_rn": (_I, [_P, _I64, _I64, _I, _I, _I, _P, _P, _P, _P]),
     "nvfp4_quantize_sr": (_I, [_P, _I64, _I64, _I, _I, _P, _U64, _U64, _P, _P]),
     "nvfp4_quantize_rht_sr": (_I, [_P, _I64, _I64, _I, _I, _P, _U16, _U64, _U64, _P, _P]),
+    "nvfp4_amax_quantize": (_I, [_P, _I64, _I64, _I, _I, _U16, _U64, _U64, _P, _P, _P]),
     "nvfp4_quantize_4o6": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
     "nvfp4_dequantize": (_I, [_P, _P, _P, _I64, _I64, _I, _P, _P]),
     "nvfp4_status_str": (C.c_char_p, [_I]),
@@ -158,6 +160,20 @@ def nvfp4_quantize_rht_sr(x: torch.Tensor, amax: torch.Tensor, sign_mask: int, s
     _check(lib().nvfp4_quantize_rht_sr(_bf16(x), rows, cols, orient, gmode, _dev(amax, "amax"), sign_mask & 0xFFFF,
                                        seed, offset, _out(out), _stream(x.device, stream)), "nvfp4_quantize_rht_sr")
     return out
+
+
+def nvfp4_amax_quantize(x: torch.Tensor, orient: int, rounding: int, sign_mask: int = 0, seed: int = 0,
+                        offset: int = 0, amax: Optional[torch.Tensor] = None, out: Optional[Quantized] = None,
+                        stream=None) -> tuple[torch.Tensor, Quantized]:
+    """amax and 1x16 quantization with a per-tensor g in one call; returns (amax, out)."""
+    rows, cols = x.shape
+    if amax is None:
+        amax = torch.empty((1,), dtype=torch.float32, device=x.device)
+    if out is None:
+        out = alloc_out(*view_shape(rows, cols, orient), G_PER_TENSOR, x.device)
+    _check(lib().nvfp4_amax_quantize(_bf16(x), rows, cols, orient, rounding, sign_mask & 0xFFFF, seed, offset,
+                                     _dev(amax, "amax"), _out(out), _stream(x.device, stream)), "nvfp4_amax_quantize")
+    return amax, out
 
 
 def nvfp4_quantize_4o6(x: torch.Tensor, amax: torch.Tensor, gmode: int = G_PER_ROW,

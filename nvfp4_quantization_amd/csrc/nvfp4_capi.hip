@@ -133,6 +133,23 @@ nvfp4_status nvfp4_quantize_rht_sr(const uint16_t* x, int64_t rows, int64_t cols
     return quantize_1x16(x, rows, cols, orient, gmode, amax, nvfp4::kRHTSR, sign_mask, seed, offset, out, stream);
 }
 
+nvfp4_status nvfp4_amax_quantize(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_orient orient,
+                                 nvfp4_rounding rounding, uint16_t sign_mask, uint64_t seed, uint64_t offset,
+                                 float* amax, const nvfp4_out* out, void* stream) {
+    if (rounding != NVFP4_ROUND_RN && rounding != NVFP4_ROUND_SR && rounding != NVFP4_ROUND_RHT_SR)
+        return NVFP4_ERR_UNSUPPORTED;
+    NVFP4_TRY(check_sizes(rows, cols));
+    NVFP4_TRY(check_view(rows, cols, orient));
+    const int64_t rv = view_rows(rows, cols, orient), cv = orient == NVFP4_COLWISE ? rows : cols;
+    NVFP4_TRY(check_input(x, rows, cols, amax, 1));
+    NVFP4_TRY(check_out(out, rv, cv, NVFP4_G_PER_TENSOR));
+    const nvfp4::Mode mode = rounding == NVFP4_ROUND_RN ? nvfp4::kRN : rounding == NVFP4_ROUND_SR ? nvfp4::kSR
+                                                                                                  : nvfp4::kRHTSR;
+    return done(nvfp4::launch_amax_quant(x, rows, cols, orient == NVFP4_COLWISE, mode, sign_mask,
+                                         nvfp4::Philox{seed, offset}, amax, out->codes, out->scales, out->g,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 nvfp4_status nvfp4_quantize_4o6(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_gmode gmode,
                                 const float* amax, const nvfp4_out* out, void* stream) {
     NVFP4_TRY(check_sizes(rows, cols));

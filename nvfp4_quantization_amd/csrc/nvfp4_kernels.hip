@@ -29,6 +29,7 @@
 #include "nvfp4_launch.h"
 
 
+
 namespace nvfp4 {
 namespace {
 
@@ -184,6 +185,27 @@ __device__ __forceinline__ float absmax16(const float (&w)[16]) {
     return __builtin_elementwise_maximum(m5, m6);
 }
 
+// Maxima over a wave / workgroup of magnitude bit patterns (integer maximum: NaN > inf > finite).
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = umax(v, (uint32_t)__shfl_xor((int)v, off));
+    return v;
+}
+
+template <int WAVES = kWavesPerGroup>
+__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* lds) {
+    v = wave_max(v);
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    if (lane == 0) lds[wave] = v;
+    __syncthreads();
+    uint32_t r = 0;
+    if (threadIdx.x == 0) {
+        for (int w = 0; w < WAVES; ++w) r = umax(r, lds[w]);
+    }
+    __syncthreads();
+    return r;  // valid in thread 0
+}
+
 // Per-tensor g: the 128 possible multipliers are tabulated once per workgroup in LDS.
 struct RTable {
     float r[128];
@@ -277,10 +299,10 @@ __device__ __forceinline__ void encode16(const float (&q)[16], const Rand4& inv,
 // 2^-124 <= r < 2^117, where fl(fl(0.25 w) r) and fl(w fl(0.25 r)) give the same code for every w (they are equal
 // when 0.25 w is exact, and both are below 2^-9 -- code 0 with the sign of w -- when it is not).
 template <bool SR, bool RHT, typename ROf>
-__device__ __forceinline__ bool quantize_block_fast(const float (&w)[16], const Divisor& d6, ROf r_of,
+__device__ __forceinline__ bool quantize_block_fast(const float (&w)[16], float m, const Divisor& d6, ROf r_of,
                                                     const Rand4& inv, uint32_t& lo, uint32_t& hi, uint32_t& sb,
                                                     float& r) {
-    const float m = absmax16(w);
+    // m = absmax16(w)
     const float bamax = RHT ? 0.25f * m : m;       // max_i fl(0.25 |w_i|) = fl(0.25 max_i |w_i|)
     sb = scale_code(bamax, d6);
     r = r_of(sb);
@@ -304,12 +326,19 @@ __device__ __forceinline__ void quantize_block_general(const float (&w)[16], flo
     hi = patch_nan8(hi, *reinterpret_cast<const float(*)[8]>(&q[8]));
 }
 
+// m is the block's absmax16(w), when the caller has it already.
+template <bool SR, bool RHT, typename ROf>
+__device__ __forceinline__ void quantize_block_m(const float (&w)[16], float m, const Divisor& d6, ROf r_of,
+                                                 const Rand4& inv, uint32_t& lo, uint32_t& hi, uint32_t& sb) {
+    float r;
+    if (!quantize_block_fast<SR, RHT>(w, m, d6, r_of, inv, lo, hi, sb, r)) [[unlikely]]
+        quantize_block_general<SR, RHT>(w, r, inv, lo, hi);
+}
+
 template <bool SR, bool RHT, typename ROf>
 __device__ __forceinline__ void quantize_block(const float (&w)[16], const Divisor& d6, ROf r_of, const Rand4& inv,
                                                uint32_t& lo, uint32_t& hi, uint32_t& sb) {
-    float r;
-    if (!quantize_block_fast<SR, RHT>(w, d6, r_of, inv, lo, hi, sb, r)) [[unlikely]]
-        quantize_block_general<SR, RHT>(w, r, inv, lo, hi);
+    quantize_block_m<SR, RHT>(w, absmax16(w), d6, r_of, inv, lo, hi, sb);
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -595,6 +624,154 @@ k_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, Co
 }
 
 // ------------------------------------------------------------------------------------------------------------
+// Single-read amax + column-wise 1x16 quantization of a tensor that the chip can hold: every workgroup keeps its
+// tile in registers, publishes its tile maximum in a slot of its own, waits until every workgroup has published,
+// reduces the slots to the tensor amax and quantizes the tile it still holds.  The tensor is read from HBM once
+// instead of twice.
+//   The wait needs every workgroup resident (one per CU, grid <= CUs).  It is bounded: a workgroup that has not
+// seen every slot filled within kWaitTicks (other work holding CUs) computes the amax by reading the whole tensor
+// itself, so the result is the same in every case, only slower.  Slots are zero between launches: each workgroup
+// clears its own slot as its last action (every other workgroup has read it by then, or has given up waiting and
+// taken the slow route), so no counter has to be shared or reset.  Launches that overlap on one GPU share the
+// slots and must not.
+// ------------------------------------------------------------------------------------------------------------
+constexpr uint32_t kFusedMaxGrid = 2048;
+constexpr uint64_t kWaitTicks = 5000000;        // 50 ms of the 100 MHz wall clock
+
+__device__ uint64_t g_fused_slot[kFusedMaxGrid];   // 0, or (1 << 32) | tile maximum (magnitude bits)
+
+// Tensor amax of the column-wise view computed by one workgroup (the route taken after a timed-out wait); v is
+// used as scratch.  Valid in thread 0.
+template <bool RHT>
+__device__ uint32_t wg_amax_colwise(const uint16_t* x, uint32_t cols, const ColGrid& cg, uint32_t sign_mask,
+                                    uint4 (&v)[16], uint32_t* red) {
+    uint32_t m = 0;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t units = cg.nrb * cg.nstrips;   // (row-block, strip) pairs
+    for (uint32_t u = wave; u < units; u += kColRB) {
+        ColPos p;
+        p.rb = u / cg.nstrips;
+        p.strip = u - p.rb * cg.nstrips;
+        p.group = p.rb / kColRB;
+        p.lane = threadIdx.x & 63u;
+        p.c8 = p.strip * 512 + 8 * p.lane;
+        if (p.c8 < cols) {
+            load_col_tile(x, cols, p, v);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float wp[2][16];
+                widen_col_pair<RHT>(v, q, sign_mask, wp[0], wp[1]);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const float bmax = absmax16(wp[t]);
+                    m = umax(m, as_u(RHT ? 0.25f * bmax : bmax) & 0x7FFFFFFFu);
+                }
+            }
+        }
+    }
+    return block_max<kColRB>(m, red);
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(kColThreads)
+k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColGrid cg, uint32_t sign_mask,
+                     RngArgs rng, float* __restrict__ amax_out, uint8_t* __restrict__ codes,
+                     uint8_t* __restrict__ scales, float* __restrict__ gout) {
+    constexpr bool SR = MODE != kRN;
+    constexpr bool RHT = MODE == kRHTSR;
+    __shared__ ColStage st;
+    __shared__ RTable tab;
+    __shared__ uint32_t red[kColRB];
+    const ColPos pos = col_position(cg);
+    const uint32_t wave = threadIdx.x >> 6;
+    const bool active = pos.rb < cg.nrb && pos.c8 < cols;
+    uint4 v[16];
+    float bm[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // block maxima of the transformed (RHT) or plain values
+    uint32_t mbits = 0;
+    if (active) {
+        load_col_tile(x, cols, pos, v);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            float wp[2][16];
+            widen_col_pair<RHT>(v, p, sign_mask, wp[0], wp[1]);
+            bm[2 * p] = absmax16(wp[0]);
+            bm[2 * p + 1] = absmax16(wp[1]);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mbits = umax(mbits, as_u(RHT ? 0.25f * bm[j] : bm[j]) & 0x7FFFFFFFu);
+    }
+    // the tile stays in registers: keep the compiler from carrying the widened values over the wait instead
+#pragma unroll
+    for (int k = 0; k < 16; ++k) asm volatile("" : "+v"(v[k].x), "+v"(v[k].y), "+v"(v[k].z), "+v"(v[k].w));
+    mbits = wave_max(mbits);
+    if ((threadIdx.x & 63u) == 0) red[wave] = mbits;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t m = 0;
+        for (int w = 0; w < kColRB; ++w) m = umax(m, red[w]);
+        __hip_atomic_store(&g_fused_slot[blockIdx.x], (1ull << 32) | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // wait for every slot (thread i watches slots i, i + 1024, ...) and reduce them
+    uint32_t m = 0;
+    bool waited_out = false;
+    const uint64_t t0 = wall_clock64();
+    for (uint32_t i = threadIdx.x; i < gridDim.x && !waited_out; i += kColThreads) {
+        uint64_t sv;
+        while ((sv = __hip_atomic_load(&g_fused_slot[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
+            if (wall_clock64() - t0 > kWaitTicks) {
+                waited_out = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        m = umax(m, (uint32_t)sv);
+    }
+    __shared__ uint32_t s_out;
+    if (threadIdx.x == 0) s_out = 0;
+    __syncthreads();
+    if (waited_out) s_out = 1;
+    m = block_max<kColRB>(m, red);
+    __shared__ float s_amax;
+    if (threadIdx.x == 0) s_amax = as_f(m);
+    __syncthreads();
+    if (s_out) {
+        // slow route: the whole tensor's amax from this workgroup alone, then the tile again
+        const uint32_t mm = wg_amax_colwise<RHT>(x, cols, cg, sign_mask, v, red);
+        if (threadIdx.x == 0) s_amax = as_f(mm);
+        if (active) load_col_tile(x, cols, pos, v);
+        __syncthreads();
+    }
+    const float amax = s_amax;
+    const float g = global_scale(amax);
+    const Divisor d6 = make_divisor(6.0f * g);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        amax_out[0] = amax;
+        gout[0] = g;
+    }
+    fill_rtable(tab, g);
+    if (active) {
+        const uint32_t rbl = pos.rb - pos.group * kColRB;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t c = pos.c8 + j;
+            Rand4 inv{{0, 0, 0, 0}};
+            if (SR) inv = block_rand_inv(rng, (uint64_t)c * cg.nrb + pos.rb);
+            float w[16];
+            widen_col_block<RHT>(v, j, sign_mask, w);
+            uint32_t lo, hi, sb;
+            quantize_block_m<SR, RHT>(w, bm[j], d6, [&](uint32_t sc) { return tab.r[sc]; }, inv, lo, hi, sb);
+            const uint32_t si = stage_index(j, pos.lane, rbl);
+            st.codes[si] = make_uint2(lo, hi);
+            st.scales[si] = (uint8_t)sb;
+            if (j & 1) __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    __syncthreads();
+    col_write_out(st, pos, rows, cols, cg.nrb, codes, scales);
+    if (threadIdx.x == 0) __hip_atomic_store(&g_fused_slot[blockIdx.x], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------------------------------------------------------
 // 16x16 RN quantization, W and/or W^T from one read ([P2, intro: 2D weight scaling; results: both weight
 // orientations]).  Same workgroup layout as the column-wise kernels (a step is one tile-row of 16 rows, lane = 8
 // columns); lane pair (2m, 2m+1) holds the two halves of a 16x16 tile, whose amax is the max over the pair (both
@@ -830,26 +1007,6 @@ k_dequantize(const uint2* __restrict__ codes, const uint8_t* __restrict__ scales
 // amax kernels.  The maximum of magnitudes with NaN dominating (v_maximum3); reductions combine the binary32 bit
 // patterns with an integer maximum, which orders NaN > inf > finite for magnitudes.
 // ------------------------------------------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = umax(v, (uint32_t)__shfl_xor((int)v, off));
-    return v;
-}
-
-template <int WAVES = kWavesPerGroup>
-__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* lds) {
-    v = wave_max(v);
-    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
-    if (lane == 0) lds[wave] = v;
-    __syncthreads();
-    uint32_t r = 0;
-    if (threadIdx.x == 0) {
-        for (int w = 0; w < WAVES; ++w) r = umax(r, lds[w]);
-    }
-    __syncthreads();
-    return r;  // valid in thread 0
-}
-
 __global__ void k_fill_zero(uint32_t* __restrict__ p, uint32_t n) {
     for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < n; i += gridDim.x * kThreads) p[i] = 0u;
 }
@@ -1079,6 +1236,29 @@ hipError_t launch_quant_1x16(const uint16_t* x, int64_t rows, int64_t cols, bool
 #undef NVFP4_COL
     }
     return hipGetLastError();
+}
+
+hipError_t launch_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, bool colwise, Mode mode, uint32_t sign_mask,
+                             Philox rng, float* amax, uint8_t* codes, uint8_t* scales, float* g, hipStream_t stream) {
+    if (rows > 0 && cols > 0 && colwise) {
+        uint32_t grid;
+        const ColGrid w = col_grid(rows, cols, grid);
+        // one 1024-thread workgroup per CU (the registers allow no second one), all resident at once
+        if (grid <= (uint32_t)cu_count() && grid <= kFusedMaxGrid) {
+            uint32_t r = (uint32_t)rows, c = (uint32_t)cols;
+            RngArgs ra = rng_args(rng);
+            void* args[] = {(void*)&x, &r, &c, (void*)&w, &sign_mask, &ra, (void*)&amax, (void*)&codes, (void*)&scales,
+                            (void*)&g};
+            const void* fn = mode == kRN ? (const void*)k_amax_quant_colwise<kRN>
+                             : mode == kSR ? (const void*)k_amax_quant_colwise<kSR>
+                                           : (const void*)k_amax_quant_colwise<kRHTSR>;
+            return hipLaunchKernel(fn, dim3(grid), dim3(kColThreads), args, 0, stream);
+        }
+    }
+    // two passes over the tensor: amax, then quantization
+    const hipError_t e = launch_amax(x, rows, cols, colwise, false, mode == kRHTSR, sign_mask, amax, stream);
+    if (e != hipSuccess) return e;
+    return launch_quant_1x16(x, rows, cols, colwise, false, mode, amax, sign_mask, rng, codes, scales, g, stream);
 }
 
 hipError_t launch_quant_16x16(const uint16_t* x, int64_t rows, int64_t cols, const float* amax, uint8_t* codes_w,

@@ -24,6 +24,11 @@ hipError_t launch_quant_1x16(const uint16_t* x, int64_t rows, int64_t cols, bool
                              const float* amax, uint32_t sign_mask, Philox rng, uint8_t* codes, uint8_t* scales,
                              float* g, hipStream_t stream);
 
+// amax and 1x16 quantization of V with a per-tensor g: one read of X when the column-wise tensor fits the chip
+// (cooperative launch), else the two launches above.
+hipError_t launch_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, bool colwise, Mode mode, uint32_t sign_mask,
+                             Philox rng, float* amax, uint8_t* codes, uint8_t* scales, float* g, hipStream_t stream);
+
 // 16x16 RN quantization; either output (codes == nullptr) may be skipped.
 hipError_t launch_quant_16x16(const uint16_t* x, int64_t rows, int64_t cols, const float* amax, uint8_t* codes_w,
                               uint8_t* scales_w, float* g_w, uint8_t* codes_wt, uint8_t* scales_wt, float* g_wt,

@@ -33,8 +33,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["nvfp4_amax", "nvfp4_quantize_rn", "nvfp4_quantize_sr",
-                                           "nvfp4_quantize_rht_sr", "nvfp4_quantize_4o6", "nvfp4_dequantize",
-                                           "nvfp4_status_str"])
+                                           "nvfp4_quantize_rht_sr", "nvfp4_amax_quantize", "nvfp4_quantize_4o6",
+                                           "nvfp4_dequantize", "nvfp4_status_str"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -89,6 +89,18 @@ def test_quantize_sr_and_rht_sr_validation(lib):
         assert f(P, 16, 16, 1, 0, None, *extra, 1, 2, out(), None) == NULL
         assert f(P, 16, 16, 1, 0, P, *extra, 1, 2, None, None) == NULL
         assert f(P, 16, 16, 1, 2, P, *extra, 1, 2, out(), None) == UNSUP
+
+
+def test_amax_quantize_validation(lib):
+    f = lib.nvfp4_amax_quantize
+    assert f(P, 16, 16, 2, 3, 0, 1, 2, P, out(), None) == UNSUP       # unknown rounding
+    assert f(P, 16, 16, 3, 0, 0, 1, 2, P, out(), None) == UNSUP       # BOTH
+    assert f(P, 24, 16, 2, 2, 0, 1, 2, P, out(), None) == SHAPE       # column-wise rows % 16
+    assert f(P, 16, 24, 1, 0, 0, 1, 2, P, out(), None) == SHAPE       # row-wise cols % 16
+    assert f(P, 16, 16, 2, 2, 0, 1, 2, None, out(), None) == NULL     # amax is an output here
+    assert f(P, 16, 16, 2, 2, 0, 1, 2, P + 2, out(), None) == ALIGN
+    assert f(P, 16, 16, 2, 2, 0, 1, 2, P, None, None) == NULL
+    assert f(MIS, 16, 16, 2, 2, 0, 1, 2, P, out(), None) == ALIGN
 
 
 def test_4o6_and_dequantize_validation(lib):

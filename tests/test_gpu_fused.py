@@ -1,0 +1,112 @@
+"""GPU parity of nvfp4_amax_quantize (amax and 1x16 quantization in one call) against the CPU oracle.
+
+Column-wise tensors of at most one 256 x 512 tile per CU take the single-read cooperative launch (the tile stays
+in registers across a grid-wide barrier); larger or row-wise ones take the two-pass path.  Bar: amax, g, codes and
+scales bit-exact, as for the separate calls.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import nvfp4_quantization_amd as Q
+from nvfp4_quantization_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+ROUNDING = {"rn": (Q.ROUND_RN, O.MODE_RN), "sr": (Q.ROUND_SR, O.MODE_SR), "rht_sr": (Q.ROUND_RHT_SR, O.MODE_RHT_SR)}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    Q.binding.lib()
+    O.lib()
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def check(x, mode, orient, mask=0x5A3C, seed=0xDEAD_BEEF_0123, offset=3, out=None, amax=None):
+    say("amax_quantize", mode, "row" if orient == Q.ROWWISE else "col", x.shape, hex(mask), offset)
+    xd = torch.from_numpy(x.view(np.int16)).cuda()
+    a, o = Q.nvfp4_amax_quantize(xd, orient, ROUNDING[mode][0], mask, seed, offset, amax=amax, out=out)
+    torch.cuda.synchronize()
+    oa = O.amax(x, orient, O.G_PER_TENSOR, mode == "rht_sr", mask)
+    oc, os_, og = O.quantize_1x16(x, oa, ROUNDING[mode][1], orient, O.G_PER_TENSOR, mask, seed, offset)
+    ga = a.cpu().numpy()
+    assert (ga.view(np.uint32) == oa.view(np.uint32)).all() or (np.isnan(ga).all() and np.isnan(oa).all())
+    assert np.array_equal(o.codes.cpu().numpy(), oc), "codes"
+    assert np.array_equal(o.scales.cpu().numpy(), os_), "scales"
+    g = o.g.cpu().numpy()
+    assert (g.view(np.uint32) == og.view(np.uint32)).all() or (np.isnan(g).all() and np.isnan(og).all())
+
+
+@pytest.mark.parametrize("mode", ["rn", "sr", "rht_sr"])
+@pytest.mark.parametrize("shape", [(512, 200), (48, 8), (1040, 72), (16, 520), (2048, 1024), (4096, 1032)])
+def test_colwise(mode, shape):
+    x = W.lognormal_gradients(*shape, seed=(shape[0] * 5 + shape[1]) & 0xFFFF)
+    check(x, mode, Q.COLWISE)
+
+
+@pytest.mark.parametrize("mode", ["rn", "rht_sr"])
+def test_rowwise_two_pass(mode):
+    check(W.outlier_columns(300, 160, seed=4, n_cols=3), mode, Q.ROWWISE)
+
+
+def test_consecutive_calls_reuse_the_barrier():
+    """Back-to-back launches on one stream: every call sees only its own workgroups at the barrier."""
+    x = W.lognormal_gradients(1024, 2048, seed=77)
+    for call in range(6):
+        check(x, "rht_sr", Q.COLWISE, mask=W.sign_mask(9, call), seed=9, offset=call)
+
+
+def test_nan_and_zero_tensors():
+    x = W.lognormal_gradients(256, 512, seed=5)
+    x[100, 7] = 0x7FC0                      # bf16 NaN
+    check(x, "rht_sr", Q.COLWISE)
+    check(np.zeros((256, 512), np.uint16), "sr", Q.COLWISE)
+
+
+def test_empty_tensor():
+    xd = torch.empty((0, 64), dtype=torch.int16, device="cuda")
+    a, o = Q.nvfp4_amax_quantize(xd, Q.COLWISE, Q.ROUND_RHT_SR, 0x1111, 1, 2)
+    torch.cuda.synchronize()
+    assert a.item() == 0.0 and o.g.item() == 0.0
+
+
+@pytest.mark.slow
+def test_full_wgrad_colwise_single_read():
+    """The benchmarked workload (8192 x 4096: one tile per CU) through the single-read launch, two fresh calls."""
+    x = W.make("wgrad_colwise_rht_sr_8192x4096")
+    for call in (0, 1):
+        check(x, "rht_sr", Q.COLWISE, mask=W.sign_mask(2, call), seed=2, offset=call)
+
+
+def test_graph_replays_match_eager():
+    """The call captured in a HIP graph; replays (with eager work between them) match the eager result."""
+    x = W.lognormal_gradients(2048, 1024, seed=31)
+    xd = torch.from_numpy(x.view(np.int16)).cuda()
+    a_e, o_e = Q.nvfp4_amax_quantize(xd, Q.COLWISE, Q.ROUND_RHT_SR, 0x0F0F, 3, 4)
+    torch.cuda.synchronize()
+    a_g = torch.full((1,), 7.0, device="cuda")
+    o_g = Q.alloc_out(1024, 2048, 0, xd.device)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        Q.nvfp4_amax_quantize(xd, Q.COLWISE, Q.ROUND_RHT_SR, 0x0F0F, 3, 4, amax=a_g, out=o_g)
+    for rep in range(4):
+        say("graph replay", rep)
+        a_g.fill_(1e30)
+        o_g.codes.zero_()
+        Q.nvfp4_amax_quantize(xd, Q.COLWISE, Q.ROUND_RN, 0, 0, 0)      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(a_g.view(torch.int32), a_e.view(torch.int32))
+        assert torch.equal(o_g.codes, o_e.codes) and torch.equal(o_g.scales, o_e.scales)
+        assert torch.equal(o_g.g, o_e.g)
