@@ -492,7 +492,6 @@ k_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, FastDiv per_
 constexpr int kColRB = 16;                     // row-blocks per workgroup (one per wave)
 constexpr int kColThreads = 64 * kColRB;       // 1024
 constexpr int kColPad = 17;                    // LDS row length (entries) per (column j, lane): 16 row-blocks + 1
-constexpr int kEarlyRng = 2;                   // blocks whose random words are generated before the data arrive
 
 struct ColStage {
     uint2 codes[8 * 64 * kColPad];             // [j][lane][row-block]: 8 codes bytes per block
@@ -560,6 +559,30 @@ __device__ __forceinline__ void col_write_out(const ColStage& st, const ColPos& 
     }
 }
 
+// LDS of a column-wise workgroup that generates every block's random words ahead of the data: entry (wave, j,
+// lane) first holds the four Philox words of the lane's block j, then that block's codes (x, y) and scale (z).  A
+// wave's region is padded by one entry so that the write-out, which reads the 16 row-blocks (= waves) of one
+// column, hits 16 different bank groups.
+struct ColStash {
+    uint4 e[kColRB][8 * 64 + 1];
+};
+
+// Writes the codes/scales held in a ColStash, as col_write_out.
+__device__ __forceinline__ void col_write_out_stash(const ColStash& st, const ColPos& p, uint32_t rows,
+                                                    uint32_t cols, uint32_t nrb, uint8_t* __restrict__ codes,
+                                                    uint8_t* __restrict__ scales) {
+    const uint32_t col0 = p.strip * 512;
+    const uint32_t ncol = min(512u, cols - col0), nr = min((uint32_t)kColRB, nrb - p.group * kColRB);
+    const uint32_t rbl = threadIdx.x % kColRB, rb = p.group * kColRB + rbl;
+    if (rbl >= nr) return;
+    for (uint32_t cl = threadIdx.x / kColRB; cl < ncol; cl += kColThreads / kColRB) {
+        const uint4 e = st.e[rbl][(cl & 7) * 64 + (cl >> 3)];
+        const uint32_t c = col0 + cl;
+        *reinterpret_cast<uint2*>(codes + (size_t)c * (rows >> 1) + 8 * (size_t)rb) = make_uint2(e.x, e.y);
+        scales[(size_t)c * nrb + rb] = (uint8_t)e.z;
+    }
+}
+
 template <int MODE, bool PER_ROW>
 __global__ void __launch_bounds__(kColThreads)
 k_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColGrid cg,
@@ -567,7 +590,7 @@ k_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, Co
                 uint8_t* __restrict__ scales, float* __restrict__ gout) {
     constexpr bool SR = MODE != kRN;
     constexpr bool RHT = MODE == kRHTSR;
-    __shared__ ColStage st;
+    __shared__ ColStash st;
     __shared__ RTable tab;
     float g = 0.0f;
     Divisor d6{};
@@ -578,49 +601,45 @@ k_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, Co
         fill_rtable(tab, g);
     }
     const ColPos pos = col_position(cg);
+    const uint32_t wave = threadIdx.x >> 6;
     if (pos.rb < cg.nrb && pos.c8 < cols) {
         uint4 v[16];
         load_col_tile(x, cols, pos, v);
-        // Random words of the first blocks, generated while the loads are in flight (they do not depend on the
-        // data); the empty asm keeps the compiler from sinking them behind the wait for the loads.  More would not
-        // fit in the registers next to the tile.
-        Rand4 inv[8];
+        // The random words do not depend on the data: they are generated while the loads are in flight and parked
+        // in LDS (registers are full with the tile).
+        if (SR) {
 #pragma unroll
-        for (int j = 0; j < kEarlyRng; ++j) {
-            inv[j] = Rand4{{0, 0, 0, 0}};
-            if (SR) {
-                inv[j] = block_rand_inv(rng, (uint64_t)(pos.c8 + j) * cg.nrb + pos.rb);
-                asm volatile("" : "+v"(inv[j].w[0]), "+v"(inv[j].w[1]), "+v"(inv[j].w[2]), "+v"(inv[j].w[3]));
-                __builtin_amdgcn_sched_barrier(0);
+            for (int j = 0; j < 8; ++j) {
+                const Rand4 r = block_rand_inv(rng, (uint64_t)(pos.c8 + j) * cg.nrb + pos.rb);
+                st.e[wave][j * 64 + pos.lane] = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
             }
         }
-        const uint32_t rbl = pos.rb - pos.group * kColRB;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const uint32_t c = pos.c8 + j;
-            if (j >= kEarlyRng) {
-                inv[j] = Rand4{{0, 0, 0, 0}};
-                if (SR) inv[j] = block_rand_inv(rng, (uint64_t)c * cg.nrb + pos.rb);
+            uint4& slot = st.e[wave][j * 64 + pos.lane];
+            Rand4 inv{{0, 0, 0, 0}};
+            if (SR) {
+                const uint4 r = slot;
+                inv = Rand4{{r.x, r.y, r.z, r.w}};
             }
             float w[16];
             widen_col_block<RHT>(v, j, sign_mask, w);
             uint32_t lo, hi, sb;
             if (PER_ROW) {
+                const uint32_t c = pos.c8 + j;
                 const float gr = global_scale(amax[c]);
                 if (pos.rb == 0) gout[c] = gr;
                 quantize_block<SR, RHT>(w, make_divisor(6.0f * gr),
-                                        [&](uint32_t sc) { return scale_multiplier(sc, gr); }, inv[j], lo, hi, sb);
+                                        [&](uint32_t sc) { return scale_multiplier(sc, gr); }, inv, lo, hi, sb);
             } else {
-                quantize_block<SR, RHT>(w, d6, [&](uint32_t sc) { return tab.r[sc]; }, inv[j], lo, hi, sb);
+                quantize_block<SR, RHT>(w, d6, [&](uint32_t sc) { return tab.r[sc]; }, inv, lo, hi, sb);
             }
-            const uint32_t si = stage_index(j, pos.lane, rbl);
-            st.codes[si] = make_uint2(lo, hi);
-            st.scales[si] = (uint8_t)sb;
+            slot = make_uint4(lo, hi, sb, 0u);
             if (j & 1) __builtin_amdgcn_sched_barrier(0);   // two blocks at a time bounds the live registers
         }
     }
     __syncthreads();
-    col_write_out(st, pos, rows, cols, cg.nrb, codes, scales);
+    col_write_out_stash(st, pos, rows, cols, cg.nrb, codes, scales);
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -679,7 +698,7 @@ k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t col
                      uint8_t* __restrict__ scales, float* __restrict__ gout) {
     constexpr bool SR = MODE != kRN;
     constexpr bool RHT = MODE == kRHTSR;
-    __shared__ ColStage st;
+    __shared__ ColStash st;
     __shared__ RTable tab;
     __shared__ uint32_t red[kColRB];
     const ColPos pos = col_position(cg);
@@ -690,6 +709,14 @@ k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t col
     uint32_t mbits = 0;
     if (active) {
         load_col_tile(x, cols, pos, v);
+        // the random words of the 8 blocks, generated while the loads are in flight, parked in LDS
+        if (SR) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const Rand4 r = block_rand_inv(rng, (uint64_t)(pos.c8 + j) * cg.nrb + pos.rb);
+                st.e[wave][j * 64 + pos.lane] = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
+            }
+        }
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             float wp[2][16];
@@ -750,24 +777,24 @@ k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t col
     }
     fill_rtable(tab, g);
     if (active) {
-        const uint32_t rbl = pos.rb - pos.group * kColRB;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const uint32_t c = pos.c8 + j;
+            uint4& slot = st.e[wave][j * 64 + pos.lane];
             Rand4 inv{{0, 0, 0, 0}};
-            if (SR) inv = block_rand_inv(rng, (uint64_t)c * cg.nrb + pos.rb);
+            if (SR) {
+                const uint4 r = slot;
+                inv = Rand4{{r.x, r.y, r.z, r.w}};
+            }
             float w[16];
             widen_col_block<RHT>(v, j, sign_mask, w);
             uint32_t lo, hi, sb;
             quantize_block_m<SR, RHT>(w, bm[j], d6, [&](uint32_t sc) { return tab.r[sc]; }, inv, lo, hi, sb);
-            const uint32_t si = stage_index(j, pos.lane, rbl);
-            st.codes[si] = make_uint2(lo, hi);
-            st.scales[si] = (uint8_t)sb;
+            slot = make_uint4(lo, hi, sb, 0u);
             if (j & 1) __builtin_amdgcn_sched_barrier(0);
         }
     }
     __syncthreads();
-    col_write_out(st, pos, rows, cols, cg.nrb, codes, scales);
+    col_write_out_stash(st, pos, rows, cols, cg.nrb, codes, scales);
     if (threadIdx.x == 0) __hip_atomic_store(&g_fused_slot[blockIdx.x], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
