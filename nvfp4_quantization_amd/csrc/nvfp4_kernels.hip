@@ -242,12 +242,20 @@ __device__ __forceinline__ uint32_t pack8_rn(const float (&q)[8]) {
 // random byte from seed bits 31..24, the second slot from bits 30..23 (the instruction shifts the seed left by one
 // for it).  Element 2k uses seed (255 - rho) << 24 and keeps the low nibble; element 2k+1 uses (255 - rho) << 23
 // and keeps the high nibble; the other nibble of each conversion is discarded by the final bit-select.
-__device__ __forceinline__ uint32_t seed_first(uint32_t inv_word, int byte) {   // byte 0 or 2
-    return (inv_word << (24 - 8 * byte)) & 0xFF000000u;
-}
-__device__ __forceinline__ uint32_t seed_second(uint32_t inv_word, int byte) {  // byte 1 or 3
-    return ((inv_word >> (8 * byte)) & 0xFFu) << 23;
-}
+// Byte b of w shifted left by 24 (first slot) or 23 (second slot), the other bits zero: one SDWA shift each.
+#define NVFP4_SEED(name, SHIFT, SEL)                                                                        \
+    __device__ __forceinline__ uint32_t name(uint32_t w) {                                                  \
+        uint32_t r;                                                                                         \
+        asm("v_lshlrev_b32_sdwa %0, " #SHIFT ", %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD "     \
+            "src1_sel:" SEL                                                                                 \
+            : "=v"(r) : "v"(w));                                                                            \
+        return r;                                                                                           \
+    }
+NVFP4_SEED(seed_first_b0, 24, "BYTE_0")
+NVFP4_SEED(seed_first_b2, 24, "BYTE_2")
+NVFP4_SEED(seed_second_b1, 23, "BYTE_1")
+NVFP4_SEED(seed_second_b3, 23, "BYTE_3")
+#undef NVFP4_SEED
 
 // The byte-select chain needs the accumulator tied to the destination (each conversion writes one byte and keeps
 // the other three); the compiler's lowering of the SR conversion builtin does not carry that operand, so the
@@ -256,20 +264,26 @@ __device__ __forceinline__ uint32_t seed_second(uint32_t inv_word, int byte) {  
     asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 " OPSEL                             \
         : "+v"(acc)                                                                       \
         : "v"(f32x2{q[2 * (k)], q[2 * (k) + 1]}), "v"(seed))
+// the first conversion of a chain: the bytes it keeps are all overwritten later, so no initial value is needed
+#define NVFP4_SR_FIRST(acc, seed)                                                         \
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0"                                    \
+        : "=v"(acc)                                                                       \
+        : "v"(f32x2{q[0], q[1]}), "v"(seed))
 
 __device__ __forceinline__ uint32_t pack8_sr(const float (&q)[8], uint32_t inv_lo, uint32_t inv_hi) {
     // inv_lo holds the complemented random bytes of elements 0..3, inv_hi of elements 4..7
-    uint32_t e = 0, o = 0;
-    NVFP4_SR_PAIR(e, 0, seed_first(inv_lo, 0), "");
-    NVFP4_SR_PAIR(o, 0, seed_second(inv_lo, 1), "");
-    NVFP4_SR_PAIR(e, 1, seed_first(inv_lo, 2), "op_sel:[0,0,1,0]");
-    NVFP4_SR_PAIR(o, 1, seed_second(inv_lo, 3), "op_sel:[0,0,1,0]");
-    NVFP4_SR_PAIR(e, 2, seed_first(inv_hi, 0), "op_sel:[0,0,0,1]");
-    NVFP4_SR_PAIR(o, 2, seed_second(inv_hi, 1), "op_sel:[0,0,0,1]");
-    NVFP4_SR_PAIR(e, 3, seed_first(inv_hi, 2), "op_sel:[0,0,1,1]");
-    NVFP4_SR_PAIR(o, 3, seed_second(inv_hi, 3), "op_sel:[0,0,1,1]");
+    uint32_t e, o;
+    NVFP4_SR_FIRST(e, seed_first_b0(inv_lo));
+    NVFP4_SR_FIRST(o, seed_second_b1(inv_lo));
+    NVFP4_SR_PAIR(e, 1, seed_first_b2(inv_lo), "op_sel:[0,0,1,0]");
+    NVFP4_SR_PAIR(o, 1, seed_second_b3(inv_lo), "op_sel:[0,0,1,0]");
+    NVFP4_SR_PAIR(e, 2, seed_first_b0(inv_hi), "op_sel:[0,0,0,1]");
+    NVFP4_SR_PAIR(o, 2, seed_second_b1(inv_hi), "op_sel:[0,0,0,1]");
+    NVFP4_SR_PAIR(e, 3, seed_first_b2(inv_hi), "op_sel:[0,0,1,1]");
+    NVFP4_SR_PAIR(o, 3, seed_second_b3(inv_hi), "op_sel:[0,0,1,1]");
     return (e & 0x0F0F0F0Fu) | (o & 0xF0F0F0F0u);
 }
+#undef NVFP4_SR_FIRST
 #undef NVFP4_SR_PAIR
 
 // NaN elements encode to 0x7 (the hardware keeps the NaN's sign).
