@@ -529,6 +529,7 @@ struct ColStage {
 struct ColGrid {
     uint32_t nrb;      // row-blocks (rows / 16)
     uint32_t nstrips;  // strips of 512 columns
+    uint32_t ntiles;   // workgroup tiles: ceil(nrb / 16) * nstrips
 };
 
 struct ColPos {
@@ -539,10 +540,10 @@ struct ColPos {
     uint32_t c8;     // first of the lane's 8 columns
 };
 
-__device__ __forceinline__ ColPos col_position(const ColGrid& g) {
+__device__ __forceinline__ ColPos col_position(const ColGrid& g, uint32_t tile) {
     ColPos p;
-    p.group = blockIdx.x / g.nstrips;
-    const uint32_t s = blockIdx.x - p.group * g.nstrips + p.group % g.nstrips;
+    p.group = tile / g.nstrips;
+    const uint32_t s = tile - p.group * g.nstrips + p.group % g.nstrips;
     p.strip = s >= g.nstrips ? s - g.nstrips : s;
     p.rb = p.group * kColRB + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     p.lane = threadIdx.x & 63u;
@@ -628,7 +629,7 @@ k_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, Co
         if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
         fill_rtable(tab, g);
     }
-    const ColPos pos = col_position(cg);
+    const ColPos pos = col_position(cg, blockIdx.x);
     const uint32_t wave = threadIdx.x >> 6;
     if (pos.rb < cg.nrb && pos.c8 < cols) {
         uint4 v[16];
@@ -729,7 +730,7 @@ k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t col
     __shared__ ColStash st;
     __shared__ RTable tab;
     __shared__ uint32_t red[kColRB];
-    const ColPos pos = col_position(cg);
+    const ColPos pos = col_position(cg, blockIdx.x);
     const uint32_t wave = threadIdx.x >> 6;
     const bool active = pos.rb < cg.nrb && pos.c8 < cols;
     uint4 v[16];
@@ -848,13 +849,19 @@ k_quant_16x16(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColG
         if (WANT_WT) gt[0] = g;
     }
     fill_rtable(tab, g);
-    const ColPos pos = col_position(cg);
+    // Workgroups loop over the tiles (grid-stride); the next tile's loads are issued before the current tile's
+    // W^T write-out, so reading overlaps writing.  Lanes of a pair own the two halves of one 16x16 tile, so both
+    // exist or neither (cols is a multiple of 16).
+    const uint32_t ntc = cols >> 4;
+    uint32_t tile = blockIdx.x;
+    ColPos pos = col_position(cg, tile);
+    bool have = tile < cg.ntiles && pos.rb < cg.nrb && pos.c8 < cols;
+    uint4 v[16];
+    if (have) load_col_tile(x, cols, pos, v);
+    while (tile < cg.ntiles) {
     const uint32_t lane = pos.lane, h = lane & 1u, c8 = pos.c8, ti = pos.rb;
-    const uint32_t ntc = cols >> 4, tj = c8 >> 4;
-    // lanes of a pair own the two halves of one tile, so both exist or neither (cols is a multiple of 16)
-    if (ti < cg.nrb && c8 < cols) {
-        uint4 v[16];
-        load_col_tile(x, cols, pos, v);
+    const uint32_t tj = c8 >> 4;
+    if (have) {
         // Maximum magnitude of the lane's 128 inputs on the bf16 bit patterns (packed 16-bit integer maxima of
         // the magnitude bits: NaN > inf > finite, as for the binary32 values they widen to exactly).
         u16x2 mb = {0, 0};
@@ -938,9 +945,18 @@ k_quant_16x16(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColG
             for (int k = 0; k < 8; ++k) st_nt(sw + (size_t)(16 * ti + 8 * h + k) * ntc + tj, (uint8_t)sb);
         }
     }
+    const uint32_t next = tile + gridDim.x;
+    const ColPos npos = col_position(cg, next);
+    const bool nhave = next < cg.ntiles && npos.rb < cg.nrb && npos.c8 < cols;
+    if (nhave) load_col_tile(x, cols, npos, v);
     if (WANT_WT) {
         __syncthreads();
         col_write_out(st, pos, rows, cols, cg.nrb, ct, st_scales);
+        __syncthreads();
+    }
+    tile = next;
+    pos = npos;
+    have = nhave;
     }
 }
 
@@ -1138,7 +1154,7 @@ k_amax_colwise(const uint16_t* __restrict__ x, uint32_t cols, ColGrid cg, uint32
                uint32_t* __restrict__ amax_bits) {
     constexpr int kWaves = kColThreads / 64;
     __shared__ uint32_t colmax_lds[PER_ROW ? 512 * kWaves : kWaves];
-    const ColPos pos = col_position(cg);
+    const ColPos pos = col_position(cg, blockIdx.x);
     const uint32_t wave = threadIdx.x >> 6;
     float cm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (pos.rb < cg.nrb && pos.c8 < cols) {
@@ -1202,9 +1218,19 @@ ColGrid col_grid(int64_t rows, int64_t cols, uint32_t& grid) {
     ColGrid g;
     g.nrb = (uint32_t)(rows / 16);
     g.nstrips = (uint32_t)((cols + 511) / 512);
-    grid = ((g.nrb + kColRB - 1) / kColRB) * g.nstrips;
+    g.ntiles = ((g.nrb + kColRB - 1) / kColRB) * g.nstrips;
+    grid = g.ntiles;
     if (grid == 0) grid = 1;
     return g;
+}
+
+// Grid of a tile-looping column kernel: one 1024-thread workgroup per CU at most, and every workgroup the same
+// number of tiles (448 tiles on 256 CUs: 224 workgroups of 2 tiles rather than two rounds with a partial second).
+uint32_t looping_grid(uint32_t ntiles) {
+    const uint32_t cus = (uint32_t)cu_count();
+    if (ntiles <= cus) return ntiles ? ntiles : 1;
+    const uint32_t per = (ntiles + cus - 1) / cus;
+    return (ntiles + per - 1) / per;
 }
 
 RngArgs rng_args(Philox p) {
@@ -1325,6 +1351,7 @@ hipError_t launch_quant_16x16(const uint16_t* x, int64_t rows, int64_t cols, con
     }
     uint32_t grid;
     const ColGrid w = col_grid(rows, cols, grid);
+    grid = looping_grid(w.ntiles);
 #define NVFP4_2D(W, T)                                                                                          \
     k_quant_16x16<W, T><<<grid, kColThreads, 0, stream>>>(x, (uint32_t)rows, (uint32_t)cols, w, amax, codes_w, \
                                                           scales_w, g_w, codes_wt, scales_wt, g_wt)
