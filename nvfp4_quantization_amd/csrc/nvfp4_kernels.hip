@@ -25,6 +25,7 @@
 //   * No host synchronisation: the global scale is computed on the device from the amax buffer ([P2, results]).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "nvfp4_launch.h"
 
@@ -677,14 +678,14 @@ k_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, Co
 // reduces the slots to the tensor amax and quantizes the tile it still holds.  The tensor is read from HBM once
 // instead of twice.
 //   The wait needs every workgroup resident (one per CU, grid <= CUs).  It is bounded: a workgroup that has not
-// seen every slot filled within kWaitTicks (other work holding CUs) computes the amax by reading the whole tensor
+// seen every slot filled within a bound (50 ms; other work holding CUs) computes the amax by reading the whole tensor
 // itself, so the result is the same in every case, only slower.  Slots are zero between launches: each workgroup
 // clears its own slot as its last action (every other workgroup has read it by then, or has given up waiting and
 // taken the slow route), so no counter has to be shared or reset.  Launches that overlap on one GPU share the
 // slots and must not.
 // ------------------------------------------------------------------------------------------------------------
 constexpr uint32_t kFusedMaxGrid = 2048;
-constexpr uint64_t kWaitTicks = 5000000;        // 50 ms of the 100 MHz wall clock
+constexpr uint64_t kWaitTicks = 5000000;        // 50 ms of the 100 MHz wall clock (the kernel's wait bound)
 
 __device__ uint64_t g_fused_slot[kFusedMaxGrid];   // 0, or (1 << 32) | tile maximum (magnitude bits)
 
@@ -724,7 +725,7 @@ template <int MODE>
 __global__ void __launch_bounds__(kColThreads)
 k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColGrid cg, uint32_t sign_mask,
                      RngArgs rng, float* __restrict__ amax_out, uint8_t* __restrict__ codes,
-                     uint8_t* __restrict__ scales, float* __restrict__ gout) {
+                     uint8_t* __restrict__ scales, float* __restrict__ gout, uint64_t wait_ticks) {
     constexpr bool SR = MODE != kRN;
     constexpr bool RHT = MODE == kRHTSR;
     __shared__ ColStash st;
@@ -774,7 +775,7 @@ k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t col
     for (uint32_t i = threadIdx.x; i < gridDim.x && !waited_out; i += kColThreads) {
         uint64_t sv;
         while ((sv = __hip_atomic_load(&g_fused_slot[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
-            if (wall_clock64() - t0 > kWaitTicks) {
+            if (wall_clock64() - t0 >= wait_ticks) {
                 waited_out = true;
                 break;
             }
@@ -1317,6 +1318,14 @@ hipError_t launch_quant_1x16(const uint16_t* x, int64_t rows, int64_t cols, bool
     return hipGetLastError();
 }
 
+// The single-read kernel's wait bound.  NVFP4_FUSED_WAIT_TICKS (100 MHz ticks) overrides it; the tests set 0 to
+// send every workgroup down the slow route (whole-tensor amax per workgroup) and check that it agrees.
+uint64_t fused_wait_ticks() {
+    const char* e = getenv("NVFP4_FUSED_WAIT_TICKS");
+    if (!e || !*e) return kWaitTicks;
+    return strtoull(e, nullptr, 10);
+}
+
 hipError_t launch_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, bool colwise, Mode mode, uint32_t sign_mask,
                              Philox rng, float* amax, uint8_t* codes, uint8_t* scales, float* g, hipStream_t stream) {
     if (rows > 0 && cols > 0 && colwise) {
@@ -1326,8 +1335,9 @@ hipError_t launch_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, bool
         if (grid <= (uint32_t)cu_count() && grid <= kFusedMaxGrid) {
             uint32_t r = (uint32_t)rows, c = (uint32_t)cols;
             RngArgs ra = rng_args(rng);
+            uint64_t wait = fused_wait_ticks();
             void* args[] = {(void*)&x, &r, &c, (void*)&w, &sign_mask, &ra, (void*)&amax, (void*)&codes, (void*)&scales,
-                            (void*)&g};
+                            (void*)&g, &wait};
             const void* fn = mode == kRN ? (const void*)k_amax_quant_colwise<kRN>
                              : mode == kSR ? (const void*)k_amax_quant_colwise<kSR>
                                            : (const void*)k_amax_quant_colwise<kRHTSR>;

@@ -66,6 +66,18 @@ def test_consecutive_calls_reuse_the_barrier():
         check(x, "rht_sr", Q.COLWISE, mask=W.sign_mask(9, call), seed=9, offset=call)
 
 
+@pytest.mark.parametrize("mode", ["rn", "rht_sr"])
+def test_slow_route_after_a_timed_out_wait(monkeypatch, mode):
+    """A zero wait bound sends workgroups that find a slot still empty down the slow route (each computes the whole
+    tensor's amax itself); the result must not change."""
+    monkeypatch.setenv("NVFP4_FUSED_WAIT_TICKS", "0")
+    x = W.lognormal_gradients(2048, 1024, seed=91)
+    for call in range(3):
+        check(x, mode, Q.COLWISE, mask=W.sign_mask(4, call), seed=4, offset=call)
+    monkeypatch.delenv("NVFP4_FUSED_WAIT_TICKS")
+    check(x, mode, Q.COLWISE, mask=W.sign_mask(4, 7), seed=4, offset=7)     # and back on the fast route
+
+
 def test_nan_and_zero_tensors():
     x = W.lognormal_gradients(256, 512, seed=5)
     x[100, 7] = 0x7FC0                      # bf16 NaN
