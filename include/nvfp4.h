@@ -38,8 +38,8 @@
  *     non-zero nvfp4_status and enqueues nothing; there is no fallback path.  NVFP4_ERR_HIP reports a failed
  *     launch (the kernels may then not have run).
  *   - Alignment: x, codes, scales and y must be 16-byte aligned; amax and g 4-byte aligned.
- *   - Sizes: rows, cols >= 0; rows * cols < 2^36.  A zero-sized tensor is valid: its amax is 0 and a quantize
- *     call only writes g.
+ *   - Sizes: rows, cols >= 0; rows * cols < 2^35.  Column-wise views and 16x16 blocks also need cols < 2^26.
+ *     A zero-sized tensor is valid: its amax is 0 and a quantize call only writes g.
  *   - Calls on different streams may run concurrently; they share no state (nvfp4_amax_quantize excepted: see it).
  */
 #ifndef NVFP4_H
@@ -117,12 +117,13 @@ nvfp4_status nvfp4_quantize_rht_sr(const uint16_t* x, int64_t rows, int64_t cols
 /* The amax pass and a 1x16 quantization with a per-tensor g in one call ([P2, results: amax and quantization
  * with no host round trip]).  The result equals nvfp4_amax (per tensor, use_rht = rounding is RHT_SR) followed by
  * nvfp4_quantize_rn / _sr / _rht_sr with the same arguments, and amax[0] is written too.
- *   A column-wise tensor of at most one 256-row x 512-column tile per CU (8192 x 4096 on MI355X) is read from
- *   memory once: a single cooperative launch keeps each tile in registers across a grid-wide barrier on the
- *   amax.  Other shapes (and row-wise) run the two passes.  The single-read launch uses one barrier per GPU, whose
- *   state resets itself between launches: calls of this entry point must not overlap on one GPU (consecutive
- *   calls on a stream are fine).  If the launch could not hold every workgroup resident the barrier gives up
- *   after about half a second and the call writes NaN scales instead of hanging.
+ *   A tensor that fits one workgroup per CU is read from memory once: column-wise up to one 256-row x
+ *   512-column tile per CU, row-wise up to 8192 blocks per CU (8192 x 4096 either way on MI355X).  Each
+ *   workgroup keeps its share in registers, publishes its maximum in a per-GPU slot array and waits for every
+ *   other workgroup's; larger tensors run the two passes.  The slots reset themselves between launches: calls of
+ *   this entry point must not overlap on one GPU (consecutive calls on a stream are fine).  The wait is bounded
+ *   (50 ms): a workgroup that is still waiting then reads the whole tensor to compute the amax itself, so the
+ *   result never changes, only the time (this happens when other work holds CUs).
  *   rounding: NVFP4_ROUND_RN, _SR or _RHT_SR; sign_mask is used with RHT, seed and offset with SR.
  *   amax: [1] device float (output).  Shapes and outputs as for the quantize calls. */
 nvfp4_status nvfp4_amax_quantize(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_orient orient,

@@ -11,8 +11,11 @@
 
 namespace {
 
-// Kernels index 16-element blocks with 32-bit integers: at most 2^36 elements per tensor (128 GiB of bf16).
-constexpr int64_t kMaxElems = int64_t(1) << 36;
+// Kernels index 16-element blocks with 32-bit integers and add grid strides (< 2^22) to them: at most 2^35
+// elements per tensor (64 GiB of bf16) keeps every block index and index + stride below 2^32.
+constexpr int64_t kMaxElems = int64_t(1) << 35;
+// Column-wise kernels address a 16-row slab through a buffer resource of 32 * cols bytes (a 32-bit signed size).
+constexpr int64_t kMaxColwiseCols = int64_t(1) << 26;
 
 #define NVFP4_TRY(expr)                  \
     do {                                 \
@@ -32,7 +35,7 @@ nvfp4_status check_sizes(int64_t rows, int64_t cols) {
 // Shape rules of a 1x16 quantization (and of the amax that feeds it).
 nvfp4_status check_view(int64_t rows, int64_t cols, nvfp4_orient orient) {
     if (orient == NVFP4_ROWWISE) return (cols % 16) ? NVFP4_ERR_SHAPE : NVFP4_OK;
-    if (orient == NVFP4_COLWISE) return (rows % 16 || cols % 8) ? NVFP4_ERR_SHAPE : NVFP4_OK;
+    if (orient == NVFP4_COLWISE) return (rows % 16 || cols % 8 || cols >= kMaxColwiseCols) ? NVFP4_ERR_SHAPE : NVFP4_OK;
     return NVFP4_ERR_UNSUPPORTED;
 }
 
@@ -109,7 +112,7 @@ nvfp4_status nvfp4_quantize_rn(const uint16_t* x, int64_t rows, int64_t cols, nv
     NVFP4_TRY(check_gmode(gmode));
     if (gmode != NVFP4_G_PER_TENSOR) return NVFP4_ERR_UNSUPPORTED;
     if (orient != NVFP4_ROWWISE && orient != NVFP4_COLWISE && orient != NVFP4_BOTH) return NVFP4_ERR_UNSUPPORTED;
-    if (rows % 16 || cols % 16) return NVFP4_ERR_SHAPE;
+    if (rows % 16 || cols % 16 || cols >= kMaxColwiseCols) return NVFP4_ERR_SHAPE;
     NVFP4_TRY(check_input(x, rows, cols, amax, 1));
     const bool want_w = orient == NVFP4_ROWWISE || orient == NVFP4_BOTH;
     const bool want_wt = orient == NVFP4_COLWISE || orient == NVFP4_BOTH;

@@ -721,6 +721,57 @@ __device__ uint32_t wg_amax_colwise(const uint16_t* x, uint32_t cols, const ColG
     return block_max<kColRB>(m, red);
 }
 
+// The cross-workgroup step of the single-read kernels: the workgroup maximum of mbits (magnitude bits) goes to this
+// workgroup's slot, then the slots of every workgroup are read (thread i watches slots i, i + 1024, ...) and
+// reduced.  Returns the tensor maximum in every thread; slow (uniform) is set when some slot stayed empty past
+// wait_ticks, in which case the return value is not the tensor maximum.  Uses red[blockDim.x / 64].
+__device__ uint32_t exchange_max(uint32_t mbits, uint64_t wait_ticks, uint32_t* red, bool& slow) {
+    __shared__ uint32_t s_max, s_out;
+    mbits = wave_max(mbits);
+    if ((threadIdx.x & 63u) == 0) red[threadIdx.x >> 6] = mbits;
+    if (threadIdx.x == 0) s_out = 0;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t m = 0;
+        for (uint32_t w = 0; w < blockDim.x / 64; ++w) m = umax(m, red[w]);
+        __hip_atomic_store(&g_fused_slot[blockIdx.x], (1ull << 32) | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    uint32_t m = 0;
+    bool waited_out = false;
+    const uint64_t t0 = wall_clock64();
+    for (uint32_t i = threadIdx.x; i < gridDim.x && !waited_out; i += blockDim.x) {
+        uint64_t sv;
+        while ((sv = __hip_atomic_load(&g_fused_slot[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
+            if (wall_clock64() - t0 >= wait_ticks) {
+                waited_out = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        m = umax(m, (uint32_t)sv);
+    }
+    if (waited_out) s_out = 1;
+    m = wave_max(m);
+    __syncthreads();   // red is free again, s_out settled
+    if ((threadIdx.x & 63u) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = 0;
+        for (uint32_t w = 0; w < blockDim.x / 64; ++w) r = umax(r, red[w]);
+        s_max = r;
+    }
+    __syncthreads();
+    slow = s_out != 0;
+    return s_max;
+}
+
+// Clears this workgroup's slot: the last action of a single-read kernel (every other workgroup has read the slot by
+// then, or has given up waiting and taken the slow route).
+__device__ __forceinline__ void release_slot() {
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&g_fused_slot[blockIdx.x], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int MODE>
 __global__ void __launch_bounds__(kColThreads)
 k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColGrid cg, uint32_t sign_mask,
@@ -760,38 +811,12 @@ k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t col
     // the tile stays in registers: keep the compiler from carrying the widened values over the wait instead
 #pragma unroll
     for (int k = 0; k < 16; ++k) asm volatile("" : "+v"(v[k].x), "+v"(v[k].y), "+v"(v[k].z), "+v"(v[k].w));
-    mbits = wave_max(mbits);
-    if ((threadIdx.x & 63u) == 0) red[wave] = mbits;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t m = 0;
-        for (int w = 0; w < kColRB; ++w) m = umax(m, red[w]);
-        __hip_atomic_store(&g_fused_slot[blockIdx.x], (1ull << 32) | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    // wait for every slot (thread i watches slots i, i + 1024, ...) and reduce them
-    uint32_t m = 0;
-    bool waited_out = false;
-    const uint64_t t0 = wall_clock64();
-    for (uint32_t i = threadIdx.x; i < gridDim.x && !waited_out; i += kColThreads) {
-        uint64_t sv;
-        while ((sv = __hip_atomic_load(&g_fused_slot[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
-            if (wall_clock64() - t0 >= wait_ticks) {
-                waited_out = true;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
-        m = umax(m, (uint32_t)sv);
-    }
-    __shared__ uint32_t s_out;
-    if (threadIdx.x == 0) s_out = 0;
-    __syncthreads();
-    if (waited_out) s_out = 1;
-    m = block_max<kColRB>(m, red);
+    bool slow;
+    uint32_t abits = exchange_max(mbits, wait_ticks, red, slow);
     __shared__ float s_amax;
-    if (threadIdx.x == 0) s_amax = as_f(m);
+    if (threadIdx.x == 0) s_amax = as_f(abits);
     __syncthreads();
-    if (s_out) {
+    if (slow) {
         // slow route: the whole tensor's amax from this workgroup alone, then the tile again
         const uint32_t mm = wg_amax_colwise<RHT>(x, cols, cg, sign_mask, v, red);
         if (threadIdx.x == 0) s_amax = as_f(mm);
@@ -825,7 +850,7 @@ k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t col
     }
     __syncthreads();
     col_write_out_stash(st, pos, rows, cols, cg.nrb, codes, scales);
-    if (threadIdx.x == 0) __hip_atomic_store(&g_fused_slot[blockIdx.x], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    release_slot();
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -1104,29 +1129,31 @@ __device__ __forceinline__ uint32_t rowblock_absmax(const uint4& a, const uint4&
     return as_u(RHT ? 0.25f * m : m) & 0x7FFFFFFFu;
 }
 
-// Row-wise, per tensor: grid-stride over blocks, one atomic max per workgroup into a zeroed amax[0].
+// Row-wise, per tensor: one 1024-thread workgroup per CU; a lane takes 8 blocks a round (base + 1024 j + t) with
+// all 16 loads issued before the first is used; one atomic max per workgroup into a zeroed amax[0].
+constexpr uint32_t kRowAmaxPerLane = 8;
+
 template <bool RHT>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kColThreads)
 k_amax_rowwise_tensor(const uint4* __restrict__ x, uint32_t total_blocks, uint32_t sign_mask, uint32_t* amax_bits) {
-    __shared__ uint32_t lds[kWavesPerGroup];
+    __shared__ uint32_t red[kColRB];
+    constexpr uint32_t kPer = kRowAmaxPerLane * kColThreads;   // blocks per workgroup round
     uint32_t m = 0;
-    const uint32_t stride = gridDim.x * kThreads;
-    uint32_t n = blockIdx.x * kThreads + threadIdx.x;
-    if (n < total_blocks) {
-        uint4 a = ld16(x + 2 * (size_t)n), b = ld16(x + 2 * (size_t)n + 1);
-        for (; n < total_blocks; n += stride) {
-            const uint32_t nn = n + stride;
-            uint4 a2 = a, b2 = b;
-            if (nn < total_blocks) {
-                a2 = ld16(x + 2 * (size_t)nn);
-                b2 = ld16(x + 2 * (size_t)nn + 1);
+    for (uint32_t base = blockIdx.x * kPer + threadIdx.x; base < total_blocks; base += gridDim.x * kPer) {
+        uint4 a[kRowAmaxPerLane], b[kRowAmaxPerLane];
+#pragma unroll
+        for (uint32_t j = 0; j < kRowAmaxPerLane; ++j) {
+            const uint32_t n = base + j * kColThreads;
+            a[j] = b[j] = make_uint4(0, 0, 0, 0);   // blocks past the end count as zeros
+            if (n < total_blocks) {
+                a[j] = ld16(x + 2 * (size_t)n);
+                b[j] = ld16(x + 2 * (size_t)n + 1);
             }
-            m = umax(m, rowblock_absmax<RHT>(a, b, sign_mask));
-            a = a2;
-            b = b2;
         }
+#pragma unroll
+        for (uint32_t j = 0; j < kRowAmaxPerLane; ++j) m = umax(m, rowblock_absmax<RHT>(a[j], b[j], sign_mask));
     }
-    m = block_max(m, lds);
+    m = block_max<kColRB>(m, red);
     if (threadIdx.x == 0) publish_max(amax_bits, m);
 }
 
@@ -1190,6 +1217,103 @@ k_amax_colwise(const uint16_t* __restrict__ x, uint32_t cols, ColGrid cg, uint32
         m = block_max<kWaves>(m, colmax_lds);
         if (threadIdx.x == 0) publish_max(amax_bits, m);
     }
+}
+
+// ------------------------------------------------------------------------------------------------------------
+// Single-read amax + row-wise 1x16 quantization (same exchange as the column-wise single-read kernel).  A
+// workgroup owns bpl * 1024 consecutive blocks (bpl <= 8 per lane), lane t of the workgroup blocks base + 1024 j + t,
+// so every load instruction of a wave covers 2 KiB of the tensor with its partner; the tile is held in registers
+// across the wait and the codes and scales are stored straight from the lanes.
+// ------------------------------------------------------------------------------------------------------------
+constexpr uint32_t kRowFusedPerLane = 8;
+
+template <int MODE>
+__global__ void __launch_bounds__(kColThreads)
+k_amax_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, uint32_t bpl, uint32_t sign_mask,
+                     RngArgs rng, float* __restrict__ amax_out, uint2* __restrict__ codes,
+                     uint8_t* __restrict__ scales, float* __restrict__ gout, uint64_t wait_ticks) {
+    constexpr bool SR = MODE != kRN;
+    constexpr bool RHT = MODE == kRHTSR;
+    __shared__ ColStash st;
+    __shared__ RTable tab;
+    __shared__ uint32_t red[kColRB];
+    const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63u;
+    const uint32_t base = blockIdx.x * bpl * kColThreads + threadIdx.x;
+    uint4 a[kRowFusedPerLane], b[kRowFusedPerLane];
+    float bm[kRowFusedPerLane];
+    uint32_t mbits = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < kRowFusedPerLane; ++j) {
+        const uint32_t n = base + j * kColThreads;
+        a[j] = b[j] = make_uint4(0, 0, 0, 0);
+        if (j < bpl && n < total_blocks) {
+            a[j] = ld16(x + 2 * (size_t)n);
+            b[j] = ld16(x + 2 * (size_t)n + 1);
+        }
+    }
+    // the random words, generated while the loads are in flight, parked in LDS
+    if (SR) {
+#pragma unroll
+        for (uint32_t j = 0; j < kRowFusedPerLane; ++j) {
+            const uint32_t n = base + j * kColThreads;
+            if (j < bpl && n < total_blocks) {
+                const Rand4 r = block_rand_inv(rng, n);
+                st.e[wave][j * 64 + lane] = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
+            }
+        }
+    }
+#pragma unroll
+    for (uint32_t j = 0; j < kRowFusedPerLane; ++j) {
+        float w[16];
+        widen_row_block<RHT>(a[j], b[j], sign_mask, w);
+        bm[j] = absmax16(w);   // 0 for the zero words of blocks outside the tensor
+        mbits = umax(mbits, as_u(RHT ? 0.25f * bm[j] : bm[j]) & 0x7FFFFFFFu);
+    }
+#pragma unroll
+    for (uint32_t j = 0; j < kRowFusedPerLane; ++j) {
+        asm volatile("" : "+v"(a[j].x), "+v"(a[j].y), "+v"(a[j].z), "+v"(a[j].w));
+        asm volatile("" : "+v"(b[j].x), "+v"(b[j].y), "+v"(b[j].z), "+v"(b[j].w));
+    }
+    bool slow;
+    const uint32_t abits = exchange_max(mbits, wait_ticks, red, slow);
+    __shared__ float s_amax;
+    if (threadIdx.x == 0) s_amax = as_f(abits);
+    __syncthreads();
+    if (slow) {
+        // slow route: the whole tensor's amax from this workgroup alone (the tile stays in registers)
+        uint32_t m = 0;
+        for (uint32_t n = threadIdx.x; n < total_blocks; n += kColThreads)
+            m = umax(m, rowblock_absmax<RHT>(ld16(x + 2 * (size_t)n), ld16(x + 2 * (size_t)n + 1), sign_mask));
+        m = block_max<kColRB>(m, red);
+        if (threadIdx.x == 0) s_amax = as_f(m);
+        __syncthreads();
+    }
+    const float amax = s_amax;
+    const float g = global_scale(amax);
+    const Divisor d6 = make_divisor(6.0f * g);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        amax_out[0] = amax;
+        gout[0] = g;
+    }
+    fill_rtable(tab, g);
+#pragma unroll
+    for (uint32_t j = 0; j < kRowFusedPerLane; ++j) {
+        const uint32_t n = base + j * kColThreads;
+        if (j < bpl && n < total_blocks) {
+            Rand4 inv{{0, 0, 0, 0}};
+            if (SR) {
+                const uint4 r = st.e[wave][j * 64 + lane];
+                inv = Rand4{{r.x, r.y, r.z, r.w}};
+            }
+            float w[16];
+            widen_row_block<RHT>(a[j], b[j], sign_mask, w);
+            uint32_t lo, hi, sb;
+            quantize_block_m<SR, RHT>(w, bm[j], d6, [&](uint32_t sc) { return tab.r[sc]; }, inv, lo, hi, sb);
+            st_nt(codes + n, make_uint2(lo, hi));
+            st_nt(scales + n, (uint8_t)sb);
+        }
+    }
+    release_slot();
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -1265,9 +1389,9 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, bool colwi
             if (use_rht) k_amax_rowwise_rows<true><<<grid, kThreads, 0, stream>>>(xv, (uint32_t)rows, bpr, sign_mask, bits);
             else k_amax_rowwise_rows<false><<<grid, kThreads, 0, stream>>>(xv, (uint32_t)rows, bpr, sign_mask, bits);
         } else {
-            const uint32_t grid = grid_for(total, kThreads * 4, 8);
-            if (use_rht) k_amax_rowwise_tensor<true><<<grid, kThreads, 0, stream>>>(xv, total, sign_mask, bits);
-            else k_amax_rowwise_tensor<false><<<grid, kThreads, 0, stream>>>(xv, total, sign_mask, bits);
+            const uint32_t grid = grid_for(total, kColThreads * kRowAmaxPerLane, 1);
+            if (use_rht) k_amax_rowwise_tensor<true><<<grid, kColThreads, 0, stream>>>(xv, total, sign_mask, bits);
+            else k_amax_rowwise_tensor<false><<<grid, kColThreads, 0, stream>>>(xv, total, sign_mask, bits);
         }
     } else {
         uint32_t grid;
@@ -1342,6 +1466,28 @@ hipError_t launch_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, bool
                              : mode == kSR ? (const void*)k_amax_quant_colwise<kSR>
                                            : (const void*)k_amax_quant_colwise<kRHTSR>;
             return hipLaunchKernel(fn, dim3(grid), dim3(kColThreads), args, 0, stream);
+        }
+    }
+    if (rows > 0 && cols > 0 && !colwise) {
+        const uint32_t total = (uint32_t)(rows * (cols / 16));
+        const uint32_t cus = (uint32_t)cu_count();
+        const uint32_t bpl = (uint32_t)(((uint64_t)total + (uint64_t)cus * kColThreads - 1) / ((uint64_t)cus * kColThreads));
+        if (bpl <= kRowFusedPerLane) {
+            const uint32_t per = bpl * kColThreads;
+            const uint32_t grid = (total + per - 1) / per;   // <= CUs
+            if (grid <= kFusedMaxGrid) {
+                const uint4* xv = reinterpret_cast<const uint4*>(x);
+                uint2* cv = reinterpret_cast<uint2*>(codes);
+                RngArgs ra = rng_args(rng);
+                uint64_t wait = fused_wait_ticks();
+                uint32_t t = total, bp = bpl;
+                void* args[] = {(void*)&xv, &t, &bp, &sign_mask, &ra, (void*)&amax, (void*)&cv, (void*)&scales,
+                                (void*)&g, &wait};
+                const void* fn = mode == kRN ? (const void*)k_amax_quant_rowwise<kRN>
+                                 : mode == kSR ? (const void*)k_amax_quant_rowwise<kSR>
+                                               : (const void*)k_amax_quant_rowwise<kRHTSR>;
+                return hipLaunchKernel(fn, dim3(grid), dim3(kColThreads), args, 0, stream);
+            }
         }
     }
     // two passes over the tensor: amax, then quantization

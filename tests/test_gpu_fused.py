@@ -1,8 +1,8 @@
 """GPU parity of nvfp4_amax_quantize (amax and 1x16 quantization in one call) against the CPU oracle.
 
-Column-wise tensors of at most one 256 x 512 tile per CU take the single-read cooperative launch (the tile stays
-in registers across a grid-wide barrier); larger or row-wise ones take the two-pass path.  Bar: amax, g, codes and
-scales bit-exact, as for the separate calls.
+Tensors that fit the chip in one wave of workgroups take the single-read kernels (the tile stays in registers while
+the workgroups exchange their maxima): column-wise up to one 256 x 512 tile per CU, row-wise up to 8192 blocks per
+CU.  Larger ones take the two-pass path.  Bar: amax, g, codes and scales bit-exact, as for the separate calls.
 """
 import sys
 
@@ -54,9 +54,18 @@ def test_colwise(mode, shape):
     check(x, mode, Q.COLWISE)
 
 
+@pytest.mark.parametrize("mode", ["rn", "sr", "rht_sr"])
+@pytest.mark.parametrize("shape", [(300, 160), (1, 16), (16, 16), (1000, 1040), (2048, 2048), (4096, 1056)])
+def test_rowwise(mode, shape):
+    """Ragged block counts: partial workgroups, lanes with fewer blocks than others, 1 or 2 blocks per lane."""
+    x = W.outlier_columns(*shape, seed=(shape[0] * 3 + shape[1]) & 0xFFFF, n_cols=3)
+    check(x, mode, Q.ROWWISE)
+
+
 @pytest.mark.parametrize("mode", ["rn", "rht_sr"])
 def test_rowwise_two_pass(mode):
-    check(W.outlier_columns(300, 160, seed=4, n_cols=3), mode, Q.ROWWISE)
+    """More than 8192 blocks per CU: amax, then quantization."""
+    check(W.lognormal_gradients(8208, 4096, seed=12), mode, Q.ROWWISE)
 
 
 def test_consecutive_calls_reuse_the_barrier():
@@ -78,11 +87,23 @@ def test_slow_route_after_a_timed_out_wait(monkeypatch, mode):
     check(x, mode, Q.COLWISE, mask=W.sign_mask(4, 7), seed=4, offset=7)     # and back on the fast route
 
 
+@pytest.mark.parametrize("mode", ["sr", "rht_sr"])
+def test_rowwise_slow_route(monkeypatch, mode):
+    monkeypatch.setenv("NVFP4_FUSED_WAIT_TICKS", "0")
+    x = W.outlier_columns(2048, 1024, seed=92, n_cols=5)
+    for call in range(2):
+        check(x, mode, Q.ROWWISE, mask=W.sign_mask(5, call), seed=5, offset=call)
+    monkeypatch.delenv("NVFP4_FUSED_WAIT_TICKS")
+    check(x, mode, Q.ROWWISE, mask=W.sign_mask(5, 2), seed=5, offset=2)
+
+
 def test_nan_and_zero_tensors():
     x = W.lognormal_gradients(256, 512, seed=5)
     x[100, 7] = 0x7FC0                      # bf16 NaN
     check(x, "rht_sr", Q.COLWISE)
+    check(x, "rht_sr", Q.ROWWISE)
     check(np.zeros((256, 512), np.uint16), "sr", Q.COLWISE)
+    check(np.zeros((256, 512), np.uint16), "sr", Q.ROWWISE)
 
 
 def test_empty_tensor():
@@ -98,6 +119,14 @@ def test_full_wgrad_colwise_single_read():
     x = W.make("wgrad_colwise_rht_sr_8192x4096")
     for call in (0, 1):
         check(x, "rht_sr", Q.COLWISE, mask=W.sign_mask(2, call), seed=2, offset=call)
+
+
+@pytest.mark.slow
+def test_full_fprop_rowwise_single_read():
+    """8192 x 4096 row-wise (8 blocks per lane on 256 CUs) through the single-read launch."""
+    x = W.make("fprop_rn_8192x4096")
+    check(x, "rn", Q.ROWWISE)
+    check(x, "rht_sr", Q.ROWWISE, mask=W.sign_mask(6, 0), seed=6, offset=0)
 
 
 def test_graph_replays_match_eager():
