@@ -152,8 +152,10 @@ __device__ __forceinline__ float scale_multiplier(uint32_t sb, float g) {
 // method (P. Markstein, "Computation of elementary functions on the IBM RISC System/6000 processor", IBM J. Res.
 // Dev. 34(1), 1990): from y = fl(1/d) and q = fl(bamax y), which is within one ulp of bamax/d, the exact FMA
 // residual e = bamax - q d gives the correctly rounded quotient fl(q + e y), provided no step underflows or
-// overflows.  That holds for 2^-60 <= d <= 2^60 and 2^-20 <= q <= 2^64; below that window of q the quotient is
-// under 2^-10 and the code is 0 either way, above it the code saturates either way.  Other d use the division.
+// overflows.  That holds for 2^-60 <= d <= 2^60 and 2^-20 <= q <= 2^64.  Below that window of q the result stays
+// within a few units of the (sub)normal grid of a quotient under 2^-20, so the code is 0 either way; q is clamped to
+// 2^20 from above, where the code saturates either way (an infinite or NaN bamax still yields inf or NaN).  Other d
+// use the division.
 struct Divisor {
     float d, y;
     bool fast;
@@ -163,16 +165,23 @@ __device__ __forceinline__ Divisor make_divisor(float d) {
     return Divisor{d, 1.0f / d, d >= 0x1p-60f && d <= 0x1p60f};
 }
 
-// Block scale code: sb = E4M3(fl(bamax / d)), with s = 0 for bamax = 0.
+// The same for a d that is equal in every lane: the branch on fast becomes a scalar one.
+__device__ __forceinline__ Divisor make_divisor_uniform(float d) {
+    const Divisor v = make_divisor(d);
+    return Divisor{v.d, v.y, __builtin_amdgcn_readfirstlane((uint32_t)v.fast) != 0};
+}
+
+// Block scale code: sb = E4M3(fl(bamax / d)), with s = 0 for bamax = 0 (which the Markstein branch gives by itself:
+// y is finite there).
 __device__ __forceinline__ uint32_t scale_code(float bamax, const Divisor& dv) {
     float s;
     if (dv.fast) {
-        const float q = bamax * dv.y;
-        s = (q >= 0x1p-20f && q <= 0x1p64f) ? __builtin_fmaf(__builtin_fmaf(-q, dv.d, bamax), dv.y, q) : q;
+        const float q = __builtin_fminf(bamax * dv.y, 0x1p20f);
+        s = __builtin_fmaf(__builtin_fmaf(-q, dv.d, bamax), dv.y, q);
     } else {
-        s = bamax / dv.d;
+        s = bamax == 0.0f ? 0.0f : bamax / dv.d;
     }
-    return e4m3_encode(bamax == 0.0f ? 0.0f : s);
+    return e4m3_encode(s);
 }
 
 // NaN-propagating maximum of the 16 magnitudes (a depth-3 tree of v_maximum3).
@@ -208,15 +217,52 @@ __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* lds) {
     return r;  // valid in thread 0
 }
 
-// Per-tensor g: the 128 possible multipliers are tabulated once per workgroup in LDS.
+// Fast-path multiplier of a block whose scale multiplier is r: what w is multiplied by directly (0.25 r with the
+// RHT, where w is the value before the transform's final 0.25), or NaN where the fast path might not reproduce the
+// definition's codes, so that the block takes the general path (which maps NaN products to 0x7).  A finite r > 0
+// is exact without the RHT (a zero r can meet an infinite value: inf * 0).  With it, fl(w fl(0.25 r)) and
+// fl(fl(0.25 w) r) give the same code for 2^-124 <= r < 2^117: they are equal when 0.25 w is exact, and both are
+// below 2^-9 (code 0 with the sign of w) when it is not.  Negative and NaN r (degenerate g) go general too.
+template <bool RHT>
+__device__ __forceinline__ float fast_multiplier(float r) {
+    const float nan = __builtin_nanf("");
+    if (RHT) return (r >= 0x1p-124f && r < 0x1p117f) ? 0.25f * r : nan;
+    return (r > 0.0f && r <= kFltMax) ? r : nan;
+}
+
+// Per-tensor g: the multipliers of the 128 scale codes are tabulated once per workgroup in LDS, as r and as the
+// fast-path multiplier.
 struct RTable {
     float r[128];
+    float rq[128];
 };
 
+template <bool RHT>
+__device__ __forceinline__ void fill_rtable_entry(RTable& t, uint32_t c, float g) {
+    const float r = scale_multiplier(c, g);
+    t.r[c] = r;
+    t.rq[c] = fast_multiplier<RHT>(r);
+}
+
+template <bool RHT>
 __device__ __forceinline__ void fill_rtable(RTable& t, float g) {
-    if (threadIdx.x < 128) t.r[threadIdx.x] = scale_multiplier(threadIdx.x, g);
+    if (threadIdx.x < 128) fill_rtable_entry<RHT>(t, threadIdx.x, g);
     __syncthreads();
 }
+
+// Sources of the block multipliers: a per-tensor table, or computed per block from a per-row g.
+struct TableMul {
+    const RTable& t;
+    __device__ float rq(uint32_t c) const { return t.rq[c]; }
+    __device__ float r(uint32_t c) const { return t.r[c]; }
+};
+
+template <bool RHT>
+struct RowMul {
+    float g;
+    __device__ float rq(uint32_t c) const { return fast_multiplier<RHT>(scale_multiplier(c, g)); }
+    __device__ float r(uint32_t c) const { return scale_multiplier(c, g); }
+};
 
 // ------------------------------------------------------------------------------------------------------------
 // E2M1 encoding with the gfx950 conversions (unit scale).  Element 2k goes to the low nibble of byte k.
@@ -310,24 +356,20 @@ __device__ __forceinline__ void encode16(const float (&q)[16], const Rand4& inv,
 }
 
 // Quantize one 16-element block.  w[] are the values before the final 0.25 of the transform when RHT is set
-// (y = fl(0.25 w)), the values themselves otherwise.  r_of(sb) gives the element multiplier of scale code sb.
-// Fast path (no NaN possible): the block's multiplier r is finite and positive; with the RHT additionally
-// 2^-124 <= r < 2^117, where fl(fl(0.25 w) r) and fl(w fl(0.25 r)) give the same code for every w (they are equal
-// when 0.25 w is exact, and both are below 2^-9 -- code 0 with the sign of w -- when it is not).
-template <bool SR, bool RHT, typename ROf>
-__device__ __forceinline__ bool quantize_block_fast(const float (&w)[16], float m, const Divisor& d6, ROf r_of,
-                                                    const Rand4& inv, uint32_t& lo, uint32_t& hi, uint32_t& sb,
-                                                    float& r) {
+// (y = fl(0.25 w)), the values themselves otherwise; mul gives the multipliers of a scale code (fast_multiplier).
+// Returns false when the block needs the general path.
+template <bool SR, bool RHT, typename Mul>
+__device__ __forceinline__ bool quantize_block_fast(const float (&w)[16], float m, const Divisor& d6, const Mul& mul,
+                                                    const Rand4& inv, uint32_t& lo, uint32_t& hi, uint32_t& sb) {
     // m = absmax16(w)
     const float bamax = RHT ? 0.25f * m : m;       // max_i fl(0.25 |w_i|) = fl(0.25 max_i |w_i|)
     sb = scale_code(bamax, d6);
-    r = r_of(sb);
-    const float rq = RHT ? 0.25f * r : r;
+    const float rq = mul.rq(sb);
     float q[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) q[i] = w[i] * rq;
     encode16<SR>(q, inv, lo, hi);
-    return RHT ? (r >= 0x1p-124f && r < 0x1p117f) : (r > 0.0f && r <= kFltMax);
+    return rq == rq;
 }
 
 // The definition step by step for blocks outside the fast path: y = fl(0.25 w) (RHT), q = fl(y r); NaN -> 0x7.
@@ -343,18 +385,17 @@ __device__ __forceinline__ void quantize_block_general(const float (&w)[16], flo
 }
 
 // m is the block's absmax16(w), when the caller has it already.
-template <bool SR, bool RHT, typename ROf>
-__device__ __forceinline__ void quantize_block_m(const float (&w)[16], float m, const Divisor& d6, ROf r_of,
+template <bool SR, bool RHT, typename Mul>
+__device__ __forceinline__ void quantize_block_m(const float (&w)[16], float m, const Divisor& d6, const Mul& mul,
                                                  const Rand4& inv, uint32_t& lo, uint32_t& hi, uint32_t& sb) {
-    float r;
-    if (!quantize_block_fast<SR, RHT>(w, m, d6, r_of, inv, lo, hi, sb, r)) [[unlikely]]
-        quantize_block_general<SR, RHT>(w, r, inv, lo, hi);
+    if (!quantize_block_fast<SR, RHT>(w, m, d6, mul, inv, lo, hi, sb)) [[unlikely]]
+        quantize_block_general<SR, RHT>(w, mul.r(sb), inv, lo, hi);
 }
 
-template <bool SR, bool RHT, typename ROf>
-__device__ __forceinline__ void quantize_block(const float (&w)[16], const Divisor& d6, ROf r_of, const Rand4& inv,
-                                               uint32_t& lo, uint32_t& hi, uint32_t& sb) {
-    quantize_block_m<SR, RHT>(w, absmax16(w), d6, r_of, inv, lo, hi, sb);
+template <bool SR, bool RHT, typename Mul>
+__device__ __forceinline__ void quantize_block(const float (&w)[16], const Divisor& d6, const Mul& mul,
+                                               const Rand4& inv, uint32_t& lo, uint32_t& hi, uint32_t& sb) {
+    quantize_block_m<SR, RHT>(w, absmax16(w), d6, mul, inv, lo, hi, sb);
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -471,9 +512,9 @@ k_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, FastDiv per_
     Divisor d6{};
     if (!PER_ROW) {
         g = global_scale(amax[0]);
-        d6 = make_divisor(6.0f * g);
+        d6 = make_divisor_uniform(6.0f * g);
         if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
-        fill_rtable(tab, g);
+        fill_rtable<RHT>(tab, g);
     }
     const uint32_t stride = gridDim.x * kThreads;
     uint32_t n = blockIdx.x * kThreads + threadIdx.x;
@@ -495,10 +536,9 @@ k_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, FastDiv per_
             const uint32_t row = fdiv(n, per_row);
             const float gr = global_scale(amax[row]);
             if (n == row * per_row.d) gout[row] = gr;
-            quantize_block<SR, RHT>(w, make_divisor(6.0f * gr), [&](uint32_t c) { return scale_multiplier(c, gr); }, rnd, lo, hi,
-                                    sb);
+            quantize_block<SR, RHT>(w, make_divisor(6.0f * gr), RowMul<RHT>{gr}, rnd, lo, hi, sb);
         } else {
-            quantize_block<SR, RHT>(w, d6, [&](uint32_t c) { return tab.r[c]; }, rnd, lo, hi, sb);
+            quantize_block<SR, RHT>(w, d6, TableMul{tab}, rnd, lo, hi, sb);
         }
         st_nt(codes + n, make_uint2(lo, hi));
         st_nt(scales + n, (uint8_t)sb);
@@ -613,6 +653,27 @@ __device__ __forceinline__ void col_write_out_stash(const ColStash& st, const Co
     }
 }
 
+// Writes the codes/scales of column blocks j = 2 jp and 2 jp + 1 of every lane held in a ColStash: thread t takes
+// row-block t % 16 of column 8 (t / 16) + j, so 16 consecutive threads write one column's 128 contiguous code bytes.
+__device__ __forceinline__ void col_write_out_pair(const ColStash& st, const ColPos& p, uint32_t rows, uint32_t cols,
+                                                   uint32_t nrb, int jp, uint8_t* __restrict__ codes,
+                                                   uint8_t* __restrict__ scales) {
+    const uint32_t col0 = p.strip * 512;
+    const uint32_t ncol = min(512u, cols - col0), nr = min((uint32_t)kColRB, nrb - p.group * kColRB);
+    const uint32_t rbl = threadIdx.x % kColRB, lq = threadIdx.x / kColRB, rb = p.group * kColRB + rbl;
+    if (rbl >= nr) return;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const uint32_t j = 2 * jp + jj, cl = 8 * lq + j;
+        if (cl < ncol) {
+            const uint4 e = st.e[rbl][j * 64 + lq];
+            const uint32_t c = col0 + cl;
+            st_nt(codes + (size_t)c * (rows >> 1) + 8 * (size_t)rb, make_uint2(e.x, e.y));
+            st_nt(scales + (size_t)c * nrb + rb, (uint8_t)e.z);
+        }
+    }
+}
+
 template <int MODE, bool PER_ROW>
 __global__ void __launch_bounds__(kColThreads)
 k_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColGrid cg,
@@ -626,9 +687,9 @@ k_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, Co
     Divisor d6{};
     if (!PER_ROW) {
         g = global_scale(amax[0]);
-        d6 = make_divisor(6.0f * g);
+        d6 = make_divisor_uniform(6.0f * g);
         if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
-        fill_rtable(tab, g);
+        fill_rtable<RHT>(tab, g);
     }
     const ColPos pos = col_position(cg, blockIdx.x);
     const uint32_t wave = threadIdx.x >> 6;
@@ -659,10 +720,9 @@ k_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, Co
                 const uint32_t c = pos.c8 + j;
                 const float gr = global_scale(amax[c]);
                 if (pos.rb == 0) gout[c] = gr;
-                quantize_block<SR, RHT>(w, make_divisor(6.0f * gr),
-                                        [&](uint32_t sc) { return scale_multiplier(sc, gr); }, inv, lo, hi, sb);
+                quantize_block<SR, RHT>(w, make_divisor(6.0f * gr), RowMul<RHT>{gr}, inv, lo, hi, sb);
             } else {
-                quantize_block<SR, RHT>(w, d6, [&](uint32_t sc) { return tab.r[sc]; }, inv, lo, hi, sb);
+                quantize_block<SR, RHT>(w, d6, TableMul{tab}, inv, lo, hi, sb);
             }
             slot = make_uint4(lo, hi, sb, 0u);
             if (j & 1) __builtin_amdgcn_sched_barrier(0);   // two blocks at a time bounds the live registers
@@ -707,62 +767,60 @@ __device__ uint32_t wg_amax_colwise(const uint16_t* x, uint32_t cols, const ColG
         if (p.c8 < cols) {
             load_col_tile(x, cols, p, v);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float wp[2][16];
-                widen_col_pair<RHT>(v, q, sign_mask, wp[0], wp[1]);
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const float bmax = absmax16(wp[t]);
-                    m = umax(m, as_u(RHT ? 0.25f * bmax : bmax) & 0x7FFFFFFFu);
-                }
+            for (int j = 0; j < 8; ++j) {   // one block at a time: this runs with the caller's state live
+                float w[16];
+                widen_col_block<RHT>(v, j, sign_mask, w);
+                const float bmax = absmax16(w);
+                m = umax(m, as_u(RHT ? 0.25f * bmax : bmax) & 0x7FFFFFFFu);
             }
         }
     }
     return block_max<kColRB>(m, red);
 }
 
-// The cross-workgroup step of the single-read kernels: the workgroup maximum of mbits (magnitude bits) goes to this
-// workgroup's slot, then the slots of every workgroup are read (thread i watches slots i, i + 1024, ...) and
-// reduced.  Returns the tensor maximum in every thread; slow (uniform) is set when some slot stayed empty past
-// wait_ticks, in which case the return value is not the tensor maximum.  Uses red[blockDim.x / 64].
-__device__ uint32_t exchange_max(uint32_t mbits, uint64_t wait_ticks, uint32_t* red, bool& slow) {
+// The cross-workgroup step of the single-read kernels (1024-thread workgroups).  The workgroup maximum of mbits
+// (magnitude bits) goes to this workgroup's slot.  Wave 0 then reads the slots of every workgroup (lane l watches
+// slots l, l + 64, ...), reduces them to the tensor amax and fills tab for g = amax / 2688, while the other waves
+// wait at the one barrier that follows.  Returns the amax bits, equal in every thread; slow (uniform) is set when
+// some slot stayed empty past wait_ticks, and then neither the return value nor tab is valid.  Uses red[16].
+template <bool RHT>
+__device__ uint32_t exchange_max(uint32_t mbits, uint64_t wait_ticks, uint32_t* red, RTable& tab, bool& slow) {
     __shared__ uint32_t s_max, s_out;
+    const uint32_t lane = threadIdx.x & 63u;
     mbits = wave_max(mbits);
-    if ((threadIdx.x & 63u) == 0) red[threadIdx.x >> 6] = mbits;
-    if (threadIdx.x == 0) s_out = 0;
+    if (lane == 0) red[threadIdx.x >> 6] = mbits;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t m = 0;
-        for (uint32_t w = 0; w < blockDim.x / 64; ++w) m = umax(m, red[w]);
-        __hip_atomic_store(&g_fused_slot[blockIdx.x], (1ull << 32) | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    uint32_t m = 0;
-    bool waited_out = false;
-    const uint64_t t0 = wall_clock64();
-    for (uint32_t i = threadIdx.x; i < gridDim.x && !waited_out; i += blockDim.x) {
-        uint64_t sv;
-        while ((sv = __hip_atomic_load(&g_fused_slot[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
-            if (wall_clock64() - t0 >= wait_ticks) {
-                waited_out = true;
-                break;
+    if (threadIdx.x < 64) {
+        uint32_t m = wave_max(lane < kColRB ? red[lane] : 0u);
+        if (lane == 0)
+            __hip_atomic_store(&g_fused_slot[blockIdx.x], (1ull << 32) | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        m = 0;
+        bool waited_out = false;
+        const uint64_t t0 = wall_clock64();
+        for (uint32_t i = lane; i < gridDim.x && !waited_out; i += 64) {
+            uint64_t sv;
+            while ((sv = __hip_atomic_load(&g_fused_slot[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
+                if (wall_clock64() - t0 >= wait_ticks) {
+                    waited_out = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
             }
-            __builtin_amdgcn_s_sleep(1);
+            m = umax(m, (uint32_t)sv);
         }
-        m = umax(m, (uint32_t)sv);
-    }
-    if (waited_out) s_out = 1;
-    m = wave_max(m);
-    __syncthreads();   // red is free again, s_out settled
-    if ((threadIdx.x & 63u) == 0) red[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t r = 0;
-        for (uint32_t w = 0; w < blockDim.x / 64; ++w) r = umax(r, red[w]);
-        s_max = r;
+        m = wave_max(m);
+        const bool out = __ballot(waited_out) != 0;
+        const float g = global_scale(as_f(m));
+#pragma unroll 1
+        for (uint32_t c = lane; c < 128; c += 64) fill_rtable_entry<RHT>(tab, c, g);
+        if (lane == 0) {
+            s_max = m;
+            s_out = out;
+        }
     }
     __syncthreads();
     slow = s_out != 0;
-    return s_max;
+    return __builtin_amdgcn_readfirstlane(s_max);
 }
 
 // Clears this workgroup's slot: the last action of a single-read kernel (every other workgroup has read the slot by
@@ -812,44 +870,48 @@ k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t col
 #pragma unroll
     for (int k = 0; k < 16; ++k) asm volatile("" : "+v"(v[k].x), "+v"(v[k].y), "+v"(v[k].z), "+v"(v[k].w));
     bool slow;
-    uint32_t abits = exchange_max(mbits, wait_ticks, red, slow);
-    __shared__ float s_amax;
-    if (threadIdx.x == 0) s_amax = as_f(abits);
-    __syncthreads();
+    uint32_t abits = exchange_max<RHT>(mbits, wait_ticks, red, tab, slow);
     if (slow) {
         // slow route: the whole tensor's amax from this workgroup alone, then the tile again
+        __shared__ uint32_t s_bits;
         const uint32_t mm = wg_amax_colwise<RHT>(x, cols, cg, sign_mask, v, red);
-        if (threadIdx.x == 0) s_amax = as_f(mm);
+        if (threadIdx.x == 0) s_bits = mm;
         if (active) load_col_tile(x, cols, pos, v);
         __syncthreads();
+        abits = __builtin_amdgcn_readfirstlane(s_bits);
+        fill_rtable<RHT>(tab, global_scale(as_f(abits)));
     }
-    const float amax = s_amax;
+    const float amax = as_f(abits);
     const float g = global_scale(amax);
-    const Divisor d6 = make_divisor(6.0f * g);
+    const Divisor d6 = make_divisor_uniform(6.0f * g);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         amax_out[0] = amax;
         gout[0] = g;
     }
-    fill_rtable(tab, g);
-    if (active) {
+    // Two blocks at a time: quantize, then (after a barrier) write them out, so that the stores of one pair overlap
+    // the arithmetic of the next.
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            uint4& slot = st.e[wave][j * 64 + pos.lane];
-            Rand4 inv{{0, 0, 0, 0}};
-            if (SR) {
-                const uint4 r = slot;
-                inv = Rand4{{r.x, r.y, r.z, r.w}};
+    for (int jp = 0; jp < 4; ++jp) {
+        if (active) {
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int j = 2 * jp + jj;
+                uint4& slot = st.e[wave][j * 64 + pos.lane];
+                Rand4 inv{{0, 0, 0, 0}};
+                if (SR) {
+                    const uint4 r = slot;
+                    inv = Rand4{{r.x, r.y, r.z, r.w}};
+                }
+                float w[16];
+                widen_col_block<RHT>(v, j, sign_mask, w);
+                uint32_t lo, hi, sb;
+                quantize_block_m<SR, RHT>(w, bm[j], d6, TableMul{tab}, inv, lo, hi, sb);
+                slot = make_uint4(lo, hi, sb, 0u);
             }
-            float w[16];
-            widen_col_block<RHT>(v, j, sign_mask, w);
-            uint32_t lo, hi, sb;
-            quantize_block_m<SR, RHT>(w, bm[j], d6, [&](uint32_t sc) { return tab.r[sc]; }, inv, lo, hi, sb);
-            slot = make_uint4(lo, hi, sb, 0u);
-            if (j & 1) __builtin_amdgcn_sched_barrier(0);
         }
+        __syncthreads();
+        col_write_out_pair(st, pos, rows, cols, cg.nrb, jp, codes, scales);
     }
-    __syncthreads();
-    col_write_out_stash(st, pos, rows, cols, cg.nrb, codes, scales);
     release_slot();
 }
 
@@ -869,12 +931,12 @@ k_quant_16x16(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColG
     __shared__ ColStage st;
     __shared__ RTable tab;
     const float g = global_scale(amax[0]);
-    const Divisor d6 = make_divisor(6.0f * g);
+    const Divisor d6 = make_divisor_uniform(6.0f * g);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         if (WANT_W) gw[0] = g;
         if (WANT_WT) gt[0] = g;
     }
-    fill_rtable(tab, g);
+    fill_rtable<false>(tab, g);
     // Workgroups loop over the tiles (grid-stride); the next tile's loads are issued before the current tile's
     // W^T write-out, so reading overlaps writing.  Lanes of a pair own the two halves of one 16x16 tile, so both
     // exist or neither (cols is a multiple of 16).
@@ -901,7 +963,7 @@ k_quant_16x16(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColG
         m = __builtin_elementwise_maximum(m, __shfl_xor(m, 1));
         const uint32_t sb = scale_code(m, d6);
         const float r = tab.r[sb];
-        const bool fast = r > 0.0f && r <= kFltMax;
+        const bool fast = tab.rq[sb] == tab.rq[sb];   // see fast_multiplier
         // Every product is converted once and packed both ways: column pair (2p, 2p+1) gives byte p of every W row
         // and the two W^T column blocks 2p, 2p+1.
         uint32_t rowc[16];
@@ -1009,8 +1071,8 @@ k_quant_4o6(const uint4* __restrict__ x, uint32_t total_blocks, FastDiv per_row,
     if (!PER_ROW) {
         g = global_scale(amax[0]);
         if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
-        dv[0] = make_divisor(6.0f * g);
-        dv[1] = make_divisor(4.0f * g);
+        dv[0] = make_divisor_uniform(6.0f * g);
+        dv[1] = make_divisor_uniform(4.0f * g);
     }
     const uint32_t stride = gridDim.x * kThreads;
     uint32_t n = blockIdx.x * kThreads + threadIdx.x;
@@ -1275,27 +1337,26 @@ k_amax_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, uint32_
         asm volatile("" : "+v"(b[j].x), "+v"(b[j].y), "+v"(b[j].z), "+v"(b[j].w));
     }
     bool slow;
-    const uint32_t abits = exchange_max(mbits, wait_ticks, red, slow);
-    __shared__ float s_amax;
-    if (threadIdx.x == 0) s_amax = as_f(abits);
-    __syncthreads();
+    uint32_t abits = exchange_max<RHT>(mbits, wait_ticks, red, tab, slow);
     if (slow) {
         // slow route: the whole tensor's amax from this workgroup alone (the tile stays in registers)
+        __shared__ uint32_t s_bits;
         uint32_t m = 0;
         for (uint32_t n = threadIdx.x; n < total_blocks; n += kColThreads)
             m = umax(m, rowblock_absmax<RHT>(ld16(x + 2 * (size_t)n), ld16(x + 2 * (size_t)n + 1), sign_mask));
         m = block_max<kColRB>(m, red);
-        if (threadIdx.x == 0) s_amax = as_f(m);
+        if (threadIdx.x == 0) s_bits = m;
         __syncthreads();
+        abits = __builtin_amdgcn_readfirstlane(s_bits);
+        fill_rtable<RHT>(tab, global_scale(as_f(abits)));
     }
-    const float amax = s_amax;
+    const float amax = as_f(abits);
     const float g = global_scale(amax);
-    const Divisor d6 = make_divisor(6.0f * g);
+    const Divisor d6 = make_divisor_uniform(6.0f * g);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         amax_out[0] = amax;
         gout[0] = g;
     }
-    fill_rtable(tab, g);
 #pragma unroll
     for (uint32_t j = 0; j < kRowFusedPerLane; ++j) {
         const uint32_t n = base + j * kColThreads;
@@ -1308,7 +1369,7 @@ k_amax_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, uint32_
             float w[16];
             widen_row_block<RHT>(a[j], b[j], sign_mask, w);
             uint32_t lo, hi, sb;
-            quantize_block_m<SR, RHT>(w, bm[j], d6, [&](uint32_t sc) { return tab.r[sc]; }, inv, lo, hi, sb);
+            quantize_block_m<SR, RHT>(w, bm[j], d6, TableMul{tab}, inv, lo, hi, sb);
             st_nt(codes + n, make_uint2(lo, hi));
             st_nt(scales + n, (uint8_t)sb);
         }

@@ -146,27 +146,62 @@ def test_edge_values_all_modes():
         check_1x16(x, mode, Q.ROWWISE, 0)
 
 
-def test_degenerate_amax_inputs():
-    """Caller-supplied amax values that are not the tensor's own: 0 (g = 0), negative, inf and NaN, with inf
-    elements present.  The element multiplier is then 0, negative or NaN and every element takes the general
-    path of the definition."""
-    x = W.gaussian(16, 64, seed=3)
-    xf = x.copy()
-    xf[2, 5] = 0x7F80   # +inf
-    xf[7, 9] = 0xFF80   # -inf
+# Caller-supplied amax values that are not the tensor's own.  0 gives g = 0; negative, inf and NaN give degenerate
+# multipliers; 1e-40 and 1e30 put fl(6 g) outside the window of the fast quotient (the division is used); 1e-12 makes
+# the block quotients exceed 2^20 (the clamped branch, codes saturate); 1e20 makes them fall below 2^-20 (codes 0);
+# 1e-30 gives multipliers above 2^117, outside the transform's fast range.
+ODD_AMAX = (0.0, -3.0, float("inf"), float("nan"), 1e-40, 3e38, 1e-30, 1e-12, 1e20, 1e30)
+
+
+def odd_amax_input():
+    x = W.gaussian(32, 64, seed=3)
+    x[2, 5] = 0x7F80   # +inf
+    x[7, 9] = 0xFF80   # -inf
+    return x
+
+
+@pytest.mark.parametrize("orient", [Q.ROWWISE, Q.COLWISE])
+@pytest.mark.parametrize("mode", ["rn", "sr", "rht_sr"])
+def test_degenerate_amax_inputs(mode, orient):
+    """Every element of such a tensor takes the general path of the definition, or a fast path that must agree."""
+    xf = odd_amax_input()
     xd = dev(xf)
-    for amax_val in (0.0, -3.0, float("inf"), float("nan"), 1e-40, 3e38):
-        say("degenerate amax", amax_val)
+    mask = 0x6B2D
+    for amax_val in ODD_AMAX:
+        say("degenerate amax", mode, orient, amax_val)
         a = torch.full((1,), amax_val, dtype=torch.float32, device="cuda")
-        for mode in ("rn", "sr"):
-            if mode == "rn":
-                out, _ = Q.nvfp4_quantize_rn(xd, a, Q.BLOCK_1X16, Q.ROWWISE, 0)
-            else:
-                out = Q.nvfp4_quantize_sr(xd, a, 5, 6, Q.ROWWISE, 0)
-            oc, os_, og = O.quantize_1x16(xf, np.array([amax_val], np.float32), MODES[mode], seed=5, offset=6)
-            same_u8(host(out.codes), oc, "codes")
-            same_u8(host(out.scales), os_, "scales")
-            same_f32(host(out.g), og)
+        if mode == "rn":
+            r, c = Q.nvfp4_quantize_rn(xd, a, Q.BLOCK_1X16, orient, 0)
+            out = r if orient == Q.ROWWISE else c
+        elif mode == "sr":
+            out = Q.nvfp4_quantize_sr(xd, a, 5, 6, orient, 0)
+        else:
+            out = Q.nvfp4_quantize_rht_sr(xd, a, mask, 5, 6, orient, 0)
+        oc, os_, og = O.quantize_1x16(xf, np.array([amax_val], np.float32), MODES[mode], orient, 0, mask, 5, 6)
+        same_u8(host(out.codes), oc, "codes")
+        same_u8(host(out.scales), os_, "scales")
+        same_f32(host(out.g), og)
+
+
+def test_degenerate_amax_16x16_and_4o6():
+    xf = odd_amax_input()
+    xd = dev(xf)
+    for amax_val in ODD_AMAX:
+        say("degenerate amax 16x16 / 4o6", amax_val)
+        a = torch.full((1,), amax_val, dtype=torch.float32, device="cuda")
+        w, wt = Q.nvfp4_quantize_rn(xd, a, Q.BLOCK_16X16, Q.BOTH, 0)
+        (ow, osw, ogw), (ot, ost, ogt) = O.quantize_16x16(xf, np.array([amax_val], np.float32))
+        same_u8(host(w.codes), ow, "W codes")
+        same_u8(host(w.scales), osw, "W scales")
+        same_f32(host(w.g), ogw)
+        same_u8(host(wt.codes), ot, "W^T codes")
+        same_u8(host(wt.scales), ost, "W^T scales")
+        same_f32(host(wt.g), ogt)
+        o4 = Q.nvfp4_quantize_4o6(xd, a, 0)
+        oc4, os4, og4, _ = O.quantize_4o6(xf, np.array([amax_val], np.float32), 0)
+        same_u8(host(o4.codes), oc4, "4o6 codes")
+        same_u8(host(o4.scales), os4, "4o6 scales")
+        same_f32(host(o4.g), og4)
 
 
 def test_empty_tensors():
