@@ -780,7 +780,7 @@ __device__ uint32_t wg_amax_colwise(const uint16_t* x, uint32_t cols, const ColG
 
 // The cross-workgroup step of the single-read kernels (1024-thread workgroups).  The workgroup maximum of mbits
 // (magnitude bits) goes to this workgroup's slot.  Wave 0 then reads the slots of every workgroup (lane l watches
-// slots l, l + 64, ...), reduces them to the tensor amax and fills tab for g = amax / 2688, while the other waves
+// slots l + 64 k), reduces them to the tensor amax and fills tab for g = amax / 2688, while the other waves
 // wait at the one barrier that follows.  Returns the amax bits, equal in every thread; slow (uniform) is set when
 // some slot stayed empty past wait_ticks, and then neither the return value nor tab is valid.  Uses red[16].
 template <bool RHT>
@@ -794,19 +794,30 @@ __device__ uint32_t exchange_max(uint32_t mbits, uint64_t wait_ticks, uint32_t* 
         uint32_t m = wave_max(lane < kColRB ? red[lane] : 0u);
         if (lane == 0)
             __hip_atomic_store(&g_fused_slot[blockIdx.x], (1ull << 32) | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // A lane reads its slots four at a time with the four loads in flight together: each read is a round trip
+        // to memory (the slots are shared by all XCDs), so reading them one after another would cost four.
         m = 0;
         bool waited_out = false;
         const uint64_t t0 = wall_clock64();
-        for (uint32_t i = lane; i < gridDim.x && !waited_out; i += 64) {
-            uint64_t sv;
-            while ((sv = __hip_atomic_load(&g_fused_slot[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
+        for (uint32_t base = lane; base < gridDim.x && !waited_out; base += 256) {
+            uint64_t sv[4];
+            while (true) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t i = base + 64 * k;
+                    sv[k] = i < gridDim.x
+                                ? __hip_atomic_load(&g_fused_slot[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                : (1ull << 32);
+                }
+                if (sv[0] != 0 && sv[1] != 0 && sv[2] != 0 && sv[3] != 0) break;
                 if (wall_clock64() - t0 >= wait_ticks) {
                     waited_out = true;
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);
             }
-            m = umax(m, (uint32_t)sv);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) m = umax(m, (uint32_t)sv[k]);
         }
         m = wave_max(m);
         const bool out = __ballot(waited_out) != 0;
