@@ -743,11 +743,16 @@ k_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, Co
 // clears its own slot as its last action (every other workgroup has read it by then, or has given up waiting and
 // taken the slow route), so no counter has to be shared or reset.  Launches that overlap on one GPU share the
 // slots and must not.
+//   Each slot is written to kSlotCopies copies and workgroup b polls copy b % kSlotCopies: with one copy, every
+// workgroup polls the same few cache lines while it waits for the last one, and those reads queue behind each other
+// (the exchange then took ~2.5 us against a one-way latency of ~0.6 us between XCDs).
 // ------------------------------------------------------------------------------------------------------------
 constexpr uint32_t kFusedMaxGrid = 2048;
+constexpr uint32_t kSlotCopies = 16;
 constexpr uint64_t kWaitTicks = 5000000;        // 50 ms of the 100 MHz wall clock (the kernel's wait bound)
 
-__device__ uint64_t g_fused_slot[kFusedMaxGrid];   // 0, or (1 << 32) | tile maximum (magnitude bits)
+// 0, or (1 << 32) | tile maximum (magnitude bits); copy c of slot b at [c][b] (256 KiB per GPU)
+__device__ uint64_t g_fused_slot[kSlotCopies][kFusedMaxGrid];
 
 // Tensor amax of the column-wise view computed by one workgroup (the route taken after a timed-out wait); v is
 // used as scratch.  Valid in thread 0.
@@ -780,9 +785,11 @@ __device__ uint32_t wg_amax_colwise(const uint16_t* x, uint32_t cols, const ColG
 
 // The cross-workgroup step of the single-read kernels (1024-thread workgroups).  The workgroup maximum of mbits
 // (magnitude bits) goes to this workgroup's slot.  Wave 0 then reads the slots of every workgroup (lane l watches
-// slots l + 64 k), reduces them to the tensor amax and fills tab for g = amax / 2688, while the other waves
-// wait at the one barrier that follows.  Returns the amax bits, equal in every thread; slow (uniform) is set when
-// some slot stayed empty past wait_ticks, and then neither the return value nor tab is valid.  Uses red[16].
+// slots l + 64 k, four loads in flight together: each read is a round trip to memory, since the slots are shared by
+// all XCDs; a slot once seen filled is not read again, since every workgroup polls the same 16 cache lines),
+// reduces them to the tensor amax and fills tab for g = amax / 2688, while the other waves wait at the one barrier
+// that follows.  Returns the amax bits, equal in every thread; slow (uniform) is set when some slot stayed empty
+// past wait_ticks, and then neither the return value nor tab is valid.  Uses red[16].
 template <bool RHT>
 __device__ uint32_t exchange_max(uint32_t mbits, uint64_t wait_ticks, uint32_t* red, RTable& tab, bool& slow) {
     __shared__ uint32_t s_max, s_out;
@@ -792,23 +799,22 @@ __device__ uint32_t exchange_max(uint32_t mbits, uint64_t wait_ticks, uint32_t* 
     __syncthreads();
     if (threadIdx.x < 64) {
         uint32_t m = wave_max(lane < kColRB ? red[lane] : 0u);
-        if (lane == 0)
-            __hip_atomic_store(&g_fused_slot[blockIdx.x], (1ull << 32) | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // A lane reads its slots four at a time with the four loads in flight together: each read is a round trip
-        // to memory (the slots are shared by all XCDs), so reading them one after another would cost four.
+        if (lane < kSlotCopies)
+            __hip_atomic_store(&g_fused_slot[lane][blockIdx.x], (1ull << 32) | m, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t* copy = g_fused_slot[blockIdx.x % kSlotCopies];
         m = 0;
         bool waited_out = false;
         const uint64_t t0 = wall_clock64();
         for (uint32_t base = lane; base < gridDim.x && !waited_out; base += 256) {
             uint64_t sv[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) sv[k] = base + 64 * k < gridDim.x ? 0ull : (1ull << 32);
             while (true) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const uint32_t i = base + 64 * k;
-                    sv[k] = i < gridDim.x
-                                ? __hip_atomic_load(&g_fused_slot[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                : (1ull << 32);
-                }
+                for (int k = 0; k < 4; ++k)
+                    if (sv[k] == 0)
+                        sv[k] = __hip_atomic_load(&copy[base + 64 * k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (sv[0] != 0 && sv[1] != 0 && sv[2] != 0 && sv[3] != 0) break;
                 if (wall_clock64() - t0 >= wait_ticks) {
                     waited_out = true;
@@ -837,8 +843,8 @@ __device__ uint32_t exchange_max(uint32_t mbits, uint64_t wait_ticks, uint32_t* 
 // Clears this workgroup's slot: the last action of a single-read kernel (every other workgroup has read the slot by
 // then, or has given up waiting and taken the slow route).
 __device__ __forceinline__ void release_slot() {
-    if (threadIdx.x == 0)
-        __hip_atomic_store(&g_fused_slot[blockIdx.x], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x < kSlotCopies)
+        __hip_atomic_store(&g_fused_slot[threadIdx.x][blockIdx.x], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int MODE>
