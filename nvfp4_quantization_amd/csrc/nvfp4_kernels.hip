@@ -653,18 +653,20 @@ __device__ __forceinline__ void col_write_out_stash(const ColStash& st, const Co
     }
 }
 
-// Writes the codes/scales of column blocks j = 2 jp and 2 jp + 1 of every lane held in a ColStash: thread t takes
-// row-block t % 16 of column 8 (t / 16) + j, so 16 consecutive threads write one column's 128 contiguous code bytes.
-__device__ __forceinline__ void col_write_out_pair(const ColStash& st, const ColPos& p, uint32_t rows, uint32_t cols,
-                                                   uint32_t nrb, int jp, uint8_t* __restrict__ codes,
-                                                   uint8_t* __restrict__ scales) {
+// Writes the codes/scales of column blocks j = G jg .. G jg + G - 1 of every lane held in a ColStash: thread t
+// takes row-block t % 16 of column 8 (t / 16) + j, so 16 consecutive threads write one column's 128 contiguous code
+// bytes.
+template <int G>
+__device__ __forceinline__ void col_write_out_group(const ColStash& st, const ColPos& p, uint32_t rows,
+                                                    uint32_t cols, uint32_t nrb, int jg, uint8_t* __restrict__ codes,
+                                                    uint8_t* __restrict__ scales) {
     const uint32_t col0 = p.strip * 512;
     const uint32_t ncol = min(512u, cols - col0), nr = min((uint32_t)kColRB, nrb - p.group * kColRB);
     const uint32_t rbl = threadIdx.x % kColRB, lq = threadIdx.x / kColRB, rb = p.group * kColRB + rbl;
     if (rbl >= nr) return;
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-        const uint32_t j = 2 * jp + jj, cl = 8 * lq + j;
+    for (int jj = 0; jj < G; ++jj) {
+        const uint32_t j = G * jg + jj, cl = 8 * lq + j;
         if (cl < ncol) {
             const uint4 e = st.e[rbl][j * 64 + lq];
             const uint32_t c = col0 + cl;
@@ -847,6 +849,8 @@ __device__ __forceinline__ void release_slot() {
         __hip_atomic_store(&g_fused_slot[threadIdx.x][blockIdx.x], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+constexpr int kOutGroup = 2;   // column blocks per write-out in phase 2 of the single-read kernel
+
 template <int MODE>
 __global__ void __launch_bounds__(kColThreads)
 k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColGrid cg, uint32_t sign_mask,
@@ -893,7 +897,13 @@ k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t col
         __shared__ uint32_t s_bits;
         const uint32_t mm = wg_amax_colwise<RHT>(x, cols, cg, sign_mask, v, red);
         if (threadIdx.x == 0) s_bits = mm;
-        if (active) load_col_tile(x, cols, pos, v);
+        if (active) {
+            load_col_tile(x, cols, pos, v);
+            // wait for the reloaded tile here: left pending, the wait would land in phase 2 on the common path,
+            // where it also waits for the write-out stores
+#pragma unroll
+            for (int k = 0; k < 16; ++k) asm volatile("" : "+v"(v[k].x), "+v"(v[k].y), "+v"(v[k].z), "+v"(v[k].w));
+        }
         __syncthreads();
         abits = __builtin_amdgcn_readfirstlane(s_bits);
         fill_rtable<RHT>(tab, global_scale(as_f(abits)));
@@ -905,14 +915,14 @@ k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t col
         amax_out[0] = amax;
         gout[0] = g;
     }
-    // Two blocks at a time: quantize, then (after a barrier) write them out, so that the stores of one pair overlap
-    // the arithmetic of the next.
+    // kOutGroup blocks at a time: quantize, then (after a barrier) write them out, so that the stores of one group
+    // overlap the arithmetic of the next.
 #pragma unroll
-    for (int jp = 0; jp < 4; ++jp) {
+    for (int jg = 0; jg < 8 / kOutGroup; ++jg) {
         if (active) {
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int j = 2 * jp + jj;
+            for (int jj = 0; jj < kOutGroup; ++jj) {
+                const int j = kOutGroup * jg + jj;
                 uint4& slot = st.e[wave][j * 64 + pos.lane];
                 Rand4 inv{{0, 0, 0, 0}};
                 if (SR) {
@@ -927,7 +937,7 @@ k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t col
             }
         }
         __syncthreads();
-        col_write_out_pair(st, pos, rows, cols, cg.nrb, jp, codes, scales);
+        col_write_out_group<kOutGroup>(st, pos, rows, cols, cg.nrb, jg, codes, scales);
     }
     release_slot();
 }
