@@ -20,7 +20,10 @@ Also printed in the same JSON line:
                 traffic measured with rocprofv3 counters (null unless measured on the current kernel source);
   cpu_baseline  the CPU oracle (test infrastructure) on the same workload, timed on the host cores;
   extra         the two-pass step (nvfp4_amax + nvfp4_quantize_rht_sr), the quantize kernel alone given a
-                device-resident amax (the pages' kernel-only comparison), the amax call, and the row-wise RHT+SR pass.
+                device-resident amax (the pages' kernel-only comparison), the amax call, the row-wise RHT+SR pass,
+                and under "configs" the other workloads: the 256x1024 RHT+SR/RN pair, the 8192x4096 row-wise RN
+                activation pass, the 14336x4096 16x16 weight pass (W and W^T), the 16384x8192 four-over-six pass
+                and the decode of its output (each timed as a graph of K launches, inputs rotating through HBM).
 """
 from __future__ import annotations
 
@@ -59,6 +62,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target duration of the CPU-oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--config-launches", type=int, default=50,
+                   help="graph launches per kernel for the other workloads (0 skips them)")
     p.add_argument("--counter-launches", type=int, default=0, metavar="N",
                    help="for a rocprofv3 --pmc run: launch N steps eagerly, then N copies of a 128 MiB buffer "
                         "(the calibration copy), and exit without timing")
@@ -123,6 +128,93 @@ def time_graph(g: torch.cuda.CUDAGraph) -> float:
     stop.record()
     torch.cuda.synchronize()
     return start.elapsed_time(stop)
+
+
+def gbs(nbytes: int, ms: float) -> float:
+    return round(nbytes / (ms * 1e-3) / 1e9, 2)
+
+
+def config_figures(Q, W, dev, launches: int) -> dict:
+    """Kernel times of the other workloads, each as the mean over a graph of `launches` launches whose inputs
+    rotate over enough buffers to exceed twice the Infinity Cache."""
+    out = {}
+
+    def rotation(x_bits, extra_bytes):
+        x = torch.from_numpy(x_bits.view(np.int16)).to(dev)
+        n = max(2, -(-2 * MALL_BYTES // (x.numel() * 2 + extra_bytes)) + 1)
+        return [x] + [x.clone() for _ in range(n - 1)]
+
+    def timed(fn):
+        return time_graph(capture(fn, 0, launches)) / launches
+
+    # 256 x 1024, row-wise, RHT+SR and RN, amax and quantization in one call each (launch-bound at this size)
+    xb = W.make("rht_sr_small_256x1024")
+    x = torch.from_numpy(xb.view(np.int16)).to(dev)
+    o = Q.alloc_out(256, 1024, Q.G_PER_TENSOR, dev)
+    a = torch.empty(1, dtype=torch.float32, device=dev)
+    m0 = W.sign_mask(0, 0)
+    out["rht_sr_small_256x1024"] = {
+        "call": "nvfp4_amax_quantize, row-wise",
+        "rht_sr_us": round(1e3 * timed(lambda k: Q.nvfp4_amax_quantize(x, Q.ROWWISE, Q.ROUND_RHT_SR, m0, 0, k,
+                                                                         amax=a, out=o)), 2),
+        "rn_us": round(1e3 * timed(lambda k: Q.nvfp4_amax_quantize(x, Q.ROWWISE, Q.ROUND_RN, amax=a, out=o)), 2),
+        "bytes_per_call": algorithmic_bytes(256, 1024)}
+
+    # 8192 x 4096 activations, row-wise RN: single read, and the quantize kernel given the amax
+    r, c = 8192, 4096
+    xs = rotation(W.make("fprop_rn_8192x4096"), algorithmic_bytes(r, c) - 2 * r * c)
+    n = len(xs)
+    outs = [Q.alloc_out(r, c, Q.G_PER_TENSOR, dev) for _ in range(n)]
+    am = [Q.nvfp4_amax(xs[i], Q.ROWWISE, Q.G_PER_TENSOR) for i in range(n)]
+    b = algorithmic_bytes(r, c)
+    single = timed(lambda k: Q.nvfp4_amax_quantize(xs[k % n], Q.ROWWISE, Q.ROUND_RN, amax=am[k % n], out=outs[k % n]))
+    qonly = timed(lambda k: Q.nvfp4_quantize_rn(xs[k % n], am[k % n], Q.BLOCK_1X16, Q.ROWWISE, Q.G_PER_TENSOR,
+                                                row_out=outs[k % n]))
+    out["fprop_rn_8192x4096"] = {
+        "single_read_us": round(1e3 * single, 2), "single_read_gbs": gbs(b, single),
+        "quantize_kernel_us": round(1e3 * qonly, 2), "quantize_kernel_gbs": gbs(b, qonly),
+        "quantize_kernel_frac_of_hbm_peak": round(gbs(b, qonly) / HBM_PEAK_GBS, 4)}
+    del xs, outs, am
+
+    # 14336 x 4096 weight, 16x16 blocks, W and W^T from one read (amax given)
+    r, c = 14336, 4096
+    b16 = 2 * r * c + 2 * (r * c // 2) + 2 * (r * c // 16) + 4
+    xs = rotation(W.make("weight_16x16_14336x4096"), b16 - 2 * r * c)
+    n = len(xs)
+    outs = [(Q.alloc_out(r, c, Q.G_PER_TENSOR, dev), Q.alloc_out(c, r, Q.G_PER_TENSOR, dev)) for _ in range(n)]
+    am = [Q.nvfp4_amax(xs[i], Q.ROWWISE, Q.G_PER_TENSOR) for i in range(n)]
+    t16 = timed(lambda k: Q.nvfp4_quantize_rn(xs[k % n], am[k % n], Q.BLOCK_16X16, Q.BOTH, Q.G_PER_TENSOR,
+                                              row_out=outs[k % n][0], col_out=outs[k % n][1]))
+    ta = timed(lambda k: Q.nvfp4_amax(xs[k % n], Q.ROWWISE, Q.G_PER_TENSOR, amax=am[k % n]))
+    out["weight_16x16_14336x4096"] = {
+        "quantize_kernel_us": round(1e3 * t16, 2), "quantize_kernel_gbs": gbs(b16, t16),
+        "quantize_kernel_frac_of_hbm_peak": round(gbs(b16, t16) / HBM_PEAK_GBS, 4), "bytes_per_call": b16,
+        "amax_us": round(1e3 * ta, 2)}
+    del xs, outs, am
+
+    # 16384 x 8192 four-over-six with per-row g (per-row amax given), and the decode of its output
+    r, c = 16384, 8192
+    b46 = 2 * r * c + r * c // 2 + r * c // 16 + 4 * r
+    xs = rotation(W.make("four_over_six_16384x8192"), b46 - 2 * r * c)
+    n = len(xs)
+    outs = [Q.alloc_out(r, c, Q.G_PER_ROW, dev) for _ in range(n)]
+    am = [Q.nvfp4_amax(xs[i], Q.ROWWISE, Q.G_PER_ROW) for i in range(n)]
+    t46 = timed(lambda k: Q.nvfp4_quantize_4o6(xs[k % n], am[k % n], Q.G_PER_ROW, out=outs[k % n]))
+    tar = timed(lambda k: Q.nvfp4_amax(xs[k % n], Q.ROWWISE, Q.G_PER_ROW, amax=am[k % n]))
+    out["four_over_six_16384x8192"] = {
+        "quantize_kernel_us": round(1e3 * t46, 2), "quantize_kernel_gbs": gbs(b46, t46),
+        "quantize_kernel_frac_of_hbm_peak": round(gbs(b46, t46) / HBM_PEAK_GBS, 4), "bytes_per_call": b46,
+        "per_row_amax_us": round(1e3 * tar, 2)}
+    del xs
+    y = torch.empty((r, c), dtype=torch.float32, device=dev)
+    bdq = r * c // 2 + r * c // 16 + 4 * r + 4 * r * c
+    tdq = timed(lambda k: Q.nvfp4_dequantize(outs[k % n].codes, outs[k % n].scales, outs[k % n].g, Q.G_PER_ROW, y=y))
+    out["dequantize_16384x8192"] = {
+        "kernel_us": round(1e3 * tdq, 2), "gbs": gbs(bdq, tdq),
+        "frac_of_hbm_peak": round(gbs(bdq, tdq) / HBM_PEAK_GBS, 4), "bytes_per_call": bdq}
+    del outs, am, y
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(x_bits: np.ndarray, masks, target_s: float) -> dict:
@@ -211,6 +303,8 @@ def main():
     rowq = lambda k: Q.nvfp4_quantize_rht_sr(xs[k % nbuf], row_amax, masks[0], SEED, k, Q.ROWWISE, Q.G_PER_TENSOR,
                                              out=row_outs[k % nbuf])
     row_ms = time_graph(capture(rowq, 0, args.steps)) / args.steps
+    del row_outs
+    configs = config_figures(Q, W, dev, args.config_launches) if args.config_launches else {}
 
     result = {
         "metric": "effective GB/s (bf16 in + fp4/scale out) and % of HBM peak, 8192x4096 RHT+SR",
@@ -245,6 +339,7 @@ def main():
             "rowwise_rht_sr_kernel_ms": round(row_ms, 5),
             "rowwise_rht_sr_kernel_gbs": round(step_bytes / (row_ms * 1e-3) / 1e9, 2),
             "pages_context": "~1270 GB/s (~71% of HBM peak) fused RHT+SR kernel on an RTX 5090, shape unstated",
+            "configs": configs,
         },
     }
     if not args.no_cpu_baseline:
