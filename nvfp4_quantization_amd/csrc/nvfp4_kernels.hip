@@ -1122,6 +1122,17 @@ k_quant_4o6(const uint4* __restrict__ x, uint32_t total_blocks, FastDiv per_row,
         float xv[16];
         widen_row_block<false>(a, b, 0u, xv);
         const float m = absmax16(xv);
+        if (!(__builtin_fabsf(g) < __builtin_inff())) [[unlikely]] {
+            // NaN or infinite g (a row whose amax is NaN or infinite): every multiplier is NaN, so both candidates
+            // give codes 0x7 and NaN errors (the map-to-6 one is kept).  Its scale code is 0 where the quotient is 0
+            // (bamax = 0; with an infinite g, any finite bamax) and 0x7F (NaN) otherwise.
+            const uint32_t sb = (g != g) ? (m == 0.0f ? 0u : 0x7Fu) : (m < __builtin_inff() ? 0u : 0x7Fu);
+            st_nt(codes + n, make_uint2(0x77777777u, 0x77777777u));
+            st_nt(scales + n, (uint8_t)sb);
+            a = a2;
+            b = b2;
+            continue;
+        }
         uint32_t cand_lo[2], cand_hi[2], cand_sb[2];
         float err[2];
 #pragma unroll
