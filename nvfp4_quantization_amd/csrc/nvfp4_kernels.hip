@@ -69,26 +69,9 @@ __device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
     return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
 }
 
-__device__ __forceinline__ Rand4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
-                                               uint32_t k1) {
-#pragma unroll
-    for (int round = 0; round < 10; ++round) {
-        const uint64_t pa = (uint64_t)kPhiloxMulA * c0;
-        const uint64_t pb = (uint64_t)kPhiloxMulB * c2;
-        const uint32_t n0 = xor3((uint32_t)(pb >> 32), c1, k0);
-        const uint32_t n2 = xor3((uint32_t)(pa >> 32), c3, k1);
-        c1 = (uint32_t)pb;
-        c3 = (uint32_t)pa;
-        c0 = n0;
-        c2 = n2;
-        k0 += kPhiloxWeylA;
-        k1 += kPhiloxWeylB;
-    }
-    return Rand4{{c0, c1, c2, c3}};
-}
-
-// The same generator returning the bitwise complement of the four output words (folded into the last round's
-// three-way xors where possible).
+// Philox4x32-10 of counter (c0, c1, c2, c3) and key (k0, k1), returning the bitwise complement of the four output
+// words (the SR seeds need 255 - rho); the complement is folded into the last round's three-way xors where
+// possible.
 __device__ __forceinline__ Rand4 philox4x32_10_inv(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
                                                    uint32_t k1) {
 #pragma unroll
