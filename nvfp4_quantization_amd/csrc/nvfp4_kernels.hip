@@ -1072,18 +1072,71 @@ __device__ __forceinline__ void unpack8(uint32_t d, float (&v)[8]) {
     v[4] = p2.x; v[5] = p2.y; v[6] = p3.x; v[7] = p3.y;
 }
 
-template <bool PER_ROW>
-__global__ void __launch_bounds__(kThreads)
-k_quant_4o6(const uint4* __restrict__ x, uint32_t total_blocks, FastDiv per_row, const float* __restrict__ amax,
-            uint2* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gout) {
-    float g = 0.0f;
-    Divisor dv[2] = {};   // T = 6 and T = 4
-    if (!PER_ROW) {
-        g = global_scale(amax[0]);
-        if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
-        dv[0] = make_divisor_uniform(6.0f * g);
-        dv[1] = make_divisor_uniform(4.0f * g);
+// One block: both candidates, their decoded squared errors, and the choice.  xv are the 16 values, m their absmax,
+// dv the divisors 6 g and 4 g, tab the multipliers of g.  A NaN or infinite g (a row whose amax is NaN or infinite)
+// makes every multiplier NaN: both candidates give codes 0x7 and NaN errors (the map-to-6 one is kept), and its
+// scale code is 0 where the quotient is 0 (bamax = 0; with an infinite g, any finite bamax), 0x7F (NaN) otherwise;
+// that case is written directly.
+__device__ __forceinline__ void quant_4o6_block(const float (&xv)[16], float m, float g, const Divisor (&dv)[2],
+                                                const RTable& tab, uint32_t& lo_out, uint32_t& hi_out,
+                                                uint32_t& sb_out) {
+    if (!(__builtin_fabsf(g) < __builtin_inff())) [[unlikely]] {
+        sb_out = (g != g) ? (m == 0.0f ? 0u : 0x7Fu) : (m < __builtin_inff() ? 0u : 0x7Fu);
+        lo_out = hi_out = 0x77777777u;
+        return;
     }
+    uint32_t cand_lo[2], cand_hi[2], cand_sb[2];
+    float err[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const uint32_t sb = scale_code(m, dv[c]);
+        const float r = tab.r[sb];
+        const bool fast = tab.rq[sb] == tab.rq[sb];   // see fast_multiplier
+        float q[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) q[i] = xv[i] * r;
+        const float(&q0)[8] = *reinterpret_cast<const float(*)[8]>(&q[0]);
+        const float(&q1)[8] = *reinterpret_cast<const float(*)[8]>(&q[8]);
+        uint32_t lo = pack8_rn(q0), hi = pack8_rn(q1);
+        if (!fast) [[unlikely]] {
+            lo = patch_nan8(lo, q0);
+            hi = patch_nan8(hi, q1);
+        }
+        const float sbf = e4m3_decode(sb);
+        float dq[16];
+        unpack8(lo, *reinterpret_cast<float(*)[8]>(&dq[0]));
+        unpack8(hi, *reinterpret_cast<float(*)[8]>(&dq[8]));
+        float e[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float df = (dq[i] * sbf) * g - xv[i];
+            e[i] = df * df;
+        }
+#pragma unroll
+        for (int s = 8; s >= 1; s >>= 1)
+#pragma unroll
+            for (int i = 0; i < s; ++i) e[i] = e[i] + e[i + s];
+        cand_lo[c] = lo;
+        cand_hi[c] = hi;
+        cand_sb[c] = sb;
+        err[c] = e[0];
+    }
+    const int pick = (err[1] < err[0]) ? 1 : 0;
+    lo_out = cand_lo[pick];
+    hi_out = cand_hi[pick];
+    sb_out = cand_sb[pick];
+}
+
+// Per-tensor g: grid-stride over blocks with the next block's loads in flight; the multipliers of the 128 scale
+// codes are tabulated once per workgroup.
+__global__ void __launch_bounds__(kThreads)
+k_quant_4o6_tensor(const uint4* __restrict__ x, uint32_t total_blocks, const float* __restrict__ amax,
+                   uint2* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gout) {
+    __shared__ RTable tab;
+    const float g = global_scale(amax[0]);
+    if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
+    const Divisor dv[2] = {make_divisor_uniform(6.0f * g), make_divisor_uniform(4.0f * g)};   // T = 6 and T = 4
+    fill_rtable<false>(tab, g);
     const uint32_t stride = gridDim.x * kThreads;
     uint32_t n = blockIdx.x * kThreads + threadIdx.x;
     if (n >= total_blocks) return;
@@ -1095,68 +1148,68 @@ k_quant_4o6(const uint4* __restrict__ x, uint32_t total_blocks, FastDiv per_row,
             a2 = ld16(x + 2 * (size_t)nn);
             b2 = ld16(x + 2 * (size_t)nn + 1);
         }
-        if (PER_ROW) {
-            const uint32_t row = fdiv(n, per_row);
-            g = global_scale(amax[row]);
-            if (n == row * per_row.d) gout[row] = g;
-            dv[0] = make_divisor(6.0f * g);
-            dv[1] = make_divisor(4.0f * g);
-        }
         float xv[16];
         widen_row_block<false>(a, b, 0u, xv);
-        const float m = absmax16(xv);
-        if (!(__builtin_fabsf(g) < __builtin_inff())) [[unlikely]] {
-            // NaN or infinite g (a row whose amax is NaN or infinite): every multiplier is NaN, so both candidates
-            // give codes 0x7 and NaN errors (the map-to-6 one is kept).  Its scale code is 0 where the quotient is 0
-            // (bamax = 0; with an infinite g, any finite bamax) and 0x7F (NaN) otherwise.
-            const uint32_t sb = (g != g) ? (m == 0.0f ? 0u : 0x7Fu) : (m < __builtin_inff() ? 0u : 0x7Fu);
-            st_nt(codes + n, make_uint2(0x77777777u, 0x77777777u));
+        uint32_t lo, hi, sb;
+        quant_4o6_block(xv, absmax16(xv), g, dv, tab, lo, hi, sb);
+        st_nt(codes + n, make_uint2(lo, hi));
+        st_nt(scales + n, (uint8_t)sb);
+        a = a2;
+        b = b2;
+    }
+}
+
+// Per-row g: a workgroup walks whole rows (grid-stride over rows), lane t taking blocks t, t + 256, ... of each, with
+// the next block's loads (in this row or the next) in flight.  g, its two divisors and the row's multiplier table
+// are computed once per row: the table is double-buffered, so one barrier per row orders it (a thread writes the
+// table of row i only after the barrier of row i - 1, which every thread passes only after its reads of row i - 2).
+__global__ void __launch_bounds__(kThreads)
+k_quant_4o6_rows(const uint4* __restrict__ x, uint32_t rows, uint32_t bpr, const float* __restrict__ amax,
+                 uint2* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gout) {
+    __shared__ RTable tabs[2];
+    const uint32_t t = threadIdx.x;
+    uint32_t row = blockIdx.x;
+    uint4 a = make_uint4(0, 0, 0, 0), b = a;
+    if (row < rows && t < bpr) {
+        const size_t n0 = (size_t)row * bpr + t;
+        a = ld16(x + 2 * n0);
+        b = ld16(x + 2 * n0 + 1);
+    }
+    for (uint32_t parity = 0; row < rows; row += gridDim.x, parity ^= 1u) {
+        const float g = global_scale(amax[row]);
+        if (t == 0) gout[row] = g;
+        // a NaN or infinite g needs neither the table nor the divisors (every block of the row is written directly)
+        const bool finite = __builtin_amdgcn_readfirstlane((uint32_t)(__builtin_fabsf(g) < __builtin_inff())) != 0;
+        RTable& tab = tabs[parity];
+        if (finite && t < 128) fill_rtable_entry<false>(tab, t, g);
+        __syncthreads();
+        Divisor dv[2] = {};
+        if (finite) {
+            dv[0] = make_divisor_uniform(6.0f * g);
+            dv[1] = make_divisor_uniform(4.0f * g);
+        }
+        for (uint32_t blk = t; blk < bpr; blk += kThreads) {
+            uint32_t nrow = row, nblk = blk + kThreads;
+            if (nblk >= bpr) {
+                nrow = row + gridDim.x;
+                nblk = t;
+            }
+            uint4 a2 = a, b2 = b;
+            if (nrow < rows) {
+                const size_t nn = (size_t)nrow * bpr + nblk;
+                a2 = ld16(x + 2 * nn);
+                b2 = ld16(x + 2 * nn + 1);
+            }
+            float xv[16];
+            widen_row_block<false>(a, b, 0u, xv);
+            uint32_t lo, hi, sb;
+            quant_4o6_block(xv, absmax16(xv), g, dv, tab, lo, hi, sb);
+            const size_t n = (size_t)row * bpr + blk;
+            st_nt(codes + n, make_uint2(lo, hi));
             st_nt(scales + n, (uint8_t)sb);
             a = a2;
             b = b2;
-            continue;
         }
-        uint32_t cand_lo[2], cand_hi[2], cand_sb[2];
-        float err[2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const uint32_t sb = scale_code(m, dv[c]);
-            const float r = scale_multiplier(sb, g);
-            const bool fast = r > 0.0f && r <= kFltMax;
-            float q[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) q[i] = xv[i] * r;
-            const float(&q0)[8] = *reinterpret_cast<const float(*)[8]>(&q[0]);
-            const float(&q1)[8] = *reinterpret_cast<const float(*)[8]>(&q[8]);
-            uint32_t lo = pack8_rn(q0), hi = pack8_rn(q1);
-            if (!fast) {
-                lo = patch_nan8(lo, q0);
-                hi = patch_nan8(hi, q1);
-            }
-            const float sbf = e4m3_decode(sb);
-            float dv[16];
-            unpack8(lo, *reinterpret_cast<float(*)[8]>(&dv[0]));
-            unpack8(hi, *reinterpret_cast<float(*)[8]>(&dv[8]));
-            float e[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float df = (dv[i] * sbf) * g - xv[i];
-                e[i] = df * df;
-            }
-#pragma unroll
-            for (int s = 8; s >= 1; s >>= 1)
-#pragma unroll
-                for (int i = 0; i < s; ++i) e[i] = e[i] + e[i + s];
-            cand_lo[c] = lo;
-            cand_hi[c] = hi;
-            cand_sb[c] = sb;
-            err[c] = e[0];
-        }
-        const int pick = (err[1] < err[0]) ? 1 : 0;
-        st_nt(codes + n, make_uint2(cand_lo[pick], cand_hi[pick]));
-        st_nt(scales + n, (uint8_t)cand_sb[pick]);
-        a = a2;
-        b = b2;
     }
 }
 
@@ -1605,14 +1658,14 @@ hipError_t launch_quant_4o6(const uint16_t* x, int64_t rows, int64_t cols, bool 
     if (rows == 0 || cols == 0) return write_empty_g(amax, g, per_row ? (uint32_t)rows : 1u, stream);
     const uint32_t bpr = (uint32_t)(cols / 16);
     const uint32_t total = (uint32_t)(rows * bpr);
-    const FastDiv fd = make_fastdiv(bpr);
-    const uint32_t grid = grid_for(total, kThreads, 8);
-    if (per_row)
-        k_quant_4o6<true><<<grid, kThreads, 0, stream>>>(reinterpret_cast<const uint4*>(x), total, fd, amax,
-                                                          reinterpret_cast<uint2*>(codes), scales, g);
-    else
-        k_quant_4o6<false><<<grid, kThreads, 0, stream>>>(reinterpret_cast<const uint4*>(x), total, fd, amax,
-                                                           reinterpret_cast<uint2*>(codes), scales, g);
+    const uint4* xv = reinterpret_cast<const uint4*>(x);
+    uint2* cv = reinterpret_cast<uint2*>(codes);
+    if (per_row) {
+        const uint32_t grid = (uint32_t)std::min<int64_t>(rows, (int64_t)cu_count() * 8);
+        k_quant_4o6_rows<<<grid, kThreads, 0, stream>>>(xv, (uint32_t)rows, bpr, amax, cv, scales, g);
+    } else {
+        k_quant_4o6_tensor<<<grid_for(total, kThreads, 8), kThreads, 0, stream>>>(xv, total, amax, cv, scales, g);
+    }
     return hipGetLastError();
 }
 
