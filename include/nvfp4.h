@@ -40,7 +40,7 @@
  *   - Alignment: x, codes, scales and y must be 16-byte aligned; amax and g 4-byte aligned.
  *   - Sizes: rows, cols >= 0; rows * cols < 2^35.  Column-wise views and 16x16 blocks also need cols < 2^26.
  *     A zero-sized tensor is valid: its amax is 0 and a quantize call only writes g.
- *   - Calls on different streams may run concurrently; they share no state (nvfp4_amax_quantize excepted: see it).
+ *   - Calls on different streams may run concurrently; they share no state (nvfp4_amax_quantize: see it).
  */
 #ifndef NVFP4_H
 #define NVFP4_H
@@ -120,10 +120,11 @@ nvfp4_status nvfp4_quantize_rht_sr(const uint16_t* x, int64_t rows, int64_t cols
  *   A tensor that fits one workgroup per CU is read from memory once: column-wise up to one 256-row x
  *   512-column tile per CU, row-wise up to 8192 blocks per CU (8192 x 4096 either way on MI355X).  Each
  *   workgroup keeps its share in registers, publishes its maximum in a per-GPU slot array and waits for every
- *   other workgroup's; larger tensors run the two passes.  The slots reset themselves between launches: calls of
- *   this entry point must not overlap on one GPU (consecutive calls on a stream are fine).  The wait is bounded
- *   (50 ms): a workgroup that is still waiting then reads the whole tensor to compute the amax itself, so the
- *   result never changes, only the time (this happens when other work holds CUs).
+ *   other workgroup's; larger tensors run the two passes.  The slots reset themselves between launches, and
+ *   launches take them from 8 regions in turn: up to 8 calls may be in flight at once on one GPU (on different
+ *   streams); calls sharing a region must not overlap.  The wait is bounded (50 ms): a workgroup that is still
+ *   waiting then reads the whole tensor to compute the amax itself, so the result never changes, only the time
+ *   (this happens when other work, such as a concurrent call, holds CUs).
  *   rounding: NVFP4_ROUND_RN, _SR or _RHT_SR; sign_mask is used with RHT, seed and offset with SR.
  *   amax: [1] device float (output).  Shapes and outputs as for the quantize calls. */
 nvfp4_status nvfp4_amax_quantize(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_orient orient,

@@ -27,6 +27,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
+
 #include "nvfp4_launch.h"
 
 
@@ -730,18 +732,20 @@ k_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, Co
 // seen every slot filled within a bound (50 ms; other work holding CUs) computes the amax by reading the whole tensor
 // itself, so the result is the same in every case, only slower.  Slots are zero between launches: each workgroup
 // clears its own slot as its last action (every other workgroup has read it by then, or has given up waiting and
-// taken the slow route), so no counter has to be shared or reset.  Launches that overlap on one GPU share the
-// slots and must not.
+// taken the slow route), so no counter has to be shared or reset.  Launches take their slots from one of
+// kSlotRegions regions in turn, so up to that many launches may be in flight at once on one GPU (on different
+// streams); more could share a region, and two launches sharing one must not overlap.
 //   Each slot is written to kSlotCopies copies and workgroup b polls copy b % kSlotCopies: with one copy, every
 // workgroup polls the same few cache lines while it waits for the last one, and those reads queue behind each other
 // (the exchange then took ~2.5 us against a one-way latency of ~0.6 us between XCDs).
 // ------------------------------------------------------------------------------------------------------------
 constexpr uint32_t kFusedMaxGrid = 2048;
 constexpr uint32_t kSlotCopies = 16;
+constexpr uint32_t kSlotRegions = 8;
 constexpr uint64_t kWaitTicks = 5000000;        // 50 ms of the 100 MHz wall clock (the kernel's wait bound)
 
-// 0, or (1 << 32) | tile maximum (magnitude bits); copy c of slot b at [c][b] (256 KiB per GPU)
-__device__ uint64_t g_fused_slot[kSlotCopies][kFusedMaxGrid];
+// 0, or (1 << 32) | tile maximum (magnitude bits); copy c of slot b of region r at [r][c][b] (2 MiB per GPU)
+__device__ uint64_t g_fused_slot[kSlotRegions][kSlotCopies][kFusedMaxGrid];
 
 // Tensor amax of the column-wise view computed by one workgroup (the route taken after a timed-out wait); v is
 // used as scratch.  Valid in thread 0.
@@ -780,7 +784,8 @@ __device__ uint32_t wg_amax_colwise(const uint16_t* x, uint32_t cols, const ColG
 // that follows.  Returns the amax bits, equal in every thread; slow (uniform) is set when some slot stayed empty
 // past wait_ticks, and then neither the return value nor tab is valid.  Uses red[16].
 template <bool RHT>
-__device__ uint32_t exchange_max(uint32_t mbits, uint64_t wait_ticks, uint32_t* red, RTable& tab, bool& slow) {
+__device__ uint32_t exchange_max(uint32_t mbits, uint64_t wait_ticks, uint32_t region, uint32_t* red, RTable& tab,
+                             bool& slow) {
     __shared__ uint32_t s_max, s_out;
     const uint32_t lane = threadIdx.x & 63u;
     mbits = wave_max(mbits);
@@ -789,9 +794,9 @@ __device__ uint32_t exchange_max(uint32_t mbits, uint64_t wait_ticks, uint32_t* 
     if (threadIdx.x < 64) {
         uint32_t m = wave_max(lane < kColRB ? red[lane] : 0u);
         if (lane < kSlotCopies)
-            __hip_atomic_store(&g_fused_slot[lane][blockIdx.x], (1ull << 32) | m, __ATOMIC_RELAXED,
+            __hip_atomic_store(&g_fused_slot[region][lane][blockIdx.x], (1ull << 32) | m, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-        const uint64_t* copy = g_fused_slot[blockIdx.x % kSlotCopies];
+        const uint64_t* copy = g_fused_slot[region][blockIdx.x % kSlotCopies];
         m = 0;
         bool waited_out = false;
         const uint64_t t0 = wall_clock64();
@@ -831,9 +836,10 @@ __device__ uint32_t exchange_max(uint32_t mbits, uint64_t wait_ticks, uint32_t* 
 
 // Clears this workgroup's slot: the last action of a single-read kernel (every other workgroup has read the slot by
 // then, or has given up waiting and taken the slow route).
-__device__ __forceinline__ void release_slot() {
+__device__ __forceinline__ void release_slot(uint32_t region) {
     if (threadIdx.x < kSlotCopies)
-        __hip_atomic_store(&g_fused_slot[threadIdx.x][blockIdx.x], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&g_fused_slot[region][threadIdx.x][blockIdx.x], 0ull, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 constexpr int kOutGroup = 2;   // column blocks per write-out in phase 2 of the single-read kernel
@@ -842,7 +848,7 @@ template <int MODE>
 __global__ void __launch_bounds__(kColThreads)
 k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColGrid cg, uint32_t sign_mask,
                      RngArgs rng, float* __restrict__ amax_out, uint8_t* __restrict__ codes,
-                     uint8_t* __restrict__ scales, float* __restrict__ gout, uint64_t wait_ticks) {
+                     uint8_t* __restrict__ scales, float* __restrict__ gout, uint64_t wait_ticks, uint32_t region) {
     constexpr bool SR = MODE != kRN;
     constexpr bool RHT = MODE == kRHTSR;
     __shared__ ColStash st;
@@ -878,7 +884,7 @@ k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t col
 #pragma unroll
     for (int k = 0; k < 16; ++k) asm volatile("" : "+v"(v[k].x), "+v"(v[k].y), "+v"(v[k].z), "+v"(v[k].w));
     bool slow;
-    uint32_t abits = exchange_max<RHT>(mbits, wait_ticks, red, tab, slow);
+    uint32_t abits = exchange_max<RHT>(mbits, wait_ticks, region, red, tab, slow);
     if (slow) {
         // slow route: the whole tensor's amax from this workgroup alone, then the tile again
         __shared__ uint32_t s_bits;
@@ -926,7 +932,7 @@ k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t col
         __syncthreads();
         col_write_out_group<kOutGroup>(st, pos, rows, cols, cg.nrb, jg, codes, scales);
     }
-    release_slot();
+    release_slot(region);
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -1371,7 +1377,7 @@ template <int MODE>
 __global__ void __launch_bounds__(kColThreads)
 k_amax_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, uint32_t bpl, uint32_t sign_mask,
                      RngArgs rng, float* __restrict__ amax_out, uint2* __restrict__ codes,
-                     uint8_t* __restrict__ scales, float* __restrict__ gout, uint64_t wait_ticks) {
+                     uint8_t* __restrict__ scales, float* __restrict__ gout, uint64_t wait_ticks, uint32_t region) {
     constexpr bool SR = MODE != kRN;
     constexpr bool RHT = MODE == kRHTSR;
     __shared__ ColStash st;
@@ -1415,7 +1421,7 @@ k_amax_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, uint32_
         asm volatile("" : "+v"(b[j].x), "+v"(b[j].y), "+v"(b[j].z), "+v"(b[j].w));
     }
     bool slow;
-    uint32_t abits = exchange_max<RHT>(mbits, wait_ticks, red, tab, slow);
+    uint32_t abits = exchange_max<RHT>(mbits, wait_ticks, region, red, tab, slow);
     if (slow) {
         // slow route: the whole tensor's amax from this workgroup alone (the tile stays in registers)
         __shared__ uint32_t s_bits;
@@ -1452,7 +1458,7 @@ k_amax_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, uint32_
             st_nt(scales + n, (uint8_t)sb);
         }
     }
-    release_slot();
+    release_slot(region);
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -1584,6 +1590,12 @@ hipError_t launch_quant_1x16(const uint16_t* x, int64_t rows, int64_t cols, bool
 
 // The single-read kernel's wait bound.  NVFP4_FUSED_WAIT_TICKS (100 MHz ticks) overrides it; the tests set 0 to
 // send every workgroup down the slow route (whole-tensor amax per workgroup) and check that it agrees.
+// Slot region of the next single-read launch: regions are taken in turn.
+uint32_t next_slot_region() {
+    static std::atomic<uint32_t> launches{0};
+    return launches.fetch_add(1, std::memory_order_relaxed) % kSlotRegions;
+}
+
 uint64_t fused_wait_ticks() {
     const char* e = getenv("NVFP4_FUSED_WAIT_TICKS");
     if (!e || !*e) return kWaitTicks;
@@ -1600,8 +1612,9 @@ hipError_t launch_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, bool
             uint32_t r = (uint32_t)rows, c = (uint32_t)cols;
             RngArgs ra = rng_args(rng);
             uint64_t wait = fused_wait_ticks();
+            uint32_t region = next_slot_region();
             void* args[] = {(void*)&x, &r, &c, (void*)&w, &sign_mask, &ra, (void*)&amax, (void*)&codes, (void*)&scales,
-                            (void*)&g, &wait};
+                            (void*)&g, &wait, &region};
             const void* fn = mode == kRN ? (const void*)k_amax_quant_colwise<kRN>
                              : mode == kSR ? (const void*)k_amax_quant_colwise<kSR>
                                            : (const void*)k_amax_quant_colwise<kRHTSR>;
@@ -1620,9 +1633,10 @@ hipError_t launch_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, bool
                 uint2* cv = reinterpret_cast<uint2*>(codes);
                 RngArgs ra = rng_args(rng);
                 uint64_t wait = fused_wait_ticks();
+                uint32_t region = next_slot_region();
                 uint32_t t = total, bp = bpl;
                 void* args[] = {(void*)&xv, &t, &bp, &sign_mask, &ra, (void*)&amax, (void*)&cv, (void*)&scales,
-                                (void*)&g, &wait};
+                                (void*)&g, &wait, &region};
                 const void* fn = mode == kRN ? (const void*)k_amax_quant_rowwise<kRN>
                                  : mode == kSR ? (const void*)k_amax_quant_rowwise<kSR>
                                                : (const void*)k_amax_quant_rowwise<kRHTSR>;

@@ -97,6 +97,33 @@ def test_rowwise_slow_route(monkeypatch, mode):
     check(x, mode, Q.ROWWISE, mask=W.sign_mask(5, 2), seed=5, offset=2)
 
 
+def test_concurrent_calls_on_two_streams():
+    """Single-read calls in flight at once on two streams, on tensors of very different magnitudes: each launch
+    exchanges its maxima in a slot region of its own, so neither sees the other's."""
+    xa = W.lognormal_gradients(1024, 2048, seed=61)
+    xb = W.gaussian(2048, 1024, seed=62, scale=1000.0)
+    cases = [(xa, Q.COLWISE, "rht_sr"), (xb, Q.ROWWISE, "sr"), (xb, Q.COLWISE, "rn"), (xa, Q.ROWWISE, "rht_sr")]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    devs = [torch.from_numpy(x.view(np.int16)).cuda() for x, _, _ in cases]
+    torch.cuda.synchronize()
+    results = []
+    for rep in range(3):
+        for i, (x, orient, mode) in enumerate(cases):
+            s_ = streams[i % 2]
+            with torch.cuda.stream(s_):
+                say("concurrent", rep, i, mode, x.shape)
+                results.append((i, rep) + Q.nvfp4_amax_quantize(devs[i], orient, ROUNDING[mode][0], 0x3C5A, 8, rep,
+                                                                stream=s_))
+    torch.cuda.synchronize()
+    for i, rep, a, o in results:
+        x, orient, mode = cases[i]
+        oa = O.amax(x, orient, O.G_PER_TENSOR, mode == "rht_sr", 0x3C5A)
+        oc, os_, og = O.quantize_1x16(x, oa, ROUNDING[mode][1], orient, O.G_PER_TENSOR, 0x3C5A, 8, rep)
+        assert (a.cpu().numpy().view(np.uint32) == oa.view(np.uint32)).all(), (i, rep)
+        assert np.array_equal(o.codes.cpu().numpy(), oc), (i, rep)
+        assert np.array_equal(o.scales.cpu().numpy(), os_), (i, rep)
+
+
 def test_nan_and_zero_tensors():
     x = W.lognormal_gradients(256, 512, seed=5)
     x[100, 7] = 0x7FC0                      # bf16 NaN
