@@ -6,6 +6,7 @@ The library is built in-tree next to this file so that it travels with the sourc
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 
@@ -34,29 +35,68 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the NVFP4 HIP library cannot be built")
 
 
-def _run(cmd: list[str]) -> None:
+RESOURCE_REPORT = os.path.join(ROOT, "_build", "kernel_resources.txt")
+
+
+def _run(cmd: list[str]) -> str:
+    """Runs hipcc; returns the kernel resource-usage remarks it printed (other output is passed through)."""
     p = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass of hipcc does not know the device-only feature flag; that warning is expected
     noise = ("packed-fp32-ops", "warning: unknown target feature", "1 warning generated")
-    msg = "\n".join(l for l in (p.stdout + p.stderr).splitlines() if not any(n in l for n in noise))
+    remarks, kept, in_remark = [], [], False
+    for l in (p.stdout + p.stderr).splitlines():
+        if "kernel-resource-usage" in l:
+            remarks.append(l)
+            in_remark = True
+        elif in_remark and re.match(r"^\s*\d*\s*\|", l):
+            continue                     # the source excerpt clang prints under a remark
+        else:
+            in_remark = False
+            if not any(n in l for n in noise):
+                kept.append(l)
+    msg = "\n".join(kept)
     if p.returncode != 0:
         raise RuntimeError("hipcc failed (%d):\n%s\n%s" % (p.returncode, " ".join(cmd), msg))
     if msg.strip():
         print(msg)
+    return "\n".join(remarks)
+
+
+def resource_table(remarks: str) -> list[dict]:
+    """Per kernel: name, VGPRs, AGPRs, spilled VGPRs and SGPRs, scratch bytes per lane, LDS bytes, occupancy."""
+    rows, cur = [], None
+    keys = {"VGPRs": "vgpr", "AGPRs": "agpr", "VGPRs Spill": "vgpr_spill", "SGPRs Spill": "sgpr_spill",
+            "ScratchSize [bytes/lane]": "scratch", "LDS Size [bytes/block]": "lds",
+            "Occupancy [waves/SIMD]": "occupancy"}
+    for line in remarks.splitlines():
+        body = line.split("remark:", 1)[-1].split("[-Rpass", 1)[0].strip()
+        if body.startswith("Function Name:"):
+            cur = {"name": body.split(":", 1)[1].strip()}
+            rows.append(cur)
+            continue
+        key, sep, val = body.partition(":")
+        if cur is not None and sep and key.strip() in keys and val.strip().isdigit():
+            cur[keys[key.strip()]] = int(val)
+    return rows
 
 
 def build(verbose: bool = False) -> str:
     """Compile every HIP source and link the shared library (always rebuilds)."""
     obj_dir = os.path.join(ROOT, "_build")
     os.makedirs(obj_dir, exist_ok=True)
-    objs = []
+    objs, remarks = [], []
     for src in SOURCES:
         obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
-        cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc(), *HIPCC_FLAGS, "-Rpass-analysis=kernel-resource-usage", f"-I{INCLUDE}", f"-I{CSRC}", "-c",
+               os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        _run(cmd)
+        remarks.append(_run(cmd))
         objs.append(obj)
+    # registers, spills, LDS and occupancy of every kernel, for the build's own check (tests read this file)
+    with open(RESOURCE_REPORT, "w") as f:
+        for r in resource_table("\n".join(remarks)):
+            f.write(" ".join(f"{k}={v}" for k, v in r.items()) + "\n")
     tmp = LIB_PATH + ".tmp%d" % os.getpid()
     _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB_PATH)

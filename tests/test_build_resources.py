@@ -1,0 +1,39 @@
+"""Register use of the built kernels (from the compiler's resource-usage remarks that the build records): no
+kernel may spill vector registers or use scratch memory (a spill in the hot loop turns into memory traffic per
+block; scalar registers spilled into vector-register lanes cost no memory), and the kernels that hold a whole tile
+in registers must keep one 1024-thread workgroup per CU (4 waves per SIMD)."""
+import os
+
+import pytest
+
+from nvfp4_quantization_amd import _build
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_build.RESOURCE_REPORT),
+                                reason="no build record (run the build first)")
+
+
+def kernels():
+    rows = []
+    with open(_build.RESOURCE_REPORT) as f:
+        for line in f:
+            rows.append(dict(kv.split("=", 1) for kv in line.split()))
+    return rows
+
+
+def test_every_kernel_is_listed():
+    names = " ".join(r["name"] for r in kernels())
+    for k in ("k_amax_quant_colwise", "k_amax_quant_rowwise", "k_quant_colwise", "k_quant_rowwise", "k_quant_16x16",
+              "k_quant_4o6_rows", "k_quant_4o6_tensor", "k_dequantize", "k_amax_colwise", "k_amax_rowwise_tensor"):
+        assert k in names, k
+
+
+def test_no_spills_to_memory():
+    spilled = [(r["name"], r.get("vgpr_spill"), r.get("scratch")) for r in kernels()
+               if int(r.get("vgpr_spill", 0)) or int(r.get("scratch", 0))]
+    assert not spilled, spilled
+
+
+def test_tile_kernels_keep_four_waves_per_simd():
+    for r in kernels():
+        if any(k in r["name"] for k in ("k_amax_quant_colwise", "k_quant_colwise", "k_quant_16x16")):
+            assert int(r["vgpr"]) <= 128 and int(r["occupancy"]) >= 4, r
