@@ -47,6 +47,7 @@ ROWS, COLS = 8192, 4096
 SEED = 2
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_amax_quant_colwise_rht_sr_8192x4096_traffic.txt")
 COPY_BYTES = 128 << 20       # the calibration copy for the L2-to-memory byte counters
+PERCENTILE_LAUNCHES = 200    # launches timed one by one for the percentiles
 
 
 def algorithmic_bytes(rows: int, cols: int) -> int:
@@ -132,6 +133,69 @@ def time_graph(g: torch.cuda.CUDAGraph) -> float:
 
 def gbs(nbytes: int, ms: float) -> float:
     return round(nbytes / (ms * 1e-3) / 1e9, 2)
+
+
+_bench_lib = None
+
+
+def bench_lib():
+    """The streaming ceiling kernel and the stream-hold kernel (libnvfp4_bench.so, built with the HIP library)."""
+    global _bench_lib
+    if _bench_lib is None:
+        import ctypes as C
+        from nvfp4_quantization_amd._build import BENCH_LIB_PATH
+        if not os.path.exists(BENCH_LIB_PATH):
+            raise RuntimeError(f"{BENCH_LIB_PATH} is missing: build first (python -m nvfp4_quantization_amd._build)")
+        L = C.CDLL(BENCH_LIB_PATH)
+        L.nvfp4_bench_stream.restype = C.c_int
+        L.nvfp4_bench_stream.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p]
+        L.nvfp4_bench_hold.restype = C.c_int
+        L.nvfp4_bench_hold.argtypes = [C.c_int64, C.c_void_p]
+        _bench_lib = L
+    return _bench_lib
+
+
+def launch_percentiles(fn, count: int) -> dict:
+    """p10 / median / p90 of single-launch durations (microseconds): a hold kernel keeps the stream busy while the
+    host queues count launches, each between two events on the launch stream, so that they run back to back.  Each
+    figure includes the gap that an event record puts between two kernels (about 3 us here); the rocprofv3
+    kernel trace gives the same percentiles without it."""
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(count + 1)]
+    torch.cuda.synchronize()
+    rc = bench_lib().nvfp4_bench_hold(50000, stream.cuda_stream)
+    if rc:
+        raise RuntimeError(f"hold kernel launch failed: {rc}")
+    ev[0].record(stream)
+    for k in range(count):
+        fn(k)
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    us = np.array([1e3 * ev[k].elapsed_time(ev[k + 1]) for k in range(count)])
+    p10, p50, p90 = np.percentile(us, [10, 50, 90])
+    return {"p10_us": round(float(p10), 2), "median_us": round(float(p50), 2), "p90_us": round(float(p90), 2),
+            "launches": count}
+
+
+def stream_ceiling(xs, outs, launches: int) -> dict:
+    """The streaming kernel with the quantizer's byte mix (32 B read, 8 + 1 B written per block) on the same
+    rotating buffers: the practical bandwidth ceiling for this traffic."""
+    L = bench_lib()
+    nblocks = xs[0].numel() // 16
+    n = len(xs)
+
+    def launch(k):
+        i = k % n
+        rc = L.nvfp4_bench_stream(xs[i].data_ptr(), nblocks, outs[i].codes.data_ptr(), outs[i].scales.data_ptr(),
+                                  torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(f"streaming kernel launch failed: {rc}")
+
+    launch(0)
+    ms = time_graph(capture(launch, 0, launches)) / launches
+    b = 32 * nblocks + 9 * nblocks
+    return {"kernel_us": round(1e3 * ms, 2), "gbs": gbs(b, ms), "frac_of_hbm_peak": round(gbs(b, ms) / HBM_PEAK_GBS, 4),
+            "bytes_per_launch": b}
 
 
 def config_figures(Q, W, dev, launches: int) -> dict:
@@ -225,24 +289,45 @@ def config_figures(Q, W, dev, launches: int) -> dict:
     return out
 
 
-def cpu_baseline(x_bits: np.ndarray, masks, target_s: float) -> dict:
+def cpu_baseline(Q, x_bits: np.ndarray, x0: torch.Tensor, masks, target_s: float) -> dict:
+    """The CPU oracle (test infrastructure, untuned) on the same workload: full steps on every host core for about
+    target_s seconds, then on one thread for about a third of that; and one step's output of the GPU compared byte
+    for byte with the oracle's."""
     import oracle as O
     cores = len(os.sched_getaffinity(0))
-    O.set_num_threads(cores)
-    t0 = time.perf_counter()
-    steps = 0
-    while True:
-        m = masks[steps % len(masks)]
+
+    def oracle_step(k):
+        m = masks[k % len(masks)]
         a = O.amax(x_bits, O.COLWISE, O.G_PER_TENSOR, True, m)
-        O.quantize_1x16(x_bits, a, O.MODE_RHT_SR, O.COLWISE, O.G_PER_TENSOR, m, SEED, steps)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= target_s:
-            break
-    gbs = algorithmic_bytes(ROWS, COLS) * steps / el / 1e9
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": O.num_threads(), "kind": "oracle",
-            "sample": f"{steps} full steps (amax + RHT+SR quantize) of the {ROWS}x{COLS} workload, "
-                      f"{el:.1f} s wall"}
+        return (a,) + tuple(O.quantize_1x16(x_bits, a, O.MODE_RHT_SR, O.COLWISE, O.G_PER_TENSOR, m, SEED, k))
+
+    def timed_steps(threads, seconds):
+        O.set_num_threads(threads)
+        t0 = time.perf_counter()
+        steps = 0
+        while True:
+            oracle_step(steps)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return steps, el, O.num_threads()
+
+    steps, el, used = timed_steps(cores, target_s)
+    steps1, el1, _ = timed_steps(1, target_s / 3)
+    O.set_num_threads(cores)
+    # step 0 on the GPU (fresh outputs) against the oracle's step 0
+    a_gpu, o_gpu = Q.nvfp4_amax_quantize(x0, Q.COLWISE, Q.ROUND_RHT_SR, masks[0], SEED, 0)
+    torch.cuda.synchronize()
+    a, codes, scales, g = oracle_step(0)
+    match = (np.array_equal(a_gpu.cpu().numpy().view(np.uint32), a.view(np.uint32))
+             and np.array_equal(o_gpu.codes.cpu().numpy(), codes) and np.array_equal(o_gpu.scales.cpu().numpy(), scales)
+             and np.array_equal(o_gpu.g.cpu().numpy().view(np.uint32), g.view(np.uint32)))
+    nbytes = algorithmic_bytes(ROWS, COLS)
+    return {"value": round(nbytes * steps / el / 1e9, 3), "unit": "GB/s", "cores": used, "kind": "oracle",
+            "sample": f"{steps} full steps (amax + RHT+SR quantize) of the {ROWS}x{COLS} workload, {el:.1f} s wall",
+            "single_thread": {"value": round(nbytes * steps1 / el1 / 1e9, 4), "unit": "GB/s",
+                              "sample": f"{steps1} full steps on one thread, {el1:.1f} s wall"},
+            "gpu_step_equals_oracle_bytes": bool(match)}
 
 
 def main():
@@ -268,6 +353,17 @@ def main():
     torch.cuda.synchronize()
 
     step = lambda k: run_step(Q, xs, outs, amaxes, k, masks)
+    stream = torch.cuda.Stream()          # a dedicated stream (default priority) for every timed launch
+    with torch.cuda.stream(stream):
+        result = measure(args, Q, W, dev, x_bits, x0, xs, outs, amaxes, masks, step, nbuf, step_bytes)
+    if result is None:
+        return
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(Q, x_bits, x0, masks, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def measure(args, Q, W, dev, x_bits, x0, xs, outs, amaxes, masks, step, nbuf, step_bytes):
     if args.counter_launches:
         for k in range(args.counter_launches):
             step(k)
@@ -278,7 +374,7 @@ def main():
         torch.cuda.synchronize()
         print(f"counter pass: {args.counter_launches} steps and {args.counter_launches} copies of "
               f"{COPY_BYTES >> 20} MiB launched", flush=True)
-        return
+        return None
     for k in range(args.warmup):                       # eager warm-up (also initialises the library)
         step(k)
     torch.cuda.synchronize()
@@ -312,6 +408,11 @@ def main():
                                              out=row_outs[k % nbuf])
     row_ms = time_graph(capture(rowq, 0, args.steps)) / args.steps
     del row_outs
+    # single-launch durations (p10 / median / p90) of the step and of the quantize kernel, and the streaming ceiling
+    n_pct = min(PERCENTILE_LAUNCHES, max(args.steps, 10))
+    step_pct = launch_percentiles(lambda k: step(args.warmup + args.steps + k), n_pct)
+    quant_pct = launch_percentiles(quant, n_pct)
+    ceiling = stream_ceiling(xs, outs, args.steps)
     configs = config_figures(Q, W, dev, args.config_launches) if args.config_launches else {}
 
     result = {
@@ -335,13 +436,18 @@ def main():
         "roofline": {"kernel": "k_amax_quant_colwise<RHT+SR> (single read: amax + quantize)", "bound": "hbm",
                      "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(value / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "algorithmic_bytes_per_launch": step_bytes, "mean_launch_ms": round(ms_per_step, 5)},
+                     "algorithmic_bytes_per_launch": step_bytes, "mean_launch_ms": round(ms_per_step, 5),
+                     "event_bracketed_launch_us": step_pct,
+                     "frac_of_stream_ceiling": round(value / ceiling["gbs"], 4)},
         "extra": {
+            "stream_ceiling": ceiling,
             "two_pass_step_ms": round(two_ms, 5),
             "two_pass_step_gbs": round(step_bytes / (two_ms * 1e-3) / 1e9, 2),
             "quantize_kernel_ms": round(q_ms, 5),
             "quantize_kernel_gbs": round(q_gbs, 2),
             "quantize_kernel_frac_of_hbm_peak": round(q_gbs / HBM_PEAK_GBS, 4),
+            "quantize_kernel_frac_of_stream_ceiling": round(q_gbs / ceiling["gbs"], 4),
+            "quantize_kernel_event_bracketed_launch_us": quant_pct,
             "amax_call_ms": round(amax_ms, 5),
             "amax_call_gbs_read": round(2 * ROWS * COLS / (amax_ms * 1e-3) / 1e9, 2),
             "rowwise_rht_sr_kernel_ms": round(row_ms, 5),
@@ -350,9 +456,7 @@ def main():
             "configs": configs,
         },
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(x_bits, masks, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+    return result
 
 
 if __name__ == "__main__":

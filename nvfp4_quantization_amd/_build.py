@@ -1,6 +1,7 @@
-"""Build the HIP library (libnvfp4_hip.so) for gfx950 with hipcc.
+"""Build the HIP library (libnvfp4_hip.so) for gfx950 with hipcc, and the streaming kernel the benchmark
+compares against (libnvfp4_bench.so, not part of the C ABI).
 
-The library is built in-tree next to this file so that it travels with the source tree.  Object files go to
+The libraries are built in-tree next to this file so that they travel with the source tree.  Object files go to
 ``_build/`` at the repository root.
 """
 from __future__ import annotations
@@ -17,6 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libnvfp4_hip.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = ["nvfp4_kernels.hip", "nvfp4_capi.hip"]
+BENCH_LIB_PATH = os.path.join(PKG_DIR, "libnvfp4_bench.so")
+BENCH_SOURCES = ["bench_stream.hip"]
 ARCH = "gfx950"
 
 # -ffp-contract=off: every a*b+c stays two correctly rounded operations (the rounding of each step is part of the
@@ -100,6 +103,9 @@ def build(verbose: bool = False) -> str:
     tmp = LIB_PATH + ".tmp%d" % os.getpid()
     _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB_PATH)
+    tmp = BENCH_LIB_PATH + ".tmp%d" % os.getpid()
+    _run([hipcc(), *HIPCC_FLAGS, "-shared", *(os.path.join(CSRC, s) for s in BENCH_SOURCES), "-o", tmp])
+    os.replace(tmp, BENCH_LIB_PATH)
     return LIB_PATH
 
 

@@ -43,6 +43,19 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(B.SIGNATURES) == set(declared_functions())
 
 
+def test_bench_library_is_separate():
+    """The benchmark's streaming and stream-hold kernels live in their own library, outside the C ABI."""
+    from nvfp4_quantization_amd._build import BENCH_LIB_PATH
+    if not os.path.exists(BENCH_LIB_PATH):
+        pytest.skip("benchmark library not built")
+    L = C.CDLL(BENCH_LIB_PATH)
+    assert hasattr(L, "nvfp4_bench_stream") and hasattr(L, "nvfp4_bench_hold")
+    L.nvfp4_bench_hold.restype = C.c_int
+    L.nvfp4_bench_hold.argtypes = [C.c_int64, C.c_void_p]
+    assert L.nvfp4_bench_hold(-1, None) != 0 and L.nvfp4_bench_hold(2_000_000, None) != 0   # rejected on the host
+    assert not any(n.startswith("nvfp4_bench") for n in declared_functions())
+
+
 def test_status_strings(lib):
     for code, name in B.STATUS.items():
         assert lib.nvfp4_status_str(code).decode().startswith(name)
