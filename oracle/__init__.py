@@ -83,6 +83,11 @@ def _declare(L: C.CDLL) -> None:
     L.nvo_quantize_4o6.restype = i32
     L.nvo_dequantize.argtypes = [p, p, p, i64, i64, i32, p]
     L.nvo_dequantize.restype = i32
+    L.nvo_rht16_inverse.argtypes = [p, u16, p]
+    L.nvo_f32_to_bf16.argtypes = [f32]
+    L.nvo_f32_to_bf16.restype = u16
+    L.nvo_dequantize_fused.argtypes = [p, p, p, i64, i64, i32, i32, u16, i32, p]
+    L.nvo_dequantize_fused.restype = i32
 
 
 def _ptr(a: np.ndarray | None):
@@ -182,6 +187,18 @@ def rht16(v: np.ndarray, sign_mask: int) -> np.ndarray:
     return y
 
 
+def rht16_inverse(y: np.ndarray, sign_mask: int) -> np.ndarray:
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    assert y.shape == (16,)
+    v = np.zeros(16, dtype=np.float32)
+    lib().nvo_rht16_inverse(_ptr(y), int(sign_mask), _ptr(v))
+    return v
+
+
+def f32_to_bf16(x: float) -> int:
+    return int(lib().nvo_f32_to_bf16(float(x)))
+
+
 def global_scale(amax: float) -> np.float32:
     return np.float32(lib().nvo_global_scale(float(amax)))
 
@@ -262,4 +279,17 @@ def dequantize(codes: np.ndarray, scales: np.ndarray, g: np.ndarray, gmode: int 
     rv, half = codes.shape
     y = np.zeros((rv, 2 * half), dtype=np.float32)
     _check(lib().nvo_dequantize(_ptr(codes), _ptr(scales), _ptr(g), rv, 2 * half, gmode, _ptr(y)), "dequantize")
+    return y
+
+
+def dequantize_fused(codes: np.ndarray, scales: np.ndarray, g: np.ndarray, gmode: int = G_PER_TENSOR,
+                     use_rht: bool = False, sign_mask: int = 0, out_bf16: bool = False) -> np.ndarray:
+    """Decode, optionally followed by the inverse RHT; float32 [rv, cv], or uint16 bf16 patterns with out_bf16."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    rv, cv = codes.shape[0], codes.shape[1] * 2
+    y = np.zeros((rv, cv), dtype=np.uint16 if out_bf16 else np.float32)
+    _check(lib().nvo_dequantize_fused(_ptr(codes), _ptr(scales), _ptr(g), rv, cv, gmode, int(use_rht),
+                                      int(sign_mask), int(out_bf16), _ptr(y)), "dequantize_fused")
     return y

@@ -229,6 +229,29 @@ void nvo_rht16(const float v[16], uint16_t sign_mask, float y[16]) {
     for (int i = 0; i < 16; ++i) y[i] = 0.25f * w[i];
 }
 
+/* Inverse of nvo_rht16.  The forward map is M = (1/4) H16 diag(s) with H16 symmetric and H16 H16 = 16 I, so
+ * M^-1 = diag(s) (1/4) H16.  READING (the pages only say the transform is orthogonal; its inverse is its
+ * transpose): the product is evaluated in the forward's own way on the decoded block d -- the butterfly with
+ * stages of stride 1, 2, 4, 8, (a, b) -> (a + b, a - b) in binary32, then one multiply by 0.25 -- and the random
+ * signs are applied last, negating element i where bit i of the mask is set (exact). */
+void nvo_rht16_inverse(const float y[16], uint16_t sign_mask, float v[16]) {
+    float w[16];
+    for (int i = 0; i < 16; ++i) w[i] = y[i];
+    for (int h = 1; h < 16; h *= 2) {
+        for (int i = 0; i < 16; ++i) {
+            if ((i & h) == 0) {
+                float a = w[i], b = w[i + h];
+                w[i] = a + b;
+                w[i + h] = a - b;
+            }
+        }
+    }
+    for (int i = 0; i < 16; ++i) {
+        float t = 0.25f * w[i];
+        v[i] = ((sign_mask >> i) & 1) ? -t : t;
+    }
+}
+
 /* Absolute maximum as an integer maximum of the magnitude bit patterns.  [P1, sections on the RHT GEMM
  * rewrite and the vibe-coding process]: NaN must propagate (min/max helpers that drop NaN were a bug).  On the
  * magnitude bits, every NaN pattern is above +inf, which is above every finite value, so one NaN makes the
@@ -511,6 +534,64 @@ int nvo_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g, 
             uint8_t code = (c & 1) ? (byte >> 4) : (byte & 0xF);
             float sbf = nvo_e4m3_decode(scales[r * (cv / 16) + c / 16]);
             y[r * cv + c] = (nvo_e2m1_decode(code) * sbf) * gr;
+        }
+    }
+    return NVO_OK;
+}
+
+/* binary32 -> bf16, round to nearest even on the 16 dropped bits.  READING (the pages name bf16 as the
+ * high-precision format and never state a rounding for it): IEEE round-to-nearest-even, the usual conversion;
+ * overflow rounds to infinity as in IEEE; every NaN becomes the quiet NaN 0x7FC0 (the sign of a NaN made by
+ * arithmetic, such as inf - inf, differs between processors, so no NaN sign is part of the result).  Found by
+ * comparing the candidate values: the two bf16 neighbours of x are the truncation t and the next pattern
+ * t + 1 (same sign), and x goes to the nearer in exact binary64 arithmetic, to the even pattern on a tie. */
+uint16_t nvo_f32_to_bf16(float x) {
+    if (isnan(x)) return 0x7FC0;
+    uint32_t u = bits_of(x);
+    uint16_t t = (uint16_t)(u >> 16);                 /* truncation toward zero: |bf16(t)| <= |x| */
+    if ((u & 0xFFFF) == 0) return t;                   /* exactly representable (includes +-0 and +-inf) */
+    uint16_t up = (uint16_t)(t + 1);                   /* next magnitude (may become +-inf: exponent all ones) */
+    double dx = fabs((double)x);
+    double dt = fabs((double)f32_of((uint32_t)t << 16));
+    double du = fabs((double)f32_of((uint32_t)up << 16));   /* +inf when t is the largest finite magnitude */
+    double lo = dx - dt, hi = du - dx;                 /* both exact in binary64; hi is inf for du = inf */
+    if (isinf(du)) {
+        /* the gap above the largest finite bf16 is that of the binade below: ties and beyond go to inf */
+        hi = dt + (dt - fabs((double)f32_of((uint32_t)(t - 1) << 16))) - dx;
+    }
+    if (lo < hi) return t;
+    if (hi < lo) return up;
+    return (t & 1) ? up : t;
+}
+
+/* Fused decode.  [P3]: the optimized decode is named as future kernel work; [P1, random Hadamard transform]:
+ * blocks quantized after the rotation are brought back by its inverse.  Per 16-element block of a row:
+ * d_i = fl(fl(val(code_i) * decode(sb)) * g) (as nvo_dequantize), then, when use_rht is set,
+ * z = nvo_rht16_inverse(d, sign_mask), and the binary32 result is written as float (out_bf16 = 0) or rounded by
+ * nvo_f32_to_bf16 (out_bf16 = 1).  y is [rv, cv] float or uint16 (bf16 bit patterns). */
+int nvo_dequantize_fused(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv, int64_t cv,
+                         int gmode, int use_rht, uint16_t sign_mask, int out_bf16, void* y) {
+    if (!codes || !scales || !g || !y) return NVO_ERR_NULL;
+    if (rv < 0 || cv < 0 || cv % 16) return NVO_ERR_SHAPE;
+    if (gmode != NVO_G_PER_TENSOR && gmode != NVO_G_PER_ROW) return NVO_ERR_UNSUPPORTED;
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rv; ++r) {
+        float gr = (gmode == NVO_G_PER_ROW) ? g[r] : g[0];
+        for (int64_t b = 0; b < cv / 16; ++b) {
+            float d[16], z[16];
+            float sbf = nvo_e4m3_decode(scales[r * (cv / 16) + b]);
+            for (int i = 0; i < 16; ++i) {
+                uint8_t byte = codes[r * (cv / 2) + 8 * b + i / 2];
+                uint8_t code = (i & 1) ? (byte >> 4) : (byte & 0xF);
+                d[i] = (nvo_e2m1_decode(code) * sbf) * gr;
+            }
+            if (use_rht) nvo_rht16_inverse(d, sign_mask, z);
+            else memcpy(z, d, sizeof z);
+            for (int i = 0; i < 16; ++i) {
+                int64_t k = r * cv + 16 * b + i;
+                if (out_bf16) ((uint16_t*)y)[k] = nvo_f32_to_bf16(z[i]);
+                else ((float*)y)[k] = z[i];
+            }
         }
     }
     return NVO_OK;
