@@ -38,7 +38,7 @@
  *     non-zero nvfp4_status and enqueues nothing; there is no fallback path.  NVFP4_ERR_HIP reports a failed
  *     launch (the kernels may then not have run).
  *   - Alignment: x, codes, scales and y must be 16-byte aligned; amax and g 4-byte aligned.
- *   - Sizes: rows, cols >= 0; rows * cols < 2^35.  Column-wise views and 16x16 blocks also need cols < 2^26.
+ *   - Sizes: rows, cols >= 0; rows * cols < 2^35.  Column-wise views and 16x16 blocks also need cols < 2^25.
  *     A zero-sized tensor is valid: its amax is 0 and a quantize call only writes g.
  *   - Calls on different streams may run concurrently; they share no state (nvfp4_amax_quantize: see it).
  */

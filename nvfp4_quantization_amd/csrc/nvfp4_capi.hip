@@ -14,8 +14,9 @@ namespace {
 // Kernels index 16-element blocks with 32-bit integers and add grid strides (< 2^22) to them: at most 2^35
 // elements per tensor (64 GiB of bf16) keeps every block index and index + stride below 2^32.
 constexpr int64_t kMaxElems = int64_t(1) << 35;
-// Column-wise kernels address a 16-row slab through a buffer resource of 32 * cols bytes (a 32-bit signed size).
-constexpr int64_t kMaxColwiseCols = int64_t(1) << 26;
+// Column-wise kernels address the rows of up to four row-blocks (64 rows, 128 * cols bytes) with 32-bit offsets from
+// a buffer resource.
+constexpr int64_t kMaxColwiseCols = int64_t(1) << 25;
 
 #define NVFP4_TRY(expr)                  \
     do {                                 \

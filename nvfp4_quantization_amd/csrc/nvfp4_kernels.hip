@@ -101,9 +101,12 @@ struct RngArgs {
     uint32_t k0, k1, o0, o1;
 };
 
-// Complemented random words of the block (bytes 255 - rho).
-__device__ __forceinline__ Rand4 block_rand_inv(const RngArgs& a, uint64_t n) {
-    return philox4x32_10_inv((uint32_t)n, (uint32_t)(n >> 32), a.o0, a.o1, a.k0, a.k1);
+// Complemented random words of the block (bytes 255 - rho).  Block indices stay below 2^31 (a tensor holds fewer
+// than 2^35 elements), so the high counter word is zero; with the offset words uniform, the first round's product of
+// counter word 2 and the second round's product of word 0 are then the same in every lane and are formed by the
+// scalar unit.
+__device__ __forceinline__ Rand4 block_rand_inv(const RngArgs& a, uint32_t n) {
+    return philox4x32_10_inv(n, 0u, a.o0, a.o1, a.k0, a.k1);
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -626,22 +629,6 @@ struct ColStash {
     uint4 e[kColRB][8 * 64 + 1];
 };
 
-// Writes the codes/scales held in a ColStash, as col_write_out.
-__device__ __forceinline__ void col_write_out_stash(const ColStash& st, const ColPos& p, uint32_t rows,
-                                                    uint32_t cols, uint32_t nrb, uint8_t* __restrict__ codes,
-                                                    uint8_t* __restrict__ scales) {
-    const uint32_t col0 = p.strip * 512;
-    const uint32_t ncol = min(512u, cols - col0), nr = min((uint32_t)kColRB, nrb - p.group * kColRB);
-    const uint32_t rbl = threadIdx.x % kColRB, rb = p.group * kColRB + rbl;
-    if (rbl >= nr) return;
-    for (uint32_t cl = threadIdx.x / kColRB; cl < ncol; cl += kColThreads / kColRB) {
-        const uint4 e = st.e[rbl][(cl & 7) * 64 + (cl >> 3)];
-        const uint32_t c = col0 + cl;
-        st_nt(codes + (size_t)c * (rows >> 1) + 8 * (size_t)rb, make_uint2(e.x, e.y));
-        st_nt(scales + (size_t)c * nrb + rb, (uint8_t)e.z);
-    }
-}
-
 // Writes the codes/scales of column blocks j = G jg .. G jg + G - 1 of every lane held in a ColStash: thread t
 // takes row-block t % 16 of column 8 (t / 16) + j, so 16 consecutive threads write one column's 128 contiguous code
 // bytes.
@@ -665,6 +652,121 @@ __device__ __forceinline__ void col_write_out_group(const ColStash& st, const Co
     }
 }
 
+// Column-wise quantization with a device-resident amax.  The workgroup tile is the same 16 row-blocks x 512 columns,
+// but split among the waves so that the four waves that receive their data together finish a complete piece of the
+// output: wave w = 4 q + i covers columns 128 q .. 128 q + 127 of the strip and row-blocks 4 i .. 4 i + 3 (lanes
+// 16 s .. 16 s + 15 take row-block 4 i + s, 8 columns each), so waves 4 q .. 4 q + 3 hold all 16 row-blocks of 128
+// columns.  Waves of a workgroup are dispatched in order to the four SIMDs, which serve their oldest wave first, and
+// the memory system answers in about the order of the requests: waves 0-3 get their data first, then 4-7, and so on.
+// Each quad's last wave to finish (an LDS counter) writes the quad's 128 output rows of 128 bytes of codes and 16 of
+// scales, so those stores overlap the later quads' loads and arithmetic instead of following a workgroup barrier.
+struct QuadPos {
+    uint32_t group;  // row group (16 row-blocks)
+    uint32_t strip;  // 512-column strip
+    uint32_t q;      // column quarter of the strip (128 columns) = the wave's quad
+    uint32_t i;      // the wave's four row-blocks within the group: 4 i .. 4 i + 3
+    uint32_t s;      // the lane's row-block within those four
+    uint32_t lane;
+    uint32_t rb0;    // first row-block of the wave (wave-uniform)
+    uint32_t rb;     // the lane's row-block
+    uint32_t c8;     // first of the lane's 8 columns
+};
+
+__device__ __forceinline__ QuadPos quad_position(const ColGrid& g, uint32_t tile) {
+    QuadPos p;
+    p.group = tile / g.nstrips;
+    const uint32_t s = tile - p.group * g.nstrips + p.group % g.nstrips;
+    p.strip = s >= g.nstrips ? s - g.nstrips : s;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    p.q = wave >> 2;
+    p.i = wave & 3u;
+    p.lane = threadIdx.x & 63u;
+    p.s = p.lane >> 4;
+    p.rb0 = p.group * kColRB + 4 * p.i;
+    p.rb = p.rb0 + p.s;
+    p.c8 = p.strip * 512 + 128 * p.q + 8 * (p.lane & 15u);
+    return p;
+}
+
+// The lane's 16 rows x 8 columns (row k of its row-block in v[k]); one load instruction reads 256 contiguous bytes
+// of a row in each of the wave's four row-blocks.  Offsets from the wave's first row-block stay below 128 cols bytes,
+// which the column-wise size limit (cols < 2^25) keeps below 2^32.
+__device__ __forceinline__ void load_quad_tile(const uint16_t* x, uint32_t rows, uint32_t cols, const QuadPos& p,
+                                               uint4 (&v)[16]) {
+    const uint16_t* base = x + (size_t)(16 * p.rb0) * cols;
+    const uint64_t span = (uint64_t)(rows - 16 * p.rb0) * cols * 2;
+    const uint32_t nrec = span > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)span;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, (int)nrec, 0x00020000);
+    const uint32_t voff = p.s * 32u * cols + 2u * p.c8;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff, (int)(2u * k * cols), 0);
+        v[k] = make_uint4(t.x, t.y, t.z, t.w);
+    }
+}
+
+// LDS of the quad-mapped kernel: entry (wave, j, lane) first holds the Philox words of the lane's block j, then its
+// codes (x, y); the scale codes go to sc[quad][column within the quarter][row-block]; cnt counts finished waves per
+// quad.
+struct QuadStash {
+    uint4 e[kColRB][8 * 64 + 1];
+    uint8_t sc[4][128][kColRB];
+    uint32_t cnt[4];
+};
+
+__device__ __forceinline__ void st_nt(void* p, uint4 v) {
+    typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(u32x4v{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4v*>(p));
+}
+
+// Writes quad q's 128 columns x nr row-blocks (one wave).  Codes: instruction t covers output rows 8 t .. 8 t + 7 of
+// the quarter, 8 lanes per row, each lane 16 bytes = row-blocks 2 p and 2 p + 1.  Scales: one lane per output row,
+// 16 bytes.
+__device__ __forceinline__ void quad_write_out(const QuadStash& st, const QuadPos& pos, uint32_t rows, uint32_t cols,
+                                               uint32_t nrb, uint8_t* __restrict__ codes,
+                                               uint8_t* __restrict__ scales) {
+    const uint32_t col0 = pos.strip * 512 + 128 * pos.q;
+    const uint32_t rbg = pos.group * kColRB;
+    const uint32_t nr = min((uint32_t)kColRB, nrb - rbg);
+    const uint32_t p = pos.lane & 7u, cl = pos.lane >> 3;
+    const uint32_t wv = 4 * pos.q + (p >> 1), s0 = 2 * (p & 1u);   // slots of row-blocks 2p, 2p + 1
+    const bool aligned16 = (rows & 31u) == 0;   // 16-byte stores need (rows / 2) % 16 == 0
+#pragma unroll 4
+    for (uint32_t t = 0; t < 16; ++t) {
+        const uint32_t cc = 8 * t + cl, c = col0 + cc;
+        if (c < cols && 2 * p < nr) {
+            const uint32_t jj = cc & 7u, ln = cc >> 3;
+            const uint4 a = st.e[wv][jj * 64 + 16 * s0 + ln];
+            uint8_t* dst = codes + (size_t)c * (rows >> 1) + 8 * (size_t)(rbg + 2 * p);
+            if (2 * p + 1 < nr) {
+                const uint4 b = st.e[wv][jj * 64 + 16 * (s0 + 1) + ln];
+                if (aligned16) {
+                    st_nt(dst, make_uint4(a.x, a.y, b.x, b.y));
+                } else {
+                    st_nt(dst, make_uint2(a.x, a.y));
+                    st_nt(dst + 8, make_uint2(b.x, b.y));
+                }
+            } else {
+                st_nt(dst, make_uint2(a.x, a.y));
+            }
+        }
+    }
+#pragma unroll
+    for (uint32_t t = 0; t < 2; ++t) {
+        const uint32_t cc = 64 * t + pos.lane, c = col0 + cc;
+        if (c < cols) {
+            uint8_t* dst = scales + (size_t)c * nrb + rbg;
+            if (nr == kColRB && (nrb & 15u) == 0) {
+                st_nt(dst, *reinterpret_cast<const uint4*>(&st.sc[pos.q][cc][0]));
+            } else {
+                for (uint32_t r = 0; r < nr; ++r) st_nt(dst + r, st.sc[pos.q][cc][r]);
+            }
+        }
+    }
+}
+
 template <int MODE, bool PER_ROW>
 __global__ void __launch_bounds__(kColThreads)
 k_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColGrid cg,
@@ -672,27 +774,30 @@ k_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, Co
                 uint8_t* __restrict__ scales, float* __restrict__ gout) {
     constexpr bool SR = MODE != kRN;
     constexpr bool RHT = MODE == kRHTSR;
-    __shared__ ColStash st;
+    __shared__ QuadStash st;
     __shared__ RTable tab;
+    if (threadIdx.x < 4) st.cnt[threadIdx.x] = 0;
     float g = 0.0f;
     Divisor d6{};
     if (!PER_ROW) {
         g = global_scale(amax[0]);
         d6 = make_divisor_uniform(6.0f * g);
         if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
-        fill_rtable<RHT>(tab, g);
+        fill_rtable<RHT>(tab, g);   // its barrier also orders the counters' reset
+    } else {
+        __syncthreads();
     }
-    const ColPos pos = col_position(cg, blockIdx.x);
+    const QuadPos pos = quad_position(cg, blockIdx.x);
     const uint32_t wave = threadIdx.x >> 6;
     if (pos.rb < cg.nrb && pos.c8 < cols) {
         uint4 v[16];
-        load_col_tile(x, cols, pos, v);
+        load_quad_tile(x, rows, cols, pos, v);
         // The random words do not depend on the data: they are generated while the loads are in flight and parked
         // in LDS (registers are full with the tile).
         if (SR) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const Rand4 r = block_rand_inv(rng, (uint64_t)(pos.c8 + j) * cg.nrb + pos.rb);
+                const Rand4 r = block_rand_inv(rng, (pos.c8 + j) * cg.nrb + pos.rb);
                 st.e[wave][j * 64 + pos.lane] = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
             }
         }
@@ -715,12 +820,17 @@ k_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, Co
             } else {
                 quantize_block<SR, RHT>(w, d6, TableMul{tab}, inv, lo, hi, sb);
             }
-            slot = make_uint4(lo, hi, sb, 0u);
+            slot = make_uint4(lo, hi, 0u, 0u);
+            st.sc[pos.q][8 * (pos.lane & 15u) + j][4 * pos.i + pos.s] = (uint8_t)sb;
             if (j & 1) __builtin_amdgcn_sched_barrier(0);   // two blocks at a time bounds the live registers
         }
     }
-    __syncthreads();
-    col_write_out_stash(st, pos, rows, cols, cg.nrb, codes, scales);
+    // Every wave counts itself in (active or not); the last of the quad writes the quad's output.  The release half
+    // of the atomic orders this wave's LDS writes before it, the acquire half the writer's reads after it.
+    uint32_t before = 0;
+    if (pos.lane == 0)
+        before = __hip_atomic_fetch_add(&st.cnt[pos.q], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (__builtin_amdgcn_readfirstlane(before) == 3) quad_write_out(st, pos, rows, cols, cg.nrb, codes, scales);
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -866,7 +976,7 @@ k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t col
         if (SR) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const Rand4 r = block_rand_inv(rng, (uint64_t)(pos.c8 + j) * cg.nrb + pos.rb);
+                const Rand4 r = block_rand_inv(rng, (pos.c8 + j) * cg.nrb + pos.rb);
                 st.e[wave][j * 64 + pos.lane] = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
             }
         }
@@ -1320,7 +1430,7 @@ k_amax_rowwise_rows(const uint4* __restrict__ x, uint32_t rows, uint32_t blocks_
     }
 }
 
-// Column-wise (V = X^T), same workgroup layout as k_quant_colwise.  Per tensor: one publish per workgroup.  Per row
+// Column-wise (V = X^T), same workgroup layout as k_amax_quant_colwise (one row-block per wave).  Per tensor: one publish per workgroup.  Per row
 // of V (= per column of X): the waves' column maxima are combined in LDS, then one atomic per column.
 template <bool RHT, bool PER_ROW>
 __global__ void __launch_bounds__(kColThreads)

@@ -79,7 +79,7 @@ def test_amax_validation(lib):
     assert f(P, 16, 16, 1, 7, 0, 0, P, None) == UNSUP
     assert f(P, 1 << 20, 1 << 20, 1, 0, 0, 0, P, None) == SHAPE  # 2^40 elements
     assert f(P, 1 << 19, 1 << 16, 1, 0, 0, 0, P, None) == SHAPE  # 2^35 elements: block index + stride could wrap
-    assert f(P, 16, 1 << 26, 2, 0, 0, 0, P, None) == SHAPE       # column-wise: cols < 2^26
+    assert f(P, 16, 1 << 25, 2, 0, 0, 0, P, None) == SHAPE       # column-wise: cols < 2^25
 
 
 def test_quantize_rn_validation(lib):
@@ -88,7 +88,7 @@ def test_quantize_rn_validation(lib):
     assert f(P, 16, 16, 1, 1, 1, P, out(), None, None) == UNSUP       # 16x16 per-row g
     assert f(P, 16, 24, 1, 1, 0, P, out(), None, None) == SHAPE       # 16x16 cols % 16
     assert f(P, 24, 16, 1, 2, 0, P, None, out(), None) == SHAPE       # 16x16 rows % 16
-    assert f(P, 16, 1 << 26, 1, 2, 0, P, None, out(), None) == SHAPE  # 16x16 cols < 2^26
+    assert f(P, 16, 1 << 25, 1, 2, 0, P, None, out(), None) == SHAPE  # 16x16 cols < 2^25
     assert f(P, 16, 16, 1, 3, 0, P, out(), None, None) == NULL        # BOTH needs both outputs
     assert f(P, 16, 16, 0, 1, 0, P, None, out(), None) == NULL        # row-wise needs row_out
     assert f(P, 16, 16, 0, 1, 0, P, out(g=None), None, None) == NULL
