@@ -23,7 +23,9 @@ Also printed in the same JSON line:
                 device-resident amax (the pages' kernel-only comparison), the amax call, the row-wise RHT+SR pass,
                 and under "configs" the other workloads: the 256x1024 RHT+SR/RN pair, the 8192x4096 row-wise RN
                 activation pass, the 14336x4096 16x16 weight pass (W and W^T), the 16384x8192 four-over-six pass
-                and the decode of its output (each timed as a graph of K launches, inputs rotating through HBM).
+                the decode of its output (to float, and to bf16 through the fused decode), and the fused decode of the
+                column-wise RHT+SR output back through the inverse transform to bf16 (each timed as a graph of K
+                launches, inputs rotating through HBM).
 """
 from __future__ import annotations
 
@@ -284,7 +286,36 @@ def config_figures(Q, W, dev, launches: int) -> dict:
     out["dequantize_16384x8192"] = {
         "kernel_us": round(1e3 * tdq, 2), "gbs": gbs(bdq, tdq),
         "frac_of_hbm_peak": round(gbs(bdq, tdq) / HBM_PEAK_GBS, 4), "bytes_per_call": bdq}
-    del outs, am, y
+    del y
+    # the same decode written as bf16 by the fused decode (no rotation)
+    yb = torch.empty((r, c), dtype=torch.bfloat16, device=dev)
+    bdb = r * c // 2 + r * c // 16 + 4 * r + 2 * r * c
+    tdb = timed(lambda k: Q.nvfp4_dequantize_fused(outs[k % n].codes, outs[k % n].scales, outs[k % n].g, Q.G_PER_ROW,
+                                                   False, 0, True, y=yb))
+    out["dequantize_bf16_16384x8192"] = {
+        "call": "nvfp4_dequantize_fused, bf16 output",
+        "kernel_us": round(1e3 * tdb, 2), "gbs": gbs(bdb, tdb),
+        "frac_of_hbm_peak": round(gbs(bdb, tdb) / HBM_PEAK_GBS, 4), "bytes_per_call": bdb}
+    del outs, am, yb
+    torch.cuda.empty_cache()
+
+    # 8192 x 4096 weight gradient quantized column-wise with RHT + SR, decoded back through the inverse transform
+    # to bf16 (V = X^T, 4096 x 8192); outputs and decoded tensors rotate through HBM
+    r, c = 8192, 4096
+    bdr = algorithmic_bytes(r, c)          # codes + scales + g in, bf16 out: the quantizer's bytes reversed
+    n = max(2, -(-2 * MALL_BYTES // bdr) + 1)
+    x = torch.from_numpy(W.make(WORKLOAD).view(np.int16)).to(dev)
+    mask = W.sign_mask(SEED, 0)
+    qs = [Q.nvfp4_amax_quantize(x, Q.COLWISE, Q.ROUND_RHT_SR, mask, SEED, i)[1] for i in range(n)]
+    ys = [torch.empty((c, r), dtype=torch.bfloat16, device=dev) for _ in range(n)]
+    del x
+    tdr = timed(lambda k: Q.nvfp4_dequantize_fused(qs[k % n].codes, qs[k % n].scales, qs[k % n].g, Q.G_PER_TENSOR,
+                                                   True, mask, True, y=ys[k % n]))
+    out["dequantize_rht_bf16_8192x4096"] = {
+        "call": "nvfp4_dequantize_fused, inverse RHT, bf16 output, of the column-wise RHT+SR quantization",
+        "kernel_us": round(1e3 * tdr, 2), "gbs": gbs(bdr, tdr),
+        "frac_of_hbm_peak": round(gbs(bdr, tdr) / HBM_PEAK_GBS, 4), "bytes_per_call": bdr}
+    del qs, ys
     torch.cuda.empty_cache()
     return out
 

@@ -144,6 +144,19 @@ nvfp4_status nvfp4_quantize_4o6(const uint16_t* x, int64_t rows, int64_t cols, n
 nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv, int64_t cv,
                               nvfp4_gmode gmode, float* y, void* stream);
 
+/* Fused decode ([P3]: an optimized decode is named there as future kernel work; [P1, random Hadamard transform]:
+ * a block quantized after the rotation is brought back by the rotation's inverse, its transpose).  For each block of
+ * 16 elements of a row: d_i = fl(fl(val(code_i) * decode(sb)) * g), as nvfp4_dequantize; with use_rht != 0, the
+ * inverse of the transform of nvfp4_quantize_rht_sr with the same sign_mask: the butterfly with strides 1, 2, 4, 8,
+ * (a, b) -> (a + b, a - b) in binary32, one multiply by 0.25, and element i negated where bit i of sign_mask is set.
+ * The binary32 result is written as float (out_bf16 = 0) or as bf16 bit patterns (out_bf16 != 0) rounded to nearest
+ * even, overflowing to infinity, with every NaN written as 0x7FC0.
+ *   codes [rv, cv/2], scales [rv, cv/16], g [1] or [rv] (gmode), y [rv, cv] float or uint16.
+ *   Shape: cv % 16 == 0.  A column-wise quantization decodes to V = X^T.  Alignment: codes, scales, y 16 bytes. */
+nvfp4_status nvfp4_dequantize_fused(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv,
+                                    int64_t cv, nvfp4_gmode gmode, int use_rht, uint16_t sign_mask, int out_bf16,
+                                    void* y, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* nvfp4_status_str(nvfp4_status status);
 

@@ -33,6 +33,7 @@ SIGNATURES = {
     "nvfp4_amax_quantize": (_I, [_P, _I64, _I64, _I, _I, _U16, _U64, _U64, _P, _P, _P]),
     "nvfp4_quantize_4o6": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
     "nvfp4_dequantize": (_I, [_P, _P, _P, _I64, _I64, _I, _P, _P]),
+    "nvfp4_dequantize_fused": (_I, [_P, _P, _P, _I64, _I64, _I, _I, _U16, _I, _P, _P]),
     "nvfp4_status_str": (C.c_char_p, [_I]),
 }
 
@@ -193,4 +194,20 @@ def nvfp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, g: torch.Tensor,
         y = torch.empty((rv, 2 * half), dtype=torch.float32, device=codes.device)
     _check(lib().nvfp4_dequantize(_dev(codes, "codes"), _dev(scales, "scales"), _dev(g, "g"), rv, 2 * half, gmode,
                                   _dev(y, "y"), _stream(codes.device, stream)), "nvfp4_dequantize")
+    return y
+
+
+def nvfp4_dequantize_fused(codes: torch.Tensor, scales: torch.Tensor, g: torch.Tensor, gmode: int = G_PER_TENSOR,
+                           use_rht: bool = False, sign_mask: int = 0, out_bf16: bool = False,
+                           y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode, optionally through the inverse RHT; y is float32, or bfloat16 with out_bf16."""
+    rv, half = codes.shape
+    dtype = torch.bfloat16 if out_bf16 else torch.float32
+    if y is None:
+        y = torch.empty((rv, 2 * half), dtype=dtype, device=codes.device)
+    elif y.dtype not in ((torch.bfloat16, torch.int16, torch.uint16) if out_bf16 else (torch.float32,)):
+        raise TypeError("y must be bf16 (or its 16-bit patterns) with out_bf16, else float32")
+    _check(lib().nvfp4_dequantize_fused(_dev(codes, "codes"), _dev(scales, "scales"), _dev(g, "g"), rv, 2 * half,
+                                        gmode, int(bool(use_rht)), sign_mask & 0xFFFF, int(bool(out_bf16)),
+                                        _dev(y, "y"), _stream(codes.device, stream)), "nvfp4_dequantize_fused")
     return y

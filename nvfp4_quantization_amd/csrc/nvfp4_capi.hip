@@ -178,6 +178,20 @@ nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const
                                          static_cast<hipStream_t>(stream)));
 }
 
+nvfp4_status nvfp4_dequantize_fused(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv,
+                                    int64_t cv, nvfp4_gmode gmode, int use_rht, uint16_t sign_mask, int out_bf16,
+                                    void* y, void* stream) {
+    NVFP4_TRY(check_sizes(rv, cv));
+    NVFP4_TRY(check_gmode(gmode));
+    if (cv % 16) return NVFP4_ERR_SHAPE;
+    NVFP4_TRY(check_buf(codes, rv * (cv / 2), 16));
+    NVFP4_TRY(check_buf(scales, rv * (cv / 16), 16));
+    NVFP4_TRY(check_buf(g, gmode == NVFP4_G_PER_ROW ? rv : 1, 4));
+    NVFP4_TRY(check_buf(y, rv * cv, 16));
+    return done(nvfp4::launch_dequantize_fused(codes, scales, g, rv, cv, gmode == NVFP4_G_PER_ROW, use_rht != 0,
+                                               sign_mask, out_bf16 != 0, y, static_cast<hipStream_t>(stream)));
+}
+
 const char* nvfp4_status_str(nvfp4_status status) {
     switch (status) {
         case NVFP4_OK: return "NVFP4_OK";

@@ -1355,6 +1355,84 @@ k_dequantize(const uint16_t* __restrict__ codes, const uint8_t* __restrict__ sca
 }
 
 // ------------------------------------------------------------------------------------------------------------
+// Fused decode ([P3]: the optimized decode is named as future kernel work; [P1, random Hadamard transform]: blocks
+// quantized after the rotation are brought back by its inverse).  d_i = fl(fl(val(code_i) * decode(sb)) * g) as in
+// k_dequantize; with RHT the inverse transform: the butterfly with strides 1, 2, 4, 8 in binary32, one multiply by
+// 0.25, then element i negated where bit i of the mask is set; written as float or as bf16 (round to nearest even,
+// every NaN as 0x7FC0).
+//   Two lanes per block: lane parity h holds elements 8 h .. 8 h + 7 (4 code bytes), so strides 1, 2 and 4 stay in
+// the lane and stride 8 pairs the lane with its neighbour (one DPP exchange per value).  bf16 rows are then stored
+// 16 bytes per lane, contiguous across the wave.
+// ------------------------------------------------------------------------------------------------------------
+// The value held by the other lane of this lane's pair (lanes 2m, 2m + 1): DPP quad permutation [1, 0, 3, 2].
+__device__ __forceinline__ float pair_swap(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+
+// binary32 -> bf16 bits (in the high half of the result), round to nearest even on the 16 dropped bits; the
+// increment carries into the exponent exactly as the rounded magnitude does (up to infinity).  NaN -> 0x7FC0.
+__device__ __forceinline__ uint32_t bf16_rne_hi(float f) {
+    const uint32_t u = as_u(f);
+    const uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
+    return (f != f) ? 0x7FC00000u : r;
+}
+
+template <bool RHT, bool BF16, bool PER_ROW>
+__global__ void __launch_bounds__(kThreads)
+k_dequantize_fused(const uint32_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                   const float* __restrict__ g, uint64_t total_halves, FastDiv per_row, uint32_t sign_mask,
+                   void* __restrict__ y) {
+    const uint32_t h = threadIdx.x & 1u;   // the grid stride is even, so a lane keeps its half
+    float qm[8];                           // 0.25 with the lane's eight random signs
+#pragma unroll
+    for (int k = 0; k < 8; ++k) qm[k] = ((sign_mask >> (8 * h + k)) & 1u) ? -0.25f : 0.25f;
+    const float other = h ? -1.0f : 1.0f;
+    const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+    for (uint64_t t = (uint64_t)blockIdx.x * kThreads + threadIdx.x; t < total_halves; t += stride) {
+        const uint32_t n = (uint32_t)(t >> 1);
+        const float gr = PER_ROW ? g[fdiv(n, per_row)] : g[0];
+        const float sbf = e4m3_decode(scales[n]);
+        float d[8];
+        unpack8(codes[t], d);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) d[k] = (d[k] * sbf) * gr;
+        if (RHT) {
+#pragma unroll
+            for (int st = 1; st < 8; st <<= 1) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    if ((i & st) == 0) {
+                        const float a = d[i], b = d[i + st];
+                        d[i] = a + b;
+                        d[i + st] = a - b;
+                    }
+                }
+            }
+            // stride 8: the even lane forms w_k + w_(k+8) = own + other, the odd lane w_k - w_(k+8) = other - own;
+            // fma(own, +-1, other) rounds that sum once, as the addition does
+#pragma unroll
+            for (int k = 0; k < 8; ++k) d[k] = __builtin_fmaf(d[k], other, pair_swap(d[k]));
+#pragma unroll
+            for (int k = 0; k < 8; ++k) d[k] = d[k] * qm[k];   // fl(-0.25 w) = -fl(0.25 w) exactly
+        }
+        if (BF16) {
+            uint32_t r[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) r[k] = bf16_rne_hi(d[k]);
+            const uint4 o = make_uint4(__builtin_amdgcn_perm(r[1], r[0], 0x07060302u),
+                                       __builtin_amdgcn_perm(r[3], r[2], 0x07060302u),
+                                       __builtin_amdgcn_perm(r[5], r[4], 0x07060302u),
+                                       __builtin_amdgcn_perm(r[7], r[6], 0x07060302u));
+            st_nt(reinterpret_cast<uint4*>(y) + t, o);
+        } else {
+            float4* yf = reinterpret_cast<float4*>(y) + 2 * t;
+            st_nt(yf, make_float4(d[0], d[1], d[2], d[3]));
+            st_nt(yf + 1, make_float4(d[4], d[5], d[6], d[7]));
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------------------
 // amax kernels.  The maximum of magnitudes with NaN dominating (v_maximum3); reductions combine the binary32 bit
 // patterns with an integer maximum, which orders NaN > inf > finite for magnitudes.
 // ------------------------------------------------------------------------------------------------------------
@@ -1814,6 +1892,31 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const 
         k_dequantize<true><<<grid, kThreads, 0, stream>>>(c16, scales, g, quarters, fd, reinterpret_cast<float4*>(y));
     else
         k_dequantize<false><<<grid, kThreads, 0, stream>>>(c16, scales, g, quarters, fd, reinterpret_cast<float4*>(y));
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize_fused(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv,
+                                   int64_t cv, bool per_row, bool use_rht, uint32_t sign_mask, bool out_bf16, void* y,
+                                   hipStream_t stream) {
+    if (rv == 0 || cv == 0) return hipSuccess;
+    const uint64_t halves = (uint64_t)rv * cv / 8;
+    const FastDiv fd = make_fastdiv((uint32_t)(cv / 16));
+    const uint32_t grid = grid_for(halves, kThreads * 4, 16);
+    const uint32_t* c32 = reinterpret_cast<const uint32_t*>(codes);
+#define NVFP4_DQ(R, B, P) \
+    k_dequantize_fused<R, B, P><<<grid, kThreads, 0, stream>>>(c32, scales, g, halves, fd, sign_mask, y)
+    const int sel = (use_rht ? 4 : 0) | (out_bf16 ? 2 : 0) | (per_row ? 1 : 0);
+    switch (sel) {
+        case 0: NVFP4_DQ(false, false, false); break;
+        case 1: NVFP4_DQ(false, false, true); break;
+        case 2: NVFP4_DQ(false, true, false); break;
+        case 3: NVFP4_DQ(false, true, true); break;
+        case 4: NVFP4_DQ(true, false, false); break;
+        case 5: NVFP4_DQ(true, false, true); break;
+        case 6: NVFP4_DQ(true, true, false); break;
+        default: NVFP4_DQ(true, true, true); break;
+    }
+#undef NVFP4_DQ
     return hipGetLastError();
 }
 

@@ -41,4 +41,9 @@ hipError_t launch_quant_4o6(const uint16_t* x, int64_t rows, int64_t cols, bool 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv, int64_t cv,
                              bool per_row, float* y, hipStream_t stream);
 
+// Decode with an optional inverse RHT; y is float or bf16 bits.
+hipError_t launch_dequantize_fused(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv,
+                                   int64_t cv, bool per_row, bool use_rht, uint32_t sign_mask, bool out_bf16, void* y,
+                                   hipStream_t stream);
+
 }  // namespace nvfp4

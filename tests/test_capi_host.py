@@ -34,7 +34,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["nvfp4_amax", "nvfp4_quantize_rn", "nvfp4_quantize_sr",
                                            "nvfp4_quantize_rht_sr", "nvfp4_amax_quantize", "nvfp4_quantize_4o6",
-                                           "nvfp4_dequantize", "nvfp4_status_str"])
+                                           "nvfp4_dequantize", "nvfp4_dequantize_fused", "nvfp4_status_str"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -128,3 +128,20 @@ def test_4o6_and_dequantize_validation(lib):
     assert d(P, P, P, 4, 32, 0, P + 4, None) == ALIGN          # y must be 16-byte aligned
     assert d(None, P, P, 4, 32, 0, P, None) == NULL
     assert d(P, P, P, -4, 32, 0, P, None) == SHAPE
+
+
+def test_dequantize_fused_validation(lib):
+    d = lib.nvfp4_dequantize_fused
+    #        codes scales g  rv  cv  gmode rht mask bf16 y  stream
+    assert d(P, P, P, 4, 24, 0, 1, 0x1234, 1, P, None) == SHAPE           # cv % 16
+    assert d(P, P, P, -1, 32, 0, 1, 0x1234, 1, P, None) == SHAPE
+    assert d(P, P, P, 1 << 20, 1 << 20, 0, 1, 0, 1, P, None) == SHAPE      # 2^40 elements
+    assert d(P, P, P, 4, 32, 2, 1, 0, 1, P, None) == UNSUP                 # unknown g mode
+    assert d(None, P, P, 4, 32, 0, 1, 0, 1, P, None) == NULL
+    assert d(P, None, P, 4, 32, 0, 1, 0, 1, P, None) == NULL
+    assert d(P, P, None, 4, 32, 1, 1, 0, 1, P, None) == NULL
+    assert d(P, P, P, 4, 32, 0, 1, 0, 1, None, None) == NULL
+    assert d(MIS, P, P, 4, 32, 0, 1, 0, 1, P, None) == ALIGN
+    assert d(P, P, P + 2, 4, 32, 0, 1, 0, 1, P, None) == ALIGN
+    assert d(P, P, P, 4, 32, 0, 1, 0, 0, P + 8, None) == ALIGN             # y must be 16-byte aligned
+    assert d(None, None, P, 0, 32, 0, 1, 0, 1, None, None) == OK          # empty: nothing to decode

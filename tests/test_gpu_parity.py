@@ -292,18 +292,22 @@ def test_4o6_with_nan_inf():
 # ------------------------------------------------------------------------------------------------ dequantize
 @pytest.mark.parametrize("gmode", [0, 1])
 def test_dequantize(gmode):
+    """Decode of the oracle's four-over-six output and of seeded arbitrary bytes (every scale code, including the
+    sign bit and NaN patterns); both sides decode the same arrays."""
     x = W.heavy_tail_rows(128, 256, seed=2, frac_special=2e-4)
-    xd = dev(x)
-    a = Q.nvfp4_amax(xd, Q.ROWWISE, gmode)
-    out = Q.nvfp4_quantize_4o6(xd, a, gmode)
-    y = Q.nvfp4_dequantize(out.codes, out.scales, out.g, gmode)
-    same_f32(host(y), O.dequantize(host(out.codes), host(out.scales), host(out.g), gmode))
-    # arbitrary bytes too (every scale code, including the sign bit and NaN patterns)
-    codes = torch.randint(0, 256, (64, 32), dtype=torch.uint8, device="cuda")
-    scales = torch.arange(256, dtype=torch.uint8, device="cuda").reshape(64, 4)
-    g = torch.rand((64 if gmode else 1,), device="cuda")
-    y = Q.nvfp4_dequantize(codes, scales, g, gmode)
-    same_f32(host(y), O.dequantize(host(codes), host(scales), host(g), gmode))
+    codes, scales, g, _ = O.quantize_4o6(x, O.amax(x, O.ROWWISE, gmode), gmode)
+    y = Q.nvfp4_dequantize(dev_u8(codes), dev_u8(scales), torch.from_numpy(g).cuda(), gmode)
+    same_f32(host(y), O.dequantize(codes, scales, g, gmode))
+    rng = np.random.default_rng(40 + gmode)
+    codes = rng.integers(0, 256, size=(64, 32), dtype=np.uint8)
+    scales = np.arange(256, dtype=np.uint8).reshape(64, 4)
+    g = rng.uniform(0.0, 1.0, size=(64 if gmode else 1,)).astype(np.float32)
+    y = Q.nvfp4_dequantize(dev_u8(codes), dev_u8(scales), torch.from_numpy(g).cuda(), gmode)
+    same_f32(host(y), O.dequantize(codes, scales, g, gmode))
+
+
+def dev_u8(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
 # ----------------------------------------------------------------------------------- full-size workloads
