@@ -398,10 +398,11 @@ def measure(args, Q, W, dev, x_bits, x0, xs, outs, amaxes, masks, step, nbuf, st
     if args.counter_launches:
         for k in range(args.counter_launches):
             step(k)
-        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).uniform_()
-        dst = torch.empty_like(src)
-        for _ in range(args.counter_launches):
-            dst.copy_(src)
+        # four source/destination pairs in turn, so that no copy finds its source still in the L2 caches (32 MB)
+        srcs = [torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).uniform_() for _ in range(4)]
+        dsts = [torch.empty_like(srcs[0]) for _ in range(4)]
+        for k in range(args.counter_launches):
+            dsts[k % 4].copy_(srcs[k % 4])
         torch.cuda.synchronize()
         print(f"counter pass: {args.counter_launches} steps and {args.counter_launches} copies of "
               f"{COPY_BYTES >> 20} MiB launched", flush=True)
