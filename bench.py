@@ -24,8 +24,9 @@ Also printed in the same JSON line:
                 and under "configs" the other workloads: the 256x1024 RHT+SR/RN pair, the 8192x4096 row-wise RN
                 activation pass, the 14336x4096 16x16 weight pass (W and W^T), the 16384x8192 four-over-six pass
                 the decode of its output (to float, and to bf16 through the fused decode), and the fused decode of the
-                column-wise RHT+SR output back through the inverse transform to bf16 (each timed as a graph of K
-                launches, inputs rotating through HBM).
+                column-wise RHT+SR output back through the inverse transform to bf16, and 32 small tensors quantized
+                by two grouped launches against 64 single-tensor calls (each timed as a graph of K launches, inputs
+                rotating through HBM).
 """
 from __future__ import annotations
 
@@ -298,6 +299,33 @@ def config_figures(Q, W, dev, launches: int) -> dict:
         "frac_of_hbm_peak": round(gbs(bdb, tdb) / HBM_PEAK_GBS, 4), "bytes_per_call": bdb}
     del outs, am, yb
     torch.cuda.empty_cache()
+
+    # 32 small tensors (256 x 1024, the pages' small RHT+SR case, each with its own seed): amax + RHT+SR quantization
+    # as two grouped launches, against the same work as 64 single-tensor calls; both at the same bytes
+    G, r, c = 32, 256, 1024
+    gx = [torch.from_numpy(W.outlier_columns(r, c, seed=100 + k).view(np.int16)).to(dev) for k in range(G)]
+    gm = [W.sign_mask(100 + k, 0) for k in range(G)]
+    ga = [torch.empty(1, dtype=torch.float32, device=dev) for _ in range(G)]
+    go = [Q.alloc_out(r, c, Q.G_PER_TENSOR, dev) for _ in range(G)]
+    seeds = [7] * G
+
+    def grouped(k):
+        Q.nvfp4_amax_grouped(gx, Q.G_PER_TENSOR, True, gm, amaxes=ga)
+        Q.nvfp4_quantize_grouped(gx, ga, Q.ROUND_RHT_SR, Q.G_PER_TENSOR, gm, seeds, [k] * G, outs=go)
+
+    def separate(k):
+        for i in range(G):
+            Q.nvfp4_amax(gx[i], Q.ROWWISE, Q.G_PER_TENSOR, True, gm[i], amax=ga[i])
+            Q.nvfp4_quantize_rht_sr(gx[i], ga[i], gm[i], 7, k, Q.ROWWISE, Q.G_PER_TENSOR, out=go[i])
+
+    tg, ts = timed(grouped), timed(separate)
+    bg = G * algorithmic_bytes(r, c)
+    out["grouped_32x_256x1024_rht_sr"] = {
+        "call": "nvfp4_amax_grouped + nvfp4_quantize_grouped (2 launches) vs nvfp4_amax + nvfp4_quantize_rht_sr per "
+                "tensor (64 calls), row-wise",
+        "grouped_us": round(1e3 * tg, 2), "separate_us": round(1e3 * ts, 2), "speedup": round(ts / tg, 2),
+        "grouped_gbs": gbs(bg, tg), "bytes_per_call": bg}
+    del gx, ga, go
 
     # 8192 x 4096 weight gradient quantized column-wise with RHT + SR, decoded back through the inverse transform
     # to bf16 (V = X^T, 4096 x 8192); outputs and decoded tensors rotate through HBM

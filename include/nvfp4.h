@@ -63,13 +63,30 @@ typedef enum {
 typedef enum { NVFP4_ROWWISE = 1, NVFP4_COLWISE = 2, NVFP4_BOTH = 3 } nvfp4_orient;
 typedef enum { NVFP4_BLOCK_1X16 = 0, NVFP4_BLOCK_16X16 = 1 } nvfp4_block;
 typedef enum { NVFP4_G_PER_TENSOR = 0, NVFP4_G_PER_ROW = 1 } nvfp4_gmode;
-typedef enum { NVFP4_ROUND_RN = 0, NVFP4_ROUND_SR = 1, NVFP4_ROUND_RHT_SR = 2 } nvfp4_rounding;
+typedef enum {
+    NVFP4_ROUND_RN = 0,
+    NVFP4_ROUND_SR = 1,
+    NVFP4_ROUND_RHT_SR = 2,
+    NVFP4_ROUND_4O6 = 3   /* four-over-six: grouped calls only (nvfp4_quantize_4o6 for one tensor) */
+} nvfp4_rounding;
 
 typedef struct {
     uint8_t* codes;  /* [Rv, Cv/2] */
     uint8_t* scales; /* [Rv, Cv/16] */
     float* g;        /* [1] or [Rv] */
 } nvfp4_out;
+
+/* One tensor of a grouped call (row-wise view, 1x16 blocks).  All pointers are device memory. */
+#define NVFP4_MAX_GROUP 32
+typedef struct {
+    const uint16_t* x;   /* [rows, cols] bf16 */
+    int64_t rows, cols;  /* cols % 16 == 0 */
+    float* amax;         /* [1] or [rows] (gmode): written by nvfp4_amax_grouped, read by nvfp4_quantize_grouped */
+    nvfp4_out out;       /* codes [rows, cols/2], scales [rows, cols/16], g [1] or [rows]; unused by the amax call */
+    uint16_t sign_mask;  /* the random signs of the transform (RHT+SR, and the amax with use_rht) */
+    uint64_t seed;       /* Philox key (SR, RHT+SR) */
+    uint64_t offset;     /* Philox offset (SR, RHT+SR) */
+} nvfp4_group_item;
 
 /* Absolute maximum ([P2, results: per-tensor amax kept on the device]; [P3]: row-scaled global scales).
  *   x [rows, cols] bf16; orient NVFP4_ROWWISE or NVFP4_COLWISE selects the view V;
@@ -143,6 +160,21 @@ nvfp4_status nvfp4_quantize_4o6(const uint16_t* x, int64_t rows, int64_t cols, n
  *   codes [rv, cv/2], scales [rv, cv/16], g [1] or [rv] (gmode), y [rv, cv] float.  Shape: cv % 16 == 0. */
 nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv, int64_t cv,
                               nvfp4_gmode gmode, float* y, void* stream);
+
+/* Grouped calls ([P3]: grouped variants of the quantizer are named there as future kernel work): up to
+ * NVFP4_MAX_GROUP row-wise tensors of any shapes, one launch for all of them.  items is a HOST array of count
+ * descriptors (read during the call; the descriptors travel as kernel arguments, nothing is allocated).  The result
+ * for item i is exactly that of the single-tensor call on it:
+ *   nvfp4_amax_grouped     = nvfp4_amax(x, rows, cols, NVFP4_ROWWISE, gmode, use_rht, sign_mask, amax);
+ *   nvfp4_quantize_grouped = nvfp4_quantize_rn / _sr / _rht_sr (row-wise, with the item's sign_mask, seed, offset)
+ *                            or nvfp4_quantize_4o6 (rounding NVFP4_ROUND_4O6), reading the item's amax.
+ *   Errors: count < 0 or > NVFP4_MAX_GROUP -> NVFP4_ERR_SHAPE; items NULL with count > 0 -> NVFP4_ERR_NULL; every
+ *   item is checked as the single-tensor call would check it, and the first failing item's status is returned
+ *   (nothing is enqueued then).  count == 0 is a no-op.  The tensors' buffers must not overlap one another. */
+nvfp4_status nvfp4_amax_grouped(const nvfp4_group_item* items, int32_t count, nvfp4_gmode gmode, int use_rht,
+                                void* stream);
+nvfp4_status nvfp4_quantize_grouped(const nvfp4_group_item* items, int32_t count, nvfp4_gmode gmode,
+                                    nvfp4_rounding rounding, void* stream);
 
 /* Fused decode ([P3]: an optimized decode is named there as future kernel work; [P1, random Hadamard transform]:
  * a block quantized after the rotation is brought back by the rotation's inverse, its transpose).  For each block of

@@ -18,7 +18,8 @@ from ._build import LIB_PATH
 ROWWISE, COLWISE, BOTH = 1, 2, 3
 BLOCK_1X16, BLOCK_16X16 = 0, 1
 G_PER_TENSOR, G_PER_ROW = 0, 1
-ROUND_RN, ROUND_SR, ROUND_RHT_SR = 0, 1, 2
+ROUND_RN, ROUND_SR, ROUND_RHT_SR, ROUND_4O6 = 0, 1, 2, 3
+MAX_GROUP = 32
 
 STATUS = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_SHAPE", 3: "NVFP4_ERR_ALIGN",
           4: "NVFP4_ERR_UNSUPPORTED", 5: "NVFP4_ERR_HIP"}
@@ -34,6 +35,8 @@ SIGNATURES = {
     "nvfp4_quantize_4o6": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
     "nvfp4_dequantize": (_I, [_P, _P, _P, _I64, _I64, _I, _P, _P]),
     "nvfp4_dequantize_fused": (_I, [_P, _P, _P, _I64, _I64, _I, _I, _U16, _I, _P, _P]),
+    "nvfp4_amax_grouped": (_I, [_P, C.c_int32, _I, _I, _P]),
+    "nvfp4_quantize_grouped": (_I, [_P, C.c_int32, _I, _I, _P]),
     "nvfp4_status_str": (C.c_char_p, [_I]),
 }
 
@@ -46,6 +49,11 @@ class NVFP4Error(RuntimeError):
 
 class _Out(C.Structure):
     _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("g", C.c_void_p)]
+
+
+class _GroupItem(C.Structure):
+    _fields_ = [("x", C.c_void_p), ("rows", C.c_int64), ("cols", C.c_int64), ("amax", C.c_void_p), ("out", _Out),
+                ("sign_mask", C.c_uint16), ("seed", C.c_uint64), ("offset", C.c_uint64)]
 
 
 class Quantized(NamedTuple):
@@ -211,3 +219,43 @@ def nvfp4_dequantize_fused(codes: torch.Tensor, scales: torch.Tensor, g: torch.T
                                         gmode, int(bool(use_rht)), sign_mask & 0xFFFF, int(bool(out_bf16)),
                                         _dev(y, "y"), _stream(codes.device, stream)), "nvfp4_dequantize_fused")
     return y
+
+
+def _group(xs, amaxes, outs, sign_masks, seeds, offsets):
+    n = len(xs)
+    arr = (_GroupItem * max(n, 1))()
+    for i, x in enumerate(xs):
+        rows, cols = x.shape
+        o = outs[i] if outs is not None else None
+        arr[i] = _GroupItem(_bf16(x), rows, cols, _dev(amaxes[i], "amax"),
+                            _Out(*(_dev(t, w) for t, w in zip(o, ("codes", "scales", "g")))) if o is not None
+                            else _Out(None, None, None),
+                            (sign_masks[i] if sign_masks is not None else 0) & 0xFFFF,
+                            seeds[i] if seeds is not None else 0, offsets[i] if offsets is not None else 0)
+    return arr
+
+
+def nvfp4_amax_grouped(xs, gmode: int = G_PER_TENSOR, use_rht: bool = False, sign_masks=None, amaxes=None,
+                       stream=None):
+    """Row-wise amax of every tensor of xs in one launch; returns the list of amax tensors."""
+    if amaxes is None:
+        amaxes = [torch.empty((x.shape[0] if gmode == G_PER_ROW else 1,), dtype=torch.float32, device=x.device)
+                  for x in xs]
+    arr = _group(xs, amaxes, None, sign_masks, None, None)
+    dev = xs[0].device if xs else torch.device("cuda")
+    _check(lib().nvfp4_amax_grouped(arr, len(xs), gmode, int(bool(use_rht)), _stream(dev, stream)),
+           "nvfp4_amax_grouped")
+    return amaxes
+
+
+def nvfp4_quantize_grouped(xs, amaxes, rounding: int, gmode: int = G_PER_TENSOR, sign_masks=None, seeds=None,
+                           offsets=None, outs=None, stream=None):
+    """Row-wise 1x16 quantization of every tensor of xs in one launch (RN, SR, RHT+SR or four-over-six); returns
+    the list of Quantized outputs."""
+    if outs is None:
+        outs = [alloc_out(x.shape[0], x.shape[1], gmode, x.device) for x in xs]
+    arr = _group(xs, amaxes, outs, sign_masks, seeds, offsets)
+    dev = xs[0].device if xs else torch.device("cuda")
+    _check(lib().nvfp4_quantize_grouped(arr, len(xs), gmode, rounding, _stream(dev, stream)),
+           "nvfp4_quantize_grouped")
+    return outs

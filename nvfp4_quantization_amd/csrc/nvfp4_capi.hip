@@ -68,6 +68,25 @@ int64_t view_rows(int64_t rows, int64_t cols, nvfp4_orient orient) {
     return orient == NVFP4_COLWISE ? cols : rows;
 }
 
+static_assert(NVFP4_MAX_GROUP == nvfp4::kMaxGroup, "grouped-call limit");
+
+nvfp4_status check_group(const nvfp4_group_item* items, int32_t count, nvfp4_gmode gmode, bool quantize,
+                         nvfp4::GroupTensor* out) {
+    if (count < 0 || count > NVFP4_MAX_GROUP) return NVFP4_ERR_SHAPE;
+    if (count > 0 && !items) return NVFP4_ERR_NULL;
+    NVFP4_TRY(check_gmode(gmode));
+    for (int32_t i = 0; i < count; ++i) {
+        const nvfp4_group_item& it = items[i];
+        NVFP4_TRY(check_sizes(it.rows, it.cols));
+        if (it.cols % 16) return NVFP4_ERR_SHAPE;
+        NVFP4_TRY(check_input(it.x, it.rows, it.cols, it.amax, gmode == NVFP4_G_PER_ROW ? it.rows : 1));
+        if (quantize) NVFP4_TRY(check_out(&it.out, it.rows, it.cols, gmode));
+        out[i] = nvfp4::GroupTensor{it.x, it.rows, it.cols, it.amax, it.out.codes, it.out.scales, it.out.g,
+                                    it.sign_mask, nvfp4::Philox{it.seed, it.offset}};
+    }
+    return NVFP4_OK;
+}
+
 nvfp4_status done(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
 
 nvfp4_status quantize_1x16(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_orient orient, nvfp4_gmode gmode,
@@ -176,6 +195,29 @@ nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const
     NVFP4_TRY(check_buf(y, rv * cv, 16));
     return done(nvfp4::launch_dequantize(codes, scales, g, rv, cv, gmode == NVFP4_G_PER_ROW, y,
                                          static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_amax_grouped(const nvfp4_group_item* items, int32_t count, nvfp4_gmode gmode, int use_rht,
+                                void* stream) {
+    nvfp4::GroupTensor t[NVFP4_MAX_GROUP];
+    NVFP4_TRY(check_group(items, count, gmode, false, t));
+    if (count == 0) return NVFP4_OK;
+    return done(nvfp4::launch_amax_grouped(t, count, gmode == NVFP4_G_PER_ROW, use_rht != 0,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_quantize_grouped(const nvfp4_group_item* items, int32_t count, nvfp4_gmode gmode,
+                                    nvfp4_rounding rounding, void* stream) {
+    if (rounding != NVFP4_ROUND_RN && rounding != NVFP4_ROUND_SR && rounding != NVFP4_ROUND_RHT_SR &&
+        rounding != NVFP4_ROUND_4O6)
+        return NVFP4_ERR_UNSUPPORTED;
+    nvfp4::GroupTensor t[NVFP4_MAX_GROUP];
+    NVFP4_TRY(check_group(items, count, gmode, true, t));
+    if (count == 0) return NVFP4_OK;
+    const int method = rounding == NVFP4_ROUND_RN ? nvfp4::kRN : rounding == NVFP4_ROUND_SR ? nvfp4::kSR
+                       : rounding == NVFP4_ROUND_RHT_SR ? nvfp4::kRHTSR : nvfp4::kFourOverSix;
+    return done(nvfp4::launch_quant_grouped(t, count, gmode == NVFP4_G_PER_ROW, method,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 nvfp4_status nvfp4_dequantize_fused(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv,

@@ -488,24 +488,24 @@ __device__ __forceinline__ float global_scale(float amax) { return amax / 2688.0
 // Row-wise 1x16 quantization: one 16-element block per lane per step; lanes walk the blocks with a grid stride
 // and keep the next block's two loads in flight.
 // ------------------------------------------------------------------------------------------------------------
+// The work of workgroup wg of nwg on one tensor (a kernel's own grid, or its share of a grouped launch).
 template <int MODE, bool PER_ROW>
-__global__ void __launch_bounds__(kThreads)
-k_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, FastDiv per_row, const float* __restrict__ amax,
-                uint32_t sign_mask, RngArgs rng, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
-                float* __restrict__ gout) {
+__device__ __forceinline__ void quant_rowwise_wg(const uint4* __restrict__ x, uint32_t total_blocks, FastDiv per_row,
+                                                 const float* __restrict__ amax, uint32_t sign_mask, RngArgs rng,
+                                                 uint2* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                 float* __restrict__ gout, uint32_t wg, uint32_t nwg, RTable& tab) {
     constexpr bool SR = MODE != kRN;
     constexpr bool RHT = MODE == kRHTSR;
-    __shared__ RTable tab;
     float g = 0.0f;
     Divisor d6{};
     if (!PER_ROW) {
         g = global_scale(amax[0]);
         d6 = make_divisor_uniform(6.0f * g);
-        if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
+        if (wg == 0 && threadIdx.x == 0) gout[0] = g;
         fill_rtable<RHT>(tab, g);
     }
-    const uint32_t stride = gridDim.x * kThreads;
-    uint32_t n = blockIdx.x * kThreads + threadIdx.x;
+    const uint32_t stride = nwg * kThreads;
+    uint32_t n = wg * kThreads + threadIdx.x;
     if (n >= total_blocks) return;
     uint4 a = ld16(x + 2 * (size_t)n), b = ld16(x + 2 * (size_t)n + 1);
     for (; n < total_blocks; n += stride) {
@@ -533,6 +533,16 @@ k_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, FastDiv per_
         a = a2;
         b = b2;
     }
+}
+
+template <int MODE, bool PER_ROW>
+__global__ void __launch_bounds__(kThreads)
+k_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, FastDiv per_row, const float* __restrict__ amax,
+                uint32_t sign_mask, RngArgs rng, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
+                float* __restrict__ gout) {
+    __shared__ RTable tab;
+    quant_rowwise_wg<MODE, PER_ROW>(x, total_blocks, per_row, amax, sign_mask, rng, codes, scales, gout, blockIdx.x,
+                                    gridDim.x, tab);
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -1249,16 +1259,16 @@ __device__ __forceinline__ void quant_4o6_block(const float (&xv)[16], float m, 
 
 // Per-tensor g: grid-stride over blocks with the next block's loads in flight; the multipliers of the 128 scale
 // codes are tabulated once per workgroup.
-__global__ void __launch_bounds__(kThreads)
-k_quant_4o6_tensor(const uint4* __restrict__ x, uint32_t total_blocks, const float* __restrict__ amax,
-                   uint2* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gout) {
-    __shared__ RTable tab;
+__device__ __forceinline__ void quant_4o6_tensor_wg(const uint4* __restrict__ x, uint32_t total_blocks,
+                                                    const float* __restrict__ amax, uint2* __restrict__ codes,
+                                                    uint8_t* __restrict__ scales, float* __restrict__ gout,
+                                                    uint32_t wg, uint32_t nwg, RTable& tab) {
     const float g = global_scale(amax[0]);
-    if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
+    if (wg == 0 && threadIdx.x == 0) gout[0] = g;
     const Divisor dv[2] = {make_divisor_uniform(6.0f * g), make_divisor_uniform(4.0f * g)};   // T = 6 and T = 4
     fill_rtable<false>(tab, g);
-    const uint32_t stride = gridDim.x * kThreads;
-    uint32_t n = blockIdx.x * kThreads + threadIdx.x;
+    const uint32_t stride = nwg * kThreads;
+    uint32_t n = wg * kThreads + threadIdx.x;
     if (n >= total_blocks) return;
     uint4 a = ld16(x + 2 * (size_t)n), b = ld16(x + 2 * (size_t)n + 1);
     for (; n < total_blocks; n += stride) {
@@ -1279,23 +1289,30 @@ k_quant_4o6_tensor(const uint4* __restrict__ x, uint32_t total_blocks, const flo
     }
 }
 
+__global__ void __launch_bounds__(kThreads)
+k_quant_4o6_tensor(const uint4* __restrict__ x, uint32_t total_blocks, const float* __restrict__ amax,
+                   uint2* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gout) {
+    __shared__ RTable tab;
+    quant_4o6_tensor_wg(x, total_blocks, amax, codes, scales, gout, blockIdx.x, gridDim.x, tab);
+}
+
 // Per-row g: a workgroup walks whole rows (grid-stride over rows), lane t taking blocks t, t + 256, ... of each, with
 // the next block's loads (in this row or the next) in flight.  g, its two divisors and the row's multiplier table
 // are computed once per row: the table is double-buffered, so one barrier per row orders it (a thread writes the
 // table of row i only after the barrier of row i - 1, which every thread passes only after its reads of row i - 2).
-__global__ void __launch_bounds__(kThreads)
-k_quant_4o6_rows(const uint4* __restrict__ x, uint32_t rows, uint32_t bpr, const float* __restrict__ amax,
-                 uint2* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gout) {
-    __shared__ RTable tabs[2];
+__device__ __forceinline__ void quant_4o6_rows_wg(const uint4* __restrict__ x, uint32_t rows, uint32_t bpr,
+                                                  const float* __restrict__ amax, uint2* __restrict__ codes,
+                                                  uint8_t* __restrict__ scales, float* __restrict__ gout, uint32_t wg,
+                                                  uint32_t nwg, RTable (&tabs)[2]) {
     const uint32_t t = threadIdx.x;
-    uint32_t row = blockIdx.x;
+    uint32_t row = wg;
     uint4 a = make_uint4(0, 0, 0, 0), b = a;
     if (row < rows && t < bpr) {
         const size_t n0 = (size_t)row * bpr + t;
         a = ld16(x + 2 * n0);
         b = ld16(x + 2 * n0 + 1);
     }
-    for (uint32_t parity = 0; row < rows; row += gridDim.x, parity ^= 1u) {
+    for (uint32_t parity = 0; row < rows; row += nwg, parity ^= 1u) {
         const float g = global_scale(amax[row]);
         if (t == 0) gout[row] = g;
         // a NaN or infinite g needs neither the table nor the divisors (every block of the row is written directly)
@@ -1311,7 +1328,7 @@ k_quant_4o6_rows(const uint4* __restrict__ x, uint32_t rows, uint32_t bpr, const
         for (uint32_t blk = t; blk < bpr; blk += kThreads) {
             uint32_t nrow = row, nblk = blk + kThreads;
             if (nblk >= bpr) {
-                nrow = row + gridDim.x;
+                nrow = row + nwg;
                 nblk = t;
             }
             uint4 a2 = a, b2 = b;
@@ -1331,6 +1348,13 @@ k_quant_4o6_rows(const uint4* __restrict__ x, uint32_t rows, uint32_t bpr, const
             b = b2;
         }
     }
+}
+
+__global__ void __launch_bounds__(kThreads)
+k_quant_4o6_rows(const uint4* __restrict__ x, uint32_t rows, uint32_t bpr, const float* __restrict__ amax,
+                 uint2* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gout) {
+    __shared__ RTable tabs[2];
+    quant_4o6_rows_wg(x, rows, bpr, amax, codes, scales, gout, blockIdx.x, gridDim.x, tabs);
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -1468,12 +1492,12 @@ __device__ __forceinline__ uint32_t rowblock_absmax(const uint4& a, const uint4&
 constexpr uint32_t kRowAmaxPerLane = 8;
 
 template <bool RHT>
-__global__ void __launch_bounds__(kColThreads)
-k_amax_rowwise_tensor(const uint4* __restrict__ x, uint32_t total_blocks, uint32_t sign_mask, uint32_t* amax_bits) {
-    __shared__ uint32_t red[kColRB];
+__device__ __forceinline__ void amax_rowwise_tensor_wg(const uint4* __restrict__ x, uint32_t total_blocks,
+                                                       uint32_t sign_mask, uint32_t* amax_bits, uint32_t wg,
+                                                       uint32_t nwg, uint32_t* red) {
     constexpr uint32_t kPer = kRowAmaxPerLane * kColThreads;   // blocks per workgroup round
     uint32_t m = 0;
-    for (uint32_t base = blockIdx.x * kPer + threadIdx.x; base < total_blocks; base += gridDim.x * kPer) {
+    for (uint32_t base = wg * kPer + threadIdx.x; base < total_blocks; base += nwg * kPer) {
         uint4 a[kRowAmaxPerLane], b[kRowAmaxPerLane];
 #pragma unroll
         for (uint32_t j = 0; j < kRowAmaxPerLane; ++j) {
@@ -1491,13 +1515,20 @@ k_amax_rowwise_tensor(const uint4* __restrict__ x, uint32_t total_blocks, uint32
     if (threadIdx.x == 0) publish_max(amax_bits, m);
 }
 
+template <bool RHT>
+__global__ void __launch_bounds__(kColThreads)
+k_amax_rowwise_tensor(const uint4* __restrict__ x, uint32_t total_blocks, uint32_t sign_mask, uint32_t* amax_bits) {
+    __shared__ uint32_t red[kColRB];
+    amax_rowwise_tensor_wg<RHT>(x, total_blocks, sign_mask, amax_bits, blockIdx.x, gridDim.x, red);
+}
+
 // Row-wise, per row: one workgroup per row (grid-stride over rows), direct store.
 template <bool RHT>
-__global__ void __launch_bounds__(kThreads)
-k_amax_rowwise_rows(const uint4* __restrict__ x, uint32_t rows, uint32_t blocks_per_row, uint32_t sign_mask,
-                    uint32_t* __restrict__ amax_bits) {
-    __shared__ uint32_t lds[kWavesPerGroup];
-    for (uint32_t r = blockIdx.x; r < rows; r += gridDim.x) {
+__device__ __forceinline__ void amax_rowwise_rows_wg(const uint4* __restrict__ x, uint32_t rows,
+                                                     uint32_t blocks_per_row, uint32_t sign_mask,
+                                                     uint32_t* __restrict__ amax_bits, uint32_t wg, uint32_t nwg,
+                                                     uint32_t* lds) {
+    for (uint32_t r = wg; r < rows; r += nwg) {
         uint32_t m = 0;
         for (uint32_t b = threadIdx.x; b < blocks_per_row; b += kThreads) {
             const size_t n = (size_t)r * blocks_per_row + b;
@@ -1508,7 +1539,16 @@ k_amax_rowwise_rows(const uint4* __restrict__ x, uint32_t rows, uint32_t blocks_
     }
 }
 
-// Column-wise (V = X^T), same workgroup layout as k_amax_quant_colwise (one row-block per wave).  Per tensor: one publish per workgroup.  Per row
+template <bool RHT>
+__global__ void __launch_bounds__(kThreads)
+k_amax_rowwise_rows(const uint4* __restrict__ x, uint32_t rows, uint32_t blocks_per_row, uint32_t sign_mask,
+                    uint32_t* __restrict__ amax_bits) {
+    __shared__ uint32_t lds[kWavesPerGroup];
+    amax_rowwise_rows_wg<RHT>(x, rows, blocks_per_row, sign_mask, amax_bits, blockIdx.x, gridDim.x, lds);
+}
+
+// Column-wise (V = X^T), same workgroup layout as k_amax_quant_colwise (one row-block per wave).  Per tensor: one
+// publish per workgroup.  Per row
 // of V (= per column of X): the waves' column maxima are combined in LDS, then one atomic per column.
 template <bool RHT, bool PER_ROW>
 __global__ void __launch_bounds__(kColThreads)
@@ -1650,6 +1690,84 @@ k_amax_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, uint32_
 }
 
 // ------------------------------------------------------------------------------------------------------------
+// Grouped launches ([P3]: grouped variants of the quantizer are named as future kernel work): up to kMaxGroup
+// row-wise tensors of any shapes in one launch.  The descriptors travel as kernel arguments (nothing is allocated);
+// the workgroups are split among the tensors in proportion to their blocks, each workgroup finds its tensor with a
+// scalar search over the first-workgroup indices and then runs the single-tensor body on its share, so every result
+// equals that of the per-tensor call.
+// ------------------------------------------------------------------------------------------------------------
+struct GroupItemK {
+    const uint4* x;
+    uint2* codes;
+    uint8_t* scales;
+    float* g;
+    const float* amax;
+    uint32_t rows, bpr, blocks;   // bpr = blocks per row
+    FastDiv per_row;              // n / bpr
+    uint32_t sign_mask;
+    RngArgs rng;
+    uint32_t wg0;                 // first workgroup of this tensor
+};
+
+struct GroupArgs {
+    uint32_t count, total_wg;
+    GroupItemK it[kMaxGroup];
+};
+static_assert(sizeof(GroupArgs) <= 4096, "grouped descriptors must fit the kernel-argument space");
+
+// The tensor of this workgroup and the workgroup's index and count within it.
+__device__ __forceinline__ uint32_t group_item(const GroupArgs& ga, uint32_t& wg, uint32_t& nwg) {
+    uint32_t i = 0;
+    for (uint32_t j = 1; j < ga.count; ++j)
+        if (ga.it[j].wg0 <= blockIdx.x) i = j;
+    const uint32_t end = i + 1 < ga.count ? ga.it[i + 1].wg0 : ga.total_wg;
+    wg = blockIdx.x - ga.it[i].wg0;
+    nwg = end - ga.it[i].wg0;
+    return i;
+}
+
+template <int MODE, bool PER_ROW>
+__global__ void __launch_bounds__(kThreads) k_quant_grouped(const GroupArgs ga) {
+    __shared__ RTable tab;
+    uint32_t wg, nwg;
+    const GroupItemK& it = ga.it[group_item(ga, wg, nwg)];
+    quant_rowwise_wg<MODE, PER_ROW>(it.x, it.blocks, it.per_row, it.amax, it.sign_mask, it.rng, it.codes, it.scales,
+                                    it.g, wg, nwg, tab);
+}
+
+template <bool PER_ROW>
+__global__ void __launch_bounds__(kThreads) k_quant_4o6_grouped(const GroupArgs ga) {
+    __shared__ RTable tabs[2];
+    uint32_t wg, nwg;
+    const GroupItemK& it = ga.it[group_item(ga, wg, nwg)];
+    if (PER_ROW) quant_4o6_rows_wg(it.x, it.rows, it.bpr, it.amax, it.codes, it.scales, it.g, wg, nwg, tabs);
+    else quant_4o6_tensor_wg(it.x, it.blocks, it.amax, it.codes, it.scales, it.g, wg, nwg, tabs[0]);
+}
+
+// Zeroes the per-tensor amax of every tensor (the grouped per-tensor amax publishes into zeroed values).
+__global__ void k_zero_group_amax(const GroupArgs ga) {
+    if (threadIdx.x < ga.count) *const_cast<float*>(ga.it[threadIdx.x].amax) = 0.0f;
+}
+
+template <bool RHT>
+__global__ void __launch_bounds__(kColThreads) k_amax_grouped_tensor(const GroupArgs ga) {
+    __shared__ uint32_t red[kColRB];
+    uint32_t wg, nwg;
+    const GroupItemK& it = ga.it[group_item(ga, wg, nwg)];
+    amax_rowwise_tensor_wg<RHT>(it.x, it.blocks, it.sign_mask, reinterpret_cast<uint32_t*>(const_cast<float*>(it.amax)),
+                                wg, nwg, red);
+}
+
+template <bool RHT>
+__global__ void __launch_bounds__(kThreads) k_amax_grouped_rows(const GroupArgs ga) {
+    __shared__ uint32_t lds[kWavesPerGroup];
+    uint32_t wg, nwg;
+    const GroupItemK& it = ga.it[group_item(ga, wg, nwg)];
+    amax_rowwise_rows_wg<RHT>(it.x, it.rows, it.bpr, it.sign_mask, reinterpret_cast<uint32_t*>(const_cast<float*>(it.amax)),
+                              wg, nwg, lds);
+}
+
+// ------------------------------------------------------------------------------------------------------------
 // Launch helpers
 // ------------------------------------------------------------------------------------------------------------
 int cu_count() {
@@ -1723,7 +1841,7 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, bool colwi
             if (use_rht) k_amax_rowwise_rows<true><<<grid, kThreads, 0, stream>>>(xv, (uint32_t)rows, bpr, sign_mask, bits);
             else k_amax_rowwise_rows<false><<<grid, kThreads, 0, stream>>>(xv, (uint32_t)rows, bpr, sign_mask, bits);
         } else {
-            const uint32_t grid = grid_for(total, kColThreads * kRowAmaxPerLane, 1);
+            const uint32_t grid = grid_for(total, kColThreads, 1);   // small tensors still spread over several CUs
             if (use_rht) k_amax_rowwise_tensor<true><<<grid, kColThreads, 0, stream>>>(xv, total, sign_mask, bits);
             else k_amax_rowwise_tensor<false><<<grid, kColThreads, 0, stream>>>(xv, total, sign_mask, bits);
         }
@@ -1892,6 +2010,95 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const 
         k_dequantize<true><<<grid, kThreads, 0, stream>>>(c16, scales, g, quarters, fd, reinterpret_cast<float4*>(y));
     else
         k_dequantize<false><<<grid, kThreads, 0, stream>>>(c16, scales, g, quarters, fd, reinterpret_cast<float4*>(y));
+    return hipGetLastError();
+}
+
+// Kernel arguments of a grouped launch over the non-empty tensors; wgs(item) gives a tensor's workgroups.
+template <typename F>
+uint32_t build_group(const GroupTensor* items, int count, GroupArgs& ga, F wgs) {
+    ga.count = 0;
+    uint32_t total = 0;
+    for (int i = 0; i < count; ++i) {
+        const GroupTensor& t = items[i];
+        if (t.rows == 0 || t.cols == 0) continue;
+        GroupItemK& k = ga.it[ga.count++];
+        k.x = reinterpret_cast<const uint4*>(t.x);
+        k.codes = reinterpret_cast<uint2*>(t.codes);
+        k.scales = t.scales;
+        k.g = t.g;
+        k.amax = t.amax;
+        k.rows = (uint32_t)t.rows;
+        k.bpr = (uint32_t)(t.cols / 16);
+        k.blocks = k.rows * k.bpr;
+        k.per_row = make_fastdiv(k.bpr);
+        k.sign_mask = t.sign_mask;
+        k.rng = rng_args(t.rng);
+        k.wg0 = total;
+        total += wgs(k);
+    }
+    ga.total_wg = total;
+    return total;
+}
+
+uint32_t capped(uint64_t need, uint64_t cap) { return (uint32_t)(need == 0 ? 1 : need < cap ? need : cap); }
+
+hipError_t launch_amax_grouped(const GroupTensor* items, int count, bool per_row, bool use_rht, hipStream_t stream) {
+    const uint64_t cus = (uint64_t)cu_count();
+    for (int i = 0; i < count; ++i) {   // empty tensors: amax 0 (per tensor, or per row for rows x 0)
+        const GroupTensor& t = items[i];
+        const uint32_t n = per_row ? (uint32_t)t.rows : 1u;
+        if ((t.rows == 0 || t.cols == 0) && n)
+            k_fill_zero<<<grid_for(n, kThreads, 1), kThreads, 0, stream>>>(reinterpret_cast<uint32_t*>(t.amax), n);
+    }
+    GroupArgs ga;
+    if (per_row) {
+        const uint32_t total = build_group(items, count, ga, [&](const GroupItemK& k) { return capped(k.rows, cus * 16); });
+        if (ga.count) {
+            if (use_rht) k_amax_grouped_rows<true><<<total, kThreads, 0, stream>>>(ga);
+            else k_amax_grouped_rows<false><<<total, kThreads, 0, stream>>>(ga);
+        }
+    } else {
+        // one block per lane and round at least, so that a small tensor still spreads over several CUs
+        const uint32_t total = build_group(items, count, ga, [&](const GroupItemK& k) {
+            return capped((k.blocks + kColThreads - 1) / kColThreads, cus);
+        });
+        if (ga.count) {
+            k_zero_group_amax<<<1, 64, 0, stream>>>(ga);
+            if (use_rht) k_amax_grouped_tensor<true><<<total, kColThreads, 0, stream>>>(ga);
+            else k_amax_grouped_tensor<false><<<total, kColThreads, 0, stream>>>(ga);
+        }
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_grouped(const GroupTensor* items, int count, bool per_row, int method, hipStream_t stream) {
+    const uint64_t cus = (uint64_t)cu_count();
+    for (int i = 0; i < count; ++i) {   // empty tensors: only g is written
+        const GroupTensor& t = items[i];
+        if (t.rows == 0 || t.cols == 0) {
+            const hipError_t e = write_empty_g(t.amax, t.g, per_row ? (uint32_t)t.rows : 1u, stream);
+            if (e != hipSuccess) return e;
+        }
+    }
+    GroupArgs ga;
+    uint32_t total;
+    if (method == kFourOverSix && per_row)
+        total = build_group(items, count, ga, [&](const GroupItemK& k) { return capped(k.rows, cus * 8); });
+    else
+        total = build_group(items, count, ga, [&](const GroupItemK& k) {
+            return capped((k.blocks + kThreads - 1) / kThreads, cus * 8);
+        });
+    if (ga.count == 0) return hipGetLastError();
+#define NVFP4_GQ(M, P) k_quant_grouped<M, P><<<total, kThreads, 0, stream>>>(ga)
+    switch (method) {
+        case kRN: if (per_row) NVFP4_GQ(kRN, true); else NVFP4_GQ(kRN, false); break;
+        case kSR: if (per_row) NVFP4_GQ(kSR, true); else NVFP4_GQ(kSR, false); break;
+        case kRHTSR: if (per_row) NVFP4_GQ(kRHTSR, true); else NVFP4_GQ(kRHTSR, false); break;
+        default:
+            if (per_row) k_quant_4o6_grouped<true><<<total, kThreads, 0, stream>>>(ga);
+            else k_quant_4o6_grouped<false><<<total, kThreads, 0, stream>>>(ga);
+    }
+#undef NVFP4_GQ
     return hipGetLastError();
 }
 

@@ -15,6 +15,21 @@ struct Philox {
     uint64_t offset;
 };
 
+// Grouped launches: at most this many tensors per launch (their descriptors travel as kernel arguments).
+constexpr int kMaxGroup = 32;
+
+// One row-wise tensor of a grouped launch (amax [1] or [rows]; codes/scales/g unused by the amax launch).
+struct GroupTensor {
+    const uint16_t* x;
+    int64_t rows, cols;
+    float* amax;
+    uint8_t* codes;
+    uint8_t* scales;
+    float* g;
+    uint32_t sign_mask;
+    Philox rng;
+};
+
 // amax of V (row-wise: V = X, column-wise: V = X^T); per_row selects one value per row of V.
 hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, bool colwise, bool per_row, bool use_rht,
                        uint32_t sign_mask, float* amax, hipStream_t stream);
@@ -40,6 +55,12 @@ hipError_t launch_quant_4o6(const uint16_t* x, int64_t rows, int64_t cols, bool 
 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv, int64_t cv,
                              bool per_row, float* y, hipStream_t stream);
+
+// Grouped row-wise amax and quantization (method: kRN, kSR, kRHTSR, or kFourOverSix); each tensor's result equals
+// that of the single-tensor launch.
+constexpr int kFourOverSix = 3;
+hipError_t launch_amax_grouped(const GroupTensor* items, int count, bool per_row, bool use_rht, hipStream_t stream);
+hipError_t launch_quant_grouped(const GroupTensor* items, int count, bool per_row, int method, hipStream_t stream);
 
 // Decode with an optional inverse RHT; y is float or bf16 bits.
 hipError_t launch_dequantize_fused(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv,

@@ -34,7 +34,8 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["nvfp4_amax", "nvfp4_quantize_rn", "nvfp4_quantize_sr",
                                            "nvfp4_quantize_rht_sr", "nvfp4_amax_quantize", "nvfp4_quantize_4o6",
-                                           "nvfp4_dequantize", "nvfp4_dequantize_fused", "nvfp4_status_str"])
+                                           "nvfp4_dequantize", "nvfp4_dequantize_fused", "nvfp4_amax_grouped",
+                                           "nvfp4_quantize_grouped", "nvfp4_status_str"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -145,3 +146,31 @@ def test_dequantize_fused_validation(lib):
     assert d(P, P, P + 2, 4, 32, 0, 1, 0, 1, P, None) == ALIGN
     assert d(P, P, P, 4, 32, 0, 1, 0, 0, P + 8, None) == ALIGN             # y must be 16-byte aligned
     assert d(None, None, P, 0, 32, 0, 1, 0, 1, None, None) == OK          # empty: nothing to decode
+
+
+def test_grouped_validation(lib):
+    def items(n, over=None):
+        arr = (B._GroupItem * max(n, 1))()
+        for i in range(n):
+            f = dict(x=P, rows=32, cols=64, amax=P, out=B._Out(P, P, P), sign_mask=1, seed=2, offset=3)
+            f.update((over or {}).get(i, {}))
+            arr[i] = B._GroupItem(**f)
+        return arr
+    a, q = lib.nvfp4_amax_grouped, lib.nvfp4_quantize_grouped
+    assert C.sizeof(B._GroupItem) == 80                                   # the C layout of nvfp4_group_item
+    assert a(items(0), 0, 0, 1, None) == OK                               # nothing to do
+    assert q(items(0), 0, 0, 2, None) == OK
+    assert a(items(2), -1, 0, 1, None) == SHAPE
+    assert a(items(33), 33, 0, 1, None) == SHAPE                          # more than NVFP4_MAX_GROUP
+    assert a(None, 2, 0, 1, None) == NULL
+    assert a(items(2), 2, 5, 1, None) == UNSUP                            # unknown g mode
+    assert q(items(2), 2, 0, 9, None) == UNSUP                            # unknown rounding
+    assert a(items(3, {2: dict(cols=24)}), 3, 0, 1, None) == SHAPE      # item 2: cols % 16
+    assert a(items(3, {1: dict(x=MIS)}), 3, 0, 1, None) == ALIGN
+    assert a(items(3, {1: dict(amax=None)}), 3, 0, 1, None) == NULL
+    assert a(items(2, {0: dict(rows=-1)}), 2, 0, 1, None) == SHAPE
+    assert q(items(2, {1: dict(out=B._Out(P, None, P))}), 2, 0, 0, None) == NULL
+    assert q(items(2, {1: dict(out=B._Out(P, P, P + 2))}), 2, 1, 3, None) == ALIGN
+    assert q(items(2, {0: dict(rows=1 << 20, cols=1 << 20)}), 2, 0, 1, None) == SHAPE
+    # four-over-six is a grouped method only
+    assert lib.nvfp4_amax_quantize(P, 16, 16, 1, 3, 0, 0, 0, P, out(), None) == UNSUP
