@@ -1841,7 +1841,7 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, bool colwi
             if (use_rht) k_amax_rowwise_rows<true><<<grid, kThreads, 0, stream>>>(xv, (uint32_t)rows, bpr, sign_mask, bits);
             else k_amax_rowwise_rows<false><<<grid, kThreads, 0, stream>>>(xv, (uint32_t)rows, bpr, sign_mask, bits);
         } else {
-            const uint32_t grid = grid_for(total, kColThreads, 1);   // small tensors still spread over several CUs
+            const uint32_t grid = grid_for(total, kColThreads * kRowAmaxPerLane, 1);
             if (use_rht) k_amax_rowwise_tensor<true><<<grid, kColThreads, 0, stream>>>(xv, total, sign_mask, bits);
             else k_amax_rowwise_tensor<false><<<grid, kColThreads, 0, stream>>>(xv, total, sign_mask, bits);
         }
@@ -2058,9 +2058,9 @@ hipError_t launch_amax_grouped(const GroupTensor* items, int count, bool per_row
             else k_amax_grouped_rows<false><<<total, kThreads, 0, stream>>>(ga);
         }
     } else {
-        // one block per lane and round at least, so that a small tensor still spreads over several CUs
+        const uint64_t per = (uint64_t)kColThreads * kRowAmaxPerLane;
         const uint32_t total = build_group(items, count, ga, [&](const GroupItemK& k) {
-            return capped((k.blocks + kColThreads - 1) / kColThreads, cus);
+            return capped((k.blocks + per - 1) / per, cus);
         });
         if (ga.count) {
             k_zero_group_amax<<<1, 64, 0, stream>>>(ga);
