@@ -81,6 +81,8 @@ def _declare(L: C.CDLL) -> None:
     L.nvo_quantize_16x16.restype = i32
     L.nvo_quantize_4o6.argtypes = [p, i64, i64, i32, p, i64, i64, p, p, p, p]
     L.nvo_quantize_4o6.restype = i32
+    L.nvo_quantize_4o6_16x16.argtypes = [p, i64, i64, p, i64, i64, p, p, p, p, p, p, p]
+    L.nvo_quantize_4o6_16x16.restype = i32
     L.nvo_dequantize.argtypes = [p, p, p, i64, i64, i32, p]
     L.nvo_dequantize.restype = i32
     L.nvo_rht16_inverse.argtypes = [p, u16, p]
@@ -270,6 +272,25 @@ def quantize_4o6(x: np.ndarray, amax_arr: np.ndarray, gmode: int = G_PER_ROW,
     _check(lib().nvo_quantize_4o6(_ptr(x), rows, cols, gmode, _ptr(amax_arr), a, b, _ptr(codes), _ptr(scales),
                                   _ptr(g), _ptr(choice)), "quantize_4o6")
     return codes, scales, g, choice
+
+
+def quantize_4o6_16x16(x: np.ndarray, amax_arr: np.ndarray, tile_rows: tuple[int, int] | None = None):
+    """Four-over-six with 16x16 tiles (per-tensor g).  Returns ((codes_w, scales_w, g_w), (codes_wt, scales_wt,
+    g_wt), choice) with choice[ti, tj] = 1 where map-to-4 was kept."""
+    x = _bits(x)
+    rows, cols = x.shape
+    a, b = tile_rows if tile_rows is not None else (0, rows // 16)
+    amax_arr = np.ascontiguousarray(amax_arr, dtype=np.float32)
+    cw = np.zeros((rows, cols // 2), np.uint8)
+    sw = np.zeros((rows, cols // 16), np.uint8)
+    gw = np.zeros(1, np.float32)
+    ct = np.zeros((cols, rows // 2), np.uint8)
+    stt = np.zeros((cols, rows // 16), np.uint8)
+    gt = np.zeros(1, np.float32)
+    choice = np.zeros((rows // 16, cols // 16), np.uint8)
+    _check(lib().nvo_quantize_4o6_16x16(_ptr(x), rows, cols, _ptr(amax_arr), a, b, _ptr(cw), _ptr(sw), _ptr(gw),
+                                        _ptr(ct), _ptr(stt), _ptr(gt), _ptr(choice)), "quantize_4o6_16x16")
+    return (cw, sw, gw), (ct, stt, gt), choice
 
 
 def dequantize(codes: np.ndarray, scales: np.ndarray, g: np.ndarray, gmode: int = G_PER_TENSOR) -> np.ndarray:

@@ -517,6 +517,80 @@ int nvo_quantize_4o6(const uint16_t* x, int64_t rows, int64_t cols, int gmode, c
 }
 
 /* ------------------------------------------------------------------------------------------------------------
+ * Four-over-six with 16x16 blocks.  [P3]: the four-over-six reference quantizer takes 1x16 or 16x16 blocks, with a
+ * per-tensor global scale for the 16x16 case here (a tile spans 16 rows, so a row-scaled g does not define one
+ * tile scale).  Per 16x16 tile of X: tamax = the NaN-dominant maximum magnitude of its 256 values; for T in {6, 4}
+ * the tile scale sb_T and the element codes follow the 1x16 rules with tamax in place of bamax; the decoded values
+ * and squared errors are as in the 1x16 case.  READING (the pages pin only the width-16 reduction): each of the
+ * tile's 16 rows is summed by the width-16 tree, then the 16 row sums (row 0 first) by the same tree; map-to-4 is
+ * kept only if its tile sum is strictly lower.  The chosen codes are written in W (packed along X's rows) and/or
+ * W^T (packed along X's columns) orientation, with the tile's scale repeated in each orientation's 1x16 scale
+ * layout, exactly as nvo_quantize_16x16.  choice[tile] (optional, [rows/16, cols/16]) receives 1 for map-to-4.
+ * ---------------------------------------------------------------------------------------------------------- */
+int nvo_quantize_4o6_16x16(const uint16_t* x, int64_t rows, int64_t cols, const float* amax, int64_t tr_begin,
+                           int64_t tr_end, uint8_t* codes_w, uint8_t* scales_w, float* g_w, uint8_t* codes_wt,
+                           uint8_t* scales_wt, float* g_wt, uint8_t* choice) {
+    if (!x || !amax) return NVO_ERR_NULL;
+    if (rows < 0 || cols < 0 || rows % 16 || cols % 16) return NVO_ERR_SHAPE;
+    int want_w = codes_w != NULL, want_wt = codes_wt != NULL;
+    if ((want_w && (!scales_w || !g_w)) || (want_wt && (!scales_wt || !g_wt)) || (!want_w && !want_wt))
+        return NVO_ERR_NULL;
+    int64_t ntr = rows / 16, ntc = cols / 16;
+    if (tr_begin < 0 || tr_end > ntr || tr_begin > tr_end) return NVO_ERR_SHAPE;
+    float g = nvo_global_scale(amax[0]);
+    if (want_w) g_w[0] = g;
+    if (want_wt) g_wt[0] = g;
+    #pragma omp parallel for schedule(static)
+    for (int64_t ti = tr_begin; ti < tr_end; ++ti) {
+        for (int64_t tj = 0; tj < ntc; ++tj) {
+            float v[256];
+            for (int i = 0; i < 16; ++i)
+                for (int j = 0; j < 16; ++j) v[16 * i + j] = nvo_bf16_to_f32(x[(16 * ti + i) * cols + 16 * tj + j]);
+            float tamax = max_of_block(v, 256);
+            uint8_t cand_code[2][256], cand_sb[2];
+            float err[2];
+            const float T[2] = {6.0f, 4.0f};
+            for (int c = 0; c < 2; ++c) {
+                float r;
+                nvo_block_scale(tamax, g, T[c], &cand_sb[c], &r);
+                float sbf = nvo_e4m3_decode(cand_sb[c]);
+                float rowsum[16];
+                for (int i = 0; i < 16; ++i) {
+                    float e[16];
+                    for (int j = 0; j < 16; ++j) {
+                        uint8_t code = nvo_e2m1_rn(v[16 * i + j] * r);
+                        cand_code[c][16 * i + j] = code;
+                        float xh = (nvo_e2m1_decode(code) * sbf) * g;
+                        float d = xh - v[16 * i + j];
+                        e[j] = d * d;
+                    }
+                    rowsum[i] = tree_sum16(e);
+                }
+                err[c] = tree_sum16(rowsum);
+            }
+            int pick = (err[1] < err[0]) ? 1 : 0;
+            const uint8_t* code = cand_code[pick];
+            uint8_t sb = cand_sb[pick];
+            if (choice) choice[ti * ntc + tj] = (uint8_t)pick;
+            for (int i = 0; i < 16; ++i) {
+                int64_t rr = 16 * ti + i, cc = 16 * tj + i;
+                for (int k = 0; k < 8; ++k) {
+                    if (want_w)
+                        codes_w[rr * (cols / 2) + 8 * tj + k] =
+                            (uint8_t)(code[16 * i + 2 * k] | (code[16 * i + 2 * k + 1] << 4));
+                    if (want_wt)
+                        codes_wt[cc * (rows / 2) + 8 * ti + k] =
+                            (uint8_t)(code[16 * (2 * k) + i] | (code[16 * (2 * k + 1) + i] << 4));
+                }
+                if (want_w) scales_w[rr * ntc + tj] = sb;
+                if (want_wt) scales_wt[cc * ntr + ti] = sb;
+            }
+        }
+    }
+    return NVO_OK;
+}
+
+/* ------------------------------------------------------------------------------------------------------------
  * Standard NVFP4 decode.  [P3]: a recipe-agnostic decode of codes, block scales and global scale.
  * y = fl(fl(val(code) * decode(sb)) * g) in binary32 (the inner product is exact: at most 2 x 4 significant bits).
  * codes [rv, cv/2], scales [rv, cv/16], g [1] or [rv]; y [rv, cv] binary32.
