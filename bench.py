@@ -257,6 +257,13 @@ def config_figures(Q, W, dev, launches: int) -> dict:
         "quantize_kernel_us": round(1e3 * t16, 2), "quantize_kernel_gbs": gbs(b16, t16),
         "quantize_kernel_frac_of_hbm_peak": round(gbs(b16, t16) / HBM_PEAK_GBS, 4), "bytes_per_call": b16,
         "amax_us": round(1e3 * ta, 2)}
+    # the same weight, four-over-six with 16x16 tiles (W orientation only; amax given)
+    b46t = 2 * r * c + r * c // 2 + r * c // 16 + 4
+    t46t = timed(lambda k: Q.nvfp4_quantize_4o6_16x16(xs[k % n], am[k % n], out=outs[k % n][0]))
+    out["four_over_six_16x16_14336x4096"] = {
+        "call": "nvfp4_quantize_4o6_16x16", "quantize_kernel_us": round(1e3 * t46t, 2),
+        "quantize_kernel_gbs": gbs(b46t, t46t), "quantize_kernel_frac_of_hbm_peak": round(gbs(b46t, t46t) / HBM_PEAK_GBS, 4),
+        "bytes_per_call": b46t}
     del xs, outs, am
 
     # 16384 x 8192 four-over-six with per-row g (per-row amax given), and the decode of its output

@@ -156,6 +156,16 @@ nvfp4_status nvfp4_amax_quantize(const uint16_t* x, int64_t rows, int64_t cols, 
 nvfp4_status nvfp4_quantize_4o6(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_gmode gmode,
                                 const float* amax, const nvfp4_out* out, void* stream);
 
+/* Four-over-six with 16x16 tiles ([P3]: the reference quantizer takes 1x16 or 16x16 blocks).  One E4M3 scale per
+ * 16x16 tile of X from the tile's maximum; both candidates (T = 6, 4) are formed as in nvfp4_quantize_4o6 with the
+ * tile maximum; the tile's squared error is the sum of its rows, each row by the width-16 tree ((i, i+8), then
+ * strides 4, 2, 1), and the 16 row sums by the same tree; map-to-4 is kept only if strictly lower.  Per-tensor g.
+ *   Output *out: codes [rows, cols/2] packed along X's rows, scales [rows, cols/16] (each tile's scale repeated in
+ *   its 16 rows), g [1].  amax: [1] from nvfp4_amax (row-wise, per tensor, no RHT).
+ *   Shape: rows % 16 == 0 and cols % 16 == 0. */
+nvfp4_status nvfp4_quantize_4o6_16x16(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
+                                      const nvfp4_out* out, void* stream);
+
 /* Standard NVFP4 decode ([P3]: the recipe-agnostic decode): y = fl(fl(val(code) * decode(sb)) * g) as binary32.
  *   codes [rv, cv/2], scales [rv, cv/16], g [1] or [rv] (gmode), y [rv, cv] float.  Shape: cv % 16 == 0. */
 nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv, int64_t cv,

@@ -33,6 +33,7 @@ SIGNATURES = {
     "nvfp4_quantize_rht_sr": (_I, [_P, _I64, _I64, _I, _I, _P, _U16, _U64, _U64, _P, _P]),
     "nvfp4_amax_quantize": (_I, [_P, _I64, _I64, _I, _I, _U16, _U64, _U64, _P, _P, _P]),
     "nvfp4_quantize_4o6": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
+    "nvfp4_quantize_4o6_16x16": (_I, [_P, _I64, _I64, _P, _P, _P]),
     "nvfp4_dequantize": (_I, [_P, _P, _P, _I64, _I64, _I, _P, _P]),
     "nvfp4_dequantize_fused": (_I, [_P, _P, _P, _I64, _I64, _I, _I, _U16, _I, _P, _P]),
     "nvfp4_amax_grouped": (_I, [_P, C.c_int32, _I, _I, _P]),
@@ -192,6 +193,17 @@ def nvfp4_quantize_4o6(x: torch.Tensor, amax: torch.Tensor, gmode: int = G_PER_R
         out = alloc_out(rows, cols, gmode, x.device)
     _check(lib().nvfp4_quantize_4o6(_bf16(x), rows, cols, gmode, _dev(amax, "amax"), _out(out),
                                     _stream(x.device, stream)), "nvfp4_quantize_4o6")
+    return out
+
+
+def nvfp4_quantize_4o6_16x16(x: torch.Tensor, amax: torch.Tensor, out: Optional[Quantized] = None,
+                             stream=None) -> Quantized:
+    """Four-over-six with 16x16 tiles (per-tensor g); codes packed along X's rows."""
+    rows, cols = x.shape
+    if out is None:
+        out = alloc_out(rows, cols, G_PER_TENSOR, x.device)
+    _check(lib().nvfp4_quantize_4o6_16x16(_bf16(x), rows, cols, _dev(amax, "amax"), _out(out),
+                                          _stream(x.device, stream)), "nvfp4_quantize_4o6_16x16")
     return out
 
 

@@ -184,6 +184,16 @@ nvfp4_status nvfp4_quantize_4o6(const uint16_t* x, int64_t rows, int64_t cols, n
                                         out->g, static_cast<hipStream_t>(stream)));
 }
 
+nvfp4_status nvfp4_quantize_4o6_16x16(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
+                                      const nvfp4_out* out, void* stream) {
+    NVFP4_TRY(check_sizes(rows, cols));
+    if (rows % 16 || cols % 16) return NVFP4_ERR_SHAPE;
+    NVFP4_TRY(check_input(x, rows, cols, amax, 1));
+    NVFP4_TRY(check_out(out, rows, cols, NVFP4_G_PER_TENSOR));
+    return done(nvfp4::launch_quant_4o6_16x16(x, rows, cols, amax, out->codes, out->scales, out->g,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv, int64_t cv,
                               nvfp4_gmode gmode, float* y, void* stream) {
     NVFP4_TRY(check_sizes(rv, cv));

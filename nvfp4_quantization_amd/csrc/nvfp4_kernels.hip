@@ -39,6 +39,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerGroup = kThreads / 64;
+constexpr int kThreads16 = 1024;                  // 16x16 four-over-six workgroups
+constexpr int kWavesPerGroup16 = kThreads16 / 64;
 constexpr float kFltMax = 3.402823466e38f;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -182,6 +184,11 @@ __device__ __forceinline__ float absmax16(const float (&w)[16]) {
     const float m5 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m0, m1), m2);
     const float m6 = absmax3(__builtin_elementwise_maximum(m3, m4), w[15], w[15]);
     return __builtin_elementwise_maximum(m5, m6);
+}
+
+// The value held by the other lane of this lane's pair (lanes 2m, 2m + 1): DPP quad permutation [1, 0, 3, 2].
+__device__ __forceinline__ float pair_swap(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
 }
 
 // Maxima over a wave / workgroup of magnitude bit patterns (integer maximum: NaN > inf > finite).
@@ -1358,6 +1365,117 @@ k_quant_4o6_rows(const uint4* __restrict__ x, uint32_t rows, uint32_t bpr, const
 }
 
 // ------------------------------------------------------------------------------------------------------------
+// Four-over-six with 16x16 tiles ([P3]: the reference quantizer takes 1x16 or 16x16 blocks), per-tensor g, codes
+// packed along X's rows (W).  One lane per row of a tile: a 16-lane row of the wave holds one tile (lane i = tile
+// row i), so a row's error sum stays in the lane and the tree over the 16 row sums, like the tile maximum, runs over
+// DPP rotations within the 16-lane row.  A wave takes 4 tiles side by side; a workgroup 64 tiles of one row-block.
+// ------------------------------------------------------------------------------------------------------------
+constexpr uint32_t kTilesPerWave46 = 4;
+constexpr uint32_t kTilesPerGroup46 = kTilesPerWave46 * kWavesPerGroup16;
+
+// The value of lane (i + n) mod 16 of this lane's 16-lane row (DPP row rotation by n).
+template <int N>
+__device__ __forceinline__ uint32_t row_ror(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x120 + N, 0xF, 0xF, false);
+}
+
+template <int N>
+__device__ __forceinline__ float row_ror_f(float v) {
+    return as_f(row_ror<N>(as_u(v)));
+}
+
+// Squared-error sum of one candidate over the tile: this lane's row (the width-16 tree: i with i + 8, then 4, 2, 1),
+// then the 16 row sums by the same tree (rows i and i + 8 first).  Every lane of the 16-lane row returns lane 0's
+// sum, whose operand order is the pinned one.
+__device__ __forceinline__ float tile_error(const float (&xv)[16], uint32_t lo, uint32_t hi, float sbf, float g) {
+    float e[16];
+    unpack8(lo, *reinterpret_cast<float(*)[8]>(&e[0]));
+    unpack8(hi, *reinterpret_cast<float(*)[8]>(&e[8]));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float d = (e[i] * sbf) * g - xv[i];
+        e[i] = d * d;
+    }
+#pragma unroll
+    for (int s2 = 8; s2 >= 1; s2 >>= 1)
+#pragma unroll
+        for (int i = 0; i < s2; ++i) e[i] = e[i] + e[i + s2];
+    float t = e[0];
+    t = t + row_ror_f<8>(t);   // lane i: row i + row i + 8 (lane 0: rows 0 and 8)
+    t = t + row_ror_f<4>(t);
+    t = t + row_ror_f<2>(t);
+    t = t + row_ror_f<1>(t);
+    return __shfl(t, (int)(threadIdx.x & 48u), 64);   // lane 0 of the 16-lane row
+}
+
+__global__ void __launch_bounds__(kThreads16)
+k_quant_4o6_16x16(const uint4* __restrict__ x, uint32_t rows, uint32_t cols, uint32_t groups_per_rb,
+                  const float* __restrict__ amax, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
+                  float* __restrict__ gout) {
+    __shared__ RTable tab;
+    const float g = global_scale(amax[0]);
+    if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
+    const bool gfinite = __builtin_fabsf(g) < __builtin_inff();
+    Divisor dv[2] = {};
+    if (gfinite) {
+        dv[0] = make_divisor_uniform(6.0f * g);
+        dv[1] = make_divisor_uniform(4.0f * g);
+    }
+    fill_rtable<false>(tab, g);
+    const uint32_t rb = blockIdx.x / groups_per_rb;
+    const uint32_t tgrp = blockIdx.x - rb * groups_per_rb;
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    const uint32_t tj = tgrp * kTilesPerGroup46 + wave * kTilesPerWave46 + (lane >> 4);   // tile column
+    const uint32_t r = 16 * rb + (lane & 15u);                                             // X row of this lane
+    const uint32_t ntc = cols >> 4;
+    if (tj >= ntc) return;   // whole 16-lane rows only: every lane of a tile takes the same path
+    const size_t blk = (size_t)r * ntc + tj;   // this lane's 16 elements = block blk of the row-wise view
+    const uint4 a = ld16(x + 2 * blk), b = ld16(x + 2 * blk + 1);
+    float xv[16];
+    widen_row_block<false>(a, b, 0u, xv);
+    // tile maximum: the row's (NaN-dominant), then over the 16 rows on the magnitude bits (NaN > inf > finite)
+    uint32_t mb = as_u(absmax16(xv)) & 0x7FFFFFFFu;
+    mb = umax(mb, row_ror<8>(mb));
+    mb = umax(mb, row_ror<4>(mb));
+    mb = umax(mb, row_ror<2>(mb));
+    mb = umax(mb, row_ror<1>(mb));
+    const float m = as_f(mb);
+    uint32_t lo, hi, sb;
+    if (!gfinite) {
+        // every multiplier is NaN: codes 0x7, and the kept (map-to-6) scale is 0 where the quotient is 0
+        sb = (g != g) ? (m == 0.0f ? 0u : 0x7Fu) : (m < __builtin_inff() ? 0u : 0x7Fu);
+        lo = hi = 0x77777777u;
+    } else {
+        uint32_t cl[2], ch[2], cs[2];
+        float err[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            cs[c] = scale_code(m, dv[c]);
+            const float rr = tab.r[cs[c]];
+            float q[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) q[i] = xv[i] * rr;
+            const float(&q0)[8] = *reinterpret_cast<const float(*)[8]>(&q[0]);
+            const float(&q1)[8] = *reinterpret_cast<const float(*)[8]>(&q[8]);
+            cl[c] = pack8_rn(q0);
+            ch[c] = pack8_rn(q1);
+            // a multiplier of 0 (g = 0) or NaN (NaN tile maximum) can make products NaN (inf * 0, x * NaN): code 0x7
+            if (!(tab.rq[cs[c]] == tab.rq[cs[c]])) [[unlikely]] {
+                cl[c] = patch_nan8(cl[c], q0);
+                ch[c] = patch_nan8(ch[c], q1);
+            }
+            err[c] = tile_error(xv, cl[c], ch[c], e4m3_decode(cs[c]), g);
+        }
+        const bool four = err[1] < err[0];   // ties and NaN keep map-to-6
+        lo = four ? cl[1] : cl[0];
+        hi = four ? ch[1] : ch[0];
+        sb = four ? cs[1] : cs[0];
+    }
+    st_nt(codes + blk, make_uint2(lo, hi));
+    st_nt(scales + blk, (uint8_t)sb);
+}
+
+// ------------------------------------------------------------------------------------------------------------
 // Standard NVFP4 decode ([P3]): y = fl(fl(val(code) * decode(sb)) * g); one 16-element block per lane.
 // ------------------------------------------------------------------------------------------------------------
 template <bool PER_ROW>
@@ -1388,11 +1506,6 @@ k_dequantize(const uint16_t* __restrict__ codes, const uint8_t* __restrict__ sca
 // the lane and stride 8 pairs the lane with its neighbour (one DPP exchange per value).  bf16 rows are then stored
 // 16 bytes per lane, contiguous across the wave.
 // ------------------------------------------------------------------------------------------------------------
-// The value held by the other lane of this lane's pair (lanes 2m, 2m + 1): DPP quad permutation [1, 0, 3, 2].
-__device__ __forceinline__ float pair_swap(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
-}
-
 // binary32 -> bf16 bits (in the high half of the result), round to nearest even on the 16 dropped bits; the
 // increment carries into the exponent exactly as the rounded magnitude does (up to infinity).  NaN -> 0x7FC0.
 __device__ __forceinline__ uint32_t bf16_rne_hi(float f) {
@@ -1979,6 +2092,18 @@ hipError_t launch_quant_16x16(const uint16_t* x, int64_t rows, int64_t cols, con
     else if (codes_w) NVFP4_2D(true, false);
     else NVFP4_2D(false, true);
 #undef NVFP4_2D
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_4o6_16x16(const uint16_t* x, int64_t rows, int64_t cols, const float* amax, uint8_t* codes,
+                                  uint8_t* scales, float* g, hipStream_t stream) {
+    if (rows == 0 || cols == 0) return write_empty_g(amax, g, 1u, stream);
+    const uint32_t ntc = (uint32_t)(cols / 16);
+    const uint32_t groups_per_rb = (ntc + kTilesPerGroup46 - 1) / kTilesPerGroup46;
+    const uint64_t grid = (uint64_t)(rows / 16) * groups_per_rb;
+    k_quant_4o6_16x16<<<(uint32_t)grid, kThreads16, 0, stream>>>(reinterpret_cast<const uint4*>(x), (uint32_t)rows,
+                                                                 (uint32_t)cols, groups_per_rb, amax,
+                                                                 reinterpret_cast<uint2*>(codes), scales, g);
     return hipGetLastError();
 }
 

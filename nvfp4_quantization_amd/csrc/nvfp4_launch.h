@@ -49,6 +49,10 @@ hipError_t launch_quant_16x16(const uint16_t* x, int64_t rows, int64_t cols, con
                               uint8_t* scales_w, float* g_w, uint8_t* codes_wt, uint8_t* scales_wt, float* g_wt,
                               hipStream_t stream);
 
+// Four-over-six with 16x16 tiles, per-tensor g, codes packed along X's rows (scales repeated per row).
+hipError_t launch_quant_4o6_16x16(const uint16_t* x, int64_t rows, int64_t cols, const float* amax, uint8_t* codes,
+                                  uint8_t* scales, float* g, hipStream_t stream);
+
 // Four-over-six, row-wise 1x16 RN.
 hipError_t launch_quant_4o6(const uint16_t* x, int64_t rows, int64_t cols, bool per_row, const float* amax,
                             uint8_t* codes, uint8_t* scales, float* g, hipStream_t stream);

@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["nvfp4_amax", "nvfp4_quantize_rn", "nvfp4_quantize_sr",
                                            "nvfp4_quantize_rht_sr", "nvfp4_amax_quantize", "nvfp4_quantize_4o6",
                                            "nvfp4_dequantize", "nvfp4_dequantize_fused", "nvfp4_amax_grouped",
-                                           "nvfp4_quantize_grouped", "nvfp4_status_str"])
+                                           "nvfp4_quantize_grouped", "nvfp4_quantize_4o6_16x16", "nvfp4_status_str"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -174,3 +174,16 @@ def test_grouped_validation(lib):
     assert q(items(2, {0: dict(rows=1 << 20, cols=1 << 20)}), 2, 0, 1, None) == SHAPE
     # four-over-six is a grouped method only
     assert lib.nvfp4_amax_quantize(P, 16, 16, 1, 3, 0, 0, 0, P, out(), None) == UNSUP
+
+
+def test_4o6_16x16_validation(lib):
+    f = lib.nvfp4_quantize_4o6_16x16
+    assert f(P, 24, 16, P, out(), None) == SHAPE          # rows % 16
+    assert f(P, 16, 24, P, out(), None) == SHAPE          # cols % 16
+    assert f(P, -16, 16, P, out(), None) == SHAPE
+    assert f(None, 16, 16, P, out(), None) == NULL
+    assert f(P, 16, 16, None, out(), None) == NULL
+    assert f(P, 16, 16, P, None, None) == NULL
+    assert f(P, 16, 16, P, out(scales=None), None) == NULL
+    assert f(MIS, 16, 16, P, out(), None) == ALIGN
+    assert f(P, 16, 16, P, out(g=P + 2), None) == ALIGN
