@@ -155,6 +155,11 @@ __device__ __forceinline__ Divisor make_divisor(float d) {
     return Divisor{d, 1.0f / d, d >= 0x1p-60f && d <= 0x1p60f};
 }
 
+// A value equal in every lane, moved to a scalar register.
+__device__ __forceinline__ float uniform_f(float v) {
+    return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(v)));
+}
+
 // The same for a d that is equal in every lane: the branch on fast becomes a scalar one.
 __device__ __forceinline__ Divisor make_divisor_uniform(float d) {
     const Divisor v = make_divisor(d);
@@ -1199,6 +1204,16 @@ k_quant_16x16(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColG
 // Four-over-six ([P3]): row-wise 1x16 RN; candidates T = 6 and T = 4; decode, squared errors, pinned tree sum
 // (i, i+8), then strides 4, 2, 1; map-to-4 kept only if strictly lower.
 // ------------------------------------------------------------------------------------------------------------
+// Decode byte p of d (two codes) with the gfx950 FP4 -> f32 conversion.
+__device__ __forceinline__ f32x2 cvt_fp4_pair(uint32_t d, int p) {
+    switch (p) {
+        case 0: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
+        case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1);
+        case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);
+        default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3);
+    }
+}
+
 // Decode 8 packed codes (element 2k in the low nibble of byte k) with the gfx950 FP4 -> f32 conversion.
 __device__ __forceinline__ void unpack8(uint32_t d, float (&v)[8]) {
     const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
@@ -1385,19 +1400,28 @@ __device__ __forceinline__ float row_ror_f(float v) {
 }
 
 // Squared-error sum of one candidate over the tile: this lane's row (the width-16 tree: i with i + 8, then 4, 2, 1),
-// then the 16 row sums by the same tree (rows i and i + 8 first).  Every lane of the 16-lane row returns lane 0's
-// sum, whose operand order is the pinned one.
+// then the 16 row sums by the same tree (rows i and i + 8 first).  Lane i of the 16-lane row gets the sum over the
+// rows rotated by i; lane 0's operand order is the pinned one.
 __device__ __forceinline__ float tile_error(const float (&xv)[16], uint32_t lo, uint32_t hi, float sbf, float g) {
-    float e[16];
-    unpack8(lo, *reinterpret_cast<float(*)[8]>(&e[0]));
-    unpack8(hi, *reinterpret_cast<float(*)[8]>(&e[8]));
+    // the first half's squares, then each square of the second half added to its partner at once (the first level
+    // of the tree) so that fewer values are live
+    float e[8];
+    unpack8(lo, e);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8; ++i) {
         const float d = (e[i] * sbf) * g - xv[i];
         e[i] = d * d;
     }
 #pragma unroll
-    for (int s2 = 8; s2 >= 1; s2 >>= 1)
+    for (int p = 0; p < 4; ++p) {
+        const f32x2 v = cvt_fp4_pair(hi, p);
+        const float d0 = (v.x * sbf) * g - xv[8 + 2 * p];
+        const float d1 = (v.y * sbf) * g - xv[9 + 2 * p];
+        e[2 * p] = e[2 * p] + d0 * d0;
+        e[2 * p + 1] = e[2 * p + 1] + d1 * d1;
+    }
+#pragma unroll
+    for (int s2 = 4; s2 >= 1; s2 >>= 1)
 #pragma unroll
         for (int i = 0; i < s2; ++i) e[i] = e[i] + e[i + s2];
     float t = e[0];
@@ -1405,34 +1429,27 @@ __device__ __forceinline__ float tile_error(const float (&xv)[16], uint32_t lo, 
     t = t + row_ror_f<4>(t);
     t = t + row_ror_f<2>(t);
     t = t + row_ror_f<1>(t);
-    return __shfl(t, (int)(threadIdx.x & 48u), 64);   // lane 0 of the 16-lane row
+    return t;
 }
 
-__global__ void __launch_bounds__(kThreads16)
-k_quant_4o6_16x16(const uint4* __restrict__ x, uint32_t rows, uint32_t cols, uint32_t groups_per_rb,
-                  const float* __restrict__ amax, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
-                  float* __restrict__ gout) {
-    __shared__ RTable tab;
-    const float g = global_scale(amax[0]);
-    if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
-    const bool gfinite = __builtin_fabsf(g) < __builtin_inff();
-    Divisor dv[2] = {};
-    if (gfinite) {
-        dv[0] = make_divisor_uniform(6.0f * g);
-        dv[1] = make_divisor_uniform(4.0f * g);
-    }
-    fill_rtable<false>(tab, g);
-    const uint32_t rb = blockIdx.x / groups_per_rb;
-    const uint32_t tgrp = blockIdx.x - rb * groups_per_rb;
-    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
-    const uint32_t tj = tgrp * kTilesPerGroup46 + wave * kTilesPerWave46 + (lane >> 4);   // tile column
-    const uint32_t r = 16 * rb + (lane & 15u);                                             // X row of this lane
-    const uint32_t ntc = cols >> 4;
-    if (tj >= ntc) return;   // whole 16-lane rows only: every lane of a tile takes the same path
-    const size_t blk = (size_t)r * ntc + tj;   // this lane's 16 elements = block blk of the row-wise view
-    const uint4 a = ld16(x + 2 * blk), b = ld16(x + 2 * blk + 1);
-    float xv[16];
-    widen_row_block<false>(a, b, 0u, xv);
+// Lane 0's value of this lane's 16-lane row (DPP row broadcast).
+__device__ __forceinline__ uint32_t row_bcast0(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x150, 0xF, 0xF, false);
+}
+
+// A workgroup's outputs for one item: 64 tiles x 16 rows, tile-major (the lanes of a 16-lane row write consecutive
+// slots), one pad slot per tile so that the row-major read-out spreads over the banks; two buffers, so that one
+// barrier per item separates the writes of an item from the read-out of the item before it.
+struct Stage46 {
+    uint2 codes[2][kTilesPerGroup46][17];
+    uint8_t scales[2][kTilesPerGroup46][17];
+};
+static_assert(kWavesPerGroup16 == 16 && kTilesPerGroup46 == 64, "the write-out takes one wave per row, one lane per tile");
+
+// One tile row: both candidates, the tile's errors and the choice (lane 0's, broadcast over the tile's lanes).
+__device__ __forceinline__ void quant_4o6_tile_row(const float (&xv)[16], float g, bool gfinite,
+                                                   const Divisor (&dv)[2], const RTable& tab, uint32_t& lo,
+                                                   uint32_t& hi, uint32_t& sb) {
     // tile maximum: the row's (NaN-dominant), then over the 16 rows on the magnitude bits (NaN > inf > finite)
     uint32_t mb = as_u(absmax16(xv)) & 0x7FFFFFFFu;
     mb = umax(mb, row_ror<8>(mb));
@@ -1440,39 +1457,98 @@ k_quant_4o6_16x16(const uint4* __restrict__ x, uint32_t rows, uint32_t cols, uin
     mb = umax(mb, row_ror<2>(mb));
     mb = umax(mb, row_ror<1>(mb));
     const float m = as_f(mb);
-    uint32_t lo, hi, sb;
     if (!gfinite) {
         // every multiplier is NaN: codes 0x7, and the kept (map-to-6) scale is 0 where the quotient is 0
         sb = (g != g) ? (m == 0.0f ? 0u : 0x7Fu) : (m < __builtin_inff() ? 0u : 0x7Fu);
         lo = hi = 0x77777777u;
-    } else {
-        uint32_t cl[2], ch[2], cs[2];
-        float err[2];
+        return;
+    }
+    uint32_t cl[2], ch[2], cs[2];
+    float err[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        cs[c] = scale_code(m, dv[c]);
+        const float rr = tab.r[cs[c]];
+        float q[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) q[k] = xv[k] * rr;
+        const float(&q0)[8] = *reinterpret_cast<const float(*)[8]>(&q[0]);
+        const float(&q1)[8] = *reinterpret_cast<const float(*)[8]>(&q[8]);
+        cl[c] = pack8_rn(q0);
+        ch[c] = pack8_rn(q1);
+        // a multiplier of 0 (g = 0) or NaN (NaN tile maximum) can make products NaN (inf * 0, x * NaN): code 0x7
+        if (!(tab.rq[cs[c]] == tab.rq[cs[c]])) [[unlikely]] {
+            cl[c] = patch_nan8(cl[c], q0);
+            ch[c] = patch_nan8(ch[c], q1);
+        }
+        err[c] = tile_error(xv, cl[c], ch[c], e4m3_decode(cs[c]), g);
+    }
+    // lane 0's comparison; ties and NaN keep map-to-6
+    const bool four = row_bcast0(err[1] < err[0] ? 1u : 0u) != 0u;
+    lo = four ? cl[1] : cl[0];
+    hi = four ? ch[1] : ch[0];
+    sb = four ? cs[1] : cs[0];
+}
+
+// Items: (16-row band, group of 64 tile columns), band-major; each workgroup loops over items with the next item's
+// loads in flight, and fills the multiplier table once.
+__global__ void __launch_bounds__(kThreads16) __attribute__((amdgpu_waves_per_eu(8, 8)))
+k_quant_4o6_16x16(const uint4* __restrict__ x, uint32_t ntc, uint32_t groups_per_rb, uint32_t items,
+                  const float* __restrict__ amax, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
+                  float* __restrict__ gout) {
+    __shared__ RTable tab;
+    __shared__ Stage46 st;
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    const uint32_t tw = wave * kTilesPerWave46 + (lane >> 4);   // tile of the item
+    const uint32_t i = lane & 15u;                             // row within the tile
+    // this lane's 16 elements of item w = block (16 rb + i) * ntc + tj of the row-wise view
+    auto load = [&](uint32_t w, uint4& a, uint4& b) {
+        const uint32_t rb = w / groups_per_rb;
+        const uint32_t tj = (w - rb * groups_per_rb) * kTilesPerGroup46 + tw;
+        if (tj < ntc) {   // whole 16-lane rows: every lane of a tile takes the same path
+            const size_t blk = (size_t)(16 * rb + i) * ntc + tj;
+            a = ld16(x + 2 * blk);
+            b = ld16(x + 2 * blk + 1);
+        }
+    };
+    uint32_t w = blockIdx.x;
+    uint4 a = {}, b = {};
+    load(w, a, b);
+    const float g = uniform_f(global_scale(amax[0]));   // uniform values kept in scalar registers
+    if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
+    const bool gfinite = __builtin_fabsf(g) < __builtin_inff();
+    Divisor dv[2] = {};
+    if (gfinite) {
+        dv[0] = make_divisor_uniform(6.0f * g);
+        dv[1] = make_divisor_uniform(4.0f * g);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            cs[c] = scale_code(m, dv[c]);
-            const float rr = tab.r[cs[c]];
-            float q[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) q[i] = xv[i] * rr;
-            const float(&q0)[8] = *reinterpret_cast<const float(*)[8]>(&q[0]);
-            const float(&q1)[8] = *reinterpret_cast<const float(*)[8]>(&q[8]);
-            cl[c] = pack8_rn(q0);
-            ch[c] = pack8_rn(q1);
-            // a multiplier of 0 (g = 0) or NaN (NaN tile maximum) can make products NaN (inf * 0, x * NaN): code 0x7
-            if (!(tab.rq[cs[c]] == tab.rq[cs[c]])) [[unlikely]] {
-                cl[c] = patch_nan8(cl[c], q0);
-                ch[c] = patch_nan8(ch[c], q1);
-            }
-            err[c] = tile_error(xv, cl[c], ch[c], e4m3_decode(cs[c]), g);
+            dv[c].d = uniform_f(dv[c].d);
+            dv[c].y = uniform_f(dv[c].y);
         }
-        const bool four = err[1] < err[0];   // ties and NaN keep map-to-6
-        lo = four ? cl[1] : cl[0];
-        hi = four ? ch[1] : ch[0];
-        sb = four ? cs[1] : cs[0];
     }
-    st_nt(codes + blk, make_uint2(lo, hi));
-    st_nt(scales + blk, (uint8_t)sb);
+    fill_rtable<false>(tab, g);
+    for (uint32_t buf = 0; w < items; w += gridDim.x, buf ^= 1u) {
+        const uint32_t rb = w / groups_per_rb;
+        const uint32_t t0 = (w - rb * groups_per_rb) * kTilesPerGroup46;   // first tile column of the item
+        const bool active = t0 + tw < ntc;
+        float xv[16];
+        widen_row_block<false>(a, b, 0u, xv);
+        if (w + gridDim.x < items) load(w + gridDim.x, a, b);   // in flight during this item's arithmetic
+        uint32_t lo = 0, hi = 0, sb = 0;
+        if (active) quant_4o6_tile_row(xv, g, gfinite, dv, tab, lo, hi, sb);
+        if (active) {
+            st.codes[buf][tw][i] = make_uint2(lo, hi);
+            st.scales[buf][tw][i] = (uint8_t)sb;
+        }
+        __syncthreads();
+        // write-out: wave v takes output row v of the band, lane t tile t: 512 contiguous bytes of codes, 64 of scales
+        if (t0 + lane < ntc) {
+            const size_t o = (size_t)(16 * rb + wave) * ntc + t0 + lane;
+            st_nt(codes + o, st.codes[buf][lane][wave]);
+            st_nt(scales + o, st.scales[buf][lane][wave]);
+        }
+    }
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -2100,10 +2176,11 @@ hipError_t launch_quant_4o6_16x16(const uint16_t* x, int64_t rows, int64_t cols,
     if (rows == 0 || cols == 0) return write_empty_g(amax, g, 1u, stream);
     const uint32_t ntc = (uint32_t)(cols / 16);
     const uint32_t groups_per_rb = (ntc + kTilesPerGroup46 - 1) / kTilesPerGroup46;
-    const uint64_t grid = (uint64_t)(rows / 16) * groups_per_rb;
-    k_quant_4o6_16x16<<<(uint32_t)grid, kThreads16, 0, stream>>>(reinterpret_cast<const uint4*>(x), (uint32_t)rows,
-                                                                 (uint32_t)cols, groups_per_rb, amax,
-                                                                 reinterpret_cast<uint2*>(codes), scales, g);
+    const uint32_t items = (uint32_t)(rows / 16) * groups_per_rb;
+    // two 1024-thread workgroups per CU (48 VGPRs), each looping over its share of the items
+    const uint32_t grid = std::min<uint32_t>(items, 2u * (uint32_t)cu_count());
+    k_quant_4o6_16x16<<<grid, kThreads16, 0, stream>>>(reinterpret_cast<const uint4*>(x), ntc, groups_per_rb, items,
+                                                       amax, reinterpret_cast<uint2*>(codes), scales, g);
     return hipGetLastError();
 }
 
