@@ -90,6 +90,8 @@ def _declare(L: C.CDLL) -> None:
     L.nvo_f32_to_bf16.restype = u16
     L.nvo_dequantize_fused.argtypes = [p, p, p, i64, i64, i32, i32, u16, i32, p]
     L.nvo_dequantize_fused.restype = i32
+    L.nvo_swizzle_scales.argtypes = [p, i64, i64, p]
+    L.nvo_swizzle_scales.restype = i32
 
 
 def _ptr(a: np.ndarray | None):
@@ -314,3 +316,17 @@ def dequantize_fused(codes: np.ndarray, scales: np.ndarray, g: np.ndarray, gmode
     _check(lib().nvo_dequantize_fused(_ptr(codes), _ptr(scales), _ptr(g), rv, cv, gmode, int(use_rht),
                                       int(sign_mask), int(out_bf16), _ptr(y)), "dequantize_fused")
     return y
+
+
+def swizzled_size(rv: int, nb: int) -> int:
+    """Bytes of the tiled scale layout of an [rv, nb] scale matrix (whole 128 x 4 tiles)."""
+    return (rv + 127) // 128 * 128 * ((nb + 3) // 4 * 4)
+
+
+def swizzle_scales(scales: np.ndarray) -> np.ndarray:
+    """The [rv, nb] E4M3 scale matrix in the tiled 128 x 4 (32 x 4 x 4) layout, zero-padded; flat uint8."""
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rv, nb = scales.shape
+    out = np.empty(swizzled_size(rv, nb), dtype=np.uint8)
+    _check(lib().nvo_swizzle_scales(_ptr(scales), rv, nb, _ptr(out)), "swizzle_scales")
+    return out

@@ -670,3 +670,28 @@ int nvo_dequantize_fused(const uint8_t* codes, const uint8_t* scales, const floa
     }
     return NVO_OK;
 }
+
+/* ------------------------------------------------------------------------------------------------------------
+ * Tiled scale layout for the FP4 GEMM ([P2, approach]: the quantized operands go to the FP4 GEMM with 1x16 block
+ * scales in the SWIZZLE_32_4_4 layout; [P2, results]: that swizzle is part of the per-call wrapper overhead).
+ * READING (the pages name the layout only): the scale matrix [rv, nb] (nb = scales per row) is cut into tiles of
+ * 128 rows x 4 scale columns, padded with zero bytes to whole tiles; tiles are stored one after another, row tile
+ * major (tile (R, B) at byte 512 * (R * ceil(nb/4) + B)), and inside a tile the 512 bytes are the [32][4][4] array
+ * the name spells out: byte 16 a + 4 b + c holds the scale of row 128 R + 32 b + a, column 4 B + c.  This is the
+ * layout of the 1D block-scaling factors in the cuBLAS documentation.  out holds
+ * ceil(rv/128) * 128 * ceil(nb/4) * 4 bytes.
+ * ---------------------------------------------------------------------------------------------------------- */
+int nvo_swizzle_scales(const uint8_t* scales, int64_t rv, int64_t nb, uint8_t* out) {
+    if (!out || (rv * nb > 0 && !scales)) return NVO_ERR_NULL;
+    if (rv < 0 || nb < 0) return NVO_ERR_SHAPE;
+    int64_t rt = (rv + 127) / 128, bt = (nb + 3) / 4;
+    memset(out, 0, (size_t)(rt * bt * 512));
+    for (int64_t m = 0; m < rv; ++m) {
+        for (int64_t k = 0; k < nb; ++k) {
+            int64_t tile = (m / 128) * bt + k / 4;
+            int64_t a = m % 32, b = (m % 128) / 32, c = k % 4;
+            out[tile * 512 + 16 * a + 4 * b + c] = scales[m * nb + k];
+        }
+    }
+    return NVO_OK;
+}
