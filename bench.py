@@ -352,6 +352,16 @@ def config_figures(Q, W, dev, launches: int) -> dict:
         "frac_of_hbm_peak": round(gbs(bdr, tdr) / HBM_PEAK_GBS, 4), "bytes_per_call": bdr}
     del qs, ys
     torch.cuda.empty_cache()
+
+    # the scales of the 8192 x 4096 row-wise quantization (8192 x 256) to the FP4 GEMM's tiled layout; 8 buffers
+    rv, nb = 8192, 256
+    ss = [torch.randint(0, 256, (rv, nb), dtype=torch.uint8, device=dev) for _ in range(8)]
+    so = [torch.empty(Q.nvfp4_swizzled_scales_size(rv, nb), dtype=torch.uint8, device=dev) for _ in range(8)]
+    tsw = timed(lambda k: Q.nvfp4_swizzle_scales(ss[k % 8], out=so[k % 8]))
+    out["swizzle_scales_8192x256"] = {
+        "call": "nvfp4_swizzle_scales (scales of the 8192x4096 row-wise quantization)",
+        "kernel_us": round(1e3 * tsw, 2), "bytes_per_call": 2 * rv * nb}
+    del ss, so
     return out
 
 

@@ -166,6 +166,20 @@ nvfp4_status nvfp4_quantize_4o6(const uint16_t* x, int64_t rows, int64_t cols, n
 nvfp4_status nvfp4_quantize_4o6_16x16(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
                                       const nvfp4_out* out, void* stream);
 
+/* Scale matrix to the tiled layout of the FP4 GEMM ([P2, approach]: the quantized operands reach the FP4 GEMM with
+ * 1x16 block scales in the SWIZZLE_32_4_4 layout; [P2, results]: the swizzle is part of the per-call wrapper
+ * overhead).  The scale matrix [rv, nb] (row-major, nb scales per row, as written by the quantize calls) is cut into
+ * tiles of 128 rows x 4 scale columns, zero-padded to whole tiles; tile (R, B) is stored at byte
+ * 512 * (R * ceil(nb/4) + B), and inside it byte 16 a + 4 b + c holds the scale of row 128 R + 32 b + a, column
+ * 4 B + c (a [32][4][4] array; the layout of the 1D block-scaling factors in the cuBLAS documentation).
+ *   scales: device, any alignment; out: device, 16-byte aligned, nvfp4_swizzled_scales_size(rv, nb) bytes, every
+ *   byte written (padding = 0).  rv * nb < 2^31.  Errors: NVFP4_ERR_SHAPE, _NULL, _ALIGN; nothing is enqueued then. */
+nvfp4_status nvfp4_swizzle_scales(const uint8_t* scales, int64_t rv, int64_t nb, uint8_t* out, void* stream);
+
+/* Bytes of the tiled layout of an [rv, nb] scale matrix: ceil(rv/128) * 128 * ceil(nb/4) * 4 (0 for negative
+ * sizes).  Host only; no GPU call. */
+int64_t nvfp4_swizzled_scales_size(int64_t rv, int64_t nb);
+
 /* Standard NVFP4 decode ([P3]: the recipe-agnostic decode): y = fl(fl(val(code) * decode(sb)) * g) as binary32.
  *   codes [rv, cv/2], scales [rv, cv/16], g [1] or [rv] (gmode), y [rv, cv] float.  Shape: cv % 16 == 0. */
 nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv, int64_t cv,

@@ -36,6 +36,8 @@ SIGNATURES = {
     "nvfp4_quantize_4o6_16x16": (_I, [_P, _I64, _I64, _P, _P, _P]),
     "nvfp4_dequantize": (_I, [_P, _P, _P, _I64, _I64, _I, _P, _P]),
     "nvfp4_dequantize_fused": (_I, [_P, _P, _P, _I64, _I64, _I, _I, _U16, _I, _P, _P]),
+    "nvfp4_swizzle_scales": (_I, [_P, _I64, _I64, _P, _P]),
+    "nvfp4_swizzled_scales_size": (_I64, [_I64, _I64]),
     "nvfp4_amax_grouped": (_I, [_P, C.c_int32, _I, _I, _P]),
     "nvfp4_quantize_grouped": (_I, [_P, C.c_int32, _I, _I, _P]),
     "nvfp4_status_str": (C.c_char_p, [_I]),
@@ -204,6 +206,20 @@ def nvfp4_quantize_4o6_16x16(x: torch.Tensor, amax: torch.Tensor, out: Optional[
         out = alloc_out(rows, cols, G_PER_TENSOR, x.device)
     _check(lib().nvfp4_quantize_4o6_16x16(_bf16(x), rows, cols, _dev(amax, "amax"), _out(out),
                                           _stream(x.device, stream)), "nvfp4_quantize_4o6_16x16")
+    return out
+
+
+def nvfp4_swizzled_scales_size(rv: int, nb: int) -> int:
+    return int(lib().nvfp4_swizzled_scales_size(rv, nb))
+
+
+def nvfp4_swizzle_scales(scales: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The [rv, nb] uint8 scale matrix in the FP4 GEMM's tiled layout (flat uint8, zero-padded to 128 x 4 tiles)."""
+    rv, nb = scales.shape
+    if out is None:
+        out = torch.empty(nvfp4_swizzled_scales_size(rv, nb), dtype=torch.uint8, device=scales.device)
+    _check(lib().nvfp4_swizzle_scales(_dev(scales, "scales"), rv, nb, _dev(out, "out"),
+                                      _stream(scales.device, stream)), "nvfp4_swizzle_scales")
     return out
 
 

@@ -207,6 +207,19 @@ nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const
                                          static_cast<hipStream_t>(stream)));
 }
 
+nvfp4_status nvfp4_swizzle_scales(const uint8_t* scales, int64_t rv, int64_t nb, uint8_t* out, void* stream) {
+    if (rv < 0 || nb < 0 || rv >= kMaxElems / 16 || nb >= kMaxElems / 16) return NVFP4_ERR_SHAPE;
+    if (rv != 0 && nb > (kMaxElems / 16 - 1) / rv) return NVFP4_ERR_SHAPE;
+    NVFP4_TRY(check_buf(scales, rv * nb, 1));
+    NVFP4_TRY(check_buf(out, nvfp4_swizzled_scales_size(rv, nb), 16));
+    return done(nvfp4::launch_swizzle_scales(scales, rv, nb, out, static_cast<hipStream_t>(stream)));
+}
+
+int64_t nvfp4_swizzled_scales_size(int64_t rv, int64_t nb) {
+    if (rv < 0 || nb < 0) return 0;
+    return (rv + 127) / 128 * 128 * ((nb + 3) / 4 * 4);
+}
+
 nvfp4_status nvfp4_amax_grouped(const nvfp4_group_item* items, int32_t count, nvfp4_gmode gmode, int use_rht,
                                 void* stream) {
     nvfp4::GroupTensor t[NVFP4_MAX_GROUP];

@@ -1552,6 +1552,41 @@ k_quant_4o6_16x16(const uint4* __restrict__ x, uint32_t ntc, uint32_t groups_per
 }
 
 // ------------------------------------------------------------------------------------------------------------
+// Tiled scale layout of the FP4 GEMM ([P2, approach]: 1x16 block scales in the SWIZZLE_32_4_4 layout): tiles of
+// 128 rows x 4 scale columns, row-tile major, each a [32][4][4] byte array (byte 16 a + 4 b + c = row 32 b + a,
+// column c of the tile), zero padding to whole tiles.  One lane per 16-byte row a of a tile: four 4-byte pieces of
+// the rows a, a + 32, a + 64, a + 96.  A workgroup takes 8 consecutive tiles of one row tile.
+// ------------------------------------------------------------------------------------------------------------
+constexpr uint32_t kSwzTilesPerGroup = 8;
+
+template <bool ALIGNED>
+__global__ void __launch_bounds__(256)
+k_swizzle_scales(const uint8_t* __restrict__ s, uint32_t rv, uint32_t nb, uint32_t bt, uint32_t groups_per_rt,
+                 uint4* __restrict__ out) {
+    const uint32_t rt = blockIdx.x / groups_per_rt;
+    const uint32_t B = (blockIdx.x - rt * groups_per_rt) * kSwzTilesPerGroup + (threadIdx.x >> 5);
+    if (B >= bt) return;
+    const uint32_t a = threadIdx.x & 31u, k0 = 4 * B;
+    uint32_t w[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const uint32_t m = 128 * rt + 32 * b + a;
+        w[b] = 0;
+        if (m < rv) {
+            const uint8_t* row = s + (size_t)m * nb + k0;
+            if (ALIGNED) {   // nb % 4 == 0 and s 4-byte aligned: the 4 scales are one aligned word
+                w[b] = *reinterpret_cast<const uint32_t*>(row);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (k0 + c < nb) w[b] |= (uint32_t)row[c] << (8 * c);
+            }
+        }
+    }
+    st_nt(out + ((size_t)rt * bt + B) * 32 + a, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+// ------------------------------------------------------------------------------------------------------------
 // Standard NVFP4 decode ([P3]): y = fl(fl(val(code) * decode(sb)) * g); one 16-element block per lane.
 // ------------------------------------------------------------------------------------------------------------
 template <bool PER_ROW>
@@ -2197,6 +2232,19 @@ hipError_t launch_quant_4o6(const uint16_t* x, int64_t rows, int64_t cols, bool 
     } else {
         k_quant_4o6_tensor<<<grid_for(total, kThreads, 8), kThreads, 0, stream>>>(xv, total, amax, cv, scales, g);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_swizzle_scales(const uint8_t* scales, int64_t rv, int64_t nb, uint8_t* out, hipStream_t stream) {
+    if (rv == 0 || nb == 0) return hipSuccess;
+    const uint32_t rt = (uint32_t)((rv + 127) / 128), bt = (uint32_t)((nb + 3) / 4);
+    const uint32_t gpr = (bt + kSwzTilesPerGroup - 1) / kSwzTilesPerGroup;
+    const uint32_t grid = rt * gpr;
+    uint4* o = reinterpret_cast<uint4*>(out);
+    if (nb % 4 == 0 && reinterpret_cast<uintptr_t>(scales) % 4 == 0)
+        k_swizzle_scales<true><<<grid, 256, 0, stream>>>(scales, (uint32_t)rv, (uint32_t)nb, bt, gpr, o);
+    else
+        k_swizzle_scales<false><<<grid, 256, 0, stream>>>(scales, (uint32_t)rv, (uint32_t)nb, bt, gpr, o);
     return hipGetLastError();
 }
 

@@ -67,6 +67,9 @@ hipError_t launch_amax_grouped(const GroupTensor* items, int count, bool per_row
 hipError_t launch_quant_grouped(const GroupTensor* items, int count, bool per_row, int method, hipStream_t stream);
 
 // Decode with an optional inverse RHT; y is float or bf16 bits.
+// Scale matrix [rv, nb] -> tiled layout of the FP4 GEMM (out: ceil(rv/128) * 128 * ceil(nb/4) * 4 bytes).
+hipError_t launch_swizzle_scales(const uint8_t* scales, int64_t rv, int64_t nb, uint8_t* out, hipStream_t stream);
+
 hipError_t launch_dequantize_fused(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv,
                                    int64_t cv, bool per_row, bool use_rht, uint32_t sign_mask, bool out_bf16, void* y,
                                    hipStream_t stream);

@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["nvfp4_amax", "nvfp4_quantize_rn", "nvfp4_quantize_sr",
                                            "nvfp4_quantize_rht_sr", "nvfp4_amax_quantize", "nvfp4_quantize_4o6",
                                            "nvfp4_dequantize", "nvfp4_dequantize_fused", "nvfp4_amax_grouped",
-                                           "nvfp4_quantize_grouped", "nvfp4_quantize_4o6_16x16", "nvfp4_status_str"])
+                                           "nvfp4_quantize_grouped", "nvfp4_quantize_4o6_16x16", "nvfp4_swizzle_scales",
+                                           "nvfp4_swizzled_scales_size", "nvfp4_status_str"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -187,3 +188,18 @@ def test_4o6_16x16_validation(lib):
     assert f(P, 16, 16, P, out(scales=None), None) == NULL
     assert f(MIS, 16, 16, P, out(), None) == ALIGN
     assert f(P, 16, 16, P, out(g=P + 2), None) == ALIGN
+
+
+def test_swizzle_validation(lib):
+    import oracle as O
+    f = lib.nvfp4_swizzle_scales
+    for rv, nb in [(0, 0), (1, 1), (128, 4), (129, 5), (300, 65), (8192, 256)]:
+        assert lib.nvfp4_swizzled_scales_size(rv, nb) == O.swizzled_size(rv, nb)
+    assert lib.nvfp4_swizzled_scales_size(-1, 4) == 0
+    assert f(P, -1, 4, P, None) == SHAPE
+    assert f(P, 4, -1, P, None) == SHAPE
+    assert f(P, 1 << 16, 1 << 15, P, None) == SHAPE      # rv * nb >= 2^31
+    assert f(None, 4, 4, P, None) == NULL
+    assert f(P, 4, 4, None, None) == NULL
+    assert f(P + 1, 4, 4, P + 4, None) == ALIGN           # out must be 16-byte aligned (scales need not be)
+    assert f(None, 0, 4, None, None) == OK                # nothing to do: no pointer needed
