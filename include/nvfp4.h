@@ -70,10 +70,18 @@ typedef enum {
     NVFP4_ROUND_4O6 = 3   /* four-over-six: grouped calls only (nvfp4_quantize_4o6 for one tensor) */
 } nvfp4_rounding;
 
+/* Layout of an output's scale codes.  NVFP4_SCALES_TILED is the FP4 GEMM's tiled layout (see
+ * nvfp4_swizzle_scales: nvfp4_swizzled_scales_size(Rv, Cv/16) bytes, padding written as zero); it is taken by the
+ * column-wise 1x16 quantize calls (nvfp4_quantize_rn with NVFP4_BLOCK_1X16, _sr, _rht_sr and nvfp4_amax_quantize,
+ * orient NVFP4_COLWISE), whose workgroups own whole 128 x 4 tiles of scales; every other call returns
+ * NVFP4_ERR_UNSUPPORTED for it (row-wise scales: nvfp4_swizzle_scales afterwards). */
+typedef enum { NVFP4_SCALES_ROWMAJOR = 0, NVFP4_SCALES_TILED = 1 } nvfp4_scale_layout;
+
 typedef struct {
-    uint8_t* codes;  /* [Rv, Cv/2] */
-    uint8_t* scales; /* [Rv, Cv/16] */
-    float* g;        /* [1] or [Rv] */
+    uint8_t* codes;       /* [Rv, Cv/2] */
+    uint8_t* scales;      /* [Rv, Cv/16] (NVFP4_SCALES_ROWMAJOR) or the tiled layout */
+    float* g;             /* [1] or [Rv] */
+    int32_t scale_layout; /* nvfp4_scale_layout; zero-initialised = row-major */
 } nvfp4_out;
 
 /* One tensor of a grouped call (row-wise view, 1x16 blocks).  All pointers are device memory. */

@@ -20,6 +20,7 @@ BLOCK_1X16, BLOCK_16X16 = 0, 1
 G_PER_TENSOR, G_PER_ROW = 0, 1
 ROUND_RN, ROUND_SR, ROUND_RHT_SR, ROUND_4O6 = 0, 1, 2, 3
 MAX_GROUP = 32
+SCALES_ROWMAJOR, SCALES_TILED = 0, 1
 
 STATUS = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_SHAPE", 3: "NVFP4_ERR_ALIGN",
           4: "NVFP4_ERR_UNSUPPORTED", 5: "NVFP4_ERR_HIP"}
@@ -51,7 +52,7 @@ class NVFP4Error(RuntimeError):
 
 
 class _Out(C.Structure):
-    _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("g", C.c_void_p)]
+    _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("g", C.c_void_p), ("scale_layout", C.c_int32)]
 
 
 class _GroupItem(C.Structure):
@@ -61,8 +62,9 @@ class _GroupItem(C.Structure):
 
 class Quantized(NamedTuple):
     codes: torch.Tensor   # [Rv, Cv/2] uint8
-    scales: torch.Tensor  # [Rv, Cv/16] uint8 (E4M3 codes)
+    scales: torch.Tensor  # [Rv, Cv/16] uint8 (E4M3 codes), or flat in the tiled layout (scale_layout SCALES_TILED)
     g: torch.Tensor       # [1] or [Rv] float32
+    scale_layout: int = 0
 
 
 _lib: Optional[C.CDLL] = None
@@ -113,16 +115,17 @@ def view_shape(rows: int, cols: int, orient: int) -> tuple[int, int]:
     return (rows, cols) if orient == ROWWISE else (cols, rows)
 
 
-def alloc_out(rv: int, cv: int, gmode: int, device) -> Quantized:
-    return Quantized(torch.empty((rv, cv // 2), dtype=torch.uint8, device=device),
-                     torch.empty((rv, cv // 16), dtype=torch.uint8, device=device),
-                     torch.empty((rv if gmode == G_PER_ROW else 1,), dtype=torch.float32, device=device))
+def alloc_out(rv: int, cv: int, gmode: int, device, scale_layout: int = SCALES_ROWMAJOR) -> Quantized:
+    scales = (torch.empty((rv, cv // 16), dtype=torch.uint8, device=device) if scale_layout == SCALES_ROWMAJOR
+              else torch.empty((nvfp4_swizzled_scales_size(rv, cv // 16),), dtype=torch.uint8, device=device))
+    return Quantized(torch.empty((rv, cv // 2), dtype=torch.uint8, device=device), scales,
+                     torch.empty((rv if gmode == G_PER_ROW else 1,), dtype=torch.float32, device=device), scale_layout)
 
 
 def _out(o: Optional[Quantized]):
     if o is None:
         return None
-    return C.byref(_Out(_dev(o.codes, "codes"), _dev(o.scales, "scales"), _dev(o.g, "g")))
+    return C.byref(_Out(_dev(o.codes, "codes"), _dev(o.scales, "scales"), _dev(o.g, "g"), o.scale_layout))
 
 
 def nvfp4_amax(x: torch.Tensor, orient: int = ROWWISE, gmode: int = G_PER_TENSOR, use_rht: bool = False,
@@ -256,8 +259,8 @@ def _group(xs, amaxes, outs, sign_masks, seeds, offsets):
         rows, cols = x.shape
         o = outs[i] if outs is not None else None
         arr[i] = _GroupItem(_bf16(x), rows, cols, _dev(amaxes[i], "amax"),
-                            _Out(*(_dev(t, w) for t, w in zip(o, ("codes", "scales", "g")))) if o is not None
-                            else _Out(None, None, None),
+                            _Out(_dev(o.codes, "codes"), _dev(o.scales, "scales"), _dev(o.g, "g"), o.scale_layout)
+                            if o is not None else _Out(None, None, None, 0),
                             (sign_masks[i] if sign_masks is not None else 0) & 0xFFFF,
                             seeds[i] if seeds is not None else 0, offsets[i] if offsets is not None else 0)
     return arr

@@ -51,9 +51,11 @@ nvfp4_status check_buf(const void* p, int64_t n, uintptr_t align) {
     return NVFP4_OK;
 }
 
-// Output of a quantization of the view V = [rv, cv].
-nvfp4_status check_out(const nvfp4_out* out, int64_t rv, int64_t cv, nvfp4_gmode gmode) {
+// Output of a quantization of the view V = [rv, cv]; tiled_ok: the call can write the tiled scale layout.
+nvfp4_status check_out(const nvfp4_out* out, int64_t rv, int64_t cv, nvfp4_gmode gmode, bool tiled_ok = false) {
     if (!out) return NVFP4_ERR_NULL;
+    if (out->scale_layout != NVFP4_SCALES_ROWMAJOR && !(tiled_ok && out->scale_layout == NVFP4_SCALES_TILED))
+        return NVFP4_ERR_UNSUPPORTED;
     NVFP4_TRY(check_buf(out->codes, rv * (cv / 2), 16));
     NVFP4_TRY(check_buf(out->scales, rv * (cv / 16), 16));
     return check_buf(out->g, gmode == NVFP4_G_PER_ROW ? rv : 1, 4);
@@ -69,6 +71,7 @@ int64_t view_rows(int64_t rows, int64_t cols, nvfp4_orient orient) {
 }
 
 static_assert(NVFP4_MAX_GROUP == nvfp4::kMaxGroup, "grouped-call limit");
+static_assert(sizeof(nvfp4_out) == 32 && sizeof(nvfp4_group_item) == 88, "the C layouts the binding mirrors");
 
 nvfp4_status check_group(const nvfp4_group_item* items, int32_t count, nvfp4_gmode gmode, bool quantize,
                          nvfp4::GroupTensor* out) {
@@ -97,10 +100,11 @@ nvfp4_status quantize_1x16(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_
     NVFP4_TRY(check_view(rows, cols, orient));
     const int64_t rv = view_rows(rows, cols, orient), cv = orient == NVFP4_COLWISE ? rows : cols;
     NVFP4_TRY(check_input(x, rows, cols, amax, gmode == NVFP4_G_PER_ROW ? rv : 1));
-    NVFP4_TRY(check_out(out, rv, cv, gmode));
+    NVFP4_TRY(check_out(out, rv, cv, gmode, orient == NVFP4_COLWISE));
     return done(nvfp4::launch_quant_1x16(x, rows, cols, orient == NVFP4_COLWISE, gmode == NVFP4_G_PER_ROW, mode,
                                          amax, sign_mask, nvfp4::Philox{seed, offset}, out->codes, out->scales,
-                                         out->g, static_cast<hipStream_t>(stream)));
+                                         out->g, static_cast<hipStream_t>(stream),
+                                         out->scale_layout == NVFP4_SCALES_TILED));
 }
 
 }  // namespace
@@ -165,12 +169,12 @@ nvfp4_status nvfp4_amax_quantize(const uint16_t* x, int64_t rows, int64_t cols, 
     NVFP4_TRY(check_view(rows, cols, orient));
     const int64_t rv = view_rows(rows, cols, orient), cv = orient == NVFP4_COLWISE ? rows : cols;
     NVFP4_TRY(check_input(x, rows, cols, amax, 1));
-    NVFP4_TRY(check_out(out, rv, cv, NVFP4_G_PER_TENSOR));
+    NVFP4_TRY(check_out(out, rv, cv, NVFP4_G_PER_TENSOR, orient == NVFP4_COLWISE));
     const nvfp4::Mode mode = rounding == NVFP4_ROUND_RN ? nvfp4::kRN : rounding == NVFP4_ROUND_SR ? nvfp4::kSR
                                                                                                   : nvfp4::kRHTSR;
     return done(nvfp4::launch_amax_quant(x, rows, cols, orient == NVFP4_COLWISE, mode, sign_mask,
                                          nvfp4::Philox{seed, offset}, amax, out->codes, out->scales, out->g,
-                                         static_cast<hipStream_t>(stream)));
+                                         static_cast<hipStream_t>(stream), out->scale_layout == NVFP4_SCALES_TILED));
 }
 
 nvfp4_status nvfp4_quantize_4o6(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_gmode gmode,

@@ -433,6 +433,11 @@ __device__ __forceinline__ void st_nt(void* p, uint2 v) {
 }
 __device__ __forceinline__ void st_nt(void* p, uint32_t v) { __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p)); }
 __device__ __forceinline__ void st_nt(void* p, uint8_t v) { __builtin_nontemporal_store(v, reinterpret_cast<uint8_t*>(p)); }
+__device__ __forceinline__ void st_nt(void* p, uint4 v) {
+    typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(u32x4v{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4v*>(p));
+}
+
 __device__ __forceinline__ void st_nt(void* p, float4 v) {
     __builtin_nontemporal_store(f32x4v{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4v*>(p));
 }
@@ -657,7 +662,7 @@ struct ColStash {
 template <int G>
 __device__ __forceinline__ void col_write_out_group(const ColStash& st, const ColPos& p, uint32_t rows,
                                                     uint32_t cols, uint32_t nrb, int jg, uint8_t* __restrict__ codes,
-                                                    uint8_t* __restrict__ scales) {
+                                                    uint8_t* __restrict__ scales, bool tiled) {
     const uint32_t col0 = p.strip * 512;
     const uint32_t ncol = min(512u, cols - col0), nr = min((uint32_t)kColRB, nrb - p.group * kColRB);
     const uint32_t rbl = threadIdx.x % kColRB, lq = threadIdx.x / kColRB, rb = p.group * kColRB + rbl;
@@ -669,9 +674,35 @@ __device__ __forceinline__ void col_write_out_group(const ColStash& st, const Co
             const uint4 e = st.e[rbl][j * 64 + lq];
             const uint32_t c = col0 + cl;
             st_nt(codes + (size_t)c * (rows >> 1) + 8 * (size_t)rb, make_uint2(e.x, e.y));
-            st_nt(scales + (size_t)c * nrb + rb, (uint8_t)e.z);
+            if (!tiled) st_nt(scales + (size_t)c * nrb + rb, (uint8_t)e.z);
         }
     }
+}
+
+// The workgroup's scale codes (held in the z words of a ColStash) in the tiled layout of the FP4 GEMM: its 512
+// columns of X are 4 row tiles of V and its 16 row-blocks 4 scale-column tiles, 16 tiles in all; thread t < 512
+// takes tile row a = t % 32 of tile (t / 128, (t / 32) % 4), so each row tile's 2 KiB go out contiguously.  Rows
+// past cols and scale columns past nrb are written as zero.
+__device__ __forceinline__ void col_write_scales_tiled(const ColStash& st, const ColPos& p, uint32_t cols,
+                                                       uint32_t nrb, uint8_t* __restrict__ scales) {
+    if (threadIdx.x >= 512) return;
+    const uint32_t rt = threadIdx.x >> 7, tb = (threadIdx.x >> 5) & 3u, a = threadIdx.x & 31u;
+    const uint32_t col0 = p.strip * 512 + 128 * rt;
+    const uint32_t nr = min((uint32_t)kColRB, nrb - p.group * kColRB);
+    if (col0 >= cols || 4 * tb >= nr) return;
+    const uint32_t bt = (nrb + 3) / 4;
+    uint32_t w[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const uint32_t cl = 128 * rt + 32 * b + a;   // column within the strip
+        w[b] = 0;
+        if (p.strip * 512 + cl < cols) {
+#pragma unroll
+            for (uint32_t c = 0; c < 4; ++c)
+                if (4 * tb + c < nr) w[b] |= (st.e[4 * tb + c][(cl & 7u) * 64 + (cl >> 3)].z & 0xFFu) << (8 * c);
+        }
+    }
+    st_nt(scales + ((size_t)(col0 / 128) * bt + 4 * p.group + tb) * 512 + 16 * a, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
 // Column-wise quantization with a device-resident amax.  The workgroup tile is the same 16 row-blocks x 512 columns,
@@ -738,14 +769,9 @@ struct QuadStash {
     uint32_t cnt[4];
 };
 
-__device__ __forceinline__ void st_nt(void* p, uint4 v) {
-    typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
-    __builtin_nontemporal_store(u32x4v{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4v*>(p));
-}
-
 // Writes quad q's 128 columns x nr row-blocks (one wave).  Codes: instruction t covers output rows 8 t .. 8 t + 7 of
-// the quarter, 8 lanes per row, each lane 16 bytes = row-blocks 2 p and 2 p + 1.  Scales: one lane per output row,
-// 16 bytes.
+// the quarter, 8 lanes per row, each lane 16 bytes = row-blocks 2 p and 2 p + 1.  Scales (unless scales is null):
+// one lane per output row, 16 bytes.
 __device__ __forceinline__ void quad_write_out(const QuadStash& st, const QuadPos& pos, uint32_t rows, uint32_t cols,
                                                uint32_t nrb, uint8_t* __restrict__ codes,
                                                uint8_t* __restrict__ scales) {
@@ -775,6 +801,7 @@ __device__ __forceinline__ void quad_write_out(const QuadStash& st, const QuadPo
             }
         }
     }
+    if (!scales) return;   // tiled scales: quad_write_scales_tiled
 #pragma unroll
     for (uint32_t t = 0; t < 2; ++t) {
         const uint32_t cc = 64 * t + pos.lane, c = col0 + cc;
@@ -789,11 +816,40 @@ __device__ __forceinline__ void quad_write_out(const QuadStash& st, const QuadPo
     }
 }
 
+// The scale codes of quad q in the tiled layout of the FP4 GEMM (tiles of 128 rows x 4 scale columns, each a
+// [32][4][4] byte array: byte 16 a + 4 b + c = row 32 b + a, scale column c; row-tile major; zero padding).  The
+// quad's 128 columns of X are exactly the 128 rows of row tile col0 / 128 of V, and its 16 row-blocks the 4 tiles
+// 4 group .. 4 group + 3 of that row tile, so the quad writes 2 KiB contiguously: lane l takes tile row
+// a = l % 32 of tiles l / 32 and 2 + l / 32 (16 bytes: four 4-byte pieces of rows a, a + 32, a + 64, a + 96).
+// Rows past cols and scale columns past nrb are written as zero.
+__device__ __forceinline__ void quad_write_scales_tiled(const QuadStash& st, const QuadPos& pos, uint32_t cols,
+                                                        uint32_t nrb, uint8_t* __restrict__ scales) {
+    const uint32_t col0 = pos.strip * 512 + 128 * pos.q;
+    if (col0 >= cols) return;
+    const uint32_t nr = min((uint32_t)kColRB, nrb - pos.group * kColRB);
+    const uint32_t bt = (nrb + 3) / 4;
+    uint8_t* base = scales + ((size_t)(col0 / 128) * bt + 4 * pos.group) * 512;
+#pragma unroll
+    for (uint32_t t = 0; t < 2; ++t) {
+        const uint32_t id = 64 * t + pos.lane, tb = id >> 5, a = id & 31u;
+        if (4 * tb < nr) {
+            const uint32_t keep = nr >= 4 * tb + 4 ? 0xFFFFFFFFu : (1u << (8 * (nr - 4 * tb))) - 1u;
+            uint32_t w[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const uint32_t cc = 32 * b + a;
+                w[b] = col0 + cc < cols ? *reinterpret_cast<const uint32_t*>(&st.sc[pos.q][cc][4 * tb]) & keep : 0u;
+            }
+            st_nt(base + (size_t)tb * 512 + 16 * a, make_uint4(w[0], w[1], w[2], w[3]));
+        }
+    }
+}
+
 template <int MODE, bool PER_ROW>
 __global__ void __launch_bounds__(kColThreads)
 k_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColGrid cg,
                 const float* __restrict__ amax, uint32_t sign_mask, RngArgs rng, uint8_t* __restrict__ codes,
-                uint8_t* __restrict__ scales, float* __restrict__ gout) {
+                uint8_t* __restrict__ scales, float* __restrict__ gout, uint32_t tiled) {
     constexpr bool SR = MODE != kRN;
     constexpr bool RHT = MODE == kRHTSR;
     __shared__ QuadStash st;
@@ -852,7 +908,10 @@ k_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, Co
     uint32_t before = 0;
     if (pos.lane == 0)
         before = __hip_atomic_fetch_add(&st.cnt[pos.q], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
-    if (__builtin_amdgcn_readfirstlane(before) == 3) quad_write_out(st, pos, rows, cols, cg.nrb, codes, scales);
+    if (__builtin_amdgcn_readfirstlane(before) == 3) {
+        quad_write_out(st, pos, rows, cols, cg.nrb, codes, tiled ? nullptr : scales);
+        if (tiled) quad_write_scales_tiled(st, pos, cols, cg.nrb, scales);
+    }
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -980,7 +1039,8 @@ template <int MODE>
 __global__ void __launch_bounds__(kColThreads)
 k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColGrid cg, uint32_t sign_mask,
                      RngArgs rng, float* __restrict__ amax_out, uint8_t* __restrict__ codes,
-                     uint8_t* __restrict__ scales, float* __restrict__ gout, uint64_t wait_ticks, uint32_t region) {
+                     uint8_t* __restrict__ scales, float* __restrict__ gout, uint64_t wait_ticks, uint32_t region,
+                     uint32_t tiled) {
     constexpr bool SR = MODE != kRN;
     constexpr bool RHT = MODE == kRHTSR;
     __shared__ ColStash st;
@@ -1062,8 +1122,10 @@ k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t col
             }
         }
         __syncthreads();
-        col_write_out_group<kOutGroup>(st, pos, rows, cols, cg.nrb, jg, codes, scales);
+        col_write_out_group<kOutGroup>(st, pos, rows, cols, cg.nrb, jg, codes, scales, tiled != 0);
     }
+    // every block's scale is in LDS since the last barrier
+    if (tiled) col_write_scales_tiled(st, pos, cols, cg.nrb, scales);
     release_slot(region);
 }
 
@@ -2083,7 +2145,7 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, bool colwi
 
 hipError_t launch_quant_1x16(const uint16_t* x, int64_t rows, int64_t cols, bool colwise, bool per_row, Mode mode,
                              const float* amax, uint32_t sign_mask, Philox rng, uint8_t* codes, uint8_t* scales,
-                             float* g, hipStream_t stream) {
+                             float* g, hipStream_t stream, bool tiled) {
     const RngArgs ra = rng_args(rng);
     const int64_t rv = colwise ? cols : rows;
     if (rows == 0 || cols == 0) return write_empty_g(amax, g, per_row ? (uint32_t)rv : 1u, stream);
@@ -2107,7 +2169,7 @@ hipError_t launch_quant_1x16(const uint16_t* x, int64_t rows, int64_t cols, bool
         const ColGrid w = col_grid(rows, cols, grid);
 #define NVFP4_COL(M, P)                                                                                     \
     k_quant_colwise<M, P><<<grid, kColThreads, 0, stream>>>(x, (uint32_t)rows, (uint32_t)cols, w, amax,    \
-                                                            sign_mask, ra, codes, scales, g)
+                                                            sign_mask, ra, codes, scales, g, tiled ? 1u : 0u)
         switch (mode) {
             case kRN: if (per_row) NVFP4_COL(kRN, true); else NVFP4_COL(kRN, false); break;
             case kSR: if (per_row) NVFP4_COL(kSR, true); else NVFP4_COL(kSR, false); break;
@@ -2133,7 +2195,8 @@ uint64_t fused_wait_ticks() {
 }
 
 hipError_t launch_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, bool colwise, Mode mode, uint32_t sign_mask,
-                             Philox rng, float* amax, uint8_t* codes, uint8_t* scales, float* g, hipStream_t stream) {
+                             Philox rng, float* amax, uint8_t* codes, uint8_t* scales, float* g, hipStream_t stream,
+                             bool tiled) {
     if (rows > 0 && cols > 0 && colwise) {
         uint32_t grid;
         const ColGrid w = col_grid(rows, cols, grid);
@@ -2143,8 +2206,9 @@ hipError_t launch_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, bool
             RngArgs ra = rng_args(rng);
             uint64_t wait = fused_wait_ticks();
             uint32_t region = next_slot_region();
+            uint32_t tl = tiled ? 1u : 0u;
             void* args[] = {(void*)&x, &r, &c, (void*)&w, &sign_mask, &ra, (void*)&amax, (void*)&codes, (void*)&scales,
-                            (void*)&g, &wait, &region};
+                            (void*)&g, &wait, &region, &tl};
             const void* fn = mode == kRN ? (const void*)k_amax_quant_colwise<kRN>
                              : mode == kSR ? (const void*)k_amax_quant_colwise<kSR>
                                            : (const void*)k_amax_quant_colwise<kRHTSR>;
@@ -2177,7 +2241,8 @@ hipError_t launch_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, bool
     // two passes over the tensor: amax, then quantization
     const hipError_t e = launch_amax(x, rows, cols, colwise, false, mode == kRHTSR, sign_mask, amax, stream);
     if (e != hipSuccess) return e;
-    return launch_quant_1x16(x, rows, cols, colwise, false, mode, amax, sign_mask, rng, codes, scales, g, stream);
+    return launch_quant_1x16(x, rows, cols, colwise, false, mode, amax, sign_mask, rng, codes, scales, g, stream,
+                             tiled);
 }
 
 hipError_t launch_quant_16x16(const uint16_t* x, int64_t rows, int64_t cols, const float* amax, uint8_t* codes_w,

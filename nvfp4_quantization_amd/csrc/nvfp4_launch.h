@@ -34,15 +34,17 @@ struct GroupTensor {
 hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, bool colwise, bool per_row, bool use_rht,
                        uint32_t sign_mask, float* amax, hipStream_t stream);
 
-// 1x16 quantization of V (RN, SR or RHT+SR).
+// 1x16 quantization of V (RN, SR or RHT+SR).  tiled (column-wise only): scales in the FP4 GEMM's tiled layout
+// (128 x 4 tiles, [32][4][4] bytes each, zero padding) instead of [Rv, Cv/16].
 hipError_t launch_quant_1x16(const uint16_t* x, int64_t rows, int64_t cols, bool colwise, bool per_row, Mode mode,
                              const float* amax, uint32_t sign_mask, Philox rng, uint8_t* codes, uint8_t* scales,
-                             float* g, hipStream_t stream);
+                             float* g, hipStream_t stream, bool tiled = false);
 
-// amax and 1x16 quantization of V with a per-tensor g: one read of X when the column-wise tensor fits the chip
-// (cooperative launch), else the two launches above.
+// amax and 1x16 quantization of V with a per-tensor g: one read of X when the tensor fits one workgroup per CU,
+// else the two launches above.  tiled as for launch_quant_1x16.
 hipError_t launch_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, bool colwise, Mode mode, uint32_t sign_mask,
-                             Philox rng, float* amax, uint8_t* codes, uint8_t* scales, float* g, hipStream_t stream);
+                             Philox rng, float* amax, uint8_t* codes, uint8_t* scales, float* g, hipStream_t stream,
+                             bool tiled = false);
 
 // 16x16 RN quantization; either output (codes == nullptr) may be skipped.
 hipError_t launch_quant_16x16(const uint16_t* x, int64_t rows, int64_t cols, const float* amax, uint8_t* codes_w,

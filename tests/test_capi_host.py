@@ -63,8 +63,8 @@ def test_status_strings(lib):
         assert lib.nvfp4_status_str(code).decode().startswith(name)
 
 
-def out(codes=P, scales=P, g=P):
-    return C.byref(B._Out(codes, scales, g))
+def out(codes=P, scales=P, g=P, layout=0):
+    return C.byref(B._Out(codes, scales, g, layout))
 
 
 def test_amax_validation(lib):
@@ -158,7 +158,7 @@ def test_grouped_validation(lib):
             arr[i] = B._GroupItem(**f)
         return arr
     a, q = lib.nvfp4_amax_grouped, lib.nvfp4_quantize_grouped
-    assert C.sizeof(B._GroupItem) == 80                                   # the C layout of nvfp4_group_item
+    assert C.sizeof(B._GroupItem) == 88                                   # the C layout of nvfp4_group_item
     assert a(items(0), 0, 0, 1, None) == OK                               # nothing to do
     assert q(items(0), 0, 0, 2, None) == OK
     assert a(items(2), -1, 0, 1, None) == SHAPE
@@ -203,3 +203,20 @@ def test_swizzle_validation(lib):
     assert f(P, 4, 4, None, None) == NULL
     assert f(P + 1, 4, 4, P + 4, None) == ALIGN           # out must be 16-byte aligned (scales need not be)
     assert f(None, 0, 4, None, None) == OK                # nothing to do: no pointer needed
+
+
+def test_tiled_scale_layout_validation(lib):
+    """The tiled scale layout is taken by the column-wise 1x16 calls only (checked before anything is enqueued)."""
+    T = 1
+    assert lib.nvfp4_quantize_rn(P, 16, 16, 0, 1, 0, P, out(layout=T), None, None) == UNSUP   # row-wise
+    assert lib.nvfp4_quantize_sr(P, 16, 16, 1, 0, P, 0, 0, out(layout=T), None) == UNSUP
+    assert lib.nvfp4_quantize_rht_sr(P, 16, 16, 1, 0, P, 0, 0, 0, out(layout=T), None) == UNSUP
+    assert lib.nvfp4_amax_quantize(P, 16, 16, 1, 0, 0, 0, 0, P, out(layout=T), None) == UNSUP
+    assert lib.nvfp4_quantize_rn(P, 16, 16, 1, 3, 0, P, out(), out(layout=T), None) == UNSUP  # 16x16
+    assert lib.nvfp4_quantize_4o6(P, 16, 16, 0, P, out(layout=T), None) == UNSUP
+    assert lib.nvfp4_quantize_4o6_16x16(P, 16, 16, P, out(layout=T), None) == UNSUP
+    assert lib.nvfp4_quantize_sr(P, 16, 16, 2, 0, P, 0, 0, out(layout=7), None) == UNSUP   # unknown layout
+    assert lib.nvfp4_quantize_sr(P, 16, 16, 2, 0, P, 0, 0, out(scales=None, layout=T), None) == NULL
+    it = (B._GroupItem * 1)()
+    it[0] = B._GroupItem(P, 16, 16, P, B._Out(P, P, P, T), 0, 0, 0)
+    assert lib.nvfp4_quantize_grouped(it, 1, 0, 0, None) == UNSUP
