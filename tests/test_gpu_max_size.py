@@ -1,0 +1,169 @@
+"""The largest tensors the C ABI accepts (rows * cols < 2^35 elements, column-wise views with cols < 2^25): 64 GiB
+of bf16 quantized with RN and per-tensor g, row-wise and column-wise, compared with the CPU oracle on sampled rows of
+V (the first and last rows, the rows holding the planted maxima and a seeded random sample).
+
+The input is seeded uniform noise in [-1, 1) generated on the device, with +3 and -3 planted at two positions, so the
+tensor amax is 3 by construction (a property that holds at any size) and the oracle can quantize each sampled row of
+V on its own (round-to-nearest with a per-tensor g makes every row independent of the others).
+"""
+import gc
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import nvfp4_quantization_amd as Q
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    Q.binding.lib()
+    O.lib()
+    free, _ = torch.cuda.mem_get_info()
+    if free < 100 * 2**30:
+        pytest.skip("needs about 90 GiB of free device memory")
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def planted_input(rows, cols, seed):
+    x = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
+    x.uniform_(-1.0, 1.0, generator=torch.Generator(device="cuda").manual_seed(seed))
+    rng = np.random.default_rng(seed)
+    p = [(int(rng.integers(rows)), int(rng.integers(cols))) for _ in range(2)]
+    x[p[0]] = 3.0
+    x[p[1]] = -3.0
+    torch.cuda.synchronize()
+    return x, p
+
+
+def bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def compare(sample_idx, sub_bits, orient, out, amax):
+    oc, os_, og = O.quantize_1x16(sub_bits, np.array([3.0], np.float32), O.MODE_RN, orient, O.G_PER_TENSOR)
+    idx = torch.as_tensor(sample_idx, device="cuda")
+    codes = out.codes.index_select(0, idx).cpu().numpy()
+    scales = out.scales.index_select(0, idx).cpu().numpy()
+    assert amax.item() == 3.0
+    assert out.g.cpu().numpy().view(np.uint32)[0] == og.view(np.uint32)[0]
+    assert np.array_equal(codes, oc), "codes"
+    assert np.array_equal(scales, os_), "scales"
+
+
+def test_rowwise_rn_64gib():
+    rows, cols = 1 << 21, (1 << 14) - 16          # 34,326,183,936 elements: 2,145,386,496 blocks
+    assert rows * cols < 1 << 35
+    say("max size row-wise RN", rows, cols)
+    x, p = planted_input(rows, cols, 41)
+    a = Q.nvfp4_amax(x, Q.ROWWISE, Q.G_PER_TENSOR)
+    out, _ = Q.nvfp4_quantize_rn(x, a, Q.BLOCK_1X16, Q.ROWWISE, Q.G_PER_TENSOR)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    sample = sorted({0, 1, p[0][0], p[1][0], rows // 2, rows - 1, *rng.integers(0, rows, 24).tolist()})
+    sub = bits(x.index_select(0, torch.as_tensor(sample, device="cuda")))
+    compare(sample, sub, O.ROWWISE, out, a)
+    del x, out, a
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_colwise_rn_64gib():
+    rows, cols = 1024, (1 << 25) - 8              # 34,359,730,176 elements; V = X^T has 33,554,424 rows
+    assert rows * cols < 1 << 35
+    say("max size column-wise RN", rows, cols)
+    x, p = planted_input(rows, cols, 43)
+    a = Q.nvfp4_amax(x, Q.COLWISE, Q.G_PER_TENSOR)
+    _, out = Q.nvfp4_quantize_rn(x, a, Q.BLOCK_1X16, Q.COLWISE, Q.G_PER_TENSOR)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    sample = sorted({0, 1, p[0][1], p[1][1], cols // 2, cols - 8, cols - 1, *rng.integers(0, cols, 24).tolist()})
+    sub = bits(x.index_select(1, torch.as_tensor(sample, device="cuda")))   # X[:, sample]: its V rows
+    compare(sample, sub, O.COLWISE, out, a)
+    del x, out, a
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def bands_of(sample_bands):
+    return torch.as_tensor([16 * b + i for b in sample_bands for i in range(16)], device="cuda")
+
+
+def test_16x16_both_orientations_64gib():
+    rows, cols = 1 << 21, (1 << 14) - 16
+    say("max size 16x16 RN, W and W^T", rows, cols)
+    x, p = planted_input(rows, cols, 45)
+    a = Q.nvfp4_amax(x, Q.ROWWISE, Q.G_PER_TENSOR)
+    w, wt = Q.nvfp4_quantize_rn(x, a, Q.BLOCK_16X16, Q.BOTH, Q.G_PER_TENSOR)
+    torch.cuda.synchronize()
+    assert a.item() == 3.0
+    rng = np.random.default_rng(11)
+    nb = rows // 16
+    bands = sorted({0, p[0][0] // 16, p[1][0] // 16, nb // 2, nb - 1, *rng.integers(0, nb, 12).tolist()})
+    ridx = bands_of(bands)
+    sub = bits(x.index_select(0, ridx))
+    (cw, sw, gw), (ct, stt, gt) = O.quantize_16x16(sub, np.array([3.0], np.float32))
+    assert np.array_equal(w.codes.index_select(0, ridx).cpu().numpy(), cw), "W codes"
+    assert np.array_equal(w.scales.index_select(0, ridx).cpu().numpy(), sw), "W scales"
+    # W^T: the sampled bands are byte columns 8 b .. 8 b + 7 of the codes and column b of the scales
+    cidx = torch.as_tensor([8 * b + k for b in bands for k in range(8)], device="cuda")
+    assert np.array_equal(wt.codes.index_select(1, cidx).cpu().numpy(), ct), "W^T codes"
+    assert np.array_equal(wt.scales.index_select(1, torch.as_tensor(bands, device="cuda")).cpu().numpy(), stt)
+    assert w.g.cpu().numpy().view(np.uint32)[0] == gw.view(np.uint32)[0] == gt.view(np.uint32)[0]
+    del x, w, wt, a
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_four_over_six_per_row_64gib():
+    rows, cols = 1 << 21, (1 << 14) - 16
+    say("max size four-over-six, per-row g", rows, cols)
+    x, p = planted_input(rows, cols, 47)
+    a = Q.nvfp4_amax(x, Q.ROWWISE, Q.G_PER_ROW)
+    out = Q.nvfp4_quantize_4o6(x, a, Q.G_PER_ROW)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(13)
+    sample = sorted({0, p[0][0], p[1][0], rows // 2, rows - 1, *rng.integers(0, rows, 24).tolist()})
+    idx = torch.as_tensor(sample, device="cuda")
+    sub = bits(x.index_select(0, idx))
+    oa = O.amax(sub, O.ROWWISE, O.G_PER_ROW)
+    assert np.array_equal(a.index_select(0, idx).cpu().numpy().view(np.uint32), oa.view(np.uint32))
+    oc, os_, og, _ = O.quantize_4o6(sub, oa, O.G_PER_ROW)
+    assert np.array_equal(out.codes.index_select(0, idx).cpu().numpy(), oc), "codes"
+    assert np.array_equal(out.scales.index_select(0, idx).cpu().numpy(), os_), "scales"
+    assert np.array_equal(out.g.index_select(0, idx).cpu().numpy().view(np.uint32), og.view(np.uint32))
+    del x, out, a
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_four_over_six_16x16_64gib():
+    rows, cols = 1 << 21, (1 << 14) - 16
+    say("max size four-over-six 16x16", rows, cols)
+    x, p = planted_input(rows, cols, 49)
+    a = Q.nvfp4_amax(x, Q.ROWWISE, Q.G_PER_TENSOR)
+    out = Q.nvfp4_quantize_4o6_16x16(x, a)
+    torch.cuda.synchronize()
+    assert a.item() == 3.0
+    rng = np.random.default_rng(15)
+    nb = rows // 16
+    bands = sorted({0, p[0][0] // 16, p[1][0] // 16, nb // 2, nb - 1, *rng.integers(0, nb, 12).tolist()})
+    ridx = bands_of(bands)
+    sub = bits(x.index_select(0, ridx))
+    (cw, sw, gw), _, _ = O.quantize_4o6_16x16(sub, np.array([3.0], np.float32))
+    assert np.array_equal(out.codes.index_select(0, ridx).cpu().numpy(), cw), "codes"
+    assert np.array_equal(out.scales.index_select(0, ridx).cpu().numpy(), sw), "scales"
+    assert out.g.cpu().numpy().view(np.uint32)[0] == gw.view(np.uint32)[0]
+    del x, out, a
+    gc.collect()
+    torch.cuda.empty_cache()
