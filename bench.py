@@ -237,11 +237,18 @@ def config_figures(Q, W, dev, launches: int) -> dict:
     single = timed(lambda k: Q.nvfp4_amax_quantize(xs[k % n], Q.ROWWISE, Q.ROUND_RN, amax=am[k % n], out=outs[k % n]))
     qonly = timed(lambda k: Q.nvfp4_quantize_rn(xs[k % n], am[k % n], Q.BLOCK_1X16, Q.ROWWISE, Q.G_PER_TENSOR,
                                                 row_out=outs[k % n]))
+    # the same calls writing the scales in the FP4 GEMM's tiled layout
+    touts = [Q.alloc_out(r, c, Q.G_PER_TENSOR, dev, Q.SCALES_TILED) for _ in range(n)]
+    single_t = timed(lambda k: Q.nvfp4_amax_quantize(xs[k % n], Q.ROWWISE, Q.ROUND_RN, amax=am[k % n],
+                                                     out=touts[k % n]))
+    qonly_t = timed(lambda k: Q.nvfp4_quantize_rn(xs[k % n], am[k % n], Q.BLOCK_1X16, Q.ROWWISE, Q.G_PER_TENSOR,
+                                                  row_out=touts[k % n]))
     out["fprop_rn_8192x4096"] = {
         "single_read_us": round(1e3 * single, 2), "single_read_gbs": gbs(b, single),
         "quantize_kernel_us": round(1e3 * qonly, 2), "quantize_kernel_gbs": gbs(b, qonly),
-        "quantize_kernel_frac_of_hbm_peak": round(gbs(b, qonly) / HBM_PEAK_GBS, 4)}
-    del xs, outs, am
+        "quantize_kernel_frac_of_hbm_peak": round(gbs(b, qonly) / HBM_PEAK_GBS, 4),
+        "tiled_scales": {"single_read_us": round(1e3 * single_t, 2), "quantize_kernel_us": round(1e3 * qonly_t, 2)}}
+    del xs, outs, am, touts
 
     # 14336 x 4096 weight, 16x16 blocks, W and W^T from one read (amax given)
     r, c = 14336, 4096

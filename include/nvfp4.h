@@ -71,10 +71,10 @@ typedef enum {
 } nvfp4_rounding;
 
 /* Layout of an output's scale codes.  NVFP4_SCALES_TILED is the FP4 GEMM's tiled layout (see
- * nvfp4_swizzle_scales: nvfp4_swizzled_scales_size(Rv, Cv/16) bytes, padding written as zero); it is taken by the
- * column-wise 1x16 quantize calls (nvfp4_quantize_rn with NVFP4_BLOCK_1X16, _sr, _rht_sr and nvfp4_amax_quantize,
- * orient NVFP4_COLWISE), whose workgroups own whole 128 x 4 tiles of scales; every other call returns
- * NVFP4_ERR_UNSUPPORTED for it (row-wise scales: nvfp4_swizzle_scales afterwards). */
+ * nvfp4_swizzle_scales: nvfp4_swizzled_scales_size(Rv, Cv/16) bytes, padding written as zero), written by the
+ * quantize kernels themselves; it is taken by the 1x16 quantize calls (nvfp4_quantize_rn with NVFP4_BLOCK_1X16,
+ * nvfp4_quantize_sr, nvfp4_quantize_rht_sr and nvfp4_amax_quantize, either orientation).  The 16x16, four-over-six
+ * and grouped calls return NVFP4_ERR_UNSUPPORTED for it (their scales can be re-laid by nvfp4_swizzle_scales). */
 typedef enum { NVFP4_SCALES_ROWMAJOR = 0, NVFP4_SCALES_TILED = 1 } nvfp4_scale_layout;
 
 typedef struct {

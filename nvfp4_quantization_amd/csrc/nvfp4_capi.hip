@@ -100,7 +100,7 @@ nvfp4_status quantize_1x16(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_
     NVFP4_TRY(check_view(rows, cols, orient));
     const int64_t rv = view_rows(rows, cols, orient), cv = orient == NVFP4_COLWISE ? rows : cols;
     NVFP4_TRY(check_input(x, rows, cols, amax, gmode == NVFP4_G_PER_ROW ? rv : 1));
-    NVFP4_TRY(check_out(out, rv, cv, gmode, orient == NVFP4_COLWISE));
+    NVFP4_TRY(check_out(out, rv, cv, gmode, true));
     return done(nvfp4::launch_quant_1x16(x, rows, cols, orient == NVFP4_COLWISE, gmode == NVFP4_G_PER_ROW, mode,
                                          amax, sign_mask, nvfp4::Philox{seed, offset}, out->codes, out->scales,
                                          out->g, static_cast<hipStream_t>(stream),
@@ -169,7 +169,7 @@ nvfp4_status nvfp4_amax_quantize(const uint16_t* x, int64_t rows, int64_t cols, 
     NVFP4_TRY(check_view(rows, cols, orient));
     const int64_t rv = view_rows(rows, cols, orient), cv = orient == NVFP4_COLWISE ? rows : cols;
     NVFP4_TRY(check_input(x, rows, cols, amax, 1));
-    NVFP4_TRY(check_out(out, rv, cv, NVFP4_G_PER_TENSOR, orient == NVFP4_COLWISE));
+    NVFP4_TRY(check_out(out, rv, cv, NVFP4_G_PER_TENSOR, true));
     const nvfp4::Mode mode = rounding == NVFP4_ROUND_RN ? nvfp4::kRN : rounding == NVFP4_ROUND_SR ? nvfp4::kSR
                                                                                                   : nvfp4::kRHTSR;
     return done(nvfp4::launch_amax_quant(x, rows, cols, orient == NVFP4_COLWISE, mode, sign_mask,

@@ -563,6 +563,121 @@ k_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, FastDiv per_
 }
 
 // ------------------------------------------------------------------------------------------------------------
+// Row-wise quantization with the scales in the FP4 GEMM's tiled layout (128 x 4 tiles, each a [32][4][4] byte
+// array: byte 16 a + 4 b + c = row 32 b + a, scale column c; row-tile major; zero padding).  A tile needs 128 rows,
+// so these kernels give each workgroup item a 128-row x 64-block piece of V (16 tiles of scales): slice j = 0..7 of
+// the item is rows 16 j .. 16 j + 15, wave w takes row 16 j + w and lane l block l, so a wave reads 2 KiB of a row
+// and writes 512 contiguous bytes of codes; the scale bytes are collected in LDS and written as 16 whole tiles
+// (8 KiB, contiguous).
+// ------------------------------------------------------------------------------------------------------------
+struct RowTileItem {
+    uint32_t row0;   // first row of V
+    uint32_t blk0;   // first block of those rows
+};
+
+__device__ __forceinline__ RowTileItem row_tile_item(uint32_t item, uint32_t items_per_band) {
+    const uint32_t band = item / items_per_band;
+    return RowTileItem{128 * band, 64 * (item - band * items_per_band)};
+}
+
+// Writes the item's 16 tiles (8 KiB, contiguous); get(r, c) is the scale byte of row r (0..127) and block c (0..63)
+// of the item.  Thread t < 512 takes tile row a = t % 32 of tile t / 32: four 4-byte pieces of rows a, a + 32,
+// a + 64, a + 96.  Rows past rows and blocks past nb are written as zero; tiles past the last scale column are not
+// written.
+template <typename F>
+__device__ __forceinline__ void row_write_scales_tiled(const RowTileItem& it, uint32_t rows, uint32_t nb,
+                                                       uint8_t* __restrict__ scales, F get) {
+    if (threadIdx.x >= 512) return;
+    const uint32_t tb = threadIdx.x >> 5, a = threadIdx.x & 31u;
+    const uint32_t bt = (nb + 3) / 4, B = it.blk0 / 4 + tb;
+    if (B >= bt) return;
+    uint32_t w[4];
+#pragma unroll
+    for (uint32_t b = 0; b < 4; ++b) {
+        const uint32_t r = 32 * b + a;
+        uint32_t v = 0;
+        if (it.row0 + r < rows) {
+#pragma unroll
+            for (uint32_t c = 0; c < 4; ++c)
+                if (it.blk0 + 4 * tb + c < nb) v |= (uint32_t)get(r, 4 * tb + c) << (8 * c);
+        }
+        w[b] = v;
+    }
+    st_nt(scales + ((size_t)(it.row0 / 128) * bt + B) * 512 + 16 * a, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+// Amax given: 512-thread workgroups loop over the items; wave w takes rows 8 j + w (j = 0..15) of the item, block l
+// in lane l, with the next block's loads in flight.  The LDS scale stage is double-buffered, so one barrier per item
+// separates its writes from the read-out of the item before.
+constexpr uint32_t kThreadsRT = 512;
+
+template <int MODE, bool PER_ROW>
+__global__ void __launch_bounds__(kThreadsRT)
+k_quant_rowwise_tiled(const uint4* __restrict__ x, uint32_t rows, uint32_t nb, uint32_t items_per_band, uint32_t items,
+                      const float* __restrict__ amax, uint32_t sign_mask, RngArgs rng, uint2* __restrict__ codes,
+                      uint8_t* __restrict__ scales, float* __restrict__ gout) {
+    constexpr bool SR = MODE != kRN;
+    constexpr bool RHT = MODE == kRHTSR;
+    __shared__ RTable tab;
+    __shared__ uint8_t sc[2][128][68];
+    float g = 0.0f;
+    Divisor d6{};
+    if (!PER_ROW) {
+        g = uniform_f(global_scale(amax[0]));   // uniform values kept in scalar registers
+        d6 = make_divisor_uniform(6.0f * g);
+        d6.d = uniform_f(d6.d);
+        d6.y = uniform_f(d6.y);
+        if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
+        fill_rtable<RHT>(tab, g);
+    }
+    const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63u;
+    uint32_t buf = 0;
+    for (uint32_t item = blockIdx.x; item < items; item += gridDim.x, buf ^= 1u) {
+        const RowTileItem it = row_tile_item(item, items_per_band);
+        const uint32_t blk = it.blk0 + lane;
+        auto row_of = [&](uint32_t j) { return it.row0 + 8 * j + wave; };
+        auto valid = [&](uint32_t j) { return blk < nb && row_of(j) < rows; };
+        uint4 a = {}, b = {};
+        if (valid(0)) {
+            const size_t n = (size_t)row_of(0) * nb + blk;
+            a = ld16(x + 2 * n);
+            b = ld16(x + 2 * n + 1);
+        }
+#pragma unroll 2
+        for (uint32_t j = 0; j < 16; ++j) {
+            uint4 a2 = a, b2 = b;
+            if (j + 1 < 16 && valid(j + 1)) {
+                const size_t nn = (size_t)row_of(j + 1) * nb + blk;
+                a2 = ld16(x + 2 * nn);
+                b2 = ld16(x + 2 * nn + 1);
+            }
+            if (valid(j)) {
+                const uint32_t row = row_of(j);
+                const size_t n = (size_t)row * nb + blk;
+                float w[16];
+                widen_row_block<RHT>(a, b, sign_mask, w);
+                Rand4 rnd{{0, 0, 0, 0}};
+                if (SR) rnd = block_rand_inv(rng, (uint32_t)n);
+                uint32_t lo, hi, sb;
+                if (PER_ROW) {
+                    const float gr = global_scale(amax[row]);
+                    if (blk == 0) gout[row] = gr;
+                    quantize_block<SR, RHT>(w, make_divisor(6.0f * gr), RowMul<RHT>{gr}, rnd, lo, hi, sb);
+                } else {
+                    quantize_block<SR, RHT>(w, d6, TableMul{tab}, rnd, lo, hi, sb);
+                }
+                st_nt(codes + n, make_uint2(lo, hi));
+                sc[buf][8 * j + wave][lane] = (uint8_t)sb;
+            }
+            a = a2;
+            b = b2;
+        }
+        __syncthreads();
+        row_write_scales_tiled(it, rows, nb, scales, [&](uint32_t r, uint32_t c) { return sc[buf][r][c]; });
+    }
+}
+
+// ------------------------------------------------------------------------------------------------------------
 // Column-wise kernels (quantize, amax, 16x16).  A workgroup covers 16 row-blocks (256 rows) by a strip of 512
 // columns; each of its 16 waves takes one row-block (16 rows) of the strip, and lane l owns columns 8l..8l+7, so one
 // load instruction reads 1 KiB of a row.  A lane keeps its 16 rows x 8 columns in registers (word p of row k holds
@@ -1887,11 +2002,15 @@ k_amax_colwise(const uint16_t* __restrict__ x, uint32_t cols, ColGrid cg, uint32
 // ------------------------------------------------------------------------------------------------------------
 constexpr uint32_t kRowFusedPerLane = 8;
 
-template <int MODE>
+// TILED: the workgroup takes item blockIdx.x of the tiled-scale mapping (128 rows x 64 blocks, 8 blocks per lane:
+// block l of row 16 j + w for lane l of wave w) and writes its scales as 16 whole tiles at the end; otherwise lane t
+// takes blocks blockIdx.x * bpl * 1024 + 1024 j + t.  rows, nb and items_per_band are used only when TILED.
+template <int MODE, bool TILED>
 __global__ void __launch_bounds__(kColThreads)
 k_amax_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, uint32_t bpl, uint32_t sign_mask,
                      RngArgs rng, float* __restrict__ amax_out, uint2* __restrict__ codes,
-                     uint8_t* __restrict__ scales, float* __restrict__ gout, uint64_t wait_ticks, uint32_t region) {
+                     uint8_t* __restrict__ scales, float* __restrict__ gout, uint64_t wait_ticks, uint32_t region,
+                     uint32_t rows, uint32_t nb, uint32_t items_per_band) {
     constexpr bool SR = MODE != kRN;
     constexpr bool RHT = MODE == kRHTSR;
     __shared__ ColStash st;
@@ -1899,14 +2018,22 @@ k_amax_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, uint32_
     __shared__ uint32_t red[kColRB];
     const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63u;
     const uint32_t base = blockIdx.x * bpl * kColThreads + threadIdx.x;
+    const RowTileItem it = TILED ? row_tile_item(blockIdx.x, items_per_band) : RowTileItem{0, 0};
+    // block index of the lane's j-th block, and whether it exists
+    auto index = [&](uint32_t j) -> uint32_t {
+        return TILED ? (it.row0 + 16 * j + wave) * nb + it.blk0 + lane : base + j * kColThreads;
+    };
+    auto valid = [&](uint32_t j) -> bool {
+        return TILED ? (it.blk0 + lane < nb && it.row0 + 16 * j + wave < rows) : (j < bpl && index(j) < total_blocks);
+    };
     uint4 a[kRowFusedPerLane], b[kRowFusedPerLane];
     float bm[kRowFusedPerLane];
     uint32_t mbits = 0;
 #pragma unroll
     for (uint32_t j = 0; j < kRowFusedPerLane; ++j) {
-        const uint32_t n = base + j * kColThreads;
+        const uint32_t n = index(j);
         a[j] = b[j] = make_uint4(0, 0, 0, 0);
-        if (j < bpl && n < total_blocks) {
+        if (valid(j)) {
             a[j] = ld16(x + 2 * (size_t)n);
             b[j] = ld16(x + 2 * (size_t)n + 1);
         }
@@ -1915,8 +2042,8 @@ k_amax_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, uint32_
     if (SR) {
 #pragma unroll
         for (uint32_t j = 0; j < kRowFusedPerLane; ++j) {
-            const uint32_t n = base + j * kColThreads;
-            if (j < bpl && n < total_blocks) {
+            const uint32_t n = index(j);
+            if (valid(j)) {
                 const Rand4 r = block_rand_inv(rng, n);
                 st.e[wave][j * 64 + lane] = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
             }
@@ -1957,8 +2084,8 @@ k_amax_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, uint32_
     }
 #pragma unroll
     for (uint32_t j = 0; j < kRowFusedPerLane; ++j) {
-        const uint32_t n = base + j * kColThreads;
-        if (j < bpl && n < total_blocks) {
+        const uint32_t n = index(j);
+        if (valid(j)) {
             Rand4 inv{{0, 0, 0, 0}};
             if (SR) {
                 const uint4 r = st.e[wave][j * 64 + lane];
@@ -1969,8 +2096,16 @@ k_amax_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, uint32_
             uint32_t lo, hi, sb;
             quantize_block_m<SR, RHT>(w, bm[j], d6, TableMul{tab}, inv, lo, hi, sb);
             st_nt(codes + n, make_uint2(lo, hi));
-            st_nt(scales + n, (uint8_t)sb);
+            if (TILED) st.e[wave][j * 64 + lane].z = sb;   // the slot's random words are used up
+            else st_nt(scales + n, (uint8_t)sb);
         }
+    }
+    if (TILED) {
+        __syncthreads();
+        // row r of the item is slice r / 16 of wave r % 16
+        row_write_scales_tiled(it, rows, nb, scales, [&](uint32_t r, uint32_t c) {
+            return (uint8_t)st.e[r & 15u][(r >> 4) * 64 + c].z;
+        });
     }
     release_slot(region);
 }
@@ -2149,7 +2284,22 @@ hipError_t launch_quant_1x16(const uint16_t* x, int64_t rows, int64_t cols, bool
     const RngArgs ra = rng_args(rng);
     const int64_t rv = colwise ? cols : rows;
     if (rows == 0 || cols == 0) return write_empty_g(amax, g, per_row ? (uint32_t)rv : 1u, stream);
-    if (!colwise) {
+    if (!colwise && tiled) {
+        const uint32_t nb = (uint32_t)(cols / 16), ipb = (nb + 63) / 64;
+        const uint32_t items = (uint32_t)((rows + 127) / 128) * ipb;
+        const uint32_t grid = std::min<uint32_t>(items, 3u * (uint32_t)cu_count());
+        const uint4* xv = reinterpret_cast<const uint4*>(x);
+        uint2* cv = reinterpret_cast<uint2*>(codes);
+#define NVFP4_ROWT(M, P)                                                                                        \
+    k_quant_rowwise_tiled<M, P><<<grid, kThreadsRT, 0, stream>>>(xv, (uint32_t)rows, nb, ipb, items, amax, sign_mask, \
+                                                                ra, cv, scales, g)
+        switch (mode) {
+            case kRN: if (per_row) NVFP4_ROWT(kRN, true); else NVFP4_ROWT(kRN, false); break;
+            case kSR: if (per_row) NVFP4_ROWT(kSR, true); else NVFP4_ROWT(kSR, false); break;
+            case kRHTSR: if (per_row) NVFP4_ROWT(kRHTSR, true); else NVFP4_ROWT(kRHTSR, false); break;
+        }
+#undef NVFP4_ROWT
+    } else if (!colwise) {
         const uint32_t bpr = (uint32_t)(cols / 16);
         const uint32_t total = (uint32_t)(rows * bpr);
         const FastDiv fd = make_fastdiv(bpr);
@@ -2215,7 +2365,25 @@ hipError_t launch_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, bool
             return hipLaunchKernel(fn, dim3(grid), dim3(kColThreads), args, 0, stream);
         }
     }
-    if (rows > 0 && cols > 0 && !colwise) {
+    if (rows > 0 && cols > 0 && !colwise && tiled) {
+        // one tiled-scale item (128 rows x 64 blocks) per workgroup, all resident
+        const uint32_t nb = (uint32_t)(cols / 16), ipb = (nb + 63) / 64;
+        const uint64_t items = (uint64_t)((rows + 127) / 128) * ipb;
+        if (items <= (uint64_t)cu_count() && items <= kFusedMaxGrid) {
+            const uint4* xv = reinterpret_cast<const uint4*>(x);
+            uint2* cv = reinterpret_cast<uint2*>(codes);
+            RngArgs ra = rng_args(rng);
+            uint64_t wait = fused_wait_ticks();
+            uint32_t region = next_slot_region();
+            uint32_t t = (uint32_t)(rows * nb), bp = kRowFusedPerLane, r = (uint32_t)rows, nbv = nb, ip = ipb;
+            void* args[] = {(void*)&xv, &t, &bp, &sign_mask, &ra, (void*)&amax, (void*)&cv, (void*)&scales,
+                            (void*)&g, &wait, &region, &r, &nbv, &ip};
+            const void* fn = mode == kRN ? (const void*)k_amax_quant_rowwise<kRN, true>
+                             : mode == kSR ? (const void*)k_amax_quant_rowwise<kSR, true>
+                                           : (const void*)k_amax_quant_rowwise<kRHTSR, true>;
+            return hipLaunchKernel(fn, dim3((uint32_t)items), dim3(kColThreads), args, 0, stream);
+        }
+    } else if (rows > 0 && cols > 0 && !colwise) {
         const uint32_t total = (uint32_t)(rows * (cols / 16));
         const uint32_t cus = (uint32_t)cu_count();
         const uint32_t bpl = (uint32_t)(((uint64_t)total + (uint64_t)cus * kColThreads - 1) / ((uint64_t)cus * kColThreads));
@@ -2228,12 +2396,12 @@ hipError_t launch_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, bool
                 RngArgs ra = rng_args(rng);
                 uint64_t wait = fused_wait_ticks();
                 uint32_t region = next_slot_region();
-                uint32_t t = total, bp = bpl;
+                uint32_t t = total, bp = bpl, unused = 0;
                 void* args[] = {(void*)&xv, &t, &bp, &sign_mask, &ra, (void*)&amax, (void*)&cv, (void*)&scales,
-                                (void*)&g, &wait, &region};
-                const void* fn = mode == kRN ? (const void*)k_amax_quant_rowwise<kRN>
-                                 : mode == kSR ? (const void*)k_amax_quant_rowwise<kSR>
-                                               : (const void*)k_amax_quant_rowwise<kRHTSR>;
+                                (void*)&g, &wait, &region, &unused, &unused, &unused};
+                const void* fn = mode == kRN ? (const void*)k_amax_quant_rowwise<kRN, false>
+                                 : mode == kSR ? (const void*)k_amax_quant_rowwise<kSR, false>
+                                               : (const void*)k_amax_quant_rowwise<kRHTSR, false>;
                 return hipLaunchKernel(fn, dim3(grid), dim3(kColThreads), args, 0, stream);
             }
         }

@@ -206,12 +206,8 @@ def test_swizzle_validation(lib):
 
 
 def test_tiled_scale_layout_validation(lib):
-    """The tiled scale layout is taken by the column-wise 1x16 calls only (checked before anything is enqueued)."""
+    """The tiled scale layout is taken by the 1x16 calls only (checked before anything is enqueued)."""
     T = 1
-    assert lib.nvfp4_quantize_rn(P, 16, 16, 0, 1, 0, P, out(layout=T), None, None) == UNSUP   # row-wise
-    assert lib.nvfp4_quantize_sr(P, 16, 16, 1, 0, P, 0, 0, out(layout=T), None) == UNSUP
-    assert lib.nvfp4_quantize_rht_sr(P, 16, 16, 1, 0, P, 0, 0, 0, out(layout=T), None) == UNSUP
-    assert lib.nvfp4_amax_quantize(P, 16, 16, 1, 0, 0, 0, 0, P, out(layout=T), None) == UNSUP
     assert lib.nvfp4_quantize_rn(P, 16, 16, 1, 3, 0, P, out(), out(layout=T), None) == UNSUP  # 16x16
     assert lib.nvfp4_quantize_4o6(P, 16, 16, 0, P, out(layout=T), None) == UNSUP
     assert lib.nvfp4_quantize_4o6_16x16(P, 16, 16, P, out(layout=T), None) == UNSUP
