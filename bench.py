@@ -417,7 +417,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the quantizer has no "
-              "multi-GPU path in this build).", file=sys.stderr)
+              "multi-GPU path: each GPU would quantize its own shard after a 4-byte MAX all-reduce of the amax).",
+              file=sys.stderr)
         sys.exit(2)
     import nvfp4_quantization_amd as Q
     from nvfp4_quantization_amd import workloads as W
