@@ -90,6 +90,10 @@ def _declare(L: C.CDLL) -> None:
     L.nvo_f32_to_bf16.restype = u16
     L.nvo_dequantize_fused.argtypes = [p, p, p, i64, i64, i32, i32, u16, i32, p]
     L.nvo_dequantize_fused.restype = i32
+    L.nvo_quantize_4o6_f32.argtypes = [p, i64, i64, i32, p, i64, i64, p, p, p, p]
+    L.nvo_quantize_4o6_f32.restype = i32
+    L.nvo_amax_f32.argtypes = [p, i64, i64, i32, p]
+    L.nvo_amax_f32.restype = i32
     L.nvo_swizzle_scales.argtypes = [p, i64, i64, p]
     L.nvo_swizzle_scales.restype = i32
 
@@ -330,3 +334,26 @@ def swizzle_scales(scales: np.ndarray) -> np.ndarray:
     out = np.empty(swizzled_size(rv, nb), dtype=np.uint8)
     _check(lib().nvo_swizzle_scales(_ptr(scales), rv, nb, _ptr(out)), "swizzle_scales")
     return out
+
+
+def amax_f32(x: np.ndarray, gmode: int = G_PER_TENSOR) -> np.ndarray:
+    """Row-wise amax of a float32 array (no transform): [1] or [rows]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, cols = x.shape
+    out = np.zeros(rows if gmode == G_PER_ROW else 1, dtype=np.float32)
+    _check(lib().nvo_amax_f32(_ptr(x), rows, cols, gmode, _ptr(out)), "amax_f32")
+    return out
+
+
+def quantize_4o6_f32(x: np.ndarray, amax_arr: np.ndarray, gmode: int = G_PER_ROW):
+    """Four-over-six of a float32 array; returns (codes, scales, g, choice) as quantize_4o6."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, cols = x.shape
+    amax_arr = np.ascontiguousarray(amax_arr, dtype=np.float32)
+    codes = np.zeros((rows, cols // 2), dtype=np.uint8)
+    scales = np.zeros((rows, cols // 16), dtype=np.uint8)
+    g = np.zeros(rows if gmode == G_PER_ROW else 1, dtype=np.float32)
+    choice = np.zeros((rows, cols // 16), dtype=np.uint8)
+    _check(lib().nvo_quantize_4o6_f32(_ptr(x), rows, cols, gmode, _ptr(amax_arr), 0, rows, _ptr(codes), _ptr(scales),
+                                      _ptr(g), _ptr(choice)), "quantize_4o6_f32")
+    return codes, scales, g, choice

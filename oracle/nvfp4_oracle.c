@@ -473,9 +473,50 @@ static float tree_sum16(const float e[16]) {
     return p[0];
 }
 
+/* The input element (r, c): a bf16 pattern widened exactly, or a binary32 value as given.  [P3]: the reference
+ * quantizer takes bf16 or fp32 inputs and its sweep covers both dtypes; every later step is the same. */
+static float input_at(const uint16_t* xb, const float* xf, int64_t cols, int64_t r, int64_t c) {
+    return xb ? nvo_bf16_to_f32(xb[r * cols + c]) : xf[r * cols + c];
+}
+
+static int quantize_4o6_rows(const uint16_t* xb, const float* xf, int64_t rows, int64_t cols, int gmode,
+                             const float* amax, int64_t r_begin, int64_t r_end, uint8_t* codes, uint8_t* scales,
+                             float* g, uint8_t* choice);
+
 int nvo_quantize_4o6(const uint16_t* x, int64_t rows, int64_t cols, int gmode, const float* amax, int64_t r_begin,
                      int64_t r_end, uint8_t* codes, uint8_t* scales, float* g, uint8_t* choice) {
-    if (!x || !amax || !codes || !scales || !g) return NVO_ERR_NULL;
+    if (!x) return NVO_ERR_NULL;
+    return quantize_4o6_rows(x, NULL, rows, cols, gmode, amax, r_begin, r_end, codes, scales, g, choice);
+}
+
+/* Four-over-six of a binary32 input: nvo_quantize_4o6 on the values as given. */
+int nvo_quantize_4o6_f32(const float* x, int64_t rows, int64_t cols, int gmode, const float* amax, int64_t r_begin,
+                         int64_t r_end, uint8_t* codes, uint8_t* scales, float* g, uint8_t* choice) {
+    if (!x) return NVO_ERR_NULL;
+    return quantize_4o6_rows(NULL, x, rows, cols, gmode, amax, r_begin, r_end, codes, scales, g, choice);
+}
+
+/* Row-wise amax of a binary32 input (no transform), per tensor or per row: the largest magnitude as an integer
+ * maximum of the magnitude bits, so NaN > inf > every finite value, as nvo_amax does for bf16. */
+int nvo_amax_f32(const float* x, int64_t rows, int64_t cols, int gmode, float* amax) {
+    if (!x || !amax) return NVO_ERR_NULL;
+    if (rows < 0 || cols < 0 || cols % 16) return NVO_ERR_SHAPE;
+    uint32_t total = 0;
+    for (int64_t r = 0; r < rows; ++r) {
+        uint32_t row_max = 0;
+        for (int64_t c = 0; c < cols; ++c)
+            if (absbits(x[r * cols + c]) > row_max) row_max = absbits(x[r * cols + c]);
+        if (gmode == NVO_G_PER_ROW) amax[r] = f32_of(row_max);
+        if (row_max > total) total = row_max;
+    }
+    if (gmode != NVO_G_PER_ROW) amax[0] = f32_of(total);
+    return NVO_OK;
+}
+
+static int quantize_4o6_rows(const uint16_t* xb, const float* xf, int64_t rows, int64_t cols, int gmode,
+                             const float* amax, int64_t r_begin, int64_t r_end, uint8_t* codes, uint8_t* scales,
+                             float* g, uint8_t* choice) {
+    if (!amax || !codes || !scales || !g) return NVO_ERR_NULL;
     if (rows < 0 || cols < 0 || cols % 16) return NVO_ERR_SHAPE;
     if (gmode != NVO_G_PER_TENSOR && gmode != NVO_G_PER_ROW) return NVO_ERR_UNSUPPORTED;
     if (r_begin < 0 || r_end > rows || r_begin > r_end) return NVO_ERR_SHAPE;
@@ -487,7 +528,7 @@ int nvo_quantize_4o6(const uint16_t* x, int64_t rows, int64_t cols, int gmode, c
         if (gmode == NVO_G_PER_ROW) g[r] = gr;
         for (int64_t b = 0; b < nb; ++b) {
             float xv[16];
-            for (int i = 0; i < 16; ++i) xv[i] = nvo_bf16_to_f32(x[r * cols + 16 * b + i]);
+            for (int i = 0; i < 16; ++i) xv[i] = input_at(xb, xf, cols, r, 16 * b + i);
             float bamax = max_of_block(xv, 16);
             uint8_t cand_code[2][16], cand_sb[2];
             float err[2];
