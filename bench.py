@@ -294,7 +294,16 @@ def config_figures(Q, W, dev, launches: int) -> dict:
     out["four_over_six_16384x8192_no_nan_inf"] = {
         "quantize_kernel_us": round(1e3 * tc, 2), "quantize_kernel_gbs": gbs(b46, tc),
         "quantize_kernel_frac_of_hbm_peak": round(gbs(b46, tc) / HBM_PEAK_GBS, 4)}
-    del xs, xc, amc
+    # the same no-NaN/Inf input widened to float32, through the binary32-input four-over-six (2 buffers)
+    b46f = 4 * r * c + r * c // 2 + r * c // 16 + 4 * r
+    xf = [(t.to(torch.int32) << 16).view(torch.float32) for t in xc[:2]]
+    amf = [Q.nvfp4_amax_f32(t, Q.G_PER_ROW) for t in xf]
+    tf = timed(lambda k: Q.nvfp4_quantize_4o6_f32(xf[k % 2], amf[k % 2], Q.G_PER_ROW, out=outs[k % n]))
+    out["four_over_six_f32_16384x8192"] = {
+        "call": "nvfp4_quantize_4o6_f32, per-row g", "quantize_kernel_us": round(1e3 * tf, 2),
+        "quantize_kernel_gbs": gbs(b46f, tf), "quantize_kernel_frac_of_hbm_peak": round(gbs(b46f, tf) / HBM_PEAK_GBS, 4),
+        "bytes_per_call": b46f}
+    del xs, xc, amc, xf, amf
     y = torch.empty((r, c), dtype=torch.float32, device=dev)
     bdq = r * c // 2 + r * c // 16 + 4 * r + 4 * r * c
     tdq = timed(lambda k: Q.nvfp4_dequantize(outs[k % n].codes, outs[k % n].scales, outs[k % n].g, Q.G_PER_ROW, y=y))

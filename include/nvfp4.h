@@ -164,6 +164,16 @@ nvfp4_status nvfp4_amax_quantize(const uint16_t* x, int64_t rows, int64_t cols, 
 nvfp4_status nvfp4_quantize_4o6(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_gmode gmode,
                                 const float* amax, const nvfp4_out* out, void* stream);
 
+/* Four-over-six of a binary32 tensor ([P3]: the reference quantizer takes bf16 or fp32 inputs, and its sweep covers
+ * both): nvfp4_quantize_4o6 with x [rows, cols] binary32 (16-byte aligned) in place of bf16; every step is the same,
+ * on the binary32 values as given.  amax: [1] or [rows] from nvfp4_amax_f32. */
+nvfp4_status nvfp4_quantize_4o6_f32(const float* x, int64_t rows, int64_t cols, nvfp4_gmode gmode,
+                                    const float* amax, const nvfp4_out* out, void* stream);
+
+/* Row-wise amax of a binary32 tensor (no transform): the NaN-dominant maximum magnitude per tensor (amax[0]) or per
+ * row (amax[rows]), for nvfp4_quantize_4o6_f32.  x [rows, cols] binary32, 16-byte aligned; cols % 16 == 0. */
+nvfp4_status nvfp4_amax_f32(const float* x, int64_t rows, int64_t cols, nvfp4_gmode gmode, float* amax, void* stream);
+
 /* Four-over-six with 16x16 tiles ([P3]: the reference quantizer takes 1x16 or 16x16 blocks).  One E4M3 scale per
  * 16x16 tile of X from the tile's maximum; both candidates (T = 6, 4) are formed as in nvfp4_quantize_4o6 with the
  * tile maximum; the tile's squared error is the sum of its rows, each row by the width-16 tree ((i, i+8), then

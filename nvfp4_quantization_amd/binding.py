@@ -35,6 +35,8 @@ SIGNATURES = {
     "nvfp4_amax_quantize": (_I, [_P, _I64, _I64, _I, _I, _U16, _U64, _U64, _P, _P, _P]),
     "nvfp4_quantize_4o6": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
     "nvfp4_quantize_4o6_16x16": (_I, [_P, _I64, _I64, _P, _P, _P]),
+    "nvfp4_quantize_4o6_f32": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
+    "nvfp4_amax_f32": (_I, [_P, _I64, _I64, _I, _P, _P]),
     "nvfp4_dequantize": (_I, [_P, _P, _P, _I64, _I64, _I, _P, _P]),
     "nvfp4_dequantize_fused": (_I, [_P, _P, _P, _I64, _I64, _I, _I, _U16, _I, _P, _P]),
     "nvfp4_swizzle_scales": (_I, [_P, _I64, _I64, _P, _P]),
@@ -198,6 +200,33 @@ def nvfp4_quantize_4o6(x: torch.Tensor, amax: torch.Tensor, gmode: int = G_PER_R
         out = alloc_out(rows, cols, gmode, x.device)
     _check(lib().nvfp4_quantize_4o6(_bf16(x), rows, cols, gmode, _dev(amax, "amax"), _out(out),
                                     _stream(x.device, stream)), "nvfp4_quantize_4o6")
+    return out
+
+
+def _f32(x: torch.Tensor) -> int:
+    if x.dtype != torch.float32 or x.dim() != 2:
+        raise TypeError("x must be a 2-D float32 tensor")
+    return _dev(x, "x")
+
+
+def nvfp4_amax_f32(x: torch.Tensor, gmode: int = G_PER_TENSOR, amax: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    rows, cols = x.shape
+    if amax is None:
+        amax = torch.empty((rows if gmode == G_PER_ROW else 1,), dtype=torch.float32, device=x.device)
+    _check(lib().nvfp4_amax_f32(_f32(x), rows, cols, gmode, _dev(amax, "amax"), _stream(x.device, stream)),
+           "nvfp4_amax_f32")
+    return amax
+
+
+def nvfp4_quantize_4o6_f32(x: torch.Tensor, amax: torch.Tensor, gmode: int = G_PER_ROW,
+                           out: Optional[Quantized] = None, stream=None) -> Quantized:
+    """Four-over-six of a float32 tensor (row-wise 1x16)."""
+    rows, cols = x.shape
+    if out is None:
+        out = alloc_out(rows, cols, gmode, x.device)
+    _check(lib().nvfp4_quantize_4o6_f32(_f32(x), rows, cols, gmode, _dev(amax, "amax"), _out(out),
+                                        _stream(x.device, stream)), "nvfp4_quantize_4o6_f32")
     return out
 
 

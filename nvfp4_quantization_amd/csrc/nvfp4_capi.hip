@@ -198,6 +198,27 @@ nvfp4_status nvfp4_quantize_4o6_16x16(const uint16_t* x, int64_t rows, int64_t c
                                               static_cast<hipStream_t>(stream)));
 }
 
+nvfp4_status nvfp4_amax_f32(const float* x, int64_t rows, int64_t cols, nvfp4_gmode gmode, float* amax, void* stream) {
+    NVFP4_TRY(check_sizes(rows, cols));
+    NVFP4_TRY(check_gmode(gmode));
+    if (cols % 16) return NVFP4_ERR_SHAPE;
+    NVFP4_TRY(check_buf(x, rows * cols, 16));
+    NVFP4_TRY(check_buf(amax, gmode == NVFP4_G_PER_ROW ? rows : 1, 4));
+    return done(nvfp4::launch_amax_f32(x, rows, cols, gmode == NVFP4_G_PER_ROW, amax, static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_quantize_4o6_f32(const float* x, int64_t rows, int64_t cols, nvfp4_gmode gmode,
+                                    const float* amax, const nvfp4_out* out, void* stream) {
+    NVFP4_TRY(check_sizes(rows, cols));
+    NVFP4_TRY(check_gmode(gmode));
+    if (cols % 16) return NVFP4_ERR_SHAPE;
+    NVFP4_TRY(check_buf(x, rows * cols, 16));
+    NVFP4_TRY(check_buf(amax, gmode == NVFP4_G_PER_ROW ? rows : 1, 4));
+    NVFP4_TRY(check_out(out, rows, cols, gmode));
+    return done(nvfp4::launch_quant_4o6(x, rows, cols, gmode == NVFP4_G_PER_ROW, amax, out->codes, out->scales,
+                                        out->g, static_cast<hipStream_t>(stream), true));
+}
+
 nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv, int64_t cv,
                               nvfp4_gmode gmode, float* y, void* stream) {
     NVFP4_TRY(check_sizes(rv, cv));

@@ -1451,6 +1451,37 @@ __device__ __forceinline__ void unpack8(uint32_t d, float (&v)[8]) {
     v[4] = p2.x; v[5] = p2.y; v[6] = p3.x; v[7] = p3.y;
 }
 
+// One row-wise block's input words: 16 bf16 (two 16-byte words) or 16 binary32 (four), loaded from x viewed as
+// 16-byte words, and widened to binary32 (exactly: a bf16 is the high half of its binary32).
+template <bool F32>
+struct BlockWords {
+    uint4 w[F32 ? 4 : 2];
+};
+
+template <bool F32>
+__device__ __forceinline__ BlockWords<F32> ld_block(const uint4* __restrict__ x, size_t n) {
+    constexpr int K = F32 ? 4 : 2;
+    BlockWords<F32> r;
+#pragma unroll
+    for (int k = 0; k < K; ++k) r.w[k] = ld16(x + K * n + k);
+    return r;
+}
+
+template <bool F32>
+__device__ __forceinline__ void widen_block(const BlockWords<F32>& r, float (&xv)[16]) {
+    if constexpr (F32) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            xv[4 * k] = as_f(r.w[k].x);
+            xv[4 * k + 1] = as_f(r.w[k].y);
+            xv[4 * k + 2] = as_f(r.w[k].z);
+            xv[4 * k + 3] = as_f(r.w[k].w);
+        }
+    } else {
+        widen_row_block<false>(r.w[0], r.w[1], 0u, xv);
+    }
+}
+
 // One block: both candidates, their decoded squared errors, and the choice.  xv are the 16 values, m their absmax,
 // dv the divisors 6 g and 4 g, tab the multipliers of g.  A NaN or infinite g (a row whose amax is NaN or infinite)
 // makes every multiplier NaN: both candidates give codes 0x7 and NaN errors (the map-to-6 one is kept), and its
@@ -1508,6 +1539,7 @@ __device__ __forceinline__ void quant_4o6_block(const float (&xv)[16], float m, 
 
 // Per-tensor g: grid-stride over blocks with the next block's loads in flight; the multipliers of the 128 scale
 // codes are tabulated once per workgroup.
+template <bool F32 = false>
 __device__ __forceinline__ void quant_4o6_tensor_wg(const uint4* __restrict__ x, uint32_t total_blocks,
                                                     const float* __restrict__ amax, uint2* __restrict__ codes,
                                                     uint8_t* __restrict__ scales, float* __restrict__ gout,
@@ -1519,48 +1551,42 @@ __device__ __forceinline__ void quant_4o6_tensor_wg(const uint4* __restrict__ x,
     const uint32_t stride = nwg * kThreads;
     uint32_t n = wg * kThreads + threadIdx.x;
     if (n >= total_blocks) return;
-    uint4 a = ld16(x + 2 * (size_t)n), b = ld16(x + 2 * (size_t)n + 1);
+    BlockWords<F32> a = ld_block<F32>(x, n);
     for (; n < total_blocks; n += stride) {
         const uint32_t nn = n + stride;
-        uint4 a2 = a, b2 = b;
-        if (nn < total_blocks) {
-            a2 = ld16(x + 2 * (size_t)nn);
-            b2 = ld16(x + 2 * (size_t)nn + 1);
-        }
+        BlockWords<F32> a2 = a;
+        if (nn < total_blocks) a2 = ld_block<F32>(x, nn);
         float xv[16];
-        widen_row_block<false>(a, b, 0u, xv);
+        widen_block<F32>(a, xv);
         uint32_t lo, hi, sb;
         quant_4o6_block(xv, absmax16(xv), g, dv, tab, lo, hi, sb);
         st_nt(codes + n, make_uint2(lo, hi));
         st_nt(scales + n, (uint8_t)sb);
         a = a2;
-        b = b2;
     }
 }
 
+template <bool F32>
 __global__ void __launch_bounds__(kThreads)
 k_quant_4o6_tensor(const uint4* __restrict__ x, uint32_t total_blocks, const float* __restrict__ amax,
                    uint2* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gout) {
     __shared__ RTable tab;
-    quant_4o6_tensor_wg(x, total_blocks, amax, codes, scales, gout, blockIdx.x, gridDim.x, tab);
+    quant_4o6_tensor_wg<F32>(x, total_blocks, amax, codes, scales, gout, blockIdx.x, gridDim.x, tab);
 }
 
 // Per-row g: a workgroup walks whole rows (grid-stride over rows), lane t taking blocks t, t + 256, ... of each, with
 // the next block's loads (in this row or the next) in flight.  g, its two divisors and the row's multiplier table
 // are computed once per row: the table is double-buffered, so one barrier per row orders it (a thread writes the
 // table of row i only after the barrier of row i - 1, which every thread passes only after its reads of row i - 2).
+template <bool F32 = false>
 __device__ __forceinline__ void quant_4o6_rows_wg(const uint4* __restrict__ x, uint32_t rows, uint32_t bpr,
                                                   const float* __restrict__ amax, uint2* __restrict__ codes,
                                                   uint8_t* __restrict__ scales, float* __restrict__ gout, uint32_t wg,
                                                   uint32_t nwg, RTable (&tabs)[2]) {
     const uint32_t t = threadIdx.x;
     uint32_t row = wg;
-    uint4 a = make_uint4(0, 0, 0, 0), b = a;
-    if (row < rows && t < bpr) {
-        const size_t n0 = (size_t)row * bpr + t;
-        a = ld16(x + 2 * n0);
-        b = ld16(x + 2 * n0 + 1);
-    }
+    BlockWords<F32> a{};
+    if (row < rows && t < bpr) a = ld_block<F32>(x, (size_t)row * bpr + t);
     for (uint32_t parity = 0; row < rows; row += nwg, parity ^= 1u) {
         const float g = global_scale(amax[row]);
         if (t == 0) gout[row] = g;
@@ -1580,30 +1606,26 @@ __device__ __forceinline__ void quant_4o6_rows_wg(const uint4* __restrict__ x, u
                 nrow = row + nwg;
                 nblk = t;
             }
-            uint4 a2 = a, b2 = b;
-            if (nrow < rows) {
-                const size_t nn = (size_t)nrow * bpr + nblk;
-                a2 = ld16(x + 2 * nn);
-                b2 = ld16(x + 2 * nn + 1);
-            }
+            BlockWords<F32> a2 = a;
+            if (nrow < rows) a2 = ld_block<F32>(x, (size_t)nrow * bpr + nblk);
             float xv[16];
-            widen_row_block<false>(a, b, 0u, xv);
+            widen_block<F32>(a, xv);
             uint32_t lo, hi, sb;
             quant_4o6_block(xv, absmax16(xv), g, dv, tab, lo, hi, sb);
             const size_t n = (size_t)row * bpr + blk;
             st_nt(codes + n, make_uint2(lo, hi));
             st_nt(scales + n, (uint8_t)sb);
             a = a2;
-            b = b2;
         }
     }
 }
 
+template <bool F32>
 __global__ void __launch_bounds__(kThreads)
 k_quant_4o6_rows(const uint4* __restrict__ x, uint32_t rows, uint32_t bpr, const float* __restrict__ amax,
                  uint2* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gout) {
     __shared__ RTable tabs[2];
-    quant_4o6_rows_wg(x, rows, bpr, amax, codes, scales, gout, blockIdx.x, gridDim.x, tabs);
+    quant_4o6_rows_wg<F32>(x, rows, bpr, amax, codes, scales, gout, blockIdx.x, gridDim.x, tabs);
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -1938,43 +1960,52 @@ __device__ __forceinline__ uint32_t rowblock_absmax(const uint4& a, const uint4&
     return as_u(RHT ? 0.25f * m : m) & 0x7FFFFFFFu;
 }
 
+// The same on a block's words (bf16 with the optional transform, or binary32 without).
+template <bool RHT, bool F32>
+__device__ __forceinline__ uint32_t rowblock_absmax(const BlockWords<F32>& r, uint32_t mask) {
+    if constexpr (F32) {
+        float w[16];
+        widen_block<true>(r, w);
+        return as_u(absmax16(w)) & 0x7FFFFFFFu;
+    } else {
+        return rowblock_absmax<RHT>(r.w[0], r.w[1], mask);
+    }
+}
+
 // Row-wise, per tensor: one 1024-thread workgroup per CU; a lane takes 8 blocks a round (base + 1024 j + t) with
 // all 16 loads issued before the first is used; one atomic max per workgroup into a zeroed amax[0].
 constexpr uint32_t kRowAmaxPerLane = 8;
 
-template <bool RHT>
+template <bool RHT, bool F32 = false>
 __device__ __forceinline__ void amax_rowwise_tensor_wg(const uint4* __restrict__ x, uint32_t total_blocks,
                                                        uint32_t sign_mask, uint32_t* amax_bits, uint32_t wg,
                                                        uint32_t nwg, uint32_t* red) {
     constexpr uint32_t kPer = kRowAmaxPerLane * kColThreads;   // blocks per workgroup round
     uint32_t m = 0;
     for (uint32_t base = wg * kPer + threadIdx.x; base < total_blocks; base += nwg * kPer) {
-        uint4 a[kRowAmaxPerLane], b[kRowAmaxPerLane];
+        BlockWords<F32> a[kRowAmaxPerLane];
 #pragma unroll
         for (uint32_t j = 0; j < kRowAmaxPerLane; ++j) {
             const uint32_t n = base + j * kColThreads;
-            a[j] = b[j] = make_uint4(0, 0, 0, 0);   // blocks past the end count as zeros
-            if (n < total_blocks) {
-                a[j] = ld16(x + 2 * (size_t)n);
-                b[j] = ld16(x + 2 * (size_t)n + 1);
-            }
+            a[j] = BlockWords<F32>{};   // blocks past the end count as zeros
+            if (n < total_blocks) a[j] = ld_block<F32>(x, n);
         }
 #pragma unroll
-        for (uint32_t j = 0; j < kRowAmaxPerLane; ++j) m = umax(m, rowblock_absmax<RHT>(a[j], b[j], sign_mask));
+        for (uint32_t j = 0; j < kRowAmaxPerLane; ++j) m = umax(m, rowblock_absmax<RHT, F32>(a[j], sign_mask));
     }
     m = block_max<kColRB>(m, red);
     if (threadIdx.x == 0) publish_max(amax_bits, m);
 }
 
-template <bool RHT>
+template <bool RHT, bool F32>
 __global__ void __launch_bounds__(kColThreads)
 k_amax_rowwise_tensor(const uint4* __restrict__ x, uint32_t total_blocks, uint32_t sign_mask, uint32_t* amax_bits) {
     __shared__ uint32_t red[kColRB];
-    amax_rowwise_tensor_wg<RHT>(x, total_blocks, sign_mask, amax_bits, blockIdx.x, gridDim.x, red);
+    amax_rowwise_tensor_wg<RHT, F32>(x, total_blocks, sign_mask, amax_bits, blockIdx.x, gridDim.x, red);
 }
 
 // Row-wise, per row: one workgroup per row (grid-stride over rows), direct store.
-template <bool RHT>
+template <bool RHT, bool F32 = false>
 __device__ __forceinline__ void amax_rowwise_rows_wg(const uint4* __restrict__ x, uint32_t rows,
                                                      uint32_t blocks_per_row, uint32_t sign_mask,
                                                      uint32_t* __restrict__ amax_bits, uint32_t wg, uint32_t nwg,
@@ -1983,19 +2014,19 @@ __device__ __forceinline__ void amax_rowwise_rows_wg(const uint4* __restrict__ x
         uint32_t m = 0;
         for (uint32_t b = threadIdx.x; b < blocks_per_row; b += kThreads) {
             const size_t n = (size_t)r * blocks_per_row + b;
-            m = umax(m, rowblock_absmax<RHT>(ld16(x + 2 * n), ld16(x + 2 * n + 1), sign_mask));
+            m = umax(m, rowblock_absmax<RHT, F32>(ld_block<F32>(x, n), sign_mask));
         }
         m = block_max(m, lds);
         if (threadIdx.x == 0) amax_bits[r] = m;
     }
 }
 
-template <bool RHT>
+template <bool RHT, bool F32>
 __global__ void __launch_bounds__(kThreads)
 k_amax_rowwise_rows(const uint4* __restrict__ x, uint32_t rows, uint32_t blocks_per_row, uint32_t sign_mask,
                     uint32_t* __restrict__ amax_bits) {
     __shared__ uint32_t lds[kWavesPerGroup];
-    amax_rowwise_rows_wg<RHT>(x, rows, blocks_per_row, sign_mask, amax_bits, blockIdx.x, gridDim.x, lds);
+    amax_rowwise_rows_wg<RHT, F32>(x, rows, blocks_per_row, sign_mask, amax_bits, blockIdx.x, gridDim.x, lds);
 }
 
 // Column-wise (V = X^T), same workgroup layout as k_amax_quant_colwise (one row-block per wave).  Per tensor: one
@@ -2293,6 +2324,37 @@ hipError_t write_empty_g(const float* amax, float* g, uint32_t n, hipStream_t st
 
 }  // namespace
 
+// Row-wise amax kernels (bf16, or binary32 without the transform), into zeroed bits (per tensor) or bits[rows].
+void launch_amax_rowwise(const void* x, int64_t rows, int64_t cols, bool per_row, bool use_rht, bool f32,
+                         uint32_t sign_mask, uint32_t* bits, hipStream_t stream) {
+    const uint32_t bpr = (uint32_t)(cols / 16);
+    const uint32_t total = (uint32_t)(rows * bpr);
+    const uint4* xv = reinterpret_cast<const uint4*>(x);
+    if (per_row) {
+        const uint32_t grid = (uint32_t)(rows < 65536 * 16 ? rows : 65536 * 16);
+        if (f32) k_amax_rowwise_rows<false, true><<<grid, kThreads, 0, stream>>>(xv, (uint32_t)rows, bpr, 0u, bits);
+        else if (use_rht)
+            k_amax_rowwise_rows<true, false><<<grid, kThreads, 0, stream>>>(xv, (uint32_t)rows, bpr, sign_mask, bits);
+        else k_amax_rowwise_rows<false, false><<<grid, kThreads, 0, stream>>>(xv, (uint32_t)rows, bpr, sign_mask, bits);
+    } else {
+        const uint32_t grid = grid_for(total, kColThreads * kRowAmaxPerLane, 1);
+        if (f32) k_amax_rowwise_tensor<false, true><<<grid, kColThreads, 0, stream>>>(xv, total, 0u, bits);
+        else if (use_rht) k_amax_rowwise_tensor<true, false><<<grid, kColThreads, 0, stream>>>(xv, total, sign_mask, bits);
+        else k_amax_rowwise_tensor<false, false><<<grid, kColThreads, 0, stream>>>(xv, total, sign_mask, bits);
+    }
+}
+
+hipError_t launch_amax_f32(const float* x, int64_t rows, int64_t cols, bool per_row, float* amax, hipStream_t stream) {
+    uint32_t* bits = reinterpret_cast<uint32_t*>(amax);
+    if (!per_row || rows == 0 || cols == 0) {
+        const uint32_t n = per_row ? (uint32_t)rows : 1u;
+        if (n) k_fill_zero<<<grid_for(n, kThreads, 1), kThreads, 0, stream>>>(bits, n);
+    }
+    if (rows == 0 || cols == 0) return hipGetLastError();
+    launch_amax_rowwise(x, rows, cols, per_row, false, true, 0u, bits, stream);
+    return hipGetLastError();
+}
+
 hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, bool colwise, bool per_row, bool use_rht,
                        uint32_t sign_mask, float* amax, hipStream_t stream) {
     uint32_t* bits = reinterpret_cast<uint32_t*>(amax);
@@ -2304,18 +2366,7 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, bool colwi
     }
     if (rows == 0 || cols == 0) return hipGetLastError();
     if (!colwise) {
-        const uint32_t bpr = (uint32_t)(cols / 16);
-        const uint32_t total = (uint32_t)(rows * bpr);
-        const uint4* xv = reinterpret_cast<const uint4*>(x);
-        if (per_row) {
-            const uint32_t grid = (uint32_t)(rows < 65536 * 16 ? rows : 65536 * 16);
-            if (use_rht) k_amax_rowwise_rows<true><<<grid, kThreads, 0, stream>>>(xv, (uint32_t)rows, bpr, sign_mask, bits);
-            else k_amax_rowwise_rows<false><<<grid, kThreads, 0, stream>>>(xv, (uint32_t)rows, bpr, sign_mask, bits);
-        } else {
-            const uint32_t grid = grid_for(total, kColThreads * kRowAmaxPerLane, 1);
-            if (use_rht) k_amax_rowwise_tensor<true><<<grid, kColThreads, 0, stream>>>(xv, total, sign_mask, bits);
-            else k_amax_rowwise_tensor<false><<<grid, kColThreads, 0, stream>>>(xv, total, sign_mask, bits);
-        }
+        launch_amax_rowwise(x, rows, cols, per_row, use_rht, false, sign_mask, bits, stream);
     } else {
         uint32_t grid;
         const ColGrid w = col_grid(rows, cols, grid);
@@ -2502,8 +2553,8 @@ hipError_t launch_quant_4o6_16x16(const uint16_t* x, int64_t rows, int64_t cols,
     return hipGetLastError();
 }
 
-hipError_t launch_quant_4o6(const uint16_t* x, int64_t rows, int64_t cols, bool per_row, const float* amax,
-                            uint8_t* codes, uint8_t* scales, float* g, hipStream_t stream) {
+hipError_t launch_quant_4o6(const void* x, int64_t rows, int64_t cols, bool per_row, const float* amax,
+                            uint8_t* codes, uint8_t* scales, float* g, hipStream_t stream, bool f32) {
     if (rows == 0 || cols == 0) return write_empty_g(amax, g, per_row ? (uint32_t)rows : 1u, stream);
     const uint32_t bpr = (uint32_t)(cols / 16);
     const uint32_t total = (uint32_t)(rows * bpr);
@@ -2511,9 +2562,12 @@ hipError_t launch_quant_4o6(const uint16_t* x, int64_t rows, int64_t cols, bool 
     uint2* cv = reinterpret_cast<uint2*>(codes);
     if (per_row) {
         const uint32_t grid = (uint32_t)std::min<int64_t>(rows, (int64_t)cu_count() * 8);
-        k_quant_4o6_rows<<<grid, kThreads, 0, stream>>>(xv, (uint32_t)rows, bpr, amax, cv, scales, g);
+        if (f32) k_quant_4o6_rows<true><<<grid, kThreads, 0, stream>>>(xv, (uint32_t)rows, bpr, amax, cv, scales, g);
+        else k_quant_4o6_rows<false><<<grid, kThreads, 0, stream>>>(xv, (uint32_t)rows, bpr, amax, cv, scales, g);
     } else {
-        k_quant_4o6_tensor<<<grid_for(total, kThreads, 8), kThreads, 0, stream>>>(xv, total, amax, cv, scales, g);
+        const uint32_t grid = grid_for(total, kThreads, 8);
+        if (f32) k_quant_4o6_tensor<true><<<grid, kThreads, 0, stream>>>(xv, total, amax, cv, scales, g);
+        else k_quant_4o6_tensor<false><<<grid, kThreads, 0, stream>>>(xv, total, amax, cv, scales, g);
     }
     return hipGetLastError();
 }

@@ -56,8 +56,11 @@ hipError_t launch_quant_4o6_16x16(const uint16_t* x, int64_t rows, int64_t cols,
                                   uint8_t* scales, float* g, hipStream_t stream);
 
 // Four-over-six, row-wise 1x16 RN.
-hipError_t launch_quant_4o6(const uint16_t* x, int64_t rows, int64_t cols, bool per_row, const float* amax,
-                            uint8_t* codes, uint8_t* scales, float* g, hipStream_t stream);
+hipError_t launch_quant_4o6(const void* x, int64_t rows, int64_t cols, bool per_row, const float* amax,
+                            uint8_t* codes, uint8_t* scales, float* g, hipStream_t stream, bool f32 = false);
+
+// Row-wise amax of a binary32 tensor (per tensor or per row), for the binary32 four-over-six input.
+hipError_t launch_amax_f32(const float* x, int64_t rows, int64_t cols, bool per_row, float* amax, hipStream_t stream);
 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv, int64_t cv,
                              bool per_row, float* y, hipStream_t stream);

@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
                                            "nvfp4_quantize_rht_sr", "nvfp4_amax_quantize", "nvfp4_quantize_4o6",
                                            "nvfp4_dequantize", "nvfp4_dequantize_fused", "nvfp4_amax_grouped",
                                            "nvfp4_quantize_grouped", "nvfp4_quantize_4o6_16x16", "nvfp4_swizzle_scales",
-                                           "nvfp4_swizzled_scales_size", "nvfp4_status_str"])
+                                           "nvfp4_swizzled_scales_size", "nvfp4_quantize_4o6_f32",
+                                           "nvfp4_amax_f32", "nvfp4_status_str"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -216,3 +217,18 @@ def test_tiled_scale_layout_validation(lib):
     it = (B._GroupItem * 1)()
     it[0] = B._GroupItem(P, 16, 16, P, B._Out(P, P, P, T), 0, 0, 0)
     assert lib.nvfp4_quantize_grouped(it, 1, 0, 0, None) == UNSUP
+
+
+def test_f32_input_validation(lib):
+    q, a = lib.nvfp4_quantize_4o6_f32, lib.nvfp4_amax_f32
+    assert q(P, 16, 24, 0, P, out(), None) == SHAPE          # cols % 16
+    assert q(P, -1, 16, 0, P, out(), None) == SHAPE
+    assert q(P, 16, 16, 5, P, out(), None) == UNSUP          # unknown g mode
+    assert q(None, 16, 16, 0, P, out(), None) == NULL
+    assert q(P, 16, 16, 0, None, out(), None) == NULL
+    assert q(MIS, 16, 16, 0, P, out(), None) == ALIGN
+    assert q(P, 16, 16, 0, P, out(layout=1), None) == UNSUP  # tiled scales: not for four-over-six
+    assert a(P, 16, 24, 0, P, None) == SHAPE
+    assert a(None, 16, 16, 0, P, None) == NULL
+    assert a(P, 16, 16, 1, None, None) == NULL
+    assert a(MIS, 16, 16, 0, P, None) == ALIGN
