@@ -23,7 +23,9 @@ def kernels():
 def test_every_kernel_is_listed():
     names = " ".join(r["name"] for r in kernels())
     for k in ("k_amax_quant_colwise", "k_amax_quant_rowwise", "k_quant_colwise", "k_quant_rowwise", "k_quant_16x16",
-              "k_quant_4o6_rows", "k_quant_4o6_tensor", "k_dequantize", "k_amax_colwise", "k_amax_rowwise_tensor"):
+              "k_quant_4o6_rows", "k_quant_4o6_tensor", "k_dequantize", "k_amax_colwise", "k_amax_rowwise_tensor",
+              "k_quant_4o6_16x16", "k_swizzle_scales", "k_quant_rowwise_tiled", "k_dequantize_fused",
+              "k_quant_grouped", "k_quant_4o6_grouped"):
         assert k in names, k
 
 
@@ -37,3 +39,17 @@ def test_tile_kernels_keep_four_waves_per_simd():
     for r in kernels():
         if any(k in r["name"] for k in ("k_amax_quant_colwise", "k_quant_colwise", "k_quant_16x16")):
             assert int(r["vgpr"]) <= 128 and int(r["occupancy"]) >= 4, r
+
+
+def test_looping_grids_fit_their_occupancy():
+    """Kernels whose launchers size a looping grid to a fixed number of resident workgroups per CU must keep that
+    occupancy: k_quant_4o6_16x16 two 1024-thread workgroups (8 waves per SIMD), k_quant_rowwise_tiled three
+    512-thread ones (6 waves per SIMD), the single-read row-wise kernel one 1024-thread workgroup (4)."""
+    need = {"k_quant_4o6_16x16": 8, "k_quant_rowwise_tiled": 6, "k_amax_quant_rowwise": 4}
+    seen = set()
+    for r in kernels():
+        for k, occ in need.items():
+            if k in r["name"]:
+                assert int(r["occupancy"]) >= occ, r
+                seen.add(k)
+    assert seen == set(need)
