@@ -92,6 +92,8 @@ def _declare(L: C.CDLL) -> None:
     L.nvo_dequantize_fused.restype = i32
     L.nvo_quantize_4o6_f32.argtypes = [p, i64, i64, i32, p, i64, i64, p, p, p, p]
     L.nvo_quantize_4o6_f32.restype = i32
+    L.nvo_quantize_4o6_16x16_f32.argtypes = [p, i64, i64, p, i64, i64, p, p, p, p, p, p, p]
+    L.nvo_quantize_4o6_16x16_f32.restype = i32
     L.nvo_amax_f32.argtypes = [p, i64, i64, i32, p]
     L.nvo_amax_f32.restype = i32
     L.nvo_swizzle_scales.argtypes = [p, i64, i64, p]
@@ -357,3 +359,21 @@ def quantize_4o6_f32(x: np.ndarray, amax_arr: np.ndarray, gmode: int = G_PER_ROW
     _check(lib().nvo_quantize_4o6_f32(_ptr(x), rows, cols, gmode, _ptr(amax_arr), 0, rows, _ptr(codes), _ptr(scales),
                                       _ptr(g), _ptr(choice)), "quantize_4o6_f32")
     return codes, scales, g, choice
+
+
+def quantize_4o6_16x16_f32(x: np.ndarray, amax_arr: np.ndarray):
+    """Four-over-six with 16x16 tiles of a float32 array; returns as quantize_4o6_16x16."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, cols = x.shape
+    amax_arr = np.ascontiguousarray(amax_arr, dtype=np.float32)
+    cw = np.zeros((rows, cols // 2), dtype=np.uint8)
+    sw = np.zeros((rows, cols // 16), dtype=np.uint8)
+    gw = np.zeros(1, dtype=np.float32)
+    ct = np.zeros((cols, rows // 2), dtype=np.uint8)
+    stt = np.zeros((cols, rows // 16), dtype=np.uint8)
+    gt = np.zeros(1, dtype=np.float32)
+    choice = np.zeros((rows // 16, cols // 16), dtype=np.uint8)
+    _check(lib().nvo_quantize_4o6_16x16_f32(_ptr(x), rows, cols, _ptr(amax_arr), 0, rows // 16, _ptr(cw), _ptr(sw),
+                                            _ptr(gw), _ptr(ct), _ptr(stt), _ptr(gt), _ptr(choice)),
+           "quantize_4o6_16x16_f32")
+    return (cw, sw, gw), (ct, stt, gt), choice

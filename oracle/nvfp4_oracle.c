@@ -568,10 +568,31 @@ static int quantize_4o6_rows(const uint16_t* xb, const float* xf, int64_t rows, 
  * W^T (packed along X's columns) orientation, with the tile's scale repeated in each orientation's 1x16 scale
  * layout, exactly as nvo_quantize_16x16.  choice[tile] (optional, [rows/16, cols/16]) receives 1 for map-to-4.
  * ---------------------------------------------------------------------------------------------------------- */
+static int quantize_4o6_tiles(const uint16_t* xb, const float* xf, int64_t rows, int64_t cols, const float* amax,
+                              int64_t tr_begin, int64_t tr_end, uint8_t* codes_w, uint8_t* scales_w, float* g_w,
+                              uint8_t* codes_wt, uint8_t* scales_wt, float* g_wt, uint8_t* choice);
+
 int nvo_quantize_4o6_16x16(const uint16_t* x, int64_t rows, int64_t cols, const float* amax, int64_t tr_begin,
                            int64_t tr_end, uint8_t* codes_w, uint8_t* scales_w, float* g_w, uint8_t* codes_wt,
                            uint8_t* scales_wt, float* g_wt, uint8_t* choice) {
-    if (!x || !amax) return NVO_ERR_NULL;
+    if (!x) return NVO_ERR_NULL;
+    return quantize_4o6_tiles(x, NULL, rows, cols, amax, tr_begin, tr_end, codes_w, scales_w, g_w, codes_wt,
+                              scales_wt, g_wt, choice);
+}
+
+/* The same for a binary32 input ([P3]: bf16 or fp32 inputs), on the values as given. */
+int nvo_quantize_4o6_16x16_f32(const float* x, int64_t rows, int64_t cols, const float* amax, int64_t tr_begin,
+                               int64_t tr_end, uint8_t* codes_w, uint8_t* scales_w, float* g_w, uint8_t* codes_wt,
+                               uint8_t* scales_wt, float* g_wt, uint8_t* choice) {
+    if (!x) return NVO_ERR_NULL;
+    return quantize_4o6_tiles(NULL, x, rows, cols, amax, tr_begin, tr_end, codes_w, scales_w, g_w, codes_wt,
+                              scales_wt, g_wt, choice);
+}
+
+static int quantize_4o6_tiles(const uint16_t* xb, const float* xf, int64_t rows, int64_t cols, const float* amax,
+                              int64_t tr_begin, int64_t tr_end, uint8_t* codes_w, uint8_t* scales_w, float* g_w,
+                              uint8_t* codes_wt, uint8_t* scales_wt, float* g_wt, uint8_t* choice) {
+    if (!amax) return NVO_ERR_NULL;
     if (rows < 0 || cols < 0 || rows % 16 || cols % 16) return NVO_ERR_SHAPE;
     int want_w = codes_w != NULL, want_wt = codes_wt != NULL;
     if ((want_w && (!scales_w || !g_w)) || (want_wt && (!scales_wt || !g_wt)) || (!want_w && !want_wt))
@@ -586,7 +607,7 @@ int nvo_quantize_4o6_16x16(const uint16_t* x, int64_t rows, int64_t cols, const 
         for (int64_t tj = 0; tj < ntc; ++tj) {
             float v[256];
             for (int i = 0; i < 16; ++i)
-                for (int j = 0; j < 16; ++j) v[16 * i + j] = nvo_bf16_to_f32(x[(16 * ti + i) * cols + 16 * tj + j]);
+                for (int j = 0; j < 16; ++j) v[16 * i + j] = input_at(xb, xf, cols, 16 * ti + i, 16 * tj + j);
             float tamax = max_of_block(v, 256);
             uint8_t cand_code[2][256], cand_sb[2];
             float err[2];

@@ -88,3 +88,27 @@ def test_block_on_map_to_4_grid_decodes_exactly(oracle):
     codes, scales, g, choice = oracle.quantize_4o6_f32(x, np.array([2688.0], np.float32), 0)
     assert choice[0, 0] == 1 and scales[0, 0] == oracle.e4m3_encode(1.5)
     np.testing.assert_array_equal(oracle.dequantize(codes, scales, g), x)
+
+
+def test_16x16_tiles_match_the_bf16_path_on_bf16_inputs(oracle):
+    xb = W.weight_outliers(64, 96, seed=8)
+    xb[3, 5] = 0x7FC0                                               # a NaN tile
+    xf = (xb.astype(np.uint32) << 16).view(np.float32)
+    a = oracle.amax(xb)
+    rb = oracle.quantize_4o6_16x16(xb, a)
+    rf = oracle.quantize_4o6_16x16_f32(xf, a)
+    for u, v in zip(rb[0] + rb[1] + (rb[2],), rf[0] + rf[1] + (rf[2],)):
+        assert np.array_equal(np.asarray(u).view(np.uint8), np.asarray(v).view(np.uint8))
+
+
+def test_16x16_tile_of_identical_rows_makes_the_1x16_choice(oracle):
+    """A tile of 16 copies of one full-mantissa row: 16 times the block's error, so the 1x16 choice and codes."""
+    rng = np.random.default_rng(21)
+    for trial in range(20):
+        row = (rng.standard_normal(16) * 2.0 ** rng.integers(-6, 6)).astype(np.float32)
+        x = np.tile(row, (16, 1))
+        a = np.array([2688.0], np.float32)
+        (cw, sw, _), _, choice = oracle.quantize_4o6_16x16_f32(x, a)
+        c1, s1, _, ch1 = oracle.quantize_4o6_f32(row[None, :], a, 0)
+        assert choice[0, 0] == ch1[0, 0] and sw[0, 0] == s1[0, 0]
+        assert all(np.array_equal(cw[i], c1[0]) for i in range(16))
