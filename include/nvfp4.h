@@ -184,6 +184,11 @@ nvfp4_status nvfp4_amax_f32(const float* x, int64_t rows, int64_t cols, nvfp4_gm
 nvfp4_status nvfp4_quantize_4o6_16x16(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
                                       const nvfp4_out* out, void* stream);
 
+/* nvfp4_quantize_4o6_16x16 for a binary32 tensor ([P3]: bf16 or fp32 inputs): x [rows, cols] binary32, 16-byte
+ * aligned; amax [1] from nvfp4_amax_f32 (per tensor).  Every step is the same, on the values as given. */
+nvfp4_status nvfp4_quantize_4o6_16x16_f32(const float* x, int64_t rows, int64_t cols, const float* amax,
+                                          const nvfp4_out* out, void* stream);
+
 /* Scale matrix to the tiled layout of the FP4 GEMM ([P2, approach]: the quantized operands reach the FP4 GEMM with
  * 1x16 block scales in the SWIZZLE_32_4_4 layout; [P2, results]: the swizzle is part of the per-call wrapper
  * overhead).  The scale matrix [rv, nb] (row-major, nb scales per row, as written by the quantize calls) is cut into

@@ -36,6 +36,7 @@ SIGNATURES = {
     "nvfp4_quantize_4o6": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
     "nvfp4_quantize_4o6_16x16": (_I, [_P, _I64, _I64, _P, _P, _P]),
     "nvfp4_quantize_4o6_f32": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
+    "nvfp4_quantize_4o6_16x16_f32": (_I, [_P, _I64, _I64, _P, _P, _P]),
     "nvfp4_amax_f32": (_I, [_P, _I64, _I64, _I, _P, _P]),
     "nvfp4_dequantize": (_I, [_P, _P, _P, _I64, _I64, _I, _P, _P]),
     "nvfp4_dequantize_fused": (_I, [_P, _P, _P, _I64, _I64, _I, _I, _U16, _I, _P, _P]),
@@ -227,6 +228,17 @@ def nvfp4_quantize_4o6_f32(x: torch.Tensor, amax: torch.Tensor, gmode: int = G_P
         out = alloc_out(rows, cols, gmode, x.device)
     _check(lib().nvfp4_quantize_4o6_f32(_f32(x), rows, cols, gmode, _dev(amax, "amax"), _out(out),
                                         _stream(x.device, stream)), "nvfp4_quantize_4o6_f32")
+    return out
+
+
+def nvfp4_quantize_4o6_16x16_f32(x: torch.Tensor, amax: torch.Tensor, out: Optional[Quantized] = None,
+                                 stream=None) -> Quantized:
+    """Four-over-six with 16x16 tiles of a float32 tensor (per-tensor g); codes packed along X's rows."""
+    rows, cols = x.shape
+    if out is None:
+        out = alloc_out(rows, cols, G_PER_TENSOR, x.device)
+    _check(lib().nvfp4_quantize_4o6_16x16_f32(_f32(x), rows, cols, _dev(amax, "amax"), _out(out),
+                                              _stream(x.device, stream)), "nvfp4_quantize_4o6_16x16_f32")
     return out
 
 

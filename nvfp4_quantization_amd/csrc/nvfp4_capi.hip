@@ -219,6 +219,17 @@ nvfp4_status nvfp4_quantize_4o6_f32(const float* x, int64_t rows, int64_t cols, 
                                         out->g, static_cast<hipStream_t>(stream), true));
 }
 
+nvfp4_status nvfp4_quantize_4o6_16x16_f32(const float* x, int64_t rows, int64_t cols, const float* amax,
+                                          const nvfp4_out* out, void* stream) {
+    NVFP4_TRY(check_sizes(rows, cols));
+    if (rows % 16 || cols % 16) return NVFP4_ERR_SHAPE;
+    NVFP4_TRY(check_buf(x, rows * cols, 16));
+    NVFP4_TRY(check_buf(amax, 1, 4));
+    NVFP4_TRY(check_out(out, rows, cols, NVFP4_G_PER_TENSOR));
+    return done(nvfp4::launch_quant_4o6_16x16(x, rows, cols, amax, out->codes, out->scales, out->g,
+                                              static_cast<hipStream_t>(stream), true));
+}
+
 nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv, int64_t cv,
                               nvfp4_gmode gmode, float* y, void* stream) {
     NVFP4_TRY(check_sizes(rv, cv));

@@ -1741,6 +1741,7 @@ __device__ __forceinline__ void quant_4o6_tile_row(const float (&xv)[16], float 
 
 // Items: (16-row band, group of 64 tile columns), band-major; each workgroup loops over items with the next item's
 // loads in flight, and fills the multiplier table once.
+template <bool F32>
 __global__ void __launch_bounds__(kThreads16) __attribute__((amdgpu_waves_per_eu(8, 8)))
 k_quant_4o6_16x16(const uint4* __restrict__ x, uint32_t ntc, uint32_t groups_per_rb, uint32_t items,
                   const float* __restrict__ amax, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
@@ -1751,18 +1752,14 @@ k_quant_4o6_16x16(const uint4* __restrict__ x, uint32_t ntc, uint32_t groups_per
     const uint32_t tw = wave * kTilesPerWave46 + (lane >> 4);   // tile of the item
     const uint32_t i = lane & 15u;                             // row within the tile
     // this lane's 16 elements of item w = block (16 rb + i) * ntc + tj of the row-wise view
-    auto load = [&](uint32_t w, uint4& a, uint4& b) {
+    auto load = [&](uint32_t w, BlockWords<F32>& a) {
         const uint32_t rb = w / groups_per_rb;
         const uint32_t tj = (w - rb * groups_per_rb) * kTilesPerGroup46 + tw;
-        if (tj < ntc) {   // whole 16-lane rows: every lane of a tile takes the same path
-            const size_t blk = (size_t)(16 * rb + i) * ntc + tj;
-            a = ld16(x + 2 * blk);
-            b = ld16(x + 2 * blk + 1);
-        }
+        if (tj < ntc) a = ld_block<F32>(x, (size_t)(16 * rb + i) * ntc + tj);   // whole 16-lane rows per tile
     };
     uint32_t w = blockIdx.x;
-    uint4 a = {}, b = {};
-    load(w, a, b);
+    BlockWords<F32> a{};
+    load(w, a);
     const float g = uniform_f(global_scale(amax[0]));   // uniform values kept in scalar registers
     if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
     const bool gfinite = __builtin_fabsf(g) < __builtin_inff();
@@ -1782,10 +1779,13 @@ k_quant_4o6_16x16(const uint4* __restrict__ x, uint32_t ntc, uint32_t groups_per
         const uint32_t t0 = (w - rb * groups_per_rb) * kTilesPerGroup46;   // first tile column of the item
         const bool active = t0 + tw < ntc;
         float xv[16];
-        widen_row_block<false>(a, b, 0u, xv);
-        if (w + gridDim.x < items) load(w + gridDim.x, a, b);   // in flight during this item's arithmetic
+        widen_block<F32>(a, xv);
+        // bf16: the next item's loads are in flight during this item's arithmetic; binary32 words would not fit in
+        // the registers beside it, so they go out after it (overlapping the write-out)
+        if (!F32 && w + gridDim.x < items) load(w + gridDim.x, a);
         uint32_t lo = 0, hi = 0, sb = 0;
         if (active) quant_4o6_tile_row(xv, g, gfinite, dv, tab, lo, hi, sb);
+        if (F32 && w + gridDim.x < items) load(w + gridDim.x, a);
         if (active) {
             st.codes[buf][tw][i] = make_uint2(lo, hi);
             st.scales[buf][tw][i] = (uint8_t)sb;
@@ -2540,16 +2540,18 @@ hipError_t launch_quant_16x16(const uint16_t* x, int64_t rows, int64_t cols, con
     return hipGetLastError();
 }
 
-hipError_t launch_quant_4o6_16x16(const uint16_t* x, int64_t rows, int64_t cols, const float* amax, uint8_t* codes,
-                                  uint8_t* scales, float* g, hipStream_t stream) {
+hipError_t launch_quant_4o6_16x16(const void* x, int64_t rows, int64_t cols, const float* amax, uint8_t* codes,
+                                  uint8_t* scales, float* g, hipStream_t stream, bool f32) {
     if (rows == 0 || cols == 0) return write_empty_g(amax, g, 1u, stream);
     const uint32_t ntc = (uint32_t)(cols / 16);
     const uint32_t groups_per_rb = (ntc + kTilesPerGroup46 - 1) / kTilesPerGroup46;
     const uint32_t items = (uint32_t)(rows / 16) * groups_per_rb;
     // two 1024-thread workgroups per CU (48 VGPRs), each looping over its share of the items
     const uint32_t grid = std::min<uint32_t>(items, 2u * (uint32_t)cu_count());
-    k_quant_4o6_16x16<<<grid, kThreads16, 0, stream>>>(reinterpret_cast<const uint4*>(x), ntc, groups_per_rb, items,
-                                                       amax, reinterpret_cast<uint2*>(codes), scales, g);
+    const uint4* xv = reinterpret_cast<const uint4*>(x);
+    uint2* cv = reinterpret_cast<uint2*>(codes);
+    if (f32) k_quant_4o6_16x16<true><<<grid, kThreads16, 0, stream>>>(xv, ntc, groups_per_rb, items, amax, cv, scales, g);
+    else k_quant_4o6_16x16<false><<<grid, kThreads16, 0, stream>>>(xv, ntc, groups_per_rb, items, amax, cv, scales, g);
     return hipGetLastError();
 }
 

@@ -52,8 +52,8 @@ hipError_t launch_quant_16x16(const uint16_t* x, int64_t rows, int64_t cols, con
                               hipStream_t stream);
 
 // Four-over-six with 16x16 tiles, per-tensor g, codes packed along X's rows (scales repeated per row).
-hipError_t launch_quant_4o6_16x16(const uint16_t* x, int64_t rows, int64_t cols, const float* amax, uint8_t* codes,
-                                  uint8_t* scales, float* g, hipStream_t stream);
+hipError_t launch_quant_4o6_16x16(const void* x, int64_t rows, int64_t cols, const float* amax, uint8_t* codes,
+                                  uint8_t* scales, float* g, hipStream_t stream, bool f32 = false);
 
 // Four-over-six, row-wise 1x16 RN.
 hipError_t launch_quant_4o6(const void* x, int64_t rows, int64_t cols, bool per_row, const float* amax,

@@ -37,7 +37,7 @@ def test_header_declares_the_boundary():
                                            "nvfp4_dequantize", "nvfp4_dequantize_fused", "nvfp4_amax_grouped",
                                            "nvfp4_quantize_grouped", "nvfp4_quantize_4o6_16x16", "nvfp4_swizzle_scales",
                                            "nvfp4_swizzled_scales_size", "nvfp4_quantize_4o6_f32",
-                                           "nvfp4_amax_f32", "nvfp4_status_str"])
+                                           "nvfp4_amax_f32", "nvfp4_quantize_4o6_16x16_f32", "nvfp4_status_str"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -228,6 +228,10 @@ def test_f32_input_validation(lib):
     assert q(P, 16, 16, 0, None, out(), None) == NULL
     assert q(MIS, 16, 16, 0, P, out(), None) == ALIGN
     assert q(P, 16, 16, 0, P, out(layout=1), None) == UNSUP  # tiled scales: not for four-over-six
+    t = lib.nvfp4_quantize_4o6_16x16_f32
+    assert t(P, 24, 16, P, out(), None) == SHAPE and t(P, 16, 24, P, out(), None) == SHAPE
+    assert t(None, 16, 16, P, out(), None) == NULL and t(MIS, 16, 16, P, out(), None) == ALIGN
+    assert t(P, 16, 16, P, out(layout=1), None) == UNSUP
     assert a(P, 16, 24, 0, P, None) == SHAPE
     assert a(None, 16, 16, 0, P, None) == NULL
     assert a(P, 16, 16, 1, None, None) == NULL

@@ -75,3 +75,37 @@ def test_4o6_f32_16384x8192():
     x = make(16384, 8192, seed=4)
     say("4o6 f32 full", x.shape)
     check(x, 1)
+
+
+def check_16x16(x, amax=None):
+    xd = torch.from_numpy(x).cuda()
+    a = Q.nvfp4_amax_f32(xd, 0) if amax is None else torch.from_numpy(amax).cuda()
+    out = Q.nvfp4_quantize_4o6_16x16_f32(xd, a)
+    torch.cuda.synchronize()
+    oa = O.amax_f32(x, 0) if amax is None else amax
+    (cw, sw, gw), _, _ = O.quantize_4o6_16x16_f32(x, oa)
+    bad = np.argwhere(out.codes.cpu().numpy() != cw)
+    assert bad.size == 0, f"codes: {len(bad)} mismatches, first {bad[:4].tolist()}"
+    assert np.array_equal(out.scales.cpu().numpy(), sw), "scales"
+    g = out.g.cpu().numpy()
+    assert g.view(np.uint32)[0] == gw.view(np.uint32)[0] or (np.isnan(g[0]) and np.isnan(gw[0]))
+
+
+@pytest.mark.parametrize("shape", [(16, 16), (48, 1040), (256, 4096), (80, 2064)])
+def test_4o6_16x16_f32(shape):
+    say("4o6 16x16 f32", shape)
+    check_16x16(make(*shape, seed=3 * shape[0] + shape[1], special=False))
+
+
+def test_4o6_16x16_f32_special_values():
+    say("4o6 16x16 f32 special values")
+    x = make(64, 96, seed=9, special=True)
+    for amax in (None, np.array([0.0], np.float32), np.array([np.inf], np.float32), np.array([3.5], np.float32)):
+        check_16x16(x, amax)
+
+
+@pytest.mark.slow
+def test_4o6_16x16_f32_14336x4096():
+    x = make(14336, 4096, seed=6)
+    say("4o6 16x16 f32 full", x.shape)
+    check_16x16(x)
