@@ -271,6 +271,16 @@ def config_figures(Q, W, dev, launches: int) -> dict:
         "call": "nvfp4_quantize_4o6_16x16", "quantize_kernel_us": round(1e3 * t46t, 2),
         "quantize_kernel_gbs": gbs(b46t, t46t), "quantize_kernel_frac_of_hbm_peak": round(gbs(b46t, t46t) / HBM_PEAK_GBS, 4),
         "bytes_per_call": b46t}
+    # the same weight widened to float32 (2 buffers)
+    b46f = 4 * r * c + r * c // 2 + r * c // 16 + 4
+    wf = [(t.to(torch.int32) << 16).view(torch.float32) for t in xs[:2]]
+    amw = [Q.nvfp4_amax_f32(t, Q.G_PER_TENSOR) for t in wf]
+    t46f = timed(lambda k: Q.nvfp4_quantize_4o6_16x16_f32(wf[k % 2], amw[k % 2], out=outs[k % n][0]))
+    out["four_over_six_16x16_f32_14336x4096"] = {
+        "call": "nvfp4_quantize_4o6_16x16_f32", "quantize_kernel_us": round(1e3 * t46f, 2),
+        "quantize_kernel_gbs": gbs(b46f, t46f), "quantize_kernel_frac_of_hbm_peak": round(gbs(b46f, t46f) / HBM_PEAK_GBS, 4),
+        "bytes_per_call": b46f}
+    del wf, amw
     del xs, outs, am
 
     # 16384 x 8192 four-over-six with per-row g (per-row amax given), and the decode of its output
