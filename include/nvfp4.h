@@ -20,13 +20,15 @@
  *     synchronises; every call is asynchronous on `stream` (a hipStream_t; NULL = the default stream).
  *     The global amax stays on the device: nothing is read back to the host ([P2, results: a host sync on the
  *     amax dominated quantization time]).
- *   - Inputs are bf16 bit patterns (uint16), row-major and contiguous, [rows, cols].
+ *   - Inputs are bf16 bit patterns (uint16), row-major and contiguous, [rows, cols]; the *_f32 calls take
+ *     binary32 instead.
  *   - "View" V: row-wise quantization works on V = X ([rows, cols]); column-wise on V = X^T ([cols, rows]),
  *     read directly from X without a transposed copy.  Blocks are 16 consecutive elements of a row of V.
  *   - Outputs of a quantization (struct nvfp4_out, all device pointers):
  *       codes  [Rv, Cv/2] uint8: byte k of a row holds element 2k in its low nibble and 2k+1 in its high nibble;
  *              a code is sign << 3 | m, m indexing the magnitude list above;
- *       scales [Rv, Cv/16] uint8: E4M3 ("fn": bias 7, max 448, 0x7F = NaN) block scales;
+ *       scales [Rv, Cv/16] uint8: E4M3 ("fn": bias 7, max 448, 0x7F = NaN) block scales, or the FP4 GEMM's
+ *              tiled layout when scale_layout is NVFP4_SCALES_TILED (see nvfp4_scale_layout);
  *       g      [1] (per tensor) or [Rv] (per row of V) float: the global scale amax / 2688 actually used.
  *   - Element scaling: with T = 6, s = bamax / fl(T g) (correctly rounded), sb = E4M3(s) (round to nearest even,
  *     saturating at 448, NaN -> 0x7F), S = fl(decode(sb) g), r = fl(1 / S) (r = 0 if S = 0, NaN if S is NaN,
