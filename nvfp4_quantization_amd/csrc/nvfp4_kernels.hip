@@ -1408,8 +1408,10 @@ k_quant_16x16(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColG
 #pragma unroll
             for (int k = 0; k < 16; ++k)
                 st_nt(cw_codes + (size_t)(16 * ti + k) * (cols >> 1) + (c8 >> 1), rowc[k]);
+            // cached byte stores: the 32-byte pieces of a W scale row that neighbouring workgroups write merge in L2
+            // (45.6 -> 43.6 us at 14336 x 4096 against non-temporal stores)
 #pragma unroll
-            for (int k = 0; k < 8; ++k) st_nt(sw + (size_t)(16 * ti + 8 * h + k) * ntc + tj, (uint8_t)sb);
+            for (int k = 0; k < 8; ++k) sw[(size_t)(16 * ti + 8 * h + k) * ntc + tj] = (uint8_t)sb;
         }
     }
     const uint32_t next = tile + gridDim.x;
