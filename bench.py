@@ -545,6 +545,8 @@ def measure(args, Q, W, dev, x_bits, x0, xs, outs, amaxes, masks, step, nbuf, st
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "input_dtype": "bf16",
+        "output_dtype": "e2m1 codes + e4m3 block scales + f32 global scale",
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "rows": ROWS, "cols": COLS, "orient": "colwise", "block": "1x16",
                    "rht": True, "rounding": "philox_sr", "gmode": "per_tensor",

@@ -206,9 +206,12 @@ nvfp4_status nvfp4_swizzle_scales(const uint8_t* scales, int64_t rv, int64_t nb,
 int64_t nvfp4_swizzled_scales_size(int64_t rv, int64_t nb);
 
 /* Standard NVFP4 decode ([P3]: the recipe-agnostic decode): y = fl(fl(val(code) * decode(sb)) * g) as binary32.
- *   codes [rv, cv/2], scales [rv, cv/16], g [1] or [rv] (gmode), y [rv, cv] float.  Shape: cv % 16 == 0. */
-nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv, int64_t cv,
-                              nvfp4_gmode gmode, float* y, void* stream);
+ *   in: a quantization's outputs (device pointers, as written by the quantize calls): in->codes [rv, cv/2],
+ *   in->scales [rv, cv/16] row-major (in->scale_layout NVFP4_SCALES_ROWMAJOR; the tiled layout returns
+ *   NVFP4_ERR_UNSUPPORTED), in->g [1] or [rv] (gmode).  y [rv, cv] float (device).  Shape: cv % 16 == 0.
+ *   Alignment as for the quantize calls' outputs (codes, scales 16 bytes, g 4) and y 16 bytes.  in is read on the
+ *   host during the call only. */
+nvfp4_status nvfp4_dequantize(const nvfp4_out* in, int64_t rv, int64_t cv, nvfp4_gmode gmode, float* y, void* stream);
 
 /* Grouped calls ([P3]: grouped variants of the quantizer are named there as future kernel work): up to
  * NVFP4_MAX_GROUP row-wise tensors of any shapes, one launch for all of them.  items is a HOST array of count
@@ -232,11 +235,10 @@ nvfp4_status nvfp4_quantize_grouped(const nvfp4_group_item* items, int32_t count
  * (a, b) -> (a + b, a - b) in binary32, one multiply by 0.25, and element i negated where bit i of sign_mask is set.
  * The binary32 result is written as float (out_bf16 = 0) or as bf16 bit patterns (out_bf16 != 0) rounded to nearest
  * even, overflowing to infinity, with every NaN written as 0x7FC0.
- *   codes [rv, cv/2], scales [rv, cv/16], g [1] or [rv] (gmode), y [rv, cv] float or uint16.
- *   Shape: cv % 16 == 0.  A column-wise quantization decodes to V = X^T.  Alignment: codes, scales, y 16 bytes. */
-nvfp4_status nvfp4_dequantize_fused(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv,
-                                    int64_t cv, nvfp4_gmode gmode, int use_rht, uint16_t sign_mask, int out_bf16,
-                                    void* y, void* stream);
+ *   in: as for nvfp4_dequantize (row-major scales).  y [rv, cv] float or uint16, 16-byte aligned.
+ *   Shape: cv % 16 == 0.  A column-wise quantization decodes to V = X^T. */
+nvfp4_status nvfp4_dequantize_fused(const nvfp4_out* in, int64_t rv, int64_t cv, nvfp4_gmode gmode, int use_rht,
+                                    uint16_t sign_mask, int out_bf16, void* y, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* nvfp4_status_str(nvfp4_status status);

@@ -1,9 +1,10 @@
 """Thin Python binding over the C ABI of ``include/nvfp4.h`` (ctypes).
 
-Argument marshalling only: tensors must already live on the GPU; this module checks dtypes and contiguity,
-allocates missing outputs with torch (device memory is torch's job), passes raw pointers and the current HIP
-stream, and turns a non-zero ``nvfp4_status`` into an exception.  Every step of the method runs in the HIP
-library; there is no CPU path.
+Argument marshalling only: tensors must already live on the GPU; this module checks the dtype, the number of
+elements and the contiguity of every tensor it hands to the library (a wrong-sized buffer would otherwise be read
+or written past its end by the kernels), allocates missing outputs with torch (device memory is torch's job),
+passes raw pointers and the current HIP stream, and turns a non-zero ``nvfp4_status`` into an exception.  Every
+step of the method runs in the HIP library; there is no CPU path.
 """
 from __future__ import annotations
 
@@ -38,8 +39,8 @@ SIGNATURES = {
     "nvfp4_quantize_4o6_f32": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
     "nvfp4_quantize_4o6_16x16_f32": (_I, [_P, _I64, _I64, _P, _P, _P]),
     "nvfp4_amax_f32": (_I, [_P, _I64, _I64, _I, _P, _P]),
-    "nvfp4_dequantize": (_I, [_P, _P, _P, _I64, _I64, _I, _P, _P]),
-    "nvfp4_dequantize_fused": (_I, [_P, _P, _P, _I64, _I64, _I, _I, _U16, _I, _P, _P]),
+    "nvfp4_dequantize": (_I, [_P, _I64, _I64, _I, _P, _P]),
+    "nvfp4_dequantize_fused": (_I, [_P, _I64, _I64, _I, _I, _U16, _I, _P, _P]),
     "nvfp4_swizzle_scales": (_I, [_P, _I64, _I64, _P, _P]),
     "nvfp4_swizzled_scales_size": (_I64, [_I64, _I64]),
     "nvfp4_amax_grouped": (_I, [_P, C.c_int32, _I, _I, _P]),
@@ -94,16 +95,31 @@ def _check(status: int, where: str) -> None:
         raise NVFP4Error(status, where)
 
 
-def _dev(t: torch.Tensor, what: str) -> int:
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise TypeError(f"{what} must be a GPU tensor")
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _dev(t: torch.Tensor, what: str, dtypes=None, numel: Optional[int] = None) -> int:
+    """Device pointer of t after checking it: a tensor of one of dtypes, with exactly numel elements (when given),
+    contiguous, on the GPU.  The checks that need no GPU come first."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch tensor")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{what} must have dtype {' or '.join(str(d) for d in dtypes)}, not {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{what} must hold {numel} elements, not {t.numel()} (shape {tuple(t.shape)})")
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
+    if not t.is_cuda:
+        raise TypeError(f"{what} must be a GPU tensor")
     return t.data_ptr()
 
 
+def _f32buf(t: torch.Tensor, what: str, n: int) -> int:
+    return _dev(t, what, (torch.float32,), n)
+
+
 def _bf16(x: torch.Tensor) -> int:
-    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or x.dim() != 2:
+    if not isinstance(x, torch.Tensor) or x.dtype not in _BF16 or x.dim() != 2:
         raise TypeError("x must be a 2-D bf16 tensor (or its int16 bit patterns)")
     return _dev(x, "x")
 
@@ -125,10 +141,20 @@ def alloc_out(rv: int, cv: int, gmode: int, device, scale_layout: int = SCALES_R
                      torch.empty((rv if gmode == G_PER_ROW else 1,), dtype=torch.float32, device=device), scale_layout)
 
 
-def _out(o: Optional[Quantized]):
+def _out(o: Optional[Quantized], rv: int, cv: int, gmode: int):
+    """The C struct of an output for the view [rv, cv], after checking every buffer's dtype and size."""
     if o is None:
         return None
-    return C.byref(_Out(_dev(o.codes, "codes"), _dev(o.scales, "scales"), _dev(o.g, "g"), o.scale_layout))
+    if o.scale_layout not in (SCALES_ROWMAJOR, SCALES_TILED):
+        raise ValueError(f"unknown scale layout {o.scale_layout}")
+    n_sc = rv * (cv // 16) if o.scale_layout == SCALES_ROWMAJOR else nvfp4_swizzled_scales_size(rv, cv // 16)
+    return C.byref(_Out(_dev(o.codes, "codes", (torch.uint8,), rv * (cv // 2)),
+                        _dev(o.scales, "scales", (torch.uint8,), n_sc),
+                        _f32buf(o.g, "g", rv if gmode == G_PER_ROW else 1), o.scale_layout))
+
+
+def _amax_n(rv: int, gmode: int) -> int:
+    return rv if gmode == G_PER_ROW else 1
 
 
 def nvfp4_amax(x: torch.Tensor, orient: int = ROWWISE, gmode: int = G_PER_TENSOR, use_rht: bool = False,
@@ -138,7 +164,7 @@ def nvfp4_amax(x: torch.Tensor, orient: int = ROWWISE, gmode: int = G_PER_TENSOR
     if amax is None:
         amax = torch.empty((rv if gmode == G_PER_ROW else 1,), dtype=torch.float32, device=x.device)
     _check(lib().nvfp4_amax(_bf16(x), rows, cols, orient, gmode, int(bool(use_rht)), sign_mask & 0xFFFF,
-                            _dev(amax, "amax"), _stream(x.device, stream)), "nvfp4_amax")
+                            _f32buf(amax, "amax", _amax_n(rv, gmode)), _stream(x.device, stream)), "nvfp4_amax")
     return amax
 
 
@@ -153,8 +179,10 @@ def nvfp4_quantize_rn(x: torch.Tensor, amax: torch.Tensor, block: int = BLOCK_1X
         row_out = alloc_out(rows, cols, gmode, x.device)
     if want_col and col_out is None:
         col_out = alloc_out(cols, rows, gmode, x.device)
-    _check(lib().nvfp4_quantize_rn(_bf16(x), rows, cols, block, orient, gmode, _dev(amax, "amax"),
-                                   _out(row_out if want_row else None), _out(col_out if want_col else None),
+    n_amax = _amax_n(rows if orient == ROWWISE else cols, gmode)
+    _check(lib().nvfp4_quantize_rn(_bf16(x), rows, cols, block, orient, gmode, _f32buf(amax, "amax", n_amax),
+                                   _out(row_out if want_row else None, rows, cols, gmode),
+                                   _out(col_out if want_col else None, cols, rows, gmode),
                                    _stream(x.device, stream)), "nvfp4_quantize_rn")
     return (row_out if want_row else None), (col_out if want_col else None)
 
@@ -162,10 +190,12 @@ def nvfp4_quantize_rn(x: torch.Tensor, amax: torch.Tensor, block: int = BLOCK_1X
 def nvfp4_quantize_sr(x: torch.Tensor, amax: torch.Tensor, seed: int, offset: int, orient: int = ROWWISE,
                       gmode: int = G_PER_TENSOR, out: Optional[Quantized] = None, stream=None) -> Quantized:
     rows, cols = x.shape
+    rv, cv = view_shape(rows, cols, orient)
     if out is None:
-        out = alloc_out(*view_shape(rows, cols, orient), gmode, x.device)
-    _check(lib().nvfp4_quantize_sr(_bf16(x), rows, cols, orient, gmode, _dev(amax, "amax"), seed, offset, _out(out),
-                                   _stream(x.device, stream)), "nvfp4_quantize_sr")
+        out = alloc_out(rv, cv, gmode, x.device)
+    _check(lib().nvfp4_quantize_sr(_bf16(x), rows, cols, orient, gmode, _f32buf(amax, "amax", _amax_n(rv, gmode)),
+                                   seed, offset, _out(out, rv, cv, gmode), _stream(x.device, stream)),
+           "nvfp4_quantize_sr")
     return out
 
 
@@ -173,10 +203,12 @@ def nvfp4_quantize_rht_sr(x: torch.Tensor, amax: torch.Tensor, sign_mask: int, s
                           orient: int = ROWWISE, gmode: int = G_PER_TENSOR, out: Optional[Quantized] = None,
                           stream=None) -> Quantized:
     rows, cols = x.shape
+    rv, cv = view_shape(rows, cols, orient)
     if out is None:
-        out = alloc_out(*view_shape(rows, cols, orient), gmode, x.device)
-    _check(lib().nvfp4_quantize_rht_sr(_bf16(x), rows, cols, orient, gmode, _dev(amax, "amax"), sign_mask & 0xFFFF,
-                                       seed, offset, _out(out), _stream(x.device, stream)), "nvfp4_quantize_rht_sr")
+        out = alloc_out(rv, cv, gmode, x.device)
+    _check(lib().nvfp4_quantize_rht_sr(_bf16(x), rows, cols, orient, gmode, _f32buf(amax, "amax", _amax_n(rv, gmode)),
+                                       sign_mask & 0xFFFF, seed, offset, _out(out, rv, cv, gmode),
+                                       _stream(x.device, stream)), "nvfp4_quantize_rht_sr")
     return out
 
 
@@ -185,12 +217,14 @@ def nvfp4_amax_quantize(x: torch.Tensor, orient: int, rounding: int, sign_mask: 
                         stream=None) -> tuple[torch.Tensor, Quantized]:
     """amax and 1x16 quantization with a per-tensor g in one call; returns (amax, out)."""
     rows, cols = x.shape
+    rv, cv = view_shape(rows, cols, orient)
     if amax is None:
         amax = torch.empty((1,), dtype=torch.float32, device=x.device)
     if out is None:
-        out = alloc_out(*view_shape(rows, cols, orient), G_PER_TENSOR, x.device)
+        out = alloc_out(rv, cv, G_PER_TENSOR, x.device)
     _check(lib().nvfp4_amax_quantize(_bf16(x), rows, cols, orient, rounding, sign_mask & 0xFFFF, seed, offset,
-                                     _dev(amax, "amax"), _out(out), _stream(x.device, stream)), "nvfp4_amax_quantize")
+                                     _f32buf(amax, "amax", 1), _out(out, rv, cv, G_PER_TENSOR),
+                                     _stream(x.device, stream)), "nvfp4_amax_quantize")
     return amax, out
 
 
@@ -199,13 +233,13 @@ def nvfp4_quantize_4o6(x: torch.Tensor, amax: torch.Tensor, gmode: int = G_PER_R
     rows, cols = x.shape
     if out is None:
         out = alloc_out(rows, cols, gmode, x.device)
-    _check(lib().nvfp4_quantize_4o6(_bf16(x), rows, cols, gmode, _dev(amax, "amax"), _out(out),
-                                    _stream(x.device, stream)), "nvfp4_quantize_4o6")
+    _check(lib().nvfp4_quantize_4o6(_bf16(x), rows, cols, gmode, _f32buf(amax, "amax", _amax_n(rows, gmode)),
+                                    _out(out, rows, cols, gmode), _stream(x.device, stream)), "nvfp4_quantize_4o6")
     return out
 
 
 def _f32(x: torch.Tensor) -> int:
-    if x.dtype != torch.float32 or x.dim() != 2:
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.float32 or x.dim() != 2:
         raise TypeError("x must be a 2-D float32 tensor")
     return _dev(x, "x")
 
@@ -215,8 +249,8 @@ def nvfp4_amax_f32(x: torch.Tensor, gmode: int = G_PER_TENSOR, amax: Optional[to
     rows, cols = x.shape
     if amax is None:
         amax = torch.empty((rows if gmode == G_PER_ROW else 1,), dtype=torch.float32, device=x.device)
-    _check(lib().nvfp4_amax_f32(_f32(x), rows, cols, gmode, _dev(amax, "amax"), _stream(x.device, stream)),
-           "nvfp4_amax_f32")
+    _check(lib().nvfp4_amax_f32(_f32(x), rows, cols, gmode, _f32buf(amax, "amax", _amax_n(rows, gmode)),
+                                _stream(x.device, stream)), "nvfp4_amax_f32")
     return amax
 
 
@@ -226,8 +260,9 @@ def nvfp4_quantize_4o6_f32(x: torch.Tensor, amax: torch.Tensor, gmode: int = G_P
     rows, cols = x.shape
     if out is None:
         out = alloc_out(rows, cols, gmode, x.device)
-    _check(lib().nvfp4_quantize_4o6_f32(_f32(x), rows, cols, gmode, _dev(amax, "amax"), _out(out),
-                                        _stream(x.device, stream)), "nvfp4_quantize_4o6_f32")
+    _check(lib().nvfp4_quantize_4o6_f32(_f32(x), rows, cols, gmode, _f32buf(amax, "amax", _amax_n(rows, gmode)),
+                                        _out(out, rows, cols, gmode), _stream(x.device, stream)),
+           "nvfp4_quantize_4o6_f32")
     return out
 
 
@@ -237,8 +272,9 @@ def nvfp4_quantize_4o6_16x16_f32(x: torch.Tensor, amax: torch.Tensor, out: Optio
     rows, cols = x.shape
     if out is None:
         out = alloc_out(rows, cols, G_PER_TENSOR, x.device)
-    _check(lib().nvfp4_quantize_4o6_16x16_f32(_f32(x), rows, cols, _dev(amax, "amax"), _out(out),
-                                              _stream(x.device, stream)), "nvfp4_quantize_4o6_16x16_f32")
+    _check(lib().nvfp4_quantize_4o6_16x16_f32(_f32(x), rows, cols, _f32buf(amax, "amax", 1),
+                                              _out(out, rows, cols, G_PER_TENSOR), _stream(x.device, stream)),
+           "nvfp4_quantize_4o6_16x16_f32")
     return out
 
 
@@ -248,8 +284,9 @@ def nvfp4_quantize_4o6_16x16(x: torch.Tensor, amax: torch.Tensor, out: Optional[
     rows, cols = x.shape
     if out is None:
         out = alloc_out(rows, cols, G_PER_TENSOR, x.device)
-    _check(lib().nvfp4_quantize_4o6_16x16(_bf16(x), rows, cols, _dev(amax, "amax"), _out(out),
-                                          _stream(x.device, stream)), "nvfp4_quantize_4o6_16x16")
+    _check(lib().nvfp4_quantize_4o6_16x16(_bf16(x), rows, cols, _f32buf(amax, "amax", 1),
+                                          _out(out, rows, cols, G_PER_TENSOR), _stream(x.device, stream)),
+           "nvfp4_quantize_4o6_16x16")
     return out
 
 
@@ -262,18 +299,28 @@ def nvfp4_swizzle_scales(scales: torch.Tensor, out: Optional[torch.Tensor] = Non
     rv, nb = scales.shape
     if out is None:
         out = torch.empty(nvfp4_swizzled_scales_size(rv, nb), dtype=torch.uint8, device=scales.device)
-    _check(lib().nvfp4_swizzle_scales(_dev(scales, "scales"), rv, nb, _dev(out, "out"),
+    _check(lib().nvfp4_swizzle_scales(_dev(scales, "scales", (torch.uint8,)), rv, nb,
+                                      _dev(out, "out", (torch.uint8,), nvfp4_swizzled_scales_size(rv, nb)),
                                       _stream(scales.device, stream)), "nvfp4_swizzle_scales")
     return out
 
 
+def _decode_in(codes: torch.Tensor, scales: torch.Tensor, g: torch.Tensor, gmode: int):
+    if not isinstance(codes, torch.Tensor) or codes.dim() != 2:
+        raise TypeError("codes must be a 2-D uint8 tensor [rv, cv/2]")
+    rv, half = codes.shape
+    cv = 2 * half
+    return rv, cv, _out(Quantized(codes, scales, g), rv, cv, gmode)
+
+
 def nvfp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, g: torch.Tensor, gmode: int = G_PER_TENSOR,
                      y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    rv, half = codes.shape
+    """Decode of a quantization's outputs (codes [rv, cv/2], row-major scales [rv, cv/16], g) to float32."""
+    rv, cv, src = _decode_in(codes, scales, g, gmode)
     if y is None:
-        y = torch.empty((rv, 2 * half), dtype=torch.float32, device=codes.device)
-    _check(lib().nvfp4_dequantize(_dev(codes, "codes"), _dev(scales, "scales"), _dev(g, "g"), rv, 2 * half, gmode,
-                                  _dev(y, "y"), _stream(codes.device, stream)), "nvfp4_dequantize")
+        y = torch.empty((rv, cv), dtype=torch.float32, device=codes.device)
+    _check(lib().nvfp4_dequantize(src, rv, cv, gmode, _dev(y, "y", (torch.float32,), rv * cv),
+                                  _stream(codes.device, stream)), "nvfp4_dequantize")
     return y
 
 
@@ -281,27 +328,27 @@ def nvfp4_dequantize_fused(codes: torch.Tensor, scales: torch.Tensor, g: torch.T
                            use_rht: bool = False, sign_mask: int = 0, out_bf16: bool = False,
                            y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Decode, optionally through the inverse RHT; y is float32, or bfloat16 with out_bf16."""
-    rv, half = codes.shape
+    rv, cv, src = _decode_in(codes, scales, g, gmode)
     dtype = torch.bfloat16 if out_bf16 else torch.float32
     if y is None:
-        y = torch.empty((rv, 2 * half), dtype=dtype, device=codes.device)
-    elif y.dtype not in ((torch.bfloat16, torch.int16, torch.uint16) if out_bf16 else (torch.float32,)):
-        raise TypeError("y must be bf16 (or its 16-bit patterns) with out_bf16, else float32")
-    _check(lib().nvfp4_dequantize_fused(_dev(codes, "codes"), _dev(scales, "scales"), _dev(g, "g"), rv, 2 * half,
-                                        gmode, int(bool(use_rht)), sign_mask & 0xFFFF, int(bool(out_bf16)),
-                                        _dev(y, "y"), _stream(codes.device, stream)), "nvfp4_dequantize_fused")
+        y = torch.empty((rv, cv), dtype=dtype, device=codes.device)
+    ydt = _BF16 if out_bf16 else (torch.float32,)
+    _check(lib().nvfp4_dequantize_fused(src, rv, cv, gmode, int(bool(use_rht)), sign_mask & 0xFFFF,
+                                        int(bool(out_bf16)), _dev(y, "y", ydt, rv * cv),
+                                        _stream(codes.device, stream)), "nvfp4_dequantize_fused")
     return y
 
 
-def _group(xs, amaxes, outs, sign_masks, seeds, offsets):
+def _group(xs, amaxes, outs, sign_masks, seeds, offsets, gmode):
     n = len(xs)
+    if n > MAX_GROUP:
+        raise ValueError(f"at most {MAX_GROUP} tensors per grouped call")
     arr = (_GroupItem * max(n, 1))()
     for i, x in enumerate(xs):
         rows, cols = x.shape
-        o = outs[i] if outs is not None else None
-        arr[i] = _GroupItem(_bf16(x), rows, cols, _dev(amaxes[i], "amax"),
-                            _Out(_dev(o.codes, "codes"), _dev(o.scales, "scales"), _dev(o.g, "g"), o.scale_layout)
-                            if o is not None else _Out(None, None, None, 0),
+        o = _out(outs[i], rows, cols, gmode) if outs is not None else None
+        arr[i] = _GroupItem(_bf16(x), rows, cols, _f32buf(amaxes[i], "amax", _amax_n(rows, gmode)),
+                            o._obj if o is not None else _Out(None, None, None, 0),
                             (sign_masks[i] if sign_masks is not None else 0) & 0xFFFF,
                             seeds[i] if seeds is not None else 0, offsets[i] if offsets is not None else 0)
     return arr
@@ -313,7 +360,7 @@ def nvfp4_amax_grouped(xs, gmode: int = G_PER_TENSOR, use_rht: bool = False, sig
     if amaxes is None:
         amaxes = [torch.empty((x.shape[0] if gmode == G_PER_ROW else 1,), dtype=torch.float32, device=x.device)
                   for x in xs]
-    arr = _group(xs, amaxes, None, sign_masks, None, None)
+    arr = _group(xs, amaxes, None, sign_masks, None, None, gmode)
     dev = xs[0].device if xs else torch.device("cuda")
     _check(lib().nvfp4_amax_grouped(arr, len(xs), gmode, int(bool(use_rht)), _stream(dev, stream)),
            "nvfp4_amax_grouped")
@@ -326,7 +373,7 @@ def nvfp4_quantize_grouped(xs, amaxes, rounding: int, gmode: int = G_PER_TENSOR,
     the list of Quantized outputs."""
     if outs is None:
         outs = [alloc_out(x.shape[0], x.shape[1], gmode, x.device) for x in xs]
-    arr = _group(xs, amaxes, outs, sign_masks, seeds, offsets)
+    arr = _group(xs, amaxes, outs, sign_masks, seeds, offsets, gmode)
     dev = xs[0].device if xs else torch.device("cuda")
     _check(lib().nvfp4_quantize_grouped(arr, len(xs), gmode, rounding, _stream(dev, stream)),
            "nvfp4_quantize_grouped")

@@ -230,16 +230,14 @@ nvfp4_status nvfp4_quantize_4o6_16x16_f32(const float* x, int64_t rows, int64_t 
                                               static_cast<hipStream_t>(stream), true));
 }
 
-nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv, int64_t cv,
-                              nvfp4_gmode gmode, float* y, void* stream) {
+nvfp4_status nvfp4_dequantize(const nvfp4_out* in, int64_t rv, int64_t cv, nvfp4_gmode gmode, float* y,
+                              void* stream) {
     NVFP4_TRY(check_sizes(rv, cv));
     NVFP4_TRY(check_gmode(gmode));
     if (cv % 16) return NVFP4_ERR_SHAPE;
-    NVFP4_TRY(check_buf(codes, rv * (cv / 2), 16));
-    NVFP4_TRY(check_buf(scales, rv * (cv / 16), 16));
-    NVFP4_TRY(check_buf(g, gmode == NVFP4_G_PER_ROW ? rv : 1, 4));
+    NVFP4_TRY(check_out(in, rv, cv, gmode));
     NVFP4_TRY(check_buf(y, rv * cv, 16));
-    return done(nvfp4::launch_dequantize(codes, scales, g, rv, cv, gmode == NVFP4_G_PER_ROW, y,
+    return done(nvfp4::launch_dequantize(in->codes, in->scales, in->g, rv, cv, gmode == NVFP4_G_PER_ROW, y,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -279,18 +277,16 @@ nvfp4_status nvfp4_quantize_grouped(const nvfp4_group_item* items, int32_t count
                                             static_cast<hipStream_t>(stream)));
 }
 
-nvfp4_status nvfp4_dequantize_fused(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rv,
-                                    int64_t cv, nvfp4_gmode gmode, int use_rht, uint16_t sign_mask, int out_bf16,
-                                    void* y, void* stream) {
+nvfp4_status nvfp4_dequantize_fused(const nvfp4_out* in, int64_t rv, int64_t cv, nvfp4_gmode gmode, int use_rht,
+                                    uint16_t sign_mask, int out_bf16, void* y, void* stream) {
     NVFP4_TRY(check_sizes(rv, cv));
     NVFP4_TRY(check_gmode(gmode));
     if (cv % 16) return NVFP4_ERR_SHAPE;
-    NVFP4_TRY(check_buf(codes, rv * (cv / 2), 16));
-    NVFP4_TRY(check_buf(scales, rv * (cv / 16), 16));
-    NVFP4_TRY(check_buf(g, gmode == NVFP4_G_PER_ROW ? rv : 1, 4));
+    NVFP4_TRY(check_out(in, rv, cv, gmode));
     NVFP4_TRY(check_buf(y, rv * cv, 16));
-    return done(nvfp4::launch_dequantize_fused(codes, scales, g, rv, cv, gmode == NVFP4_G_PER_ROW, use_rht != 0,
-                                               sign_mask, out_bf16 != 0, y, static_cast<hipStream_t>(stream)));
+    return done(nvfp4::launch_dequantize_fused(in->codes, in->scales, in->g, rv, cv, gmode == NVFP4_G_PER_ROW,
+                                               use_rht != 0, sign_mask, out_bf16 != 0, y,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 const char* nvfp4_status_str(nvfp4_status status) {

@@ -127,27 +127,30 @@ def test_4o6_and_dequantize_validation(lib):
     assert lib.nvfp4_quantize_4o6(P, 16, 16, 9, P, out(), None) == UNSUP
     assert lib.nvfp4_quantize_4o6(P, 16, 16, 1, P, out(scales=None), None) == NULL
     d = lib.nvfp4_dequantize
-    assert d(P, P, P, 4, 24, 0, P, None) == SHAPE
-    assert d(P, P, P, 4, 32, 0, P + 4, None) == ALIGN          # y must be 16-byte aligned
-    assert d(None, P, P, 4, 32, 0, P, None) == NULL
-    assert d(P, P, P, -4, 32, 0, P, None) == SHAPE
+    assert d(out(), 4, 24, 0, P, None) == SHAPE
+    assert d(out(), 4, 32, 0, P + 4, None) == ALIGN                # y must be 16-byte aligned
+    assert d(out(codes=None), 4, 32, 0, P, None) == NULL
+    assert d(None, 4, 32, 0, P, None) == NULL
+    assert d(out(), -4, 32, 0, P, None) == SHAPE
+    assert d(out(layout=1), 4, 32, 0, P, None) == UNSUP            # tiled scales are not decoded
 
 
 def test_dequantize_fused_validation(lib):
     d = lib.nvfp4_dequantize_fused
-    #        codes scales g  rv  cv  gmode rht mask bf16 y  stream
-    assert d(P, P, P, 4, 24, 0, 1, 0x1234, 1, P, None) == SHAPE           # cv % 16
-    assert d(P, P, P, -1, 32, 0, 1, 0x1234, 1, P, None) == SHAPE
-    assert d(P, P, P, 1 << 20, 1 << 20, 0, 1, 0, 1, P, None) == SHAPE      # 2^40 elements
-    assert d(P, P, P, 4, 32, 2, 1, 0, 1, P, None) == UNSUP                 # unknown g mode
-    assert d(None, P, P, 4, 32, 0, 1, 0, 1, P, None) == NULL
-    assert d(P, None, P, 4, 32, 0, 1, 0, 1, P, None) == NULL
-    assert d(P, P, None, 4, 32, 1, 1, 0, 1, P, None) == NULL
-    assert d(P, P, P, 4, 32, 0, 1, 0, 1, None, None) == NULL
-    assert d(MIS, P, P, 4, 32, 0, 1, 0, 1, P, None) == ALIGN
-    assert d(P, P, P + 2, 4, 32, 0, 1, 0, 1, P, None) == ALIGN
-    assert d(P, P, P, 4, 32, 0, 1, 0, 0, P + 8, None) == ALIGN             # y must be 16-byte aligned
-    assert d(None, None, P, 0, 32, 0, 1, 0, 1, None, None) == OK          # empty: nothing to decode
+    #        in     rv  cv  gmode rht mask bf16 y  stream
+    assert d(out(), 4, 24, 0, 1, 0x1234, 1, P, None) == SHAPE           # cv % 16
+    assert d(out(), -1, 32, 0, 1, 0x1234, 1, P, None) == SHAPE
+    assert d(out(), 1 << 20, 1 << 20, 0, 1, 0, 1, P, None) == SHAPE      # 2^40 elements
+    assert d(out(), 4, 32, 2, 1, 0, 1, P, None) == UNSUP                 # unknown g mode
+    assert d(None, 4, 32, 0, 1, 0, 1, P, None) == NULL
+    assert d(out(codes=None), 4, 32, 0, 1, 0, 1, P, None) == NULL
+    assert d(out(scales=None), 4, 32, 0, 1, 0, 1, P, None) == NULL
+    assert d(out(g=None), 4, 32, 1, 1, 0, 1, P, None) == NULL
+    assert d(out(), 4, 32, 0, 1, 0, 1, None, None) == NULL
+    assert d(out(codes=MIS), 4, 32, 0, 1, 0, 1, P, None) == ALIGN
+    assert d(out(g=P + 2), 4, 32, 0, 1, 0, 1, P, None) == ALIGN
+    assert d(out(), 4, 32, 0, 1, 0, 0, P + 8, None) == ALIGN             # y must be 16-byte aligned
+    assert d(out(codes=None, scales=None), 0, 32, 0, 1, 0, 1, None, None) == OK   # empty: nothing to decode
 
 
 def test_grouped_validation(lib):

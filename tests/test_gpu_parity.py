@@ -334,10 +334,40 @@ def test_full_weight_16x16_14336x4096():
 
 @pytest.mark.slow
 def test_full_four_over_six_16384x8192():
-    """Per-row g; compared on 1024 rows spread over the tensor (the GPU ran the full tensor)."""
+    """Per-row g with the injected NaN/+-inf: all 16384 rows compared (amax, codes, scales, g)."""
     x = W.make("four_over_six_16384x8192")
-    for lo in (0, 5000, 16384 - 512):
-        check_4o6(x, 1, rows_range=(lo, lo + 512))
+    check_4o6(x, 1)
+
+
+@pytest.mark.slow
+def test_full_four_over_six_16384x8192_without_specials():
+    """The same rows with no NaN/inf injected (every block's choice is then made by the error sums), all rows."""
+    check_4o6(W.heavy_tail_rows(16384, 8192, seed=4, inject=False), 1)
+
+
+def test_4o6_sum_order_block():
+    """A block (and two 16x16 tiles) whose map-to-4 / map-to-6 choice only the clamped shuffle-down error sum makes
+    (map-to-6); a left-to-right sum or a stride-1,2,4,8 tree keeps map-to-4 (tests/test_oracle_4o6_order.py).  Every
+    four-over-six entry point, bf16 and binary32, against the oracle."""
+    from test_oracle_4o6_order import bf16_bits, discriminating_block, tiles_for_16x16
+    blk = np.tile(discriminating_block(), (3, 4))          # 3 rows x 4 blocks of the same block
+    tiles = np.tile(tiles_for_16x16(), (2, 3))             # 2 x 6 tiles
+    amax = np.array([2688.0], np.float32)
+    a = torch.from_numpy(amax).cuda()
+    xb = bf16_bits(blk)
+    oc, os_, og, ch = O.quantize_4o6(xb, amax, 0)
+    assert not ch.any()
+    for out in (Q.nvfp4_quantize_4o6(dev(xb), a, 0),
+                Q.nvfp4_quantize_4o6_f32(torch.from_numpy(blk).cuda(), a, 0)):
+        same_u8(host(out.codes), oc, "4o6 codes")
+        same_u8(host(out.scales), os_, "4o6 scales")
+    tb = bf16_bits(tiles)
+    (cw, sw, _), _, ch = O.quantize_4o6_16x16(tb, amax)
+    assert not ch.any()
+    for out in (Q.nvfp4_quantize_4o6_16x16(dev(tb), a),
+                Q.nvfp4_quantize_4o6_16x16_f32(torch.from_numpy(tiles).cuda(), a)):
+        same_u8(host(out.codes), cw, "4o6 16x16 codes")
+        same_u8(host(out.scales), sw, "4o6 16x16 scales")
 
 
 # ------------------------------------------------------------------------------------------------ HIP graphs
