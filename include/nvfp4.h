@@ -146,12 +146,14 @@ nvfp4_status nvfp4_quantize_rht_sr(const uint16_t* x, int64_t rows, int64_t cols
  * nvfp4_quantize_rn / _sr / _rht_sr with the same arguments, and amax[0] is written too.
  *   A tensor that fits one workgroup per CU is read from memory once: column-wise up to one 256-row x
  *   512-column tile per CU, row-wise up to 8192 blocks per CU (8192 x 4096 either way on MI355X).  Each
- *   workgroup keeps its share in registers, publishes its maximum in a per-GPU slot array and waits for every
- *   other workgroup's; larger tensors run the two passes.  The slots reset themselves between launches, and
- *   launches take them from 8 regions in turn: up to 8 calls may be in flight at once on one GPU (on different
- *   streams); calls sharing a region must not overlap.  The wait is bounded (50 ms): a workgroup that is still
- *   waiting then reads the whole tensor to compute the amax itself, so the result never changes, only the time
- *   (this happens when other work, such as a concurrent call, holds CUs).
+ *   workgroup keeps its share in registers, publishes its maximum in a slot and waits for every other workgroup's;
+ *   larger tensors run the two passes.
+ *   The exchange slots are a 2 MiB array in the library's own device memory (one per GPU).  Each launch tags its slots with a fresh 32-bit epoch and takes one of the 8 regions in turn.  Calls that overlap
+ *   on one GPU (other streams, graph replays) may share a region: a workgroup never takes a slot that carries
+ *   another launch's epoch, so sharing costs time, never correctness.  The wait is bounded: after 100 us with some
+ *   workgroup of the launch not yet started (not all resident, e.g. CUs held by other work), or after 2 ms in any
+ *   case, a waiting workgroup reads the tiles whose maxima it has not seen from the tensor itself, so the result
+ *   never changes, only the time.
  *   rounding: NVFP4_ROUND_RN, _SR or _RHT_SR; sign_mask is used with RHT, seed and offset with SR.
  *   amax: [1] device float (output).  Shapes and outputs as for the quantize calls. */
 nvfp4_status nvfp4_amax_quantize(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_orient orient,

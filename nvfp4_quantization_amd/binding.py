@@ -98,15 +98,16 @@ def _check(status: int, where: str) -> None:
 _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
 
 
-def _dev(t: torch.Tensor, what: str, dtypes=None, numel: Optional[int] = None) -> int:
-    """Device pointer of t after checking it: a tensor of one of dtypes, with exactly numel elements (when given),
-    contiguous, on the GPU.  The checks that need no GPU come first."""
+def _dev(t: torch.Tensor, what: str, dtypes=None, numel: Optional[int] = None, at_least: bool = False) -> int:
+    """Device pointer of t after checking it: a tensor of one of dtypes, with exactly numel elements (at least numel
+    with at_least), contiguous, on the GPU.  The checks that need no GPU come first."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{what} must be a torch tensor")
     if dtypes is not None and t.dtype not in dtypes:
         raise TypeError(f"{what} must have dtype {' or '.join(str(d) for d in dtypes)}, not {t.dtype}")
-    if numel is not None and t.numel() != numel:
-        raise ValueError(f"{what} must hold {numel} elements, not {t.numel()} (shape {tuple(t.shape)})")
+    if numel is not None and (t.numel() < numel if at_least else t.numel() != numel):
+        raise ValueError(f"{what} must hold {'at least ' if at_least else ''}{numel} elements, not {t.numel()} "
+                         f"(shape {tuple(t.shape)})")
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
     if not t.is_cuda:
@@ -300,7 +301,7 @@ def nvfp4_swizzle_scales(scales: torch.Tensor, out: Optional[torch.Tensor] = Non
     if out is None:
         out = torch.empty(nvfp4_swizzled_scales_size(rv, nb), dtype=torch.uint8, device=scales.device)
     _check(lib().nvfp4_swizzle_scales(_dev(scales, "scales", (torch.uint8,)), rv, nb,
-                                      _dev(out, "out", (torch.uint8,), nvfp4_swizzled_scales_size(rv, nb)),
+                                      _dev(out, "out", (torch.uint8,), nvfp4_swizzled_scales_size(rv, nb), True),
                                       _stream(scales.device, stream)), "nvfp4_swizzle_scales")
     return out
 
@@ -341,8 +342,6 @@ def nvfp4_dequantize_fused(codes: torch.Tensor, scales: torch.Tensor, g: torch.T
 
 def _group(xs, amaxes, outs, sign_masks, seeds, offsets, gmode):
     n = len(xs)
-    if n > MAX_GROUP:
-        raise ValueError(f"at most {MAX_GROUP} tensors per grouped call")
     arr = (_GroupItem * max(n, 1))()
     for i, x in enumerate(xs):
         rows, cols = x.shape

@@ -1081,118 +1081,167 @@ k_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, Co
 // tile in registers, publishes its tile maximum in a slot of its own, waits until every workgroup has published,
 // reduces the slots to the tensor amax and quantizes the tile it still holds.  The tensor is read from HBM once
 // instead of twice.
-//   The wait needs every workgroup resident (one per CU, grid <= CUs).  It is bounded: a workgroup that has not
-// seen every slot filled within a bound (50 ms; other work holding CUs) computes the amax by reading the whole tensor
-// itself, so the result is the same in every case, only slower.  Slots are zero between launches: each workgroup
-// clears its own slot as its last action (every other workgroup has read it by then, or has given up waiting and
-// taken the slow route), so no counter has to be shared or reset.  Launches take their slots from one of
-// kSlotRegions regions in turn, so up to that many launches may be in flight at once on one GPU (on different
-// streams); more could share a region, and two launches sharing one must not overlap.
-//   Each slot is written to kSlotCopies copies and workgroup b polls copy b % kSlotCopies: with one copy, every
-// workgroup polls the same few cache lines while it waits for the last one, and those reads queue behind each other
-// (the exchange then took ~2.5 us against a one-way latency of ~0.6 us between XCDs).
+//   The exchange.  Every launch carries a nonzero 32-bit tag (its epoch, from a host counter) and uses slot region
+// epoch % kSlotRegions; workgroup b owns slot b of the region, written to kSlotCopies copies.  A slot holds 0 or
+// (epoch << 32) | v, where v = kArrived once the workgroup has started and v = its tile maximum (magnitude bits,
+// <= 0x7FFFFFFF) once that is known.  Readers take only values that carry their own epoch: a slot holding another
+// launch's value (a launch sharing the region, or a stale one) reads as absent, never as a maximum.
+//   The wait is bounded twice: once arrive_ticks have passed with some slot still absent (its workgroup has not
+// started, so not every workgroup is resident at once), or once wait_ticks have passed in any case, the workgroup
+// stops waiting and computes the maxima of the tiles it has not seen from the tensor itself (the slow route).  The
+// result is the same on every route; only the time changes.
+//   Each workgroup clears its slot as its last action with a compare-and-swap of its own value, so a slot taken over
+// by another launch keeps that launch's value, and launches that follow one another (replays of a captured graph
+// repeat their epoch) find the region clear.
+//   Workgroup b polls copy b % kSlotCopies: with one copy, every workgroup polls the same few cache lines while it
+// waits for the last one, and those reads queue behind each other (the exchange then took ~2.5 us against a one-way
+// latency of ~0.6 us between XCDs).
 // ------------------------------------------------------------------------------------------------------------
 constexpr uint32_t kFusedMaxGrid = 2048;
 constexpr uint32_t kSlotCopies = 16;
 constexpr uint32_t kSlotRegions = 8;
-constexpr uint64_t kWaitTicks = 5000000;        // 50 ms of the 100 MHz wall clock (the kernel's wait bound)
+constexpr uint32_t kSlotsPerRegion = kSlotCopies * kFusedMaxGrid;
+constexpr uint32_t kArrived = 0xFFFFFFFFu;     // low word of a slot whose workgroup has started
+// Wait bounds in ticks of the 100 MHz wall clock.  At 8192 x 4096 the last workgroup publishes ~16 us after the
+// launch and the exchange completes within ~2 us of that; a workgroup starts waiting only after its own loads, by
+// which time every co-resident workgroup has long started.
+constexpr uint64_t kWaitTicks = 200000;        // 2 ms: the whole wait
+constexpr uint64_t kArriveTicks = 10000;       // 100 us: the wait for workgroups that have not started
 
-// 0, or (1 << 32) | tile maximum (magnitude bits); copy c of slot b of region r at [r][c][b] (2 MiB per GPU)
-__device__ uint64_t g_fused_slot[kSlotRegions][kSlotCopies][kFusedMaxGrid];
+// The exchange slots of every single-read launch on a GPU (2 MiB): region r, copy c, slot b at
+// scratch[r * kSlotsPerRegion + c * kFusedMaxGrid + b].  Host code hands its device address (hipGetSymbolAddress,
+// once per device) to the kernels.
+static __device__ __align__(256) uint64_t scratch[kSlotRegions * kSlotsPerRegion];
 
-// Tensor amax of the column-wise view computed by one workgroup (the route taken after a timed-out wait); v is
-// used as scratch.  Valid in thread 0.
-template <bool RHT>
-__device__ uint32_t wg_amax_colwise(const uint16_t* x, uint32_t cols, const ColGrid& cg, uint32_t sign_mask,
-                                    uint4 (&v)[16], uint32_t* red) {
-    uint32_t m = 0;
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t units = cg.nrb * cg.nstrips;   // (row-block, strip) pairs
-    for (uint32_t u = wave; u < units; u += kColRB) {
-        ColPos p;
-        p.rb = u / cg.nstrips;
-        p.strip = u - p.rb * cg.nstrips;
-        p.group = p.rb / kColRB;
-        p.lane = threadIdx.x & 63u;
-        p.c8 = p.strip * 512 + 8 * p.lane;
-        if (p.c8 < cols) {
-            load_col_tile(x, cols, p, v);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {   // one block at a time: this runs with the caller's state live
-                float w[16];
-                widen_col_block<RHT>(v, j, sign_mask, w);
-                const float bmax = absmax16(w);
-                m = umax(m, as_u(RHT ? 0.25f * bmax : bmax) & 0x7FFFFFFFu);
-            }
-        }
-    }
-    return block_max<kColRB>(m, red);
+struct Exchange {
+    uint64_t* region;        // this launch's slot region: kSlotCopies copies of kFusedMaxGrid slots
+    uint32_t epoch;          // the launch's tag, nonzero
+    uint32_t pad;
+    uint64_t wait_ticks;     // bound of the whole wait
+    uint64_t arrive_ticks;   // bound of the wait while some workgroup has not started
+};
+
+__device__ __forceinline__ uint64_t* slot_copy(const Exchange& ex, uint32_t copy) {
+    return ex.region + (size_t)copy * kFusedMaxGrid;
+}
+
+// The first action of a single-read kernel: this workgroup's slot says it has started.
+__device__ __forceinline__ void announce(const Exchange& ex) {
+    if (threadIdx.x < kSlotCopies)
+        __hip_atomic_store(slot_copy(ex, threadIdx.x) + blockIdx.x, ((uint64_t)ex.epoch << 32) | kArrived,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The cross-workgroup step of the single-read kernels (1024-thread workgroups).  The workgroup maximum of mbits
-// (magnitude bits) goes to this workgroup's slot.  Wave 0 then reads the slots of every workgroup (lane l watches
-// slots l + 64 k, four loads in flight together: each read is a round trip to memory, since the slots are shared by
-// all XCDs; a slot once seen filled is not read again, since every workgroup polls the same 16 cache lines),
-// reduces them to the tensor amax and fills tab for g = amax / 2688, while the other waves wait at the one barrier
-// that follows.  Returns the amax bits, equal in every thread; slow (uniform) is set when some slot stayed empty
-// past wait_ticks, and then neither the return value nor tab is valid.  Uses red[16].
+// (magnitude bits) goes to this workgroup's slot (kept in s_own for release_slot).  Wave 0 then reads the slots of
+// every workgroup (lane l watches slots l + 64 k, four loads in flight together: each read is a round trip to
+// memory, since the slots are shared by all XCDs; a slot once seen with its maximum is not read again), reduces them
+// and, when none is missing, fills tab for g = amax / 2688, while the other waves wait at the one barrier that
+// follows.  Returns the maximum over the slots seen, equal in every thread; missing[l] (l < 64) gets bit k set for
+// each slot l + 64 k not seen, and nmissing (uniform) their count (then tab is not filled).  Uses red[16].
 template <bool RHT>
-__device__ uint32_t exchange_max(uint32_t mbits, uint64_t wait_ticks, uint32_t region, uint32_t* red, RTable& tab,
-                             bool& slow) {
-    __shared__ uint32_t s_max, s_out;
+__device__ uint32_t exchange_max(uint32_t mbits, const Exchange& ex, uint32_t* red, uint32_t* missing,
+                                 uint32_t* s_own, RTable& tab, uint32_t& nmissing) {
+    __shared__ uint32_t s_max, s_nmiss;
     const uint32_t lane = threadIdx.x & 63u;
     mbits = wave_max(mbits);
     if (lane == 0) red[threadIdx.x >> 6] = mbits;
     __syncthreads();
     if (threadIdx.x < 64) {
         uint32_t m = wave_max(lane < kColRB ? red[lane] : 0u);
+        if (lane == 0) *s_own = m;
         if (lane < kSlotCopies)
-            __hip_atomic_store(&g_fused_slot[region][lane][blockIdx.x], (1ull << 32) | m, __ATOMIC_RELAXED,
+            __hip_atomic_store(slot_copy(ex, lane) + blockIdx.x, ((uint64_t)ex.epoch << 32) | m, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-        const uint64_t* copy = g_fused_slot[region][blockIdx.x % kSlotCopies];
+        const uint64_t* copy = slot_copy(ex, blockIdx.x % kSlotCopies);
+        const uint32_t nk = (gridDim.x + 63) / 64;   // slots per lane, <= 32
+        uint32_t pending = 0, absent = 0;            // bit k: slot lane + 64 k not seen yet / last read foreign
+        for (uint32_t k = 0; k < nk; ++k)
+            if (lane + 64 * k < gridDim.x) pending |= 1u << k;
         m = 0;
-        bool waited_out = false;
         const uint64_t t0 = wall_clock64();
-        for (uint32_t base = lane; base < gridDim.x && !waited_out; base += 256) {
-            uint64_t sv[4];
+        while (true) {
+            for (uint32_t k0 = 0; k0 < nk; k0 += 4) {
+                uint64_t sv[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) sv[k] = base + 64 * k < gridDim.x ? 0ull : (1ull << 32);
-            while (true) {
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    if (sv[k] == 0)
-                        sv[k] = __hip_atomic_load(&copy[base + 64 * k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (sv[0] != 0 && sv[1] != 0 && sv[2] != 0 && sv[3] != 0) break;
-                if (wall_clock64() - t0 >= wait_ticks) {
-                    waited_out = true;
-                    break;
+                for (uint32_t kk = 0; kk < 4; ++kk) {
+                    const uint32_t k = k0 + kk;
+                    sv[kk] = (k < nk && ((pending >> k) & 1u))
+                                 ? __hip_atomic_load(&copy[lane + 64 * k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                 : 0ull;
                 }
-                __builtin_amdgcn_s_sleep(1);
-            }
 #pragma unroll
-            for (int k = 0; k < 4; ++k) m = umax(m, (uint32_t)sv[k]);
+                for (uint32_t kk = 0; kk < 4; ++kk) {
+                    const uint32_t k = k0 + kk;
+                    if (k < nk && ((pending >> k) & 1u)) {
+                        const bool ours = (uint32_t)(sv[kk] >> 32) == ex.epoch;
+                        const uint32_t v = (uint32_t)sv[kk];
+                        absent = ours ? absent & ~(1u << k) : absent | (1u << k);
+                        if (ours && v != kArrived) {
+                            m = umax(m, v);
+                            pending &= ~(1u << k);
+                        }
+                    }
+                }
+            }
+            if (__ballot(pending != 0) == 0) break;
+            const uint64_t dt = wall_clock64() - t0;
+            if (dt >= ex.wait_ticks || (dt >= ex.arrive_ticks && __ballot(absent != 0) != 0)) break;
+            __builtin_amdgcn_s_sleep(1);
         }
         m = wave_max(m);
-        const bool out = __ballot(waited_out) != 0;
-        const float g = global_scale(as_f(m));
+        missing[lane] = pending;
+        uint32_t cnt = __builtin_popcount(pending);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) cnt += (uint32_t)__shfl_xor((int)cnt, off);
+        if (cnt == 0) {
+            const float g = global_scale(as_f(m));
 #pragma unroll 1
-        for (uint32_t c = lane; c < 128; c += 64) fill_rtable_entry<RHT>(tab, c, g);
+            for (uint32_t c = lane; c < 128; c += 64) fill_rtable_entry<RHT>(tab, c, g);
+        }
         if (lane == 0) {
             s_max = m;
-            s_out = out;
+            s_nmiss = cnt;
         }
     }
     __syncthreads();
-    slow = s_out != 0;
+    nmissing = __builtin_amdgcn_readfirstlane(s_nmiss);
     return __builtin_amdgcn_readfirstlane(s_max);
 }
 
-// Clears this workgroup's slot: the last action of a single-read kernel (every other workgroup has read the slot by
-// then, or has given up waiting and taken the slow route).
-__device__ __forceinline__ void release_slot(uint32_t region) {
-    if (threadIdx.x < kSlotCopies)
-        __hip_atomic_store(&g_fused_slot[region][threadIdx.x][blockIdx.x], 0ull, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+// Whether slot s was missing in the exchange (missing as written by exchange_max).
+__device__ __forceinline__ bool slot_missing(const uint32_t* missing, uint32_t s) {
+    return (missing[s & 63u] >> (s >> 6)) & 1u;
+}
+
+// Clears this workgroup's slot if it still holds this launch's value: the last action of a single-read kernel
+// (every other workgroup of the launch has read the slot by then, or has stopped waiting and taken the slow route).
+__device__ __forceinline__ void release_slot(const Exchange& ex, uint32_t own) {
+    if (threadIdx.x < kSlotCopies) {
+        uint64_t expect = ((uint64_t)ex.epoch << 32) | own;
+        __hip_atomic_compare_exchange_strong(slot_copy(ex, threadIdx.x) + blockIdx.x, &expect, 0ull,
+                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// The maximum (magnitude bits) over this wave's piece of column-wise tile s: row-block 16 group + wave of the tile's
+// strip, as workgroup s loads it (tiled selects the tile order of the tiled-scale launch).  v is used as scratch.
+template <bool RHT>
+__device__ uint32_t tile_max_colwise(const uint16_t* x, uint32_t cols, const ColGrid& cg, uint32_t s, bool tiled,
+                                     uint32_t sign_mask, uint4 (&v)[16]) {
+    const ColPos p = tiled ? col_position(cg, s) : col_position_octets(cg, s);
+    uint32_t m = 0;
+    if (p.rb < cg.nrb && p.c8 < cols) {
+        load_col_tile(x, cols, p, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {   // one block at a time: this runs with the caller's state live
+            float w[16];
+            widen_col_block<RHT>(v, j, sign_mask, w);
+            const float bmax = absmax16(w);
+            m = umax(m, as_u(RHT ? 0.25f * bmax : bmax) & 0x7FFFFFFFu);
+        }
+    }
+    return m;
 }
 
 constexpr int kOutGroup = 2;   // column blocks per write-out in phase 2 of the single-read kernel
@@ -1201,13 +1250,13 @@ template <int MODE>
 __global__ void __launch_bounds__(kColThreads)
 k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColGrid cg, uint32_t sign_mask,
                      RngArgs rng, float* __restrict__ amax_out, uint8_t* __restrict__ codes,
-                     uint8_t* __restrict__ scales, float* __restrict__ gout, uint64_t wait_ticks, uint32_t region,
-                     uint32_t tiled) {
+                     uint8_t* __restrict__ scales, float* __restrict__ gout, Exchange ex, uint32_t tiled) {
     constexpr bool SR = MODE != kRN;
     constexpr bool RHT = MODE == kRHTSR;
     __shared__ ColStash st;
     __shared__ RTable tab;
-    __shared__ uint32_t red[kColRB];
+    __shared__ uint32_t red[kColRB], missing[64], s_own;
+    announce(ex);
     // row-major scales: row groups by octets on one XCD (measured 30.5 -> 29.7 us at 8192 x 4096); tiled scales
     // are whole 2 KiB runs and do better in the usual order (28.6 against 29.4 us)
     const ColPos pos = tiled ? col_position(cg, blockIdx.x) : col_position_octets(cg, blockIdx.x);
@@ -1239,13 +1288,16 @@ k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t col
     // the tile stays in registers: keep the compiler from carrying the widened values over the wait instead
 #pragma unroll
     for (int k = 0; k < 16; ++k) asm volatile("" : "+v"(v[k].x), "+v"(v[k].y), "+v"(v[k].z), "+v"(v[k].w));
-    bool slow;
-    uint32_t abits = exchange_max<RHT>(mbits, wait_ticks, region, red, tab, slow);
-    if (slow) {
-        // slow route: the whole tensor's amax from this workgroup alone, then the tile again
+    uint32_t nmiss;
+    uint32_t abits = exchange_max<RHT>(mbits, ex, red, missing, &s_own, tab, nmiss);
+    if (nmiss) {
+        // slow route: the maxima of the tiles whose slots were not seen, from the tensor, then the own tile again
         __shared__ uint32_t s_bits;
-        const uint32_t mm = wg_amax_colwise<RHT>(x, cols, cg, sign_mask, v, red);
-        if (threadIdx.x == 0) s_bits = mm;
+        uint32_t mm = 0;
+        for (uint32_t t = 0; t < gridDim.x; ++t)
+            if (slot_missing(missing, t)) mm = umax(mm, tile_max_colwise<RHT>(x, cols, cg, t, tiled, sign_mask, v));
+        mm = block_max<kColRB>(mm, red);
+        if (threadIdx.x == 0) s_bits = umax(mm, abits);
         if (active) {
             load_col_tile(x, cols, pos, v);
             // wait for the reloaded tile here: left pending, the wait would land in phase 2 on the common path,
@@ -1291,7 +1343,7 @@ k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t col
     // every block's scale is in LDS since the last barrier
     if (tiled) col_write_scales_tiled(st, pos, cols, cg.nrb, scales);
     else col_write_scales_rows(st, pos, cols, cg.nrb, scales);
-    release_slot(region);
+    release_slot(ex, s_own);
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -2088,27 +2140,46 @@ constexpr uint32_t kRowFusedPerLane = 8;
 // TILED: the workgroup takes item blockIdx.x of the tiled-scale mapping (128 rows x 64 blocks, 8 blocks per lane:
 // block l of row 16 j + w for lane l of wave w) and writes its scales as 16 whole tiles at the end; otherwise lane t
 // takes blocks blockIdx.x * bpl * 1024 + 1024 j + t.  rows, nb and items_per_band are used only when TILED.
+// The blocks of row-wise single-read workgroup (tile) t: index and existence of the lane's j-th block.
+struct RowFusedTile {
+    uint32_t total_blocks, bpl, rows, nb, items_per_band;
+    bool tiled;
+    __device__ uint32_t index(uint32_t t, uint32_t j) const {
+        if (tiled) {
+            const RowTileItem it = row_tile_item(t, items_per_band);
+            return (it.row0 + 16 * j + (threadIdx.x >> 6)) * nb + it.blk0 + (threadIdx.x & 63u);
+        }
+        return t * bpl * kColThreads + threadIdx.x + j * kColThreads;
+    }
+    __device__ bool valid(uint32_t t, uint32_t j) const {
+        if (tiled) {
+            const RowTileItem it = row_tile_item(t, items_per_band);
+            return it.blk0 + (threadIdx.x & 63u) < nb && it.row0 + 16 * j + (threadIdx.x >> 6) < rows;
+        }
+        return j < bpl && index(t, j) < total_blocks;
+    }
+};
+
+// TILED: the workgroup takes item blockIdx.x of the tiled-scale mapping (128 rows x 64 blocks, 8 blocks per lane:
+// block l of row 16 j + w for lane l of wave w) and writes its scales as 16 whole tiles at the end; otherwise lane t
+// takes blocks blockIdx.x * bpl * 1024 + 1024 j + t.  rows, nb and items_per_band are used only when TILED.
 template <int MODE, bool TILED>
 __global__ void __launch_bounds__(kColThreads)
 k_amax_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, uint32_t bpl, uint32_t sign_mask,
                      RngArgs rng, float* __restrict__ amax_out, uint2* __restrict__ codes,
-                     uint8_t* __restrict__ scales, float* __restrict__ gout, uint64_t wait_ticks, uint32_t region,
-                     uint32_t rows, uint32_t nb, uint32_t items_per_band) {
+                     uint8_t* __restrict__ scales, float* __restrict__ gout, Exchange ex, uint32_t rows, uint32_t nb,
+                     uint32_t items_per_band) {
     constexpr bool SR = MODE != kRN;
     constexpr bool RHT = MODE == kRHTSR;
     __shared__ ColStash st;
     __shared__ RTable tab;
-    __shared__ uint32_t red[kColRB];
+    __shared__ uint32_t red[kColRB], missing[64], s_own;
+    announce(ex);
     const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63u;
-    const uint32_t base = blockIdx.x * bpl * kColThreads + threadIdx.x;
+    const RowFusedTile tl{total_blocks, bpl, rows, nb, items_per_band, TILED};
     const RowTileItem it = TILED ? row_tile_item(blockIdx.x, items_per_band) : RowTileItem{0, 0};
-    // block index of the lane's j-th block, and whether it exists
-    auto index = [&](uint32_t j) -> uint32_t {
-        return TILED ? (it.row0 + 16 * j + wave) * nb + it.blk0 + lane : base + j * kColThreads;
-    };
-    auto valid = [&](uint32_t j) -> bool {
-        return TILED ? (it.blk0 + lane < nb && it.row0 + 16 * j + wave < rows) : (j < bpl && index(j) < total_blocks);
-    };
+    auto index = [&](uint32_t j) -> uint32_t { return tl.index(blockIdx.x, j); };
+    auto valid = [&](uint32_t j) -> bool { return tl.valid(blockIdx.x, j); };
     uint4 a[kRowFusedPerLane], b[kRowFusedPerLane];
     float bm[kRowFusedPerLane];
     uint32_t mbits = 0;
@@ -2144,16 +2215,24 @@ k_amax_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, uint32_
         asm volatile("" : "+v"(a[j].x), "+v"(a[j].y), "+v"(a[j].z), "+v"(a[j].w));
         asm volatile("" : "+v"(b[j].x), "+v"(b[j].y), "+v"(b[j].z), "+v"(b[j].w));
     }
-    bool slow;
-    uint32_t abits = exchange_max<RHT>(mbits, wait_ticks, region, red, tab, slow);
-    if (slow) {
-        // slow route: the whole tensor's amax from this workgroup alone (the tile stays in registers)
+    uint32_t nmiss;
+    uint32_t abits = exchange_max<RHT>(mbits, ex, red, missing, &s_own, tab, nmiss);
+    if (nmiss) {
+        // slow route: the maxima of the tiles whose slots were not seen, from the tensor (the own tile stays in
+        // registers)
         __shared__ uint32_t s_bits;
         uint32_t m = 0;
-        for (uint32_t n = threadIdx.x; n < total_blocks; n += kColThreads)
-            m = umax(m, rowblock_absmax<RHT>(ld16(x + 2 * (size_t)n), ld16(x + 2 * (size_t)n + 1), sign_mask));
+        for (uint32_t t = 0; t < gridDim.x; ++t) {
+            if (!slot_missing(missing, t)) continue;
+            for (uint32_t j = 0; j < kRowFusedPerLane; ++j) {
+                if (tl.valid(t, j)) {
+                    const uint32_t n = tl.index(t, j);
+                    m = umax(m, rowblock_absmax<RHT>(ld16(x + 2 * (size_t)n), ld16(x + 2 * (size_t)n + 1), sign_mask));
+                }
+            }
+        }
         m = block_max<kColRB>(m, red);
-        if (threadIdx.x == 0) s_bits = m;
+        if (threadIdx.x == 0) s_bits = umax(m, abits);
         __syncthreads();
         abits = __builtin_amdgcn_readfirstlane(s_bits);
         fill_rtable<RHT>(tab, global_scale(as_f(abits)));
@@ -2190,7 +2269,7 @@ k_amax_quant_rowwise(const uint4* __restrict__ x, uint32_t total_blocks, uint32_
             return (uint8_t)st.e[r & 15u][(r >> 4) * 64 + c].z;
         });
     }
-    release_slot(region);
+    release_slot(ex, s_own);
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -2433,18 +2512,50 @@ hipError_t launch_quant_1x16(const uint16_t* x, int64_t rows, int64_t cols, bool
     return hipGetLastError();
 }
 
-// The single-read kernel's wait bound.  NVFP4_FUSED_WAIT_TICKS (100 MHz ticks) overrides it; the tests set 0 to
-// send every workgroup down the slow route (whole-tensor amax per workgroup) and check that it agrees.
-// Slot region of the next single-read launch: regions are taken in turn.
-uint32_t next_slot_region() {
-    static std::atomic<uint32_t> launches{0};
-    return launches.fetch_add(1, std::memory_order_relaxed) % kSlotRegions;
+// Device address of `scratch` (the single-read exchange slots) on the current device, looked up once per device with
+// that device current; host code uses this address, never the array's name.
+hipError_t scratch_on_device(uint64_t** out) {
+    static std::atomic<uint64_t*> cached[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    uint64_t* p = cached[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void* q = nullptr;
+        e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        p = static_cast<uint64_t*>(q);
+        cached[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
 }
 
-uint64_t fused_wait_ticks() {
-    const char* e = getenv("NVFP4_FUSED_WAIT_TICKS");
-    if (!e || !*e) return kWaitTicks;
+uint64_t ticks_from_env(const char* name, uint64_t dflt) {
+    const char* e = getenv(name);
+    if (!e || !*e) return dflt;
     return strtoull(e, nullptr, 10);
+}
+
+// The exchange of the next single-read launch: a fresh nonzero epoch and its slot region.  The wait bounds can be
+// overridden (100 MHz ticks) by NVFP4_FUSED_WAIT_TICKS and NVFP4_FUSED_ARRIVE_TICKS, and NVFP4_FUSED_REGION puts
+// every launch in one region: the tests use them to send workgroups down the slow route and to make concurrent
+// launches share a region, and check that the results do not change.
+hipError_t next_exchange(Exchange* ex) {
+    uint64_t* base = nullptr;
+    const hipError_t e = scratch_on_device(&base);
+    if (e != hipSuccess) return e;
+    static std::atomic<uint32_t> launches{0};
+    uint32_t epoch = launches.fetch_add(1, std::memory_order_relaxed) + 1;
+    if (epoch == 0) epoch = launches.fetch_add(1, std::memory_order_relaxed) + 1;   // after 2^32 launches
+    const uint64_t fixed = ticks_from_env("NVFP4_FUSED_REGION", kSlotRegions);
+    ex->region = base + (size_t)(fixed < kSlotRegions ? fixed : epoch % kSlotRegions) * kSlotsPerRegion;
+    ex->epoch = epoch;
+    ex->pad = 0;
+    ex->wait_ticks = ticks_from_env("NVFP4_FUSED_WAIT_TICKS", kWaitTicks);
+    ex->arrive_ticks = ticks_from_env("NVFP4_FUSED_ARRIVE_TICKS", kArriveTicks);
+    return hipSuccess;
 }
 
 hipError_t launch_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, bool colwise, Mode mode, uint32_t sign_mask,
@@ -2457,11 +2568,12 @@ hipError_t launch_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, bool
         if (grid <= (uint32_t)cu_count() && grid <= kFusedMaxGrid) {
             uint32_t r = (uint32_t)rows, c = (uint32_t)cols;
             RngArgs ra = rng_args(rng);
-            uint64_t wait = fused_wait_ticks();
-            uint32_t region = next_slot_region();
+            Exchange ex;
+            const hipError_t e = next_exchange(&ex);
+            if (e != hipSuccess) return e;
             uint32_t tl = tiled ? 1u : 0u;
             void* args[] = {(void*)&x, &r, &c, (void*)&w, &sign_mask, &ra, (void*)&amax, (void*)&codes, (void*)&scales,
-                            (void*)&g, &wait, &region, &tl};
+                            (void*)&g, &ex, &tl};
             const void* fn = mode == kRN ? (const void*)k_amax_quant_colwise<kRN>
                              : mode == kSR ? (const void*)k_amax_quant_colwise<kSR>
                                            : (const void*)k_amax_quant_colwise<kRHTSR>;
@@ -2476,11 +2588,12 @@ hipError_t launch_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, bool
             const uint4* xv = reinterpret_cast<const uint4*>(x);
             uint2* cv = reinterpret_cast<uint2*>(codes);
             RngArgs ra = rng_args(rng);
-            uint64_t wait = fused_wait_ticks();
-            uint32_t region = next_slot_region();
+            Exchange ex;
+            const hipError_t e = next_exchange(&ex);
+            if (e != hipSuccess) return e;
             uint32_t t = (uint32_t)(rows * nb), bp = kRowFusedPerLane, r = (uint32_t)rows, nbv = nb, ip = ipb;
             void* args[] = {(void*)&xv, &t, &bp, &sign_mask, &ra, (void*)&amax, (void*)&cv, (void*)&scales,
-                            (void*)&g, &wait, &region, &r, &nbv, &ip};
+                            (void*)&g, &ex, &r, &nbv, &ip};
             const void* fn = mode == kRN ? (const void*)k_amax_quant_rowwise<kRN, true>
                              : mode == kSR ? (const void*)k_amax_quant_rowwise<kSR, true>
                                            : (const void*)k_amax_quant_rowwise<kRHTSR, true>;
@@ -2497,11 +2610,12 @@ hipError_t launch_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, bool
                 const uint4* xv = reinterpret_cast<const uint4*>(x);
                 uint2* cv = reinterpret_cast<uint2*>(codes);
                 RngArgs ra = rng_args(rng);
-                uint64_t wait = fused_wait_ticks();
-                uint32_t region = next_slot_region();
+                Exchange ex;
+                const hipError_t e = next_exchange(&ex);
+                if (e != hipSuccess) return e;
                 uint32_t t = total, bp = bpl, unused = 0;
                 void* args[] = {(void*)&xv, &t, &bp, &sign_mask, &ra, (void*)&amax, (void*)&cv, (void*)&scales,
-                                (void*)&g, &wait, &region, &unused, &unused, &unused};
+                                (void*)&g, &ex, &unused, &unused, &unused};
                 const void* fn = mode == kRN ? (const void*)k_amax_quant_rowwise<kRN, false>
                                  : mode == kSR ? (const void*)k_amax_quant_rowwise<kSR, false>
                                                : (const void*)k_amax_quant_rowwise<kRHTSR, false>;

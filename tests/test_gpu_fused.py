@@ -77,8 +77,8 @@ def test_consecutive_calls_reuse_the_barrier():
 
 @pytest.mark.parametrize("mode", ["rn", "rht_sr"])
 def test_slow_route_after_a_timed_out_wait(monkeypatch, mode):
-    """A zero wait bound sends workgroups that find a slot still empty down the slow route (each computes the whole
-    tensor's amax itself); the result must not change."""
+    """A zero wait bound sends workgroups that find a slot still empty down the slow route (each computes the maxima
+    of the tiles it has not seen from the tensor itself); the result must not change."""
     monkeypatch.setenv("NVFP4_FUSED_WAIT_TICKS", "0")
     x = W.lognormal_gradients(2048, 1024, seed=91)
     for call in range(3):
@@ -122,6 +122,106 @@ def test_concurrent_calls_on_two_streams():
         assert (a.cpu().numpy().view(np.uint32) == oa.view(np.uint32)).all(), (i, rep)
         assert np.array_equal(o.codes.cpu().numpy(), oc), (i, rep)
         assert np.array_equal(o.scales.cpu().numpy(), os_), (i, rep)
+
+
+def expect(x, orient, mode, mask, seed, offset, a, o, what):
+    oa = O.amax(x, orient, O.G_PER_TENSOR, mode == "rht_sr", mask)
+    oc, os_, og = O.quantize_1x16(x, oa, ROUNDING[mode][1], orient, O.G_PER_TENSOR, mask, seed, offset)
+    assert (a.cpu().numpy().view(np.uint32) == oa.view(np.uint32)).all(), what
+    assert np.array_equal(o.codes.cpu().numpy(), oc), what
+    assert np.array_equal(o.scales.cpu().numpy(), os_), what
+    assert (o.g.cpu().numpy().view(np.uint32) == og.view(np.uint32)).all(), what
+
+
+def overlap_cases():
+    xs = [W.lognormal_gradients(1024, 2048, seed=61), W.gaussian(2048, 1024, seed=62, scale=1000.0),
+          W.outlier_columns(512, 4096, seed=63, n_cols=7), W.lognormal_gradients(2048, 4096, seed=64)]
+    out = []
+    for i in range(10):
+        x = xs[i % 4]
+        out.append((x, Q.COLWISE if i % 3 else Q.ROWWISE, ("rn", "sr", "rht_sr")[i % 3], W.sign_mask(70, i), 70, i))
+    return out
+
+
+def run_overlapping(cases, spin=200_000, rounds=2):
+    """Every case on a stream of its own, each stream first held by a short spin so that the calls start together;
+    no synchronisation until all are queued."""
+    streams = [torch.cuda.Stream() for _ in cases]
+    devs = [torch.from_numpy(c[0].view(np.int16)).cuda() for c in cases]
+    torch.cuda.synchronize()
+    results = []
+    for rep in range(rounds):
+        for i, (x, orient, mode, mask, seed, off) in enumerate(cases):
+            with torch.cuda.stream(streams[i]):
+                torch.cuda._sleep(spin)
+                say("overlap", rep, i, mode, x.shape, orient)
+                results.append((i, rep) + Q.nvfp4_amax_quantize(devs[i], orient, ROUNDING[mode][0], mask, seed,
+                                                                off + 100 * rep, stream=streams[i]))
+    torch.cuda.synchronize()
+    for i, rep, a, o in results:
+        x, orient, mode, mask, seed, off = cases[i]
+        expect(x, orient, mode, mask, seed, off + 100 * rep, a, o, (i, rep))
+
+
+def test_ten_overlapping_calls():
+    """Ten single-read calls in flight at once on ten streams (more than the 8 slot regions, so launches may share
+    one), column- and row-wise, on tensors of very different magnitudes: each must equal the oracle."""
+    run_overlapping(overlap_cases())
+
+
+def test_overlapping_calls_forced_into_one_region(monkeypatch):
+    """Every launch in the same slot region while several run at once: a slot holding another launch's value is
+    never taken as a maximum (it carries another epoch), so the launches fall back to reading the missing tiles
+    and every result still equals the oracle."""
+    monkeypatch.setenv("NVFP4_FUSED_REGION", "5")
+    run_overlapping(overlap_cases()[:6], rounds=2)
+    monkeypatch.delenv("NVFP4_FUSED_REGION")
+    run_overlapping(overlap_cases()[:2], rounds=1)    # and the regions in turn again
+
+
+def test_graph_replays_against_eager_calls_on_another_stream():
+    """A captured single-read call (its epoch and region fixed at capture) replayed on one stream while eager calls
+    run on another stream at the same time: the replays and the eager calls all equal the oracle."""
+    xg = W.lognormal_gradients(2048, 1024, seed=33)
+    xe = W.gaussian(1024, 2048, seed=34, scale=300.0)
+    dg = torch.from_numpy(xg.view(np.int16)).cuda()
+    de = torch.from_numpy(xe.view(np.int16)).cuda()
+    sg, se = torch.cuda.Stream(), torch.cuda.Stream()
+    a_g = torch.empty((1,), device="cuda")
+    o_g = Q.alloc_out(1024, 2048, 0, dg.device)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=sg):
+        Q.nvfp4_amax_quantize(dg, Q.COLWISE, Q.ROUND_RHT_SR, 0x2B2B, 3, 9, amax=a_g, out=o_g, stream=sg)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        say("graph vs eager", rep)
+        a_g.fill_(1e30)
+        o_g.codes.zero_()
+        torch.cuda.synchronize()
+        eager = []
+        with torch.cuda.stream(sg):
+            torch.cuda._sleep(200_000)
+            graph.replay()
+        with torch.cuda.stream(se):
+            torch.cuda._sleep(200_000)
+            for k in range(3):
+                eager.append((k,) + Q.nvfp4_amax_quantize(de, Q.ROWWISE if k % 2 else Q.COLWISE, Q.ROUND_SR, 0, 5,
+                                                          k, stream=se))
+        torch.cuda.synchronize()
+        expect(xg, Q.COLWISE, "rht_sr", 0x2B2B, 3, 9, a_g, o_g, ("graph", rep))
+        for k, a, o in eager:
+            expect(xe, Q.ROWWISE if k % 2 else Q.COLWISE, "sr", 0, 5, k, a, o, ("eager", rep, k))
+
+
+def test_not_all_workgroups_waited_for(monkeypatch):
+    """A zero bound on the wait for workgroups that have not started: a workgroup that polls before every other has
+    announced itself stops waiting at once and reads the missing tiles; the result must not change."""
+    monkeypatch.setenv("NVFP4_FUSED_ARRIVE_TICKS", "0")
+    for call in range(3):
+        check(W.lognormal_gradients(2048, 4096, seed=95), "rht_sr", Q.COLWISE, mask=W.sign_mask(8, call), seed=8,
+              offset=call)
+        check(W.outlier_columns(4096, 2048, seed=96, n_cols=4), "sr", Q.ROWWISE, mask=0, seed=8, offset=call)
+    monkeypatch.delenv("NVFP4_FUSED_ARRIVE_TICKS")
 
 
 def test_nan_and_zero_tensors():
