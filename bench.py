@@ -552,7 +552,7 @@ def measure(args, Q, W, dev, x_bits, x0, xs, outs, amaxes, masks, step, nbuf, st
                    "rht": True, "rounding": "philox_sr", "gmode": "per_tensor",
                    "step": "nvfp4_amax_quantize (single read)", "input_buffers": nbuf},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "roofline": {"kernel": "k_amax_quant_colwise<RHT+SR> (single read: amax + quantize)", "bound": "hbm",
+        "roofline": {"kernel": "k_amax_quant_colwise4<RHT+SR> (single read: amax + quantize)", "bound": "hbm",
                      "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(value / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "algorithmic_bytes_per_launch": step_bytes, "mean_launch_ms": round(ms_per_step, 5),

@@ -144,10 +144,10 @@ nvfp4_status nvfp4_quantize_rht_sr(const uint16_t* x, int64_t rows, int64_t cols
 /* The amax pass and a 1x16 quantization with a per-tensor g in one call ([P2, results: amax and quantization
  * with no host round trip]).  The result equals nvfp4_amax (per tensor, use_rht = rounding is RHT_SR) followed by
  * nvfp4_quantize_rn / _sr / _rht_sr with the same arguments, and amax[0] is written too.
- *   A tensor that fits one workgroup per CU is read from memory once: column-wise up to one 256-row x
- *   512-column tile per CU, row-wise up to 8192 blocks per CU (8192 x 4096 either way on MI355X).  Each
- *   workgroup keeps its share in registers, publishes its maximum in a slot and waits for every other workgroup's;
- *   larger tensors run the two passes.
+ *   A tensor that the chip can hold in registers is read from memory once: column-wise (cols % 4 == 0) up to two
+ *   256-row x 256-column tiles per CU, row-wise up to 8192 blocks per CU (8192 x 4096 either way on MI355X).
+ *   Each workgroup keeps its share in registers, publishes its maximum in a slot and waits for every other
+ *   workgroup's; larger tensors run the two passes.
  *   The exchange slots are a 2 MiB array in the library's own device memory (one per GPU).  Each launch tags its slots with a fresh 32-bit epoch and takes one of the 8 regions in turn.  Calls that overlap
  *   on one GPU (other streams, graph replays) may share a region: a workgroup never takes a slot that carries
  *   another launch's epoch, so sharing costs time, never correctness.  The wait is bounded: after 100 us with some

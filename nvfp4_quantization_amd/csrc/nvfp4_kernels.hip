@@ -342,59 +342,84 @@ __device__ __forceinline__ uint32_t patch_nan8(uint32_t d, const float (&q)[8]) 
     return d;
 }
 
-template <bool SR>
-__device__ __forceinline__ void encode16(const float (&q)[16], const Rand4& inv, uint32_t& lo, uint32_t& hi) {
+// Sources of a block's complemented random words: held in registers (Rand4), or read from LDS half a block at a
+// time (LdsRand), so that only the two words of the half being encoded are live.
+__device__ __forceinline__ uint2 rand_lo(const Rand4& r) { return make_uint2(r.w[0], r.w[1]); }
+__device__ __forceinline__ uint2 rand_hi(const Rand4& r) { return make_uint2(r.w[2], r.w[3]); }
+struct LdsRand {
+    const uint4* p;
+};
+__device__ __forceinline__ uint2 rand_lo(const LdsRand& r) { return reinterpret_cast<const uint2*>(r.p)[0]; }
+__device__ __forceinline__ uint2 rand_hi(const LdsRand& r) { return reinterpret_cast<const uint2*>(r.p)[1]; }
+
+template <bool SR, typename R>
+__device__ __forceinline__ void encode16(const float (&q)[16], const R& inv, uint32_t& lo, uint32_t& hi) {
     const float(&q0)[8] = *reinterpret_cast<const float(*)[8]>(&q[0]);
     const float(&q1)[8] = *reinterpret_cast<const float(*)[8]>(&q[8]);
     if (SR) {
-        lo = pack8_sr(q0, inv.w[0], inv.w[1]);
-        hi = pack8_sr(q1, inv.w[2], inv.w[3]);
+        const uint2 a = rand_lo(inv);
+        lo = pack8_sr(q0, a.x, a.y);
+        __builtin_amdgcn_sched_barrier(0);
+        const uint2 b = rand_hi(inv);
+        hi = pack8_sr(q1, b.x, b.y);
     } else {
         lo = pack8_rn(q0);
         hi = pack8_rn(q1);
     }
 }
 
-// Quantize one 16-element block.  w[] are the values before the final 0.25 of the transform when RHT is set
-// (y = fl(0.25 w)), the values themselves otherwise; mul gives the multipliers of a scale code (fast_multiplier).
-// Returns false when the block needs the general path.
-template <bool SR, bool RHT, typename Mul>
-__device__ __forceinline__ bool quantize_block_fast(const float (&w)[16], float m, const Divisor& d6, const Mul& mul,
-                                                    const Rand4& inv, uint32_t& lo, uint32_t& hi, uint32_t& sb) {
-    // m = absmax16(w)
+// Quantize one 16-element block; w[] is consumed (the scaled values are formed in its place).  w[] are the values
+// before the final 0.25 of the transform when RHT is set (y = fl(0.25 w)), the values themselves otherwise; m is
+// the block's absmax16(w); mul gives the multipliers of a scale code (fast_multiplier).  Which path a block takes
+// depends only on its scale code, so it is decided before the multiply: the fast path q = fl(w rq), or the
+// definition step by step, q = fl(fl(0.25 w) r) (RHT) or fl(w r), with NaN products patched to code 0x7.
+template <bool SR, bool RHT, typename Mul, typename R>
+__device__ __forceinline__ void quantize_block_m(float (&w)[16], float m, const Divisor& d6, const Mul& mul,
+                                                 const R& inv, uint32_t& lo, uint32_t& hi, uint32_t& sb) {
     const float bamax = RHT ? 0.25f * m : m;       // max_i fl(0.25 |w_i|) = fl(0.25 max_i |w_i|)
     sb = scale_code(bamax, d6);
     const float rq = mul.rq(sb);
-    float q[16];
+    const bool fast = rq == rq;
+    const float r = fast ? rq : mul.r(sb);
+    if (SR) {
+        // The SR conversion reads its operands as aligned register pairs, so the products are formed in pairs of
+        // their own, half a block at a time (fewer registers live than forming all 16 next to w).
+        float q[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) q[i] = w[i] * rq;
-    encode16<SR>(q, inv, lo, hi);
-    return rq == rq;
-}
-
-// The definition step by step for blocks outside the fast path: y = fl(0.25 w) (RHT), q = fl(y r); NaN -> 0x7.
-template <bool SR, bool RHT>
-__device__ __forceinline__ void quantize_block_general(const float (&w)[16], float r, const Rand4& inv, uint32_t& lo,
-                                                       uint32_t& hi) {
-    float q[16];
+        for (int h = 0; h < 2; ++h) {
+            if (fast) [[likely]] {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) q[i] = (RHT ? 0.25f * w[i] : w[i]) * r;
-    encode16<SR>(q, inv, lo, hi);
-    lo = patch_nan8(lo, *reinterpret_cast<const float(*)[8]>(&q[0]));
-    hi = patch_nan8(hi, *reinterpret_cast<const float(*)[8]>(&q[8]));
+                for (int i = 0; i < 8; ++i) q[i] = w[8 * h + i] * r;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) q[i] = (RHT ? 0.25f * w[8 * h + i] : w[8 * h + i]) * r;
+            }
+            const uint2 rw = h ? rand_hi(inv) : rand_lo(inv);
+            uint32_t d = pack8_sr(q, rw.x, rw.y);
+            if (!fast) [[unlikely]] d = patch_nan8(d, q);
+            (h ? hi : lo) = d;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        if (fast) [[likely]] {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) w[i] = w[i] * r;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) w[i] = (RHT ? 0.25f * w[i] : w[i]) * r;
+        }
+        lo = pack8_rn(*reinterpret_cast<const float(*)[8]>(&w[0]));
+        hi = pack8_rn(*reinterpret_cast<const float(*)[8]>(&w[8]));
+        if (!fast) [[unlikely]] {
+            lo = patch_nan8(lo, *reinterpret_cast<const float(*)[8]>(&w[0]));
+            hi = patch_nan8(hi, *reinterpret_cast<const float(*)[8]>(&w[8]));
+        }
+    }
 }
 
-// m is the block's absmax16(w), when the caller has it already.
-template <bool SR, bool RHT, typename Mul>
-__device__ __forceinline__ void quantize_block_m(const float (&w)[16], float m, const Divisor& d6, const Mul& mul,
-                                                 const Rand4& inv, uint32_t& lo, uint32_t& hi, uint32_t& sb) {
-    if (!quantize_block_fast<SR, RHT>(w, m, d6, mul, inv, lo, hi, sb)) [[unlikely]]
-        quantize_block_general<SR, RHT>(w, mul.r(sb), inv, lo, hi);
-}
-
-template <bool SR, bool RHT, typename Mul>
-__device__ __forceinline__ void quantize_block(const float (&w)[16], const Divisor& d6, const Mul& mul,
-                                               const Rand4& inv, uint32_t& lo, uint32_t& hi, uint32_t& sb) {
+template <bool SR, bool RHT, typename Mul, typename R>
+__device__ __forceinline__ void quantize_block(float (&w)[16], const Divisor& d6, const Mul& mul,
+                                               const R& inv, uint32_t& lo, uint32_t& hi, uint32_t& sb) {
     quantize_block_m<SR, RHT>(w, absmax16(w), d6, mul, inv, lo, hi, sb);
 }
 
@@ -724,26 +749,6 @@ __device__ __forceinline__ ColPos col_position(const ColGrid& g, uint32_t tile) 
     return p;
 }
 
-// The single-read kernel's launch index -> tile, such that the 8 row groups 8 o .. 8 o + 7 of one strip run on the
-// same XCD (workgroups are dealt round-robin to the 8 XCDs): the 16-byte pieces of row-major scales that those 8
-// workgroups write into each output row then fill one 128-byte line in one L2, where pieces from 8 XCDs would each
-// leave as a partial line.  Pairs (octet, strip) are dealt to the XCDs in turn, so every XCD still reads several
-// strips.  Needs whole octets and a multiple of 8 pairs; otherwise the usual order.
-__device__ __forceinline__ ColPos col_position_octets(const ColGrid& g, uint32_t b) {
-    const uint32_t ngroups = (g.nrb + kColRB - 1) / kColRB;
-    const uint32_t pairs = (ngroups / 8) * g.nstrips;
-    if ((ngroups & 7u) != 0 || (pairs & 7u) != 0) return col_position(g, b);
-    const uint32_t x = b & 7u, i = b >> 3;
-    const uint32_t pr = (i >> 3) * 8 + x, o = pr / g.nstrips;
-    ColPos p;
-    p.group = 8 * o + (i & 7u);
-    p.strip = pr - o * g.nstrips;
-    p.rb = p.group * kColRB + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    p.lane = threadIdx.x & 63u;
-    p.c8 = p.strip * 512 + 8 * p.lane;
-    return p;
-}
-
 // Issues the 16 loads of the lane's 16 x 8 tile (cols is a multiple of 8: a lane's columns exist all or none).  The
 // loads go through a buffer resource over the wave's 16 rows (a wave-uniform base): the lane offset is one 32-bit
 // register and the row offset a scalar, where 64-bit addresses would take two registers per load in flight.  The
@@ -790,82 +795,6 @@ __device__ __forceinline__ void col_write_out(const ColStage<RB>& st, const ColP
 struct ColStash {
     uint4 e[kColRB][8 * 64 + 1];
 };
-
-// Writes the codes/scales of column blocks j = G jg .. G jg + G - 1 of every lane held in a ColStash: thread t
-// takes row-block t % 16 of column 8 (t / 16) + j, so 16 consecutive threads write one column's 128 contiguous code
-// bytes.
-template <int G>
-__device__ __forceinline__ void col_write_out_group(const ColStash& st, const ColPos& p, uint32_t rows,
-                                                    uint32_t cols, uint32_t nrb, int jg, uint8_t* __restrict__ codes,
-                                                    uint8_t* __restrict__ scales, bool tiled) {
-    const uint32_t col0 = p.strip * 512;
-    const uint32_t ncol = min(512u, cols - col0), nr = min((uint32_t)kColRB, nrb - p.group * kColRB);
-    const uint32_t rbl = threadIdx.x % kColRB, lq = threadIdx.x / kColRB, rb = p.group * kColRB + rbl;
-    if (rbl >= nr) return;
-#pragma unroll
-    for (int jj = 0; jj < G; ++jj) {
-        const uint32_t j = G * jg + jj, cl = 8 * lq + j;
-        if (cl < ncol) {
-            const uint4 e = st.e[rbl][j * 64 + lq];
-            const uint32_t c = col0 + cl;
-            st_nt(codes + (size_t)c * (rows >> 1) + 8 * (size_t)rb, make_uint2(e.x, e.y));
-            if (!tiled) st_nt(scales + (size_t)c * nrb + rb, (uint8_t)e.z);
-        }
-    }
-}
-
-// The workgroup's scale codes (held in the z words of a ColStash), row-major: thread t < 512 writes the 16 bytes
-// (row-blocks of the group) of output row strip * 512 + t with one store where they are a whole aligned 16-byte
-// piece, byte by byte otherwise.  The 16-byte stores are ordinary (cached) ones, so that the pieces of the 8 row
-// groups of an octet (one XCD, see col_position_octets) meet in L2 as whole 128-byte lines: 30.8 us with
-// non-temporal stores against 29.7 us at 8192 x 4096.
-__device__ __forceinline__ void col_write_scales_rows(const ColStash& st, const ColPos& p, uint32_t cols,
-                                                      uint32_t nrb, uint8_t* __restrict__ scales) {
-    if (threadIdx.x >= 512) return;
-    const uint32_t cl = threadIdx.x, c = p.strip * 512 + cl;
-    if (c >= cols) return;
-    const uint32_t nr = min((uint32_t)kColRB, nrb - p.group * kColRB);
-    const uint32_t slot = (cl & 7u) * 64 + (cl >> 3);
-    uint8_t* dst = scales + (size_t)c * nrb + p.group * kColRB;
-    if (nr == kColRB && (nrb & 15u) == 0) {
-        uint32_t w[4];
-#pragma unroll
-        for (uint32_t q = 0; q < 4; ++q) {
-            w[q] = 0;
-#pragma unroll
-            for (uint32_t k = 0; k < 4; ++k) w[q] |= (st.e[4 * q + k][slot].z & 0xFFu) << (8 * k);
-        }
-        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-    } else {
-        for (uint32_t r = 0; r < nr; ++r) st_nt(dst + r, (uint8_t)st.e[r][slot].z);
-    }
-}
-
-// The workgroup's scale codes (held in the z words of a ColStash) in the tiled layout of the FP4 GEMM: its 512
-// columns of X are 4 row tiles of V and its 16 row-blocks 4 scale-column tiles, 16 tiles in all; thread t < 512
-// takes tile row a = t % 32 of tile (t / 128, (t / 32) % 4), so each row tile's 2 KiB go out contiguously.  Rows
-// past cols and scale columns past nrb are written as zero.
-__device__ __forceinline__ void col_write_scales_tiled(const ColStash& st, const ColPos& p, uint32_t cols,
-                                                       uint32_t nrb, uint8_t* __restrict__ scales) {
-    if (threadIdx.x >= 512) return;
-    const uint32_t rt = threadIdx.x >> 7, tb = (threadIdx.x >> 5) & 3u, a = threadIdx.x & 31u;
-    const uint32_t col0 = p.strip * 512 + 128 * rt;
-    const uint32_t nr = min((uint32_t)kColRB, nrb - p.group * kColRB);
-    if (col0 >= cols || 4 * tb >= nr) return;
-    const uint32_t bt = (nrb + 3) / 4;
-    uint32_t w[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const uint32_t cl = 128 * rt + 32 * b + a;   // column within the strip
-        w[b] = 0;
-        if (p.strip * 512 + cl < cols) {
-#pragma unroll
-            for (uint32_t c = 0; c < 4; ++c)
-                if (4 * tb + c < nr) w[b] |= (st.e[4 * tb + c][(cl & 7u) * 64 + (cl >> 3)].z & 0xFFu) << (8 * c);
-        }
-    }
-    st_nt(scales + ((size_t)(col0 / 128) * bt + 4 * p.group + tb) * 512 + 16 * a, make_uint4(w[0], w[1], w[2], w[3]));
-}
 
 // Column-wise quantization with a device-resident amax.  The workgroup tile is the same 16 row-blocks x 512 columns,
 // but split among the waves so that the four waves that receive their data together finish a complete piece of the
@@ -1077,6 +1006,237 @@ k_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, Co
 }
 
 // ------------------------------------------------------------------------------------------------------------
+// Column-wise kernels with narrow lane tiles: a lane holds 16 rows x 4 columns (16 loads of 8 bytes, 32 VGPRs) and
+// a 1024-thread workgroup 16 row-blocks x 256 columns (wave w = row-block w), so that two workgroups fit on a CU: 8
+// waves per SIMD instead of 4.  The VALU work per element is the same, but twice the waves are there to issue it
+// while others wait for memory, and each wave's share (4 blocks) is half as long, which shortens the tail after
+// the last data arrives.  At 8192 x 4096 the 512 workgroups are all resident at once.  Codes and scales are staged
+// in LDS and written per output row of X^T: 128 contiguous bytes of codes (16 row-blocks) and 16 of scales.
+// ------------------------------------------------------------------------------------------------------------
+constexpr uint32_t kStrip4 = 256;   // columns of X per narrow workgroup tile
+
+struct Col4Pos {
+    uint32_t group;  // row group (16 row-blocks)
+    uint32_t strip;  // 256-column strip
+    uint32_t rb;     // this wave's row-block
+    uint32_t lane;
+    uint32_t c4;     // first of the lane's 4 columns
+};
+
+// Workgroup b -> (row group, strip), strip-fastest with the strip rotated by the row group (every XCD reads every
+// strip); ns divides by the strip count (uniform values, so the divisions stay on the scalar unit).  octets: the 8 row groups 8 o .. 8 o + 7 of a strip go to one XCD (workgroups are dealt to the 8 XCDs in
+// turn), so that their 16-byte pieces of each row-major scale row meet in one L2 as whole lines; needs whole
+// octets and a multiple of 8 (octet, strip) pairs, else the usual order.
+// n / d for a uniform n (scalar unit): the multiply-high of FastDiv on 64-bit scalar arithmetic.
+__device__ __forceinline__ uint32_t sfdiv(uint32_t n, const FastDiv& f) {
+    n = __builtin_amdgcn_readfirstlane(n);
+    return __builtin_amdgcn_readfirstlane((uint32_t)((((uint64_t)n * f.m >> 32) + n) >> f.s));
+}
+
+__device__ __forceinline__ Col4Pos col4_at(uint32_t group, uint32_t strip) {
+    Col4Pos p;
+    p.group = group;
+    p.strip = strip;
+    p.rb = group * kColRB + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    p.lane = threadIdx.x & 63u;
+    p.c4 = strip * kStrip4 + 4 * p.lane;
+    return p;
+}
+
+__device__ __forceinline__ Col4Pos col4_position(uint32_t nrb, const FastDiv& ns, uint32_t b, bool octets) {
+    const uint32_t nstrips = ns.d;
+    const uint32_t ngroups = (nrb + kColRB - 1) / kColRB;
+    const uint32_t pairs = (ngroups / 8) * nstrips;
+    uint32_t group, strip;
+    b = __builtin_amdgcn_readfirstlane(b);
+    if (octets && (ngroups & 7u) == 0 && (pairs & 7u) == 0) {
+        const uint32_t x = b & 7u, i = b >> 3;
+        const uint32_t pr = (i >> 3) * 8 + x, o = sfdiv(pr, ns);
+        group = 8 * o + (i & 7u);
+        strip = pr - o * nstrips;
+    } else {
+        group = sfdiv(b, ns);
+        const uint32_t s = b - group * nstrips + (group - sfdiv(group, ns) * nstrips);
+        strip = s >= nstrips ? s - nstrips : s;
+    }
+    return col4_at(__builtin_amdgcn_readfirstlane(group), __builtin_amdgcn_readfirstlane(strip));
+}
+
+// The lane's 16 rows x 4 columns: v[k] = row k of the wave's row-block, columns c4 .. c4 + 3 (cols % 4 == 0).  A
+// buffer resource over the row-block: one 32-bit lane offset, the row offset in a scalar.
+__device__ __forceinline__ void load_col4_tile(const uint16_t* x, uint32_t cols, const Col4Pos& p, uint2 (&v)[16]) {
+    const uint16_t* base = x + (size_t)(16 * p.rb) * cols;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, (int)(32u * cols), 0x00020000);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(2u * p.c4), (int)(2u * k * cols), 0);
+        v[k] = make_uint2(t.x, t.y);
+    }
+}
+
+// Column j (0..3) of the lane's 16 x 4 tile -> the 16 values of its column block (sign-flipped and transformed with
+// RHT).
+template <bool RHT>
+__device__ __forceinline__ void widen_col4_block(const uint2 (&v)[16], int j, uint32_t mask, float (&w)[16]) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const uint32_t word = (j >> 1) ? v[k].y : v[k].x;
+        const uint32_t f = RHT ? flip_bit(mask, k) : 0u;
+        w[k] = (j & 1) ? bf16_hi(word, f) : bf16_lo(word, f);
+    }
+    if (RHT) fwht16(w);
+}
+
+// The random signs applied to the packed words of a lane's tile: row k of a column block is element k, so both
+// halves of the words of row k are negated where bit k of mask is set (exact sign-bit flips).
+__device__ __forceinline__ void flip_col4_tile(uint2 (&v)[16], uint32_t mask) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const uint32_t f = ((mask >> k) & 1u) ? 0x80008000u : 0u;
+        v[k].x ^= f;
+        v[k].y ^= f;
+        asm volatile("" : "+v"(v[k].x), "+v"(v[k].y));   // the flipped words replace the loaded ones
+    }
+}
+
+// LDS of a narrow column-wise workgroup: entry (wave, j, lane) first holds the Philox words of the lane's block j,
+// then its codes (x, y) and scale (z).  A wave's region is padded by one entry.
+struct Col4Stash {
+    uint4 e[kColRB][4 * 64 + 1];
+};
+
+__device__ __forceinline__ const uint4& col4_entry(const Col4Stash& st, uint32_t rbl, uint32_t cl) {
+    return st.e[rbl][(cl & 3u) * 64 + (cl >> 2)];   // column cl (0..255) of the strip = block cl % 4 of lane cl / 4
+}
+
+// Writes the workgroup's staged codes: thread t takes column 128 r + t / 8 of the strip (r = 0, 1) and row-blocks
+// 2 (t % 8), 2 (t % 8) + 1, so 8 consecutive threads write one output row's 128 contiguous bytes.
+__device__ __forceinline__ void col4_write_codes(const Col4Stash& st, const Col4Pos& p, uint32_t rows, uint32_t cols,
+                                                 uint32_t nrb, uint8_t* __restrict__ codes) {
+    const uint32_t nr = min((uint32_t)kColRB, nrb - p.group * kColRB);
+    const uint32_t q = threadIdx.x & 7u, rb0 = p.group * kColRB + 2 * q;
+    const bool aligned16 = (rows & 31u) == 0;   // 16-byte stores need (rows / 2) % 16 == 0
+#pragma unroll
+    for (uint32_t r = 0; r < 2; ++r) {
+        const uint32_t cl = 128 * r + (threadIdx.x >> 3), c = p.strip * kStrip4 + cl;
+        if (c < cols && 2 * q < nr) {
+            const uint4 a = col4_entry(st, 2 * q, cl);
+            uint8_t* dst = codes + (size_t)c * (rows >> 1) + 8 * (size_t)rb0;
+            if (2 * q + 1 < nr) {
+                const uint4 b = col4_entry(st, 2 * q + 1, cl);
+                if (aligned16) {
+                    st_nt(dst, make_uint4(a.x, a.y, b.x, b.y));
+                } else {
+                    st_nt(dst, make_uint2(a.x, a.y));
+                    st_nt(dst + 8, make_uint2(b.x, b.y));
+                }
+            } else {
+                st_nt(dst, make_uint2(a.x, a.y));
+            }
+        }
+    }
+}
+
+// The workgroup's scale codes, row-major: thread t < 256 writes the 16 bytes (row-blocks of the group) of output row
+// strip * 256 + t with one store when they form a whole aligned 16-byte piece, byte by byte otherwise.  The 16-byte
+// stores are ordinary (cached) ones, so that the pieces of an octet's row groups (one XCD) meet in L2 as whole lines.
+__device__ __forceinline__ void col4_write_scales_rows(const Col4Stash& st, const Col4Pos& p, uint32_t cols,
+                                                       uint32_t nrb, uint8_t* __restrict__ scales) {
+    if (threadIdx.x >= kStrip4) return;
+    const uint32_t cl = threadIdx.x, c = p.strip * kStrip4 + cl;
+    if (c >= cols) return;
+    const uint32_t nr = min((uint32_t)kColRB, nrb - p.group * kColRB);
+    uint8_t* dst = scales + (size_t)c * nrb + p.group * kColRB;
+    if (nr == kColRB && (nrb & 15u) == 0) {
+        uint32_t w[4];
+#pragma unroll
+        for (uint32_t q = 0; q < 4; ++q) {
+            w[q] = 0;
+#pragma unroll
+            for (uint32_t k = 0; k < 4; ++k) w[q] |= (col4_entry(st, 4 * q + k, cl).z & 0xFFu) << (8 * k);
+        }
+        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+        for (uint32_t r = 0; r < nr; ++r) st_nt(dst + r, (uint8_t)col4_entry(st, r, cl).z);
+    }
+}
+
+// The workgroup's scale codes in the tiled layout of the FP4 GEMM: its 256 columns of X are 2 row tiles of V and its
+// 16 row-blocks 4 scale-column tiles; thread t < 256 takes tile row a = t % 32 of tile (t / 128, (t / 32) % 4).
+// Rows past cols and scale columns past nrb are written as zero.
+__device__ __forceinline__ void col4_write_scales_tiled(const Col4Stash& st, const Col4Pos& p, uint32_t cols,
+                                                        uint32_t nrb, uint8_t* __restrict__ scales) {
+    if (threadIdx.x >= kStrip4) return;
+    const uint32_t rt = threadIdx.x >> 7, tb = (threadIdx.x >> 5) & 3u, a = threadIdx.x & 31u;
+    const uint32_t col0 = p.strip * kStrip4 + 128 * rt;
+    const uint32_t nr = min((uint32_t)kColRB, nrb - p.group * kColRB);
+    if (col0 >= cols || 4 * tb >= nr) return;
+    const uint32_t bt = (nrb + 3) / 4;
+    uint32_t w[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const uint32_t cl = 128 * rt + 32 * b + a;
+        w[b] = 0;
+        if (p.strip * kStrip4 + cl < cols) {
+#pragma unroll
+            for (uint32_t c = 0; c < 4; ++c)
+                if (4 * tb + c < nr) w[b] |= (col4_entry(st, 4 * tb + c, cl).z & 0xFFu) << (8 * c);
+        }
+    }
+    st_nt(scales + ((size_t)(col0 / 128) * bt + 4 * p.group + tb) * 512 + 16 * a, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+// Column-wise quantization with a device-resident per-tensor amax, narrow lane tiles (cols % 4 == 0).  The Philox
+// words are generated while the loads are in flight and parked in LDS; each block's codes and scale replace its
+// words; after one workgroup barrier the output rows are written.  (Per-row g needs two divisions per block, whose
+// temporaries do not fit the 64 registers; it keeps the wide-tile kernel.)
+template <int MODE>
+__global__ void __launch_bounds__(kColThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+k_quant_colwise4(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, uint32_t nrb, FastDiv ns,
+                 const float* __restrict__ amax, uint32_t sign_mask, RngArgs rng, uint8_t* __restrict__ codes,
+                 uint8_t* __restrict__ scales, float* __restrict__ gout, uint32_t tiled) {
+    constexpr bool SR = MODE != kRN;
+    constexpr bool RHT = MODE == kRHTSR;
+    __shared__ Col4Stash st;
+    __shared__ RTable tab;
+    const float g = global_scale(amax[0]);
+    const Divisor d6 = make_divisor_uniform(6.0f * g);
+    if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
+    fill_rtable<RHT>(tab, g);
+    const Col4Pos pos = col4_position(nrb, ns, blockIdx.x, !tiled);
+    const uint32_t wave = threadIdx.x >> 6;
+    if (pos.rb < nrb && pos.c4 < cols) {
+        uint2 v[16];
+        load_col4_tile(x, cols, pos, v);
+        if (SR) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const Rand4 r = block_rand_inv(rng, (pos.c4 + j) * nrb + pos.rb);
+                st.e[wave][j * 64 + pos.lane] = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
+                __builtin_amdgcn_sched_barrier(0);   // one call at a time: the tile's registers are in flight
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint4& slot = st.e[wave][j * 64 + pos.lane];
+            const LdsRand inv{&slot};
+            float w[16];
+            widen_col4_block<RHT>(v, j, sign_mask, w);
+            uint32_t lo, hi, sb;
+            quantize_block<SR, RHT>(w, d6, TableMul{tab}, inv, lo, hi, sb);
+            slot = make_uint4(lo, hi, sb, 0u);
+            __builtin_amdgcn_sched_barrier(0);   // one block at a time bounds the live registers
+        }
+    }
+    __syncthreads();
+    col4_write_codes(st, pos, rows, cols, nrb, codes);
+    if (tiled) col4_write_scales_tiled(st, pos, cols, nrb, scales);
+    else col4_write_scales_rows(st, pos, cols, nrb, scales);
+}
+
+// ------------------------------------------------------------------------------------------------------------
 // Single-read amax + column-wise 1x16 quantization of a tensor that the chip can hold: every workgroup keeps its
 // tile in registers, publishes its tile maximum in a slot of its own, waits until every workgroup has published,
 // reduces the slots to the tensor amax and quantizes the tile it still holds.  The tensor is read from HBM once
@@ -1125,35 +1285,47 @@ __device__ __forceinline__ uint64_t* slot_copy(const Exchange& ex, uint32_t copy
     return ex.region + (size_t)copy * kFusedMaxGrid;
 }
 
+// Copy `copy` of this workgroup's own slot (the workgroup index taken as a scalar, so that the address stays a
+// scalar base plus the lane's copy offset).
+__device__ __forceinline__ uint64_t* own_slot(const Exchange& ex, uint32_t copy) {
+    return ex.region + __builtin_amdgcn_readfirstlane(blockIdx.x) + (size_t)copy * kFusedMaxGrid;
+}
+
 // The first action of a single-read kernel: this workgroup's slot says it has started.
 __device__ __forceinline__ void announce(const Exchange& ex) {
     if (threadIdx.x < kSlotCopies)
-        __hip_atomic_store(slot_copy(ex, threadIdx.x) + blockIdx.x, ((uint64_t)ex.epoch << 32) | kArrived,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(own_slot(ex, threadIdx.x), ((uint64_t)ex.epoch << 32) | kArrived, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The cross-workgroup step of the single-read kernels (1024-thread workgroups).  The workgroup maximum of mbits
-// (magnitude bits) goes to this workgroup's slot (kept in s_own for release_slot).  Wave 0 then reads the slots of
-// every workgroup (lane l watches slots l + 64 k, four loads in flight together: each read is a round trip to
-// memory, since the slots are shared by all XCDs; a slot once seen with its maximum is not read again), reduces them
-// and, when none is missing, fills tab for g = amax / 2688, while the other waves wait at the one barrier that
-// follows.  Returns the maximum over the slots seen, equal in every thread; missing[l] (l < 64) gets bit k set for
-// each slot l + 64 k not seen, and nmissing (uniform) their count (then tab is not filled).  Uses red[16].
-template <bool RHT>
+// (magnitude bits) goes to this workgroup's slot (kept in s_own for release_slot).  Every wave then runs between()
+// (work that needs neither the amax nor the tile, e.g. the random words, overlapping the wait), and wave 0 reads the
+// slots of every workgroup (lane l watches slots l + 64 k, up to eight loads in flight together: each read is a round
+// trip to memory, since the slots are shared by all XCDs; a slot once seen with its maximum is not read again),
+// reduces them and, when none is missing, fills tab for g = amax / 2688, while the other waves wait at the one
+// barrier that follows.  Returns the maximum over the slots seen, equal in every thread; missing[l] (l < 64) gets
+// bit k set for each slot l + 64 k not seen, and nmissing (uniform) their count (then tab is not filled).  Uses
+// red[16].
+template <bool RHT, typename Between>
 __device__ uint32_t exchange_max(uint32_t mbits, const Exchange& ex, uint32_t* red, uint32_t* missing,
-                                 uint32_t* s_own, RTable& tab, uint32_t& nmissing) {
+                                 uint32_t* s_own, RTable& tab, uint32_t& nmissing, const Between& between) {
     __shared__ uint32_t s_max, s_nmiss;
     const uint32_t lane = threadIdx.x & 63u;
     mbits = wave_max(mbits);
     if (lane == 0) red[threadIdx.x >> 6] = mbits;
     __syncthreads();
+    uint32_t m = 0;
     if (threadIdx.x < 64) {
-        uint32_t m = wave_max(lane < kColRB ? red[lane] : 0u);
+        m = wave_max(lane < kColRB ? red[lane] : 0u);
         if (lane == 0) *s_own = m;
         if (lane < kSlotCopies)
-            __hip_atomic_store(slot_copy(ex, lane) + blockIdx.x, ((uint64_t)ex.epoch << 32) | m, __ATOMIC_RELAXED,
+            __hip_atomic_store(own_slot(ex, lane), ((uint64_t)ex.epoch << 32) | m, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-        const uint64_t* copy = slot_copy(ex, blockIdx.x % kSlotCopies);
+    }
+    between();
+    if (threadIdx.x < 64) {
+        const uint64_t* copy = slot_copy(ex, __builtin_amdgcn_readfirstlane(blockIdx.x) % kSlotCopies);
         const uint32_t nk = (gridDim.x + 63) / 64;   // slots per lane, <= 32
         uint32_t pending = 0, absent = 0;            // bit k: slot lane + 64 k not seen yet / last read foreign
         for (uint32_t k = 0; k < nk; ++k)
@@ -1161,17 +1333,17 @@ __device__ uint32_t exchange_max(uint32_t mbits, const Exchange& ex, uint32_t* r
         m = 0;
         const uint64_t t0 = wall_clock64();
         while (true) {
-            for (uint32_t k0 = 0; k0 < nk; k0 += 4) {
-                uint64_t sv[4];
+            for (uint32_t k0 = 0; k0 < nk; k0 += 8) {
+                uint64_t sv[8];
 #pragma unroll
-                for (uint32_t kk = 0; kk < 4; ++kk) {
+                for (uint32_t kk = 0; kk < 8; ++kk) {
                     const uint32_t k = k0 + kk;
                     sv[kk] = (k < nk && ((pending >> k) & 1u))
                                  ? __hip_atomic_load(&copy[lane + 64 * k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                  : 0ull;
                 }
 #pragma unroll
-                for (uint32_t kk = 0; kk < 4; ++kk) {
+                for (uint32_t kk = 0; kk < 8; ++kk) {
                     const uint32_t k = k0 + kk;
                     if (k < nk && ((pending >> k) & 1u)) {
                         const bool ours = (uint32_t)(sv[kk] >> 32) == ex.epoch;
@@ -1209,6 +1381,12 @@ __device__ uint32_t exchange_max(uint32_t mbits, const Exchange& ex, uint32_t* r
     return __builtin_amdgcn_readfirstlane(s_max);
 }
 
+template <bool RHT>
+__device__ uint32_t exchange_max(uint32_t mbits, const Exchange& ex, uint32_t* red, uint32_t* missing,
+                                 uint32_t* s_own, RTable& tab, uint32_t& nmissing) {
+    return exchange_max<RHT>(mbits, ex, red, missing, s_own, tab, nmissing, [] {});
+}
+
 // Whether slot s was missing in the exchange (missing as written by exchange_max).
 __device__ __forceinline__ bool slot_missing(const uint32_t* missing, uint32_t s) {
     return (missing[s & 63u] >> (s >> 6)) & 1u;
@@ -1217,26 +1395,33 @@ __device__ __forceinline__ bool slot_missing(const uint32_t* missing, uint32_t s
 // Clears this workgroup's slot if it still holds this launch's value: the last action of a single-read kernel
 // (every other workgroup of the launch has read the slot by then, or has stopped waiting and taken the slow route).
 __device__ __forceinline__ void release_slot(const Exchange& ex, uint32_t own) {
-    if (threadIdx.x < kSlotCopies) {
+    uint32_t copy = threadIdx.x;
+    asm volatile("" : "+v"(copy));   // formed here, not kept in a register from the start of the kernel
+    if (copy < kSlotCopies) {
         uint64_t expect = ((uint64_t)ex.epoch << 32) | own;
-        __hip_atomic_compare_exchange_strong(slot_copy(ex, threadIdx.x) + blockIdx.x, &expect, 0ull,
-                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_compare_exchange_strong(own_slot(ex, copy), &expect, 0ull, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
-// The maximum (magnitude bits) over this wave's piece of column-wise tile s: row-block 16 group + wave of the tile's
-// strip, as workgroup s loads it (tiled selects the tile order of the tiled-scale launch).  v is used as scratch.
+// ------------------------------------------------------------------------------------------------------------
+// Single-read amax + column-wise quantization with narrow lane tiles (16 rows x 4 columns per lane, cols % 4 == 0):
+// two 1024-thread workgroups per CU, 8 waves per SIMD, so a tensor of up to 512 tiles of 16 row-blocks x 256 columns
+// (8192 x 4096 on MI355X) stays in registers.  Phase 2 is bound by VALU issue, which twice the waves per SIMD issue
+// faster; the block maxima are recomputed there (six instructions per block) rather than held in registers.
+// Codes leave in two groups of two column blocks (each after a barrier), so the first group's stores overlap the
+// second group's arithmetic; the scales leave at the end.
 template <bool RHT>
-__device__ uint32_t tile_max_colwise(const uint16_t* x, uint32_t cols, const ColGrid& cg, uint32_t s, bool tiled,
-                                     uint32_t sign_mask, uint4 (&v)[16]) {
-    const ColPos p = tiled ? col_position(cg, s) : col_position_octets(cg, s);
+__device__ uint32_t tile_max_col4(const uint16_t* x, uint32_t cols, uint32_t nrb, const FastDiv& ns, uint32_t t,
+                                  bool tiled, uint32_t sign_mask, uint2 (&v)[16]) {
+    const Col4Pos p = col4_position(nrb, ns, t, !tiled);
     uint32_t m = 0;
-    if (p.rb < cg.nrb && p.c8 < cols) {
-        load_col_tile(x, cols, p, v);
+    if (p.rb < nrb && p.c4 < cols) {
+        load_col4_tile(x, cols, p, v);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {   // one block at a time: this runs with the caller's state live
+        for (int j = 0; j < 4; ++j) {
             float w[16];
-            widen_col_block<RHT>(v, j, sign_mask, w);
+            widen_col4_block<RHT>(v, j, sign_mask, w);
             const float bmax = absmax16(w);
             m = umax(m, as_u(RHT ? 0.25f * bmax : bmax) & 0x7FFFFFFFu);
         }
@@ -1244,66 +1429,89 @@ __device__ uint32_t tile_max_colwise(const uint16_t* x, uint32_t cols, const Col
     return m;
 }
 
-constexpr int kOutGroup = 2;   // column blocks per write-out in phase 2 of the single-read kernel
+// The staged codes of column blocks 2 h and 2 h + 1 of every lane (h = 0, 1): output rows strip * 256 + 4 l + 2 h + b
+// (b = 0, 1) for l < 64; thread t takes row 2 (t / 16) + (t / 8) % 2 of that set... i.e. 8 consecutive threads write
+// one output row's 16 row-blocks (128 contiguous bytes).
+__device__ __forceinline__ void col4_write_codes_half(const Col4Stash& st, const Col4Pos& p, uint32_t rows,
+                                                      uint32_t cols, uint32_t nrb, uint32_t h,
+                                                      uint8_t* __restrict__ codes) {
+    const uint32_t nr = min((uint32_t)kColRB, nrb - p.group * kColRB);
+    const uint32_t q = threadIdx.x & 7u, rb0 = p.group * kColRB + 2 * q;
+    const uint32_t r = threadIdx.x >> 3;                 // 0..127: lane r / 2, block 2 h + r % 2
+    const uint32_t cl = 4 * (r >> 1) + 2 * h + (r & 1u), c = p.strip * kStrip4 + cl;
+    if (c >= cols || 2 * q >= nr) return;
+    const uint4 a = col4_entry(st, 2 * q, cl);
+    uint8_t* dst = codes + (size_t)c * (rows >> 1) + 8 * (size_t)rb0;
+    if (2 * q + 1 < nr) {
+        const uint4 b = col4_entry(st, 2 * q + 1, cl);
+        if ((rows & 31u) == 0) {
+            st_nt(dst, make_uint4(a.x, a.y, b.x, b.y));
+        } else {
+            st_nt(dst, make_uint2(a.x, a.y));
+            st_nt(dst + 8, make_uint2(b.x, b.y));
+        }
+    } else {
+        st_nt(dst, make_uint2(a.x, a.y));
+    }
+}
 
 template <int MODE>
-__global__ void __launch_bounds__(kColThreads)
-k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColGrid cg, uint32_t sign_mask,
-                     RngArgs rng, float* __restrict__ amax_out, uint8_t* __restrict__ codes,
-                     uint8_t* __restrict__ scales, float* __restrict__ gout, Exchange ex, uint32_t tiled) {
+__global__ void __launch_bounds__(kColThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+k_amax_quant_colwise4(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, uint32_t nrb, FastDiv ns,
+                      uint32_t sign_mask, RngArgs rng, float* __restrict__ amax_out, uint8_t* __restrict__ codes,
+                      uint8_t* __restrict__ scales, float* __restrict__ gout, Exchange ex, uint32_t tiled) {
     constexpr bool SR = MODE != kRN;
     constexpr bool RHT = MODE == kRHTSR;
-    __shared__ ColStash st;
+    __shared__ Col4Stash st;
     __shared__ RTable tab;
     __shared__ uint32_t red[kColRB], missing[64], s_own;
     announce(ex);
-    // row-major scales: row groups by octets on one XCD (measured 30.5 -> 29.7 us at 8192 x 4096); tiled scales
-    // are whole 2 KiB runs and do better in the usual order (28.6 against 29.4 us)
-    const ColPos pos = tiled ? col_position(cg, blockIdx.x) : col_position_octets(cg, blockIdx.x);
+    const Col4Pos pos = col4_position(nrb, ns, blockIdx.x, !tiled);
     const uint32_t wave = threadIdx.x >> 6;
-    const bool active = pos.rb < cg.nrb && pos.c8 < cols;
-    uint4 v[16];
-    float bm[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // block maxima of the transformed (RHT) or plain values
+    const bool active = pos.rb < nrb && pos.c4 < cols;
+    uint2 v[16];
     uint32_t mbits = 0;
     if (active) {
-        load_col_tile(x, cols, pos, v);
-        // the random words of the 8 blocks, generated while the loads are in flight, parked in LDS
-        if (SR) {
+        load_col4_tile(x, cols, pos, v);
+        if (RHT) flip_col4_tile(v, sign_mask);   // the random signs once, on the packed words
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const Rand4 r = block_rand_inv(rng, (pos.c8 + j) * cg.nrb + pos.rb);
-                st.e[wave][j * 64 + pos.lane] = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
+        for (int j = 0; j < 4; ++j) {
+            float w[16];
+            widen_col4_block<RHT>(v, j, 0u, w);
+            const float bmax = absmax16(w);
+            mbits = umax(mbits, as_u(RHT ? 0.25f * bmax : bmax) & 0x7FFFFFFFu);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // the tile stays in registers: keep the compiler from carrying widened values over the wait instead
+#pragma unroll
+    for (int k = 0; k < 16; ++k) asm volatile("" : "+v"(v[k].x), "+v"(v[k].y));
+    uint32_t nmiss;
+    // the random words of the 4 blocks, generated while the workgroups wait for each other's maxima, parked in LDS
+    uint32_t abits = exchange_max<RHT>(mbits, ex, red, missing, &s_own, tab, nmiss, [&] {
+        if (SR && active) {
+            const Col4Pos p = col4_at(pos.group, pos.strip);   // formed here rather than held since the start
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const Rand4 r = block_rand_inv(rng, (p.c4 + j) * nrb + p.rb);
+                st.e[wave][j * 64 + p.lane] = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            float wp[2][16];
-            widen_col_pair<RHT>(v, p, sign_mask, wp[0], wp[1]);
-            bm[2 * p] = absmax16(wp[0]);
-            bm[2 * p + 1] = absmax16(wp[1]);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) mbits = umax(mbits, as_u(RHT ? 0.25f * bm[j] : bm[j]) & 0x7FFFFFFFu);
-    }
-    // the tile stays in registers: keep the compiler from carrying the widened values over the wait instead
-#pragma unroll
-    for (int k = 0; k < 16; ++k) asm volatile("" : "+v"(v[k].x), "+v"(v[k].y), "+v"(v[k].z), "+v"(v[k].w));
-    uint32_t nmiss;
-    uint32_t abits = exchange_max<RHT>(mbits, ex, red, missing, &s_own, tab, nmiss);
+    });
     if (nmiss) {
         // slow route: the maxima of the tiles whose slots were not seen, from the tensor, then the own tile again
         __shared__ uint32_t s_bits;
         uint32_t mm = 0;
         for (uint32_t t = 0; t < gridDim.x; ++t)
-            if (slot_missing(missing, t)) mm = umax(mm, tile_max_colwise<RHT>(x, cols, cg, t, tiled, sign_mask, v));
+            if (slot_missing(missing, t)) mm = umax(mm, tile_max_col4<RHT>(x, cols, nrb, ns, t, tiled, sign_mask, v));
         mm = block_max<kColRB>(mm, red);
         if (threadIdx.x == 0) s_bits = umax(mm, abits);
         if (active) {
-            load_col_tile(x, cols, pos, v);
-            // wait for the reloaded tile here: left pending, the wait would land in phase 2 on the common path,
-            // where it also waits for the write-out stores
+            load_col4_tile(x, cols, col4_at(pos.group, pos.strip), v);
+            if (RHT) flip_col4_tile(v, sign_mask);
 #pragma unroll
-            for (int k = 0; k < 16; ++k) asm volatile("" : "+v"(v[k].x), "+v"(v[k].y), "+v"(v[k].z), "+v"(v[k].w));
+            for (int k = 0; k < 16; ++k) asm volatile("" : "+v"(v[k].x), "+v"(v[k].y));
         }
         __syncthreads();
         abits = __builtin_amdgcn_readfirstlane(s_bits);
@@ -1316,33 +1524,30 @@ k_amax_quant_colwise(const uint16_t* __restrict__ x, uint32_t rows, uint32_t col
         amax_out[0] = amax;
         gout[0] = g;
     }
-    // kOutGroup blocks at a time: quantize, then (after a barrier) write them out, so that the stores of one group
-    // overlap the arithmetic of the next.
+    uint32_t ln = threadIdx.x & 63u;
+    asm volatile("" : "+v"(ln));   // formed after the wait, not held across it
 #pragma unroll
-    for (int jg = 0; jg < 8 / kOutGroup; ++jg) {
+    for (int h = 0; h < 2; ++h) {
         if (active) {
 #pragma unroll
-            for (int jj = 0; jj < kOutGroup; ++jj) {
-                const int j = kOutGroup * jg + jj;
-                uint4& slot = st.e[wave][j * 64 + pos.lane];
-                Rand4 inv{{0, 0, 0, 0}};
-                if (SR) {
-                    const uint4 r = slot;
-                    inv = Rand4{{r.x, r.y, r.z, r.w}};
-                }
+            for (int jj = 0; jj < 2; ++jj) {
+                const int j = 2 * h + jj;
+                uint4& slot = st.e[wave][j * 64 + ln];
+                const LdsRand inv{&slot};
                 float w[16];
-                widen_col_block<RHT>(v, j, sign_mask, w);
+                widen_col4_block<RHT>(v, j, 0u, w);   // signs already applied
                 uint32_t lo, hi, sb;
-                quantize_block_m<SR, RHT>(w, bm[j], d6, TableMul{tab}, inv, lo, hi, sb);
+                quantize_block<SR, RHT>(w, d6, TableMul{tab}, inv, lo, hi, sb);
                 slot = make_uint4(lo, hi, sb, 0u);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         __syncthreads();
-        col_write_out_group<kOutGroup>(st, pos, rows, cols, cg.nrb, jg, codes, scales, true);
+        col4_write_codes_half(st, col4_at(pos.group, pos.strip), rows, cols, nrb, h, codes);
     }
-    // every block's scale is in LDS since the last barrier
-    if (tiled) col_write_scales_tiled(st, pos, cols, cg.nrb, scales);
-    else col_write_scales_rows(st, pos, cols, cg.nrb, scales);
+    const Col4Pos wp = col4_at(pos.group, pos.strip);
+    if (tiled) col4_write_scales_tiled(st, wp, cols, nrb, scales);
+    else col4_write_scales_rows(st, wp, cols, nrb, scales);
     release_slot(ex, s_own);
 }
 
@@ -2083,7 +2288,7 @@ k_amax_rowwise_rows(const uint4* __restrict__ x, uint32_t rows, uint32_t blocks_
     amax_rowwise_rows_wg<RHT, F32>(x, rows, blocks_per_row, sign_mask, amax_bits, blockIdx.x, gridDim.x, lds);
 }
 
-// Column-wise (V = X^T), same workgroup layout as k_amax_quant_colwise (one row-block per wave).  Per tensor: one
+// Column-wise (V = X^T): a workgroup of 16 row-blocks x 512 columns, one row-block per wave, 8 columns per lane.  Per tensor: one
 // publish per workgroup.  Per row
 // of V (= per column of X): the waves' column maxima are combined in LDS, then one atomic per column.
 template <bool RHT, bool PER_ROW>
@@ -2496,6 +2701,19 @@ hipError_t launch_quant_1x16(const uint16_t* x, int64_t rows, int64_t cols, bool
             case kRHTSR: if (per_row) NVFP4_ROW(kRHTSR, true); else NVFP4_ROW(kRHTSR, false); break;
         }
 #undef NVFP4_ROW
+    } else if (!per_row && cols % 4 == 0) {
+        const uint32_t nrb = (uint32_t)(rows / 16), nstrips = (uint32_t)((cols + kStrip4 - 1) / kStrip4);
+        const uint32_t grid = ((nrb + kColRB - 1) / kColRB) * nstrips;
+        const FastDiv ns = make_fastdiv(nstrips);
+#define NVFP4_COL4(M)                                                                                          \
+    k_quant_colwise4<M><<<grid, kColThreads, 0, stream>>>(x, (uint32_t)rows, (uint32_t)cols, nrb, ns, amax,      \
+                                                          sign_mask, ra, codes, scales, g, tiled ? 1u : 0u)
+        switch (mode) {
+            case kRN: NVFP4_COL4(kRN); break;
+            case kSR: NVFP4_COL4(kSR); break;
+            case kRHTSR: NVFP4_COL4(kRHTSR); break;
+        }
+#undef NVFP4_COL4
     } else {
         uint32_t grid;
         const ColGrid w = col_grid(rows, cols, grid);
@@ -2561,22 +2779,23 @@ hipError_t next_exchange(Exchange* ex) {
 hipError_t launch_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, bool colwise, Mode mode, uint32_t sign_mask,
                              Philox rng, float* amax, uint8_t* codes, uint8_t* scales, float* g, hipStream_t stream,
                              bool tiled) {
-    if (rows > 0 && cols > 0 && colwise) {
-        uint32_t grid;
-        const ColGrid w = col_grid(rows, cols, grid);
-        // one 1024-thread workgroup per CU (the registers allow no second one), all resident at once
-        if (grid <= (uint32_t)cu_count() && grid <= kFusedMaxGrid) {
-            uint32_t r = (uint32_t)rows, c = (uint32_t)cols;
+    if (rows > 0 && cols > 0 && colwise && cols % 4 == 0) {
+        const uint32_t nrb = (uint32_t)(rows / 16), nstrips = (uint32_t)((cols + kStrip4 - 1) / kStrip4);
+        const uint32_t grid = ((nrb + kColRB - 1) / kColRB) * nstrips;
+        // two 1024-thread workgroups per CU (registers and LDS allow no third), all resident at once
+        if (grid <= 2u * (uint32_t)cu_count() && grid <= kFusedMaxGrid) {
+            uint32_t r = (uint32_t)rows, c = (uint32_t)cols, nr = nrb;
+            FastDiv ns = make_fastdiv(nstrips);
             RngArgs ra = rng_args(rng);
             Exchange ex;
             const hipError_t e = next_exchange(&ex);
             if (e != hipSuccess) return e;
             uint32_t tl = tiled ? 1u : 0u;
-            void* args[] = {(void*)&x, &r, &c, (void*)&w, &sign_mask, &ra, (void*)&amax, (void*)&codes, (void*)&scales,
+            void* args[] = {(void*)&x, &r, &c, &nr, &ns, &sign_mask, &ra, (void*)&amax, (void*)&codes, (void*)&scales,
                             (void*)&g, &ex, &tl};
-            const void* fn = mode == kRN ? (const void*)k_amax_quant_colwise<kRN>
-                             : mode == kSR ? (const void*)k_amax_quant_colwise<kSR>
-                                           : (const void*)k_amax_quant_colwise<kRHTSR>;
+            const void* fn = mode == kRN ? (const void*)k_amax_quant_colwise4<kRN>
+                             : mode == kSR ? (const void*)k_amax_quant_colwise4<kSR>
+                                           : (const void*)k_amax_quant_colwise4<kRHTSR>;
             return hipLaunchKernel(fn, dim3(grid), dim3(kColThreads), args, 0, stream);
         }
     }

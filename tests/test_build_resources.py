@@ -22,7 +22,8 @@ def kernels():
 
 def test_every_kernel_is_listed():
     names = " ".join(r["name"] for r in kernels())
-    for k in ("k_amax_quant_colwise", "k_amax_quant_rowwise", "k_quant_colwise", "k_quant_rowwise", "k_quant_16x16",
+    for k in ("k_amax_quant_colwise4", "k_amax_quant_rowwise", "k_quant_colwise4", "k_quant_colwise", "k_quant_rowwise",
+              "k_quant_16x16",
               "k_quant_4o6_rows", "k_quant_4o6_tensor", "k_dequantize", "k_amax_colwise", "k_amax_rowwise_tensor",
               "k_quant_4o6_16x16", "k_swizzle_scales", "k_quant_rowwise_tiled", "k_dequantize_fused",
               "k_quant_grouped", "k_quant_4o6_grouped"):
@@ -37,8 +38,20 @@ def test_no_spills_to_memory():
 
 def test_tile_kernels_keep_four_waves_per_simd():
     for r in kernels():
-        if any(k in r["name"] for k in ("k_amax_quant_colwise", "k_quant_colwise", "k_quant_16x16")):
+        if any(k in r["name"] for k in ("k_quant_colwiseI", "k_quant_16x16")):
             assert int(r["vgpr"]) <= 128 and int(r["occupancy"]) >= 4, r
+
+
+def test_narrow_column_kernels_keep_eight_waves_per_simd():
+    """The narrow-tile column-wise kernels hold 16 rows x 4 columns per lane in 64 registers so that two 1024-thread
+    workgroups fit a CU; the single-read launcher relies on it (up to two workgroups per CU, all resident)."""
+    seen = 0
+    for r in kernels():
+        if "k_quant_colwise4" in r["name"] or "k_amax_quant_colwise4" in r["name"]:
+            assert int(r["vgpr"]) <= 64 and int(r["occupancy"]) >= 8, r
+            assert int(r["lds"]) <= 80 * 1024, r
+            seen += 1
+    assert seen == 6
 
 
 def test_looping_grids_fit_their_occupancy():
