@@ -148,7 +148,11 @@ nvfp4_status nvfp4_quantize_rht_sr(const uint16_t* x, int64_t rows, int64_t cols
  *   256-row x 256-column tiles per CU, row-wise up to 8192 blocks per CU (8192 x 4096 either way on MI355X).
  *   Each workgroup keeps its share in registers, publishes its maximum in a slot and waits for every other
  *   workgroup's; larger tensors run the two passes.
- *   The exchange slots are a 2 MiB array in the library's own device memory (one per GPU).  Each launch tags its slots with a fresh 32-bit epoch and takes one of the 8 regions in turn.  Calls that overlap
+ *   For callers that cannot allocate (code under HIP graph capture, tight serving loops, harnesses that forbid
+ *   hipMalloc): this call allocates nothing.  Its only scratch is the exchange slots, a 2 MiB array in the library's
+ *   own device memory (one per GPU, held until the process ends; 8 regions of 16 copies of 2048 slots), whose
+ *   address the library looks up on a device's first call; launches never need more, whatever the tensor size.
+ *   Each launch tags its slots with a fresh 32-bit epoch and takes one of the 8 regions in turn.  Calls that overlap
  *   on one GPU (other streams, graph replays) may share a region: a workgroup never takes a slot that carries
  *   another launch's epoch, so sharing costs time, never correctness.  The wait is bounded: after 100 us with some
  *   workgroup of the launch not yet started (not all resident, e.g. CUs held by other work), or after 2 ms in any
