@@ -103,7 +103,7 @@ typedef struct {
  *   gmode NVFP4_G_PER_TENSOR writes amax[0], NVFP4_G_PER_ROW writes amax[Rv] (one per row of V);
  *   use_rht != 0: the maximum is taken over the Hadamard-transformed blocks (same sign_mask as the quantize call).
  *   Shape: the same rules as the quantize call it feeds: row-wise cols % 16 == 0; column-wise rows % 16 == 0
- *   and cols % 8 == 0. */
+ *   (any cols below 2^25). */
 nvfp4_status nvfp4_amax(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_orient orient, nvfp4_gmode gmode,
                         int use_rht, uint16_t sign_mask, float* amax, void* stream);
 
@@ -115,8 +115,9 @@ nvfp4_status nvfp4_amax(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_ori
  *     COLWISE writes W^T to *col_out ([cols, rows/2], [cols, rows/16]), BOTH writes both from one read of X.
  *     Each tile's scale is repeated in the 1x16 scale layout of each orientation (16 entries per tile).
  *   amax: [1] or [Rv] device floats from nvfp4_amax (without RHT).
- *   Shape: 1x16 row-wise needs cols % 16 == 0; column-wise rows % 16 == 0 and cols % 8 == 0; 16x16 needs both
- *   rows and cols multiples of 16.  Unsupported: 16x16 with per-row g; 1x16 with BOTH. */
+ *   Shape: 1x16 row-wise needs cols % 16 == 0; column-wise rows % 16 == 0 (any cols below 2^25: the blocked
+ *   dimension is the only one the method constrains); 16x16 needs both rows and cols multiples of 16.
+ *   Unsupported: 16x16 with per-row g; 1x16 with BOTH. */
 nvfp4_status nvfp4_quantize_rn(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_block block,
                                nvfp4_orient orient, nvfp4_gmode gmode, const float* amax, const nvfp4_out* row_out,
                                const nvfp4_out* col_out, void* stream);

@@ -36,7 +36,7 @@ nvfp4_status check_sizes(int64_t rows, int64_t cols) {
 // Shape rules of a 1x16 quantization (and of the amax that feeds it).
 nvfp4_status check_view(int64_t rows, int64_t cols, nvfp4_orient orient) {
     if (orient == NVFP4_ROWWISE) return (cols % 16) ? NVFP4_ERR_SHAPE : NVFP4_OK;
-    if (orient == NVFP4_COLWISE) return (rows % 16 || cols % 8 || cols >= kMaxColwiseCols) ? NVFP4_ERR_SHAPE : NVFP4_OK;
+    if (orient == NVFP4_COLWISE) return (rows % 16 || cols >= kMaxColwiseCols) ? NVFP4_ERR_SHAPE : NVFP4_OK;
     return NVFP4_ERR_UNSUPPORTED;
 }
 

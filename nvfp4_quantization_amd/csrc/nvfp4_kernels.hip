@@ -2335,6 +2335,104 @@ k_amax_colwise(const uint16_t* __restrict__ x, uint32_t cols, ColGrid cg, uint32
 }
 
 // ------------------------------------------------------------------------------------------------------------
+// Column-wise kernels for any column count (rows % 16 == 0 is all the method needs).  The tiled kernels above read
+// 4 or 8 columns per load and so need every row to start on an 8- or 16-byte boundary; here a thread owns one
+// column block (16 rows x 1 column) and the 64 lanes of a wave take 64 consecutive columns, so each of its 16 row
+// loads still reads 128 contiguous bytes.  A workgroup covers 256 columns of up to kAnyRB row-blocks: workgroup b
+// takes column chunk b % nchunks of row-block group b / nchunks.
+// ------------------------------------------------------------------------------------------------------------
+constexpr int kAnyThreads = 256;
+constexpr uint32_t kAnyRB = 16;
+
+// The 16 values of column c in row-block rb (sign-flipped and transformed with the RHT).
+template <bool RHT>
+__device__ __forceinline__ void load_col_block_any(const uint16_t* __restrict__ x, uint32_t cols, uint32_t rb,
+                                                   uint32_t c, uint32_t mask, float (&w)[16]) {
+    const uint16_t* p = x + (size_t)(16 * rb) * cols + c;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const uint32_t b = __builtin_nontemporal_load(p + (size_t)k * cols);
+        w[k] = as_f((b << 16) ^ (RHT ? flip_bit(mask, k) : 0u));
+    }
+    if (RHT) fwht16(w);
+}
+
+// Byte offset of view row r, scale column b in the tiled scale layout of the FP4 GEMM (tiles of 128 rows x 4 scale
+// columns, each a [32][4][4] byte array: byte 16 a + 4 i + j = row 32 i + a, scale column j; bt tiles per row tile).
+__device__ __forceinline__ size_t tiled_scale_offset(uint32_t r, uint32_t b, uint32_t bt) {
+    return ((size_t)(r >> 7) * bt + (b >> 2)) * 512 + 16 * (r & 31u) + 4 * ((r >> 5) & 3u) + (b & 3u);
+}
+
+// Column-wise quantization, any column count.  The tiled scale layout is padded to whole tiles (view rows up to a
+// multiple of 128, scale columns up to a multiple of 4); the grid spans that padding and writes its bytes as zero.
+template <int MODE, bool PER_ROW>
+__global__ void __launch_bounds__(kAnyThreads)
+k_quant_colwise_any(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, uint32_t nchunks,
+                    const float* __restrict__ amax, uint32_t sign_mask, RngArgs rng, uint8_t* __restrict__ codes,
+                    uint8_t* __restrict__ scales, float* __restrict__ gout, uint32_t tiled) {
+    constexpr bool SR = MODE != kRN;
+    constexpr bool RHT = MODE == kRHTSR;
+    __shared__ RTable tab;
+    const uint32_t nrb = rows >> 4, grp = blockIdx.x / nchunks;
+    const uint32_t c = (blockIdx.x - grp * nchunks) * kAnyThreads + threadIdx.x;
+    Divisor d6{};
+    if (!PER_ROW) {
+        const float g = global_scale(amax[0]);
+        d6 = make_divisor_uniform(6.0f * g);
+        if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
+        fill_rtable<RHT>(tab, g);
+    }
+    const uint32_t bt = (nrb + 3) / 4, rb_end = tiled ? 4 * bt : nrb, c_end = tiled ? (cols + 127) & ~127u : cols;
+    if (c >= c_end) return;
+    float gr = 0.0f;
+    if (PER_ROW && c < cols) {
+        gr = global_scale(amax[c]);
+        if (grp == 0) gout[c] = gr;
+    }
+    for (uint32_t rb = grp * kAnyRB; rb < min(rb_end, (grp + 1) * kAnyRB); ++rb) {
+        const size_t so = tiled ? tiled_scale_offset(c, rb, bt) : (size_t)c * nrb + rb;
+        if (c >= cols || rb >= nrb) {                    // padding of the tiled layout
+            scales[so] = 0;
+            continue;
+        }
+        float w[16];
+        load_col_block_any<RHT>(x, cols, rb, c, sign_mask, w);
+        Rand4 inv{{0, 0, 0, 0}};
+        if (SR) inv = block_rand_inv(rng, c * nrb + rb);
+        uint32_t lo, hi, sb;
+        if (PER_ROW) quantize_block<SR, RHT>(w, make_divisor(6.0f * gr), RowMul<RHT>{gr}, inv, lo, hi, sb);
+        else quantize_block<SR, RHT>(w, d6, TableMul{tab}, inv, lo, hi, sb);
+        st_nt(reinterpret_cast<uint2*>(codes + (size_t)c * (rows >> 1) + 8 * (size_t)rb), make_uint2(lo, hi));
+        scales[so] = (uint8_t)sb;
+    }
+}
+
+// Column-wise amax, any column count: the maximum over the thread's blocks, then per column (PER_ROW: the view's
+// rows are the columns) or per tensor.
+template <bool RHT, bool PER_ROW>
+__global__ void __launch_bounds__(kAnyThreads)
+k_amax_colwise_any(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, uint32_t nchunks, uint32_t sign_mask,
+                   uint32_t* __restrict__ amax_bits) {
+    __shared__ uint32_t red[kAnyThreads / 64];
+    const uint32_t nrb = rows >> 4, grp = blockIdx.x / nchunks;
+    const uint32_t c = (blockIdx.x - grp * nchunks) * kAnyThreads + threadIdx.x;
+    uint32_t m = 0;
+    if (c < cols) {
+        for (uint32_t rb = grp * kAnyRB; rb < min(nrb, (grp + 1) * kAnyRB); ++rb) {
+            float w[16];
+            load_col_block_any<RHT>(x, cols, rb, c, sign_mask, w);
+            const float a = absmax16(w);
+            m = umax(m, as_u(RHT ? 0.25f * a : a) & 0x7FFFFFFFu);
+        }
+        if (PER_ROW) atomicMax(amax_bits + c, m);
+    }
+    if (!PER_ROW) {
+        m = block_max<kAnyThreads / 64>(m, red);
+        if (threadIdx.x == 0) publish_max(amax_bits, m);
+    }
+}
+
+// ------------------------------------------------------------------------------------------------------------
 // Single-read amax + row-wise 1x16 quantization (same exchange as the column-wise single-read kernel).  A
 // workgroup owns bpl * 1024 consecutive blocks (bpl <= 8 per lane), lane t of the workgroup blocks base + 1024 j + t,
 // so every load instruction of a wave covers 2 KiB of the tensor with its partner; the tile is held in registers
@@ -2588,6 +2686,23 @@ ColGrid col_grid(int64_t rows, int64_t cols, uint32_t& grid, uint32_t rb = kColR
     return g;
 }
 
+// Grid of the any-column-count kernels: 256-column chunks by groups of kAnyRB row-blocks, over the padded view of
+// the tiled scale layout when `tiled`.
+struct AnyGrid {
+    uint32_t nchunks, grid;
+};
+
+AnyGrid any_grid(int64_t rows, int64_t cols, bool tiled) {
+    const uint32_t nrb = (uint32_t)(rows / 16);
+    const uint32_t rb_end = tiled ? (nrb + 3) / 4 * 4 : nrb;
+    const uint32_t c_end = (uint32_t)(tiled ? (cols + 127) / 128 * 128 : cols);
+    AnyGrid a;
+    a.nchunks = (c_end + kAnyThreads - 1) / kAnyThreads;
+    a.grid = a.nchunks * ((rb_end + kAnyRB - 1) / kAnyRB);
+    if (a.grid == 0) a.grid = 1;
+    return a;
+}
+
 // Grid of a tile-looping column kernel: at most `per_cu` workgroups per CU (all resident), and every workgroup the
 // same number of tiles (448 tiles on 256 CUs: 224 workgroups of 2 tiles rather than two rounds with a partial
 // second).
@@ -2653,6 +2768,15 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, bool colwi
     if (rows == 0 || cols == 0) return hipGetLastError();
     if (!colwise) {
         launch_amax_rowwise(x, rows, cols, per_row, use_rht, false, sign_mask, bits, stream);
+    } else if (cols % 8 != 0) {
+        const AnyGrid a = any_grid(rows, cols, false);
+        const uint32_t r = (uint32_t)rows, c = (uint32_t)cols;
+#define NVFP4_ANY(R, P) k_amax_colwise_any<R, P><<<a.grid, kAnyThreads, 0, stream>>>(x, r, c, a.nchunks, sign_mask, bits)
+        if (use_rht && per_row) NVFP4_ANY(true, true);
+        else if (use_rht) NVFP4_ANY(true, false);
+        else if (per_row) NVFP4_ANY(false, true);
+        else NVFP4_ANY(false, false);
+#undef NVFP4_ANY
     } else {
         uint32_t grid;
         const ColGrid w = col_grid(rows, cols, grid);
@@ -2714,6 +2838,17 @@ hipError_t launch_quant_1x16(const uint16_t* x, int64_t rows, int64_t cols, bool
             case kRHTSR: NVFP4_COL4(kRHTSR); break;
         }
 #undef NVFP4_COL4
+    } else if (cols % 8 != 0) {
+        const AnyGrid a = any_grid(rows, cols, tiled);
+#define NVFP4_ANY(M, P)                                                                                          \
+    k_quant_colwise_any<M, P><<<a.grid, kAnyThreads, 0, stream>>>(x, (uint32_t)rows, (uint32_t)cols, a.nchunks, amax, \
+                                                                  sign_mask, ra, codes, scales, g, tiled ? 1u : 0u)
+        switch (mode) {
+            case kRN: if (per_row) NVFP4_ANY(kRN, true); else NVFP4_ANY(kRN, false); break;
+            case kSR: if (per_row) NVFP4_ANY(kSR, true); else NVFP4_ANY(kSR, false); break;
+            case kRHTSR: if (per_row) NVFP4_ANY(kRHTSR, true); else NVFP4_ANY(kRHTSR, false); break;
+        }
+#undef NVFP4_ANY
     } else {
         uint32_t grid;
         const ColGrid w = col_grid(rows, cols, grid);

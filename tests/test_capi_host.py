@@ -75,7 +75,6 @@ def test_amax_validation(lib):
     assert f(P, -1, 16, 1, 0, 0, 0, P, None) == SHAPE
     assert f(P, 16, 24, 1, 0, 0, 0, P, None) == SHAPE          # row-wise: cols % 16
     assert f(P, 24, 16, 2, 0, 0, 0, P, None) == SHAPE          # column-wise: rows % 16
-    assert f(P, 32, 12, 2, 0, 0, 0, P, None) == SHAPE          # column-wise: cols % 8
     assert f(MIS, 16, 16, 1, 0, 0, 0, P, None) == ALIGN
     assert f(P, 16, 16, 1, 0, 0, 0, P + 2, None) == ALIGN
     assert f(P, 16, 16, 3, 0, 0, 0, P, None) == UNSUP         # BOTH is not an amax view

@@ -48,7 +48,8 @@ def check(x, mode, orient, mask=0x5A3C, seed=0xDEAD_BEEF_0123, offset=3, out=Non
 
 
 @pytest.mark.parametrize("mode", ["rn", "sr", "rht_sr"])
-@pytest.mark.parametrize("shape", [(512, 200), (48, 8), (1040, 72), (16, 520), (2048, 1024), (4096, 1032)])
+@pytest.mark.parametrize("shape", [(512, 200), (48, 8), (1040, 72), (16, 520), (2048, 1024), (4096, 1032),
+                                   (48, 12), (64, 27), (4096, 4100)])
 def test_colwise(mode, shape):
     x = W.lognormal_gradients(*shape, seed=(shape[0] * 5 + shape[1]) & 0xFFFF)
     check(x, mode, Q.COLWISE)

@@ -91,7 +91,9 @@ def check_1x16(x, mode, orient, gmode, mask=0xA53C, seed=0x1234_5678_9ABC, offse
 
 
 SHAPES_ROW = [(256, 1024), (37, 160), (1, 16), (300, 48), (129, 4096)]
-SHAPES_COL = [(512, 200), (48, 8), (1040, 72), (16, 520), (2048, 1024)]
+SHAPES_COL = [(512, 200), (48, 8), (1040, 72), (16, 520), (2048, 1024),
+              # column counts that are not multiples of 8 (odd, single column, ragged 4-column groups)
+              (48, 12), (64, 27), (32, 1), (144, 300), (272, 1001), (4096, 4100)]
 
 
 @pytest.mark.parametrize("mode", ["rn", "sr", "rht_sr"])

@@ -19,7 +19,8 @@ from nvfp4_quantization_amd import workloads as W
 pytestmark = pytest.mark.gpu
 
 ROUNDING = {"rn": (Q.ROUND_RN, O.MODE_RN), "sr": (Q.ROUND_SR, O.MODE_SR), "rht_sr": (Q.ROUND_RHT_SR, O.MODE_RHT_SR)}
-SHAPES = [(512, 200), (48, 8), (80, 136), (1040, 72), (16, 520), (2048, 1024), (272, 1032)]
+SHAPES = [(512, 200), (48, 8), (80, 136), (1040, 72), (16, 520), (2048, 1024), (272, 1032), (48, 12), (64, 27),
+          (144, 300), (272, 1001)]
 
 
 @pytest.fixture(scope="module", autouse=True)
