@@ -23,6 +23,7 @@ _LIB_PATH = os.path.join(_HERE, "libnvfp4_oracle.so")
 ROWWISE, COLWISE = 1, 2
 G_PER_TENSOR, G_PER_ROW = 0, 1
 MODE_RN, MODE_SR, MODE_RHT_SR = 0, 1, 2
+ERR_MSE, ERR_MAE, ERR_MAXABS = 0, 1, 2        # four-over-six error modes (sum of squares, sum of magnitudes, max)
 
 # gcc flags: one IEEE binary32 rounding per operation (no contraction, no fast-math), OpenMP over rows.
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared", "-Wall"]
@@ -79,9 +80,9 @@ def _declare(L: C.CDLL) -> None:
     L.nvo_quantize_1x16.restype = i32
     L.nvo_quantize_16x16.argtypes = [p, i64, i64, p, i64, i64, p, p, p, p, p, p]
     L.nvo_quantize_16x16.restype = i32
-    L.nvo_quantize_4o6.argtypes = [p, i64, i64, i32, p, i64, i64, p, p, p, p]
+    L.nvo_quantize_4o6.argtypes = [p, i64, i64, i32, i32, i32, p, i64, i64, p, p, p, p]
     L.nvo_quantize_4o6.restype = i32
-    L.nvo_quantize_4o6_16x16.argtypes = [p, i64, i64, p, i64, i64, p, p, p, p, p, p, p]
+    L.nvo_quantize_4o6_16x16.argtypes = [p, i64, i64, i32, i32, p, i64, i64, p, p, p, p, p, p, p]
     L.nvo_quantize_4o6_16x16.restype = i32
     L.nvo_dequantize.argtypes = [p, p, p, i64, i64, i32, p]
     L.nvo_dequantize.restype = i32
@@ -90,9 +91,9 @@ def _declare(L: C.CDLL) -> None:
     L.nvo_f32_to_bf16.restype = u16
     L.nvo_dequantize_fused.argtypes = [p, p, p, i64, i64, i32, i32, u16, i32, p]
     L.nvo_dequantize_fused.restype = i32
-    L.nvo_quantize_4o6_f32.argtypes = [p, i64, i64, i32, p, i64, i64, p, p, p, p]
+    L.nvo_quantize_4o6_f32.argtypes = [p, i64, i64, i32, i32, i32, p, i64, i64, p, p, p, p]
     L.nvo_quantize_4o6_f32.restype = i32
-    L.nvo_quantize_4o6_16x16_f32.argtypes = [p, i64, i64, p, i64, i64, p, p, p, p, p, p, p]
+    L.nvo_quantize_4o6_16x16_f32.argtypes = [p, i64, i64, i32, i32, p, i64, i64, p, p, p, p, p, p, p]
     L.nvo_quantize_4o6_16x16_f32.restype = i32
     L.nvo_amax_f32.argtypes = [p, i64, i64, i32, p]
     L.nvo_amax_f32.restype = i32
@@ -267,8 +268,9 @@ def quantize_16x16(x: np.ndarray, amax_arr: np.ndarray, tile_rows: tuple[int, in
 
 
 def quantize_4o6(x: np.ndarray, amax_arr: np.ndarray, gmode: int = G_PER_ROW,
-                 rows_range: tuple[int, int] | None = None):
-    """Returns (codes, scales, g, choice) where choice[r, b] = 1 if map-to-4 was kept."""
+                 rows_range: tuple[int, int] | None = None, err_mode: int = ERR_MSE, bound: int = 448):
+    """Returns (codes, scales, g, choice) where choice[r, b] = 1 if map-to-4 was kept; err_mode ERR_MSE, ERR_MAE or
+    ERR_MAXABS; g = amax / (6 bound)."""
     x = _bits(x)
     rows, cols = x.shape
     a, b = rows_range if rows_range is not None else (0, rows)
@@ -277,12 +279,13 @@ def quantize_4o6(x: np.ndarray, amax_arr: np.ndarray, gmode: int = G_PER_ROW,
     scales = np.zeros((rows, cols // 16), dtype=np.uint8)
     g = np.zeros(rows if gmode == G_PER_ROW else 1, dtype=np.float32)
     choice = np.zeros((rows, cols // 16), dtype=np.uint8)
-    _check(lib().nvo_quantize_4o6(_ptr(x), rows, cols, gmode, _ptr(amax_arr), a, b, _ptr(codes), _ptr(scales),
-                                  _ptr(g), _ptr(choice)), "quantize_4o6")
+    _check(lib().nvo_quantize_4o6(_ptr(x), rows, cols, gmode, err_mode, bound, _ptr(amax_arr), a, b, _ptr(codes),
+                                  _ptr(scales), _ptr(g), _ptr(choice)), "quantize_4o6")
     return codes, scales, g, choice
 
 
-def quantize_4o6_16x16(x: np.ndarray, amax_arr: np.ndarray, tile_rows: tuple[int, int] | None = None):
+def quantize_4o6_16x16(x: np.ndarray, amax_arr: np.ndarray, tile_rows: tuple[int, int] | None = None,
+                       err_mode: int = ERR_MSE, bound: int = 448):
     """Four-over-six with 16x16 tiles (per-tensor g).  Returns ((codes_w, scales_w, g_w), (codes_wt, scales_wt,
     g_wt), choice) with choice[ti, tj] = 1 where map-to-4 was kept."""
     x = _bits(x)
@@ -296,8 +299,9 @@ def quantize_4o6_16x16(x: np.ndarray, amax_arr: np.ndarray, tile_rows: tuple[int
     stt = np.zeros((cols, rows // 16), np.uint8)
     gt = np.zeros(1, np.float32)
     choice = np.zeros((rows // 16, cols // 16), np.uint8)
-    _check(lib().nvo_quantize_4o6_16x16(_ptr(x), rows, cols, _ptr(amax_arr), a, b, _ptr(cw), _ptr(sw), _ptr(gw),
-                                        _ptr(ct), _ptr(stt), _ptr(gt), _ptr(choice)), "quantize_4o6_16x16")
+    _check(lib().nvo_quantize_4o6_16x16(_ptr(x), rows, cols, err_mode, bound, _ptr(amax_arr), a, b, _ptr(cw),
+                                        _ptr(sw), _ptr(gw), _ptr(ct), _ptr(stt), _ptr(gt), _ptr(choice)),
+           "quantize_4o6_16x16")
     return (cw, sw, gw), (ct, stt, gt), choice
 
 
@@ -347,7 +351,8 @@ def amax_f32(x: np.ndarray, gmode: int = G_PER_TENSOR) -> np.ndarray:
     return out
 
 
-def quantize_4o6_f32(x: np.ndarray, amax_arr: np.ndarray, gmode: int = G_PER_ROW):
+def quantize_4o6_f32(x: np.ndarray, amax_arr: np.ndarray, gmode: int = G_PER_ROW, err_mode: int = ERR_MSE,
+                     bound: int = 448):
     """Four-over-six of a float32 array; returns (codes, scales, g, choice) as quantize_4o6."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     rows, cols = x.shape
@@ -356,12 +361,12 @@ def quantize_4o6_f32(x: np.ndarray, amax_arr: np.ndarray, gmode: int = G_PER_ROW
     scales = np.zeros((rows, cols // 16), dtype=np.uint8)
     g = np.zeros(rows if gmode == G_PER_ROW else 1, dtype=np.float32)
     choice = np.zeros((rows, cols // 16), dtype=np.uint8)
-    _check(lib().nvo_quantize_4o6_f32(_ptr(x), rows, cols, gmode, _ptr(amax_arr), 0, rows, _ptr(codes), _ptr(scales),
-                                      _ptr(g), _ptr(choice)), "quantize_4o6_f32")
+    _check(lib().nvo_quantize_4o6_f32(_ptr(x), rows, cols, gmode, err_mode, bound, _ptr(amax_arr), 0, rows,
+                                      _ptr(codes), _ptr(scales), _ptr(g), _ptr(choice)), "quantize_4o6_f32")
     return codes, scales, g, choice
 
 
-def quantize_4o6_16x16_f32(x: np.ndarray, amax_arr: np.ndarray):
+def quantize_4o6_16x16_f32(x: np.ndarray, amax_arr: np.ndarray, err_mode: int = ERR_MSE, bound: int = 448):
     """Four-over-six with 16x16 tiles of a float32 array; returns as quantize_4o6_16x16."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     rows, cols = x.shape
@@ -373,7 +378,8 @@ def quantize_4o6_16x16_f32(x: np.ndarray, amax_arr: np.ndarray):
     stt = np.zeros((cols, rows // 16), dtype=np.uint8)
     gt = np.zeros(1, dtype=np.float32)
     choice = np.zeros((rows // 16, cols // 16), dtype=np.uint8)
-    _check(lib().nvo_quantize_4o6_16x16_f32(_ptr(x), rows, cols, _ptr(amax_arr), 0, rows // 16, _ptr(cw), _ptr(sw),
-                                            _ptr(gw), _ptr(ct), _ptr(stt), _ptr(gt), _ptr(choice)),
+    _check(lib().nvo_quantize_4o6_16x16_f32(_ptr(x), rows, cols, err_mode, bound, _ptr(amax_arr), 0, rows // 16,
+                                            _ptr(cw), _ptr(sw), _ptr(gw), _ptr(ct), _ptr(stt), _ptr(gt),
+                                            _ptr(choice)),
            "quantize_4o6_16x16_f32")
     return (cw, sw, gw), (ct, stt, gt), choice

@@ -458,19 +458,55 @@ int nvo_quantize_16x16(const uint16_t* x, int64_t rows, int64_t cols, const floa
 /* ------------------------------------------------------------------------------------------------------------
  * Four-over-six, row-wise 1x16, round-to-nearest, no RHT, rows [r_begin, r_end).  [P3]: every block is encoded
  * at the standard map-to-6 scale and at a 1.5x larger map-to-4 scale, both candidates are decoded, and the one
- * with the lower error is stored; the width-16 error reduction has a pinned order (a shuffle-down tree).
+ * with the lower error is stored; the width-16 error reduction has a pinned order (a shuffle-down tree); the
+ * recipe's sweep varies an error mode and a bound, which the page names without defining.
  * READINGS: candidate T in {6, 4} uses d_T = fl(T * g) in the block-scale rule above (bamax / (4g) is 1.5x
- * bamax / (6g) in exact arithmetic); decode xh = fl(fl(val(code) * decode(sb_T)) * g); error
- * e_i = fl(d * d) with d = fl(xh_i - x_i) against the binary32 input; the block error is the tree
- * p_i = e_i + e_{i+8} (i < 8), then stride 4, 2, 1; map-to-4 is kept only if its error is strictly lower, so
- * ties and NaN keep map-to-6.  choice[] (optional) receives 1 where map-to-4 was kept.
+ * bamax / (6g) in exact arithmetic); decode xh = fl(fl(val(code) * decode(sb_T)) * g); d_i = fl(xh_i - x_i)
+ * against the binary32 input.  The block error by err_mode:
+ *   NVO_ERR_MSE    e_i = fl(d_i * d_i), summed by the tree p_i = e_i + e_{i+8} (i < 8), then strides 4, 2, 1;
+ *   NVO_ERR_MAE    e_i = |d_i| (exact), summed by the same tree;
+ *   NVO_ERR_MAXABS the largest |d_i| (no rounding, so no order), NaN if any d_i is NaN.
+ * bound B (an integer 1..448) is the E4M3 value the tensor maximum's map-to-6 scale lands on: g = fl(A / (6 B)),
+ * 6 B exact; B = 448 is the standard g = A / 2688, and B = 256 leaves the map-to-4 scale of every block
+ * (at most 1.5 B = 384) below E4M3's 448, where with B = 448 the largest blocks' map-to-4 scales saturate.
+ * Map-to-4 is kept only if its error is strictly lower, so ties and NaN keep map-to-6.  choice[] (optional)
+ * receives 1 where map-to-4 was kept.
  * ---------------------------------------------------------------------------------------------------------- */
+#define NVO_ERR_MSE 0
+#define NVO_ERR_MAE 1
+#define NVO_ERR_MAXABS 2
+
 static float tree_sum16(const float e[16]) {
     float p[16];
     memcpy(p, e, sizeof p);
     for (int s = 8; s >= 1; s /= 2)
         for (int i = 0; i < s; ++i) p[i] = p[i] + p[i + s];
     return p[0];
+}
+
+/* The largest of n magnitudes, NaN if any is NaN. */
+static float max_or_nan(const float* a, int n) {
+    float m = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        if (isnan(a[i])) return NAN;
+        if (a[i] > m) m = a[i];
+    }
+    return m;
+}
+
+/* The error of 16 differences d under err_mode (the width-16 reduction above). */
+static float error16(const float d[16], int err_mode) {
+    float e[16];
+    for (int i = 0; i < 16; ++i) e[i] = (err_mode == NVO_ERR_MSE) ? d[i] * d[i] : fabsf(d[i]);
+    return (err_mode == NVO_ERR_MAXABS) ? max_or_nan(e, 16) : tree_sum16(e);
+}
+
+/* g = fl(A / (6 B)) for a bound B in 1..448 (6 B <= 2688 is exact). */
+static float global_scale_bound(float amax, int bound) { return amax / (float)(6 * bound); }
+
+static int knobs_ok(int err_mode, int bound) {
+    return (err_mode == NVO_ERR_MSE || err_mode == NVO_ERR_MAE || err_mode == NVO_ERR_MAXABS) && bound >= 1 &&
+           bound <= 448;
 }
 
 /* The input element (r, c): a bf16 pattern widened exactly, or a binary32 value as given.  [P3]: the reference
@@ -480,20 +516,24 @@ static float input_at(const uint16_t* xb, const float* xf, int64_t cols, int64_t
 }
 
 static int quantize_4o6_rows(const uint16_t* xb, const float* xf, int64_t rows, int64_t cols, int gmode,
-                             const float* amax, int64_t r_begin, int64_t r_end, uint8_t* codes, uint8_t* scales,
-                             float* g, uint8_t* choice);
+                             int err_mode, int bound, const float* amax, int64_t r_begin, int64_t r_end,
+                             uint8_t* codes, uint8_t* scales, float* g, uint8_t* choice);
 
-int nvo_quantize_4o6(const uint16_t* x, int64_t rows, int64_t cols, int gmode, const float* amax, int64_t r_begin,
-                     int64_t r_end, uint8_t* codes, uint8_t* scales, float* g, uint8_t* choice) {
+int nvo_quantize_4o6(const uint16_t* x, int64_t rows, int64_t cols, int gmode, int err_mode, int bound,
+                     const float* amax, int64_t r_begin, int64_t r_end, uint8_t* codes, uint8_t* scales, float* g,
+                     uint8_t* choice) {
     if (!x) return NVO_ERR_NULL;
-    return quantize_4o6_rows(x, NULL, rows, cols, gmode, amax, r_begin, r_end, codes, scales, g, choice);
+    return quantize_4o6_rows(x, NULL, rows, cols, gmode, err_mode, bound, amax, r_begin, r_end, codes, scales, g,
+                             choice);
 }
 
 /* Four-over-six of a binary32 input: nvo_quantize_4o6 on the values as given. */
-int nvo_quantize_4o6_f32(const float* x, int64_t rows, int64_t cols, int gmode, const float* amax, int64_t r_begin,
-                         int64_t r_end, uint8_t* codes, uint8_t* scales, float* g, uint8_t* choice) {
+int nvo_quantize_4o6_f32(const float* x, int64_t rows, int64_t cols, int gmode, int err_mode, int bound,
+                         const float* amax, int64_t r_begin, int64_t r_end, uint8_t* codes, uint8_t* scales,
+                         float* g, uint8_t* choice) {
     if (!x) return NVO_ERR_NULL;
-    return quantize_4o6_rows(NULL, x, rows, cols, gmode, amax, r_begin, r_end, codes, scales, g, choice);
+    return quantize_4o6_rows(NULL, x, rows, cols, gmode, err_mode, bound, amax, r_begin, r_end, codes, scales, g,
+                             choice);
 }
 
 /* Row-wise amax of a binary32 input (no transform), per tensor or per row: the largest magnitude as an integer
@@ -514,17 +554,18 @@ int nvo_amax_f32(const float* x, int64_t rows, int64_t cols, int gmode, float* a
 }
 
 static int quantize_4o6_rows(const uint16_t* xb, const float* xf, int64_t rows, int64_t cols, int gmode,
-                             const float* amax, int64_t r_begin, int64_t r_end, uint8_t* codes, uint8_t* scales,
-                             float* g, uint8_t* choice) {
+                             int err_mode, int bound, const float* amax, int64_t r_begin, int64_t r_end,
+                             uint8_t* codes, uint8_t* scales, float* g, uint8_t* choice) {
     if (!amax || !codes || !scales || !g) return NVO_ERR_NULL;
     if (rows < 0 || cols < 0 || cols % 16) return NVO_ERR_SHAPE;
     if (gmode != NVO_G_PER_TENSOR && gmode != NVO_G_PER_ROW) return NVO_ERR_UNSUPPORTED;
+    if (!knobs_ok(err_mode, bound)) return NVO_ERR_UNSUPPORTED;
     if (r_begin < 0 || r_end > rows || r_begin > r_end) return NVO_ERR_SHAPE;
     int64_t nb = cols / 16;
-    if (gmode == NVO_G_PER_TENSOR) g[0] = nvo_global_scale(amax[0]);
+    if (gmode == NVO_G_PER_TENSOR) g[0] = global_scale_bound(amax[0], bound);
     #pragma omp parallel for schedule(static)
     for (int64_t r = r_begin; r < r_end; ++r) {
-        float gr = nvo_global_scale(gmode == NVO_G_PER_ROW ? amax[r] : amax[0]);
+        float gr = global_scale_bound(gmode == NVO_G_PER_ROW ? amax[r] : amax[0], bound);
         if (gmode == NVO_G_PER_ROW) g[r] = gr;
         for (int64_t b = 0; b < nb; ++b) {
             float xv[16];
@@ -537,14 +578,13 @@ static int quantize_4o6_rows(const uint16_t* xb, const float* xf, int64_t rows, 
                 float rr;
                 nvo_block_scale(bamax, gr, T[c], &cand_sb[c], &rr);
                 float sbf = nvo_e4m3_decode(cand_sb[c]);
-                float e[16];
+                float d[16];
                 for (int i = 0; i < 16; ++i) {
                     cand_code[c][i] = nvo_e2m1_rn(xv[i] * rr);
                     float xh = (nvo_e2m1_decode(cand_code[c][i]) * sbf) * gr;
-                    float d = xh - xv[i];
-                    e[i] = d * d;
+                    d[i] = xh - xv[i];
                 }
-                err[c] = tree_sum16(e);
+                err[c] = error16(d, err_mode);
             }
             int pick = (err[1] < err[0]) ? 1 : 0;
             for (int k = 0; k < 8; ++k)
@@ -562,44 +602,49 @@ static int quantize_4o6_rows(const uint16_t* xb, const float* xf, int64_t rows, 
  * per-tensor global scale for the 16x16 case here (a tile spans 16 rows, so a row-scaled g does not define one
  * tile scale).  Per 16x16 tile of X: tamax = the NaN-dominant maximum magnitude of its 256 values; for T in {6, 4}
  * the tile scale sb_T and the element codes follow the 1x16 rules with tamax in place of bamax; the decoded values
- * and squared errors are as in the 1x16 case.  READING (the pages pin only the width-16 reduction): each of the
- * tile's 16 rows is summed by the width-16 tree, then the 16 row sums (row 0 first) by the same tree; map-to-4 is
- * kept only if its tile sum is strictly lower.  The chosen codes are written in W (packed along X's rows) and/or
+ * and their differences are as in the 1x16 case, with the same err_mode and bound.  READING (the pages pin only
+ * the width-16 reduction): each of the tile's 16 rows is reduced as a 1x16 block is (error16), then the 16 row
+ * errors (row 0 first) the same way: by the width-16 tree for MSE and MAE, as a maximum for MAXABS; map-to-4 is
+ * kept only if its tile error is strictly lower.  The chosen codes are written in W (packed along X's rows) and/or
  * W^T (packed along X's columns) orientation, with the tile's scale repeated in each orientation's 1x16 scale
  * layout, exactly as nvo_quantize_16x16.  choice[tile] (optional, [rows/16, cols/16]) receives 1 for map-to-4.
  * ---------------------------------------------------------------------------------------------------------- */
-static int quantize_4o6_tiles(const uint16_t* xb, const float* xf, int64_t rows, int64_t cols, const float* amax,
-                              int64_t tr_begin, int64_t tr_end, uint8_t* codes_w, uint8_t* scales_w, float* g_w,
-                              uint8_t* codes_wt, uint8_t* scales_wt, float* g_wt, uint8_t* choice);
+static int quantize_4o6_tiles(const uint16_t* xb, const float* xf, int64_t rows, int64_t cols, int err_mode,
+                              int bound, const float* amax, int64_t tr_begin, int64_t tr_end, uint8_t* codes_w,
+                              uint8_t* scales_w, float* g_w, uint8_t* codes_wt, uint8_t* scales_wt, float* g_wt,
+                              uint8_t* choice);
 
-int nvo_quantize_4o6_16x16(const uint16_t* x, int64_t rows, int64_t cols, const float* amax, int64_t tr_begin,
-                           int64_t tr_end, uint8_t* codes_w, uint8_t* scales_w, float* g_w, uint8_t* codes_wt,
-                           uint8_t* scales_wt, float* g_wt, uint8_t* choice) {
+int nvo_quantize_4o6_16x16(const uint16_t* x, int64_t rows, int64_t cols, int err_mode, int bound,
+                           const float* amax, int64_t tr_begin, int64_t tr_end, uint8_t* codes_w, uint8_t* scales_w,
+                           float* g_w, uint8_t* codes_wt, uint8_t* scales_wt, float* g_wt, uint8_t* choice) {
     if (!x) return NVO_ERR_NULL;
-    return quantize_4o6_tiles(x, NULL, rows, cols, amax, tr_begin, tr_end, codes_w, scales_w, g_w, codes_wt,
-                              scales_wt, g_wt, choice);
+    return quantize_4o6_tiles(x, NULL, rows, cols, err_mode, bound, amax, tr_begin, tr_end, codes_w, scales_w, g_w,
+                              codes_wt, scales_wt, g_wt, choice);
 }
 
 /* The same for a binary32 input ([P3]: bf16 or fp32 inputs), on the values as given. */
-int nvo_quantize_4o6_16x16_f32(const float* x, int64_t rows, int64_t cols, const float* amax, int64_t tr_begin,
-                               int64_t tr_end, uint8_t* codes_w, uint8_t* scales_w, float* g_w, uint8_t* codes_wt,
-                               uint8_t* scales_wt, float* g_wt, uint8_t* choice) {
+int nvo_quantize_4o6_16x16_f32(const float* x, int64_t rows, int64_t cols, int err_mode, int bound,
+                               const float* amax, int64_t tr_begin, int64_t tr_end, uint8_t* codes_w,
+                               uint8_t* scales_w, float* g_w, uint8_t* codes_wt, uint8_t* scales_wt, float* g_wt,
+                               uint8_t* choice) {
     if (!x) return NVO_ERR_NULL;
-    return quantize_4o6_tiles(NULL, x, rows, cols, amax, tr_begin, tr_end, codes_w, scales_w, g_w, codes_wt,
-                              scales_wt, g_wt, choice);
+    return quantize_4o6_tiles(NULL, x, rows, cols, err_mode, bound, amax, tr_begin, tr_end, codes_w, scales_w, g_w,
+                              codes_wt, scales_wt, g_wt, choice);
 }
 
-static int quantize_4o6_tiles(const uint16_t* xb, const float* xf, int64_t rows, int64_t cols, const float* amax,
-                              int64_t tr_begin, int64_t tr_end, uint8_t* codes_w, uint8_t* scales_w, float* g_w,
-                              uint8_t* codes_wt, uint8_t* scales_wt, float* g_wt, uint8_t* choice) {
+static int quantize_4o6_tiles(const uint16_t* xb, const float* xf, int64_t rows, int64_t cols, int err_mode,
+                              int bound, const float* amax, int64_t tr_begin, int64_t tr_end, uint8_t* codes_w,
+                              uint8_t* scales_w, float* g_w, uint8_t* codes_wt, uint8_t* scales_wt, float* g_wt,
+                              uint8_t* choice) {
     if (!amax) return NVO_ERR_NULL;
     if (rows < 0 || cols < 0 || rows % 16 || cols % 16) return NVO_ERR_SHAPE;
+    if (!knobs_ok(err_mode, bound)) return NVO_ERR_UNSUPPORTED;
     int want_w = codes_w != NULL, want_wt = codes_wt != NULL;
     if ((want_w && (!scales_w || !g_w)) || (want_wt && (!scales_wt || !g_wt)) || (!want_w && !want_wt))
         return NVO_ERR_NULL;
     int64_t ntr = rows / 16, ntc = cols / 16;
     if (tr_begin < 0 || tr_end > ntr || tr_begin > tr_end) return NVO_ERR_SHAPE;
-    float g = nvo_global_scale(amax[0]);
+    float g = global_scale_bound(amax[0], bound);
     if (want_w) g_w[0] = g;
     if (want_wt) g_wt[0] = g;
     #pragma omp parallel for schedule(static)
@@ -616,19 +661,18 @@ static int quantize_4o6_tiles(const uint16_t* xb, const float* xf, int64_t rows,
                 float r;
                 nvo_block_scale(tamax, g, T[c], &cand_sb[c], &r);
                 float sbf = nvo_e4m3_decode(cand_sb[c]);
-                float rowsum[16];
+                float rowerr[16];
                 for (int i = 0; i < 16; ++i) {
-                    float e[16];
+                    float d[16];
                     for (int j = 0; j < 16; ++j) {
                         uint8_t code = nvo_e2m1_rn(v[16 * i + j] * r);
                         cand_code[c][16 * i + j] = code;
                         float xh = (nvo_e2m1_decode(code) * sbf) * g;
-                        float d = xh - v[16 * i + j];
-                        e[j] = d * d;
+                        d[j] = xh - v[16 * i + j];
                     }
-                    rowsum[i] = tree_sum16(e);
+                    rowerr[i] = error16(d, err_mode);
                 }
-                err[c] = tree_sum16(rowsum);
+                err[c] = (err_mode == NVO_ERR_MAXABS) ? max_or_nan(rowerr, 16) : tree_sum16(rowerr);
             }
             int pick = (err[1] < err[0]) ? 1 : 0;
             const uint8_t* code = cand_code[pick];
