@@ -264,18 +264,23 @@ def config_figures(Q, W, dev, launches: int) -> dict:
         "quantize_kernel_us": round(1e3 * t16, 2), "quantize_kernel_gbs": gbs(b16, t16),
         "quantize_kernel_frac_of_hbm_peak": round(gbs(b16, t16) / HBM_PEAK_GBS, 4), "bytes_per_call": b16,
         "amax_us": round(1e3 * ta, 2)}
-    # the same weight, four-over-six with 16x16 tiles (W orientation only; amax given)
+    # the same weight, four-over-six with 16x16 tiles (amax given): W alone, and W and W^T from one read
     b46t = 2 * r * c + r * c // 2 + r * c // 16 + 4
-    t46t = timed(lambda k: Q.nvfp4_quantize_4o6_16x16(xs[k % n], am[k % n], out=outs[k % n][0]))
+    t46t = timed(lambda k: Q.nvfp4_quantize_4o6_16x16(xs[k % n], am[k % n], row_out=outs[k % n][0]))
+    t46b = timed(lambda k: Q.nvfp4_quantize_4o6_16x16(xs[k % n], am[k % n], Q.BOTH, row_out=outs[k % n][0],
+                                                      col_out=outs[k % n][1]))
     out["four_over_six_16x16_14336x4096"] = {
         "call": "nvfp4_quantize_4o6_16x16", "quantize_kernel_us": round(1e3 * t46t, 2),
         "quantize_kernel_gbs": gbs(b46t, t46t), "quantize_kernel_frac_of_hbm_peak": round(gbs(b46t, t46t) / HBM_PEAK_GBS, 4),
-        "bytes_per_call": b46t}
+        "bytes_per_call": b46t,
+        "both_orientations": {"quantize_kernel_us": round(1e3 * t46b, 2), "quantize_kernel_gbs": gbs(b16, t46b),
+                              "quantize_kernel_frac_of_hbm_peak": round(gbs(b16, t46b) / HBM_PEAK_GBS, 4),
+                              "bytes_per_call": b16}}
     # the same weight widened to float32 (2 buffers)
     b46f = 4 * r * c + r * c // 2 + r * c // 16 + 4
     wf = [(t.to(torch.int32) << 16).view(torch.float32) for t in xs[:2]]
     amw = [Q.nvfp4_amax_f32(t, Q.G_PER_TENSOR) for t in wf]
-    t46f = timed(lambda k: Q.nvfp4_quantize_4o6_16x16_f32(wf[k % 2], amw[k % 2], out=outs[k % n][0]))
+    t46f = timed(lambda k: Q.nvfp4_quantize_4o6_16x16_f32(wf[k % 2], amw[k % 2], row_out=outs[k % n][0]))
     out["four_over_six_16x16_f32_14336x4096"] = {
         "call": "nvfp4_quantize_4o6_16x16_f32", "quantize_kernel_us": round(1e3 * t46f, 2),
         "quantize_kernel_gbs": gbs(b46f, t46f), "quantize_kernel_frac_of_hbm_peak": round(gbs(b46f, t46f) / HBM_PEAK_GBS, 4),

@@ -79,6 +79,19 @@ typedef enum {
  * and grouped calls return NVFP4_ERR_UNSUPPORTED for it (their scales can be re-laid by nvfp4_swizzle_scales). */
 typedef enum { NVFP4_SCALES_ROWMAJOR = 0, NVFP4_SCALES_TILED = 1 } nvfp4_scale_layout;
 
+/* Four-over-six error measure ([P3]: the recipe's sweep varies an error mode, named there without a definition).
+ * With d_i = fl(xhat_i - x_i), xhat the candidate's decoded value: NVFP4_4O6_MSE sums fl(d_i * d_i), NVFP4_4O6_MAE
+ * sums |d_i| (both by the width-16 tree: (i, i+8), then strides 4, 2, 1), NVFP4_4O6_MAXABS takes the largest |d_i|
+ * (NaN if any d_i is NaN).  A 16x16 tile combines its 16 row errors the same way (tree, or maximum). */
+typedef enum { NVFP4_4O6_MSE = 0, NVFP4_4O6_MAE = 1, NVFP4_4O6_MAXABS = 2 } nvfp4_4o6_error;
+
+/* Four-over-six bound ([P3]: the sweep's "bound", named without a definition): the E4M3 value B (an integer,
+ * 1 <= B <= 448) that the tensor maximum's map-to-6 scale lands on, g = fl(amax / (6 B)) with 6 B exact.
+ * NVFP4_4O6_BOUND_STD (448) is the standard g = amax / 2688; NVFP4_4O6_BOUND_HEADROOM (256) keeps every map-to-4
+ * scale (at most 1.5 B = 384) below E4M3's 448, where with 448 the largest blocks' map-to-4 scales saturate. */
+#define NVFP4_4O6_BOUND_STD 448
+#define NVFP4_4O6_BOUND_HEADROOM 256
+
 typedef struct {
     uint8_t* codes;       /* [Rv, Cv/2] */
     uint8_t* scales;      /* [Rv, Cv/16] (NVFP4_SCALES_ROWMAJOR) or the tiled layout */
@@ -165,38 +178,46 @@ nvfp4_status nvfp4_amax_quantize(const uint16_t* x, int64_t rows, int64_t cols, 
                                  nvfp4_rounding rounding, uint16_t sign_mask, uint64_t seed, uint64_t offset,
                                  float* amax, const nvfp4_out* out, void* stream);
 
-/* Four-over-six quantization ([P3]): row-wise 1x16 blocks, round-to-nearest, no RHT.  Each block is encoded with
- * T = 6 and with T = 4 (scale bamax / fl(4 g), 1.5x the map-to-6 scale); both are decoded as
- * fl(fl(val * decode(sb)) * g); the squared errors fl(d * d), d = fl(xhat - x), are summed by the tree
- * (i, i+8), then strides 4, 2, 1; map-to-4 is kept only if its sum is strictly smaller (ties and NaN keep 6).
- *   amax: [1] or [rows] from nvfp4_amax (row-wise, no RHT).  Shape: cols % 16 == 0. */
+/* Four-over-six quantization ([P3]): row-wise 1x16 blocks, round-to-nearest, no RHT.  g = fl(amax / (6 bound)).
+ * Each block is encoded with T = 6 and with T = 4 (scale bamax / fl(4 g), 1.5x the map-to-6 scale); both are
+ * decoded as fl(fl(val * decode(sb)) * g); their errors are measured by err_mode (nvfp4_4o6_error); map-to-4 is
+ * kept only if its error is strictly smaller (ties and NaN keep 6).
+ *   amax: [1] or [rows] from nvfp4_amax (row-wise, no RHT).  Shape: cols % 16 == 0.
+ *   err_mode outside nvfp4_4o6_error or bound outside 1..448: NVFP4_ERR_UNSUPPORTED. */
 nvfp4_status nvfp4_quantize_4o6(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_gmode gmode,
-                                const float* amax, const nvfp4_out* out, void* stream);
+                                nvfp4_4o6_error err_mode, int32_t bound, const float* amax, const nvfp4_out* out,
+                                void* stream);
 
 /* Four-over-six of a binary32 tensor ([P3]: the reference quantizer takes bf16 or fp32 inputs, and its sweep covers
  * both): nvfp4_quantize_4o6 with x [rows, cols] binary32 (16-byte aligned) in place of bf16; every step is the same,
  * on the binary32 values as given.  amax: [1] or [rows] from nvfp4_amax_f32. */
 nvfp4_status nvfp4_quantize_4o6_f32(const float* x, int64_t rows, int64_t cols, nvfp4_gmode gmode,
-                                    const float* amax, const nvfp4_out* out, void* stream);
+                                    nvfp4_4o6_error err_mode, int32_t bound, const float* amax,
+                                    const nvfp4_out* out, void* stream);
 
 /* Row-wise amax of a binary32 tensor (no transform): the NaN-dominant maximum magnitude per tensor (amax[0]) or per
  * row (amax[rows]), for nvfp4_quantize_4o6_f32.  x [rows, cols] binary32, 16-byte aligned; cols % 16 == 0. */
 nvfp4_status nvfp4_amax_f32(const float* x, int64_t rows, int64_t cols, nvfp4_gmode gmode, float* amax, void* stream);
 
-/* Four-over-six with 16x16 tiles ([P3]: the reference quantizer takes 1x16 or 16x16 blocks).  One E4M3 scale per
- * 16x16 tile of X from the tile's maximum; both candidates (T = 6, 4) are formed as in nvfp4_quantize_4o6 with the
- * tile maximum; the tile's squared error is the sum of its rows, each row by the width-16 tree ((i, i+8), then
- * strides 4, 2, 1), and the 16 row sums by the same tree; map-to-4 is kept only if strictly lower.  Per-tensor g.
- *   Output *out: codes [rows, cols/2] packed along X's rows, scales [rows, cols/16] (each tile's scale repeated in
- *   its 16 rows), g [1].  amax: [1] from nvfp4_amax (row-wise, per tensor, no RHT).
- *   Shape: rows % 16 == 0 and cols % 16 == 0. */
-nvfp4_status nvfp4_quantize_4o6_16x16(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
-                                      const nvfp4_out* out, void* stream);
+/* Four-over-six with 16x16 tiles ([P3]: the reference quantizer takes 1x16 or 16x16 blocks; [P2, results]: weights
+ * are quantized in both orientations).  One E4M3 scale per 16x16 tile of X from the tile's maximum; both candidates
+ * (T = 6, 4) are formed as in nvfp4_quantize_4o6 with the tile maximum; the tile's error combines its rows' errors
+ * (each row by err_mode over its 16 differences, then the 16 row errors the same way, row 0 first); map-to-4 is
+ * kept only if strictly lower.  Per-tensor g = fl(amax / (6 bound)).
+ *   orient NVFP4_ROWWISE writes W to *row_out: codes [rows, cols/2] packed along X's rows, scales [rows, cols/16]
+ *   (each tile's scale repeated in its 16 rows), g [1]; NVFP4_COLWISE writes W^T to *col_out: codes [cols, rows/2]
+ *   packed along X's columns, scales [cols, rows/16], g [1]; NVFP4_BOTH writes both from one read of X.
+ *   amax: [1] from nvfp4_amax (row-wise, per tensor, no RHT).  Shape: rows % 16 == 0 and cols % 16 == 0.
+ *   err_mode outside nvfp4_4o6_error, bound outside 1..448, or another orient: NVFP4_ERR_UNSUPPORTED. */
+nvfp4_status nvfp4_quantize_4o6_16x16(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_orient orient,
+                                      nvfp4_4o6_error err_mode, int32_t bound, const float* amax,
+                                      const nvfp4_out* row_out, const nvfp4_out* col_out, void* stream);
 
 /* nvfp4_quantize_4o6_16x16 for a binary32 tensor ([P3]: bf16 or fp32 inputs): x [rows, cols] binary32, 16-byte
  * aligned; amax [1] from nvfp4_amax_f32 (per tensor).  Every step is the same, on the values as given. */
-nvfp4_status nvfp4_quantize_4o6_16x16_f32(const float* x, int64_t rows, int64_t cols, const float* amax,
-                                          const nvfp4_out* out, void* stream);
+nvfp4_status nvfp4_quantize_4o6_16x16_f32(const float* x, int64_t rows, int64_t cols, nvfp4_orient orient,
+                                          nvfp4_4o6_error err_mode, int32_t bound, const float* amax,
+                                          const nvfp4_out* row_out, const nvfp4_out* col_out, void* stream);
 
 /* Scale matrix to the tiled layout of the FP4 GEMM ([P2, approach]: the quantized operands reach the FP4 GEMM with
  * 1x16 block scales in the SWIZZLE_32_4_4 layout; [P2, results]: the swizzle is part of the per-call wrapper
@@ -226,14 +247,16 @@ nvfp4_status nvfp4_dequantize(const nvfp4_out* in, int64_t rv, int64_t cv, nvfp4
  * for item i is exactly that of the single-tensor call on it:
  *   nvfp4_amax_grouped     = nvfp4_amax(x, rows, cols, NVFP4_ROWWISE, gmode, use_rht, sign_mask, amax);
  *   nvfp4_quantize_grouped = nvfp4_quantize_rn / _sr / _rht_sr (row-wise, with the item's sign_mask, seed, offset)
- *                            or nvfp4_quantize_4o6 (rounding NVFP4_ROUND_4O6), reading the item's amax.
+ *                            or nvfp4_quantize_4o6 (rounding NVFP4_ROUND_4O6, with err_mode and bound; both are
+ *                            ignored for the other roundings), reading the item's amax.
  *   Errors: count < 0 or > NVFP4_MAX_GROUP -> NVFP4_ERR_SHAPE; items NULL with count > 0 -> NVFP4_ERR_NULL; every
  *   item is checked as the single-tensor call would check it, and the first failing item's status is returned
  *   (nothing is enqueued then).  count == 0 is a no-op.  The tensors' buffers must not overlap one another. */
 nvfp4_status nvfp4_amax_grouped(const nvfp4_group_item* items, int32_t count, nvfp4_gmode gmode, int use_rht,
                                 void* stream);
 nvfp4_status nvfp4_quantize_grouped(const nvfp4_group_item* items, int32_t count, nvfp4_gmode gmode,
-                                    nvfp4_rounding rounding, void* stream);
+                                    nvfp4_rounding rounding, nvfp4_4o6_error err_mode, int32_t bound,
+                                    void* stream);
 
 /* Fused decode ([P3]: an optimized decode is named there as future kernel work; [P1, random Hadamard transform]:
  * a block quantized after the rotation is brought back by the rotation's inverse, its transpose).  For each block of

@@ -22,29 +22,31 @@ G_PER_TENSOR, G_PER_ROW = 0, 1
 ROUND_RN, ROUND_SR, ROUND_RHT_SR, ROUND_4O6 = 0, 1, 2, 3
 MAX_GROUP = 32
 SCALES_ROWMAJOR, SCALES_TILED = 0, 1
+ERR_MSE, ERR_MAE, ERR_MAXABS = 0, 1, 2          # four-over-six error measures (nvfp4_4o6_error)
+BOUND_STD, BOUND_HEADROOM = 448, 256           # four-over-six bounds: g = amax / (6 bound)
 
 STATUS = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_SHAPE", 3: "NVFP4_ERR_ALIGN",
           4: "NVFP4_ERR_UNSUPPORTED", 5: "NVFP4_ERR_HIP"}
 
 # name -> (restype, argtypes); the same names and order as include/nvfp4.h
-_P, _I64, _U64, _U16, _I = C.c_void_p, C.c_int64, C.c_uint64, C.c_uint16, C.c_int
+_P, _I64, _U64, _U16, _I, _I32 = C.c_void_p, C.c_int64, C.c_uint64, C.c_uint16, C.c_int, C.c_int32
 SIGNATURES = {
     "nvfp4_amax": (_I, [_P, _I64, _I64, _I, _I, _I, _U16, _P, _P]),
     "nvfp4_quantize_rn": (_I, [_P, _I64, _I64, _I, _I, _I, _P, _P, _P, _P]),
     "nvfp4_quantize_sr": (_I, [_P, _I64, _I64, _I, _I, _P, _U64, _U64, _P, _P]),
     "nvfp4_quantize_rht_sr": (_I, [_P, _I64, _I64, _I, _I, _P, _U16, _U64, _U64, _P, _P]),
     "nvfp4_amax_quantize": (_I, [_P, _I64, _I64, _I, _I, _U16, _U64, _U64, _P, _P, _P]),
-    "nvfp4_quantize_4o6": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
-    "nvfp4_quantize_4o6_16x16": (_I, [_P, _I64, _I64, _P, _P, _P]),
-    "nvfp4_quantize_4o6_f32": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
-    "nvfp4_quantize_4o6_16x16_f32": (_I, [_P, _I64, _I64, _P, _P, _P]),
+    "nvfp4_quantize_4o6": (_I, [_P, _I64, _I64, _I, _I, _I32, _P, _P, _P]),
+    "nvfp4_quantize_4o6_16x16": (_I, [_P, _I64, _I64, _I, _I, _I32, _P, _P, _P, _P]),
+    "nvfp4_quantize_4o6_f32": (_I, [_P, _I64, _I64, _I, _I, _I32, _P, _P, _P]),
+    "nvfp4_quantize_4o6_16x16_f32": (_I, [_P, _I64, _I64, _I, _I, _I32, _P, _P, _P, _P]),
     "nvfp4_amax_f32": (_I, [_P, _I64, _I64, _I, _P, _P]),
     "nvfp4_dequantize": (_I, [_P, _I64, _I64, _I, _P, _P]),
     "nvfp4_dequantize_fused": (_I, [_P, _I64, _I64, _I, _I, _U16, _I, _P, _P]),
     "nvfp4_swizzle_scales": (_I, [_P, _I64, _I64, _P, _P]),
     "nvfp4_swizzled_scales_size": (_I64, [_I64, _I64]),
     "nvfp4_amax_grouped": (_I, [_P, C.c_int32, _I, _I, _P]),
-    "nvfp4_quantize_grouped": (_I, [_P, C.c_int32, _I, _I, _P]),
+    "nvfp4_quantize_grouped": (_I, [_P, _I32, _I, _I, _I, _I32, _P]),
     "nvfp4_status_str": (C.c_char_p, [_I]),
 }
 
@@ -230,12 +232,15 @@ def nvfp4_amax_quantize(x: torch.Tensor, orient: int, rounding: int, sign_mask: 
 
 
 def nvfp4_quantize_4o6(x: torch.Tensor, amax: torch.Tensor, gmode: int = G_PER_ROW,
-                       out: Optional[Quantized] = None, stream=None) -> Quantized:
+                       out: Optional[Quantized] = None, stream=None, err_mode: int = ERR_MSE,
+                       bound: int = BOUND_STD) -> Quantized:
+    """Four-over-six, row-wise 1x16 (err_mode ERR_MSE, ERR_MAE or ERR_MAXABS; g = amax / (6 bound))."""
     rows, cols = x.shape
     if out is None:
         out = alloc_out(rows, cols, gmode, x.device)
-    _check(lib().nvfp4_quantize_4o6(_bf16(x), rows, cols, gmode, _f32buf(amax, "amax", _amax_n(rows, gmode)),
-                                    _out(out, rows, cols, gmode), _stream(x.device, stream)), "nvfp4_quantize_4o6")
+    _check(lib().nvfp4_quantize_4o6(_bf16(x), rows, cols, gmode, err_mode, bound,
+                                    _f32buf(amax, "amax", _amax_n(rows, gmode)), _out(out, rows, cols, gmode),
+                                    _stream(x.device, stream)), "nvfp4_quantize_4o6")
     return out
 
 
@@ -256,39 +261,48 @@ def nvfp4_amax_f32(x: torch.Tensor, gmode: int = G_PER_TENSOR, amax: Optional[to
 
 
 def nvfp4_quantize_4o6_f32(x: torch.Tensor, amax: torch.Tensor, gmode: int = G_PER_ROW,
-                           out: Optional[Quantized] = None, stream=None) -> Quantized:
+                           out: Optional[Quantized] = None, stream=None, err_mode: int = ERR_MSE,
+                           bound: int = BOUND_STD) -> Quantized:
     """Four-over-six of a float32 tensor (row-wise 1x16)."""
     rows, cols = x.shape
     if out is None:
         out = alloc_out(rows, cols, gmode, x.device)
-    _check(lib().nvfp4_quantize_4o6_f32(_f32(x), rows, cols, gmode, _f32buf(amax, "amax", _amax_n(rows, gmode)),
-                                        _out(out, rows, cols, gmode), _stream(x.device, stream)),
-           "nvfp4_quantize_4o6_f32")
+    _check(lib().nvfp4_quantize_4o6_f32(_f32(x), rows, cols, gmode, err_mode, bound,
+                                        _f32buf(amax, "amax", _amax_n(rows, gmode)), _out(out, rows, cols, gmode),
+                                        _stream(x.device, stream)), "nvfp4_quantize_4o6_f32")
     return out
 
 
-def nvfp4_quantize_4o6_16x16_f32(x: torch.Tensor, amax: torch.Tensor, out: Optional[Quantized] = None,
-                                 stream=None) -> Quantized:
-    """Four-over-six with 16x16 tiles of a float32 tensor (per-tensor g); codes packed along X's rows."""
+def _quantize_4o6_16x16(fn, name, xp, rows, cols, device, amax, orient, err_mode, bound, row_out, col_out, stream):
+    want_row, want_col = orient in (ROWWISE, BOTH), orient in (COLWISE, BOTH)
+    if want_row and row_out is None:
+        row_out = alloc_out(rows, cols, G_PER_TENSOR, device)
+    if want_col and col_out is None:
+        col_out = alloc_out(cols, rows, G_PER_TENSOR, device)
+    _check(fn(xp, rows, cols, orient, err_mode, bound, _f32buf(amax, "amax", 1),
+              _out(row_out if want_row else None, rows, cols, G_PER_TENSOR),
+              _out(col_out if want_col else None, cols, rows, G_PER_TENSOR), _stream(device, stream)), name)
+    return (row_out if want_row else None), (col_out if want_col else None)
+
+
+def nvfp4_quantize_4o6_16x16(x: torch.Tensor, amax: torch.Tensor, orient: int = ROWWISE, err_mode: int = ERR_MSE,
+                             bound: int = BOUND_STD, row_out: Optional[Quantized] = None,
+                             col_out: Optional[Quantized] = None, stream=None):
+    """Four-over-six with 16x16 tiles (per-tensor g): W (ROWWISE), W^T (COLWISE) or both from one read; returns
+    (row_out, col_out), None for an orientation not asked for."""
     rows, cols = x.shape
-    if out is None:
-        out = alloc_out(rows, cols, G_PER_TENSOR, x.device)
-    _check(lib().nvfp4_quantize_4o6_16x16_f32(_f32(x), rows, cols, _f32buf(amax, "amax", 1),
-                                              _out(out, rows, cols, G_PER_TENSOR), _stream(x.device, stream)),
-           "nvfp4_quantize_4o6_16x16_f32")
-    return out
+    return _quantize_4o6_16x16(lib().nvfp4_quantize_4o6_16x16, "nvfp4_quantize_4o6_16x16", _bf16(x), rows, cols,
+                               x.device, amax, orient, err_mode, bound, row_out, col_out, stream)
 
 
-def nvfp4_quantize_4o6_16x16(x: torch.Tensor, amax: torch.Tensor, out: Optional[Quantized] = None,
-                             stream=None) -> Quantized:
-    """Four-over-six with 16x16 tiles (per-tensor g); codes packed along X's rows."""
+def nvfp4_quantize_4o6_16x16_f32(x: torch.Tensor, amax: torch.Tensor, orient: int = ROWWISE,
+                                 err_mode: int = ERR_MSE, bound: int = BOUND_STD,
+                                 row_out: Optional[Quantized] = None, col_out: Optional[Quantized] = None,
+                                 stream=None):
+    """nvfp4_quantize_4o6_16x16 of a float32 tensor."""
     rows, cols = x.shape
-    if out is None:
-        out = alloc_out(rows, cols, G_PER_TENSOR, x.device)
-    _check(lib().nvfp4_quantize_4o6_16x16(_bf16(x), rows, cols, _f32buf(amax, "amax", 1),
-                                          _out(out, rows, cols, G_PER_TENSOR), _stream(x.device, stream)),
-           "nvfp4_quantize_4o6_16x16")
-    return out
+    return _quantize_4o6_16x16(lib().nvfp4_quantize_4o6_16x16_f32, "nvfp4_quantize_4o6_16x16_f32", _f32(x), rows,
+                               cols, x.device, amax, orient, err_mode, bound, row_out, col_out, stream)
 
 
 def nvfp4_swizzled_scales_size(rv: int, nb: int) -> int:
@@ -367,13 +381,13 @@ def nvfp4_amax_grouped(xs, gmode: int = G_PER_TENSOR, use_rht: bool = False, sig
 
 
 def nvfp4_quantize_grouped(xs, amaxes, rounding: int, gmode: int = G_PER_TENSOR, sign_masks=None, seeds=None,
-                           offsets=None, outs=None, stream=None):
+                           offsets=None, outs=None, stream=None, err_mode: int = ERR_MSE, bound: int = BOUND_STD):
     """Row-wise 1x16 quantization of every tensor of xs in one launch (RN, SR, RHT+SR or four-over-six); returns
     the list of Quantized outputs."""
     if outs is None:
         outs = [alloc_out(x.shape[0], x.shape[1], gmode, x.device) for x in xs]
     arr = _group(xs, amaxes, outs, sign_masks, seeds, offsets, gmode)
     dev = xs[0].device if xs else torch.device("cuda")
-    _check(lib().nvfp4_quantize_grouped(arr, len(xs), gmode, rounding, _stream(dev, stream)),
+    _check(lib().nvfp4_quantize_grouped(arr, len(xs), gmode, rounding, err_mode, bound, _stream(dev, stream)),
            "nvfp4_quantize_grouped")
     return outs

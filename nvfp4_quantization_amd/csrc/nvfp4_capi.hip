@@ -40,6 +40,17 @@ nvfp4_status check_view(int64_t rows, int64_t cols, nvfp4_orient orient) {
     return NVFP4_ERR_UNSUPPORTED;
 }
 
+// Four-over-six knobs: a known error measure and a bound B with 6 B exact and B within E4M3's range.
+nvfp4_status check_knobs(nvfp4_4o6_error err_mode, int32_t bound) {
+    if (err_mode != NVFP4_4O6_MSE && err_mode != NVFP4_4O6_MAE && err_mode != NVFP4_4O6_MAXABS)
+        return NVFP4_ERR_UNSUPPORTED;
+    return (bound >= 1 && bound <= 448) ? NVFP4_OK : NVFP4_ERR_UNSUPPORTED;
+}
+
+nvfp4::ErrMode err_of(nvfp4_4o6_error e) {
+    return e == NVFP4_4O6_MSE ? nvfp4::kErrMSE : e == NVFP4_4O6_MAE ? nvfp4::kErrMAE : nvfp4::kErrMaxAbs;
+}
+
 nvfp4_status check_gmode(nvfp4_gmode gmode) {
     return (gmode == NVFP4_G_PER_TENSOR || gmode == NVFP4_G_PER_ROW) ? NVFP4_OK : NVFP4_ERR_UNSUPPORTED;
 }
@@ -105,6 +116,30 @@ nvfp4_status quantize_1x16(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_
                                          amax, sign_mask, nvfp4::Philox{seed, offset}, out->codes, out->scales,
                                          out->g, static_cast<hipStream_t>(stream),
                                          out->scale_layout == NVFP4_SCALES_TILED));
+}
+
+// Four-over-six with 16x16 tiles (bf16 or binary32 x): W to *row_out and/or W^T to *col_out.
+nvfp4_status quantize_4o6_16x16(const void* x, bool f32, int64_t rows, int64_t cols, nvfp4_orient orient,
+                                nvfp4_4o6_error err_mode, int32_t bound, const float* amax, const nvfp4_out* row_out,
+                                const nvfp4_out* col_out, void* stream) {
+    NVFP4_TRY(check_sizes(rows, cols));
+    NVFP4_TRY(check_knobs(err_mode, bound));
+    if (orient != NVFP4_ROWWISE && orient != NVFP4_COLWISE && orient != NVFP4_BOTH) return NVFP4_ERR_UNSUPPORTED;
+    if (rows % 16 || cols % 16) return NVFP4_ERR_SHAPE;
+    if (f32) {
+        NVFP4_TRY(check_buf(x, rows * cols, 16));
+        NVFP4_TRY(check_buf(amax, 1, 4));
+    } else {
+        NVFP4_TRY(check_input(static_cast<const uint16_t*>(x), rows, cols, amax, 1));
+    }
+    const bool want_w = orient == NVFP4_ROWWISE || orient == NVFP4_BOTH;
+    const bool want_wt = orient == NVFP4_COLWISE || orient == NVFP4_BOTH;
+    if (want_w) NVFP4_TRY(check_out(row_out, rows, cols, NVFP4_G_PER_TENSOR));
+    if (want_wt) NVFP4_TRY(check_out(col_out, cols, rows, NVFP4_G_PER_TENSOR));
+    return done(nvfp4::launch_quant_4o6_16x16(
+        x, rows, cols, err_of(err_mode), bound, amax, want_w ? row_out->codes : nullptr,
+        want_w ? row_out->scales : nullptr, want_w ? row_out->g : nullptr, want_wt ? col_out->codes : nullptr,
+        want_wt ? col_out->scales : nullptr, want_wt ? col_out->g : nullptr, static_cast<hipStream_t>(stream), f32));
 }
 
 }  // namespace
@@ -178,24 +213,22 @@ nvfp4_status nvfp4_amax_quantize(const uint16_t* x, int64_t rows, int64_t cols, 
 }
 
 nvfp4_status nvfp4_quantize_4o6(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_gmode gmode,
-                                const float* amax, const nvfp4_out* out, void* stream) {
+                                nvfp4_4o6_error err_mode, int32_t bound, const float* amax, const nvfp4_out* out,
+                                void* stream) {
     NVFP4_TRY(check_sizes(rows, cols));
     NVFP4_TRY(check_gmode(gmode));
+    NVFP4_TRY(check_knobs(err_mode, bound));
     if (cols % 16) return NVFP4_ERR_SHAPE;
     NVFP4_TRY(check_input(x, rows, cols, amax, gmode == NVFP4_G_PER_ROW ? rows : 1));
     NVFP4_TRY(check_out(out, rows, cols, gmode));
-    return done(nvfp4::launch_quant_4o6(x, rows, cols, gmode == NVFP4_G_PER_ROW, amax, out->codes, out->scales,
-                                        out->g, static_cast<hipStream_t>(stream)));
+    return done(nvfp4::launch_quant_4o6(x, rows, cols, gmode == NVFP4_G_PER_ROW, err_of(err_mode), bound, amax,
+                                        out->codes, out->scales, out->g, static_cast<hipStream_t>(stream)));
 }
 
-nvfp4_status nvfp4_quantize_4o6_16x16(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
-                                      const nvfp4_out* out, void* stream) {
-    NVFP4_TRY(check_sizes(rows, cols));
-    if (rows % 16 || cols % 16) return NVFP4_ERR_SHAPE;
-    NVFP4_TRY(check_input(x, rows, cols, amax, 1));
-    NVFP4_TRY(check_out(out, rows, cols, NVFP4_G_PER_TENSOR));
-    return done(nvfp4::launch_quant_4o6_16x16(x, rows, cols, amax, out->codes, out->scales, out->g,
-                                              static_cast<hipStream_t>(stream)));
+nvfp4_status nvfp4_quantize_4o6_16x16(const uint16_t* x, int64_t rows, int64_t cols, nvfp4_orient orient,
+                                      nvfp4_4o6_error err_mode, int32_t bound, const float* amax,
+                                      const nvfp4_out* row_out, const nvfp4_out* col_out, void* stream) {
+    return quantize_4o6_16x16(x, false, rows, cols, orient, err_mode, bound, amax, row_out, col_out, stream);
 }
 
 nvfp4_status nvfp4_amax_f32(const float* x, int64_t rows, int64_t cols, nvfp4_gmode gmode, float* amax, void* stream) {
@@ -208,26 +241,23 @@ nvfp4_status nvfp4_amax_f32(const float* x, int64_t rows, int64_t cols, nvfp4_gm
 }
 
 nvfp4_status nvfp4_quantize_4o6_f32(const float* x, int64_t rows, int64_t cols, nvfp4_gmode gmode,
-                                    const float* amax, const nvfp4_out* out, void* stream) {
+                                    nvfp4_4o6_error err_mode, int32_t bound, const float* amax,
+                                    const nvfp4_out* out, void* stream) {
     NVFP4_TRY(check_sizes(rows, cols));
     NVFP4_TRY(check_gmode(gmode));
+    NVFP4_TRY(check_knobs(err_mode, bound));
     if (cols % 16) return NVFP4_ERR_SHAPE;
     NVFP4_TRY(check_buf(x, rows * cols, 16));
     NVFP4_TRY(check_buf(amax, gmode == NVFP4_G_PER_ROW ? rows : 1, 4));
     NVFP4_TRY(check_out(out, rows, cols, gmode));
-    return done(nvfp4::launch_quant_4o6(x, rows, cols, gmode == NVFP4_G_PER_ROW, amax, out->codes, out->scales,
-                                        out->g, static_cast<hipStream_t>(stream), true));
+    return done(nvfp4::launch_quant_4o6(x, rows, cols, gmode == NVFP4_G_PER_ROW, err_of(err_mode), bound, amax,
+                                        out->codes, out->scales, out->g, static_cast<hipStream_t>(stream), true));
 }
 
-nvfp4_status nvfp4_quantize_4o6_16x16_f32(const float* x, int64_t rows, int64_t cols, const float* amax,
-                                          const nvfp4_out* out, void* stream) {
-    NVFP4_TRY(check_sizes(rows, cols));
-    if (rows % 16 || cols % 16) return NVFP4_ERR_SHAPE;
-    NVFP4_TRY(check_buf(x, rows * cols, 16));
-    NVFP4_TRY(check_buf(amax, 1, 4));
-    NVFP4_TRY(check_out(out, rows, cols, NVFP4_G_PER_TENSOR));
-    return done(nvfp4::launch_quant_4o6_16x16(x, rows, cols, amax, out->codes, out->scales, out->g,
-                                              static_cast<hipStream_t>(stream), true));
+nvfp4_status nvfp4_quantize_4o6_16x16_f32(const float* x, int64_t rows, int64_t cols, nvfp4_orient orient,
+                                          nvfp4_4o6_error err_mode, int32_t bound, const float* amax,
+                                          const nvfp4_out* row_out, const nvfp4_out* col_out, void* stream) {
+    return quantize_4o6_16x16(x, true, rows, cols, orient, err_mode, bound, amax, row_out, col_out, stream);
 }
 
 nvfp4_status nvfp4_dequantize(const nvfp4_out* in, int64_t rv, int64_t cv, nvfp4_gmode gmode, float* y,
@@ -264,16 +294,18 @@ nvfp4_status nvfp4_amax_grouped(const nvfp4_group_item* items, int32_t count, nv
 }
 
 nvfp4_status nvfp4_quantize_grouped(const nvfp4_group_item* items, int32_t count, nvfp4_gmode gmode,
-                                    nvfp4_rounding rounding, void* stream) {
+                                    nvfp4_rounding rounding, nvfp4_4o6_error err_mode, int32_t bound,
+                                    void* stream) {
     if (rounding != NVFP4_ROUND_RN && rounding != NVFP4_ROUND_SR && rounding != NVFP4_ROUND_RHT_SR &&
         rounding != NVFP4_ROUND_4O6)
         return NVFP4_ERR_UNSUPPORTED;
+    if (rounding == NVFP4_ROUND_4O6) NVFP4_TRY(check_knobs(err_mode, bound));
     nvfp4::GroupTensor t[NVFP4_MAX_GROUP];
     NVFP4_TRY(check_group(items, count, gmode, true, t));
     if (count == 0) return NVFP4_OK;
     const int method = rounding == NVFP4_ROUND_RN ? nvfp4::kRN : rounding == NVFP4_ROUND_SR ? nvfp4::kSR
                        : rounding == NVFP4_ROUND_RHT_SR ? nvfp4::kRHTSR : nvfp4::kFourOverSix;
-    return done(nvfp4::launch_quant_grouped(t, count, gmode == NVFP4_G_PER_ROW, method,
+    return done(nvfp4::launch_quant_grouped(t, count, gmode == NVFP4_G_PER_ROW, method, err_of(err_mode), bound,
                                             static_cast<hipStream_t>(stream)));
 }
 

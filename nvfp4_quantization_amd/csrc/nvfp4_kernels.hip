@@ -526,6 +526,9 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
 
 __device__ __forceinline__ float global_scale(float amax) { return amax / 2688.0f; }
 
+// Four-over-six global scale g = fl(amax / (6 B)) for the bound B (gden = 6 B, exact); B = 448 is global_scale.
+__device__ __forceinline__ float global_scale_den(float amax, float gden) { return amax / gden; }
+
 // ------------------------------------------------------------------------------------------------------------
 // Row-wise 1x16 quantization: one 16-element block per lane per step; lanes walk the blocks with a grid stride
 // and keep the next block's two loads in flight.
@@ -1741,11 +1744,33 @@ __device__ __forceinline__ void widen_block(const BlockWords<F32>& r, float (&xv
     }
 }
 
-// One block: both candidates, their decoded squared errors, and the choice.  xv are the 16 values, m their absmax,
+// Error of one candidate from its 16 differences d (in place): ERR kErrMSE sums fl(d * d) and kErrMAE |d| by the
+// width-16 tree (i with i + 8, then strides 4, 2, 1); kErrMaxAbs takes the largest |d| as an integer maximum of the
+// magnitude bits, so a NaN difference makes the error NaN (NaN > inf > finite).
+template <int ERR>
+__device__ __forceinline__ float error16(float (&d)[16]) {
+    if constexpr (ERR == kErrMaxAbs) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = umax(m, as_u(d[i]) & 0x7FFFFFFFu);
+        return as_f(m);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) d[i] = ERR == kErrMSE ? d[i] * d[i] : __builtin_fabsf(d[i]);
+#pragma unroll
+        for (int s = 8; s >= 1; s >>= 1)
+#pragma unroll
+            for (int i = 0; i < s; ++i) d[i] = d[i] + d[i + s];
+        return d[0];
+    }
+}
+
+// One block: both candidates, their decoded errors (ERR), and the choice.  xv are the 16 values, m their absmax,
 // dv the divisors 6 g and 4 g, tab the multipliers of g.  A NaN or infinite g (a row whose amax is NaN or infinite)
 // makes every multiplier NaN: both candidates give codes 0x7 and NaN errors (the map-to-6 one is kept), and its
 // scale code is 0 where the quotient is 0 (bamax = 0; with an infinite g, any finite bamax), 0x7F (NaN) otherwise;
 // that case is written directly.
+template <int ERR>
 __device__ __forceinline__ void quant_4o6_block(const float (&xv)[16], float m, float g, const Divisor (&dv)[2],
                                                 const RTable& tab, uint32_t& lo_out, uint32_t& hi_out,
                                                 uint32_t& sb_out) {
@@ -1775,20 +1800,12 @@ __device__ __forceinline__ void quant_4o6_block(const float (&xv)[16], float m, 
         float dq[16];
         unpack8(lo, *reinterpret_cast<float(*)[8]>(&dq[0]));
         unpack8(hi, *reinterpret_cast<float(*)[8]>(&dq[8]));
-        float e[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float df = (dq[i] * sbf) * g - xv[i];
-            e[i] = df * df;
-        }
-#pragma unroll
-        for (int s = 8; s >= 1; s >>= 1)
-#pragma unroll
-            for (int i = 0; i < s; ++i) e[i] = e[i] + e[i + s];
+        for (int i = 0; i < 16; ++i) dq[i] = (dq[i] * sbf) * g - xv[i];
         cand_lo[c] = lo;
         cand_hi[c] = hi;
         cand_sb[c] = sb;
-        err[c] = e[0];
+        err[c] = error16<ERR>(dq);
     }
     const int pick = (err[1] < err[0]) ? 1 : 0;
     lo_out = cand_lo[pick];
@@ -1798,12 +1815,12 @@ __device__ __forceinline__ void quant_4o6_block(const float (&xv)[16], float m, 
 
 // Per-tensor g: grid-stride over blocks with the next block's loads in flight; the multipliers of the 128 scale
 // codes are tabulated once per workgroup.
-template <bool F32 = false>
+template <bool F32, int ERR>
 __device__ __forceinline__ void quant_4o6_tensor_wg(const uint4* __restrict__ x, uint32_t total_blocks,
-                                                    const float* __restrict__ amax, uint2* __restrict__ codes,
-                                                    uint8_t* __restrict__ scales, float* __restrict__ gout,
-                                                    uint32_t wg, uint32_t nwg, RTable& tab) {
-    const float g = global_scale(amax[0]);
+                                                    const float* __restrict__ amax, float gden,
+                                                    uint2* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                    float* __restrict__ gout, uint32_t wg, uint32_t nwg, RTable& tab) {
+    const float g = global_scale_den(amax[0], gden);
     if (wg == 0 && threadIdx.x == 0) gout[0] = g;
     const Divisor dv[2] = {make_divisor_uniform(6.0f * g), make_divisor_uniform(4.0f * g)};   // T = 6 and T = 4
     fill_rtable<false>(tab, g);
@@ -1818,36 +1835,37 @@ __device__ __forceinline__ void quant_4o6_tensor_wg(const uint4* __restrict__ x,
         float xv[16];
         widen_block<F32>(a, xv);
         uint32_t lo, hi, sb;
-        quant_4o6_block(xv, absmax16(xv), g, dv, tab, lo, hi, sb);
+        quant_4o6_block<ERR>(xv, absmax16(xv), g, dv, tab, lo, hi, sb);
         st_nt(codes + n, make_uint2(lo, hi));
         st_nt(scales + n, (uint8_t)sb);
         a = a2;
     }
 }
 
-template <bool F32>
+template <bool F32, int ERR>
 __global__ void __launch_bounds__(kThreads)
-k_quant_4o6_tensor(const uint4* __restrict__ x, uint32_t total_blocks, const float* __restrict__ amax,
+k_quant_4o6_tensor(const uint4* __restrict__ x, uint32_t total_blocks, const float* __restrict__ amax, float gden,
                    uint2* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gout) {
     __shared__ RTable tab;
-    quant_4o6_tensor_wg<F32>(x, total_blocks, amax, codes, scales, gout, blockIdx.x, gridDim.x, tab);
+    quant_4o6_tensor_wg<F32, ERR>(x, total_blocks, amax, gden, codes, scales, gout, blockIdx.x, gridDim.x, tab);
 }
 
 // Per-row g: a workgroup walks whole rows (grid-stride over rows), lane t taking blocks t, t + 256, ... of each, with
 // the next block's loads (in this row or the next) in flight.  g, its two divisors and the row's multiplier table
 // are computed once per row: the table is double-buffered, so one barrier per row orders it (a thread writes the
 // table of row i only after the barrier of row i - 1, which every thread passes only after its reads of row i - 2).
-template <bool F32 = false>
+template <bool F32, int ERR>
 __device__ __forceinline__ void quant_4o6_rows_wg(const uint4* __restrict__ x, uint32_t rows, uint32_t bpr,
-                                                  const float* __restrict__ amax, uint2* __restrict__ codes,
-                                                  uint8_t* __restrict__ scales, float* __restrict__ gout, uint32_t wg,
-                                                  uint32_t nwg, RTable (&tabs)[2]) {
+                                                  const float* __restrict__ amax, float gden,
+                                                  uint2* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                  float* __restrict__ gout, uint32_t wg, uint32_t nwg,
+                                                  RTable (&tabs)[2]) {
     const uint32_t t = threadIdx.x;
     uint32_t row = wg;
     BlockWords<F32> a{};
     if (row < rows && t < bpr) a = ld_block<F32>(x, (size_t)row * bpr + t);
     for (uint32_t parity = 0; row < rows; row += nwg, parity ^= 1u) {
-        const float g = global_scale(amax[row]);
+        const float g = global_scale_den(amax[row], gden);
         if (t == 0) gout[row] = g;
         // a NaN or infinite g needs neither the table nor the divisors (every block of the row is written directly)
         const bool finite = __builtin_amdgcn_readfirstlane((uint32_t)(__builtin_fabsf(g) < __builtin_inff())) != 0;
@@ -1870,7 +1888,7 @@ __device__ __forceinline__ void quant_4o6_rows_wg(const uint4* __restrict__ x, u
             float xv[16];
             widen_block<F32>(a, xv);
             uint32_t lo, hi, sb;
-            quant_4o6_block(xv, absmax16(xv), g, dv, tab, lo, hi, sb);
+            quant_4o6_block<ERR>(xv, absmax16(xv), g, dv, tab, lo, hi, sb);
             const size_t n = (size_t)row * bpr + blk;
             st_nt(codes + n, make_uint2(lo, hi));
             st_nt(scales + n, (uint8_t)sb);
@@ -1879,12 +1897,12 @@ __device__ __forceinline__ void quant_4o6_rows_wg(const uint4* __restrict__ x, u
     }
 }
 
-template <bool F32>
+template <bool F32, int ERR>
 __global__ void __launch_bounds__(kThreads)
 k_quant_4o6_rows(const uint4* __restrict__ x, uint32_t rows, uint32_t bpr, const float* __restrict__ amax,
-                 uint2* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gout) {
+                 float gden, uint2* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gout) {
     __shared__ RTable tabs[2];
-    quant_4o6_rows_wg<F32>(x, rows, bpr, amax, codes, scales, gout, blockIdx.x, gridDim.x, tabs);
+    quant_4o6_rows_wg<F32, ERR>(x, rows, bpr, amax, gden, codes, scales, gout, blockIdx.x, gridDim.x, tabs);
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -1907,36 +1925,45 @@ __device__ __forceinline__ float row_ror_f(float v) {
     return as_f(row_ror<N>(as_u(v)));
 }
 
-// Squared-error sum of one candidate over the tile: this lane's row (the width-16 tree: i with i + 8, then 4, 2, 1),
-// then the 16 row sums by the same tree (rows i and i + 8 first).  Lane i of the 16-lane row gets the sum over the
-// rows rotated by i; lane 0's operand order is the pinned one.
+// Per-element error term and the combination of two terms for the error mode: fl(d * d) and addition (kErrMSE),
+// |d| and addition (kErrMAE), |d| and the integer maximum of the magnitude bits (kErrMaxAbs: NaN > inf > finite).
+template <int ERR>
+__device__ __forceinline__ float err_term(float d) { return ERR == kErrMSE ? d * d : __builtin_fabsf(d); }
+
+template <int ERR>
+__device__ __forceinline__ float err_join(float a, float b) {
+    return ERR == kErrMaxAbs ? as_f(umax(as_u(a), as_u(b))) : a + b;
+}
+
+// Error of one candidate over the tile: this lane's row (the width-16 tree: i with i + 8, then 4, 2, 1), then the
+// 16 row errors by the same tree (rows i and i + 8 first); for kErrMaxAbs the joins are maxima, whose order does not
+// matter.  Lane i of the 16-lane row gets the combination over the rows rotated by i; lane 0's operand order is the
+// pinned one.
+template <int ERR>
 __device__ __forceinline__ float tile_error(const float (&xv)[16], uint32_t lo, uint32_t hi, float sbf, float g) {
-    // the first half's squares, then each square of the second half added to its partner at once (the first level
-    // of the tree) so that fewer values are live
+    // the first half's terms, then each term of the second half joined to its partner at once (the first level of
+    // the tree) so that fewer values are live
     float e[8];
     unpack8(lo, e);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float d = (e[i] * sbf) * g - xv[i];
-        e[i] = d * d;
-    }
+    for (int i = 0; i < 8; ++i) e[i] = err_term<ERR>((e[i] * sbf) * g - xv[i]);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const f32x2 v = cvt_fp4_pair(hi, p);
         const float d0 = (v.x * sbf) * g - xv[8 + 2 * p];
         const float d1 = (v.y * sbf) * g - xv[9 + 2 * p];
-        e[2 * p] = e[2 * p] + d0 * d0;
-        e[2 * p + 1] = e[2 * p + 1] + d1 * d1;
+        e[2 * p] = err_join<ERR>(e[2 * p], err_term<ERR>(d0));
+        e[2 * p + 1] = err_join<ERR>(e[2 * p + 1], err_term<ERR>(d1));
     }
 #pragma unroll
     for (int s2 = 4; s2 >= 1; s2 >>= 1)
 #pragma unroll
-        for (int i = 0; i < s2; ++i) e[i] = e[i] + e[i + s2];
+        for (int i = 0; i < s2; ++i) e[i] = err_join<ERR>(e[i], e[i + s2]);
     float t = e[0];
-    t = t + row_ror_f<8>(t);   // lane i: row i + row i + 8 (lane 0: rows 0 and 8)
-    t = t + row_ror_f<4>(t);
-    t = t + row_ror_f<2>(t);
-    t = t + row_ror_f<1>(t);
+    t = err_join<ERR>(t, row_ror_f<8>(t));   // lane i: row i and row i + 8 (lane 0: rows 0 and 8)
+    t = err_join<ERR>(t, row_ror_f<4>(t));
+    t = err_join<ERR>(t, row_ror_f<2>(t));
+    t = err_join<ERR>(t, row_ror_f<1>(t));
     return t;
 }
 
@@ -1955,6 +1982,7 @@ struct Stage46 {
 static_assert(kWavesPerGroup16 == 16 && kTilesPerGroup46 == 64, "the write-out takes one wave per row, one lane per tile");
 
 // One tile row: both candidates, the tile's errors and the choice (lane 0's, broadcast over the tile's lanes).
+template <int ERR>
 __device__ __forceinline__ void quant_4o6_tile_row(const float (&xv)[16], float g, bool gfinite,
                                                    const Divisor (&dv)[2], const RTable& tab, uint32_t& lo,
                                                    uint32_t& hi, uint32_t& sb) {
@@ -1989,7 +2017,7 @@ __device__ __forceinline__ void quant_4o6_tile_row(const float (&xv)[16], float 
             cl[c] = patch_nan8(cl[c], q0);
             ch[c] = patch_nan8(ch[c], q1);
         }
-        err[c] = tile_error(xv, cl[c], ch[c], e4m3_decode(cs[c]), g);
+        err[c] = tile_error<ERR>(xv, cl[c], ch[c], e4m3_decode(cs[c]), g);
     }
     // lane 0's comparison; ties and NaN keep map-to-6
     const bool four = row_bcast0(err[1] < err[0] ? 1u : 0u) != 0u;
@@ -1998,64 +2026,104 @@ __device__ __forceinline__ void quant_4o6_tile_row(const float (&xv)[16], float 
     sb = four ? cs[1] : cs[0];
 }
 
-// Items: (16-row band, group of 64 tile columns), band-major; each workgroup loops over items with the next item's
-// loads in flight, and fills the multiplier table once.
-template <bool F32>
+// The chunk of workgroup b among the grid's n: workgroups are dealt round-robin to the 8 XCDs, so with n a multiple
+// of 8 the chunks b / 8 + (b % 8) n / 8 make each XCD's chunks consecutive.
+__device__ __forceinline__ uint32_t xcd_chunk(uint32_t b, uint32_t n) {
+    return (n & 7u) ? b : (b & 7u) * (n >> 3) + (b >> 3);
+}
+
+// Items: (16-row band, group of 64 tile columns), numbered column-group-major, so that consecutive items are
+// consecutive bands of one column group; workgroup b takes the per_wg consecutive items of chunk xcd_chunk(b) with
+// the next item's loads in flight, and fills the multiplier table once.  W is written from LDS by rows (512 bytes
+// of codes per row and item); W^T receives 8 bytes of codes and 1 of scales per row and item, so the consecutive
+// bands of a chunk (and the chunks of one XCD) fill its 128-byte lines in one L2: those stores are cached.
+template <bool F32, int ERR, bool W, bool WT>
 __global__ void __launch_bounds__(kThreads16) __attribute__((amdgpu_waves_per_eu(8, 8)))
-k_quant_4o6_16x16(const uint4* __restrict__ x, uint32_t ntc, uint32_t groups_per_rb, uint32_t items,
-                  const float* __restrict__ amax, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
-                  float* __restrict__ gout) {
+k_quant_4o6_16x16(const uint4* __restrict__ x, uint32_t ntc, uint32_t nbands, uint32_t items, uint32_t per_wg,
+                  float gden, const float* __restrict__ amax, uint2* __restrict__ codes_w,
+                  uint8_t* __restrict__ scales_w, float* __restrict__ g_w, uint2* __restrict__ codes_wt,
+                  uint8_t* __restrict__ scales_wt, float* __restrict__ g_wt) {
     __shared__ RTable tab;
     __shared__ Stage46 st;
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
     const uint32_t tw = wave * kTilesPerWave46 + (lane >> 4);   // tile of the item
     const uint32_t i = lane & 15u;                             // row within the tile
-    // this lane's 16 elements of item w = block (16 rb + i) * ntc + tj of the row-wise view
-    auto load = [&](uint32_t w, BlockWords<F32>& a) {
-        const uint32_t rb = w / groups_per_rb;
-        const uint32_t tj = (w - rb * groups_per_rb) * kTilesPerGroup46 + tw;
+    // this lane's 16 elements of the item (column group cg, band rb) = block (16 rb + i) * ntc + tj of the
+    // row-wise view
+    auto load = [&](uint32_t cg, uint32_t rb, BlockWords<F32>& a) {
+        const uint32_t tj = cg * kTilesPerGroup46 + tw;
         if (tj < ntc) a = ld_block<F32>(x, (size_t)(16 * rb + i) * ntc + tj);   // whole 16-lane rows per tile
     };
-    uint32_t w = blockIdx.x;
+    const uint32_t w0 = xcd_chunk(blockIdx.x, gridDim.x) * per_wg;
+    const uint32_t n = __builtin_amdgcn_readfirstlane(w0 < items ? min(per_wg, items - w0) : 0u);
+    // (cg, rb) of the current item, stepped band by band (uniform: scalar registers)
+    uint32_t cg = __builtin_amdgcn_readfirstlane(w0 / nbands);
+    uint32_t rb = __builtin_amdgcn_readfirstlane(w0 - cg * nbands);
     BlockWords<F32> a{};
-    load(w, a);
-    const float g = uniform_f(global_scale(amax[0]));   // uniform values kept in scalar registers
-    if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
+    if (n) load(cg, rb, a);
+    const float g = uniform_f(global_scale_den(amax[0], gden));   // uniform values kept in scalar registers
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (W) g_w[0] = g;
+        if (WT) g_wt[0] = g;
+    }
     const bool gfinite = __builtin_fabsf(g) < __builtin_inff();
-    Divisor dv[2] = {};
-    if (gfinite) {
-        dv[0] = make_divisor_uniform(6.0f * g);
-        dv[1] = make_divisor_uniform(4.0f * g);
+    // formed unconditionally (unused when g is not finite) and moved to scalar registers: the compiler drops a
+    // readfirstlane of a value it knows to be uniform, and the division's vector result would then stay live across
+    // the item loop; passing it through an empty asm first hides that knowledge
+    Divisor dv[2] = {make_divisor_uniform(6.0f * g), make_divisor_uniform(4.0f * g)};
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            dv[c].d = uniform_f(dv[c].d);
-            dv[c].y = uniform_f(dv[c].y);
-        }
+    for (int c = 0; c < 2; ++c) {
+        asm volatile("" : "+v"(dv[c].d), "+v"(dv[c].y));
+        dv[c].d = uniform_f(dv[c].d);
+        dv[c].y = uniform_f(dv[c].y);
     }
     fill_rtable<false>(tab, g);
-    for (uint32_t buf = 0; w < items; w += gridDim.x, buf ^= 1u) {
-        const uint32_t rb = w / groups_per_rb;
-        const uint32_t t0 = (w - rb * groups_per_rb) * kTilesPerGroup46;   // first tile column of the item
+    for (uint32_t k = 0, buf = 0; k < n; ++k, buf ^= 1u) {
+        const uint32_t ncg = rb + 1 == nbands ? cg + 1 : cg, nrb = rb + 1 == nbands ? 0u : rb + 1;
+        const uint32_t t0 = cg * kTilesPerGroup46;   // first tile column of the item
         const bool active = t0 + tw < ntc;
         float xv[16];
         widen_block<F32>(a, xv);
         // bf16: the next item's loads are in flight during this item's arithmetic; binary32 words would not fit in
         // the registers beside it, so they go out after it (overlapping the write-out)
-        if (!F32 && w + gridDim.x < items) load(w + gridDim.x, a);
+        if (!F32 && k + 1 < n) load(ncg, nrb, a);
         uint32_t lo = 0, hi = 0, sb = 0;
-        if (active) quant_4o6_tile_row(xv, g, gfinite, dv, tab, lo, hi, sb);
-        if (F32 && w + gridDim.x < items) load(w + gridDim.x, a);
+        if (active) quant_4o6_tile_row<ERR>(xv, g, gfinite, dv, tab, lo, hi, sb);
+        if (F32 && k + 1 < n) load(ncg, nrb, a);
         if (active) {
-            st.codes[buf][tw][i] = make_uint2(lo, hi);
-            st.scales[buf][tw][i] = (uint8_t)sb;
+            // the slot index formed here rather than kept in a register across the loop
+            uint32_t slot = tw * 17 + i;
+            asm volatile("" : "+v"(slot));
+            (&st.codes[buf][0][0])[slot] = make_uint2(lo, hi);
+            (&st.scales[buf][0][0])[slot] = (uint8_t)sb;
         }
         __syncthreads();
-        // write-out: wave v takes output row v of the band, lane t tile t: 512 contiguous bytes of codes, 64 of scales
-        if (t0 + lane < ntc) {
+        // W: wave v takes output row v of the band, lane t tile t: 512 contiguous bytes of codes, 64 of scales
+        if (W && t0 + lane < ntc) {
             const size_t o = (size_t)(16 * rb + wave) * ntc + t0 + lane;
-            st_nt(codes + o, st.codes[buf][lane][wave]);
-            st_nt(scales + o, st.scales[buf][lane][wave]);
+            st_nt(codes_w + o, st.codes[buf][lane][wave]);
+            st_nt(scales_w + o, st.scales[buf][lane][wave]);
         }
+        // W^T: thread (tile tt, column j) assembles row 16 (t0 + tt) + j from nibble j of the tile's 16 rows (row r
+        // of the tile is element r of that row's block: byte k holds rows 2k and 2k + 1)
+        if (WT) {
+            const uint32_t tt = threadIdx.x >> 4, j = threadIdx.x & 15u;
+            if (t0 + tt < ntc) {
+                const uint32_t* words = reinterpret_cast<const uint32_t*>(&st.codes[buf][tt][0]) + (j >> 3);
+                const uint32_t sh = 4 * (j & 7u);
+                uint32_t wl = 0, wh = 0;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) wl |= ((words[2 * r] >> sh) & 0xFu) << (4 * r);
+                __builtin_amdgcn_sched_barrier(0);   // eight LDS reads in flight at a time bound the live registers
+#pragma unroll
+                for (int r = 0; r < 8; ++r) wh |= ((words[2 * (r + 8)] >> sh) & 0xFu) << (4 * r);
+                const size_t row = 16 * (size_t)(t0 + tt) + j;
+                codes_wt[row * nbands + rb] = make_uint2(wl, wh);
+                scales_wt[row * nbands + rb] = st.scales[buf][tt][0];
+            }
+        }
+        cg = ncg;
+        rb = nrb;
     }
 }
 
@@ -2196,10 +2264,11 @@ __global__ void k_fill_zero(uint32_t* __restrict__ p, uint32_t n) {
     for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < n; i += gridDim.x * kThreads) p[i] = 0u;
 }
 
-// g = amax / 2688 for n entries (used when the tensor to quantize is empty, so no block writes g).
-__global__ void k_write_g(const float* __restrict__ amax, float* __restrict__ g, uint32_t n) {
+// g = amax / gden for n entries (gden = 2688 = 6 * 448, or 6 B for a four-over-six bound B), used when the tensor
+// to quantize is empty, so no block writes g.
+__global__ void k_write_g(const float* __restrict__ amax, float* __restrict__ g, uint32_t n, float gden) {
     for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < n; i += gridDim.x * kThreads)
-        g[i] = global_scale(amax[i]);
+        g[i] = global_scale_den(amax[i], gden);
 }
 
 // Publishes a workgroup's partial maximum (magnitude bits) into a zeroed per-tensor amax.  Same-address atomics
@@ -2597,6 +2666,7 @@ struct GroupItemK {
 
 struct GroupArgs {
     uint32_t count, total_wg;
+    float gden;                   // four-over-six: 6 B for the bound B
     GroupItemK it[kMaxGroup];
 };
 static_assert(sizeof(GroupArgs) <= 4096, "grouped descriptors must fit the kernel-argument space");
@@ -2621,13 +2691,17 @@ __global__ void __launch_bounds__(kThreads) k_quant_grouped(const GroupArgs ga) 
                                     it.g, wg, nwg, tab);
 }
 
-template <bool PER_ROW>
+template <bool PER_ROW, int ERR>
 __global__ void __launch_bounds__(kThreads) k_quant_4o6_grouped(const GroupArgs ga) {
     __shared__ RTable tabs[2];
     uint32_t wg, nwg;
     const GroupItemK& it = ga.it[group_item(ga, wg, nwg)];
-    if (PER_ROW) quant_4o6_rows_wg(it.x, it.rows, it.bpr, it.amax, it.codes, it.scales, it.g, wg, nwg, tabs);
-    else quant_4o6_tensor_wg(it.x, it.blocks, it.amax, it.codes, it.scales, it.g, wg, nwg, tabs[0]);
+    if (PER_ROW)
+        quant_4o6_rows_wg<false, ERR>(it.x, it.rows, it.bpr, it.amax, ga.gden, it.codes, it.scales, it.g, wg, nwg,
+                                      tabs);
+    else
+        quant_4o6_tensor_wg<false, ERR>(it.x, it.blocks, it.amax, ga.gden, it.codes, it.scales, it.g, wg, nwg,
+                                        tabs[0]);
 }
 
 // Zeroes the per-tensor amax of every tensor (the grouped per-tensor amax publishes into zeroed values).
@@ -2717,8 +2791,8 @@ RngArgs rng_args(Philox p) {
     return RngArgs{(uint32_t)p.seed, (uint32_t)(p.seed >> 32), (uint32_t)p.offset, (uint32_t)(p.offset >> 32)};
 }
 
-hipError_t write_empty_g(const float* amax, float* g, uint32_t n, hipStream_t stream) {
-    if (n) k_write_g<<<grid_for(n, kThreads, 1), kThreads, 0, stream>>>(amax, g, n);
+hipError_t write_empty_g(const float* amax, float* g, uint32_t n, hipStream_t stream, float gden = 2688.0f) {
+    if (n) k_write_g<<<grid_for(n, kThreads, 1), kThreads, 0, stream>>>(amax, g, n, gden);
     return hipGetLastError();
 }
 
@@ -2987,10 +3061,11 @@ hipError_t launch_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, bool
 hipError_t launch_quant_16x16(const uint16_t* x, int64_t rows, int64_t cols, const float* amax, uint8_t* codes_w,
                               uint8_t* scales_w, float* g_w, uint8_t* codes_wt, uint8_t* scales_wt, float* g_wt,
                               hipStream_t stream) {
+    // an orientation is wanted when its g is given (an empty tensor's codes may be NULL)
     if (rows == 0 || cols == 0) {
         hipError_t e = hipSuccess;
-        if (codes_w) e = write_empty_g(amax, g_w, 1u, stream);
-        if (e == hipSuccess && codes_wt) e = write_empty_g(amax, g_wt, 1u, stream);
+        if (g_w) e = write_empty_g(amax, g_w, 1u, stream);
+        if (e == hipSuccess && g_wt) e = write_empty_g(amax, g_wt, 1u, stream);
         return e;
     }
     // tiles of 16 row-blocks, one 1024-thread workgroup per CU, each W^T output row receiving 128 contiguous bytes
@@ -3003,44 +3078,84 @@ hipError_t launch_quant_16x16(const uint16_t* x, int64_t rows, int64_t cols, con
 #define NVFP4_2D(W, T)                                                                                          \
     k_quant_16x16<W, T, kRB><<<grid, 64 * kRB, 0, stream>>>(x, (uint32_t)rows, (uint32_t)cols, w, amax,       \
                                                               codes_w, scales_w, g_w, codes_wt, scales_wt, g_wt)
-    if (codes_w && codes_wt) NVFP4_2D(true, true);
-    else if (codes_w) NVFP4_2D(true, false);
+    if (g_w && g_wt) NVFP4_2D(true, true);
+    else if (g_w) NVFP4_2D(true, false);
     else NVFP4_2D(false, true);
 #undef NVFP4_2D
     return hipGetLastError();
 }
 
-hipError_t launch_quant_4o6_16x16(const void* x, int64_t rows, int64_t cols, const float* amax, uint8_t* codes,
-                                  uint8_t* scales, float* g, hipStream_t stream, bool f32) {
-    if (rows == 0 || cols == 0) return write_empty_g(amax, g, 1u, stream);
-    const uint32_t ntc = (uint32_t)(cols / 16);
-    const uint32_t groups_per_rb = (ntc + kTilesPerGroup46 - 1) / kTilesPerGroup46;
-    const uint32_t items = (uint32_t)(rows / 16) * groups_per_rb;
-    // two 1024-thread workgroups per CU (48 VGPRs), each looping over its share of the items
-    const uint32_t grid = std::min<uint32_t>(items, 2u * (uint32_t)cu_count());
+hipError_t launch_quant_4o6_16x16(const void* x, int64_t rows, int64_t cols, ErrMode err, int32_t bound,
+                                  const float* amax, uint8_t* codes_w, uint8_t* scales_w, float* g_w,
+                                  uint8_t* codes_wt, uint8_t* scales_wt, float* g_wt, hipStream_t stream, bool f32) {
+    const float gden = (float)(6 * bound);
+    // an orientation is wanted when its g is given (an empty tensor's codes may be NULL)
+    if (rows == 0 || cols == 0) {
+        hipError_t e = hipSuccess;
+        if (g_w) e = write_empty_g(amax, g_w, 1u, stream, gden);
+        if (e == hipSuccess && g_wt) e = write_empty_g(amax, g_wt, 1u, stream, gden);
+        return e;
+    }
+    const uint32_t ntc = (uint32_t)(cols / 16), nbands = (uint32_t)(rows / 16);
+    const uint32_t groups = (ntc + kTilesPerGroup46 - 1) / kTilesPerGroup46;
+    const uint32_t items = nbands * groups;
+    // two 1024-thread workgroups per CU, each taking an equal run of consecutive items
+    const uint32_t slots = std::min<uint32_t>(items, 2u * (uint32_t)cu_count());
+    const uint32_t per = (items + slots - 1) / slots;
+    const uint32_t grid = (items + per - 1) / per;
     const uint4* xv = reinterpret_cast<const uint4*>(x);
-    uint2* cv = reinterpret_cast<uint2*>(codes);
-    if (f32) k_quant_4o6_16x16<true><<<grid, kThreads16, 0, stream>>>(xv, ntc, groups_per_rb, items, amax, cv, scales, g);
-    else k_quant_4o6_16x16<false><<<grid, kThreads16, 0, stream>>>(xv, ntc, groups_per_rb, items, amax, cv, scales, g);
+    uint2* cw = reinterpret_cast<uint2*>(codes_w);
+    uint2* ct = reinterpret_cast<uint2*>(codes_wt);
+#define NVFP4_46T(F, E, W, T)                                                                                  \
+    k_quant_4o6_16x16<F, E, W, T><<<grid, kThreads16, 0, stream>>>(xv, ntc, nbands, items, per, gden, amax, cw, \
+                                                                   scales_w, g_w, ct, scales_wt, g_wt)
+#define NVFP4_46O(F, E)                              \
+    do {                                             \
+        if (g_w && g_wt) NVFP4_46T(F, E, true, true);  \
+        else if (g_w) NVFP4_46T(F, E, true, false); \
+        else NVFP4_46T(F, E, false, true);           \
+    } while (0)
+#define NVFP4_46E(F)                                           \
+    do {                                                       \
+        if (err == kErrMSE) NVFP4_46O(F, kErrMSE);             \
+        else if (err == kErrMAE) NVFP4_46O(F, kErrMAE);        \
+        else NVFP4_46O(F, kErrMaxAbs);                         \
+    } while (0)
+    if (f32) NVFP4_46E(true);
+    else NVFP4_46E(false);
+#undef NVFP4_46E
+#undef NVFP4_46O
+#undef NVFP4_46T
     return hipGetLastError();
 }
 
-hipError_t launch_quant_4o6(const void* x, int64_t rows, int64_t cols, bool per_row, const float* amax,
-                            uint8_t* codes, uint8_t* scales, float* g, hipStream_t stream, bool f32) {
-    if (rows == 0 || cols == 0) return write_empty_g(amax, g, per_row ? (uint32_t)rows : 1u, stream);
+hipError_t launch_quant_4o6(const void* x, int64_t rows, int64_t cols, bool per_row, ErrMode err, int32_t bound,
+                            const float* amax, uint8_t* codes, uint8_t* scales, float* g, hipStream_t stream,
+                            bool f32) {
+    const float gden = (float)(6 * bound);
+    if (rows == 0 || cols == 0) return write_empty_g(amax, g, per_row ? (uint32_t)rows : 1u, stream, gden);
     const uint32_t bpr = (uint32_t)(cols / 16);
     const uint32_t total = (uint32_t)(rows * bpr);
     const uint4* xv = reinterpret_cast<const uint4*>(x);
     uint2* cv = reinterpret_cast<uint2*>(codes);
-    if (per_row) {
-        const uint32_t grid = (uint32_t)std::min<int64_t>(rows, (int64_t)cu_count() * 8);
-        if (f32) k_quant_4o6_rows<true><<<grid, kThreads, 0, stream>>>(xv, (uint32_t)rows, bpr, amax, cv, scales, g);
-        else k_quant_4o6_rows<false><<<grid, kThreads, 0, stream>>>(xv, (uint32_t)rows, bpr, amax, cv, scales, g);
-    } else {
-        const uint32_t grid = grid_for(total, kThreads, 8);
-        if (f32) k_quant_4o6_tensor<true><<<grid, kThreads, 0, stream>>>(xv, total, amax, cv, scales, g);
-        else k_quant_4o6_tensor<false><<<grid, kThreads, 0, stream>>>(xv, total, amax, cv, scales, g);
-    }
+    const uint32_t r = (uint32_t)rows;
+    const uint32_t grid_rows = (uint32_t)std::min<int64_t>(rows, (int64_t)cu_count() * 8);
+    const uint32_t grid_tensor = grid_for(total, kThreads, 8);
+#define NVFP4_46(F, E)                                                                                              \
+    do {                                                                                                            \
+        if (per_row) k_quant_4o6_rows<F, E><<<grid_rows, kThreads, 0, stream>>>(xv, r, bpr, amax, gden, cv, scales, g); \
+        else k_quant_4o6_tensor<F, E><<<grid_tensor, kThreads, 0, stream>>>(xv, total, amax, gden, cv, scales, g);     \
+    } while (0)
+#define NVFP4_46F(F)                                   \
+    do {                                               \
+        if (err == kErrMSE) NVFP4_46(F, kErrMSE);      \
+        else if (err == kErrMAE) NVFP4_46(F, kErrMAE); \
+        else NVFP4_46(F, kErrMaxAbs);                  \
+    } while (0)
+    if (f32) NVFP4_46F(true);
+    else NVFP4_46F(false);
+#undef NVFP4_46F
+#undef NVFP4_46
     return hipGetLastError();
 }
 
@@ -3130,12 +3245,14 @@ hipError_t launch_amax_grouped(const GroupTensor* items, int count, bool per_row
     return hipGetLastError();
 }
 
-hipError_t launch_quant_grouped(const GroupTensor* items, int count, bool per_row, int method, hipStream_t stream) {
+hipError_t launch_quant_grouped(const GroupTensor* items, int count, bool per_row, int method, ErrMode err,
+                                int32_t bound, hipStream_t stream) {
     const uint64_t cus = (uint64_t)cu_count();
+    const float gden = method == kFourOverSix ? (float)(6 * bound) : 2688.0f;
     for (int i = 0; i < count; ++i) {   // empty tensors: only g is written
         const GroupTensor& t = items[i];
         if (t.rows == 0 || t.cols == 0) {
-            const hipError_t e = write_empty_g(t.amax, t.g, per_row ? (uint32_t)t.rows : 1u, stream);
+            const hipError_t e = write_empty_g(t.amax, t.g, per_row ? (uint32_t)t.rows : 1u, stream, gden);
             if (e != hipSuccess) return e;
         }
     }
@@ -3148,15 +3265,23 @@ hipError_t launch_quant_grouped(const GroupTensor* items, int count, bool per_ro
             return capped((k.blocks + kThreads - 1) / kThreads, cus * 8);
         });
     if (ga.count == 0) return hipGetLastError();
+    ga.gden = gden;
 #define NVFP4_GQ(M, P) k_quant_grouped<M, P><<<total, kThreads, 0, stream>>>(ga)
+#define NVFP4_G46(P)                                                                                         \
+    do {                                                                                                     \
+        if (err == kErrMSE) k_quant_4o6_grouped<P, kErrMSE><<<total, kThreads, 0, stream>>>(ga);             \
+        else if (err == kErrMAE) k_quant_4o6_grouped<P, kErrMAE><<<total, kThreads, 0, stream>>>(ga);        \
+        else k_quant_4o6_grouped<P, kErrMaxAbs><<<total, kThreads, 0, stream>>>(ga);                         \
+    } while (0)
     switch (method) {
         case kRN: if (per_row) NVFP4_GQ(kRN, true); else NVFP4_GQ(kRN, false); break;
         case kSR: if (per_row) NVFP4_GQ(kSR, true); else NVFP4_GQ(kSR, false); break;
         case kRHTSR: if (per_row) NVFP4_GQ(kRHTSR, true); else NVFP4_GQ(kRHTSR, false); break;
         default:
-            if (per_row) k_quant_4o6_grouped<true><<<total, kThreads, 0, stream>>>(ga);
-            else k_quant_4o6_grouped<false><<<total, kThreads, 0, stream>>>(ga);
+            if (per_row) NVFP4_G46(true);
+            else NVFP4_G46(false);
     }
+#undef NVFP4_G46
 #undef NVFP4_GQ
     return hipGetLastError();
 }

@@ -10,6 +10,9 @@ namespace nvfp4 {
 
 enum Mode : int { kRN = 0, kSR = 1, kRHTSR = 2 };
 
+// Four-over-six error measure of a candidate: sum of squared differences, sum of magnitudes, largest magnitude.
+enum ErrMode : int { kErrMSE = 0, kErrMAE = 1, kErrMaxAbs = 2 };
+
 struct Philox {
     uint64_t seed;
     uint64_t offset;
@@ -46,18 +49,22 @@ hipError_t launch_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, bool
                              Philox rng, float* amax, uint8_t* codes, uint8_t* scales, float* g, hipStream_t stream,
                              bool tiled = false);
 
-// 16x16 RN quantization; either output (codes == nullptr) may be skipped.
+// 16x16 RN quantization; either output (g == nullptr) may be skipped.
 hipError_t launch_quant_16x16(const uint16_t* x, int64_t rows, int64_t cols, const float* amax, uint8_t* codes_w,
                               uint8_t* scales_w, float* g_w, uint8_t* codes_wt, uint8_t* scales_wt, float* g_wt,
                               hipStream_t stream);
 
-// Four-over-six with 16x16 tiles, per-tensor g, codes packed along X's rows (scales repeated per row).
-hipError_t launch_quant_4o6_16x16(const void* x, int64_t rows, int64_t cols, const float* amax, uint8_t* codes,
-                                  uint8_t* scales, float* g, hipStream_t stream, bool f32 = false);
+// Four-over-six with 16x16 tiles, per-tensor g = amax / (6 bound): W (codes packed along X's rows) and/or W^T
+// (along X's columns), each tile's scale repeated per row; either output (g == nullptr) may be skipped.
+hipError_t launch_quant_4o6_16x16(const void* x, int64_t rows, int64_t cols, ErrMode err, int32_t bound,
+                                  const float* amax, uint8_t* codes_w, uint8_t* scales_w, float* g_w,
+                                  uint8_t* codes_wt, uint8_t* scales_wt, float* g_wt, hipStream_t stream,
+                                  bool f32 = false);
 
-// Four-over-six, row-wise 1x16 RN.
-hipError_t launch_quant_4o6(const void* x, int64_t rows, int64_t cols, bool per_row, const float* amax,
-                            uint8_t* codes, uint8_t* scales, float* g, hipStream_t stream, bool f32 = false);
+// Four-over-six, row-wise 1x16 RN, g = amax / (6 bound).
+hipError_t launch_quant_4o6(const void* x, int64_t rows, int64_t cols, bool per_row, ErrMode err, int32_t bound,
+                            const float* amax, uint8_t* codes, uint8_t* scales, float* g, hipStream_t stream,
+                            bool f32 = false);
 
 // Row-wise amax of a binary32 tensor (per tensor or per row), for the binary32 four-over-six input.
 hipError_t launch_amax_f32(const float* x, int64_t rows, int64_t cols, bool per_row, float* amax, hipStream_t stream);
@@ -69,7 +76,8 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const 
 // that of the single-tensor launch.
 constexpr int kFourOverSix = 3;
 hipError_t launch_amax_grouped(const GroupTensor* items, int count, bool per_row, bool use_rht, hipStream_t stream);
-hipError_t launch_quant_grouped(const GroupTensor* items, int count, bool per_row, int method, hipStream_t stream);
+hipError_t launch_quant_grouped(const GroupTensor* items, int count, bool per_row, int method, ErrMode err,
+                                int32_t bound, hipStream_t stream);
 
 // Decode with an optional inverse RHT; y is float or bf16 bits.
 // Scale matrix [rv, nb] -> tiled layout of the FP4 GEMM (out: ceil(rv/128) * 128 * ceil(nb/4) * 4 bytes).

@@ -122,9 +122,14 @@ def test_amax_quantize_validation(lib):
 
 
 def test_4o6_and_dequantize_validation(lib):
-    assert lib.nvfp4_quantize_4o6(P, 16, 24, 1, P, out(), None) == SHAPE
-    assert lib.nvfp4_quantize_4o6(P, 16, 16, 9, P, out(), None) == UNSUP
-    assert lib.nvfp4_quantize_4o6(P, 16, 16, 1, P, out(scales=None), None) == NULL
+    q = lib.nvfp4_quantize_4o6
+    assert q(P, 16, 24, 1, 0, 448, P, out(), None) == SHAPE
+    assert q(P, 16, 16, 9, 0, 448, P, out(), None) == UNSUP
+    assert q(P, 16, 16, 1, 0, 448, P, out(scales=None), None) == NULL
+    assert q(P, 16, 16, 1, 3, 448, P, out(), None) == UNSUP          # unknown error mode
+    assert q(P, 16, 16, 1, -1, 448, P, out(), None) == UNSUP
+    assert q(P, 16, 16, 1, 2, 0, P, out(), None) == UNSUP            # bound outside 1..448
+    assert q(P, 16, 16, 1, 2, 449, P, out(), None) == UNSUP
     d = lib.nvfp4_dequantize
     assert d(out(), 4, 24, 0, P, None) == SHAPE
     assert d(out(), 4, 32, 0, P + 4, None) == ALIGN                # y must be 16-byte aligned
@@ -163,34 +168,43 @@ def test_grouped_validation(lib):
     a, q = lib.nvfp4_amax_grouped, lib.nvfp4_quantize_grouped
     assert C.sizeof(B._GroupItem) == 88                                   # the C layout of nvfp4_group_item
     assert a(items(0), 0, 0, 1, None) == OK                               # nothing to do
-    assert q(items(0), 0, 0, 2, None) == OK
+    assert q(items(0), 0, 0, 2, 0, 448, None) == OK
     assert a(items(2), -1, 0, 1, None) == SHAPE
     assert a(items(33), 33, 0, 1, None) == SHAPE                          # more than NVFP4_MAX_GROUP
     assert a(None, 2, 0, 1, None) == NULL
     assert a(items(2), 2, 5, 1, None) == UNSUP                            # unknown g mode
-    assert q(items(2), 2, 0, 9, None) == UNSUP                            # unknown rounding
+    assert q(items(2), 2, 0, 9, 0, 448, None) == UNSUP                            # unknown rounding
     assert a(items(3, {2: dict(cols=24)}), 3, 0, 1, None) == SHAPE      # item 2: cols % 16
     assert a(items(3, {1: dict(x=MIS)}), 3, 0, 1, None) == ALIGN
     assert a(items(3, {1: dict(amax=None)}), 3, 0, 1, None) == NULL
     assert a(items(2, {0: dict(rows=-1)}), 2, 0, 1, None) == SHAPE
-    assert q(items(2, {1: dict(out=B._Out(P, None, P))}), 2, 0, 0, None) == NULL
-    assert q(items(2, {1: dict(out=B._Out(P, P, P + 2))}), 2, 1, 3, None) == ALIGN
-    assert q(items(2, {0: dict(rows=1 << 20, cols=1 << 20)}), 2, 0, 1, None) == SHAPE
-    # four-over-six is a grouped method only
+    assert q(items(2, {1: dict(out=B._Out(P, None, P))}), 2, 0, 0, 0, 448, None) == NULL
+    assert q(items(2, {1: dict(out=B._Out(P, P, P + 2))}), 2, 1, 3, 0, 448, None) == ALIGN
+    assert q(items(2, {0: dict(rows=1 << 20, cols=1 << 20)}), 2, 0, 1, 0, 448, None) == SHAPE
+    # four-over-six is a grouped method only, with its knobs checked
     assert lib.nvfp4_amax_quantize(P, 16, 16, 1, 3, 0, 0, 0, P, out(), None) == UNSUP
+    assert q(items(1), 1, 0, 3, 5, 448, None) == UNSUP
+    assert q(items(1), 1, 0, 3, 0, 500, None) == UNSUP
 
 
 def test_4o6_16x16_validation(lib):
-    f = lib.nvfp4_quantize_4o6_16x16
-    assert f(P, 24, 16, P, out(), None) == SHAPE          # rows % 16
-    assert f(P, 16, 24, P, out(), None) == SHAPE          # cols % 16
-    assert f(P, -16, 16, P, out(), None) == SHAPE
-    assert f(None, 16, 16, P, out(), None) == NULL
-    assert f(P, 16, 16, None, out(), None) == NULL
-    assert f(P, 16, 16, P, None, None) == NULL
-    assert f(P, 16, 16, P, out(scales=None), None) == NULL
-    assert f(MIS, 16, 16, P, out(), None) == ALIGN
-    assert f(P, 16, 16, P, out(g=P + 2), None) == ALIGN
+    for f in (lib.nvfp4_quantize_4o6_16x16, lib.nvfp4_quantize_4o6_16x16_f32):
+        assert f(P, 24, 16, 1, 0, 448, P, out(), None, None) == SHAPE          # rows % 16
+        assert f(P, 16, 24, 1, 0, 448, P, out(), None, None) == SHAPE          # cols % 16
+        assert f(P, -16, 16, 1, 0, 448, P, out(), None, None) == SHAPE
+        assert f(None, 16, 16, 1, 0, 448, P, out(), None, None) == NULL
+        assert f(P, 16, 16, 1, 0, 448, None, out(), None, None) == NULL
+        assert f(P, 16, 16, 1, 0, 448, P, None, out(), None) == NULL           # W asked for, no row_out
+        assert f(P, 16, 16, 2, 0, 448, P, out(), None, None) == NULL           # W^T asked for, no col_out
+        assert f(P, 16, 16, 3, 0, 448, P, out(), None, None) == NULL           # both asked for
+        assert f(P, 16, 16, 1, 0, 448, P, out(scales=None), None, None) == NULL
+        assert f(P, 16, 16, 2, 0, 448, P, None, out(g=None), None) == NULL
+        assert f(MIS, 16, 16, 1, 0, 448, P, out(), None, None) == ALIGN
+        assert f(P, 16, 16, 1, 0, 448, P, out(g=P + 2), None, None) == ALIGN
+        assert f(P, 16, 16, 2, 0, 448, P, None, out(codes=MIS), None) == ALIGN
+        assert f(P, 16, 16, 4, 0, 448, P, out(), out(), None) == UNSUP         # unknown orientation
+        assert f(P, 16, 16, 1, 7, 448, P, out(), None, None) == UNSUP          # unknown error mode
+        assert f(P, 16, 16, 1, 0, 0, P, out(), None, None) == UNSUP            # bound outside 1..448
 
 
 def test_swizzle_validation(lib):
@@ -212,28 +226,29 @@ def test_tiled_scale_layout_validation(lib):
     """The tiled scale layout is taken by the 1x16 calls only (checked before anything is enqueued)."""
     T = 1
     assert lib.nvfp4_quantize_rn(P, 16, 16, 1, 3, 0, P, out(), out(layout=T), None) == UNSUP  # 16x16
-    assert lib.nvfp4_quantize_4o6(P, 16, 16, 0, P, out(layout=T), None) == UNSUP
-    assert lib.nvfp4_quantize_4o6_16x16(P, 16, 16, P, out(layout=T), None) == UNSUP
+    assert lib.nvfp4_quantize_4o6(P, 16, 16, 0, 0, 448, P, out(layout=T), None) == UNSUP
+    assert lib.nvfp4_quantize_4o6_16x16(P, 16, 16, 1, 0, 448, P, out(layout=T), None, None) == UNSUP
+    assert lib.nvfp4_quantize_4o6_16x16(P, 16, 16, 2, 0, 448, P, None, out(layout=T), None) == UNSUP
     assert lib.nvfp4_quantize_sr(P, 16, 16, 2, 0, P, 0, 0, out(layout=7), None) == UNSUP   # unknown layout
     assert lib.nvfp4_quantize_sr(P, 16, 16, 2, 0, P, 0, 0, out(scales=None, layout=T), None) == NULL
     it = (B._GroupItem * 1)()
     it[0] = B._GroupItem(P, 16, 16, P, B._Out(P, P, P, T), 0, 0, 0)
-    assert lib.nvfp4_quantize_grouped(it, 1, 0, 0, None) == UNSUP
+    assert lib.nvfp4_quantize_grouped(it, 1, 0, 0, 0, 448, None) == UNSUP
 
 
 def test_f32_input_validation(lib):
     q, a = lib.nvfp4_quantize_4o6_f32, lib.nvfp4_amax_f32
-    assert q(P, 16, 24, 0, P, out(), None) == SHAPE          # cols % 16
-    assert q(P, -1, 16, 0, P, out(), None) == SHAPE
-    assert q(P, 16, 16, 5, P, out(), None) == UNSUP          # unknown g mode
-    assert q(None, 16, 16, 0, P, out(), None) == NULL
-    assert q(P, 16, 16, 0, None, out(), None) == NULL
-    assert q(MIS, 16, 16, 0, P, out(), None) == ALIGN
-    assert q(P, 16, 16, 0, P, out(layout=1), None) == UNSUP  # tiled scales: not for four-over-six
+    assert q(P, 16, 24, 0, 0, 448, P, out(), None) == SHAPE          # cols % 16
+    assert q(P, -1, 16, 0, 0, 448, P, out(), None) == SHAPE
+    assert q(P, 16, 16, 5, 0, 448, P, out(), None) == UNSUP          # unknown g mode
+    assert q(None, 16, 16, 0, 0, 448, P, out(), None) == NULL
+    assert q(P, 16, 16, 0, 0, 448, None, out(), None) == NULL
+    assert q(MIS, 16, 16, 0, 0, 448, P, out(), None) == ALIGN
+    assert q(P, 16, 16, 0, 0, 448, P, out(layout=1), None) == UNSUP  # tiled scales: not for four-over-six
+    assert q(P, 16, 16, 0, 9, 448, P, out(), None) == UNSUP          # unknown error mode
+    assert q(P, 16, 16, 0, 1, 1000, P, out(), None) == UNSUP         # bound outside 1..448
     t = lib.nvfp4_quantize_4o6_16x16_f32
-    assert t(P, 24, 16, P, out(), None) == SHAPE and t(P, 16, 24, P, out(), None) == SHAPE
-    assert t(None, 16, 16, P, out(), None) == NULL and t(MIS, 16, 16, P, out(), None) == ALIGN
-    assert t(P, 16, 16, P, out(layout=1), None) == UNSUP
+    assert t(P, 16, 16, 1, 0, 448, P, out(layout=1), None, None) == UNSUP
     assert a(P, 16, 24, 0, P, None) == SHAPE
     assert a(None, 16, 16, 0, P, None) == NULL
     assert a(P, 16, 16, 1, None, None) == NULL

@@ -1,8 +1,9 @@
 """GPU parity of four-over-six with 16x16 tiles (nvfp4_quantize_4o6_16x16) against the CPU oracle.
 
-Codes, scales and g must equal the oracle's W outputs bit for bit.  Inputs mix tiles where map-to-4 wins and tiles
-where map-to-6 wins, ragged tile counts per workgroup, special values (NaN, infinities, zeros) and the full
-14336x4096 weight workload of the 16x16 pass.
+Codes, scales and g must equal the oracle's W and W^T outputs bit for bit, in each orientation alone and both from
+one read, under every error mode and several bounds.  Inputs mix tiles where map-to-4 wins and tiles where map-to-6
+wins, ragged tile counts per workgroup, special values (NaN, infinities, zeros) and the full 14336x4096 weight
+workload of the 16x16 pass.
 """
 import sys
 
@@ -45,29 +46,49 @@ def mixed_tiles(rows, cols, seed):
     return bits(x)
 
 
-def check(x, amax=None, expect_both=False):
+def same(out, codes, scales, g, what):
+    c, s_, gg = out.codes.cpu().numpy(), out.scales.cpu().numpy(), out.g.cpu().numpy()
+    bad = np.argwhere(c != codes)
+    assert bad.size == 0, f"{what}: {len(bad)} code byte mismatches, first {bad[:4].tolist()}"
+    bad = np.argwhere(s_ != scales)
+    assert bad.size == 0, f"{what}: {len(bad)} scale mismatches, first {bad[:4].tolist()}"
+    assert gg.view(np.uint32)[0] == g.view(np.uint32)[0] or (np.isnan(gg[0]) and np.isnan(g[0])), what
+
+
+def check(x, amax=None, expect_both=False, orient=Q.BOTH, err_mode=Q.ERR_MSE, bound=Q.BOUND_STD):
     xd = torch.from_numpy(x.view(np.int16)).cuda()
     a = Q.nvfp4_amax(xd, Q.ROWWISE, Q.G_PER_TENSOR) if amax is None else torch.from_numpy(amax).cuda()
-    out = Q.nvfp4_quantize_4o6_16x16(xd, a)
+    row, col = Q.nvfp4_quantize_4o6_16x16(xd, a, orient, err_mode, bound)
     torch.cuda.synchronize()
     oa = O.amax(x) if amax is None else amax
     np.testing.assert_array_equal(a.cpu().numpy().view(np.uint32), oa.view(np.uint32))
-    (cw, sw, gw), _, choice = O.quantize_4o6_16x16(x, oa)
-    codes, scales, g = out.codes.cpu().numpy(), out.scales.cpu().numpy(), out.g.cpu().numpy()
-    bad = np.argwhere(codes != cw)
-    assert bad.size == 0, f"{len(bad)} code byte mismatches, first {bad[:4].tolist()}"
-    bad = np.argwhere(scales != sw)
-    assert bad.size == 0, f"{len(bad)} scale mismatches, first {bad[:4].tolist()}"
-    assert g.view(np.uint32)[0] == gw.view(np.uint32)[0] or (np.isnan(g[0]) and np.isnan(gw[0]))
+    (cw, sw, gw), (ct, st, gt), choice = O.quantize_4o6_16x16(x, oa, err_mode=err_mode, bound=bound)
+    assert (row is not None) == (orient != Q.COLWISE) and (col is not None) == (orient != Q.ROWWISE)
+    if row is not None:
+        same(row, cw, sw, gw, "W")
+    if col is not None:
+        same(col, ct, st, gt, "W^T")
     if expect_both:
         assert choice.any() and not choice.all()
     return choice
 
 
-@pytest.mark.parametrize("shape", [(16, 16), (32, 64), (48, 1040), (256, 4096), (80, 2064)])
-def test_mixed_tiles(shape):
-    say("4o6 16x16 mixed", shape)
-    check(mixed_tiles(*shape, seed=shape[0] + shape[1]), expect_both=shape[0] * shape[1] >= 2048)
+@pytest.mark.parametrize("orient", [Q.ROWWISE, Q.COLWISE, Q.BOTH])
+@pytest.mark.parametrize("shape", [(16, 16), (32, 64), (48, 1040), (256, 4096), (80, 2064), (1040, 48)])
+def test_mixed_tiles(shape, orient):
+    say("4o6 16x16 mixed", shape, orient)
+    check(mixed_tiles(*shape, seed=shape[0] + shape[1]), expect_both=shape[0] * shape[1] >= 2048, orient=orient)
+
+
+@pytest.mark.parametrize("bound", [Q.BOUND_STD, Q.BOUND_HEADROOM, 37])
+@pytest.mark.parametrize("err_mode", [Q.ERR_MSE, Q.ERR_MAE, Q.ERR_MAXABS])
+def test_error_modes_and_bounds(err_mode, bound):
+    """Every error measure and bound, both orientations; the modes must actually disagree on some tiles here."""
+    x = mixed_tiles(96, 1040, seed=11)
+    say("4o6 16x16 knobs", err_mode, bound)
+    choice = check(x, expect_both=True, err_mode=err_mode, bound=bound)
+    other = O.quantize_4o6_16x16(x, O.amax(x), err_mode=(err_mode + 1) % 3, bound=bound)[2]
+    assert (choice != other).any()
 
 
 @pytest.mark.parametrize("shape", [(64, 128), (144, 4096)])
@@ -86,20 +107,29 @@ def test_special_values():
     x[32:48, 16:32] = 0x8000         # a tile of negative zeros
     for amax in (np.array([3.5], np.float32), np.array([0.0], np.float32), np.array([np.inf], np.float32),
                  np.array([np.nan], np.float32), np.array([1e-30], np.float32)):
-        check(x, amax)
+        for err_mode in (Q.ERR_MSE, Q.ERR_MAE, Q.ERR_MAXABS):
+            check(x, amax, err_mode=err_mode, bound=Q.BOUND_HEADROOM if err_mode else Q.BOUND_STD)
     check(x)                          # the tensor's own amax (NaN)
 
 
 def test_empty():
     xd = torch.empty((0, 32), dtype=torch.int16, device="cuda")
     a = torch.tensor([7.0], device="cuda")
-    out = Q.nvfp4_quantize_4o6_16x16(xd, a)
+    row, col = Q.nvfp4_quantize_4o6_16x16(xd, a, Q.BOTH)
     torch.cuda.synchronize()
-    assert out.codes.shape == (0, 16) and out.g.cpu().numpy()[0] == O.global_scale(7.0)
+    assert row.codes.shape == (0, 16) and row.g.cpu().numpy()[0] == O.global_scale(7.0)
+    assert col.codes.shape == (32, 0) and col.g.cpu().numpy()[0] == O.global_scale(7.0)
+    # g = amax / (6 bound) for another bound, also when nothing is quantized
+    row, col = Q.nvfp4_quantize_4o6_16x16(xd, a, Q.BOTH, Q.ERR_MAE, Q.BOUND_HEADROOM)
+    torch.cuda.synchronize()
+    g256 = O.quantize_4o6_16x16(np.zeros((16, 32), np.uint16), np.array([7.0], np.float32),
+                                bound=Q.BOUND_HEADROOM)[0][2][0]
+    assert row.g.cpu().numpy()[0] == g256 and col.g.cpu().numpy()[0] == g256
 
 
 @pytest.mark.slow
 def test_full_weight_14336x4096():
+    """W and W^T from one read, in the launch configuration the benchmark times."""
     x = W.make("weight_16x16_14336x4096")
     say("4o6 16x16 full weight", x.shape)
-    check(x)
+    check(x, orient=Q.BOTH)

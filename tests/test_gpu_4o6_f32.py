@@ -77,18 +77,21 @@ def test_4o6_f32_16384x8192():
     check(x, 1)
 
 
-def check_16x16(x, amax=None):
+def check_16x16(x, amax=None, orient=Q.BOTH, err_mode=Q.ERR_MSE, bound=Q.BOUND_STD):
     xd = torch.from_numpy(x).cuda()
     a = Q.nvfp4_amax_f32(xd, 0) if amax is None else torch.from_numpy(amax).cuda()
-    out = Q.nvfp4_quantize_4o6_16x16_f32(xd, a)
+    row, col = Q.nvfp4_quantize_4o6_16x16_f32(xd, a, orient, err_mode, bound)
     torch.cuda.synchronize()
     oa = O.amax_f32(x, 0) if amax is None else amax
-    (cw, sw, gw), _, _ = O.quantize_4o6_16x16_f32(x, oa)
-    bad = np.argwhere(out.codes.cpu().numpy() != cw)
-    assert bad.size == 0, f"codes: {len(bad)} mismatches, first {bad[:4].tolist()}"
-    assert np.array_equal(out.scales.cpu().numpy(), sw), "scales"
-    g = out.g.cpu().numpy()
-    assert g.view(np.uint32)[0] == gw.view(np.uint32)[0] or (np.isnan(g[0]) and np.isnan(gw[0]))
+    (cw, sw, gw), (ct, st, gt), _ = O.quantize_4o6_16x16_f32(x, oa, err_mode=err_mode, bound=bound)
+    for out, codes, scales, gg, what in ((row, cw, sw, gw, "W"), (col, ct, st, gt, "W^T")):
+        if out is None:
+            continue
+        bad = np.argwhere(out.codes.cpu().numpy() != codes)
+        assert bad.size == 0, f"{what} codes: {len(bad)} mismatches, first {bad[:4].tolist()}"
+        assert np.array_equal(out.scales.cpu().numpy(), scales), what + " scales"
+        g = out.g.cpu().numpy()
+        assert g.view(np.uint32)[0] == gg.view(np.uint32)[0] or (np.isnan(g[0]) and np.isnan(gg[0]))
 
 
 @pytest.mark.parametrize("shape", [(16, 16), (48, 1040), (256, 4096), (80, 2064)])
@@ -102,6 +105,13 @@ def test_4o6_16x16_f32_special_values():
     x = make(64, 96, seed=9, special=True)
     for amax in (None, np.array([0.0], np.float32), np.array([np.inf], np.float32), np.array([3.5], np.float32)):
         check_16x16(x, amax)
+
+
+@pytest.mark.parametrize("err_mode", [Q.ERR_MAE, Q.ERR_MAXABS])
+@pytest.mark.parametrize("orient", [Q.ROWWISE, Q.COLWISE])
+def test_4o6_16x16_f32_knobs(orient, err_mode):
+    say("4o6 16x16 f32 knobs", orient, err_mode)
+    check_16x16(make(80, 2064, seed=31, special=True), orient=orient, err_mode=err_mode, bound=Q.BOUND_HEADROOM)
 
 
 @pytest.mark.slow

@@ -152,7 +152,7 @@ def test_four_over_six_16x16_64gib():
     say("max size four-over-six 16x16", rows, cols)
     x, p = planted_input(rows, cols, 49)
     a = Q.nvfp4_amax(x, Q.ROWWISE, Q.G_PER_TENSOR)
-    out = Q.nvfp4_quantize_4o6_16x16(x, a)
+    out, outt = Q.nvfp4_quantize_4o6_16x16(x, a, Q.BOTH)
     torch.cuda.synchronize()
     assert a.item() == 3.0
     rng = np.random.default_rng(15)
@@ -160,10 +160,20 @@ def test_four_over_six_16x16_64gib():
     bands = sorted({0, p[0][0] // 16, p[1][0] // 16, nb // 2, nb - 1, *rng.integers(0, nb, 12).tolist()})
     ridx = bands_of(bands)
     sub = bits(x.index_select(0, ridx))
-    (cw, sw, gw), _, _ = O.quantize_4o6_16x16(sub, np.array([3.0], np.float32))
+    (cw, sw, gw), (ct, st, gt), _ = O.quantize_4o6_16x16(sub, np.array([3.0], np.float32))
     assert np.array_equal(out.codes.index_select(0, ridx).cpu().numpy(), cw), "codes"
     assert np.array_equal(out.scales.index_select(0, ridx).cpu().numpy(), sw), "scales"
     assert out.g.cpu().numpy().view(np.uint32)[0] == gw.view(np.uint32)[0]
-    del x, out, a
+    # W^T: band b is bytes 8 b .. 8 b + 7 of every W^T row (scale column b); sample rows of W^T too
+    cidx = torch.as_tensor(sorted({0, p[0][1], p[1][1], cols - 1, *rng.integers(0, cols, 24).tolist()}),
+                           device="cuda")
+    bidx = torch.as_tensor(bands, device="cuda")
+    byte_idx = (8 * bidx[:, None] + torch.arange(8, device="cuda")).reshape(-1)
+    got = outt.codes.index_select(0, cidx).index_select(1, byte_idx).cpu().numpy()
+    assert np.array_equal(got, ct[cidx.cpu().numpy()]), "W^T codes"
+    got = outt.scales.index_select(0, cidx).index_select(1, bidx).cpu().numpy()
+    assert np.array_equal(got, st[cidx.cpu().numpy()]), "W^T scales"
+    assert outt.g.cpu().numpy().view(np.uint32)[0] == gt.view(np.uint32)[0]
+    del x, out, outt, a
     gc.collect()
     torch.cuda.empty_cache()

@@ -214,6 +214,14 @@ def test_empty_tensors():
         assert host(a)[0] == 0.0
         out = Q.nvfp4_quantize_sr(xd, a, 1, 2, orient, 0)
         assert host(out.g)[0] == 0.0
+    # 16x16 of an empty tensor (NULL codes) still writes g in every orientation asked for
+    xd = torch.zeros((0, 64), dtype=torch.int16, device="cuda")
+    a = torch.tensor([7.0], device="cuda")
+    for orient in (Q.ROWWISE, Q.COLWISE, Q.BOTH):
+        row, col = Q.nvfp4_quantize_rn(xd, a, Q.BLOCK_16X16, orient)
+        for o in (row, col):
+            if o is not None:
+                assert host(o.g)[0] == O.global_scale(7.0)
 
 
 def test_determinism_and_fresh_randomness():
@@ -364,12 +372,14 @@ def test_4o6_sum_order_block():
         same_u8(host(out.codes), oc, "4o6 codes")
         same_u8(host(out.scales), os_, "4o6 scales")
     tb = bf16_bits(tiles)
-    (cw, sw, _), _, ch = O.quantize_4o6_16x16(tb, amax)
+    (cw, sw, _), (ct, st, _), ch = O.quantize_4o6_16x16(tb, amax)
     assert not ch.any()
-    for out in (Q.nvfp4_quantize_4o6_16x16(dev(tb), a),
-                Q.nvfp4_quantize_4o6_16x16_f32(torch.from_numpy(tiles).cuda(), a)):
-        same_u8(host(out.codes), cw, "4o6 16x16 codes")
-        same_u8(host(out.scales), sw, "4o6 16x16 scales")
+    for row, col in (Q.nvfp4_quantize_4o6_16x16(dev(tb), a, Q.BOTH),
+                     Q.nvfp4_quantize_4o6_16x16_f32(torch.from_numpy(tiles).cuda(), a, Q.BOTH)):
+        same_u8(host(row.codes), cw, "4o6 16x16 codes")
+        same_u8(host(row.scales), sw, "4o6 16x16 scales")
+        same_u8(host(col.codes), ct, "4o6 16x16 W^T codes")
+        same_u8(host(col.scales), st, "4o6 16x16 W^T scales")
 
 
 # ------------------------------------------------------------------------------------------------ HIP graphs
