@@ -1907,9 +1907,11 @@ k_quant_4o6_rows(const uint4* __restrict__ x, uint32_t rows, uint32_t bpr, const
 
 // ------------------------------------------------------------------------------------------------------------
 // Four-over-six with 16x16 tiles ([P3]: the reference quantizer takes 1x16 or 16x16 blocks), per-tensor g, codes
-// packed along X's rows (W).  One lane per row of a tile: a 16-lane row of the wave holds one tile (lane i = tile
-// row i), so a row's error sum stays in the lane and the tree over the 16 row sums, like the tile maximum, runs over
-// DPP rotations within the 16-lane row.  A wave takes 4 tiles side by side; a workgroup 64 tiles of one row-block.
+// packed along X's rows (W) and/or along its columns (W^T).  One lane per row of a tile: a 16-lane row of the wave
+// holds one tile (lane i = tile row i), so a row's error sum stays in the lane and the tree over the 16 row sums,
+// like the tile maximum, runs over DPP rotations within the 16-lane row.  A wave takes 4 tiles side by side; a
+// workgroup 64 tiles: one band of 64 tile columns (W only), or 8 bands of 8 tile columns when W^T is written, so
+// that every output row, of W and of W^T, receives 64 contiguous bytes of codes per item.
 // ------------------------------------------------------------------------------------------------------------
 constexpr uint32_t kTilesPerWave46 = 4;
 constexpr uint32_t kTilesPerGroup46 = kTilesPerWave46 * kWavesPerGroup16;
@@ -1979,7 +1981,7 @@ struct Stage46 {
     uint2 codes[2][kTilesPerGroup46][17];
     uint8_t scales[2][kTilesPerGroup46][17];
 };
-static_assert(kWavesPerGroup16 == 16 && kTilesPerGroup46 == 64, "the write-out takes one wave per row, one lane per tile");
+static_assert(kWavesPerGroup16 == 16 && kTilesPerGroup46 == 64, "a workgroup's 1024 threads write 64 tiles");
 
 // One tile row: both candidates, the tile's errors and the choice (lane 0's, broadcast over the tile's lanes).
 template <int ERR>
@@ -2032,98 +2034,223 @@ __device__ __forceinline__ uint32_t xcd_chunk(uint32_t b, uint32_t n) {
     return (n & 7u) ? b : (b & 7u) * (n >> 3) + (b >> 3);
 }
 
-// Items: (16-row band, group of 64 tile columns), numbered column-group-major, so that consecutive items are
-// consecutive bands of one column group; workgroup b takes the per_wg consecutive items of chunk xcd_chunk(b) with
-// the next item's loads in flight, and fills the multiplier table once.  W is written from LDS by rows (512 bytes
-// of codes per row and item); W^T receives 8 bytes of codes and 1 of scales per row and item, so the consecutive
-// bands of a chunk (and the chunks of one XCD) fill its 128-byte lines in one L2: those stores are cached.
-template <bool F32, int ERR, bool W, bool WT>
-__global__ void __launch_bounds__(kThreads16) __attribute__((amdgpu_waves_per_eu(8, 8)))
-k_quant_4o6_16x16(const uint4* __restrict__ x, uint32_t ntc, uint32_t nbands, uint32_t items, uint32_t per_wg,
-                  float gden, const float* __restrict__ amax, uint2* __restrict__ codes_w,
-                  uint8_t* __restrict__ scales_w, float* __restrict__ g_w, uint2* __restrict__ codes_wt,
-                  uint8_t* __restrict__ scales_wt, float* __restrict__ g_wt) {
-    __shared__ RTable tab;
-    __shared__ Stage46 st;
-    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
-    const uint32_t tw = wave * kTilesPerWave46 + (lane >> 4);   // tile of the item
-    const uint32_t i = lane & 15u;                             // row within the tile
-    // this lane's 16 elements of the item (column group cg, band rb) = block (16 rb + i) * ntc + tj of the
-    // row-wise view
-    auto load = [&](uint32_t cg, uint32_t rb, BlockWords<F32>& a) {
-        const uint32_t tj = cg * kTilesPerGroup46 + tw;
-        if (tj < ntc) a = ld_block<F32>(x, (size_t)(16 * rb + i) * ntc + tj);   // whole 16-lane rows per tile
-    };
-    const uint32_t w0 = xcd_chunk(blockIdx.x, gridDim.x) * per_wg;
-    const uint32_t n = __builtin_amdgcn_readfirstlane(w0 < items ? min(per_wg, items - w0) : 0u);
-    // (cg, rb) of the current item, stepped band by band (uniform: scalar registers)
-    uint32_t cg = __builtin_amdgcn_readfirstlane(w0 / nbands);
-    uint32_t rb = __builtin_amdgcn_readfirstlane(w0 - cg * nbands);
-    BlockWords<F32> a{};
-    if (n) load(cg, rb, a);
-    const float g = uniform_f(global_scale_den(amax[0], gden));   // uniform values kept in scalar registers
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        if (W) g_w[0] = g;
-        if (WT) g_wt[0] = g;
-    }
-    const bool gfinite = __builtin_fabsf(g) < __builtin_inff();
-    // formed unconditionally (unused when g is not finite) and moved to scalar registers: the compiler drops a
-    // readfirstlane of a value it knows to be uniform, and the division's vector result would then stay live across
-    // the item loop; passing it through an empty asm first hides that knowledge
-    Divisor dv[2] = {make_divisor_uniform(6.0f * g), make_divisor_uniform(4.0f * g)};
+// The divisors 6 g and 4 g of a per-tensor g, formed unconditionally (unused when g is not finite) and moved to scalar
+// registers: the compiler drops a readfirstlane of a value it knows to be uniform, and the division's vector result
+// would then stay live across a kernel's item loop; passing it through an empty asm first hides that knowledge.
+__device__ __forceinline__ void divisors_4o6(float g, Divisor (&dv)[2]) {
+    dv[0] = make_divisor_uniform(6.0f * g);
+    dv[1] = make_divisor_uniform(4.0f * g);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         asm volatile("" : "+v"(dv[c].d), "+v"(dv[c].y));
         dv[c].d = uniform_f(dv[c].d);
         dv[c].y = uniform_f(dv[c].y);
     }
+}
+
+// An opaque copy of the thread index: values derived from it where they are used are not kept in registers across
+// a kernel's item loop (where they would not fit beside the tile and the next item's loads).
+__device__ __forceinline__ uint32_t opaque_tid() {
+    uint32_t t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
+// W only.  Items: one band (16 rows) by 64 tile columns, band-major; workgroup b takes items b, b + grid, ... (the
+// whole grid works on neighbouring rows at any time) with the next item's loads in flight, and fills the multiplier
+// table once.  Wave v holds tile columns 4 v .. 4 v + 3 of the item; W is written from LDS by rows (512 bytes of
+// codes per row and item).
+template <bool F32, int ERR>
+__global__ void __launch_bounds__(kThreads16) __attribute__((amdgpu_waves_per_eu(8, 8)))
+k_quant_4o6_16x16(const uint4* __restrict__ x, uint32_t ntc, uint32_t ntg, uint32_t items, float gden,
+                  const float* __restrict__ amax, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
+                  float* __restrict__ gout) {
+    __shared__ RTable tab;
+    __shared__ Stage46 st;
+    // this lane's 16 elements of the item (band rb, tile group tg) = block (16 rb + i) * ntc + tj of the row-wise view
+    auto load = [&](uint32_t rb, uint32_t tg, BlockWords<F32>& a) {
+        const uint32_t t = opaque_tid(), tj = tg * kTilesPerGroup46 + (t >> 4);
+        if (tj < ntc) a = ld_block<F32>(x, (size_t)(16 * rb + (t & 15u)) * ntc + tj);
+    };
+    uint32_t w = blockIdx.x;
+    uint32_t rb = __builtin_amdgcn_readfirstlane(w / ntg);   // (rb, tg) of the current item, in scalar registers
+    uint32_t tg = __builtin_amdgcn_readfirstlane(w - rb * ntg);
+    BlockWords<F32> a{};
+    if (w < items) load(rb, tg, a);
+    const float g = uniform_f(global_scale_den(amax[0], gden));
+    if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
+    const bool gfinite = __builtin_fabsf(g) < __builtin_inff();
+    Divisor dv[2];
+    divisors_4o6(g, dv);
     fill_rtable<false>(tab, g);
-    for (uint32_t k = 0, buf = 0; k < n; ++k, buf ^= 1u) {
-        const uint32_t ncg = rb + 1 == nbands ? cg + 1 : cg, nrb = rb + 1 == nbands ? 0u : rb + 1;
-        const uint32_t t0 = cg * kTilesPerGroup46;   // first tile column of the item
-        const bool active = t0 + tw < ntc;
+    for (uint32_t buf = 0; w < items; w += gridDim.x, buf ^= 1u) {
+        const uint32_t nw = w + gridDim.x;
+        const uint32_t nrb = __builtin_amdgcn_readfirstlane(nw / ntg), ntgi = nw - nrb * ntg;
+        const uint32_t t0 = tg * kTilesPerGroup46;   // first tile column of the item
+        const bool active = t0 + (opaque_tid() >> 4) < ntc;
         float xv[16];
         widen_block<F32>(a, xv);
         // bf16: the next item's loads are in flight during this item's arithmetic; binary32 words would not fit in
         // the registers beside it, so they go out after it (overlapping the write-out)
-        if (!F32 && k + 1 < n) load(ncg, nrb, a);
+        if (!F32 && nw < items) load(nrb, ntgi, a);
         uint32_t lo = 0, hi = 0, sb = 0;
         if (active) quant_4o6_tile_row<ERR>(xv, g, gfinite, dv, tab, lo, hi, sb);
-        if (F32 && k + 1 < n) load(ncg, nrb, a);
+        if (F32 && nw < items) load(nrb, ntgi, a);
         if (active) {
-            // the slot index formed here rather than kept in a register across the loop
-            uint32_t slot = tw * 17 + i;
-            asm volatile("" : "+v"(slot));
+            const uint32_t t = opaque_tid(), slot = (t >> 4) * 17 + (t & 15u);
             (&st.codes[buf][0][0])[slot] = make_uint2(lo, hi);
             (&st.scales[buf][0][0])[slot] = (uint8_t)sb;
         }
         __syncthreads();
-        // W: wave v takes output row v of the band, lane t tile t: 512 contiguous bytes of codes, 64 of scales
-        if (W && t0 + lane < ntc) {
+        // wave v takes output row v of the band, lane l tile l: 512 contiguous bytes of codes, 64 of scales
+        const uint32_t t = opaque_tid(), wave = t >> 6, lane = t & 63u;
+        if (t0 + lane < ntc) {
             const size_t o = (size_t)(16 * rb + wave) * ntc + t0 + lane;
-            st_nt(codes_w + o, st.codes[buf][lane][wave]);
-            st_nt(scales_w + o, st.scales[buf][lane][wave]);
+            st_nt(codes + o, st.codes[buf][lane][wave]);
+            st_nt(scales + o, st.scales[buf][lane][wave]);
         }
-        // W^T: thread (tile tt, column j) assembles row 16 (t0 + tt) + j from nibble j of the tile's 16 rows (row r
-        // of the tile is element r of that row's block: byte k holds rows 2k and 2k + 1)
-        if (WT) {
-            const uint32_t tt = threadIdx.x >> 4, j = threadIdx.x & 15u;
-            if (t0 + tt < ntc) {
-                const uint32_t* words = reinterpret_cast<const uint32_t*>(&st.codes[buf][tt][0]) + (j >> 3);
-                const uint32_t sh = 4 * (j & 7u);
-                uint32_t wl = 0, wh = 0;
-#pragma unroll
-                for (int r = 0; r < 8; ++r) wl |= ((words[2 * r] >> sh) & 0xFu) << (4 * r);
-                __builtin_amdgcn_sched_barrier(0);   // eight LDS reads in flight at a time bound the live registers
-#pragma unroll
-                for (int r = 0; r < 8; ++r) wh |= ((words[2 * (r + 8)] >> sh) & 0xFu) << (4 * r);
-                const size_t row = 16 * (size_t)(t0 + tt) + j;
-                codes_wt[row * nbands + rb] = make_uint2(wl, wh);
-                scales_wt[row * nbands + rb] = st.scales[buf][tt][0];
+        rb = nrb;
+        tg = ntgi;
+    }
+}
+
+// W^T (and W).  A super-item is 16 bands by 16 tile columns (256 tiles, 256 x 256 elements of X), computed as four
+// sub-items of 4 bands by 16 tile columns (wave v of sub-item s: band 4 s + v / 4, tile columns 4 (v % 4) .. + 3)
+// into one LDS stage, then written out: every row of W and of W^T receives 128 contiguous bytes of codes and 16 of
+// scales per super-item (eight consecutive threads, 16 and 2 bytes each: one store instruction per row), the scales
+// as cached stores so that the pieces of neighbouring super-items meet in L2.  Row j of a W^T tile is column j of X's: nibble j of each of the
+// tile's 16 rows, row 2m in the low and row 2m + 1 in the high nibble of byte m.  Super-items are numbered
+// band-group-major; workgroup b takes per_wg consecutive ones (chunk xcd_chunk(b)).
+struct Stage46T {
+    // tile (band bl, column c) row i at slot (16 bl + c) 17 + i + 2 bl: the pad of 17 per tile spreads a W row's
+    // read-out over the banks, the extra 2 per band row the W^T gather's four bands
+    static constexpr uint32_t kSlots = 256 * 17 + 2 * 16;
+    uint2 codes[kSlots];
+    uint8_t scales[kSlots];
+    __device__ static uint32_t slot(uint32_t bl, uint32_t c, uint32_t i) { return (16 * bl + c) * 17 + i + 2 * bl; }
+};
+
+template <bool F32, int ERR, bool W>
+__global__ void __launch_bounds__(kThreads16) __attribute__((amdgpu_waves_per_eu(8, 8)))
+k_quant_4o6_16x16t(const uint4* __restrict__ x, uint32_t ntc, uint32_t nbands, uint32_t nsc, uint32_t items,
+                   uint32_t per_wg, float gden, const float* __restrict__ amax, uint2* __restrict__ codes_w,
+                   uint8_t* __restrict__ scales_w, float* __restrict__ g_w, uint2* __restrict__ codes_wt,
+                   uint8_t* __restrict__ scales_wt, float* __restrict__ g_wt) {
+    __shared__ RTable tab;
+    __shared__ Stage46T st;
+    // this lane's 16 elements of sub-item s of the super-item (band group bg, column group cg)
+    auto load = [&](uint32_t bg, uint32_t cg, uint32_t s, BlockWords<F32>& a) {
+        const uint32_t t = opaque_tid(), wave = t >> 6;
+        const uint32_t rb = 16 * bg + 4 * s + (wave >> 2), tj = 16 * cg + 4 * (wave & 3u) + ((t >> 4) & 3u);
+        if (rb < nbands && tj < ntc) a = ld_block<F32>(x, (size_t)(16 * rb + (t & 15u)) * ntc + tj);
+    };
+    const uint32_t w0 = xcd_chunk(blockIdx.x, gridDim.x) * per_wg;
+    const uint32_t n = __builtin_amdgcn_readfirstlane(w0 < items ? min(per_wg, items - w0) : 0u);
+    uint32_t bg = __builtin_amdgcn_readfirstlane(w0 / nsc);   // (bg, cg) of the current super-item
+    uint32_t cg = __builtin_amdgcn_readfirstlane(w0 - bg * nsc);
+    BlockWords<F32> a{};
+    if (n) load(bg, cg, 0, a);
+    const float g = uniform_f(global_scale_den(amax[0], gden));
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (W) g_w[0] = g;
+        g_wt[0] = g;
+    }
+    const bool gfinite = __builtin_fabsf(g) < __builtin_inff();
+    Divisor dv[2];
+    divisors_4o6(g, dv);
+    fill_rtable<false>(tab, g);
+    // ntc and nbands even: every row of W and W^T starts 16-byte aligned (codes) and 2-byte aligned (scales)
+    const bool even = ((ntc | nbands) & 1u) == 0;
+    for (uint32_t k = 0; k < n; ++k) {
+        const uint32_t nbg = cg + 1 == nsc ? bg + 1 : bg, ncg = cg + 1 == nsc ? 0u : cg + 1;
+        const uint32_t b0 = 16 * bg, t0 = 16 * cg;   // first band and tile column of the super-item
+#pragma unroll 1
+        for (uint32_t s = 0; s < 4; ++s) {
+            uint32_t t = opaque_tid(), wave = t >> 6;
+            const uint32_t bl = 4 * s + (wave >> 2), c = 4 * (wave & 3u) + ((t >> 4) & 3u);
+            const bool active = b0 + bl < nbands && t0 + c < ntc;
+            float xv[16];
+            widen_block<F32>(a, xv);
+            const bool more = s < 3 || k + 1 < n;
+            const uint32_t lbg = s < 3 ? bg : nbg, lcg = s < 3 ? cg : ncg, ls = (s + 1) & 3u;
+            if (!F32 && more) load(lbg, lcg, ls, a);
+            uint32_t lo = 0, hi = 0, sb = 0;
+            if (active) quant_4o6_tile_row<ERR>(xv, g, gfinite, dv, tab, lo, hi, sb);
+            if (F32 && more) load(lbg, lcg, ls, a);
+            if (active) {
+                t = opaque_tid();
+                wave = t >> 6;
+                const uint32_t sl = Stage46T::slot(4 * s + (wave >> 2), 4 * (wave & 3u) + ((t >> 4) & 3u), t & 15u);
+                st.codes[sl] = make_uint2(lo, hi);
+                st.scales[sl] = (uint8_t)sb;
             }
         }
+        __syncthreads();
+        // eight consecutive threads write one output row's 128 bytes of codes (16 each, one store instruction per
+        // row) and 16 of scales; two passes of 128 rows
+#pragma unroll 1
+        for (uint32_t pass = 0; pass < 2; ++pass) {
+            const uint32_t t = opaque_tid(), r = 128 * pass + (t >> 3), p = t & 7u;   // r: output row
+            // W: row r = 16 bl + i of the super-item, tiles 2 p and 2 p + 1
+            if (W) {
+                const uint32_t bl = r >> 4, i = r & 15u, tc = t0 + 2 * p;
+                if (b0 + bl < nbands && tc < ntc) {
+                    const uint32_t s0 = Stage46T::slot(bl, 2 * p, i), s1 = s0 + 17;
+                    const size_t o = (size_t)(16 * (b0 + bl) + i) * ntc + tc;
+                    const uint2 c0 = st.codes[s0], c1 = st.codes[s1];
+                    const bool two = tc + 1 < ntc;
+                    if (two && even) {
+                        st_nt(codes_w + o, make_uint4(c0.x, c0.y, c1.x, c1.y));
+                        *reinterpret_cast<uint16_t*>(scales_w + o) =
+                            (uint16_t)(st.scales[s0] | ((uint32_t)st.scales[s1] << 8));
+                    } else {
+                        st_nt(codes_w + o, c0);
+                        scales_w[o] = st.scales[s0];
+                        if (two) {
+                            st_nt(codes_w + o + 1, c1);
+                            scales_w[o + 1] = st.scales[s1];
+                        }
+                    }
+                }
+            }
+            // W^T: row r = 16 c + j of the super-item (tile column c, column j within it), bands 2 p and 2 p + 1
+            const uint32_t c = r >> 4, j = r & 15u, bb = b0 + 2 * p;
+            if (t0 + c < ntc && bb < nbands) {
+                const uint32_t sh = 4 * (j & 7u);
+                uint32_t wv[4];
+#pragma unroll
+                for (uint32_t u = 0; u < 2; ++u) {
+                    const uint32_t* words =
+                        reinterpret_cast<const uint32_t*>(&st.codes[Stage46T::slot(2 * p + u, c, 0)]) + (j >> 3);
+                    uint32_t wl = 0, wh = 0;
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) wl |= ((words[2 * m] >> sh) & 0xFu) << (4 * m);
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) wh |= ((words[2 * (m + 8)] >> sh) & 0xFu) << (4 * m);
+                    wv[2 * u] = wl;
+                    wv[2 * u + 1] = wh;
+                    __builtin_amdgcn_sched_barrier(0);   // one band's LDS reads in flight at a time
+                }
+                const uint8_t sc0 = st.scales[Stage46T::slot(2 * p, c, 0)];
+                const uint8_t sc1 = st.scales[Stage46T::slot(2 * p + 1, c, 0)];
+                const size_t o = (16 * (size_t)(t0 + c) + j) * nbands + bb;
+                const bool two = bb + 1 < nbands;
+                if (two && even) {
+                    st_nt(codes_wt + o, make_uint4(wv[0], wv[1], wv[2], wv[3]));
+                    *reinterpret_cast<uint16_t*>(scales_wt + o) = (uint16_t)(sc0 | ((uint32_t)sc1 << 8));
+                } else {
+                    st_nt(codes_wt + o, make_uint2(wv[0], wv[1]));
+                    scales_wt[o] = sc0;
+                    if (two) {
+                        st_nt(codes_wt + o + 1, make_uint2(wv[2], wv[3]));
+                        scales_wt[o + 1] = sc1;
+                    }
+                }
+            }
+        }
+        __syncthreads();   // the stage is rewritten by the next super-item
+        bg = nbg;
         cg = ncg;
-        rb = nrb;
     }
 }
 
@@ -3097,34 +3224,54 @@ hipError_t launch_quant_4o6_16x16(const void* x, int64_t rows, int64_t cols, Err
         return e;
     }
     const uint32_t ntc = (uint32_t)(cols / 16), nbands = (uint32_t)(rows / 16);
-    const uint32_t groups = (ntc + kTilesPerGroup46 - 1) / kTilesPerGroup46;
-    const uint32_t items = nbands * groups;
-    // two 1024-thread workgroups per CU, each taking an equal run of consecutive items
-    const uint32_t slots = std::min<uint32_t>(items, 2u * (uint32_t)cu_count());
-    const uint32_t per = (items + slots - 1) / slots;
-    const uint32_t grid = (items + per - 1) / per;
     const uint4* xv = reinterpret_cast<const uint4*>(x);
     uint2* cw = reinterpret_cast<uint2*>(codes_w);
     uint2* ct = reinterpret_cast<uint2*>(codes_wt);
-#define NVFP4_46T(F, E, W, T)                                                                                  \
-    k_quant_4o6_16x16<F, E, W, T><<<grid, kThreads16, 0, stream>>>(xv, ntc, nbands, items, per, gden, amax, cw, \
-                                                                   scales_w, g_w, ct, scales_wt, g_wt)
-#define NVFP4_46O(F, E)                              \
-    do {                                             \
-        if (g_w && g_wt) NVFP4_46T(F, E, true, true);  \
-        else if (g_w) NVFP4_46T(F, E, true, false); \
-        else NVFP4_46T(F, E, false, true);           \
+    // two 1024-thread workgroups per CU, each taking an equal run of consecutive items
+    auto grid_of = [](uint32_t items, uint32_t& per) {
+        const uint32_t slots = std::min<uint32_t>(items, 2u * (uint32_t)cu_count());
+        per = (items + slots - 1) / slots;
+        return (items + per - 1) / per;
+    };
+    if (!g_wt) {   // W only: items of one band by 64 tile columns, grid-stride
+        const uint32_t ntg = (ntc + kTilesPerGroup46 - 1) / kTilesPerGroup46, items = nbands * ntg;
+        const uint32_t grid = std::min<uint32_t>(items, 2u * (uint32_t)cu_count());
+#define NVFP4_46W(F, E) \
+    k_quant_4o6_16x16<F, E><<<grid, kThreads16, 0, stream>>>(xv, ntc, ntg, items, gden, amax, cw, scales_w, g_w)
+#define NVFP4_46WE(F)                                      \
+    do {                                                   \
+        if (err == kErrMSE) NVFP4_46W(F, kErrMSE);         \
+        else if (err == kErrMAE) NVFP4_46W(F, kErrMAE);    \
+        else NVFP4_46W(F, kErrMaxAbs);                     \
     } while (0)
-#define NVFP4_46E(F)                                           \
-    do {                                                       \
-        if (err == kErrMSE) NVFP4_46O(F, kErrMSE);             \
-        else if (err == kErrMAE) NVFP4_46O(F, kErrMAE);        \
-        else NVFP4_46O(F, kErrMaxAbs);                         \
+        if (f32) NVFP4_46WE(true);
+        else NVFP4_46WE(false);
+#undef NVFP4_46WE
+#undef NVFP4_46W
+        return hipGetLastError();
+    }
+    // W^T (and W): super-items of 16 bands by 16 tile columns
+    const uint32_t nsc = (ntc + 15) / 16, items = ((nbands + 15) / 16) * nsc;
+    uint32_t per;
+    const uint32_t grid = grid_of(items, per);
+#define NVFP4_46T(F, E, W)                                                                                       \
+    k_quant_4o6_16x16t<F, E, W><<<grid, kThreads16, 0, stream>>>(xv, ntc, nbands, nsc, items, per, gden, amax, cw, \
+                                                                 scales_w, g_w, ct, scales_wt, g_wt)
+#define NVFP4_46TO(F, E)                 \
+    do {                                 \
+        if (g_w) NVFP4_46T(F, E, true);  \
+        else NVFP4_46T(F, E, false);     \
     } while (0)
-    if (f32) NVFP4_46E(true);
-    else NVFP4_46E(false);
-#undef NVFP4_46E
-#undef NVFP4_46O
+#define NVFP4_46TE(F)                                      \
+    do {                                                   \
+        if (err == kErrMSE) NVFP4_46TO(F, kErrMSE);        \
+        else if (err == kErrMAE) NVFP4_46TO(F, kErrMAE);   \
+        else NVFP4_46TO(F, kErrMaxAbs);                    \
+    } while (0)
+    if (f32) NVFP4_46TE(true);
+    else NVFP4_46TE(false);
+#undef NVFP4_46TE
+#undef NVFP4_46TO
 #undef NVFP4_46T
     return hipGetLastError();
 }
