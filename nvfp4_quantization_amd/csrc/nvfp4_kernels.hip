@@ -1302,17 +1302,16 @@ __device__ __forceinline__ void announce(const Exchange& ex) {
 }
 
 // The cross-workgroup step of the single-read kernels (1024-thread workgroups).  The workgroup maximum of mbits
-// (magnitude bits) goes to this workgroup's slot (kept in s_own for release_slot).  Every wave then runs between()
-// (work that needs neither the amax nor the tile, e.g. the random words, overlapping the wait), and wave 0 reads the
+// (magnitude bits) goes to this workgroup's slot (kept in s_own for release_slot), and wave 0 then reads the
 // slots of every workgroup (lane l watches slots l + 64 k, up to eight loads in flight together: each read is a round
 // trip to memory, since the slots are shared by all XCDs; a slot once seen with its maximum is not read again),
 // reduces them and, when none is missing, fills tab for g = amax / 2688, while the other waves wait at the one
 // barrier that follows.  Returns the maximum over the slots seen, equal in every thread; missing[l] (l < 64) gets
 // bit k set for each slot l + 64 k not seen, and nmissing (uniform) their count (then tab is not filled).  Uses
 // red[16].
-template <bool RHT, typename Between>
+template <bool RHT>
 __device__ uint32_t exchange_max(uint32_t mbits, const Exchange& ex, uint32_t* red, uint32_t* missing,
-                                 uint32_t* s_own, RTable& tab, uint32_t& nmissing, const Between& between) {
+                                 uint32_t* s_own, RTable& tab, uint32_t& nmissing) {
     __shared__ uint32_t s_max, s_nmiss;
     const uint32_t lane = threadIdx.x & 63u;
     mbits = wave_max(mbits);
@@ -1326,7 +1325,6 @@ __device__ uint32_t exchange_max(uint32_t mbits, const Exchange& ex, uint32_t* r
             __hip_atomic_store(own_slot(ex, lane), ((uint64_t)ex.epoch << 32) | m, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
-    between();
     if (threadIdx.x < 64) {
         const uint64_t* copy = slot_copy(ex, __builtin_amdgcn_readfirstlane(blockIdx.x) % kSlotCopies);
         const uint32_t nk = (gridDim.x + 63) / 64;   // slots per lane, <= 32
@@ -1382,12 +1380,6 @@ __device__ uint32_t exchange_max(uint32_t mbits, const Exchange& ex, uint32_t* r
     __syncthreads();
     nmissing = __builtin_amdgcn_readfirstlane(s_nmiss);
     return __builtin_amdgcn_readfirstlane(s_max);
-}
-
-template <bool RHT>
-__device__ uint32_t exchange_max(uint32_t mbits, const Exchange& ex, uint32_t* red, uint32_t* missing,
-                                 uint32_t* s_own, RTable& tab, uint32_t& nmissing) {
-    return exchange_max<RHT>(mbits, ex, red, missing, s_own, tab, nmissing, [] {});
 }
 
 // Whether slot s was missing in the exchange (missing as written by exchange_max).
@@ -1476,6 +1468,17 @@ k_amax_quant_colwise4(const uint16_t* __restrict__ x, uint32_t rows, uint32_t co
     uint32_t mbits = 0;
     if (active) {
         load_col4_tile(x, cols, pos, v);
+        // the random words of the 4 blocks, generated while the loads are in flight (the vector unit is idle then)
+        // and parked in LDS; generated later, between publishing and polling, they delayed the last workgroups'
+        // publication and so every workgroup's wait
+        if (SR) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const Rand4 r = block_rand_inv(rng, (pos.c4 + j) * nrb + pos.rb);
+                st.e[wave][j * 64 + pos.lane] = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
+                __builtin_amdgcn_sched_barrier(0);   // one call at a time: the tile's registers are in flight
+            }
+        }
         if (RHT) flip_col4_tile(v, sign_mask);   // the random signs once, on the packed words
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -1490,18 +1493,7 @@ k_amax_quant_colwise4(const uint16_t* __restrict__ x, uint32_t rows, uint32_t co
 #pragma unroll
     for (int k = 0; k < 16; ++k) asm volatile("" : "+v"(v[k].x), "+v"(v[k].y));
     uint32_t nmiss;
-    // the random words of the 4 blocks, generated while the workgroups wait for each other's maxima, parked in LDS
-    uint32_t abits = exchange_max<RHT>(mbits, ex, red, missing, &s_own, tab, nmiss, [&] {
-        if (SR && active) {
-            const Col4Pos p = col4_at(pos.group, pos.strip);   // formed here rather than held since the start
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const Rand4 r = block_rand_inv(rng, (p.c4 + j) * nrb + p.rb);
-                st.e[wave][j * 64 + p.lane] = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-    });
+    uint32_t abits = exchange_max<RHT>(mbits, ex, red, missing, &s_own, tab, nmiss);
     if (nmiss) {
         // slow route: the maxima of the tiles whose slots were not seen, from the tensor, then the own tile again
         __shared__ uint32_t s_bits;
