@@ -20,7 +20,8 @@ Also printed in the same JSON line:
                 traffic measured with rocprofv3 counters (null unless measured on the current kernel source);
   cpu_baseline  the CPU oracle (test infrastructure) on the same workload, timed on the host cores;
   extra         the two-pass step (nvfp4_amax + nvfp4_quantize_rht_sr), the quantize kernel alone given a
-                device-resident amax (the pages' kernel-only comparison), the amax call, the row-wise RHT+SR pass,
+                device-resident amax (the pages' kernel-only comparison, with a roofline object of its own and its
+                counter-measured traffic), the amax call, the row-wise RHT+SR pass,
                 and under "configs" the other workloads: the 256x1024 RHT+SR/RN pair, the 8192x4096 row-wise RN
                 activation pass, the 14336x4096 16x16 weight pass (W and W^T), the 16384x8192 four-over-six pass
                 the decode of its output (to float, and to bf16 through the fused decode), and the fused decode of the
@@ -49,6 +50,7 @@ WORKLOAD = "wgrad_colwise_rht_sr_8192x4096"
 ROWS, COLS = 8192, 4096
 SEED = 2
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_amax_quant_colwise_rht_sr_8192x4096_traffic.txt")
+QUANT_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_quant_colwise_rht_sr_8192x4096_traffic.txt")
 COPY_BYTES = 128 << 20       # the calibration copy for the L2-to-memory byte counters
 PERCENTILE_LAUNCHES = 200    # launches timed one by one for the percentiles
 
@@ -69,8 +71,8 @@ def parse():
     p.add_argument("--config-launches", type=int, default=50,
                    help="graph launches per kernel for the other workloads (0 skips them)")
     p.add_argument("--counter-launches", type=int, default=0, metavar="N",
-                   help="for a rocprofv3 --pmc run: launch N steps eagerly, then N copies of a 128 MiB buffer "
-                        "(the calibration copy), and exit without timing")
+                   help="for a rocprofv3 --pmc run: launch N steps eagerly, N quantize-only calls (amax given), "
+                        "then N copies of a 128 MiB buffer (the calibration copy), and exit without timing")
     return p.parse_args()
 
 
@@ -83,11 +85,11 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per step-kernel launch from the committed counter summary, or None when the kernels have changed."""
+def measured_traffic(path: str = TRAFFIC_SUMMARY):
+    """HBM bytes per launch of a kernel from its committed counter summary, or None when the kernels have changed."""
     fields = {}
     try:
-        with open(TRAFFIC_SUMMARY) as f:
+        with open(path) as f:
             for line in f:
                 key, sep, val = line.partition(":")
                 if sep:
@@ -475,14 +477,17 @@ def measure(args, Q, W, dev, x_bits, x0, xs, outs, amaxes, masks, step, nbuf, st
     if args.counter_launches:
         for k in range(args.counter_launches):
             step(k)
+        for k in range(args.counter_launches):           # the quantize kernel alone, on the amax the steps wrote
+            Q.nvfp4_quantize_rht_sr(xs[k % nbuf], amaxes[k % nbuf], masks[k % 64], SEED, k, Q.COLWISE,
+                                    Q.G_PER_TENSOR, out=outs[k % nbuf])
         # four source/destination pairs in turn, so that no copy finds its source still in the L2 caches (32 MB)
         srcs = [torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).uniform_() for _ in range(4)]
         dsts = [torch.empty_like(srcs[0]) for _ in range(4)]
         for k in range(args.counter_launches):
             dsts[k % 4].copy_(srcs[k % 4])
         torch.cuda.synchronize()
-        print(f"counter pass: {args.counter_launches} steps and {args.counter_launches} copies of "
-              f"{COPY_BYTES >> 20} MiB launched", flush=True)
+        print(f"counter pass: {args.counter_launches} steps, {args.counter_launches} quantize-only calls and "
+              f"{args.counter_launches} copies of {COPY_BYTES >> 20} MiB launched", flush=True)
         return None
     for k in range(args.warmup):                       # eager warm-up (also initialises the library)
         step(k)
@@ -576,6 +581,12 @@ def measure(args, Q, W, dev, x_bits, x0, xs, outs, amaxes, masks, step, nbuf, st
             "quantize_kernel_frac_of_hbm_peak": round(q_gbs / HBM_PEAK_GBS, 4),
             "quantize_kernel_frac_of_stream_ceiling": round(q_gbs / ceiling["gbs"], 4),
             "quantize_kernel_event_bracketed_launch_us": quant_pct,
+            "quantize_kernel_roofline": {"kernel": "k_quant_colwise4<RHT+SR> (quantize only, device-resident amax)",
+                                         "bound": "hbm", "achieved": round(q_gbs, 2), "peak": HBM_PEAK_GBS,
+                                         "unit": "GB/s", "frac": round(q_gbs / HBM_PEAK_GBS, 4),
+                                         "traffic": measured_traffic(QUANT_TRAFFIC_SUMMARY),
+                                         "algorithmic_bytes_per_launch": step_bytes,
+                                         "mean_launch_ms": round(q_ms, 5)},
             "amax_call_ms": round(amax_ms, 5),
             "amax_call_gbs_read": round(2 * ROWS * COLS / (amax_ms * 1e-3) / 1e9, 2),
             "rowwise_rht_sr_kernel_ms": round(row_ms, 5),
