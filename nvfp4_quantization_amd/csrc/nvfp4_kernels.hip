@@ -1995,8 +1995,9 @@ __device__ __forceinline__ void quant_4o6_tile_row(const float (&xv)[16], float 
     }
     uint32_t cl[2], ch[2], cs[2];
     float err[2];
+    constexpr int NC = ERR == kErrNone ? 1 : 2;   // kErrNone: map-to-6 alone
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < NC; ++c) {
         cs[c] = scale_code(m, dv[c]);
         const float rr = tab.r[cs[c]];
         float q[16];
@@ -2011,7 +2012,13 @@ __device__ __forceinline__ void quant_4o6_tile_row(const float (&xv)[16], float 
             cl[c] = patch_nan8(cl[c], q0);
             ch[c] = patch_nan8(ch[c], q1);
         }
-        err[c] = tile_error<ERR>(xv, cl[c], ch[c], e4m3_decode(cs[c]), g);
+        if (ERR != kErrNone) err[c] = tile_error<ERR>(xv, cl[c], ch[c], e4m3_decode(cs[c]), g);
+    }
+    if (ERR == kErrNone) {
+        lo = cl[0];
+        hi = ch[0];
+        sb = cs[0];
+        return;
     }
     // lane 0's comparison; ties and NaN keep map-to-6
     const bool four = row_bcast0(err[1] < err[0] ? 1u : 0u) != 0u;
@@ -2106,42 +2113,82 @@ k_quant_4o6_16x16(const uint4* __restrict__ x, uint32_t ntc, uint32_t ntg, uint3
     }
 }
 
-// W^T (and W).  A super-item is 16 bands by 16 tile columns (256 tiles, 256 x 256 elements of X), computed as four
-// sub-items of 4 bands by 16 tile columns (wave v of sub-item s: band 4 s + v / 4, tile columns 4 (v % 4) .. + 3)
-// into one LDS stage, then written out: every row of W and of W^T receives 128 contiguous bytes of codes and 16 of
-// scales per super-item (eight consecutive threads, 16 and 2 bytes each: one store instruction per row), the scales
-// as cached stores so that the pieces of neighbouring super-items meet in L2.  Row j of a W^T tile is column j of X's: nibble j of each of the
-// tile's 16 rows, row 2m in the low and row 2m + 1 in the high nibble of byte m.  Super-items are numbered
-// band-group-major; workgroup b takes per_wg consecutive ones (chunk xcd_chunk(b)).
-struct Stage46T {
-    // tile (band bl, column c) row i at slot (16 bl + c) 17 + i + 2 bl: the pad of 17 per tile spreads a W row's
-    // read-out over the banks, the extra 2 per band row the W^T gather's four bands
-    static constexpr uint32_t kSlots = 256 * 17 + 2 * 16;
-    uint2 codes[kSlots];
-    uint8_t scales[kSlots];
-    __device__ static uint32_t slot(uint32_t bl, uint32_t c, uint32_t i) { return (16 * bl + c) * 17 + i + 2 * bl; }
+// A tile's codes transposed as a 16 x 16 matrix of nibbles across its 16 lanes: lane i holds row i (nibble k of
+// (lo, hi) = element k) and gets column i (nibble k = element k of column i), the packing of a W^T row.  The usual
+// recursive block transpose: 8 x 8 blocks swapped across the two words (partner lane i ^ 8), then in each word 4 x 4,
+// 2 x 2 and 1 x 1 blocks (partners i ^ 4, i ^ 2, i ^ 1): each lane sends its word rotated so that the block its
+// partner needs sits where the partner takes it, and keeps its own block by a bit-field insert.
+__device__ __forceinline__ uint32_t dpp_xor8(uint32_t v) { return row_ror<8>(v); }
+__device__ __forceinline__ uint32_t dpp_xor4(uint32_t v) {
+    // lane i ^ 7 within the half row, then i ^ 3 within the quad
+    const int h = __builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_mov_dpp(h, 0x1B, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ void transpose16_nibbles(uint32_t& lo, uint32_t& hi) {
+    const uint32_t i = __lane_id() & 15u;
+    // 8 x 8 blocks: rows 0..7 give their elements 8..15 (hi) to rows 8..15, which give their elements 0..7 (lo)
+    const uint32_t recv = dpp_xor8((i & 8u) ? lo : hi);
+    if (i & 8u) lo = recv;
+    else hi = recv;
+    const uint32_t m4 = (i & 4u) ? 0xFFFF0000u : 0x0000FFFFu;
+    const uint32_t m2 = (i & 2u) ? 0xFF00FF00u : 0x00FF00FFu;
+    const uint32_t m1 = (i & 1u) ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
+    const uint32_t sh1 = (i & 1u) ? 28u : 4u;
+    uint32_t* wp[2] = {&lo, &hi};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        uint32_t w = *wp[k];
+        uint32_t r = dpp_xor4(__builtin_amdgcn_alignbit(w, w, 16));     // halves swapped
+        w = (w & m4) | (r & ~m4);
+        r = dpp_xor2(__builtin_amdgcn_perm(w, w, 0x02030001u));          // bytes swapped within each half
+        w = (w & m2) | (r & ~m2);
+        r = dpp_xor1(__builtin_amdgcn_alignbit(w, w, sh1));              // rotated by one nibble, either way
+        w = (w & m1) | (r & ~m1);
+        *wp[k] = w;
+    }
+}
+
+// W^T (and W).  Items of 8 bands by 8 tile columns (128 x 128 elements of X): wave v holds band v / 2, tile columns
+// 4 (v % 2) .. + 3 (lane 16 k + i: row i of tile k), and after quantizing transposes each tile's codes across its
+// lanes (transpose16_nibbles), so that lane i also holds row i of the tile in W^T.  Both are staged in LDS,
+// double-buffered (one barrier per item), and written by rows: every row of W and of W^T receives 64 contiguous
+// bytes of codes (four threads, 16 bytes each) and 8 of scales per item, the scales as cached stores so that the
+// pieces of neighbouring items meet in L2.  Items are numbered band-group-major; workgroup b takes per_wg
+// consecutive ones (chunk xcd_chunk(b)) with the next item's loads in flight.
+struct Stage16T {
+    uint2 w[2][64][17];     // [buffer][tile 8 bl + c][row i]: W codes; the pad spreads the row read-out over banks
+    uint2 t[2][64][17];     // [buffer][tile 8 c + bl][column j]: W^T codes
+    uint8_t s[2][64];       // [buffer][8 bl + c]: tile scales
+    uint8_t st[2][64];      // [buffer][8 c + bl]: the same, W^T order
 };
 
 template <bool F32, int ERR, bool W>
 __global__ void __launch_bounds__(kThreads16) __attribute__((amdgpu_waves_per_eu(8, 8)))
-k_quant_4o6_16x16t(const uint4* __restrict__ x, uint32_t ntc, uint32_t nbands, uint32_t nsc, uint32_t items,
+k_quant_4o6_16x16t(const uint4* __restrict__ x, uint32_t ntc, uint32_t nbands, uint32_t ncg, uint32_t items,
                    uint32_t per_wg, float gden, const float* __restrict__ amax, uint2* __restrict__ codes_w,
                    uint8_t* __restrict__ scales_w, float* __restrict__ g_w, uint2* __restrict__ codes_wt,
                    uint8_t* __restrict__ scales_wt, float* __restrict__ g_wt) {
     __shared__ RTable tab;
-    __shared__ Stage46T st;
-    // this lane's 16 elements of sub-item s of the super-item (band group bg, column group cg)
-    auto load = [&](uint32_t bg, uint32_t cg, uint32_t s, BlockWords<F32>& a) {
+    __shared__ Stage16T st;
+    // this lane's 16 elements of the item (band group bg, column group cg)
+    auto load = [&](uint32_t bg, uint32_t cg, BlockWords<F32>& a) {
         const uint32_t t = opaque_tid(), wave = t >> 6;
-        const uint32_t rb = 16 * bg + 4 * s + (wave >> 2), tj = 16 * cg + 4 * (wave & 3u) + ((t >> 4) & 3u);
+        const uint32_t rb = 8 * bg + (wave >> 1), tj = 8 * cg + 4 * (wave & 1u) + ((t >> 4) & 3u);
         if (rb < nbands && tj < ntc) a = ld_block<F32>(x, (size_t)(16 * rb + (t & 15u)) * ntc + tj);
     };
     const uint32_t w0 = xcd_chunk(blockIdx.x, gridDim.x) * per_wg;
     const uint32_t n = __builtin_amdgcn_readfirstlane(w0 < items ? min(per_wg, items - w0) : 0u);
-    uint32_t bg = __builtin_amdgcn_readfirstlane(w0 / nsc);   // (bg, cg) of the current super-item
-    uint32_t cg = __builtin_amdgcn_readfirstlane(w0 - bg * nsc);
+    uint32_t bg = __builtin_amdgcn_readfirstlane(w0 / ncg);   // (bg, cg) of the current item
+    uint32_t cg = __builtin_amdgcn_readfirstlane(w0 - bg * ncg);
     BlockWords<F32> a{};
-    if (n) load(bg, cg, 0, a);
+    if (n) load(bg, cg, a);
     const float g = uniform_f(global_scale_den(amax[0], gden));
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         if (W) g_w[0] = g;
@@ -2151,98 +2198,65 @@ k_quant_4o6_16x16t(const uint4* __restrict__ x, uint32_t ntc, uint32_t nbands, u
     Divisor dv[2];
     divisors_4o6(g, dv);
     fill_rtable<false>(tab, g);
-    // ntc and nbands even: every row of W and W^T starts 16-byte aligned (codes) and 2-byte aligned (scales)
-    const bool even = ((ntc | nbands) & 1u) == 0;
-    for (uint32_t k = 0; k < n; ++k) {
-        const uint32_t nbg = cg + 1 == nsc ? bg + 1 : bg, ncg = cg + 1 == nsc ? 0u : cg + 1;
-        const uint32_t b0 = 16 * bg, t0 = 16 * cg;   // first band and tile column of the super-item
-#pragma unroll 1
-        for (uint32_t s = 0; s < 4; ++s) {
-            uint32_t t = opaque_tid(), wave = t >> 6;
-            const uint32_t bl = 4 * s + (wave >> 2), c = 4 * (wave & 3u) + ((t >> 4) & 3u);
-            const bool active = b0 + bl < nbands && t0 + c < ntc;
+    for (uint32_t k = 0, buf = 0; k < n; ++k, buf ^= 1u) {
+        const uint32_t nbg = cg + 1 == ncg ? bg + 1 : bg, ncgi = cg + 1 == ncg ? 0u : cg + 1;
+        {
+            const uint32_t t = opaque_tid(), wave = t >> 6;
+            const uint32_t bl = wave >> 1, c = 4 * (wave & 1u) + ((t >> 4) & 3u);
+            const bool active = 8 * bg + bl < nbands && 8 * cg + c < ntc;
             float xv[16];
             widen_block<F32>(a, xv);
-            const bool more = s < 3 || k + 1 < n;
-            const uint32_t lbg = s < 3 ? bg : nbg, lcg = s < 3 ? cg : ncg, ls = (s + 1) & 3u;
-            if (!F32 && more) load(lbg, lcg, ls, a);
+            // bf16: the next item's loads are in flight during this item's arithmetic; binary32 words would not fit
+            // in the registers beside it, so they go out after it
+            if (!F32 && k + 1 < n) load(nbg, ncgi, a);
             uint32_t lo = 0, hi = 0, sb = 0;
             if (active) quant_4o6_tile_row<ERR>(xv, g, gfinite, dv, tab, lo, hi, sb);
-            if (F32 && more) load(lbg, lcg, ls, a);
+            if (F32 && k + 1 < n) load(nbg, ncgi, a);
+            uint32_t tlo = lo, thi = hi;
+            transpose16_nibbles(tlo, thi);   // a tile's 16 lanes are all active or all inactive
             if (active) {
-                t = opaque_tid();
-                wave = t >> 6;
-                const uint32_t sl = Stage46T::slot(4 * s + (wave >> 2), 4 * (wave & 3u) + ((t >> 4) & 3u), t & 15u);
-                st.codes[sl] = make_uint2(lo, hi);
-                st.scales[sl] = (uint8_t)sb;
+                const uint32_t i = t & 15u;
+                if (W) st.w[buf][8 * bl + c][i] = make_uint2(lo, hi);
+                st.t[buf][8 * c + bl][i] = make_uint2(tlo, thi);
+                if (i == 0) {
+                    st.s[buf][8 * bl + c] = (uint8_t)sb;
+                    st.st[buf][8 * c + bl] = (uint8_t)sb;
+                }
             }
         }
         __syncthreads();
-        // eight consecutive threads write one output row's 128 bytes of codes (16 each, one store instruction per
-        // row) and 16 of scales; two passes of 128 rows
-#pragma unroll 1
-        for (uint32_t pass = 0; pass < 2; ++pass) {
-            const uint32_t t = opaque_tid(), r = 128 * pass + (t >> 3), p = t & 7u;   // r: output row
-            // W: row r = 16 bl + i of the super-item, tiles 2 p and 2 p + 1
-            if (W) {
-                const uint32_t bl = r >> 4, i = r & 15u, tc = t0 + 2 * p;
-                if (b0 + bl < nbands && tc < ntc) {
-                    const uint32_t s0 = Stage46T::slot(bl, 2 * p, i), s1 = s0 + 17;
-                    const size_t o = (size_t)(16 * (b0 + bl) + i) * ntc + tc;
-                    const uint2 c0 = st.codes[s0], c1 = st.codes[s1];
-                    const bool two = tc + 1 < ntc;
-                    if (two && even) {
-                        st_nt(codes_w + o, make_uint4(c0.x, c0.y, c1.x, c1.y));
-                        *reinterpret_cast<uint16_t*>(scales_w + o) =
-                            (uint16_t)(st.scales[s0] | ((uint32_t)st.scales[s1] << 8));
-                    } else {
-                        st_nt(codes_w + o, c0);
-                        scales_w[o] = st.scales[s0];
-                        if (two) {
-                            st_nt(codes_w + o + 1, c1);
-                            scales_w[o + 1] = st.scales[s1];
-                        }
-                    }
-                }
+        // threads 0..511 write W, 512..1023 W^T: output row r of the item (0..127), tile pair q (16 bytes of codes)
+        const uint32_t t = opaque_tid(), half = t >> 9, r = (t >> 2) & 127u, q = t & 3u;
+        // W: row r = 16 bl + i, tile columns 8 cg + 2 q, + 1; W^T: row r = 16 c + j, bands 8 bg + 2 q, + 1
+        const uint32_t blk = r >> 4, e = r & 15u;
+        const uint32_t nrow = half ? ntc : nbands, ncol = half ? nbands : ntc;        // tiles down, tiles across
+        const uint32_t rblk = half ? 8 * cg + blk : 8 * bg + blk;                     // the row's tile index down
+        const uint32_t c0 = (half ? 8 * bg : 8 * cg) + 2 * q;                         // first tile across
+        if ((half || W) && rblk < nrow && c0 < ncol) {
+            const uint2(&sw)[64][17] = half ? st.t[buf] : st.w[buf];
+            const uint2 a0 = sw[8 * blk + 2 * q][e], a1 = sw[8 * blk + 2 * q + 1][e];
+            uint2* cdst = half ? codes_wt : codes_w;
+            const size_t o = (size_t)(16 * rblk + e) * ncol + c0;
+            if (c0 + 1 < ncol && (ncol & 1u) == 0) {
+                st_nt(reinterpret_cast<uint4*>(cdst + o), make_uint4(a0.x, a0.y, a1.x, a1.y));
+            } else {
+                st_nt(cdst + o, a0);
+                if (c0 + 1 < ncol) st_nt(cdst + o + 1, a1);
             }
-            // W^T: row r = 16 c + j of the super-item (tile column c, column j within it), bands 2 p and 2 p + 1
-            const uint32_t c = r >> 4, j = r & 15u, bb = b0 + 2 * p;
-            if (t0 + c < ntc && bb < nbands) {
-                const uint32_t sh = 4 * (j & 7u);
-                uint32_t wv[4];
-#pragma unroll
-                for (uint32_t u = 0; u < 2; ++u) {
-                    const uint32_t* words =
-                        reinterpret_cast<const uint32_t*>(&st.codes[Stage46T::slot(2 * p + u, c, 0)]) + (j >> 3);
-                    uint32_t wl = 0, wh = 0;
-#pragma unroll
-                    for (int m = 0; m < 8; ++m) wl |= ((words[2 * m] >> sh) & 0xFu) << (4 * m);
-#pragma unroll
-                    for (int m = 0; m < 8; ++m) wh |= ((words[2 * (m + 8)] >> sh) & 0xFu) << (4 * m);
-                    wv[2 * u] = wl;
-                    wv[2 * u + 1] = wh;
-                    __builtin_amdgcn_sched_barrier(0);   // one band's LDS reads in flight at a time
-                }
-                const uint8_t sc0 = st.scales[Stage46T::slot(2 * p, c, 0)];
-                const uint8_t sc1 = st.scales[Stage46T::slot(2 * p + 1, c, 0)];
-                const size_t o = (16 * (size_t)(t0 + c) + j) * nbands + bb;
-                const bool two = bb + 1 < nbands;
-                if (two && even) {
-                    st_nt(codes_wt + o, make_uint4(wv[0], wv[1], wv[2], wv[3]));
-                    *reinterpret_cast<uint16_t*>(scales_wt + o) = (uint16_t)(sc0 | ((uint32_t)sc1 << 8));
+            if (q == 0) {
+                // 8 scale bytes of the row (fewer at the right edge)
+                const uint8_t* ss = half ? &st.st[buf][8 * blk] : &st.s[buf][8 * blk];
+                uint8_t* sdst = (half ? scales_wt : scales_w) + (o - 2 * q);
+                const uint32_t nv = min(8u, ncol - (c0 - 2 * q));
+                if (nv == 8 && (ncol & 7u) == 0) {
+                    *reinterpret_cast<uint2*>(sdst) = *reinterpret_cast<const uint2*>(ss);
                 } else {
-                    st_nt(codes_wt + o, make_uint2(wv[0], wv[1]));
-                    scales_wt[o] = sc0;
-                    if (two) {
-                        st_nt(codes_wt + o + 1, make_uint2(wv[2], wv[3]));
-                        scales_wt[o + 1] = sc1;
-                    }
+                    for (uint32_t u = 0; u < nv; ++u) sdst[u] = ss[u];
                 }
             }
         }
-        __syncthreads();   // the stage is rewritten by the next super-item
         bg = nbg;
-        cg = ncg;
+        cg = ncgi;
     }
 }
 
@@ -3187,9 +3201,16 @@ hipError_t launch_quant_16x16(const uint16_t* x, int64_t rows, int64_t cols, con
         if (e == hipSuccess && g_wt) e = write_empty_g(amax, g_wt, 1u, stream);
         return e;
     }
-    // tiles of 16 row-blocks, one 1024-thread workgroup per CU, each W^T output row receiving 128 contiguous bytes
-    // of codes per tile (tiles of 8 row-blocks with two workgroups per CU measured 58.5 us against 47.6 us at
-    // 14336 x 4096: 64-byte runs)
+    // W alone: the four-over-six band kernel keeping the map-to-6 candidate alone, which is this quantization with
+    // g = amax / 2688 (28.8 us against 33.2 us for the kernel below at 14336 x 4096)
+    if (!g_wt)
+        return launch_quant_4o6_16x16(x, rows, cols, kErrNone, 448, amax, codes_w, scales_w, g_w, codes_wt, scales_wt,
+                                      g_wt, stream, false);
+    // W^T (and W): tiles of 16 row-blocks, one 1024-thread workgroup per CU, each W^T output row receiving 128
+    // contiguous bytes of codes per tile.  Measured at 14336 x 4096 and not kept: tiles of 8 row-blocks with two
+    // workgroups per CU (58.5 against 47.6 us: 64-byte runs), of 14 row-blocks (512 tiles, two per CU: 65 against
+    // 43.5 us: 112-byte runs that straddle 128-byte lines), and the four-over-six item kernel keeping map-to-6
+    // (48.5 us: 256-byte load runs and 64-byte store runs).
     constexpr int kRB = kColRB;
     uint32_t grid;
     const ColGrid w = col_grid(rows, cols, grid, kRB);
@@ -3197,8 +3218,7 @@ hipError_t launch_quant_16x16(const uint16_t* x, int64_t rows, int64_t cols, con
 #define NVFP4_2D(W, T)                                                                                          \
     k_quant_16x16<W, T, kRB><<<grid, 64 * kRB, 0, stream>>>(x, (uint32_t)rows, (uint32_t)cols, w, amax,       \
                                                               codes_w, scales_w, g_w, codes_wt, scales_wt, g_wt)
-    if (g_w && g_wt) NVFP4_2D(true, true);
-    else if (g_w) NVFP4_2D(true, false);
+    if (g_w) NVFP4_2D(true, true);
     else NVFP4_2D(false, true);
 #undef NVFP4_2D
     return hipGetLastError();
@@ -3236,18 +3256,19 @@ hipError_t launch_quant_4o6_16x16(const void* x, int64_t rows, int64_t cols, Err
         else if (err == kErrMAE) NVFP4_46W(F, kErrMAE);    \
         else NVFP4_46W(F, kErrMaxAbs);                     \
     } while (0)
-        if (f32) NVFP4_46WE(true);
+        if (err == kErrNone) NVFP4_46W(false, kErrNone);   // the 16x16 RN quantizer (bf16 only)
+        else if (f32) NVFP4_46WE(true);
         else NVFP4_46WE(false);
 #undef NVFP4_46WE
 #undef NVFP4_46W
         return hipGetLastError();
     }
-    // W^T (and W): super-items of 16 bands by 16 tile columns
-    const uint32_t nsc = (ntc + 15) / 16, items = ((nbands + 15) / 16) * nsc;
+    // W^T (and W): items of 8 bands by 8 tile columns
+    const uint32_t ncg = (ntc + 7) / 8, items = ((nbands + 7) / 8) * ncg;
     uint32_t per;
     const uint32_t grid = grid_of(items, per);
 #define NVFP4_46T(F, E, W)                                                                                       \
-    k_quant_4o6_16x16t<F, E, W><<<grid, kThreads16, 0, stream>>>(xv, ntc, nbands, nsc, items, per, gden, amax, cw, \
+    k_quant_4o6_16x16t<F, E, W><<<grid, kThreads16, 0, stream>>>(xv, ntc, nbands, ncg, items, per, gden, amax, cw, \
                                                                  scales_w, g_w, ct, scales_wt, g_wt)
 #define NVFP4_46TO(F, E)                 \
     do {                                 \

@@ -11,7 +11,8 @@ namespace nvfp4 {
 enum Mode : int { kRN = 0, kSR = 1, kRHTSR = 2 };
 
 // Four-over-six error measure of a candidate: sum of squared differences, sum of magnitudes, largest magnitude.
-enum ErrMode : int { kErrMSE = 0, kErrMAE = 1, kErrMaxAbs = 2 };
+// kErrNone (internal) keeps the map-to-6 candidate alone: the standard NVFP4 quantization with g = amax / (6 B).
+enum ErrMode : int { kErrMSE = 0, kErrMAE = 1, kErrMaxAbs = 2, kErrNone = 3 };
 
 struct Philox {
     uint64_t seed;
