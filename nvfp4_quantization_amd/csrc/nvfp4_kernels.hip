@@ -1842,59 +1842,72 @@ k_quant_4o6_tensor(const uint4* __restrict__ x, uint32_t total_blocks, const flo
     quant_4o6_tensor_wg<F32, ERR>(x, total_blocks, amax, gden, codes, scales, gout, blockIdx.x, gridDim.x, tab);
 }
 
-// Per-row g: a workgroup walks whole rows (grid-stride over rows), lane t taking blocks t, t + 256, ... of each, with
-// the next block's loads (in this row or the next) in flight.  g, its two divisors and the row's multiplier table
-// are computed once per row: the table is double-buffered, so one barrier per row orders it (a thread writes the
-// table of row i only after the barrier of row i - 1, which every thread passes only after its reads of row i - 2).
-template <bool F32, int ERR>
+// Per-row g: a workgroup of NT threads walks whole rows (grid-stride over rows), lane t taking blocks t, t + NT, ...
+// of each, with the next block's loads (in this row or the next) in flight.  g, its two divisors and the row's
+// multiplier table are computed once per row: the table is double-buffered, so one barrier per row orders it (a
+// thread writes the table of row i only after the barrier of row i - 1, which every thread passes only after its
+// reads of row i - 2).
+template <bool F32, int ERR, int NT = kThreads>
 __device__ __forceinline__ void quant_4o6_rows_wg(const uint4* __restrict__ x, uint32_t rows, uint32_t bpr,
                                                   const float* __restrict__ amax, float gden,
                                                   uint2* __restrict__ codes, uint8_t* __restrict__ scales,
                                                   float* __restrict__ gout, uint32_t wg, uint32_t nwg,
                                                   RTable (&tabs)[2]) {
     const uint32_t t = threadIdx.x;
-    uint32_t row = wg;
     BlockWords<F32> a{};
-    if (row < rows && t < bpr) a = ld_block<F32>(x, (size_t)row * bpr + t);
-    for (uint32_t parity = 0; row < rows; row += nwg, parity ^= 1u) {
+    uint32_t pr = wg, pb = t;   // the next block to load
+    if (pr < rows && pb < bpr) a = ld_block<F32>(x, (size_t)pr * bpr + pb);
+    pb += NT;
+    if (pb >= bpr) {
+        pr += nwg;
+        pb = t;
+    }
+    for (uint32_t row = wg, parity = 0; row < rows; row += nwg, parity ^= 1u) {
         const float g = global_scale_den(amax[row], gden);
         if (t == 0) gout[row] = g;
         // a NaN or infinite g needs neither the table nor the divisors (every block of the row is written directly)
         const bool finite = __builtin_amdgcn_readfirstlane((uint32_t)(__builtin_fabsf(g) < __builtin_inff())) != 0;
         RTable& tab = tabs[parity];
-        if (finite && t < 128) fill_rtable_entry<false>(tab, t, g);
+        if (finite)
+            for (uint32_t e = t; e < 128; e += NT) fill_rtable_entry<false>(tab, e, g);
         __syncthreads();
         Divisor dv[2] = {};
         if (finite) {
             dv[0] = make_divisor_uniform(6.0f * g);
             dv[1] = make_divisor_uniform(4.0f * g);
         }
-        for (uint32_t blk = t; blk < bpr; blk += kThreads) {
-            uint32_t nrow = row, nblk = blk + kThreads;
-            if (nblk >= bpr) {
-                nrow = row + nwg;
-                nblk = t;
+        // (a thread with blocks in this row always has pb < bpr here)
+        for (uint32_t blk = t; blk < bpr; blk += NT) {
+            const BlockWords<F32> cur = a;
+            if (pr < rows) a = ld_block<F32>(x, (size_t)pr * bpr + pb);
+            pb += NT;
+            if (pb >= bpr) {
+                pr += nwg;
+                pb = t;
             }
-            BlockWords<F32> a2 = a;
-            if (nrow < rows) a2 = ld_block<F32>(x, (size_t)nrow * bpr + nblk);
             float xv[16];
-            widen_block<F32>(a, xv);
+            widen_block<F32>(cur, xv);
             uint32_t lo, hi, sb;
             quant_4o6_block<ERR>(xv, absmax16(xv), g, dv, tab, lo, hi, sb);
             const size_t n = (size_t)row * bpr + blk;
             st_nt(codes + n, make_uint2(lo, hi));
             st_nt(scales + n, (uint8_t)sb);
-            a = a2;
         }
     }
 }
 
+// 128-thread workgroups, 16 per CU: each thread takes 4 blocks of a 512-block row, so the per-row table and barrier
+// are shared by twice the blocks of a 256-thread workgroup (16384 x 8192 with the injected NaN/Inf: 74 -> 69 us;
+// without: 79 -> 77 us; 64-thread workgroups and two blocks' loads in flight per lane measured no better)
+constexpr int kThreads4o6Rows = 128;
+
 template <bool F32, int ERR>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads4o6Rows)
 k_quant_4o6_rows(const uint4* __restrict__ x, uint32_t rows, uint32_t bpr, const float* __restrict__ amax,
                  float gden, uint2* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gout) {
     __shared__ RTable tabs[2];
-    quant_4o6_rows_wg<F32, ERR>(x, rows, bpr, amax, gden, codes, scales, gout, blockIdx.x, gridDim.x, tabs);
+    quant_4o6_rows_wg<F32, ERR, kThreads4o6Rows>(x, rows, bpr, amax, gden, codes, scales, gout, blockIdx.x,
+                                                 gridDim.x, tabs);
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -3299,11 +3312,11 @@ hipError_t launch_quant_4o6(const void* x, int64_t rows, int64_t cols, bool per_
     const uint4* xv = reinterpret_cast<const uint4*>(x);
     uint2* cv = reinterpret_cast<uint2*>(codes);
     const uint32_t r = (uint32_t)rows;
-    const uint32_t grid_rows = (uint32_t)std::min<int64_t>(rows, (int64_t)cu_count() * 8);
+    const uint32_t grid_rows = (uint32_t)std::min<int64_t>(rows, (int64_t)cu_count() * 16);
     const uint32_t grid_tensor = grid_for(total, kThreads, 8);
 #define NVFP4_46(F, E)                                                                                              \
     do {                                                                                                            \
-        if (per_row) k_quant_4o6_rows<F, E><<<grid_rows, kThreads, 0, stream>>>(xv, r, bpr, amax, gden, cv, scales, g); \
+        if (per_row) k_quant_4o6_rows<F, E><<<grid_rows, kThreads4o6Rows, 0, stream>>>(xv, r, bpr, amax, gden, cv, scales, g); \
         else k_quant_4o6_tensor<F, E><<<grid_tensor, kThreads, 0, stream>>>(xv, total, amax, gden, cv, scales, g);     \
     } while (0)
 #define NVFP4_46F(F)                                   \
