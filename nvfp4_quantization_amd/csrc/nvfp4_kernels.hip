@@ -1204,15 +1204,20 @@ k_quant_colwise4(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, u
     constexpr bool RHT = MODE == kRHTSR;
     __shared__ Col4Stash st;
     __shared__ RTable tab;
+    const Col4Pos pos = col4_position(nrb, ns, blockIdx.x, !tiled);
+    const uint32_t wave = threadIdx.x >> 6;
+    const bool active = pos.rb < nrb && pos.c4 < cols;
+    uint2 v[16];
+    // RN: the tile's loads go out before the amax read and the table fill (19.3 -> 18.1 us at 8192 x 4096); with SR
+    // they follow the table and the Philox words are generated while they are in flight (loads first measured 0.9 us
+    // slower there)
+    if (!SR && active) load_col4_tile(x, cols, pos, v);
     const float g = global_scale(amax[0]);
     const Divisor d6 = make_divisor_uniform(6.0f * g);
     if (blockIdx.x == 0 && threadIdx.x == 0) gout[0] = g;
     fill_rtable<RHT>(tab, g);
-    const Col4Pos pos = col4_position(nrb, ns, blockIdx.x, !tiled);
-    const uint32_t wave = threadIdx.x >> 6;
-    if (pos.rb < nrb && pos.c4 < cols) {
-        uint2 v[16];
-        load_col4_tile(x, cols, pos, v);
+    if (active) {
+        if (SR) load_col4_tile(x, cols, pos, v);
         if (SR) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
