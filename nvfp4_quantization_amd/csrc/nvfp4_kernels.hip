@@ -541,6 +541,14 @@ __device__ __forceinline__ void quant_rowwise_wg(const uint4* __restrict__ x, ui
                                                  float* __restrict__ gout, uint32_t wg, uint32_t nwg, RTable& tab) {
     constexpr bool SR = MODE != kRN;
     constexpr bool RHT = MODE == kRHTSR;
+    // the first block's loads go out before the amax read and the table fill (RN at 8192 x 4096: 17.3 -> 16.4 us)
+    const uint32_t stride = nwg * kThreads;
+    uint32_t n = wg * kThreads + threadIdx.x;
+    uint4 a{}, b{};
+    if (n < total_blocks) {
+        a = ld16(x + 2 * (size_t)n);
+        b = ld16(x + 2 * (size_t)n + 1);
+    }
     float g = 0.0f;
     Divisor d6{};
     if (!PER_ROW) {
@@ -549,10 +557,7 @@ __device__ __forceinline__ void quant_rowwise_wg(const uint4* __restrict__ x, ui
         if (wg == 0 && threadIdx.x == 0) gout[0] = g;
         fill_rtable<RHT>(tab, g);
     }
-    const uint32_t stride = nwg * kThreads;
-    uint32_t n = wg * kThreads + threadIdx.x;
     if (n >= total_blocks) return;
-    uint4 a = ld16(x + 2 * (size_t)n), b = ld16(x + 2 * (size_t)n + 1);
     for (; n < total_blocks; n += stride) {
         const uint32_t nn = n + stride;
         uint4 a2 = a, b2 = b;
@@ -1566,6 +1571,16 @@ k_quant_16x16(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColG
               float* __restrict__ gt) {
     __shared__ ColStage<RB> st;
     __shared__ RTable tab;
+    // Workgroups loop over the tiles (grid-stride); the next tile's loads are issued before the current tile's
+    // W^T write-out, so reading overlaps writing, and the first tile's before the amax read and the table fill
+    // (43.5 -> 41.7 us at 14336 x 4096).  Lanes of a pair own the two halves of one 16x16 tile, so both exist or
+    // neither (cols is a multiple of 16).
+    const uint32_t ntc = cols >> 4;
+    uint32_t tile = blockIdx.x;
+    ColPos pos = col_position<RB>(cg, tile);
+    bool have = tile < cg.ntiles && pos.rb < cg.nrb && pos.c8 < cols;
+    uint4 v[16];
+    if (have) load_col_tile(x, cols, pos, v);
     const float g = global_scale(amax[0]);
     const Divisor d6 = make_divisor_uniform(6.0f * g);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -1573,15 +1588,6 @@ k_quant_16x16(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColG
         if (WANT_WT) gt[0] = g;
     }
     fill_rtable<false>(tab, g);
-    // Workgroups loop over the tiles (grid-stride); the next tile's loads are issued before the current tile's
-    // W^T write-out, so reading overlaps writing.  Lanes of a pair own the two halves of one 16x16 tile, so both
-    // exist or neither (cols is a multiple of 16).
-    const uint32_t ntc = cols >> 4;
-    uint32_t tile = blockIdx.x;
-    ColPos pos = col_position<RB>(cg, tile);
-    bool have = tile < cg.ntiles && pos.rb < cg.nrb && pos.c8 < cols;
-    uint4 v[16];
-    if (have) load_col_tile(x, cols, pos, v);
     while (tile < cg.ntiles) {
     const uint32_t lane = pos.lane, h = lane & 1u, c8 = pos.c8, ti = pos.rb;
     const uint32_t tj = c8 >> 4;
