@@ -110,9 +110,12 @@ def test_full_wgrad_colwise_single_read():
 
 
 # ---------------------------------------------------------------------------------------------------------------
-# Row-wise: the kernels take 128-row x 64-block items so that a workgroup owns whole tiles.
+# Row-wise: the single-read kernel and, where the tiled layout has padding, the quantizer take 128-row x 64-block
+# items so that a workgroup owns whole tiles; without padding (rows a multiple of 128, blocks per row of 4) the
+# quantizer stores each scale byte at its tiled place (128 x 1024, 256 x 4096, 384 x 512, 1024 x 8192).
 # ---------------------------------------------------------------------------------------------------------------
-ROW_SHAPES = [(300, 160), (1, 16), (128, 1024), (129, 1040), (1000, 4096), (256, 2064), (385, 3072)]
+ROW_SHAPES = [(300, 160), (1, 16), (128, 1024), (129, 1040), (1000, 4096), (256, 2064), (385, 3072), (256, 4096),
+              (384, 512), (1024, 8192)]
 
 
 def compare_rows(x, o, a, mode, gmode, mask, seed, offset):
