@@ -352,22 +352,6 @@ struct LdsRand {
 __device__ __forceinline__ uint2 rand_lo(const LdsRand& r) { return reinterpret_cast<const uint2*>(r.p)[0]; }
 __device__ __forceinline__ uint2 rand_hi(const LdsRand& r) { return reinterpret_cast<const uint2*>(r.p)[1]; }
 
-template <bool SR, typename R>
-__device__ __forceinline__ void encode16(const float (&q)[16], const R& inv, uint32_t& lo, uint32_t& hi) {
-    const float(&q0)[8] = *reinterpret_cast<const float(*)[8]>(&q[0]);
-    const float(&q1)[8] = *reinterpret_cast<const float(*)[8]>(&q[8]);
-    if (SR) {
-        const uint2 a = rand_lo(inv);
-        lo = pack8_sr(q0, a.x, a.y);
-        __builtin_amdgcn_sched_barrier(0);
-        const uint2 b = rand_hi(inv);
-        hi = pack8_sr(q1, b.x, b.y);
-    } else {
-        lo = pack8_rn(q0);
-        hi = pack8_rn(q1);
-    }
-}
-
 // Quantize one 16-element block; w[] is consumed (the scaled values are formed in its place).  w[] are the values
 // before the final 0.25 of the transform when RHT is set (y = fl(0.25 w)), the values themselves otherwise; m is
 // the block's absmax16(w); mul gives the multipliers of a scale code (fast_multiplier).  Which path a block takes
