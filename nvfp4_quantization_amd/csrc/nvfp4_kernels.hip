@@ -197,10 +197,18 @@ __device__ __forceinline__ float pair_swap(float v) {
 }
 
 // Maxima over a wave / workgroup of magnitude bit patterns (integer maximum: NaN > inf > finite).
+// The wave's maximum, equal in every lane (every lane active): DPP steps within each 16-lane row (the quad's lanes
+// i ^ 1 and i ^ 2, then the mirrored half row and the mirrored row), then the four rows' results read into scalar
+// registers, so no step goes through LDS (cross-lane shuffles are LDS permutes, which queue behind the LDS traffic
+// of the other workgroups on the CU).  A source lane outside the row or disabled yields the lane's own value.
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = umax(v, (uint32_t)__shfl_xor((int)v, off));
-    return v;
+    v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));    // quad [1,0,3,2]
+    v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));    // quad [2,3,0,1]
+    v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+    v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false));   // row_mirror
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return umax(umax(a, b), umax(c, d));
 }
 
 template <int WAVES = kWavesPerGroup>
@@ -1315,7 +1323,7 @@ __device__ __forceinline__ void announce(const Exchange& ex) {
 // trip to memory, since the slots are shared by all XCDs; a slot once seen with its maximum is not read again),
 // reduces them and, when none is missing, fills tab for g = amax / 2688, while the other waves wait at the one
 // barrier that follows.  Returns the maximum over the slots seen, equal in every thread; missing[l] (l < 64) gets
-// bit k set for each slot l + 64 k not seen, and nmissing (uniform) their count (then tab is not filled).  Uses
+// bit k set for each slot l + 64 k not seen, and nmissing (uniform) is nonzero if any is (then tab is not filled).  Uses
 // red[16].
 template <bool RHT>
 __device__ uint32_t exchange_max(uint32_t mbits, const Exchange& ex, uint32_t* red, uint32_t* missing,
@@ -1372,9 +1380,7 @@ __device__ uint32_t exchange_max(uint32_t mbits, const Exchange& ex, uint32_t* r
         }
         m = wave_max(m);
         missing[lane] = pending;
-        uint32_t cnt = __builtin_popcount(pending);
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) cnt += (uint32_t)__shfl_xor((int)cnt, off);
+        const uint32_t cnt = __ballot(pending != 0) != 0 ? 1u : 0u;   // whether any slot is missing
         if (cnt == 0) {
             const float g = global_scale(as_f(m));
 #pragma unroll 1
