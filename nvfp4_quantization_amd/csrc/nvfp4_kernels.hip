@@ -2465,19 +2465,21 @@ __device__ __forceinline__ uint32_t rowblock_absmax(const BlockWords<F32>& r, ui
 // all 16 loads issued before the first is used; one atomic max per workgroup into a zeroed amax[0].
 constexpr uint32_t kRowAmaxPerLane = 8;
 
+// per_lane (1..8) blocks per lane and round: fewer let the workgroups of a grouped launch share small tensors.
 template <bool RHT, bool F32 = false>
 __device__ __forceinline__ void amax_rowwise_tensor_wg(const uint4* __restrict__ x, uint32_t total_blocks,
                                                        uint32_t sign_mask, uint32_t* amax_bits, uint32_t wg,
-                                                       uint32_t nwg, uint32_t* red) {
-    constexpr uint32_t kPer = kRowAmaxPerLane * kColThreads;   // blocks per workgroup round
+                                                       uint32_t nwg, uint32_t* red,
+                                                       uint32_t per_lane = kRowAmaxPerLane) {
+    const uint32_t per = per_lane * kColThreads;   // blocks per workgroup round
     uint32_t m = 0;
-    for (uint32_t base = wg * kPer + threadIdx.x; base < total_blocks; base += nwg * kPer) {
+    for (uint32_t base = wg * per + threadIdx.x; base < total_blocks; base += nwg * per) {
         BlockWords<F32> a[kRowAmaxPerLane];
 #pragma unroll
         for (uint32_t j = 0; j < kRowAmaxPerLane; ++j) {
             const uint32_t n = base + j * kColThreads;
             a[j] = BlockWords<F32>{};   // blocks past the end count as zeros
-            if (n < total_blocks) a[j] = ld_block<F32>(x, n);
+            if (j < per_lane && n < total_blocks) a[j] = ld_block<F32>(x, n);
         }
 #pragma unroll
         for (uint32_t j = 0; j < kRowAmaxPerLane; ++j) m = umax(m, rowblock_absmax<RHT, F32>(a[j], sign_mask));
@@ -2822,6 +2824,7 @@ struct GroupItemK {
 struct GroupArgs {
     uint32_t count, total_wg;
     float gden;                   // four-over-six: 6 B for the bound B
+    uint32_t per_lane = kRowAmaxPerLane;   // per-tensor amax: blocks per lane and round
     GroupItemK it[kMaxGroup];
 };
 static_assert(sizeof(GroupArgs) <= 4096, "grouped descriptors must fit the kernel-argument space");
@@ -2870,7 +2873,7 @@ __global__ void __launch_bounds__(kColThreads) k_amax_grouped_tensor(const Group
     uint32_t wg, nwg;
     const GroupItemK& it = ga.it[group_item(ga, wg, nwg)];
     amax_rowwise_tensor_wg<RHT>(it.x, it.blocks, it.sign_mask, reinterpret_cast<uint32_t*>(const_cast<float*>(it.amax)),
-                                wg, nwg, red);
+                                wg, nwg, red, ga.per_lane);
 }
 
 template <bool RHT>
@@ -3420,10 +3423,17 @@ hipError_t launch_amax_grouped(const GroupTensor* items, int count, bool per_row
             else k_amax_grouped_rows<false><<<total, kThreads, 0, stream>>>(ga);
         }
     } else {
-        const uint64_t per = (uint64_t)kColThreads * kRowAmaxPerLane;
+        // blocks per lane so that the launch has about one workgroup per CU in all (small tensors share the CUs
+        // instead of taking one or two workgroups each): 32 tensors of 256 x 1024 take 8 workgroups each
+        uint64_t all = 0;
+        for (int i = 0; i < count; ++i) all += (uint64_t)items[i].rows * (uint64_t)(items[i].cols / 16);
+        const uint64_t pl = std::min<uint64_t>(kRowAmaxPerLane,
+                                               std::max<uint64_t>(1, (all + cus * kColThreads - 1) / (cus * kColThreads)));
+        const uint64_t per = (uint64_t)kColThreads * pl;
         const uint32_t total = build_group(items, count, ga, [&](const GroupItemK& k) {
             return capped((k.blocks + per - 1) / per, cus);
         });
+        ga.per_lane = (uint32_t)pl;
         if (ga.count) {
             k_zero_group_amax<<<1, 64, 0, stream>>>(ga);
             if (use_rht) k_amax_grouped_tensor<true><<<total, kColThreads, 0, stream>>>(ga);
