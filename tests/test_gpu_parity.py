@@ -191,14 +191,18 @@ def test_degenerate_amax_16x16_and_4o6():
     for amax_val in ODD_AMAX:
         say("degenerate amax 16x16 / 4o6", amax_val)
         a = torch.full((1,), amax_val, dtype=torch.float32, device="cuda")
-        w, wt = Q.nvfp4_quantize_rn(xd, a, Q.BLOCK_16X16, Q.BOTH, 0)
         (ow, osw, ogw), (ot, ost, ogt) = O.quantize_16x16(xf, np.array([amax_val], np.float32))
-        same_u8(host(w.codes), ow, "W codes")
-        same_u8(host(w.scales), osw, "W scales")
-        same_f32(host(w.g), ogw)
-        same_u8(host(wt.codes), ot, "W^T codes")
-        same_u8(host(wt.scales), ost, "W^T scales")
-        same_f32(host(wt.g), ogt)
+        # each orientation alone and both: W alone and W^T (+ W) run different kernels
+        for orient in (Q.BOTH, Q.ROWWISE, Q.COLWISE):
+            w, wt = Q.nvfp4_quantize_rn(xd, a, Q.BLOCK_16X16, orient, 0)
+            if w is not None:
+                same_u8(host(w.codes), ow, "W codes")
+                same_u8(host(w.scales), osw, "W scales")
+                same_f32(host(w.g), ogw)
+            if wt is not None:
+                same_u8(host(wt.codes), ot, "W^T codes")
+                same_u8(host(wt.scales), ost, "W^T scales")
+                same_f32(host(wt.g), ogt)
         o4 = Q.nvfp4_quantize_4o6(xd, a, 0)
         oc4, os4, og4, _ = O.quantize_4o6(xf, np.array([amax_val], np.float32), 0)
         same_u8(host(o4.codes), oc4, "4o6 codes")
