@@ -785,8 +785,9 @@ __device__ __forceinline__ uint32_t stage_index(uint32_t j, uint32_t lane, uint3
 }
 
 // Writes the staged codes/scales of the workgroup (64 RB threads): (column, row-block) pairs with the row-block
-// fastest, so RB consecutive threads store one output row's 8 RB contiguous bytes of codes and RB of scales.
-template <int RB>
+// fastest, so RB consecutive threads store one output row's 8 RB contiguous bytes of codes and RB of scales.  The
+// scale bytes are non-temporal stores, or ordinary (cached) ones with CACHED_SCALES.
+template <int RB, bool CACHED_SCALES = false>
 __device__ __forceinline__ void col_write_out(const ColStage<RB>& st, const ColPos& p, uint32_t rows, uint32_t cols,
                                               uint32_t nrb, uint8_t* __restrict__ codes,
                                               uint8_t* __restrict__ scales) {
@@ -798,7 +799,8 @@ __device__ __forceinline__ void col_write_out(const ColStage<RB>& st, const ColP
         const uint32_t si = stage_index<RB>(cl & 7, cl >> 3, rbl);
         const uint32_t c = col0 + cl;
         st_nt(codes + (size_t)c * (rows >> 1) + 8 * (size_t)rb, st.codes[si]);
-        st_nt(scales + (size_t)c * nrb + rb, st.scales[si]);
+        if (CACHED_SCALES) scales[(size_t)c * nrb + rb] = st.scales[si];
+        else st_nt(scales + (size_t)c * nrb + rb, st.scales[si]);
     }
 }
 
@@ -1687,7 +1689,8 @@ k_quant_16x16(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColG
     if (nhave) load_col_tile(x, cols, npos, v);
     if (WANT_WT) {
         __syncthreads();
-        col_write_out<RB>(st, pos, rows, cols, cg.nrb, ct, st_scales);
+        // with W as well, cached W^T scale bytes: 41.6 -> 40.7 us at 14336 x 4096 (W^T alone: 31.8 -> 32.2 us)
+        col_write_out<RB, WANT_W>(st, pos, rows, cols, cg.nrb, ct, st_scales);
         __syncthreads();
     }
     tile = next;
