@@ -1420,8 +1420,8 @@ __device__ __forceinline__ void release_slot(const Exchange& ex, uint32_t own) {
 // two 1024-thread workgroups per CU, 8 waves per SIMD, so a tensor of up to 512 tiles of 16 row-blocks x 256 columns
 // (8192 x 4096 on MI355X) stays in registers.  Phase 2 is bound by VALU issue, which twice the waves per SIMD issue
 // faster; the block maxima are recomputed there (six instructions per block) rather than held in registers.
-// Codes leave in two groups of two column blocks (each after a barrier), so the first group's stores overlap the
-// second group's arithmetic; the scales leave at the end.
+// The codes of each column block leave after a barrier of their own, so their stores overlap the next block's
+// arithmetic; the scales leave at the end.
 template <bool RHT>
 __device__ uint32_t tile_max_col4(const uint16_t* x, uint32_t cols, uint32_t nrb, const FastDiv& ns, uint32_t t,
                                   bool tiled, uint32_t sign_mask, uint2 (&v)[16]) {
