@@ -734,7 +734,10 @@ constexpr int kColThreads = 64 * kColRB;       // 1024
 template <int RB>
 struct ColStage {
     uint2 codes[8 * 64 * (RB + 1)];            // 8 codes bytes per block
-    uint8_t scales[8 * 64 * (RB + 1)];
+    // the tile scale codes of a 16x16 item (RB row-blocks x 32 tile columns), in both orders: a W scale row takes 32
+    // contiguous tile columns of one row-block, a W^T scale row 16 contiguous row-blocks of one tile column
+    __align__(16) uint8_t tsw[RB][32];
+    __align__(16) uint8_t tst[32][RB];
 };
 
 struct ColGrid {
@@ -784,24 +787,65 @@ __device__ __forceinline__ uint32_t stage_index(uint32_t j, uint32_t lane, uint3
     return (j * 64 + lane) * (RB + 1) + rbl;
 }
 
-// Writes the staged codes/scales of the workgroup (64 RB threads): (column, row-block) pairs with the row-block
-// fastest, so RB consecutive threads store one output row's 8 RB contiguous bytes of codes and RB of scales.  The
-// scale bytes are non-temporal stores, or ordinary (cached) ones with CACHED_SCALES.
-template <int RB, bool CACHED_SCALES = false>
+// Writes the staged codes of the workgroup (64 RB threads): (column, row-block) pairs with the row-block fastest, so
+// RB consecutive threads store one output row's 8 RB contiguous bytes of codes.
+template <int RB>
 __device__ __forceinline__ void col_write_out(const ColStage<RB>& st, const ColPos& p, uint32_t rows, uint32_t cols,
-                                              uint32_t nrb, uint8_t* __restrict__ codes,
-                                              uint8_t* __restrict__ scales) {
+                                              uint32_t nrb, uint8_t* __restrict__ codes) {
     const uint32_t col0 = p.strip * 512;
     const uint32_t ncol = min(512u, cols - col0), nr = min((uint32_t)RB, nrb - p.group * RB);
     const uint32_t rbl = threadIdx.x % RB, rb = p.group * RB + rbl;
     if (rbl >= nr) return;
     for (uint32_t cl = threadIdx.x / RB; cl < ncol; cl += 64) {
         const uint32_t si = stage_index<RB>(cl & 7, cl >> 3, rbl);
-        const uint32_t c = col0 + cl;
-        st_nt(codes + (size_t)c * (rows >> 1) + 8 * (size_t)rb, st.codes[si]);
-        if (CACHED_SCALES) scales[(size_t)c * nrb + rb] = st.scales[si];
-        else st_nt(scales + (size_t)c * nrb + rb, st.scales[si]);
+        st_nt(codes + (size_t)(col0 + cl) * (rows >> 1) + 8 * (size_t)rb, st.codes[si]);
     }
+}
+
+// The first n (<= 16) bytes of v to dst: one 16-byte store when whole is set (n == 16, dst 16-byte aligned), else
+// byte by byte (straight-line predicated stores: a loop with a variable trip count here raised the register pressure
+// of the 16x16 kernel into spills).
+__device__ __forceinline__ void store_piece16(uint8_t* __restrict__ dst, const uint4& v, uint32_t n, bool whole) {
+    if (whole) {
+        *reinterpret_cast<uint4*>(dst) = v;
+        return;
+    }
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (uint32_t i = 0; i < 16; ++i)
+        if (i < n) dst[i] = (uint8_t)(w[i >> 2] >> (8 * (i & 3u)));
+}
+
+// The W scale rows of one row-block of a 16x16 item, written by its wave: row 16 rb + k takes the item's 32 tile
+// columns, two 16-byte pieces, one per lane 0..31 (lane 2 k + half).  The wave's lane pairs have put their scale codes
+// in its row of tsw; the wave reads back what it wrote itself, so no workgroup barrier is needed.  Ordinary (cached)
+// stores, so that the pieces that the items of neighbouring strips write into one line can meet in L2.  Pieces that
+// are not whole, or not 16-byte aligned in the output (cols % 256 != 0), are written byte by byte.
+template <int RB>
+__device__ __forceinline__ void write_w_scales(const ColStage<RB>& st, const ColPos& p, uint32_t cols,
+                                               uint8_t* __restrict__ sw) {
+    const uint32_t ntc = cols >> 4, tc0 = p.strip * 32, ntcs = min(32u, ntc - tc0);
+    const uint32_t rbl = p.rb - p.group * RB, k = p.lane >> 1, half = p.lane & 1u;
+    if (p.lane >= 32 || 16 * half >= ntcs) return;
+    uint8_t* dst = sw + (size_t)(16 * p.rb + k) * ntc + tc0 + 16 * half;
+    const uint8_t* src = &st.tsw[rbl][16 * half];
+    const uint32_t n = min(16u, ntcs - 16 * half);
+    store_piece16(dst, *reinterpret_cast<const uint4*>(src), n, n == 16 && (ntc & 15u) == 0);
+}
+
+// The W^T scale rows of a 16x16 item (after the workgroup barrier; threads 512 .. 1023 of 1024): output row c takes the
+// 16 row-blocks of its tile column, one 16-byte piece.  Ordinary (cached) stores; pieces that are not whole, or not
+// 16-byte aligned in the output (rows % 256 != 0), are written byte by byte.
+template <int RB>
+__device__ __forceinline__ void write_wt_scales(const ColStage<RB>& st, const ColPos& p, uint32_t cols, uint32_t nrb,
+                                                uint8_t* __restrict__ st_scales) {
+    static_assert(RB == 16, "one 16-byte piece per row needs 16 row-blocks");
+    const uint32_t col0 = p.strip * 512, nr = min((uint32_t)RB, nrb - p.group * RB);
+    const uint32_t cl = threadIdx.x - 512;
+    if (threadIdx.x < 512 || cl >= min(512u, cols - col0)) return;
+    uint8_t* dst = st_scales + (size_t)(col0 + cl) * nrb + p.group * RB;
+    const uint8_t* src = &st.tst[cl >> 4][0];
+    store_piece16(dst, *reinterpret_cast<const uint4*>(src), nr, nr == 16 && (nrb & 15u) == 0);
 }
 
 // LDS of a column-wise workgroup that generates every block's random words ahead of the data: entry (wave, j,
@@ -1577,8 +1621,8 @@ k_quant_16x16(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColG
     // Workgroups loop over the tiles (grid-stride); the next tile's loads are issued before the current tile's
     // W^T write-out, so reading overlaps writing, and the first tile's before the amax read and the table fill
     // (43.5 -> 41.7 us at 14336 x 4096).  Lanes of a pair own the two halves of one 16x16 tile, so both exist or
-    // neither (cols is a multiple of 16).
-    const uint32_t ntc = cols >> 4;
+    // neither (cols is a multiple of 16).  The scales of both orientations leave with the W^T write-out.
+    static_assert(WANT_WT, "W alone takes the band kernel");
     uint32_t tile = blockIdx.x;
     ColPos pos = col_position<RB>(cg, tile);
     bool have = tile < cg.ntiles && pos.rb < cg.nrb && pos.c8 < cols;
@@ -1593,7 +1637,6 @@ k_quant_16x16(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColG
     fill_rtable<false>(tab, g);
     while (tile < cg.ntiles) {
     const uint32_t lane = pos.lane, h = lane & 1u, c8 = pos.c8, ti = pos.rb;
-    const uint32_t tj = c8 >> 4;
     if (have) {
         // Maximum magnitude of the lane's 128 inputs on the bf16 bit patterns (packed 16-bit integer maxima of
         // the magnitude bits: NaN > inf > finite, as for the binary32 values they widen to exactly).
@@ -1638,10 +1681,6 @@ k_quant_16x16(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColG
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (WANT_WT) {
-                st.scales[stage_index<RB>(2 * p, lane, rbl)] = (uint8_t)sb;
-                st.scales[stage_index<RB>(2 * p + 1, lane, rbl)] = (uint8_t)sb;
-            }
         }
         if (!fast) [[unlikely]] {
             // NaN multiplier (NaN amax) or a degenerate scale: NaN products get code 0x7.  The tile is read again
@@ -1674,20 +1713,21 @@ k_quant_16x16(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColG
 #pragma unroll
             for (int k = 0; k < 16; ++k)
                 st_nt(cw_codes + (size_t)(16 * ti + k) * (cols >> 1) + (c8 >> 1), rowc[k]);
-            // cached byte stores: the 32-byte pieces of a W scale row that neighbouring workgroups write merge in L2
-            // (45.6 -> 43.6 us at 14336 x 4096 against non-temporal stores)
-#pragma unroll
-            for (int k = 0; k < 8; ++k) sw[(size_t)(16 * ti + 8 * h + k) * ntc + tj] = (uint8_t)sb;
+        }
+        if (h == 0) {
+            st.tsw[rbl][lane >> 1] = (uint8_t)sb;
+            st.tst[lane >> 1][rbl] = (uint8_t)sb;
         }
     }
+    if (WANT_W && pos.rb < cg.nrb) write_w_scales<RB>(st, pos, cols, sw);
     const uint32_t next = tile + gridDim.x;
     const ColPos npos = col_position<RB>(cg, next);
     const bool nhave = next < cg.ntiles && npos.rb < cg.nrb && npos.c8 < cols;
     if (nhave) load_col_tile(x, cols, npos, v);
     if (WANT_WT) {
         __syncthreads();
-        // with W as well, cached W^T scale bytes: 41.6 -> 40.7 us at 14336 x 4096 (W^T alone: 31.8 -> 32.2 us)
-        col_write_out<RB, WANT_W>(st, pos, rows, cols, cg.nrb, ct, st_scales);
+        col_write_out<RB>(st, pos, rows, cols, cg.nrb, ct);
+        write_wt_scales<RB>(st, pos, cols, cg.nrb, st_scales);
         __syncthreads();
     }
     tile = next;

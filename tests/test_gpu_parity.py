@@ -262,7 +262,7 @@ def check_16x16(x, orient, tile_rows=None):
         same_f32(host(c.g), ogt)
 
 
-@pytest.mark.parametrize("shape", [(64, 96), (272, 528), (16, 16), (1024, 2080)])
+@pytest.mark.parametrize("shape", [(64, 96), (272, 528), (16, 16), (1024, 2080), (512, 768), (2304, 256), (2048, 2048), (4096, 1792)])
 @pytest.mark.parametrize("orient", [Q.ROWWISE, Q.COLWISE, Q.BOTH])
 def test_16x16(shape, orient):
     check_16x16(W.weight_outliers(*shape, seed=shape[0] + shape[1]), orient)
