@@ -1610,6 +1610,32 @@ k_amax_quant_colwise4(const uint16_t* __restrict__ x, uint32_t rows, uint32_t co
 // lanes of a pair always take the same steps).  W rows are written directly (consecutive lanes write consecutive
 // 4-byte pieces of a row); W^T is staged in LDS like the column-wise codes.
 // ------------------------------------------------------------------------------------------------------------
+// Transposes an 8 x 8 matrix of nibbles held as 8 words (word k = row k, nibble c = column c): afterwards word c
+// holds column c (nibble k = row k).  Three exchange stages between word pairs: 4 x 4 blocks (16-bit halves of words
+// k, k + 4) and 2 x 2 blocks (bytes of words k, k + 2) by byte permutes, then single nibbles of words k, k + 1 by
+// bit-field inserts.
+__device__ __forceinline__ void transpose8x8_nibbles(uint32_t (&a)[8]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t x = a[k], y = a[k + 4];
+        a[k] = __builtin_amdgcn_perm(y, x, 0x05040100u);       // x bytes 0, 1; y bytes 0, 1
+        a[k + 4] = __builtin_amdgcn_perm(y, x, 0x07060302u);   // x bytes 2, 3; y bytes 2, 3
+    }
+#pragma unroll
+    for (int k : {0, 1, 4, 5}) {
+        const uint32_t x = a[k], y = a[k + 2];
+        a[k] = __builtin_amdgcn_perm(y, x, 0x06020400u);       // x byte 0, y byte 0, x byte 2, y byte 2
+        a[k + 2] = __builtin_amdgcn_perm(y, x, 0x07030501u);   // x byte 1, y byte 1, x byte 3, y byte 3
+    }
+    constexpr uint32_t lo = 0x0F0F0F0Fu;
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) {
+        const uint32_t x = a[k], y = a[k + 1];
+        a[k] = (x & lo) | ((y << 4) & ~lo);
+        a[k + 1] = ((x >> 4) & lo) | (y & ~lo);
+    }
+}
+
 template <bool WANT_W, bool WANT_WT, int RB>
 __global__ void __launch_bounds__(64 * RB)
 k_quant_16x16(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColGrid cg,
@@ -1652,8 +1678,8 @@ k_quant_16x16(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColG
         const uint32_t sb = scale_code(m, d6);
         const float r = tab.r[sb];
         const bool fast = tab.rq[sb] == tab.rq[sb];   // see fast_multiplier
-        // Every product is converted once and packed both ways: column pair (2p, 2p+1) gives byte p of every W row
-        // and the two W^T column blocks 2p, 2p+1.
+        // Every product is converted once: column pair (2p, 2p+1) gives byte p of every W row; the W^T codes are
+        // the W codes transposed (two 8 x 8 nibble transposes), not a second conversion.
         uint32_t rowc[16];
         const uint32_t rbl = ti - pos.group * RB;
 #pragma unroll
@@ -1668,17 +1694,9 @@ k_quant_16x16(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColG
                     qa[i] = bf16_lo(word, 0u) * r;
                     qb[i] = bf16_hi(word, 0u) * r;
                 }
-                if (WANT_W) {
 #pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        rowc[8 * half + i] = cvt_fp4_byte(p, p == 0 ? 0u : rowc[8 * half + i], qa[i], qb[i]);
-                }
-                if (WANT_WT) {
-                    uint32_t* ca = reinterpret_cast<uint32_t*>(&st.codes[stage_index<RB>(2 * p, lane, rbl)]);
-                    uint32_t* cb = reinterpret_cast<uint32_t*>(&st.codes[stage_index<RB>(2 * p + 1, lane, rbl)]);
-                    ca[half] = pack8_rn(qa);
-                    cb[half] = pack8_rn(qb);
-                }
+                for (int i = 0; i < 8; ++i)
+                    rowc[8 * half + i] = cvt_fp4_byte(p, p == 0 ? 0u : rowc[8 * half + i], qa[i], qb[i]);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -1692,22 +1710,20 @@ k_quant_16x16(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColG
                 float q[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) q[j] = ((j & 1) ? bf16_hi(ws[j >> 1], 0u) : bf16_lo(ws[j >> 1], 0u)) * r;
-                if (WANT_W) rowc[k] = patch_nan8(rowc[k], q);
+                rowc[k] = patch_nan8(rowc[k], q);
             }
-            if (WANT_WT) {
+        }
+        {
+            uint32_t t0[8], t1[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    float w[16];
-                    widen_col_block<false>(v, j, 0u, w);
-                    float q[16];
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) q[i] = w[i] * r;
-                    const uint32_t si = stage_index<RB>(j, lane, rbl);
-                    const uint2 c = st.codes[si];
-                    st.codes[si] = make_uint2(patch_nan8(c.x, *reinterpret_cast<const float(*)[8]>(&q[0])),
-                                              patch_nan8(c.y, *reinterpret_cast<const float(*)[8]>(&q[8])));
-                }
+            for (int k = 0; k < 8; ++k) {
+                t0[k] = rowc[k];
+                t1[k] = rowc[8 + k];
             }
+            transpose8x8_nibbles(t0);
+            transpose8x8_nibbles(t1);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) st.codes[stage_index<RB>(j, lane, rbl)] = make_uint2(t0[j], t1[j]);
         }
         if (WANT_W) {
 #pragma unroll
