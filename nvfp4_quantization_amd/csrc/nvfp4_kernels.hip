@@ -818,7 +818,8 @@ __device__ __forceinline__ void store_piece16(uint8_t* __restrict__ dst, const u
 
 // The W scale rows of one row-block of a 16x16 item, written by its wave: row 16 rb + k takes the item's 32 tile
 // columns, two 16-byte pieces, one per lane 0..31 (lane 2 k + half).  The wave's lane pairs have put their scale codes
-// in its row of tsw; the wave reads back what it wrote itself, so no workgroup barrier is needed.  Ordinary (cached)
+// in its row of tsw; the wave reads back what its own lanes wrote, so a wavefront-scope fence (the wait for its LDS
+// writes) stands in for a workgroup barrier.  Ordinary (cached)
 // stores, so that the pieces that the items of neighbouring strips write into one line can meet in L2.  Pieces that
 // are not whole, or not 16-byte aligned in the output (cols % 256 != 0), are written byte by byte.
 template <int RB>
@@ -826,6 +827,8 @@ __device__ __forceinline__ void write_w_scales(const ColStage<RB>& st, const Col
                                                uint8_t* __restrict__ sw) {
     const uint32_t ntc = cols >> 4, tc0 = p.strip * 32, ntcs = min(32u, ntc - tc0);
     const uint32_t rbl = p.rb - p.group * RB, k = p.lane >> 1, half = p.lane & 1u;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
     if (p.lane >= 32 || 16 * half >= ntcs) return;
     uint8_t* dst = sw + (size_t)(16 * p.rb + k) * ntc + tc0 + 16 * half;
     const uint8_t* src = &st.tsw[rbl][16 * half];
