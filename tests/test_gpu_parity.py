@@ -262,6 +262,18 @@ def check_16x16(x, orient, tile_rows=None):
         same_f32(host(c.g), ogt)
 
 
+@pytest.mark.parametrize("orient", [Q.ROWWISE, Q.COLWISE, Q.BOTH])
+def test_16x16_nan_inf_elements(orient):
+    """16x16 tiles holding a NaN (tile scale 0x7F, every code 0x7 by the general path) or +-inf, beside ordinary tiles:
+    the W^T codes of a patched tile come from its patched W codes."""
+    x = W.weight_outliers(272, 528, seed=31)
+    x[3, 7] = 0x7FC0      # NaN in tile (0, 0)
+    x[20, 40] = 0xFFC1    # negative NaN in tile (1, 2)
+    x[100, 300] = 0x7F80  # +inf in tile (6, 18)
+    x[271, 527] = 0xFF80  # -inf in the last tile
+    check_16x16(x, orient)
+
+
 @pytest.mark.parametrize("shape", [(64, 96), (272, 528), (16, 16), (1024, 2080), (512, 768), (2304, 256), (2048, 2048), (4096, 1792)])
 @pytest.mark.parametrize("orient", [Q.ROWWISE, Q.COLWISE, Q.BOTH])
 def test_16x16(shape, orient):
