@@ -819,9 +819,9 @@ __device__ __forceinline__ void store_piece16(uint8_t* __restrict__ dst, const u
 // The W scale rows of one row-block of a 16x16 item, written by its wave: row 16 rb + k takes the item's 32 tile
 // columns, two 16-byte pieces, one per lane 0..31 (lane 2 k + half).  The wave's lane pairs have put their scale codes
 // in its row of tsw; the wave reads back what its own lanes wrote, so a wavefront-scope fence (the wait for its LDS
-// writes) stands in for a workgroup barrier.  Ordinary (cached)
-// stores, so that the pieces that the items of neighbouring strips write into one line can meet in L2.  Pieces that
-// are not whole, or not 16-byte aligned in the output (cols % 256 != 0), are written byte by byte.
+// writes) stands in for a workgroup barrier.  Ordinary (cached) stores, so that the pieces that the items of
+// neighbouring strips write into one line can meet in L2.  Pieces that are not whole, or not 16-byte aligned in the
+// output (cols % 256 != 0), are written byte by byte.
 template <int RB>
 __device__ __forceinline__ void write_w_scales(const ColStage<RB>& st, const ColPos& p, uint32_t cols,
                                                uint8_t* __restrict__ sw) {
@@ -1650,7 +1650,8 @@ k_quant_16x16(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, ColG
     // Workgroups loop over the tiles (grid-stride); the next tile's loads are issued before the current tile's
     // W^T write-out, so reading overlaps writing, and the first tile's before the amax read and the table fill
     // (43.5 -> 41.7 us at 14336 x 4096).  Lanes of a pair own the two halves of one 16x16 tile, so both exist or
-    // neither (cols is a multiple of 16).  The scales of both orientations leave with the W^T write-out.
+    // neither (cols is a multiple of 16).  Each wave writes its W codes and W scale rows; the W^T codes and scale rows
+    // leave after the item's barrier.
     static_assert(WANT_WT, "W alone takes the band kernel");
     uint32_t tile = blockIdx.x;
     ColPos pos = col_position<RB>(cg, tile);
