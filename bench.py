@@ -73,6 +73,10 @@ def parse():
     p.add_argument("--counter-launches", type=int, default=0, metavar="N",
                    help="for a rocprofv3 --pmc run: launch N steps eagerly, N quantize-only calls (amax given), "
                         "then N copies of a 128 MiB buffer (the calibration copy), and exit without timing")
+    p.add_argument("--counter-configs", action="store_true",
+                   help="with --counter-launches: also launch N 16x16 W+W^T quantizations of the 14336x4096 weight and "
+                        "N four-over-six quantizations of the 16384x8192 tensor (per-row g, no NaN/Inf), amax given, "
+                        "before the calibration copies")
     return p.parse_args()
 
 
@@ -480,6 +484,27 @@ def measure(args, Q, W, dev, x_bits, x0, xs, outs, amaxes, masks, step, nbuf, st
         for k in range(args.counter_launches):           # the quantize kernel alone, on the amax the steps wrote
             Q.nvfp4_quantize_rht_sr(xs[k % nbuf], amaxes[k % nbuf], masks[k % 64], SEED, k, Q.COLWISE,
                                     Q.G_PER_TENSOR, out=outs[k % nbuf])
+        if args.counter_configs:
+            # two input buffers each, alternating; every output buffer written in full by every launch
+            r, c = 14336, 4096
+            w0 = torch.from_numpy(W.make("weight_16x16_14336x4096").view(np.int16)).to(dev)
+            ws = [w0, w0.clone()]
+            wa = Q.nvfp4_amax(w0, Q.ROWWISE, Q.G_PER_TENSOR)
+            wo = (Q.alloc_out(r, c, Q.G_PER_TENSOR, dev), Q.alloc_out(c, r, Q.G_PER_TENSOR, dev))
+            for k in range(args.counter_launches):
+                Q.nvfp4_quantize_rn(ws[k % 2], wa, Q.BLOCK_16X16, Q.BOTH, Q.G_PER_TENSOR, row_out=wo[0], col_out=wo[1])
+            torch.cuda.synchronize()
+            del ws, wo
+            r, c = 16384, 8192
+            f0 = torch.from_numpy(W.make("four_over_six_16384x8192", frac_special=0.0).view(np.int16)).to(dev)
+            fs = [f0, f0.clone()]
+            fa = Q.nvfp4_amax(f0, Q.ROWWISE, Q.G_PER_ROW)
+            fo = Q.alloc_out(r, c, Q.G_PER_ROW, dev)
+            for k in range(args.counter_launches):
+                Q.nvfp4_quantize_4o6(fs[k % 2], fa, Q.G_PER_ROW, out=fo)
+            torch.cuda.synchronize()
+            del fs, fo
+            torch.cuda.empty_cache()
         # four source/destination pairs in turn, so that no copy finds its source still in the L2 caches (32 MB)
         srcs = [torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).uniform_() for _ in range(4)]
         dsts = [torch.empty_like(srcs[0]) for _ in range(4)]
